@@ -1,0 +1,230 @@
+"""CPU float64 oracle for DuoAttention's deployment hot path.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s
+``cpu_baseline`` leg may import this module. It shares no code with the HIP library under
+``head_split_kv_amd/`` and imports nothing from it; the product path never calls it.
+
+Every function is written from the text of these pages (all about arXiv 2410.10819,
+"DuoAttention: Efficient Long-Context LLM Inference with Retrieval and Streaming Heads"):
+
+* *explainer*: the paper-graph-ui.vercel.app walkthrough of the paper;
+* *OpenReview thread*: the paperhub.cn page with the authors' rebuttal;
+* *abstract*: the arXiv abstract quoted on the mlsanity.com index page.
+
+What it computes is a plain definition, so the oracle is that definition written out with no
+blocking, splitting or reordering: per query head, softmax over the logits of the visible
+keys (masked positions get a logit of -inf), times V, all in float64 from the exact input
+values. The visible set is built from token positions only, never from a cache or a slot
+table. Readings taken where the pages are silent or garbled are marked "Reading:" below.
+
+Pins: every function here is checked in ``tests/test_oracle_pins.py`` against something other
+than itself (brute force, library routines, special cases, the worked example of the chunked
+pre-filling figure and the pages' printed memory numbers). Nothing is "parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------------------------
+# Head classes and visibility
+# --------------------------------------------------------------------------------------------
+
+def kv_head_of(h: int, group: int) -> int:
+    """KV head serving query head ``h`` when ``group`` query heads share one KV head.
+
+    OpenReview thread, reply on the proportion of retrieval heads: in Llama-3-8B four query
+    heads share one KV head; the gate (and so the retrieval/streaming class) is per KV head
+    (explainer, "Gate Parameterization"). Reading: groups are contiguous, head h -> h // G.
+    """
+    return h // group
+
+
+def visible_mask(q_pos, k_pos, retrieval: bool, sink: int, recent: int) -> np.ndarray:
+    """Boolean ``[len(q_pos), len(k_pos)]``: may query position p attend to key position t?
+
+    Explainer, "The Full and Streaming Attention Masks": the causal mask keeps t <= p; the
+    Lambda-shaped streaming mask keeps only the first ``sink`` tokens of the sequence and the
+    ``recent`` most recent tokens, every other logit being set to -inf before the softmax.
+
+    Reading: the recent window counts the query's own token, so it is t in [p-R+1, p]. The
+    decoding procedure (explainer, "Decoding Procedure", step 3-4) keeps at most S+R tokens
+    in the streaming cache, which is exactly this set after the new token is appended.
+    """
+    p = np.asarray(q_pos, dtype=np.int64)[:, None]
+    t = np.asarray(k_pos, dtype=np.int64)[None, :]
+    causal = (t <= p) & (t >= 0)
+    if retrieval:
+        return causal
+    return causal & ((t < sink) | (t >= p - recent + 1))
+
+
+# --------------------------------------------------------------------------------------------
+# Attention
+# --------------------------------------------------------------------------------------------
+
+def default_scale(d: int) -> float:
+    """Reading: the pages' mask equations omit the softmax temperature; standard Transformer
+    attention (which the explainer says Q, K, V are) uses 1/sqrt(head_dim)."""
+    return 1.0 / math.sqrt(d)
+
+
+def masked_softmax_attention(q, k, v, mask, scale):
+    """One head: ``q [P, d]``, ``k, v [T, d]``, ``mask [P, T]`` -> ``out [P, d]``, ``lse [P]``.
+
+    softmax(scale * q k^T with masked logits = -inf) v, in float64, max-subtracted.
+    ``lse`` is the natural log of the softmax denominator of the unshifted logits.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    z = scale * (q @ k.T)
+    z = np.where(mask, z, -np.inf)
+    m = z.max(axis=1, keepdims=True)
+    w = np.exp(z - m)
+    den = w.sum(axis=1, keepdims=True)
+    out = (w @ v) / den
+    lse = (m + np.log(den))[:, 0]
+    return out, lse
+
+
+def attention(q, k, v, q_pos, k_pos, retrieval, sink, recent, scale=None):
+    """All heads of one layer and one sequence.
+
+    ``q [P, Hq, d]``, ``k, v [T, Hkv, d]``, ``q_pos [P]``, ``k_pos [T]``,
+    ``retrieval [Hkv]`` (1 = retrieval KV head) -> ``out [P, Hq, d]``, ``lse [P, Hq]``.
+
+    Retrieval heads use the causal mask, streaming heads the Lambda mask (explainer,
+    "Decoding Procedure", steps 2-3); the outputs are returned in the native head order,
+    which is the concatenation of step 5 undone by the head permutation of "Head Reordering
+    Preprocessing" (heads are permutation-invariant there). No KV head is repeated for GQA:
+    each query head reads its own group's K and V (OpenReview thread, GQA compatibility).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    P, Hq, d = q.shape
+    T, Hkv, _ = k.shape
+    assert Hq % Hkv == 0
+    G = Hq // Hkv
+    if scale is None:
+        scale = default_scale(d)
+    out = np.empty((P, Hq, d), dtype=np.float64)
+    lse = np.empty((P, Hq), dtype=np.float64)
+    masks = {}
+    for h in range(Hq):
+        j = kv_head_of(h, G)
+        r = bool(retrieval[j])
+        if r not in masks:
+            masks[r] = visible_mask(q_pos, k_pos, r, sink, recent)
+        out[:, h, :], lse[:, h] = masked_softmax_attention(q[:, h, :], k[:, j, :], v[:, j, :],
+                                                           masks[r], scale)
+    return out, lse
+
+
+def decode_step(q, k_hist, v_hist, retrieval, sink, recent, scale=None):
+    """Decode one token for one sequence.
+
+    ``k_hist, v_hist [n, Hkv, d]`` hold tokens 0..n-1, the newest (position n-1) included;
+    ``q [Hq, d]`` is that token's query. Returns ``out [Hq, d]``, ``lse [Hq]``.
+
+    Reading: the cache is updated before attending (explainer, "Decoding Procedure" lists the
+    update as step 4), so the query sees its own key, as the causal mask requires. For a
+    one-token step the token overwritten in the ring is p-R, outside the window, so the order
+    does not change the result.
+    """
+    n = k_hist.shape[0]
+    out, lse = attention(np.asarray(q)[None], k_hist, v_hist, [n - 1], np.arange(n),
+                         retrieval, sink, recent, scale)
+    return out[0], lse[0]
+
+
+def prefill_chunk(q, k_hist, v_hist, start, retrieval, sink, recent, scale=None):
+    """Chunked pre-filling of positions ``start .. start+m-1`` for one sequence.
+
+    ``q [m, Hq, d]``; ``k_hist, v_hist [start+m, Hkv, d]`` (all earlier tokens plus the
+    chunk). Returns ``out [m, Hq, d]``, ``lse [m, Hq]``.
+
+    Explainer, "Chunked Pre-filling": retrieval heads attend to every earlier token plus the
+    chunk causally. Reading: streaming heads apply the same per-query Lambda mask as in
+    decoding, so the result does not depend on the chunk size and equals token-by-token
+    decoding; the pruned cache after each chunk still holds every key this mask can reach.
+    """
+    m = np.asarray(q).shape[0]
+    T = start + m
+    assert k_hist.shape[0] >= T
+    return attention(q, k_hist[:T], v_hist[:T], np.arange(start, T), np.arange(T),
+                     retrieval, sink, recent, scale)
+
+
+# --------------------------------------------------------------------------------------------
+# Streaming cache state (sink fill, then ring overwrite)
+# --------------------------------------------------------------------------------------------
+
+def slot_of(t: int, sink: int, recent: int) -> int:
+    """Streaming-cache slot of token t.
+
+    Explainer, "Decoding Procedure", step 4: the streaming cache keeps the sink tokens and
+    evicts the oldest non-sink token once it holds more than S+R tokens. Reading: sinks take
+    slots 0..S-1 in order; later tokens go round a ring of R slots starting at slot S.
+    """
+    return t if t < sink else sink + (t - sink) % recent
+
+
+def streaming_valid_tokens(n: int, sink: int, recent: int) -> np.ndarray:
+    """Positions held by a streaming cache after ``n`` tokens: the first min(S, n) tokens and
+    the last R non-sink tokens (explainer, "Decoding Procedure" step 3 and "Chunked
+    Pre-filling": the pruned cache keeps only attention sinks and recent tokens)."""
+    sinks = np.arange(min(sink, n))
+    recent_part = np.arange(max(sink, n - recent), n)
+    return np.concatenate([sinks, recent_part]).astype(np.int64)
+
+
+def slot_table(n: int, sink: int, recent: int) -> np.ndarray:
+    """int32 ``[S+R]``: the position held by each slot after ``n`` tokens, -1 if empty."""
+    table = np.full(sink + recent, -1, dtype=np.int32)
+    for t in streaming_valid_tokens(n, sink, recent):
+        table[slot_of(int(t), sink, recent)] = t
+    return table
+
+
+def streaming_cache_rows(x_hist, n, sink, recent):
+    """Expected streaming-cache contents ``[S+R, ...]`` of one head after ``n`` tokens:
+    slot s holds row ``x_hist[slot_table[s]]``; empty slots are returned as NaN."""
+    x_hist = np.asarray(x_hist)
+    table = slot_table(n, sink, recent)
+    rows = np.full((sink + recent,) + x_hist.shape[1:], np.nan, dtype=np.float64)
+    ok = table >= 0
+    rows[ok] = x_hist[table[ok]]
+    return rows, table
+
+
+# --------------------------------------------------------------------------------------------
+# KV memory model
+# --------------------------------------------------------------------------------------------
+
+def full_kv_elements(layers: int, kv_heads: int, length: int, d: int) -> int:
+    """Full-attention KV cache size in elements: 2 * D * H * L * d (explainer, "Context and
+    Motivation": K and V for every head of every layer and every token). For a GQA model H
+    counts KV heads."""
+    return 2 * layers * kv_heads * length * d
+
+
+def duo_kv_elements_layer(n_retrieval: int, n_streaming: int, length: int, sink: int,
+                          recent: int, d: int) -> int:
+    """Elements of K (or of V) held by one layer: (H_r * L + H_s * (S + R)) * d (explainer,
+    "Decoding Procedure", memory formula). Reading: a streaming cache holds min(L, S+R)
+    tokens, since it holds at most S+R and never a token that does not exist yet."""
+    return (n_retrieval * length + n_streaming * min(length, sink + recent)) * d
+
+
+def budget_ratio(retrieval_fraction: float, length: int, sink: int, recent: int) -> float:
+    """Retained KV over full KV for a retrieval fraction r: (r L + (1 - r)(S + R)) / L.
+
+    This is the memory formula above divided by H * L * d. The OpenReview thread's worked
+    budget ratios (64K tokens, 50 % retrieval, 64 sinks + 256 recent) use the same terms.
+    """
+    r = retrieval_fraction
+    return (r * length + (1.0 - r) * min(length, sink + recent)) / length

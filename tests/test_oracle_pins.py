@@ -1,0 +1,410 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Each ``pin_*`` function checks one oracle function against an independent formulation:
+a literal simulation of the cache policy, a scalar-loop softmax over the simulated cache,
+torch's float64 ``scaled_dot_product_attention``, attention over a sliced window, the
+worked example of the chunked pre-filling figure and the memory numbers the pages print.
+``test_planted_mistakes_are_caught`` plants plausible mistakes in the oracle (on the CPU)
+and requires that some pin fails for each.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import duo_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# --------------------------------------------------------------------------------------------
+# Independent formulations used by the pins
+# --------------------------------------------------------------------------------------------
+
+def sim_decode_cache(n, S, R):
+    """Streaming cache as a Python list, per the decoding procedure: append each token, and
+    when the cache holds more than S+R tokens drop the oldest token that is not a sink."""
+    cache = []
+    for t in range(n):
+        cache.append(t)
+        if len(cache) > S + R:
+            victim = min(x for x in cache if x >= S)
+            cache.remove(victim)
+    return cache
+
+
+def sim_chunked_cache(n, S, R, chunk):
+    """Chunked pre-filling: append a whole chunk, then prune to sinks + last R non-sinks."""
+    cache = []
+    for c0 in range(0, n, chunk):
+        cache.extend(range(c0, min(n, c0 + chunk)))
+        sinks = [x for x in cache if x < S]
+        rest = [x for x in cache if x >= S]
+        cache = sinks + rest[len(rest) - min(R, len(rest)):]
+    return cache
+
+
+def sim_ring_pointer(n, S, R):
+    """Physical slots filled with a write pointer: sinks fill 0..S-1, then the pointer runs
+    over S..S+R-1 and wraps back to S."""
+    slots = [-1] * (S + R)
+    ptr = 0
+    for t in range(n):
+        if t < S:
+            slots[t] = t
+            ptr = S
+            continue
+        slots[ptr] = t
+        ptr = ptr + 1 if ptr + 1 < S + R else S
+    return slots
+
+
+def scalar_head_attention(q, keys, vals, scale):
+    """Softmax over the given keys with Python floats: returns (out list, lse)."""
+    z = [scale * math.fsum(qi * ki for qi, ki in zip(q, k)) for k in keys]
+    m = max(z)
+    w = [math.exp(x - m) for x in z]
+    den = math.fsum(w)
+    d = len(vals[0])
+    out = [math.fsum(w[i] * vals[i][c] for i in range(len(keys))) / den for c in range(d)]
+    return out, m + math.log(den)
+
+
+def rand(rng, *shape):
+    return rng.standard_normal(shape)
+
+
+# --------------------------------------------------------------------------------------------
+# Pins
+# --------------------------------------------------------------------------------------------
+
+def pin_cache_policy():
+    for S in range(0, 5):
+        for R in range(1, 7):
+            for n in range(0, 25):
+                want = sorted(sim_decode_cache(n, S, R))
+                assert sorted(O.streaming_valid_tokens(n, S, R).tolist()) == want, (S, R, n)
+                table = O.slot_table(n, S, R)
+                assert sorted(int(x) for x in table if x >= 0) == want, (S, R, n)
+                assert list(table) == sim_ring_pointer(n, S, R), (S, R, n)
+                for chunk in range(1, n + 1):
+                    if n % chunk == 0:
+                        assert sorted(sim_chunked_cache(n, S, R, chunk)) == want, (S, R, n, chunk)
+
+
+def pin_streaming_rows():
+    rng = np.random.default_rng(1)
+    S, R, n = 3, 5, 17
+    x = rand(rng, n, 4)
+    rows, table = O.streaming_cache_rows(x, n, S, R)
+    slots = sim_ring_pointer(n, S, R)
+    for s, t in enumerate(slots):
+        if t < 0:
+            assert np.all(np.isnan(rows[s]))
+        else:
+            assert np.array_equal(rows[s], x[t])
+
+
+def pin_decode_scalar_bruteforce():
+    """Decode output from the list-simulated cache with a scalar-loop softmax."""
+    rng = np.random.default_rng(2)
+    for (S, R, Hkv, G, d) in [(2, 3, 2, 2, 4), (0, 2, 1, 3, 3), (1, 1, 2, 1, 5), (4, 6, 1, 2, 2)]:
+        retrieval = np.array([1, 0][:Hkv] if Hkv > 1 else [0])
+        n = 13
+        k = rand(rng, n, Hkv, d)
+        v = rand(rng, n, Hkv, d)
+        q = rand(rng, Hkv * G, d)
+        out, lse = O.decode_step(q, k, v, retrieval, S, R)
+        for h in range(Hkv * G):
+            j = h // G
+            pos = list(range(n)) if retrieval[j] else sim_decode_cache(n, S, R)
+            o_ref, l_ref = scalar_head_attention(q[h].tolist(), [k[t, j].tolist() for t in pos],
+                                                 [v[t, j].tolist() for t in pos], 1 / math.sqrt(d))
+            assert np.allclose(out[h], o_ref, rtol=0, atol=1e-12), (S, R, h)
+            assert abs(lse[h] - l_ref) < 1e-12, (S, R, h)
+
+
+def _sdpa_causal(q, k, v):
+    """torch float64 causal attention, ``[T, H, d]`` inputs, all queries 0..T-1."""
+    tq = torch.from_numpy(q).permute(1, 0, 2)[None]
+    tk = torch.from_numpy(k).permute(1, 0, 2)[None]
+    tv = torch.from_numpy(v).permute(1, 0, 2)[None]
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+def pin_all_retrieval_is_causal_attention():
+    rng = np.random.default_rng(3)
+    for (Hkv, G, d, T, start) in [(2, 4, 8, 40, 17), (4, 1, 16, 33, 0), (1, 8, 4, 20, 19)]:
+        q = rand(rng, T, Hkv * G, d)
+        k = rand(rng, T, Hkv, d)
+        v = rand(rng, T, Hkv, d)
+        ref = _sdpa_causal(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1))
+        out, _ = O.prefill_chunk(q[start:], k, v, start, np.ones(Hkv), 2, 3)
+        assert np.allclose(out, ref[start:], rtol=0, atol=1e-12)
+        o1, _ = O.decode_step(q[T - 1], k, v, np.ones(Hkv), 2, 3)
+        assert np.allclose(o1, ref[T - 1], rtol=0, atol=1e-12)
+
+
+def pin_short_streaming_is_full():
+    """A streaming head whose context holds at most S+R tokens sees everything."""
+    rng = np.random.default_rng(4)
+    S, R, d = 3, 6, 8
+    for n in range(1, S + R + 1):
+        k = rand(rng, n, 1, d)
+        v = rand(rng, n, 1, d)
+        q = rand(rng, 2, d)
+        a, la = O.decode_step(q, k, v, [0], S, R)
+        b, lb = O.decode_step(q, k, v, [1], S, R)
+        assert np.array_equal(a, b) and np.array_equal(la, lb)
+    n = S + R + 4  # beyond S+R the two must differ
+    k, v, q = rand(rng, n, 1, d), rand(rng, n, 1, d), rand(rng, 2, d)
+    a, _ = O.decode_step(q, k, v, [0], S, R)
+    b, _ = O.decode_step(q, k, v, [1], S, R)
+    assert not np.allclose(a, b)
+
+
+def pin_no_sink_is_sliding_window():
+    """S = 0: attention over the slice [p-R+1, p]; R >= n: full causal attention."""
+    rng = np.random.default_rng(5)
+    T, Hkv, G, d = 30, 2, 2, 8
+    q = rand(rng, T, Hkv * G, d)
+    k = rand(rng, T, Hkv, d)
+    v = rand(rng, T, Hkv, d)
+    for R in (1, 4, 9):
+        out, _ = O.prefill_chunk(q, k, v, 0, np.zeros(Hkv), 0, R)
+        for p in range(T):
+            lo = max(0, p - R + 1)
+            kk = np.repeat(k[lo:p + 1], G, axis=1)
+            vv = np.repeat(v[lo:p + 1], G, axis=1)
+            z = np.einsum("hd,thd->ht", q[p], kk) / math.sqrt(d)
+            w = np.exp(z - z.max(axis=1, keepdims=True))
+            ref = np.einsum("ht,thd->hd", w / w.sum(axis=1, keepdims=True), vv)
+            assert np.allclose(out[p], ref, rtol=0, atol=1e-12), (R, p)
+    full = _sdpa_causal(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1))
+    out, _ = O.prefill_chunk(q, k, v, 0, np.zeros(Hkv), 0, T)
+    assert np.allclose(out, full, rtol=0, atol=1e-12)
+
+
+def _read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            kind, *kv = line.split()
+            d = dict(x.split("=", 1) for x in kv)
+            rows.append((kind, d))
+    return rows
+
+
+def pin_fig5_worked_example():
+    rows = _read_golden("chunked_prefill_fig5.txt")
+    head = rows[0][1] if rows[0][0].startswith("sink") else None
+    S, R, chunk = 1, 2, 4
+    assert rows[0][0] == "sink=1"
+    assert head["recent"] == "2" and head["chunk"] == "4"
+    for kind, d in rows[1:]:
+        n = int(kind.split("=")[1])
+        want = sorted(int(x) for x in d["cache"].split(","))
+        assert sorted(O.streaming_valid_tokens(n, S, R).tolist()) == want
+        assert sorted(sim_chunked_cache(n, S, R, chunk)) == want
+        table = O.slot_table(n, S, R)
+        assert sorted(int(x) for x in table if x >= 0) == want
+    # the ring convention places them as [0, 3, 2] and [0, 7, 6]
+    assert list(O.slot_table(4, S, R)) == [0, 3, 2]
+    assert list(O.slot_table(8, S, R)) == [0, 7, 6]
+
+
+def pin_memory_numbers():
+    rows = _read_golden("kv_memory.txt")
+    for kind, d in rows:
+        if kind == "full_fp16_bytes":
+            b = 2 * O.full_kv_elements(int(d["layers"]), int(d["kv_heads"]), int(d["tokens"]),
+                                       int(d["d"]))
+            assert b == 137_438_953_472
+            assert 137e9 <= b < 138e9
+        elif kind == "budget_ratio":
+            got = O.budget_ratio(float(d["r"]), int(d["length"]), int(d["sink"]), int(d["recent"]))
+            assert abs(got - float(d["value"])) < 1e-12
+        elif kind == "budget_ratio_page_discrepancy":
+            r, L = float(d["r"]), int(d["length"])
+            SR = int(d["sink"]) + int(d["recent"])
+            got = O.budget_ratio(r, L, int(d["sink"]), int(d["recent"]))
+            assert abs(got - float(d["formula"])) < 1e-12
+            # the printed value equals the streaming term weighted by r instead of 1 - r
+            assert abs((r * L + r * SR) / L - float(d["page"])) < 1e-12
+    # limits: 25 % retrieval (MHA) -> 4x less KV, 50 % (GQA) -> 2x, as L grows
+    assert abs(1 / O.budget_ratio(0.25, 10**9, 64, 256) - 4) < 1e-5
+    assert abs(1 / O.budget_ratio(0.5, 10**9, 64, 256) - 2) < 1e-5
+
+
+def pin_memory_formula_by_count():
+    """Per-layer element count equals the tokens stored by the simulated caches times d."""
+    for (Hr, Hs, S, R, d) in [(1, 3, 2, 5, 4), (8, 24, 16, 512, 128), (0, 2, 0, 3, 2)]:
+        for L in (0, 1, 3, S + R - 1, S + R, S + R + 1, 4 * (S + R) + 3):
+            counted = (Hr * L + Hs * len(sim_decode_cache(L, S, R))) * d
+            assert O.duo_kv_elements_layer(Hr, Hs, L, S, R, d) == counted, (L, S, R)
+            full = O.full_kv_elements(1, Hr + Hs, L, d)
+            assert full == 2 * (Hr + Hs) * L * d
+
+
+def pin_chunk_invariance_and_decode_equivalence():
+    rng = np.random.default_rng(6)
+    T, Hkv, G, d, S, R = 23, 3, 2, 6, 2, 4
+    retrieval = np.array([0, 1, 0])
+    q = rand(rng, T, Hkv * G, d)
+    k = rand(rng, T, Hkv, d)
+    v = rand(rng, T, Hkv, d)
+    one, lone = O.prefill_chunk(q, k, v, 0, retrieval, S, R)
+    for chunk in (1, 3, 7, T):
+        parts = [O.prefill_chunk(q[c:c + chunk], k, v, c, retrieval, S, R)
+                 for c in range(0, T, chunk)]
+        got = np.concatenate([p[0] for p in parts])
+        assert np.allclose(got, one, rtol=0, atol=1e-13)
+    for p in range(T):
+        o, l = O.decode_step(q[p], k[:p + 1], v[:p + 1], retrieval, S, R)
+        assert np.allclose(o, one[p], rtol=0, atol=1e-13)
+        assert np.allclose(l, lone[p], rtol=0, atol=1e-13)
+
+
+def pin_head_permutation():
+    """Permuting KV heads (with their flags and query groups) permutes the outputs."""
+    rng = np.random.default_rng(7)
+    T, Hkv, G, d, S, R = 19, 4, 2, 5, 1, 3
+    retrieval = np.array([1, 0, 0, 1])
+    q = rand(rng, T, Hkv * G, d)
+    k = rand(rng, T, Hkv, d)
+    v = rand(rng, T, Hkv, d)
+    perm = np.array([2, 0, 3, 1])
+    qperm = np.concatenate([np.arange(j * G, (j + 1) * G) for j in perm])
+    a, _ = O.prefill_chunk(q, k, v, 0, retrieval, S, R)
+    b, _ = O.prefill_chunk(q[:, qperm], k[:, perm], v[:, perm], 0, retrieval[perm], S, R)
+    assert np.allclose(a[:, qperm], b, rtol=0, atol=1e-13)
+
+
+def pin_gqa_equals_repeated_mha():
+    rng = np.random.default_rng(8)
+    T, Hkv, G, d, S, R = 17, 2, 4, 8, 2, 5
+    retrieval = np.array([0, 1])
+    q = rand(rng, T, Hkv * G, d)
+    k = rand(rng, T, Hkv, d)
+    v = rand(rng, T, Hkv, d)
+    a, la = O.prefill_chunk(q, k, v, 0, retrieval, S, R)
+    b, lb = O.prefill_chunk(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1), 0,
+                            np.repeat(retrieval, G), S, R)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def pin_lambda_mask_literal():
+    """S=2, R=3 over 7 positions, written out by hand from the mask's description."""
+    want = np.array([
+        [1, 0, 0, 0, 0, 0, 0],
+        [1, 1, 0, 0, 0, 0, 0],
+        [1, 1, 1, 0, 0, 0, 0],
+        [1, 1, 1, 1, 0, 0, 0],
+        [1, 1, 1, 1, 1, 0, 0],
+        [1, 1, 0, 1, 1, 1, 0],
+        [1, 1, 0, 0, 1, 1, 1],
+    ], dtype=bool)
+    got = O.visible_mask(np.arange(7), np.arange(7), False, 2, 3)
+    assert np.array_equal(got, want)
+    assert np.array_equal(O.visible_mask(np.arange(7), np.arange(7), True, 2, 3),
+                          np.tril(np.ones((7, 7), dtype=bool)))
+
+
+PINS = [pin_cache_policy, pin_streaming_rows, pin_decode_scalar_bruteforce,
+        pin_all_retrieval_is_causal_attention, pin_short_streaming_is_full,
+        pin_no_sink_is_sliding_window, pin_fig5_worked_example, pin_memory_numbers,
+        pin_memory_formula_by_count, pin_chunk_invariance_and_decode_equivalence,
+        pin_head_permutation, pin_gqa_equals_repeated_mha, pin_lambda_mask_literal]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin(pin):
+    pin()
+
+
+# --------------------------------------------------------------------------------------------
+# Planted mistakes: each must make at least one pin fail
+# --------------------------------------------------------------------------------------------
+
+def _window_too_wide(q_pos, k_pos, retrieval, sink, recent):
+    p = np.asarray(q_pos)[:, None]
+    t = np.asarray(k_pos)[None, :]
+    c = t <= p
+    return c if retrieval else c & ((t < sink) | (t >= p - recent))
+
+
+def _window_excludes_self_slot(q_pos, k_pos, retrieval, sink, recent):
+    p = np.asarray(q_pos)[:, None]
+    t = np.asarray(k_pos)[None, :]
+    c = t <= p
+    return c if retrieval else c & ((t < sink) | (t >= p - recent + 2))
+
+
+def _sink_off_by_one(q_pos, k_pos, retrieval, sink, recent):
+    p = np.asarray(q_pos)[:, None]
+    t = np.asarray(k_pos)[None, :]
+    c = t <= p
+    return c if retrieval else c & ((t <= sink) | (t >= p - recent + 1))
+
+
+def _streaming_not_causal(q_pos, k_pos, retrieval, sink, recent):
+    p = np.asarray(q_pos)[:, None]
+    t = np.asarray(k_pos)[None, :]
+    return (t <= p) if retrieval else ((t < sink) | (t >= p - recent + 1))
+
+
+def _lse_log2(q, k, v, mask, scale):
+    out, lse = _ORIG_MSA(q, k, v, mask, scale)
+    return out, lse / math.log(2)
+
+
+def _softmax_unmasked_den(q, k, v, mask, scale):
+    z = scale * (np.asarray(q) @ np.asarray(k).T)
+    zm = np.where(mask, z, -np.inf)
+    m = zm.max(axis=1, keepdims=True)
+    w = np.exp(zm - m)
+    den = np.exp(z - m).sum(axis=1, keepdims=True)  # denominator over all keys
+    return (w @ np.asarray(v)) / den, (m + np.log(den))[:, 0]
+
+
+_ORIG_MSA = O.masked_softmax_attention
+
+MUTANTS = {
+    "window_too_wide": ("visible_mask", _window_too_wide),
+    "window_too_narrow": ("visible_mask", _window_excludes_self_slot),
+    "sink_off_by_one": ("visible_mask", _sink_off_by_one),
+    "streaming_not_causal": ("visible_mask", _streaming_not_causal),
+    "interleaved_groups": ("kv_head_of", lambda h, G: h % G),
+    "no_scale": ("default_scale", lambda d: 1.0),
+    "lse_base2": ("masked_softmax_attention", _lse_log2),
+    "den_over_unmasked": ("masked_softmax_attention", _softmax_unmasked_den),
+    "ring_from_zero": ("slot_of", lambda t, S, R: t if t < S else (t - S) % R),
+    "ring_wrong_modulus": ("slot_of", lambda t, S, R: t if t < S else S + (t - S) % max(1, R - 1)),
+    "recent_one_short": ("streaming_valid_tokens",
+                         lambda n, S, R: np.concatenate([np.arange(min(S, n)),
+                                                         np.arange(max(S, n - R + 1), n)])),
+    "memory_no_min": ("duo_kv_elements_layer",
+                      lambda Hr, Hs, L, S, R, d: (Hr * L + Hs * (S + R)) * d),
+    "budget_weights_r": ("budget_ratio", lambda r, L, S, R: (r * L + r * min(L, S + R)) / L),
+    "full_kv_no_factor2": ("full_kv_elements", lambda D, H, L, d: D * H * L * d),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistakes_are_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(O, attr, fn)
+    failed = []
+    np.seterr(all="ignore")
+    for pin in PINS:
+        try:
+            pin()
+        except (AssertionError, IndexError, ValueError):
+            failed.append(pin.__name__)
+    assert failed, f"planted mistake {name} passed every pin"
