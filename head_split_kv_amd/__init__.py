@@ -1,0 +1,226 @@
+"""Python binding of libduo: attention over a head-partitioned KV cache on MI355X.
+
+The functions below carry the names of the C ABI in ``include/duo.h`` and only marshal
+arguments: they check tensor shapes, dtypes, devices and contiguity (the C side sees raw
+pointers and cannot), pass data pointers and the current HIP stream, and raise
+``DuoError`` on a non-zero status. PyTorch supplies device memory and streams; every step
+of the computation runs in the library's HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import _native
+from ._native import (DUO_BF16, DUO_ERR_CAPACITY, DUO_ERR_HIP, DUO_ERR_INVALID,  # noqa: F401
+                      DUO_ERR_UNSUPPORTED, DUO_F32, DUO_OK, DuoConfig, DuoError, DuoLayout,
+                      check, lib, status_string)
+
+_DTYPES = {torch.float32: DUO_F32, torch.bfloat16: DUO_BF16}
+
+
+def _dt(dtype: torch.dtype) -> int:
+    if dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dtype}; use torch.float32 or torch.bfloat16")
+    return _DTYPES[dtype]
+
+
+def make_config(*, num_layers: int, batch: int, num_q_heads: int, num_kv_heads: int,
+                head_dim: int, sink: int, recent: int, capacity: int,
+                retrieval_mask, dtype: torch.dtype = torch.bfloat16,
+                out_dtype: Optional[torch.dtype] = None, softmax_scale: float = 0.0,
+                max_splits: int = 0):
+    """Build a ``DuoConfig``; returns ``(cfg, mask_array)`` (keep the array alive)."""
+    mask = np.ascontiguousarray(np.asarray(retrieval_mask, dtype=np.uint8)
+                                .reshape(num_layers, num_kv_heads))
+    cfg = DuoConfig(num_layers, batch, num_q_heads, num_kv_heads, head_dim, sink, recent,
+                    capacity, _dt(dtype), _dt(out_dtype or dtype), float(softmax_scale),
+                    max_splits, mask.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)))
+    return cfg, mask
+
+
+def duo_layout_query(cfg: DuoConfig) -> DuoLayout:
+    lay = DuoLayout()
+    check(lib().duo_layout_query(ctypes.byref(cfg), ctypes.byref(lay)), "duo_layout_query")
+    return lay
+
+
+def duo_kv_bytes(cfg: DuoConfig, layer: int, seq_lens: Sequence[int]):
+    """(full-attention bytes, split-layout bytes) one layer holds for these lengths."""
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    full = ctypes.c_uint64()
+    duo = ctypes.c_uint64()
+    check(lib().duo_kv_bytes(ctypes.byref(cfg), layer,
+                             lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                             ctypes.byref(full), ctypes.byref(duo)), "duo_kv_bytes")
+    return full.value, duo.value
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+class DuoCache:
+    """A head-partitioned KV cache in one device arena (``torch.uint8`` tensor)."""
+
+    def __init__(self, *, num_layers: int, batch: int, num_q_heads: int, num_kv_heads: int,
+                 head_dim: int, sink: int, recent: int, capacity: int, retrieval_mask,
+                 dtype: torch.dtype = torch.bfloat16, out_dtype: Optional[torch.dtype] = None,
+                 softmax_scale: float = 0.0, max_splits: int = 0, device="cuda",
+                 stream=None):
+        self.cfg, self._mask = make_config(
+            num_layers=num_layers, batch=batch, num_q_heads=num_q_heads,
+            num_kv_heads=num_kv_heads, head_dim=head_dim, sink=sink, recent=recent,
+            capacity=capacity, retrieval_mask=retrieval_mask, dtype=dtype, out_dtype=out_dtype,
+            softmax_scale=softmax_scale, max_splits=max_splits)
+        self.layout = duo_layout_query(self.cfg)
+        self.dtype = dtype
+        self.out_dtype = out_dtype or dtype
+        self.device = torch.device(device)
+        self.num_layers, self.batch = num_layers, batch
+        self.hq, self.hkv, self.d = num_q_heads, num_kv_heads, head_dim
+        self.sink, self.recent, self.capacity = sink, recent, capacity
+        nbytes = int(self.layout.arena_bytes)
+        self._arena_raw = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
+        off = (-self._arena_raw.data_ptr()) % 256
+        self.arena = self._arena_raw[off:off + nbytes]
+        h = ctypes.c_void_p()
+        check(lib().duo_cache_create(ctypes.byref(self.cfg), ctypes.c_void_p(self.arena.data_ptr()),
+                                     nbytes, ctypes.byref(h)), "duo_cache_create")
+        self.handle = h
+        duo_cache_reset(self, stream)
+
+    @property
+    def retrieval_mask(self) -> np.ndarray:
+        return self._mask.copy()
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            lib().duo_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # convenience wrappers
+    def kv_append(self, layer, k, v, seq=-1, stream=None):
+        return duo_kv_append(self, layer, seq, k, v, stream=stream)
+
+    def attn_decode(self, layer, q, out=None, lse=None, stream=None):
+        return duo_attn_decode(self, layer, q, out, lse, stream=stream)
+
+    def attn_prefill(self, layer, q, k, v, seq=-1, out=None, lse=None, stream=None):
+        return duo_attn_prefill(self, layer, seq, q, k, v, out, lse, stream=stream)
+
+    def slot_positions(self, layer, stream=None):
+        return duo_slot_positions(self, layer, stream)
+
+    def lengths(self):
+        return duo_cache_lengths(self)
+
+
+def _check_tensor(t: torch.Tensor, shape, dtype, device, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device and not (t.device.type == device.type == "cuda"
+                                   and (device.index is None or t.device.index == device.index)):
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.data_ptr() % 16:
+        raise ValueError(f"{name} must be 16-byte aligned")
+
+
+def duo_cache_reset(cache: DuoCache, stream=None) -> None:
+    check(lib().duo_cache_reset(cache.handle, _stream(stream)), "duo_cache_reset")
+
+
+def duo_kv_append(cache: DuoCache, layer: int, seq: int, k: torch.Tensor, v: torch.Tensor,
+                  n_new: Optional[int] = None, stream=None) -> None:
+    """Append tokens; k, v ``[B, m, Hkv, d]`` (seq = -1) or ``[m, Hkv, d]`` (seq >= 0)."""
+    m = k.shape[1] if seq < 0 else k.shape[0]
+    if n_new is not None and n_new != m:
+        raise ValueError("n_new does not match k")
+    shape = ((cache.batch, m, cache.hkv, cache.d) if seq < 0 else (m, cache.hkv, cache.d))
+    _check_tensor(k, shape, cache.dtype, cache.device, "k")
+    _check_tensor(v, shape, cache.dtype, cache.device, "v")
+    check(lib().duo_kv_append(cache.handle, layer, seq, ctypes.c_void_p(k.data_ptr()),
+                              ctypes.c_void_p(v.data_ptr()), m, _stream(stream)),
+          "duo_kv_append")
+
+
+def duo_attn_decode(cache: DuoCache, layer: int, q: torch.Tensor, out=None, lse=None,
+                    stream=None):
+    """One decode step; q ``[B, Hq, d]`` -> out ``[B, Hq, d]`` (and lse ``[B, Hq]``)."""
+    _check_tensor(q, (cache.batch, cache.hq, cache.d), cache.dtype, cache.device, "q")
+    if out is None:
+        out = torch.empty((cache.batch, cache.hq, cache.d), dtype=cache.out_dtype,
+                          device=q.device)
+    _check_tensor(out, (cache.batch, cache.hq, cache.d), cache.out_dtype, cache.device, "out")
+    lse_ptr = None
+    if lse is not None:
+        _check_tensor(lse, (cache.batch, cache.hq), torch.float32, cache.device, "lse")
+        lse_ptr = lse.data_ptr()
+    check(lib().duo_attn_decode(cache.handle, layer, ctypes.c_void_p(q.data_ptr()),
+                                ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(lse_ptr),
+                                _stream(stream)), "duo_attn_decode")
+    return out
+
+
+def duo_attn_prefill(cache: DuoCache, layer: int, seq: int, q: torch.Tensor, k: torch.Tensor,
+                     v: torch.Tensor, out=None, lse=None, stream=None):
+    """Attention of one chunk; q ``[B, m, Hq, d]`` / k, v ``[B, m, Hkv, d]`` (seq = -1) or
+    without the batch dimension (seq >= 0). Does not modify the cache."""
+    m = q.shape[1] if seq < 0 else q.shape[0]
+    lead = (cache.batch, m) if seq < 0 else (m,)
+    _check_tensor(q, lead + (cache.hq, cache.d), cache.dtype, cache.device, "q")
+    _check_tensor(k, lead + (cache.hkv, cache.d), cache.dtype, cache.device, "k")
+    _check_tensor(v, lead + (cache.hkv, cache.d), cache.dtype, cache.device, "v")
+    if out is None:
+        out = torch.empty(lead + (cache.hq, cache.d), dtype=cache.out_dtype, device=q.device)
+    _check_tensor(out, lead + (cache.hq, cache.d), cache.out_dtype, cache.device, "out")
+    lse_ptr = None
+    if lse is not None:
+        _check_tensor(lse, lead + (cache.hq,), torch.float32, cache.device, "lse")
+        lse_ptr = lse.data_ptr()
+    check(lib().duo_attn_prefill(cache.handle, layer, seq, ctypes.c_void_p(q.data_ptr()),
+                                 ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+                                 m, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(lse_ptr),
+                                 _stream(stream)), "duo_attn_prefill")
+    return out
+
+
+def duo_slot_positions(cache: DuoCache, layer: int, stream=None) -> np.ndarray:
+    """Slot table of one layer, int32 ``[B, S+R]`` (synchronizes the stream)."""
+    out = np.empty((cache.batch, cache.sink + cache.recent), dtype=np.int32)
+    check(lib().duo_slot_positions(cache.handle, layer,
+                                   out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                   _stream(stream)), "duo_slot_positions")
+    return out
+
+
+def duo_cache_lengths(cache: DuoCache) -> np.ndarray:
+    out = np.empty((cache.num_layers, cache.batch), dtype=np.int32)
+    check(lib().duo_cache_lengths(cache.handle, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))),
+          "duo_cache_lengths")
+    return out
+
+
+def duo_set_decode_splits(cache: DuoCache, splits: int) -> None:
+    check(lib().duo_set_decode_splits(cache.handle, splits), "duo_set_decode_splits")
+
+
+def duo_status_string(status: int) -> str:
+    return status_string(status)

@@ -1,0 +1,113 @@
+// Cache maintenance kernels: reset and append (sink fill, then ring overwrite).
+#include <hip/hip_runtime.h>
+
+#include "duo_internal.h"
+
+namespace duo {
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ void __launch_bounds__(kThreads) reset_kernel(ResetArgs a) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < a.n_slot; i += stride)
+    a.slot_pos[i] = -1;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < a.n_len; i += stride)
+    a.seq_len[i] = 0;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < a.n_cnt; i += stride)
+    a.counters[i] = 0u;
+}
+
+// Streaming slot of token t: sinks take slots 0..S-1, later tokens a ring of R slots after
+// them (explainer, "Decoding Procedure", step 4: evict the oldest non-sink token).
+__device__ __forceinline__ int32_t slot_of(int32_t t, int32_t S, int32_t R) {
+  return t < S ? t : S + (t - S) % R;
+}
+
+// A new token t of an append that ends at n_end is still held by a streaming cache iff it
+// is a sink or one of the last R tokens. Only those are written, so every slot is written
+// at most once per launch.
+__device__ __forceinline__ bool survives(int32_t t, int32_t n_end, int32_t S, int32_t R) {
+  return t < S || t >= n_end - R;
+}
+
+// One thread moves one 16-byte chunk of one K or V row. Work index (outer to inner):
+// tensor (K, V), sequence, token, KV head, chunk; consecutive threads read consecutive
+// bytes of the input. The extra nb*m work items at the end write the slot table.
+__global__ void __launch_bounds__(kThreads) append_kernel(AppendArgs a) {
+  const int32_t nch = a.row_bytes / 16;
+  const int64_t per_tensor = (int64_t)a.nb * a.m * a.Hkv * nch;
+  const int64_t n_slot_items = (int64_t)a.nb * a.m;
+  const int64_t total = 2 * per_tensor + n_slot_items;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int32_t SR = a.S + a.R;
+
+  if (blockIdx.x == 0)
+    for (int32_t i = threadIdx.x; i < a.nb; i += blockDim.x)
+      a.seq_len[a.b0 + i] = a.n_old[i] + a.m;
+
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < total; u += stride) {
+    if (u >= 2 * per_tensor) {
+      const int64_t w = u - 2 * per_tensor;
+      const int32_t bi = (int32_t)(w / a.m), i = (int32_t)(w % a.m);
+      const int32_t n0 = a.n_old[bi], t = n0 + i;
+      if (survives(t, n0 + a.m, a.S, a.R))
+        a.slot_pos[(int64_t)(a.b0 + bi) * SR + slot_of(t, a.S, a.R)] = t;
+      continue;
+    }
+    const int tensor = u >= per_tensor;
+    int64_t w = tensor ? u - per_tensor : u;
+    const int32_t c = (int32_t)(w % nch); w /= nch;
+    const int32_t j = (int32_t)(w % a.Hkv); w /= a.Hkv;
+    const int32_t i = (int32_t)(w % a.m); w /= a.m;
+    const int32_t bi = (int32_t)w;
+    const int32_t b = a.b0 + bi;
+    const int32_t n0 = a.n_old[bi], t = n0 + i;
+    const char* src = (const char*)(tensor ? a.v : a.k) +
+                      (((int64_t)bi * a.m + i) * a.Hkv + j) * a.row_bytes + c * 16;
+    const int32_t ci = a.cls_idx[j];
+    char* dst;
+    if (ci >= 0) {
+      dst = (char*)(tensor ? a.full_v : a.full_k) +
+            (((int64_t)b * a.Hr + ci) * a.cap + t) * a.row_bytes + c * 16;
+    } else {
+      if (!survives(t, n0 + a.m, a.S, a.R)) continue;
+      const int32_t s = -ci - 1;
+      dst = (char*)(tensor ? a.str_v : a.str_k) +
+            (((int64_t)b * a.Hs + s) * SR + slot_of(t, a.S, a.R)) * a.row_bytes + c * 16;
+    }
+    *(uint4*)dst = *(const uint4*)src;
+  }
+}
+
+int grid_for(int64_t work) {
+  int64_t g = (work + kThreads - 1) / kThreads;
+  if (g < 1) g = 1;
+  if (g > 8192) g = 8192;
+  return (int)g;
+}
+
+}  // namespace
+
+int launch_reset(const ResetArgs& a, void* stream) {
+  int64_t work = a.n_slot > a.n_len ? a.n_slot : a.n_len;
+  if (a.n_cnt > work) work = a.n_cnt;
+  hipLaunchKernelGGL(reset_kernel, dim3(grid_for(work)), dim3(kThreads), 0,
+                     (hipStream_t)stream, a);
+  return (int)hipGetLastError();
+}
+
+int launch_append(const AppendArgs& a, int /*dtype*/, void* stream) {
+  const int64_t work = 2 * (int64_t)a.nb * a.m * a.Hkv * (a.row_bytes / 16) + (int64_t)a.nb * a.m;
+  hipLaunchKernelGGL(append_kernel, dim3(grid_for(work)), dim3(kThreads), 0,
+                     (hipStream_t)stream, a);
+  return (int)hipGetLastError();
+}
+
+int copy_d2h_sync(void* dst, const void* src, uint64_t bytes, void* stream) {
+  hipError_t e = hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, (hipStream_t)stream);
+  if (e != hipSuccess) return (int)e;
+  return (int)hipStreamSynchronize((hipStream_t)stream);
+}
+
+}  // namespace duo

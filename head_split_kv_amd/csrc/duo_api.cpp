@@ -1,0 +1,231 @@
+// The C ABI entry points that enqueue device work. Every argument and capacity check runs
+// here on the host before anything is launched; on an error nothing is launched and neither
+// the host mirror nor the device state changes.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+
+#include "duo_internal.h"
+
+namespace duo {
+int copy_d2h_sync(void* dst, const void* src, uint64_t bytes, void* stream);
+}
+
+using namespace duo;
+
+namespace {
+
+// Rows are moved in 16-byte chunks, so every tensor must start on a 16-byte boundary.
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+bool layer_ok(const duo_cache* c, int32_t layer) {
+  return c && layer >= 0 && layer < c->cfg.num_layers;
+}
+
+int32_t& len_of(duo_cache* c, int32_t layer, int32_t b) {
+  return c->lens[(size_t)layer * c->cfg.batch + b];
+}
+
+struct LayerPtrs {
+  char* full_k;
+  char* full_v;
+  char* str_k;
+  char* str_v;
+  int32_t* slot_pos;
+  int32_t* seq_len;
+};
+
+LayerPtrs layer_ptrs(duo_cache* c, int32_t layer) {
+  const LayerInfo& li = c->layers[layer];
+  const uint64_t SR = (uint64_t)c->cfg.sink + c->cfg.recent;
+  LayerPtrs p;
+  p.full_k = c->arena + c->lay.full_k_off + li.full_off;
+  p.full_v = c->arena + c->lay.full_v_off + li.full_off;
+  p.str_k = c->arena + c->lay.str_k_off + li.str_off;
+  p.str_v = c->arena + c->lay.str_v_off + li.str_off;
+  p.slot_pos = (int32_t*)(c->arena + c->lay.slot_pos_off) + (uint64_t)layer * c->cfg.batch * SR;
+  p.seq_len = (int32_t*)(c->arena + c->lay.seq_len_off) + (uint64_t)layer * c->cfg.batch;
+  return p;
+}
+
+struct Workspace {
+  float* part_o;
+  float* part_ml;
+  uint32_t* counters;
+};
+
+Workspace workspace(duo_cache* c) {
+  const uint64_t B = c->cfg.batch, Hq = c->cfg.num_q_heads, D = c->cfg.head_dim;
+  const uint64_t S = c->cfg.max_splits, Hkv = c->cfg.num_kv_heads;
+  auto al = [](uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; };
+  char* base = c->arena + c->lay.workspace_off;
+  Workspace w;
+  w.part_o = (float*)base;
+  w.part_ml = (float*)(base + al(B * Hq * S * D * 4));
+  w.counters = (uint32_t*)(base + al(B * Hq * S * D * 4) + al(B * Hq * S * 2 * 4));
+  (void)Hkv;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+duo_status duo_cache_reset(duo_cache* c, void* stream) {
+  if (!c) return DUO_ERR_INVALID;
+  const uint64_t L = c->cfg.num_layers, B = c->cfg.batch;
+  const uint64_t SR = (uint64_t)c->cfg.sink + c->cfg.recent;
+  ResetArgs a;
+  a.slot_pos = (int32_t*)(c->arena + c->lay.slot_pos_off);
+  a.n_slot = (int64_t)(L * B * SR);
+  a.seq_len = (int32_t*)(c->arena + c->lay.seq_len_off);
+  a.n_len = (int64_t)(L * B);
+  a.counters = workspace(c).counters;
+  a.n_cnt = (int64_t)(B * c->cfg.num_kv_heads);
+  if (launch_reset(a, stream) != 0) return DUO_ERR_HIP;
+  std::fill(c->lens.begin(), c->lens.end(), 0);
+  return DUO_OK;
+}
+
+duo_status duo_kv_append(duo_cache* c, int32_t layer, int32_t seq, const void* k,
+                         const void* v, int32_t n_new, void* stream) {
+  if (!layer_ok(c, layer) || seq < -1 || seq >= c->cfg.batch || n_new < 0)
+    return DUO_ERR_INVALID;
+  if (n_new == 0) return DUO_OK;
+  if (!k || !v || !aligned16(k) || !aligned16(v)) return DUO_ERR_INVALID;
+  const int32_t b0 = seq < 0 ? 0 : seq, nb = seq < 0 ? c->cfg.batch : 1;
+  for (int32_t b = b0; b < b0 + nb; ++b)
+    if ((int64_t)len_of(c, layer, b) + n_new > c->cfg.capacity) return DUO_ERR_CAPACITY;
+  const LayerInfo& li = c->layers[layer];
+  const LayerPtrs p = layer_ptrs(c, layer);
+  AppendArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.k = k;
+  a.v = v;
+  a.full_k = p.full_k;
+  a.full_v = p.full_v;
+  a.str_k = p.str_k;
+  a.str_v = p.str_v;
+  a.slot_pos = p.slot_pos;
+  a.seq_len = p.seq_len;
+  a.b0 = b0;
+  a.nb = nb;
+  a.m = n_new;
+  a.Hkv = c->cfg.num_kv_heads;
+  a.Hr = li.n_ret;
+  a.Hs = li.n_str;
+  a.cap = c->cfg.capacity;
+  a.S = c->cfg.sink;
+  a.R = c->cfg.recent;
+  a.row_bytes = c->cfg.head_dim * c->esize;
+  std::memcpy(a.cls_idx, li.cls_idx, sizeof(a.cls_idx));
+  for (int32_t i = 0; i < nb; ++i) a.n_old[i] = len_of(c, layer, b0 + i);
+  if (launch_append(a, c->cfg.dtype, stream) != 0) return DUO_ERR_HIP;
+  for (int32_t b = b0; b < b0 + nb; ++b) len_of(c, layer, b) += n_new;
+  return DUO_OK;
+}
+
+duo_status duo_attn_decode(duo_cache* c, int32_t layer, const void* q, void* out, float* lse,
+                           void* stream) {
+  if (!layer_ok(c, layer) || !q || !out || !aligned16(q) || !aligned16(out) || !aligned4(lse))
+    return DUO_ERR_INVALID;
+  int32_t n_max = 0;
+  for (int32_t b = 0; b < c->cfg.batch; ++b) {
+    const int32_t n = len_of(c, layer, b);
+    if (n < 1) return DUO_ERR_INVALID;
+    n_max = std::max(n_max, n);
+  }
+  const LayerInfo& li = c->layers[layer];
+  const LayerPtrs p = layer_ptrs(c, layer);
+  const Workspace w = workspace(c);
+  DecodeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.out = out;
+  a.lse = lse;
+  a.full_k = p.full_k;
+  a.full_v = p.full_v;
+  a.str_k = p.str_k;
+  a.str_v = p.str_v;
+  a.seq_len = p.seq_len;
+  a.part_o = w.part_o;
+  a.part_ml = w.part_ml;
+  a.counters = w.counters;
+  a.B = c->cfg.batch;
+  a.Hq = c->cfg.num_q_heads;
+  a.Hkv = c->cfg.num_kv_heads;
+  a.Hr = li.n_ret;
+  a.Hs = li.n_str;
+  a.cap = c->cfg.capacity;
+  a.S = c->cfg.sink;
+  a.R = c->cfg.recent;
+  a.max_splits = c->cfg.max_splits;
+  a.nsplit = c->force_splits ? c->force_splits
+                             : choose_decode_splits(n_max, a.B, a.Hr, a.max_splits);
+  a.scale_log2 = (float)((double)c->scale * 1.4426950408889634);
+  a.out_f32 = c->cfg.out_dtype == DUO_F32;
+  std::memcpy(a.ret_kv, li.ret_kv, sizeof(a.ret_kv));
+  std::memcpy(a.str_kv, li.str_kv, sizeof(a.str_kv));
+  const int group = c->cfg.num_q_heads / c->cfg.num_kv_heads;
+  if (launch_decode(a, c->cfg.dtype, c->cfg.head_dim, group, stream) != 0) return DUO_ERR_HIP;
+  return DUO_OK;
+}
+
+duo_status duo_attn_prefill(duo_cache* c, int32_t layer, int32_t seq, const void* q,
+                            const void* k, const void* v, int32_t n_chunk, void* out,
+                            float* lse, void* stream) {
+  if (!layer_ok(c, layer) || seq < -1 || seq >= c->cfg.batch || n_chunk < 0)
+    return DUO_ERR_INVALID;
+  if (n_chunk == 0) return DUO_OK;
+  if (!q || !k || !v || !out || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
+      !aligned16(out) || !aligned4(lse))
+    return DUO_ERR_INVALID;
+  const int32_t b0 = seq < 0 ? 0 : seq, nb = seq < 0 ? c->cfg.batch : 1;
+  for (int32_t b = b0; b < b0 + nb; ++b)
+    if ((int64_t)len_of(c, layer, b) + n_chunk > c->cfg.capacity) return DUO_ERR_CAPACITY;
+  const LayerInfo& li = c->layers[layer];
+  const LayerPtrs p = layer_ptrs(c, layer);
+  PrefillArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = lse;
+  a.full_k = p.full_k;
+  a.full_v = p.full_v;
+  a.str_k = p.str_k;
+  a.str_v = p.str_v;
+  a.slot_pos = p.slot_pos;
+  a.b0 = b0;
+  a.nb = nb;
+  a.m = n_chunk;
+  a.Hq = c->cfg.num_q_heads;
+  a.Hkv = c->cfg.num_kv_heads;
+  a.Hr = li.n_ret;
+  a.Hs = li.n_str;
+  a.cap = c->cfg.capacity;
+  a.S = c->cfg.sink;
+  a.R = c->cfg.recent;
+  a.scale_log2 = (float)((double)c->scale * 1.4426950408889634);
+  a.out_f32 = c->cfg.out_dtype == DUO_F32;
+  std::memcpy(a.cls_idx, li.cls_idx, sizeof(a.cls_idx));
+  for (int32_t i = 0; i < nb; ++i) a.c0[i] = len_of(c, layer, b0 + i);
+  const int group = c->cfg.num_q_heads / c->cfg.num_kv_heads;
+  const int rc = launch_prefill(a, c->cfg.dtype, c->cfg.head_dim, group, stream);
+  if (rc == -1) return DUO_ERR_UNSUPPORTED;
+  if (rc != 0) return DUO_ERR_HIP;
+  return DUO_OK;
+}
+
+duo_status duo_slot_positions(duo_cache* c, int32_t layer, int32_t* host_out, void* stream) {
+  if (!layer_ok(c, layer) || !host_out) return DUO_ERR_INVALID;
+  const uint64_t SR = (uint64_t)c->cfg.sink + c->cfg.recent;
+  const LayerPtrs p = layer_ptrs(c, layer);
+  if (copy_d2h_sync(host_out, p.slot_pos, (uint64_t)c->cfg.batch * SR * 4, stream) != 0)
+    return DUO_ERR_HIP;
+  return DUO_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,119 @@
+// Internal declarations shared by the host logic (duo_host.cpp, plain C++) and the HIP
+// kernel launchers. Nothing here is part of the C ABI.
+#pragma once
+
+#include <cstdint>
+#include <vector>
+
+#include "../../include/duo.h"
+
+namespace duo {
+
+constexpr int kMaxKvHeads = 64;
+constexpr int kMaxBatch = 512;
+constexpr int kDefaultSplits = 128;
+constexpr int kMaxSplits = 1024;
+constexpr uint64_t kAlign = 256;
+
+// Per-layer head partition. For KV head j: cls_idx[j] >= 0 is its index among the layer's
+// retrieval heads; cls_idx[j] < 0 encodes streaming index -(cls_idx[j] + 1).
+struct LayerInfo {
+  int32_t n_ret = 0, n_str = 0;
+  uint64_t full_off = 0;  // bytes from layout.full_k_off (same offset in the V region)
+  uint64_t str_off = 0;   // bytes from layout.str_k_off (same offset in the V region)
+  int16_t cls_idx[kMaxKvHeads];
+  uint8_t ret_kv[kMaxKvHeads];  // retrieval index -> KV head
+  uint8_t str_kv[kMaxKvHeads];  // streaming index -> KV head
+};
+
+// ---------------------------------------------------------------------------------------
+// Kernel argument blocks (plain data, passed by value)
+// ---------------------------------------------------------------------------------------
+
+struct ResetArgs {
+  int32_t* slot_pos;   // [n_slot] -> -1
+  int64_t n_slot;
+  int32_t* seq_len;    // [n_len] -> 0
+  int64_t n_len;
+  uint32_t* counters;  // [n_cnt] -> 0
+  int64_t n_cnt;
+};
+
+struct AppendArgs {
+  const void* k;  // [nb][m][Hkv][D]
+  const void* v;
+  void* full_k;   // this layer: [B][Hr][cap][D]
+  void* full_v;
+  void* str_k;    // this layer: [B][Hs][S+R][D]
+  void* str_v;
+  int32_t* slot_pos;  // this layer: [B][S+R]
+  int32_t* seq_len;   // this layer: [B]
+  int32_t b0, nb, m, Hkv, Hr, Hs, cap, S, R;
+  int32_t row_bytes;  // D * element size
+  int16_t cls_idx[kMaxKvHeads];
+  int32_t n_old[kMaxBatch];  // lengths before the append, for sequences b0 .. b0+nb-1
+};
+
+struct DecodeArgs {
+  const void* q;   // [B][Hq][D]
+  void* out;       // [B][Hq][D]
+  float* lse;      // [B][Hq] or null
+  const void* full_k;
+  const void* full_v;
+  const void* str_k;
+  const void* str_v;
+  const int32_t* seq_len;  // this layer: [B]
+  float* part_o;           // [B][Hq][max_splits][D]
+  float* part_ml;          // [B][Hq][max_splits][2]
+  uint32_t* counters;      // [B][Hkv]
+  int32_t B, Hq, Hkv, Hr, Hs, cap, S, R, nsplit, max_splits;
+  float scale_log2;        // softmax scale * log2(e)
+  int32_t out_f32;
+  uint8_t ret_kv[kMaxKvHeads];
+  uint8_t str_kv[kMaxKvHeads];
+};
+
+struct PrefillArgs {
+  const void* q;   // [nb][m][Hq][D]
+  const void* k;   // [nb][m][Hkv][D]
+  const void* v;
+  void* out;       // [nb][m][Hq][D]
+  float* lse;      // [nb][m][Hq] or null
+  const void* full_k;
+  const void* full_v;
+  const void* str_k;
+  const void* str_v;
+  const int32_t* slot_pos;  // this layer: [B][S+R]
+  int32_t b0, nb, m, Hq, Hkv, Hr, Hs, cap, S, R;
+  float scale_log2;
+  int32_t out_f32;
+  int16_t cls_idx[kMaxKvHeads];
+  int32_t c0[kMaxBatch];  // chunk start (current length) of each sequence b0 .. b0+nb-1
+};
+
+// Launchers (one translation unit per kernel family). They return a hipError_t value as int.
+int launch_reset(const ResetArgs& a, void* stream);
+int launch_append(const AppendArgs& a, int dtype, void* stream);
+int launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group, void* stream);
+int launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int group, void* stream);
+
+// Host-side helpers (duo_host.cpp)
+int element_size(int32_t dtype);
+duo_status check_config(const duo_config* cfg);
+duo_status build_layout(const duo_config* cfg, duo_layout* lay, std::vector<LayerInfo>* layers);
+int choose_decode_splits(int32_t n_max, int32_t batch, int32_t n_ret, int32_t max_splits);
+
+}  // namespace duo
+
+// The opaque cache object behind duo_cache*.
+struct duo_cache {
+  duo_config cfg;                       // retrieval_mask points into `mask`
+  std::vector<uint8_t> mask;            // [L][Hkv]
+  std::vector<duo::LayerInfo> layers;   // [L]
+  duo_layout lay;
+  char* arena = nullptr;
+  std::vector<int32_t> lens;            // host mirror [L][B]
+  int32_t force_splits = 0;
+  int esize = 0;
+  float scale = 0.f;
+};

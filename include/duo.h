@@ -1,0 +1,167 @@
+/*
+ * duo.h - C ABI of libduo: attention over a head-partitioned KV cache on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The method (arXiv 2410.10819, "DuoAttention: Efficient Long-Context LLM Inference with
+ * Retrieval and Streaming Heads") splits the KV heads of every layer into retrieval heads,
+ * which keep and attend over every token, and streaming heads, which keep and attend over a
+ * constant-size cache of attention-sink tokens plus a window of recent tokens. Citations
+ * below name the web pages about the paper and the section on them:
+ *   explainer        = paper-graph-ui.vercel.app walkthrough of the paper;
+ *   OpenReview thread = paperhub.cn page with the authors' rebuttal.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All calls are C, never throw and return a duo_status. DUO_OK is 0.
+ * - Argument and capacity checks happen on the host before anything is launched; when a
+ *   call returns an error other than DUO_ERR_HIP nothing was launched and no state changed.
+ *   DUO_ERR_HIP means a HIP runtime call or launch failed (the device state is then
+ *   unspecified). Faults inside kernels surface asynchronously, as in any stream API.
+ * - Device work is enqueued on `stream` (a hipStream_t; NULL is the default stream) and is
+ *   asynchronous; only duo_slot_positions synchronizes. Calls on one cache must be ordered
+ *   on one stream: they share the cache's split-K workspace and counters.
+ * - The library never allocates or frees device memory. The caller owns the arena and every
+ *   input/output buffer; all device pointers must stay valid until the work completes.
+ * - Layouts are row-major and contiguous in the native head order of the model:
+ *     decode  q, out      [B][Hq][d]        lse [B][Hq]
+ *     prefill q, out      [B][m][Hq][d]     lse [B][m][Hq]   (seq = -1: every sequence)
+ *                         [m][Hq][d]        lse [m][Hq]      (seq >= 0: one sequence)
+ *     append/prefill k, v [B][m][Hkv][d]   or [m][Hkv][d] (seq >= 0)
+ *   Query head h reads KV head h / G with G = Hq / Hkv (contiguous groups). KV heads are
+ *   never repeated into query heads (OpenReview thread, "GQA Compatibility").
+ * - Element types: q, k, v and both caches use cfg.dtype; out uses cfg.out_dtype (DUO_F32,
+ *   or equal to cfg.dtype); lse is always float, natural log of the softmax denominator.
+ */
+#ifndef DUO_H
+#define DUO_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DUO_OK = 0,
+  DUO_ERR_INVALID = 1,     /* bad argument, null pointer, bad layer/sequence, bad config */
+  DUO_ERR_CAPACITY = 2,    /* an append would exceed cfg.capacity tokens */
+  DUO_ERR_UNSUPPORTED = 3, /* valid but not built: head_dim, group size or dtype */
+  DUO_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} duo_status;
+
+typedef enum { DUO_F32 = 0, DUO_BF16 = 1 } duo_dtype;
+
+/* Cache configuration. head_dim is 64 or 128; G = num_q_heads / num_kv_heads is 1, 2, 4 or
+ * 8; sink >= 0 and recent >= 1 (explainer, "The Full and Streaming Attention Masks": the
+ * streaming mask keeps the first `sink` tokens and the `recent` most recent ones, the query's
+ * own token included). capacity bounds the tokens of each sequence in a retrieval cache. */
+typedef struct {
+  int32_t num_layers;
+  int32_t batch;           /* sequences, 1..512 */
+  int32_t num_q_heads;
+  int32_t num_kv_heads;    /* 1..64 */
+  int32_t head_dim;
+  int32_t sink;            /* S */
+  int32_t recent;          /* R */
+  int32_t capacity;        /* max tokens per sequence, >= 1 */
+  int32_t dtype;           /* duo_dtype of q, k, v and the caches */
+  int32_t out_dtype;       /* duo_dtype of out */
+  float softmax_scale;     /* <= 0 selects 1/sqrt(head_dim) */
+  int32_t max_splits;      /* split-K workspace per (sequence, query head); 0 selects 128 */
+  const uint8_t* retrieval_mask; /* host [num_layers][num_kv_heads], nonzero = retrieval;
+                                    copied by duo_cache_create */
+} duo_config;
+
+/* Byte offsets inside the caller's arena (all 256-byte aligned). */
+typedef struct {
+  uint64_t arena_bytes;
+  uint64_t full_k_off;     /* retrieval caches: per layer [B][H_r][capacity][d] */
+  uint64_t full_v_off;
+  uint64_t str_k_off;      /* streaming caches: per layer [B][H_s][S+R][d] */
+  uint64_t str_v_off;
+  uint64_t slot_pos_off;   /* int32 [L][B][S+R]: position held by each slot, -1 = empty */
+  uint64_t seq_len_off;    /* int32 [L][B]: tokens appended so far */
+  uint64_t workspace_off;  /* split-K partials and merge counters */
+  uint64_t workspace_bytes;
+} duo_layout;
+
+typedef struct duo_cache duo_cache; /* opaque host object; owns no device memory */
+
+/* Sizes and offsets of the device arena for `cfg`. Host only. DUO_ERR_INVALID or
+ * DUO_ERR_UNSUPPORTED for a bad or unbuilt configuration. The layout is the split KV layout
+ * of the explainer's "Deployment Architecture": one full cache per retrieval head and one
+ * constant-size cache per streaming head, each head's rows contiguous. */
+duo_status duo_layout_query(const duo_config* cfg, duo_layout* out);
+
+/* Build the host object for a cache living in `arena` (device memory of at least
+ * layout.arena_bytes, 256-byte aligned). Host only: nothing is launched; call
+ * duo_cache_reset before first use. The cache keeps a host mirror of every sequence length
+ * so that capacity checks and launch shapes need no device-to-host copy. */
+duo_status duo_cache_create(const duo_config* cfg, void* arena, uint64_t arena_bytes,
+                            duo_cache** out);
+
+/* Empty every sequence of every layer: lengths 0, slot table -1, merge counters 0.
+ * Enqueues one fill kernel on `stream` (no memset node, so it can be graph-captured). */
+duo_status duo_cache_reset(duo_cache* cache, void* stream);
+
+/* Free the host object (not the arena). NULL is accepted. */
+duo_status duo_cache_destroy(duo_cache* cache);
+
+/* Append n_new tokens to one layer (explainer, "Decoding Procedure" step 4 and "Chunked
+ * Pre-filling"): for each new position t and KV head, a retrieval head stores K_t, V_t at row
+ * t of its full cache; a streaming head stores them at slot t if t < S, else at slot
+ * S + (t - S) mod R, but only when the token is still held after the append (t < S or
+ * t >= n + n_new - R), which evicts the oldest non-sink tokens. The slot table and lengths
+ * are updated. seq = -1 appends n_new tokens to every sequence (k, v [B][n_new][Hkv][d]);
+ * seq >= 0 appends to that sequence only (k, v [n_new][Hkv][d]). n_new = 0 is a no-op.
+ * DUO_ERR_CAPACITY if a sequence would exceed cfg.capacity. */
+duo_status duo_kv_append(duo_cache* cache, int32_t layer, int32_t seq, const void* k,
+                         const void* v, int32_t n_new, void* stream);
+
+/* One decoding step of one layer for every sequence (explainer, "Decoding Procedure" steps
+ * 1-5). The step's token must already be appended, so the query at position n-1 attends to
+ * itself. Retrieval heads attend over all n tokens of their full cache; streaming heads over
+ * the sinks and the last R tokens held by their cache (the Lambda mask). Outputs are written
+ * in the native head order. q [B][Hq][d]; out [B][Hq][d]; lse [B][Hq] or NULL.
+ * DUO_ERR_INVALID if some sequence is empty. */
+duo_status duo_attn_decode(duo_cache* cache, int32_t layer, const void* q, void* out,
+                           float* lse, void* stream);
+
+/* Attention of one pre-filling chunk (explainer, "Chunked Pre-filling"). The chunk holds
+ * positions c .. c+m-1 where c is the sequence's current length. Query p attends to every
+ * t <= p on retrieval heads (full cache rows 0..c-1 plus the chunk, causally) and, on
+ * streaming heads, to the t <= p with t < S or t >= p - R + 1 (sinks and ring before the
+ * chunk, plus the chunk). The cache is not modified: the caller then appends the same k, v
+ * with duo_kv_append. Layouts as in the header comment; n_chunk = 0 is a no-op. */
+duo_status duo_attn_prefill(duo_cache* cache, int32_t layer, int32_t seq, const void* q,
+                            const void* k, const void* v, int32_t n_chunk, void* out,
+                            float* lse, void* stream);
+
+/* Copy the slot table of one layer, int32 [B][S+R], to host memory. Synchronizes `stream`. */
+duo_status duo_slot_positions(duo_cache* cache, int32_t layer, int32_t* host_out,
+                              void* stream);
+
+/* Host mirror of the lengths, int32 [L][B]. Host only. */
+duo_status duo_cache_lengths(const duo_cache* cache, int32_t* host_out);
+
+/* KV bytes one layer holds for sequences of the given lengths (int32 [B]): under full
+ * attention (every KV head keeps every token) and under the split layout
+ * (H_r * n + H_s * min(n, S + R)) * d * 2 * element size, summed over sequences (explainer,
+ * "Decoding Procedure", memory formula). The second figure is also the K/V bytes one decode
+ * step of that layer reads. Host only. */
+duo_status duo_kv_bytes(const duo_config* cfg, int32_t layer, const int32_t* seq_lens,
+                        uint64_t* full_attn_bytes, uint64_t* duo_bytes);
+
+/* Override the number of context splits per retrieval head used by duo_attn_decode
+ * (0 = automatic from the lengths; otherwise 1..cfg.max_splits). The result does not depend
+ * on it beyond floating-point rounding. Host only. */
+duo_status duo_set_decode_splits(duo_cache* cache, int32_t splits);
+
+/* Static text for a status code. */
+const char* duo_status_string(duo_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DUO_H */

@@ -1,0 +1,143 @@
+"""duo_attn_decode on the GPU against the CPU float64 oracle.
+
+Every case fills a context by bulk append, then runs steps of (append one token, decode at
+that position) and compares out and lse elementwise with |gpu - ref| <= 2e-3 + 1e-2 |ref|.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import duo_oracle as O
+
+from gpu_util import assert_close, fill, make_cache, step_inputs, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_decode(w, lens0, steps, check_steps=None, splits=None, out_dtype=torch.float32,
+               layer=0, mask_layer=None, heads=None, cache=None):
+    """Fill, then decode ``steps`` steps; check the steps in ``check_steps`` (default all)."""
+    import head_split_kv_amd as hsk
+    gl = layer if mask_layer is None else mask_layer
+    if cache is None:
+        cache = make_cache(w, out_dtype=out_dtype, capacity=max(lens0) + steps)
+        fill(cache, w, layer, lens0, mask_layer=gl)
+    if splits is not None:
+        hsk.duo_set_decode_splits(cache, splits)
+    mask = W.retrieval_mask(w)[gl]
+    lens = list(lens0)
+    worst = 0.0
+    for s in range(steps):
+        q, k, v, qh = step_inputs(w, gl, lens)
+        cache.kv_append(layer, k, v)
+        lens = [n + 1 for n in lens]
+        lse = torch.empty((w.batch, w.hq), dtype=torch.float32, device="cuda")
+        out = cache.attn_decode(layer, q, lse=lse)
+        if check_steps is not None and s not in check_steps:
+            continue
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy()
+        got_lse = lse.cpu().numpy()
+        for b, n in enumerate(lens):
+            kh = W.tokens(w, "k", gl, b, 0, n)
+            vh = W.tokens(w, "v", gl, b, 0, n)
+            if heads is None:
+                ref, ref_lse = O.decode_step(qh[b], kh, vh, mask, w.sink, w.recent)
+                worst = max(worst, assert_close(got[b], ref, f"step {s} seq {b} out"))
+                assert_close(got_lse[b], ref_lse, f"step {s} seq {b} lse")
+            else:  # a subset of KV heads (their query groups), for very long contexts
+                G = w.group
+                for j in heads:
+                    hq = slice(j * G, (j + 1) * G)
+                    ref, ref_lse = O.decode_step(qh[b][hq], kh[:, j:j + 1], vh[:, j:j + 1],
+                                                 mask[j:j + 1], w.sink, w.recent)
+                    worst = max(worst, assert_close(got[b][hq], ref, f"step {s} seq {b} kv {j}"))
+                    assert_close(got_lse[b][hq], ref_lse, f"step {s} seq {b} kv {j} lse")
+    return cache, worst
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_decode_variants(dtype, d, G):
+    """Every built (dtype, head_dim, group) variant; ragged batch around S+R."""
+    w = W.Workload("decode-variant", 1, 3, 2 * G, 2, d, dtype, 4, 32, 0, 3, 1,
+                   fixed_mask=((1,),), seed=3 + G)
+    run_decode(w, [1, 37, 1500], 3)
+
+
+@pytest.mark.parametrize("S", [0, 4, 16])
+@pytest.mark.parametrize("R", [1, 32, 512])
+def test_decode_sink_recent(S, R):
+    """Sink/recent sizes, lengths just below, at and above S+R, and long."""
+    w = W.Workload("decode-sr", 1, 4, 8, 4, 128, "bf16", S, R, 0, 2, 2, fixed_mask=((0, 3),),
+                   seed=5)
+    run_decode(w, [max(1, S + R - 2), S + R - 1 if S + R > 1 else 1, S + R + 3, 2100], 2)
+
+
+@pytest.mark.parametrize("splits", [1, 7, 64, 0])
+def test_decode_split_count_invariance(splits):
+    """The result does not depend on the number of context splits (log-sum-exp merge)."""
+    w = W.Workload("decode-splits", 1, 2, 8, 2, 128, "bf16", 16, 64, 0, 2, 1,
+                   fixed_mask=((0,),), seed=7)
+    run_decode(w, [5000, 333], 2, splits=splits)
+
+
+def test_decode_bf16_output():
+    w = W.Workload("decode-bf16-out", 1, 2, 8, 2, 128, "bf16", 4, 32, 0, 2, 1,
+                   fixed_mask=((1,),), seed=9)
+    run_decode(w, [2000, 40], 2, out_dtype=torch.bfloat16)
+
+
+def test_decode_all_retrieval_and_all_streaming():
+    for mask in (((0, 1),), ((),)):
+        w = W.Workload("decode-pure", 1, 2, 8, 2, 128, "bf16", 4, 32, 0, 2, 1,
+                       fixed_mask=mask, seed=13)
+        run_decode(w, [1000, 5], 2)
+
+
+def test_decode_c1_tiny_gqa_fp32():
+    """Tiny GQA decode: 1,024-token context, 16 steps, every output checked."""
+    w = W.workload("c1")
+    _, worst = run_decode(w, [w.context], w.decode_steps)
+    assert worst < 1e-4  # fp32 inputs: only accumulation-order differences remain
+
+
+def test_decode_c2_mha_32k():
+    """Llama-2-7B-shaped MHA layer at 32K context, 64 steps (outputs checked at 5 steps)."""
+    w = W.workload("c2")
+    run_decode(w, [w.context], w.decode_steps, check_steps={0, 1, 31, 62, 63})
+
+
+def test_decode_c3_gqa_128k():
+    """Llama-3-8B-shaped GQA layer at 128K context, 128 steps (checked at 5 steps)."""
+    w = W.workload("c3")
+    run_decode(w, [w.context], w.decode_steps, check_steps={0, 1, 64, 126, 127})
+
+
+@pytest.mark.timeout(900)
+def test_decode_c4_full_depth_ragged_batch():
+    """32 layers, batch 8, ragged 16K..32K: all layers run; the oracle checks the first and
+    last step on three layers."""
+    w = W.workload("c4")
+    lens0 = [int(x) for x in W.initial_lengths(w)]
+    cache = make_cache(w, capacity=max(lens0) + w.decode_steps, layers=w.layers)
+    for layer in range(w.layers):
+        fill(cache, w, layer, lens0)
+    checked = {0, 17, 31}
+    for layer in range(w.layers):
+        run_decode(w, lens0, w.decode_steps,
+                   check_steps={0, w.decode_steps - 1} if layer in checked else set(),
+                   layer=layer, cache=cache)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("key", ["c5", "c5q"])
+def test_decode_c5_1m_context(key):
+    """1,048,576-token context, 50 % and 25 % retrieval; first 2 steps checked on every
+    retrieval head and one streaming head."""
+    w = W.workload(key)
+    mask = W.retrieval_mask(w)[0]
+    heads = list(np.nonzero(mask)[0]) + [int(np.nonzero(1 - mask)[0][0])]
+    run_decode(w, [w.context], 4, check_steps={0, 1}, heads=heads)

@@ -1,0 +1,185 @@
+"""The C ABI on the host (CPU only): exports, configuration checks, arena layout, the KV
+byte model against the oracle, and the error paths that return before any launch.
+
+These tests never make a call that passes validation with device work to do: every call
+that could launch is given an argument that must be rejected first, so they are safe with
+or without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import duo_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+hsk = pytest.importorskip("head_split_kv_amd")
+from head_split_kv_amd import _native as N  # noqa: E402
+
+if not os.path.exists(N.LIB_PATH):
+    pytest.skip("libduo.so not built", allow_module_level=True)
+
+
+def declared_symbols():
+    with open(os.path.join(ROOT, "include", "duo.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^(?:duo_status|const char\*)\s+(duo_\w+)\(", text, re.M)))
+
+
+def cfg_of(**kw):
+    base = dict(num_layers=2, batch=3, num_q_heads=8, num_kv_heads=2, head_dim=128, sink=4,
+                recent=16, capacity=1000, retrieval_mask=[[1, 0], [0, 1]])
+    base.update(kw)
+    return hsk.make_config(**base)
+
+
+def test_exports_every_declared_symbol():
+    names = declared_symbols()
+    assert len(names) >= 12
+    assert sorted(N.EXPORTS) == names
+    L = N.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for s in range(5):
+        assert N.status_string(s).startswith(("DUO_OK", "DUO_ERR_"))
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(recent=0), N.DUO_ERR_INVALID),
+    (dict(sink=-1), N.DUO_ERR_INVALID),
+    (dict(batch=0), N.DUO_ERR_INVALID),
+    (dict(batch=513), N.DUO_ERR_INVALID),
+    (dict(num_q_heads=6, num_kv_heads=4, retrieval_mask=[[1, 0, 0, 0], [0, 1, 0, 0]]),
+     N.DUO_ERR_INVALID),
+    (dict(capacity=0), N.DUO_ERR_INVALID),
+    (dict(head_dim=96), N.DUO_ERR_UNSUPPORTED),
+    (dict(num_q_heads=6, num_kv_heads=2), N.DUO_ERR_UNSUPPORTED),
+    (dict(num_q_heads=32, num_kv_heads=2), N.DUO_ERR_UNSUPPORTED),
+])
+def test_config_checks(bad, status):
+    import torch
+    kw = dict(bad)
+    cfg, _ = cfg_of(**kw)
+    lay = N.DuoLayout()
+    assert N.lib().duo_layout_query(ctypes.byref(cfg), ctypes.byref(lay)) == status
+    # out dtype must be fp32 or the input dtype
+    cfg2, _ = cfg_of(dtype=torch.float32, out_dtype=torch.bfloat16)
+    assert N.lib().duo_layout_query(ctypes.byref(cfg2), ctypes.byref(lay)) == N.DUO_ERR_UNSUPPORTED
+
+
+def test_layout_covers_the_split_caches():
+    cfg, mask = cfg_of()
+    lay = hsk.duo_layout_query(cfg)
+    offs = [lay.full_k_off, lay.full_v_off, lay.str_k_off, lay.str_v_off, lay.slot_pos_off,
+            lay.seq_len_off, lay.workspace_off]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    es, B, D, cap, SR = 2, 3, 128, 1000, 20
+    n_ret = int(mask.sum())
+    n_str = mask.size - n_ret
+    assert lay.full_v_off - lay.full_k_off >= B * n_ret * cap * D * es
+    assert lay.str_v_off - lay.str_k_off >= B * n_str * SR * D * es
+    assert lay.seq_len_off - lay.slot_pos_off >= 2 * B * SR * 4
+    assert lay.arena_bytes >= lay.workspace_off + lay.workspace_bytes
+
+
+@pytest.mark.parametrize("layer", [0, 1])
+def test_kv_bytes_match_oracle_memory_model(layer):
+    import torch
+    for dtype, es in ((torch.bfloat16, 2), (torch.float32, 4)):
+        cfg, mask = cfg_of(dtype=dtype, out_dtype=torch.float32)
+        lens = [0, 7, 3000]
+        full, duo = hsk.duo_kv_bytes(cfg, layer, lens)
+        hr = int(mask[layer].sum())
+        hs = 2 - hr
+        want_duo = sum(2 * O.duo_kv_elements_layer(hr, hs, n, 4, 16, 128) * es for n in lens)
+        want_full = sum(O.full_kv_elements(1, 2, n, 128) * es for n in lens)
+        assert (full, duo) == (want_full, want_duo)
+
+
+def test_kv_bytes_at_workload_shapes():
+    """Full/split KV ratios of the Llama-shaped layers (128K GQA 50 %, 32K MHA 25 %)."""
+    import workloads as W
+    for key, ratio in (("c3", 1_048_576 / 526_400), ("c2", 1_048_576 / 274_816)):
+        w = W.workload(key)
+        cfg, _ = hsk.make_config(num_layers=1, batch=1, num_q_heads=w.hq, num_kv_heads=w.hkv,
+                                 head_dim=w.d, sink=w.sink, recent=w.recent, capacity=w.capacity,
+                                 retrieval_mask=W.retrieval_mask(w))
+        full, duo = hsk.duo_kv_bytes(cfg, 0, [w.context])
+        assert abs(full / duo - ratio) < 1e-9
+
+
+class FakeCache:
+    """A host object over a fake (never dereferenced) arena address: only calls that the
+    host rejects before launching are made on it."""
+
+    def __init__(self, **kw):
+        self.cfg, self.mask = cfg_of(**kw)
+        lay = hsk.duo_layout_query(self.cfg)
+        self.h = ctypes.c_void_p()
+        st = N.lib().duo_cache_create(ctypes.byref(self.cfg), ctypes.c_void_p(1 << 40),
+                                      lay.arena_bytes, ctypes.byref(self.h))
+        assert st == N.DUO_OK
+        self.lay = lay
+
+    def lengths(self):
+        out = np.empty((self.cfg.num_layers, self.cfg.batch), dtype=np.int32)
+        assert N.lib().duo_cache_lengths(self.h, out.ctypes.data_as(
+            ctypes.POINTER(ctypes.c_int32))) == 0
+        return out
+
+    def close(self):
+        N.lib().duo_cache_destroy(self.h)
+
+
+def test_create_rejects_small_or_misaligned_arena():
+    cfg, _ = cfg_of()
+    lay = hsk.duo_layout_query(cfg)
+    h = ctypes.c_void_p()
+    L = N.lib()
+    assert L.duo_cache_create(ctypes.byref(cfg), ctypes.c_void_p(1 << 40),
+                              lay.arena_bytes - 1, ctypes.byref(h)) == N.DUO_ERR_INVALID
+    assert L.duo_cache_create(ctypes.byref(cfg), ctypes.c_void_p((1 << 40) + 16),
+                              lay.arena_bytes, ctypes.byref(h)) == N.DUO_ERR_INVALID
+    assert L.duo_cache_create(ctypes.byref(cfg), None, lay.arena_bytes,
+                              ctypes.byref(h)) == N.DUO_ERR_INVALID
+
+
+def test_error_paths_leave_state_unchanged():
+    fc = FakeCache()
+    L = N.lib()
+    p = ctypes.c_void_p(1 << 41)  # aligned, never dereferenced
+    mis = ctypes.c_void_p((1 << 41) + 8)
+    before = fc.lengths().copy()
+    # bad layer / sequence / count
+    assert L.duo_kv_append(fc.h, 2, -1, p, p, 1, None) == N.DUO_ERR_INVALID
+    assert L.duo_kv_append(fc.h, -1, -1, p, p, 1, None) == N.DUO_ERR_INVALID
+    assert L.duo_kv_append(fc.h, 0, 3, p, p, 1, None) == N.DUO_ERR_INVALID
+    assert L.duo_kv_append(fc.h, 0, -2, p, p, 1, None) == N.DUO_ERR_INVALID
+    assert L.duo_kv_append(fc.h, 0, -1, p, p, -1, None) == N.DUO_ERR_INVALID
+    assert L.duo_kv_append(fc.h, 0, -1, None, p, 1, None) == N.DUO_ERR_INVALID
+    assert L.duo_kv_append(fc.h, 0, -1, mis, p, 1, None) == N.DUO_ERR_INVALID
+    # zero tokens is a no-op that launches nothing
+    assert L.duo_kv_append(fc.h, 0, -1, p, p, 0, None) == N.DUO_OK
+    # capacity: 1001 tokens into a 1000-token cache
+    assert L.duo_kv_append(fc.h, 0, -1, p, p, 1001, None) == N.DUO_ERR_CAPACITY
+    assert L.duo_kv_append(fc.h, 1, 1, p, p, 1001, None) == N.DUO_ERR_CAPACITY
+    assert L.duo_attn_prefill(fc.h, 0, -1, p, p, p, 1001, p, None, None) == N.DUO_ERR_CAPACITY
+    # decode of empty sequences is rejected
+    assert L.duo_attn_decode(fc.h, 0, p, p, None, None) == N.DUO_ERR_INVALID
+    assert L.duo_attn_decode(fc.h, 0, mis, p, None, None) == N.DUO_ERR_INVALID
+    assert L.duo_attn_prefill(fc.h, 0, -1, p, p, p, 0, p, None, None) == N.DUO_OK
+    assert L.duo_attn_prefill(fc.h, 0, 5, p, p, p, 4, p, None, None) == N.DUO_ERR_INVALID
+    assert L.duo_attn_prefill(fc.h, 0, 0, p, mis, p, 4, p, None, None) == N.DUO_ERR_INVALID
+    assert L.duo_slot_positions(fc.h, 9, None, None) == N.DUO_ERR_INVALID
+    assert L.duo_set_decode_splits(fc.h, -1) == N.DUO_ERR_INVALID
+    assert L.duo_set_decode_splits(fc.h, 129) == N.DUO_ERR_INVALID
+    assert L.duo_set_decode_splits(fc.h, 7) == N.DUO_OK
+    assert np.array_equal(fc.lengths(), before)
+    assert L.duo_cache_destroy(None) == N.DUO_OK
+    fc.close()
