@@ -1,0 +1,375 @@
+"""Benchmark of the head-partitioned KV attention hot path on one MI355X.
+
+Decode leg (the headline): the Llama-3-8B-shaped GQA layer at a 128K context (32 query heads,
+8 KV heads, head_dim 128, bf16, 4 retrieval KV heads, sink 16 + recent 512). One step is, for
+each of ``--layers`` replica layers, one append of the new token followed by one decode. The
+replica layers sit at distinct addresses so that the per-step K/V (>= 2 GB) cannot stay in
+the 256 MB Infinity Cache; the time per layer-step is the step time divided by the layers.
+
+Prefill leg: the Llama-2-7B-shaped MHA layer (32 heads, 8 retrieval) pre-filling a 32K
+prompt in 4K-token chunks (prefill attention of each chunk, then its append).
+
+Prints one JSON line. ``value`` is the decode K/V bandwidth in GB/s (algorithmic bytes: the
+K/V rows the method must read, plus q, out and the appended token). Inputs are resident in
+HBM before the timed region starts.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn KV GB/s (% HBM peak) + µs/layer-step at 128K ctx; prefill TFLOP/s"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--layers", type=int, default=8, help="replica layers of the decode leg")
+    p.add_argument("--workload", default="c3", help="decode workload key (c2, c3, c5, c5q)")
+    p.add_argument("--prefill-passes", type=int, default=3)
+    p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--splits", type=int, default=0, help="force decode splits (0 = automatic)")
+    return p.parse_args()
+
+
+def source_sha(name: str) -> str:
+    with open(os.path.join(ROOT, "head_split_kv_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def committed_traffic(kernel_file: str, key: str):
+    """HBM bytes per launch measured with rocprofv3 counters for the current kernel source,
+    or None when the counters were taken on another version of the kernel."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    rec = data.get(key)
+    if not rec or rec.get("source_sha") != source_sha(kernel_file):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class Timer:
+    """HIP events on torch's current stream (the stream the library launches on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+
+    def start(self):
+        self.a.record()
+
+    def stop_ms(self):
+        self.b.record()
+        self.b.synchronize()
+        return self.a.elapsed_time(self.b)
+
+
+def decode_leg(args, torch, hsk, W, N):
+    w = W.workload(args.workload)
+    L = args.layers
+    total_steps = args.warmup + args.steps
+    n0 = w.context
+    cap = n0 + total_steps
+    mask = W.retrieval_mask(w)[0]
+    dev = torch.device("cuda")
+    cache = hsk.DuoCache(num_layers=L, batch=1, num_q_heads=w.hq, num_kv_heads=w.hkv,
+                         head_dim=w.d, sink=w.sink, recent=w.recent, capacity=cap,
+                         retrieval_mask=[mask] * L, dtype=torch.bfloat16,
+                         out_dtype=torch.bfloat16, device=dev, max_splits=1024)
+    if args.splits:
+        hsk.duo_set_decode_splits(cache, args.splits)
+    t = time.time()
+    chunk = 1 << 16
+    for t0 in range(0, n0, chunk):
+        t1 = min(n0, t0 + chunk)
+        k = torch.from_numpy(W.tokens(w, "k", 0, 0, t0, t1)).to(dev).to(torch.bfloat16)
+        v = torch.from_numpy(W.tokens(w, "v", 0, 0, t0, t1)).to(dev).to(torch.bfloat16)
+        for layer in range(L):
+            cache.kv_append(layer, k, v, seq=0)
+        del k, v
+    qs = torch.from_numpy(W.tokens(w, "q", 0, 0, n0, n0 + total_steps)).to(dev).to(torch.bfloat16)
+    ks = torch.from_numpy(W.tokens(w, "k", 0, 0, n0, n0 + total_steps)).to(dev).to(torch.bfloat16)
+    vs = torch.from_numpy(W.tokens(w, "v", 0, 0, n0, n0 + total_steps)).to(dev).to(torch.bfloat16)
+    out = torch.empty((1, w.hq, w.d), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    log(f"decode leg: {w.name}, {L} replica layers filled to {n0} tokens in {time.time() - t:.1f}s")
+
+    lib = N.lib()
+    h = cache.handle
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    qstride = w.hq * w.d * 2
+    kstride = w.hkv * w.d * 2
+    qp, kp, vp, op = qs.data_ptr(), ks.data_ptr(), vs.data_ptr(), ctypes.c_void_p(out.data_ptr())
+    append, decode = lib.duo_kv_append, lib.duo_attn_decode
+
+    def step(s):
+        kk = ctypes.c_void_p(kp + s * kstride)
+        vv = ctypes.c_void_p(vp + s * kstride)
+        qq = ctypes.c_void_p(qp + s * qstride)
+        for layer in range(L):
+            st = append(h, layer, -1, kk, vv, 1, stream)
+            st |= decode(h, layer, qq, op, None, stream)
+            if st:
+                raise RuntimeError(f"libduo call failed: {N.status_string(st)}")
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    tm.start()
+    for s in range(args.warmup, total_steps):
+        step(s)
+    total_ms = tm.stop_ms()
+    torch.cuda.synchronize()
+    ms_per_step = total_ms / args.steps
+
+    # algorithmic bytes of one layer-step, averaged over the timed steps
+    cfg1, _m = hsk.make_config(num_layers=1, batch=1, num_q_heads=w.hq, num_kv_heads=w.hkv,
+                               head_dim=w.d, sink=w.sink, recent=w.recent, capacity=cap,
+                               retrieval_mask=[mask])
+    kv_bytes = []
+    for s in range(args.warmup, total_steps):
+        kv_bytes.append(hsk.duo_kv_bytes(cfg1, 0, [n0 + s + 1])[1])
+    io_bytes = 2 * w.hq * w.d * 2 + 2 * 2 * w.hkv * w.d * 2  # q in, out, new K/V in + stored
+    step_bytes = sum(kv_bytes) / len(kv_bytes) + io_bytes
+    us_layer = ms_per_step * 1e3 / L
+    gbs = step_bytes / (us_layer * 1e-6) / 1e9
+
+    # the decode kernel alone: back-to-back launches over all replica layers at the final length
+    reps = max(4, 64 // L)
+    for layer in range(L):
+        decode(h, layer, ctypes.c_void_p(qp), op, None, stream)
+    torch.cuda.synchronize()
+    tm.start()
+    for _ in range(reps):
+        for layer in range(L):
+            decode(h, layer, ctypes.c_void_p(qp), op, None, stream)
+    dec_ms = tm.stop_ms() / (reps * L)
+    n_final = n0 + total_steps
+    dec_bytes = hsk.duo_kv_bytes(cfg1, 0, [n_final])[1] + 2 * w.hq * w.d * 2
+    dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
+    result = dict(
+        workload=w, layers=L, ms_per_step=ms_per_step, us_layer=us_layer, gbs=gbs,
+        step_bytes=step_bytes, dec_us=dec_ms * 1e3, dec_bytes=dec_bytes, dec_gbs=dec_gbs,
+        n_final=n_final, history=(n0, total_steps))
+    del cache, qs, ks, vs
+    torch.cuda.empty_cache()
+    return result
+
+
+def prefill_leg(args, torch, hsk, W, N):
+    w = W.workload("c2")
+    mask = W.retrieval_mask(w)[0]
+    dev = torch.device("cuda")
+    P, C = w.prefill_len, w.prefill_chunk
+    cache = hsk.DuoCache(num_layers=1, batch=1, num_q_heads=w.hq, num_kv_heads=w.hkv,
+                         head_dim=w.d, sink=w.sink, recent=w.recent, capacity=P,
+                         retrieval_mask=[mask], dtype=torch.bfloat16, out_dtype=torch.bfloat16,
+                         device=dev)
+    q = torch.from_numpy(W.tokens(w, "q", 0, 0, 0, P)).to(dev).to(torch.bfloat16)
+    k = torch.from_numpy(W.tokens(w, "k", 0, 0, 0, P)).to(dev).to(torch.bfloat16)
+    v = torch.from_numpy(W.tokens(w, "v", 0, 0, 0, P)).to(dev).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    lib = N.lib()
+    h = cache.handle
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    rs = w.hq * w.d * 2
+    ks = w.hkv * w.d * 2
+
+    def run_pass(timer_attn=None):
+        hsk.duo_cache_reset(cache)
+        attn_ms = 0.0
+        for c0 in range(0, P, C):
+            if timer_attn is not None:
+                timer_attn.start()
+            st = lib.duo_attn_prefill(h, 0, 0, ctypes.c_void_p(q.data_ptr() + c0 * rs),
+                                      ctypes.c_void_p(k.data_ptr() + c0 * ks),
+                                      ctypes.c_void_p(v.data_ptr() + c0 * ks), C,
+                                      ctypes.c_void_p(out.data_ptr() + c0 * rs), None, stream)
+            if timer_attn is not None:
+                attn_ms += timer_attn.stop_ms()
+            if st:
+                raise RuntimeError(f"prefill failed: {N.status_string(st)}")
+            st = lib.duo_kv_append(h, 0, 0, ctypes.c_void_p(k.data_ptr() + c0 * ks),
+                                   ctypes.c_void_p(v.data_ptr() + c0 * ks), C, stream)
+            if st:
+                raise RuntimeError(f"append failed: {N.status_string(st)}")
+        return attn_ms
+
+    run_pass()
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    tm.start()
+    for _ in range(args.prefill_passes):
+        run_pass()
+    pass_ms = tm.stop_ms() / args.prefill_passes
+    attn = []
+    for _ in range(args.prefill_passes):
+        attn.append(run_pass(Timer(torch)))
+    attn_ms = sum(attn) / len(attn)
+    # algorithmic flops: 4 d per visible (query, key) pair; query p sees p + 1 keys on a
+    # retrieval head and min(p + 1, S + R) on a streaming head
+    S, R = w.sink, w.recent
+    hr = int(mask.sum())
+    hs = w.hkv - hr
+    pairs_ret = P * (P + 1) // 2
+    pairs_str = sum(min(p + 1, S + R) for p in range(P))
+    flops = 4 * w.d * (hr * pairs_ret + hs * pairs_str) * (w.hq // w.hkv)
+    del cache, q, k, v, out
+    torch.cuda.empty_cache()
+    return dict(workload=w, pass_ms=pass_ms, attn_ms=attn_ms, flops=flops,
+                tflops=flops / (attn_ms * 1e-3) / 1e12,
+                tflops_incl_append=flops / (pass_ms * 1e-3) / 1e12)
+
+
+def copy_probe(torch):
+    """Achievable HBM bandwidth of a plain device copy (read + write bytes)."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    tm.start()
+    for _ in range(10):
+        b.copy_(a)
+    ms = tm.stop_ms() / 10
+    del a, b
+    return 2 * n / (ms * 1e-3) / 1e9
+
+
+def cpu_baseline(args, W, w, n):
+    """The float64 oracle decoding one step of the same layer on the host's cores."""
+    import numpy as np
+    from oracle import duo_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    mask = W.retrieval_mask(w)[0]
+    k = W.tokens(w, "k", 0, 0, 0, n)
+    v = W.tokens(w, "v", 0, 0, 0, n)
+    q = W.tokens(w, "q", 0, 0, n - 1, n)[0]
+    t = time.time()
+    calls = 0
+    while True:
+        O.decode_step(q, k, v, mask, w.sink, w.recent)
+        calls += 1
+        if time.time() - t > args.cpu_seconds:
+            break
+    sec = (time.time() - t) / calls
+    return dict(sec_per_step=sec, calls=calls, threads=threads)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(multi-GPU sharding is described, not built)"}))
+        sys.exit(2)
+    import torch
+    import head_split_kv_amd as hsk
+    from head_split_kv_amd import _native as N
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dec = decode_leg(args, torch, hsk, W, N)
+    log(f"decode: {dec['us_layer']:.2f} us/layer-step, {dec['gbs']:.0f} GB/s; kernel alone "
+        f"{dec['dec_us']:.2f} us = {dec['dec_gbs']:.0f} GB/s")
+    pre = None
+    if not args.no_prefill:
+        try:
+            pre = prefill_leg(args, torch, hsk, W, N)
+            log(f"prefill: {pre['attn_ms']:.3f} ms attention for {pre['flops'] / 1e12:.3f} TFLOP "
+                f"= {pre['tflops']:.1f} TFLOP/s")
+        except (RuntimeError, hsk.DuoError) as e:
+            log(f"prefill leg skipped: {e}")
+    probe = copy_probe(torch)
+    w = dec["workload"]
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(args, W, w, w.context)
+        log(f"oracle: {cpu['sec_per_step']:.3f} s per decode step on {cpu['threads']} threads")
+    traffic = committed_traffic("decode.hip", f"decode_{args.workload}")
+    out = {
+        "metric": METRIC,
+        "value": round(dec["gbs"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), bf16; no dataset)",
+        "config": {
+            "workload": f"{w.name}: decode, 1 sequence, {w.hq} q / {w.hkv} kv heads, d={w.d}, "
+                        f"{w.n_retrieval} retrieval kv heads, sink {w.sink} + recent {w.recent}, "
+                        f"context {w.context}; step = append+decode on {dec['layers']} replica "
+                        f"layers",
+            "context": w.context, "replica_layers": dec["layers"], "global_batch": 1,
+        },
+        "us_per_layer_step": round(dec["us_layer"], 3),
+        "hbm_frac": round(dec["gbs"] / HBM_PEAK_GBS, 4),
+        "decode_kernel_us": round(dec["dec_us"], 3),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(dec["dec_gbs"], 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(dec["dec_gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "decode_kernel (bf16, d=128, G=4)",
+            "algorithmic_bytes_per_launch": int(dec["dec_bytes"]),
+        },
+        "hbm_copy_probe_GBps": round(probe, 1),
+        "prefill": None if pre is None else {
+            "workload": f"{pre['workload'].name}: 32K prompt in 4K chunks",
+            "attn_ms": round(pre["attn_ms"], 3),
+            "ms_incl_append": round(pre["pass_ms"], 3),
+            "tflops": round(pre["tflops"], 1),
+            "roofline": {"bound": "mfma", "achieved": round(pre["tflops"], 1),
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(pre["tflops"] / BF16_PEAK_TFLOPS, 4),
+                         "traffic": committed_traffic("prefill.hip", "prefill_c2"),
+                         "algorithmic_flops": int(pre["flops"])},
+        },
+        "cpu_baseline": None if cpu is None else {
+            "value": round(dec["dec_bytes"] / cpu["sec_per_step"] / 1e9, 3),
+            "unit": "GB/s",
+            "cores": cpu["threads"],
+            "kind": "oracle",
+            "sample": f"{cpu['calls']} float64 oracle decode step(s) of one {w.name} layer at "
+                      f"{w.context} tokens (all 32 query heads), {cpu['sec_per_step']:.2f} s each",
+        },
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -14,8 +14,6 @@ __global__ void __launch_bounds__(kThreads) reset_kernel(ResetArgs a) {
     a.slot_pos[i] = -1;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < a.n_len; i += stride)
     a.seq_len[i] = 0;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < a.n_cnt; i += stride)
-    a.counters[i] = 0u;
 }
 
 // Streaming slot of token t: sinks take slots 0..S-1, later tokens a ring of R slots after
@@ -90,8 +88,7 @@ int grid_for(int64_t work) {
 }  // namespace
 
 int launch_reset(const ResetArgs& a, void* stream) {
-  int64_t work = a.n_slot > a.n_len ? a.n_slot : a.n_len;
-  if (a.n_cnt > work) work = a.n_cnt;
+  const int64_t work = a.n_slot > a.n_len ? a.n_slot : a.n_len;
   hipLaunchKernelGGL(reset_kernel, dim3(grid_for(work)), dim3(kThreads), 0,
                      (hipStream_t)stream, a);
   return (int)hipGetLastError();

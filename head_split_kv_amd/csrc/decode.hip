@@ -8,14 +8,14 @@
 //
 // Inside a block of 4 waves, every wave streams groups of 64/LPT tokens: LPT lanes (8 or
 // 16) share one token row (each lane owns D/LPT elements of it) and every lane keeps the
-// running state of all G query heads of the GQA group, so one load of each K/V row serves the whole group without
-// repeating KV heads (OpenReview thread, "GQA Compatibility"). Logits are reduced over the
-// LPT lanes with DPP, bf16 dot products use v_dot2_f32_bf16 with fp32 accumulation, and the
-// softmax is online in the log2 domain with a lazy rescale: the running maximum of a lane
-// group is only moved when a logit exceeds it by more than kTau, which keeps every weight
-// below 2^kTau and leaves the quotient out/l exact. At the end the lane groups of a wave are
-// merged with lane shuffles, the waves through LDS, and the splits of one (b, j) by the last
-// block to finish (atomic ticket), with the log-sum-exp weights exp2(m_i - m) .
+// running state of all G query heads of the GQA group, so one load of each K/V row serves the
+// whole group without repeating KV heads (OpenReview thread, "GQA Compatibility"). Logits are
+// reduced over the LPT lanes with DPP, bf16 dot products use v_dot2_f32_bf16 with fp32
+// accumulation, and the softmax is online in the log2 domain with a lazy rescale: the running
+// maximum of a lane group only moves when a logit exceeds it by more than kTau, which keeps
+// every weight below 2^kTau and leaves the quotient out/l exact. At the end the lane groups
+// of a wave are merged with lane shuffles, the waves through LDS, and the context splits of a
+// retrieval head by a second, small kernel with the log-sum-exp weights exp2(m_i - m).
 #include <hip/hip_runtime.h>
 
 #include "duo_internal.h"
@@ -25,9 +25,11 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kStages = 3;       // register slots of token groups per wave
-constexpr float kTau = 8.0f;     // lazy-rescale threshold (log2 units)
+constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
 constexpr float kNegInf = -__builtin_inff();
+// Initial running maximum: finite, so exp2(dot * c2 - m) of a masked token (dot = -inf) is
+// exactly 0 and exp2(m - m') of an empty group is 0 (or 1 times a zero sum) with no checks.
+constexpr float kMInit = -1e30f;
 constexpr float kLn2 = 0.69314718055994530942f;
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
@@ -148,6 +150,10 @@ __device__ __forceinline__ void accumulate_pv(const Frag<T, D, LPT>& f, const fl
   }
 }
 
+// Register slots of token groups per wave (NS - 1 groups in flight while one is processed).
+template <typename T, int D, int G>
+constexpr int stages() { return 3; }
+
 // Lanes per token row: 8 unless the per-lane state of all G heads would not fit the
 // register budget of two waves per SIMD, then 16 (halves the elements each lane owns).
 template <typename T, int D, int G>
@@ -155,21 +161,23 @@ constexpr int lanes_per_token() {
   constexpr int chunks = D * (int)sizeof(T) / 16;
   constexpr int e8 = D / 8;
   constexpr int words8 =
-      G * e8 + G * e8 * (int)sizeof(T) / 4 + kStages * 2 * (chunks / 8) * 4;
+      G * e8 + G * e8 * (int)sizeof(T) / 4 + stages<T, D, G>() * 2 * (chunks / 8) * 4;
   return (words8 > 200 && chunks >= 16) ? 16 : 8;
 }
 
-template <typename T, int D, int G, int LPT>
+template <typename T, int D, int G, int LPT, int NS>
 __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
   using Geo = RowGeom<T, D, LPT>;
-  constexpr int kTpw = 64 / LPT;  // tokens per wave per step
+  using F = Frag<T, D, LPT>;
+  constexpr int kTpw = 64 / LPT;        // tokens per wave per step
+  constexpr int kTpb = kWaves * kTpw;   // tokens per block per step
   constexpr int E = Geo::kE;
   constexpr int RB = D * (int)sizeof(T);
+  static_assert(NS == 3 || NS == 4, "3 or 4 register slots");
 
   __shared__ float s_o[kWaves][G][D];
   __shared__ float s_m[kWaves][G];
   __shared__ float s_l[kWaves][G];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, grp = lane / LPT, sub = lane % LPT;
@@ -188,10 +196,8 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
     b = (int)(i / ((int64_t)a.nsplit * a.Hr));
     j = a.ret_kv[r];
     nsplit = a.nsplit;
-    const int n = a.seq_len[b];
-    constexpr int kQuant = kWaves * kTpw;
-    int chunk = (n + nsplit - 1) / nsplit;
-    chunk = (chunk + kQuant - 1) / kQuant * kQuant;
+    const int n = a.n[b];
+    const int chunk = (n + nsplit - 1) / nsplit;
     t0 = split * chunk;
     t1 = min(n, t0 + chunk);
     head_row0 = ((int64_t)b * a.Hr + r) * a.cap;
@@ -204,7 +210,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
     j = a.str_kv[s];
     split = 0;
     nsplit = 1;
-    const int n = a.seq_len[b];
+    const int n = a.n[b];
     t0 = 0;
     t1 = min(n, a.S + a.R);
     head_row0 = ((int64_t)b * a.Hs + s) * (a.S + a.R);
@@ -225,60 +231,81 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
       for (int c = 0; c < Geo::kCpl; ++c)
         q.q[g][c] = *(const uint4*)(qb + (int64_t)g * RB + (sub + LPT * c) * 16);
   }
+  const float c2 = a.scale_log2;  // logit in log2 units = dot * c2 (c2 > 0)
+  const float inv_c2 = 1.f / c2;
 
-  float m[G], l[G], o[G][E];
+  // m: running maximum (log2 units) of this lane group; thr: the raw dot product above which
+  // the maximum must move ((m + kTau) / c2), so the hot path compares unscaled dots.
+  float m[G], thr[G], l[G], o[G][E];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    m[g] = kNegInf;
+    m[g] = kMInit;
+    thr[g] = kMInit;
     l[g] = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e) o[g][e] = 0.f;
   }
 
-  // ---- main loop: token groups of 8, interleaved over the waves, prefetched ---------------
+  // One step: the tokens of this lane group's row (masked past the end of the item).
+  auto process = [&](const F& f, int cur) {
+    const bool valid = t0 + (cur * kWaves + wave) * kTpw + grp < t1;
+    float dz[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      dz[g] = group_sum<LPT>(dot_partial<T, D, G, LPT>(f, q, g));
+      dz[g] = valid ? dz[g] : kNegInf;
+    }
+    bool need = false;
+#pragma unroll
+    for (int g = 0; g < G; ++g) need |= dz[g] > thr[g];
+    if (need) {  // rare after the first token of the group: move the running maximum
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        if (dz[g] > thr[g]) {
+          const float mn = dz[g] * c2;
+          const float al = fexp2(m[g] - mn);
+          l[g] *= al;
+#pragma unroll
+          for (int e = 0; e < E; ++e) o[g][e] *= al;
+          m[g] = mn;
+          thr[g] = (mn + kTau) * inv_c2;
+        }
+      }
+    }
+    float p[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      p[g] = fexp2(__builtin_fmaf(dz[g], c2, -m[g]));
+      l[g] += p[g];
+    }
+    accumulate_pv<T, D, G, LPT>(f, p, o);
+  };
+
+  // ---- main loop: token groups interleaved over the waves, NS register slots -------------
   if (t1 > t0) {
-    const int n_it = (t1 - t0 + kWaves * kTpw - 1) / (kWaves * kTpw);
+    const int n_it = (t1 - t0 + kTpb - 1) / kTpb;  // steps, the last possibly partial
     auto row_of = [&](int it) -> int64_t {
-      int t = t0 + (it * kWaves + wave) * kTpw + grp;
+      const int t = t0 + (it * kWaves + wave) * kTpw + grp;
       return (int64_t)(t < t1 ? t : t1 - 1);  // clamped: always inside this head's rows
     };
-    // kStages register slots rotate: slot s is consumed, then refilled with the group
-    // kStages steps ahead, so kStages - 1 groups stay in flight while one is processed.
-    // Loads are unconditional (rows past the end are clamped to the item's last row), which
-    // keeps the compiler's wait counts exact across the loop back-edge.
-    Frag<T, D, LPT> buf[kStages];
-#pragma unroll
-    for (int s = 0; s < kStages; ++s) load_frag<T, D, LPT>(buf[s], kbase, vbase, row_of(s), sub);
+    // Separate variables (not an array) so that the compiler rotates the slots without
+    // copies; loads are unconditional so its wait counts stay exact across the back-edge.
+    F f0, f1, f2, f3;
+    load_frag<T, D, LPT>(f0, kbase, vbase, row_of(0), sub);
+    load_frag<T, D, LPT>(f1, kbase, vbase, row_of(1), sub);
+    load_frag<T, D, LPT>(f2, kbase, vbase, row_of(2), sub);
+    if constexpr (NS == 4) load_frag<T, D, LPT>(f3, kbase, vbase, row_of(3), sub);
 
-    for (int it = 0; it < n_it; it += kStages) {
-#pragma unroll
-      for (int s = 0; s < kStages; ++s) {
-        const int cur = it + s;
-        const bool valid = t0 + (cur * kWaves + wave) * kTpw + grp < t1;
-        float z[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          z[g] = group_sum<LPT>(dot_partial<T, D, G, LPT>(buf[s], q, g)) * a.scale_log2;
-          if (!valid) z[g] = kNegInf;
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          if (z[g] > m[g] + kTau) {  // new running maximum for this lane group
-            const float al = fexp2(m[g] - z[g]);
-            l[g] *= al;
-#pragma unroll
-            for (int e = 0; e < E; ++e) o[g][e] *= al;
-            m[g] = z[g];
-          }
-        }
-        float p[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          p[g] = valid ? fexp2(z[g] - m[g]) : 0.f;
-          l[g] += p[g];
-        }
-        accumulate_pv<T, D, G, LPT>(buf[s], p, o);
-        load_frag<T, D, LPT>(buf[s], kbase, vbase, row_of(cur + kStages), sub);
+    for (int it = 0; it < n_it; it += NS) {
+      process(f0, it);
+      load_frag<T, D, LPT>(f0, kbase, vbase, row_of(it + NS), sub);
+      process(f1, it + 1);
+      load_frag<T, D, LPT>(f1, kbase, vbase, row_of(it + NS + 1), sub);
+      process(f2, it + 2);
+      load_frag<T, D, LPT>(f2, kbase, vbase, row_of(it + NS + 2), sub);
+      if constexpr (NS == 4) {
+        process(f3, it + 3);
+        load_frag<T, D, LPT>(f3, kbase, vbase, row_of(it + NS + 3), sub);
       }
     }
   }
@@ -290,7 +317,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
     if constexpr (LPT == 8) mx = fmaxf(mx, dpp<0x128>(mx));  // row_ror:8 -> lane ^ 8
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float sc = (m[g] == kNegInf) ? 0.f : fexp2(m[g] - mx);
+    const float sc = fexp2(m[g] - mx);
     float lg = l[g] * sc;
     if constexpr (LPT == 8) lg += dpp<0x128>(lg);
     lg += __shfl_xor(lg, 16);
@@ -320,13 +347,13 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
   // ---- merge the waves; finish or write this split's partial ------------------------------
   for (int idx = tid; idx < G * D; idx += kThreads) {
     const int g = idx / D, d = idx % D;
-    float M = kNegInf;
+    float M = kMInit;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][g]);
     float L = 0.f, O = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float sc = (s_m[w][g] == kNegInf) ? 0.f : fexp2(s_m[w][g] - M);
+      const float sc = fexp2(s_m[w][g] - M);
       L += s_l[w][g] * sc;
       O += s_o[w][g][d] * sc;
     }
@@ -344,55 +371,123 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
       }
     }
   }
-  if (nsplit == 1) return;
+}
 
-  // ---- last block of (b, j) merges the splits ----------------------------------------------
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned ticket = atomicAdd(&a.counters[(int64_t)b * a.Hkv + j], 1u);
-    s_last = (ticket == (unsigned)(nsplit - 1));
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+// Merge of the context splits of one retrieval query head (sequence b, head h): one wave
+// per 64 output columns, one pass over the splits with an online log-sum-exp
+// (M = max_s m_s, L = sum_s l_s exp2(m_s - M), out = sum_s o_s exp2(m_s - M) / L,
+// lse = (M + log2 L) ln 2). The loads of kMergeBatch splits are issued together, so the
+// wave waits on memory about once per batch. Empty splits (m = kMInit, l = 0) weigh zero.
+// A separate launch: the partials are visible without fences.
+constexpr int kMergeThreads = 64;
+constexpr int kMergeBatch = 16;
 
-  for (int idx = tid; idx < G * D; idx += kThreads) {
-    const int g = idx / D, d = idx % D;
-    const int h = h0 + g;
-    const int64_t p0 = ((int64_t)b * a.Hq + h) * a.max_splits;
-    float M = kNegInf;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, a.part_ml[(p0 + s) * 2]);
-    float L = 0.f, O = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float ms = a.part_ml[(p0 + s) * 2];
-      const float sc = (ms == kNegInf) ? 0.f : fexp2(ms - M);
-      L += a.part_ml[(p0 + s) * 2 + 1] * sc;
-      O += a.part_o[(p0 + s) * D + d] * sc;
+template <typename T, int D, int G>
+__global__ void __launch_bounds__(kMergeThreads) merge_kernel(DecodeArgs a) {
+  constexpr int kSlices = D / 64;
+  const int lane = threadIdx.x;
+  const int slice = blockIdx.x % kSlices;
+  const int qi = blockIdx.x / kSlices;  // (b, retrieval index, g)
+  const int g = qi % G;
+  const int r = (qi / G) % a.Hr;
+  const int b = qi / (G * a.Hr);
+  const int h = a.ret_kv[r] * G + g;
+  const int nsplit = a.nsplit;
+  const int64_t p0 = ((int64_t)b * a.Hq + h) * a.max_splits;
+  const int d = slice * 64 + lane;
+  const float* po = a.part_o + p0 * D + d;
+  const float2* pml = reinterpret_cast<const float2*>(a.part_ml) + p0;
+
+  float M = kMInit, L = 0.f, O = 0.f;
+  for (int s0 = 0; s0 < nsplit; s0 += kMergeBatch) {
+    float2 ml[kMergeBatch];
+    float ov[kMergeBatch];
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      const int sp = s0 + i < nsplit ? s0 + i : nsplit - 1;  // clamped; extra ones weigh 0
+      ml[i] = pml[sp];
+      ov[i] = po[(int64_t)sp * D];
     }
-    const int64_t oi = ((int64_t)b * a.Hq + h) * D + d;
-    store_out<T>(a.out, oi, O / L, a.out_f32);
-    if (d == 0 && a.lse) a.lse[(int64_t)b * a.Hq + h] = (M + __builtin_log2f(L)) * kLn2;
+    float bm = M;
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i)
+      if (s0 + i < nsplit) bm = fmaxf(bm, ml[i].x);
+    const float sc = fexp2(M - bm);
+    L *= sc;
+    O *= sc;
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      const float w = (s0 + i < nsplit) ? fexp2(ml[i].x - bm) : 0.f;
+      L = __builtin_fmaf(w, ml[i].y, L);
+      O = __builtin_fmaf(w, ov[i], O);
+    }
+    M = bm;
   }
-  if (tid == 0) atomicExch(&a.counters[(int64_t)b * a.Hkv + j], 0u);
+  store_out<T>(a.out, ((int64_t)b * a.Hq + h) * D + d, O / L, a.out_f32);
+  if (slice == 0 && lane == 0 && a.lse)
+    a.lse[(int64_t)b * a.Hq + h] = (M + __builtin_log2f(L)) * kLn2;
 }
 
 template <typename T, int D, int G>
-int launch_t(const DecodeArgs& a, void* stream) {
-  const int64_t blocks = (int64_t)a.B * a.Hr * a.nsplit + (int64_t)a.B * a.Hs;
-  constexpr int LPT = lanes_per_token<T, D, G>();
-  hipLaunchKernelGGL((decode_kernel<T, D, G, LPT>), dim3((unsigned)blocks), dim3(kThreads), 0,
-                     (hipStream_t)stream, a);
-  return (int)hipGetLastError();
+struct Variant {
+  static constexpr int LPT = lanes_per_token<T, D, G>();
+  static constexpr int NS = stages<T, D, G>();
+
+  // Decode blocks that fit on the device at once, queried once per process.
+  static int resident_blocks() {
+    static int cached = 0;
+    if (cached) return cached;
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(&decode_kernel<T, D, G, LPT, NS>), kThreads,
+            0) != hipSuccess ||
+        cus <= 0 || per_cu <= 0) {
+      (void)hipGetLastError();
+      return 512;
+    }
+    cached = cus * per_cu;
+    return cached;
+  }
+
+  static int launch(const DecodeArgs& a, void* stream) {
+    const int64_t blocks = (int64_t)a.B * a.Hr * a.nsplit + (int64_t)a.B * a.Hs;
+    hipLaunchKernelGGL((decode_kernel<T, D, G, LPT, NS>), dim3((unsigned)blocks),
+                       dim3(kThreads), 0, (hipStream_t)stream, a);
+    if (a.nsplit > 1 && a.Hr > 0) {
+      const int64_t mblocks = (int64_t)a.B * a.Hr * G * (D / 64);
+      hipLaunchKernelGGL((merge_kernel<T, D, G>), dim3((unsigned)mblocks),
+                         dim3(kMergeThreads), 0, (hipStream_t)stream, a);
+    }
+    return (int)hipGetLastError();
+  }
+};
+
+template <typename T, int D, int G>
+int run(bool query, const DecodeArgs* a, void* stream) {
+  return query ? Variant<T, D, G>::resident_blocks() : Variant<T, D, G>::launch(*a, stream);
 }
 
 template <typename T, int D>
-int launch_g(const DecodeArgs& a, int group, void* stream) {
+int dispatch_g(int group, bool query, const DecodeArgs* a, void* stream) {
   switch (group) {
-    case 1: return launch_t<T, D, 1>(a, stream);
-    case 2: return launch_t<T, D, 2>(a, stream);
-    case 4: return launch_t<T, D, 4>(a, stream);
-    case 8: return launch_t<T, D, 8>(a, stream);
+    case 1: return run<T, D, 1>(query, a, stream);
+    case 2: return run<T, D, 2>(query, a, stream);
+    case 4: return run<T, D, 4>(query, a, stream);
+    case 8: return run<T, D, 8>(query, a, stream);
+  }
+  return -1;
+}
+
+int dispatch(int dtype, int head_dim, int group, bool query, const DecodeArgs* a,
+             void* stream) {
+  if (dtype == DUO_BF16) {
+    if (head_dim == 128) return dispatch_g<uint16_t, 128>(group, query, a, stream);
+    if (head_dim == 64) return dispatch_g<uint16_t, 64>(group, query, a, stream);
+  } else {
+    if (head_dim == 128) return dispatch_g<float, 128>(group, query, a, stream);
+    if (head_dim == 64) return dispatch_g<float, 64>(group, query, a, stream);
   }
   return -1;
 }
@@ -400,14 +495,11 @@ int launch_g(const DecodeArgs& a, int group, void* stream) {
 }  // namespace
 
 int launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group, void* stream) {
-  if (dtype == DUO_BF16) {
-    if (head_dim == 128) return launch_g<uint16_t, 128>(a, group, stream);
-    if (head_dim == 64) return launch_g<uint16_t, 64>(a, group, stream);
-  } else {
-    if (head_dim == 128) return launch_g<float, 128>(a, group, stream);
-    if (head_dim == 64) return launch_g<float, 64>(a, group, stream);
-  }
-  return -1;
+  return dispatch(dtype, head_dim, group, false, &a, stream);
+}
+
+int decode_resident_blocks(int dtype, int head_dim, int group) {
+  return dispatch(dtype, head_dim, group, true, nullptr, nullptr);
 }
 
 }  // namespace duo

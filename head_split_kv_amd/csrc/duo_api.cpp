@@ -49,22 +49,19 @@ LayerPtrs layer_ptrs(duo_cache* c, int32_t layer) {
   return p;
 }
 
+// Split-K partials of the decode kernel: o [B][Hq][max_splits][D], then (m, l) pairs.
 struct Workspace {
   float* part_o;
   float* part_ml;
-  uint32_t* counters;
 };
 
 Workspace workspace(duo_cache* c) {
   const uint64_t B = c->cfg.batch, Hq = c->cfg.num_q_heads, D = c->cfg.head_dim;
-  const uint64_t S = c->cfg.max_splits, Hkv = c->cfg.num_kv_heads;
-  auto al = [](uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; };
+  const uint64_t S = c->cfg.max_splits;
   char* base = c->arena + c->lay.workspace_off;
   Workspace w;
   w.part_o = (float*)base;
-  w.part_ml = (float*)(base + al(B * Hq * S * D * 4));
-  w.counters = (uint32_t*)(base + al(B * Hq * S * D * 4) + al(B * Hq * S * 2 * 4));
-  (void)Hkv;
+  w.part_ml = (float*)(base + (B * Hq * S * D * 4 + kAlign - 1) / kAlign * kAlign);
   return w;
 }
 
@@ -81,8 +78,6 @@ duo_status duo_cache_reset(duo_cache* c, void* stream) {
   a.n_slot = (int64_t)(L * B * SR);
   a.seq_len = (int32_t*)(c->arena + c->lay.seq_len_off);
   a.n_len = (int64_t)(L * B);
-  a.counters = workspace(c).counters;
-  a.n_cnt = (int64_t)(B * c->cfg.num_kv_heads);
   if (launch_reset(a, stream) != 0) return DUO_ERR_HIP;
   std::fill(c->lens.begin(), c->lens.end(), 0);
   return DUO_OK;
@@ -148,10 +143,9 @@ duo_status duo_attn_decode(duo_cache* c, int32_t layer, const void* q, void* out
   a.full_v = p.full_v;
   a.str_k = p.str_k;
   a.str_v = p.str_v;
-  a.seq_len = p.seq_len;
+  for (int32_t b = 0; b < c->cfg.batch; ++b) a.n[b] = len_of(c, layer, b);
   a.part_o = w.part_o;
   a.part_ml = w.part_ml;
-  a.counters = w.counters;
   a.B = c->cfg.batch;
   a.Hq = c->cfg.num_q_heads;
   a.Hkv = c->cfg.num_kv_heads;
@@ -161,13 +155,16 @@ duo_status duo_attn_decode(duo_cache* c, int32_t layer, const void* q, void* out
   a.S = c->cfg.sink;
   a.R = c->cfg.recent;
   a.max_splits = c->cfg.max_splits;
-  a.nsplit = c->force_splits ? c->force_splits
-                             : choose_decode_splits(n_max, a.B, a.Hr, a.max_splits);
+  const int group = c->cfg.num_q_heads / c->cfg.num_kv_heads;
+  a.nsplit = c->force_splits
+                 ? c->force_splits
+                 : choose_decode_splits(n_max, a.B, a.Hr, a.Hs, a.max_splits,
+                                        decode_resident_blocks(c->cfg.dtype, c->cfg.head_dim,
+                                                               group));
   a.scale_log2 = (float)((double)c->scale * 1.4426950408889634);
   a.out_f32 = c->cfg.out_dtype == DUO_F32;
   std::memcpy(a.ret_kv, li.ret_kv, sizeof(a.ret_kv));
   std::memcpy(a.str_kv, li.str_kv, sizeof(a.str_kv));
-  const int group = c->cfg.num_q_heads / c->cfg.num_kv_heads;
   if (launch_decode(a, c->cfg.dtype, c->cfg.head_dim, group, stream) != 0) return DUO_ERR_HIP;
   return DUO_OK;
 }

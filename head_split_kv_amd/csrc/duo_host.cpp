@@ -89,8 +89,7 @@ duo_status build_layout(const duo_config* cfg, duo_layout* lay, std::vector<Laye
   out.slot_pos_off = off; off = align_up(off + L * B * SR * 4);
   out.seq_len_off = off;  off = align_up(off + L * B * 4);
   out.workspace_off = off;
-  const uint64_t ws = align_up(B * Hq * splits * D * 4) + align_up(B * Hq * splits * 2 * 4) +
-                      align_up(B * Hkv * 4);
+  const uint64_t ws = align_up(B * Hq * splits * D * 4) + align_up(B * Hq * splits * 2 * 4);
   out.workspace_bytes = ws;
   off = align_up(off + ws);
   out.arena_bytes = off;
@@ -98,15 +97,19 @@ duo_status build_layout(const duo_config* cfg, duo_layout* lay, std::vector<Laye
   return DUO_OK;
 }
 
-int choose_decode_splits(int32_t n_max, int32_t batch, int32_t n_ret, int32_t max_splits) {
-  // Enough work items to give every one of the 256 compute units several blocks, but no
-  // split shorter than a few hundred tokens (each split costs one partial write and merge).
-  constexpr int64_t kTargetBlocks = 1024;
-  constexpr int64_t kMinTokens = 256;
+int choose_decode_splits(int32_t n_max, int32_t batch, int32_t n_ret, int32_t n_str,
+                         int32_t max_splits, int32_t resident_blocks) {
+  // One round of resident blocks: the streaming items take one block each and the retrieval
+  // heads share the rest evenly, so no block waits for a second round; no split is made
+  // shorter than kMinTokens (each split costs one partial write and one merge read).
+  constexpr int64_t kMinTokens = 128;
   if (n_ret <= 0 || n_max <= 0) return 1;
-  int64_t by_work = (kTargetBlocks + (int64_t)batch * n_ret - 1) / ((int64_t)batch * n_ret);
-  int64_t by_len = (n_max + kMinTokens - 1) / kMinTokens;
-  int64_t s = by_work < by_len ? by_work : by_len;
+  const int64_t ret_items = (int64_t)batch * n_ret;
+  int64_t avail = (int64_t)resident_blocks - (int64_t)batch * n_str;
+  if (avail < ret_items) avail = ret_items;
+  int64_t s = avail / ret_items;
+  const int64_t by_len = (n_max + kMinTokens - 1) / kMinTokens;
+  if (s > by_len) s = by_len;
   if (s < 1) s = 1;
   if (s > max_splits) s = max_splits;
   return (int)s;

@@ -11,7 +11,7 @@ namespace duo {
 
 constexpr int kMaxKvHeads = 64;
 constexpr int kMaxBatch = 512;
-constexpr int kDefaultSplits = 128;
+constexpr int kDefaultSplits = 256;
 constexpr int kMaxSplits = 1024;
 constexpr uint64_t kAlign = 256;
 
@@ -35,8 +35,6 @@ struct ResetArgs {
   int64_t n_slot;
   int32_t* seq_len;    // [n_len] -> 0
   int64_t n_len;
-  uint32_t* counters;  // [n_cnt] -> 0
-  int64_t n_cnt;
 };
 
 struct AppendArgs {
@@ -62,15 +60,14 @@ struct DecodeArgs {
   const void* full_v;
   const void* str_k;
   const void* str_v;
-  const int32_t* seq_len;  // this layer: [B]
   float* part_o;           // [B][Hq][max_splits][D]
   float* part_ml;          // [B][Hq][max_splits][2]
-  uint32_t* counters;      // [B][Hkv]
   int32_t B, Hq, Hkv, Hr, Hs, cap, S, R, nsplit, max_splits;
   float scale_log2;        // softmax scale * log2(e)
   int32_t out_f32;
   uint8_t ret_kv[kMaxKvHeads];
   uint8_t str_kv[kMaxKvHeads];
+  int32_t n[kMaxBatch];    // current length of every sequence (host mirror)
 };
 
 struct PrefillArgs {
@@ -96,12 +93,15 @@ int launch_reset(const ResetArgs& a, void* stream);
 int launch_append(const AppendArgs& a, int dtype, void* stream);
 int launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group, void* stream);
 int launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int group, void* stream);
+// Decode blocks of this variant that are resident on the device at once (512 if unknown).
+int decode_resident_blocks(int dtype, int head_dim, int group);
 
 // Host-side helpers (duo_host.cpp)
 int element_size(int32_t dtype);
 duo_status check_config(const duo_config* cfg);
 duo_status build_layout(const duo_config* cfg, duo_layout* lay, std::vector<LayerInfo>* layers);
-int choose_decode_splits(int32_t n_max, int32_t batch, int32_t n_ret, int32_t max_splits);
+int choose_decode_splits(int32_t n_max, int32_t batch, int32_t n_ret, int32_t n_str,
+                         int32_t max_splits, int32_t resident_blocks);
 
 }  // namespace duo
 

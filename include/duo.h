@@ -19,7 +19,7 @@
  *   unspecified). Faults inside kernels surface asynchronously, as in any stream API.
  * - Device work is enqueued on `stream` (a hipStream_t; NULL is the default stream) and is
  *   asynchronous; only duo_slot_positions synchronizes. Calls on one cache must be ordered
- *   on one stream: they share the cache's split-K workspace and counters.
+ *   on one stream: decode calls share the cache's split-K workspace.
  * - The library never allocates or frees device memory. The caller owns the arena and every
  *   input/output buffer; all device pointers must stay valid until the work completes.
  * - Layouts are row-major and contiguous in the native head order of the model:
@@ -67,12 +67,14 @@ typedef struct {
   int32_t dtype;           /* duo_dtype of q, k, v and the caches */
   int32_t out_dtype;       /* duo_dtype of out */
   float softmax_scale;     /* <= 0 selects 1/sqrt(head_dim) */
-  int32_t max_splits;      /* split-K workspace per (sequence, query head); 0 selects 128 */
+  int32_t max_splits;      /* split-K workspace per (sequence, query head), <= 1024;
+                              0 selects 256 */
   const uint8_t* retrieval_mask; /* host [num_layers][num_kv_heads], nonzero = retrieval;
                                     copied by duo_cache_create */
 } duo_config;
 
-/* Byte offsets inside the caller's arena (all 256-byte aligned). */
+/* Byte offsets inside the caller's arena (all 256-byte aligned). Inside each cache region
+ * the layers follow one another in order, each starting on a 256-byte boundary. */
 typedef struct {
   uint64_t arena_bytes;
   uint64_t full_k_off;     /* retrieval caches: per layer [B][H_r][capacity][d] */
@@ -81,7 +83,7 @@ typedef struct {
   uint64_t str_v_off;
   uint64_t slot_pos_off;   /* int32 [L][B][S+R]: position held by each slot, -1 = empty */
   uint64_t seq_len_off;    /* int32 [L][B]: tokens appended so far */
-  uint64_t workspace_off;  /* split-K partials and merge counters */
+  uint64_t workspace_off;  /* split-K partials of the decode */
   uint64_t workspace_bytes;
 } duo_layout;
 
@@ -100,7 +102,7 @@ duo_status duo_layout_query(const duo_config* cfg, duo_layout* out);
 duo_status duo_cache_create(const duo_config* cfg, void* arena, uint64_t arena_bytes,
                             duo_cache** out);
 
-/* Empty every sequence of every layer: lengths 0, slot table -1, merge counters 0.
+/* Empty every sequence of every layer: lengths 0, slot table -1.
  * Enqueues one fill kernel on `stream` (no memset node, so it can be graph-captured). */
 duo_status duo_cache_reset(duo_cache* cache, void* stream);
 

@@ -178,7 +178,7 @@ def test_error_paths_leave_state_unchanged():
     assert L.duo_attn_prefill(fc.h, 0, 0, p, mis, p, 4, p, None, None) == N.DUO_ERR_INVALID
     assert L.duo_slot_positions(fc.h, 9, None, None) == N.DUO_ERR_INVALID
     assert L.duo_set_decode_splits(fc.h, -1) == N.DUO_ERR_INVALID
-    assert L.duo_set_decode_splits(fc.h, 129) == N.DUO_ERR_INVALID
+    assert L.duo_set_decode_splits(fc.h, 257) == N.DUO_ERR_INVALID
     assert L.duo_set_decode_splits(fc.h, 7) == N.DUO_OK
     assert np.array_equal(fc.lengths(), before)
     assert L.duo_cache_destroy(None) == N.DUO_OK
