@@ -34,6 +34,7 @@ class DuoConfig(ctypes.Structure):
         ("out_dtype", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float),
         ("max_splits", ctypes.c_int32),
+        ("prefill_tiles", ctypes.c_int32),
         ("retrieval_mask", ctypes.POINTER(ctypes.c_uint8)),
     ]
 

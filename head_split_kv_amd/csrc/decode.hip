@@ -373,19 +373,22 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
   }
 }
 
-// Merge of the context splits of one retrieval query head (sequence b, head h): one wave
-// per 64 output columns, one pass over the splits with an online log-sum-exp
-// (M = max_s m_s, L = sum_s l_s exp2(m_s - M), out = sum_s o_s exp2(m_s - M) / L,
-// lse = (M + log2 L) ln 2). The loads of kMergeBatch splits are issued together, so the
-// wave waits on memory about once per batch. Empty splits (m = kMInit, l = 0) weigh zero.
-// A separate launch: the partials are visible without fences.
-constexpr int kMergeThreads = 64;
+// Merge of the context splits of one retrieval query head (sequence b, head h) over 64
+// output columns: M = max_s m_s, L = sum_s l_s exp2(m_s - M), out = sum_s o_s exp2(m_s - M)
+// / L, lse = (M + log2 L) ln 2. Each of the 8 waves takes every 8th split with an online
+// log-sum-exp, issuing the loads of kMergeBatch splits together, and the waves combine
+// through LDS; with up to 128 splits every wave waits on memory once. Empty splits
+// (m = kMInit, l = 0) weigh zero. A separate launch: the partials need no fences.
+constexpr int kMergeWaves = 8;
+constexpr int kMergeThreads = kMergeWaves * 64;
 constexpr int kMergeBatch = 16;
 
 template <typename T, int D, int G>
 __global__ void __launch_bounds__(kMergeThreads) merge_kernel(DecodeArgs a) {
+  __shared__ float s_m[kMergeWaves], s_l[kMergeWaves];
+  __shared__ float s_o[kMergeWaves][64];
   constexpr int kSlices = D / 64;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int slice = blockIdx.x % kSlices;
   const int qi = blockIdx.x / kSlices;  // (b, retrieval index, g)
   const int g = qi % G;
@@ -399,33 +402,51 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(DecodeArgs a) {
   const float2* pml = reinterpret_cast<const float2*>(a.part_ml) + p0;
 
   float M = kMInit, L = 0.f, O = 0.f;
-  for (int s0 = 0; s0 < nsplit; s0 += kMergeBatch) {
+  for (int s0 = wave; s0 < nsplit; s0 += kMergeWaves * kMergeBatch) {
     float2 ml[kMergeBatch];
     float ov[kMergeBatch];
 #pragma unroll
     for (int i = 0; i < kMergeBatch; ++i) {
-      const int sp = s0 + i < nsplit ? s0 + i : nsplit - 1;  // clamped; extra ones weigh 0
-      ml[i] = pml[sp];
-      ov[i] = po[(int64_t)sp * D];
+      const int sp = s0 + kMergeWaves * i;
+      const int spc = sp < nsplit ? sp : nsplit - 1;  // clamped; the extra ones weigh 0
+      ml[i] = pml[spc];
+      ov[i] = po[(int64_t)spc * D];
     }
     float bm = M;
 #pragma unroll
     for (int i = 0; i < kMergeBatch; ++i)
-      if (s0 + i < nsplit) bm = fmaxf(bm, ml[i].x);
+      if (s0 + kMergeWaves * i < nsplit) bm = fmaxf(bm, ml[i].x);
     const float sc = fexp2(M - bm);
     L *= sc;
     O *= sc;
 #pragma unroll
     for (int i = 0; i < kMergeBatch; ++i) {
-      const float w = (s0 + i < nsplit) ? fexp2(ml[i].x - bm) : 0.f;
+      const float w = (s0 + kMergeWaves * i < nsplit) ? fexp2(ml[i].x - bm) : 0.f;
       L = __builtin_fmaf(w, ml[i].y, L);
       O = __builtin_fmaf(w, ov[i], O);
     }
     M = bm;
   }
-  store_out<T>(a.out, ((int64_t)b * a.Hq + h) * D + d, O / L, a.out_f32);
+  s_o[wave][lane] = O;
+  if (lane == 0) {
+    s_m[wave] = M;
+    s_l[wave] = L;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float Mt = kMInit;
+#pragma unroll
+  for (int w = 0; w < kMergeWaves; ++w) Mt = fmaxf(Mt, s_m[w]);
+  float Lt = 0.f, Ot = 0.f;
+#pragma unroll
+  for (int w = 0; w < kMergeWaves; ++w) {
+    const float sc = fexp2(s_m[w] - Mt);
+    Lt = __builtin_fmaf(sc, s_l[w], Lt);
+    Ot = __builtin_fmaf(sc, s_o[w][lane], Ot);
+  }
+  store_out<T>(a.out, ((int64_t)b * a.Hq + h) * D + d, Ot / Lt, a.out_f32);
   if (slice == 0 && lane == 0 && a.lse)
-    a.lse[(int64_t)b * a.Hq + h] = (M + __builtin_log2f(L)) * kLn2;
+    a.lse[(int64_t)b * a.Hq + h] = (Mt + __builtin_log2f(Lt)) * kLn2;
 }
 
 template <typename T, int D, int G>

@@ -208,8 +208,25 @@ duo_status duo_attn_prefill(duo_cache* c, int32_t layer, int32_t seq, const void
   a.scale_log2 = (float)((double)c->scale * 1.4426950408889634);
   a.out_f32 = c->cfg.out_dtype == DUO_F32;
   std::memcpy(a.cls_idx, li.cls_idx, sizeof(a.cls_idx));
-  for (int32_t i = 0; i < nb; ++i) a.c0[i] = len_of(c, layer, b0 + i);
+  std::memcpy(a.ret_kv, li.ret_kv, sizeof(a.ret_kv));
+  std::memcpy(a.str_kv, li.str_kv, sizeof(a.str_kv));
+  int32_t c_max = 0, c_sum = 0;
+  for (int32_t i = 0; i < nb; ++i) {
+    a.c0[i] = len_of(c, layer, b0 + i);
+    c_max = std::max(c_max, a.c0[i]);
+    c_sum += a.c0[i];
+  }
   const int group = c->cfg.num_q_heads / c->cfg.num_kv_heads;
+  const int qpb = kPrefillRows / group;
+  a.n_qt = (n_chunk + qpb - 1) / qpb;
+  a.nsplit = choose_prefill_splits(nb, n_chunk, c_max, c_sum, a.Hr, a.Hs, a.S, a.R, group,
+                                   c->cfg.prefill_tiles,
+                                   prefill_resident_blocks(c->cfg.head_dim, group));
+  const uint64_t D = c->cfg.head_dim;
+  char* ws = c->arena + c->lay.workspace_off;
+  a.part_o = (float*)ws;
+  a.part_ml = (float*)(ws + ((uint64_t)c->cfg.prefill_tiles * kPrefillRows * D * 4 + kAlign - 1) /
+                                kAlign * kAlign);
   const int rc = launch_prefill(a, c->cfg.dtype, c->cfg.head_dim, group, stream);
   if (rc == -1) return DUO_ERR_UNSUPPORTED;
   if (rc != 0) return DUO_ERR_HIP;

@@ -30,6 +30,7 @@ duo_status check_config(const duo_config* cfg) {
   if ((int64_t)cfg->sink + cfg->recent > (1 << 20)) return DUO_ERR_INVALID;
   if (cfg->capacity < 1) return DUO_ERR_INVALID;
   if (cfg->max_splits < 0 || cfg->max_splits > kMaxSplits) return DUO_ERR_INVALID;
+  if (cfg->prefill_tiles < 0 || cfg->prefill_tiles > kMaxPrefillTiles) return DUO_ERR_INVALID;
   if (!cfg->retrieval_mask) return DUO_ERR_INVALID;
   if (element_size(cfg->dtype) == 0 || element_size(cfg->out_dtype) == 0)
     return DUO_ERR_INVALID;
@@ -89,7 +90,11 @@ duo_status build_layout(const duo_config* cfg, duo_layout* lay, std::vector<Laye
   out.slot_pos_off = off; off = align_up(off + L * B * SR * 4);
   out.seq_len_off = off;  off = align_up(off + L * B * 4);
   out.workspace_off = off;
-  const uint64_t ws = align_up(B * Hq * splits * D * 4) + align_up(B * Hq * splits * 2 * 4);
+  const uint64_t ptiles = cfg->prefill_tiles ? cfg->prefill_tiles : kDefaultPrefillTiles;
+  const uint64_t ws_decode = align_up(B * Hq * splits * D * 4) + align_up(B * Hq * splits * 2 * 4);
+  const uint64_t ws_prefill = align_up(ptiles * kPrefillRows * D * 4) +
+                              align_up(ptiles * kPrefillRows * 2 * 4);
+  const uint64_t ws = ws_decode > ws_prefill ? ws_decode : ws_prefill;
   out.workspace_bytes = ws;
   off = align_up(off + ws);
   out.arena_bytes = off;
@@ -112,6 +117,34 @@ int choose_decode_splits(int32_t n_max, int32_t batch, int32_t n_ret, int32_t n_
   if (s > by_len) s = by_len;
   if (s < 1) s = 1;
   if (s > max_splits) s = max_splits;
+  return (int)s;
+}
+
+int choose_prefill_splits(int32_t nb, int32_t m, int32_t c_max, int32_t c_sum, int32_t n_ret,
+                          int32_t n_str, int32_t sink, int32_t recent, int32_t group,
+                          int32_t prefill_tiles, int32_t resident_blocks) {
+  // Retrieval query tiles see the whole cache prefix, streaming ones a constant window.
+  // Cut the retrieval key ranges so that the heaviest piece is about the size of a
+  // streaming tile or of 1/2 of a resident round's share of the work, whichever is larger.
+  constexpr int64_t kBN = 64;
+  if (n_ret <= 0 || m <= 0) return 1;
+  const int64_t qpb = kPrefillRows / group;
+  const int64_t n_qt = (m + qpb - 1) / qpb;
+  const int64_t chunk_tiles_avg = ((int64_t)m + 2 * kBN - 1) / (2 * kBN);
+  const int64_t t_ret_max = (c_max + kBN - 1) / kBN + (m + kBN - 1) / kBN;
+  const int64_t t_ret_avg = ((int64_t)c_sum / (nb > 0 ? nb : 1) + kBN - 1) / kBN + chunk_tiles_avg;
+  const int64_t sr = (int64_t)sink + recent;
+  int64_t t_str = (c_max > 0 ? (sr + kBN - 1) / kBN : 0) + (recent + qpb + kBN - 1) / kBN + 1;
+  if (t_str > (m + kBN - 1) / kBN + (sr + kBN - 1) / kBN) t_str = (m + kBN - 1) / kBN + (sr + kBN - 1) / kBN;
+  const int64_t work = (int64_t)nb * n_qt * ((int64_t)n_ret * t_ret_avg + (int64_t)n_str * t_str);
+  int64_t target = work / (2 * (int64_t)(resident_blocks > 0 ? resident_blocks : 512));
+  if (target < t_str) target = t_str;
+  if (target < 4) target = 4;
+  int64_t s = (t_ret_max + target - 1) / target;
+  if (s > 32) s = 32;
+  const int64_t items = (int64_t)nb * n_ret * n_qt;
+  if (s * items > prefill_tiles) s = prefill_tiles / items;
+  if (s < 1) s = 1;
   return (int)s;
 }
 
@@ -140,6 +173,7 @@ duo_status duo_cache_create(const duo_config* cfg, void* arena, uint64_t arena_b
   if (!c) return DUO_ERR_INVALID;
   c->cfg = *cfg;
   if (c->cfg.max_splits == 0) c->cfg.max_splits = kDefaultSplits;
+  if (c->cfg.prefill_tiles == 0) c->cfg.prefill_tiles = kDefaultPrefillTiles;
   const size_t nm = (size_t)cfg->num_layers * cfg->num_kv_heads;
   c->mask.assign(cfg->retrieval_mask, cfg->retrieval_mask + nm);
   for (auto& x : c->mask) x = x ? 1 : 0;

@@ -13,6 +13,9 @@ constexpr int kMaxKvHeads = 64;
 constexpr int kMaxBatch = 512;
 constexpr int kDefaultSplits = 256;
 constexpr int kMaxSplits = 1024;
+constexpr int kDefaultPrefillTiles = 2048;
+constexpr int kMaxPrefillTiles = 65536;
+constexpr int kPrefillRows = 128;  // query rows per prefill block (and per partial tile)
 constexpr uint64_t kAlign = 256;
 
 // Per-layer head partition. For KV head j: cls_idx[j] >= 0 is its index among the layer's
@@ -81,10 +84,16 @@ struct PrefillArgs {
   const void* str_k;
   const void* str_v;
   const int32_t* slot_pos;  // this layer: [B][S+R]
+  float* part_o;            // retrieval split-K partials [item][split][128][D] (nsplit > 1)
+  float* part_ml;           // [item][split][128][2]
   int32_t b0, nb, m, Hq, Hkv, Hr, Hs, cap, S, R;
+  int32_t n_qt;             // query tiles of 128 rows per (sequence, KV head)
+  int32_t nsplit;           // key-range splits of every retrieval query tile
   float scale_log2;
   int32_t out_f32;
   int16_t cls_idx[kMaxKvHeads];
+  uint8_t ret_kv[kMaxKvHeads];
+  uint8_t str_kv[kMaxKvHeads];
   int32_t c0[kMaxBatch];  // chunk start (current length) of each sequence b0 .. b0+nb-1
 };
 
@@ -95,6 +104,8 @@ int launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group, void*
 int launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int group, void* stream);
 // Decode blocks of this variant that are resident on the device at once (512 if unknown).
 int decode_resident_blocks(int dtype, int head_dim, int group);
+// Prefill blocks of this variant that are resident on the device at once (512 if unknown).
+int prefill_resident_blocks(int head_dim, int group);
 
 // Host-side helpers (duo_host.cpp)
 int element_size(int32_t dtype);
@@ -102,6 +113,9 @@ duo_status check_config(const duo_config* cfg);
 duo_status build_layout(const duo_config* cfg, duo_layout* lay, std::vector<LayerInfo>* layers);
 int choose_decode_splits(int32_t n_max, int32_t batch, int32_t n_ret, int32_t n_str,
                          int32_t max_splits, int32_t resident_blocks);
+int choose_prefill_splits(int32_t nb, int32_t m, int32_t c_max, int32_t c_sum, int32_t n_ret,
+                          int32_t n_str, int32_t sink, int32_t recent, int32_t group,
+                          int32_t prefill_tiles, int32_t resident_blocks);
 
 }  // namespace duo
 

@@ -8,20 +8,24 @@
 //
 // One block = 4 waves = 128 query rows of one (sequence, KV head): 128 / G positions times
 // the G query heads of the group, so every K/V tile staged in LDS serves the whole group
-// (no KV head is repeated). Per key tile of 64 keys a wave computes S^T = K Q^T with
-// v_mfma_f32_32x32x16_bf16 (keys as MFMA rows, so each lane owns one query and the softmax
-// row statistics stay in the lane and its partner lane l ^ 32), takes the online softmax in
-// fp32 (log2 domain, lazy rescale above kTau), splits P into two bf16 terms (hi + lo, about
-// 16 significant bits) and accumulates O^T += V^T P^T with the same MFMA; V is staged
-// transposed in LDS for that product. The key order inside a 16-key MFMA slab is permuted
-// identically in P and V^T, which matches the accumulator layout of the first product and
-// needs no data movement.
+// (no KV head is repeated). K and V tiles of 64 keys go straight from global memory into a
+// double-buffered LDS ring with global_load_lds_dwordx4 (no registers in flight), rows kept
+// in their global order with 16-byte chunks XOR-swizzled per row so that both LDS read
+// patterns below are free of bank conflicts. Per tile a wave computes S^T = K Q^T with
+// v_mfma_f32_32x32x16_bf16 (keys as MFMA rows, so each lane owns one query and its softmax
+// statistics stay in the lane and its partner lane l ^ 32), takes the online softmax in fp32
+// (log2 domain, lazy rescale above kTau), splits P into two bf16 terms (hi + lo, about 16
+// significant bits) and accumulates O^T += V^T P^T with the same MFMA. The V^T operand comes
+// from ds_read_b64_tr_b16, which transposes 4x16 blocks of the row-major tile on the way out
+// of LDS. The key order inside a 16-key MFMA slab is permuted identically in P and V^T,
+// matching the accumulator layout of the first product.
 //
 // Tiles are classified per block: skipped when no key is visible to any query of the block
 // (causally later, or outside every query's sink + recent window), computed without masks
-// when every key is visible to every query, and masked per element otherwise. Blocks of the
-// same (sequence, KV head) are placed on the same XCD so that its L2 serves their shared K/V
-// tiles, and query tiles with more keys start first.
+// when every key is visible to every query, and masked per element otherwise. Retrieval
+// query tiles, whose key range grows with the cache, are cut into `nsplit` key ranges run
+// by separate blocks that write fp32 partials (O, m, l) merged by a second kernel; the
+// heaviest query tiles are dispatched first.
 #include <hip/hip_runtime.h>
 
 #include "duo_internal.h"
@@ -31,9 +35,8 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kRows = 128;  // query rows (position, head) per block
-constexpr int kBN = 64;     // keys per tile
-constexpr int kXcds = 8;
+constexpr int kRows = kPrefillRows;  // query rows (position, head) per block
+constexpr int kBN = 64;              // keys per tile
 constexpr float kTau = 8.0f;
 constexpr float kMInit = -1e30f;
 constexpr float kNegInf = -__builtin_inff();
@@ -44,6 +47,9 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -64,56 +70,79 @@ __device__ __forceinline__ void split_bf16(float x, float y, uint32_t& hi, uint3
 template <int D>
 struct Geo {
   static constexpr int kRowBytes = D * 2;
-  static constexpr int kChunks = kRowBytes / 16;    // 16-byte chunks per K/V row
-  static constexpr int kKStride = kRowBytes + 16;   // LDS K row stride (padding vs conflicts)
-  static constexpr int kVStride = kBN * 2 + 8;      // LDS V^T row (one d) stride
-  static constexpr int kKLoads = kBN * kChunks / kThreads;         // 16-byte K loads/thread
-  static constexpr int kVTasks = (kBN / 2) * kChunks / kThreads;   // row pairs per thread
-  static constexpr int kSlabs = D / 16;             // MFMA K-slabs of the QK^T product
-  static constexpr int kDBlocks = D / 32;           // 32-wide d blocks of the output
+  static constexpr int kChunks = kRowBytes / 16;          // 16-byte chunks per K/V row
+  static constexpr int kTileBytes = kBN * kRowBytes;       // one K (or V) tile
+  static constexpr int kRowsPerKb = 1024 / kRowBytes;      // rows per 1 KB DMA instruction
+  static constexpr int kDmaPerWave = kTileBytes / 1024 / kWaves;
+  static constexpr int kSlabs = D / 16;                    // MFMA K-slabs of QK^T
+  static constexpr int kDBlocks = D / 32;                  // 32-wide d blocks of O
+  static_assert(kDmaPerWave >= 1, "tile must cover every wave");
 };
 
-enum TileKind : int { kFull = 0, kMasked = 1 };
+// Physical 16-byte chunk of logical chunk c in LDS row r: c ^ swz(r). With 16 chunks per
+// row (256 B, every row on the same banks) swz spreads the 16 rows of a K read over all
+// 16 chunk positions, and gives the 4 consecutive rows of a transposed V read distinct
+// aligned chunk pairs; with 8 chunks per row (128 B, rows alternate bank halves) the same
+// holds per half.
+template <int NCH>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (NCH == 16) return ((r & 7) << 1) | ((r >> 3) & 1);
+  else return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+}
 
 template <int D, int G>
 __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
   using Gm = Geo<D>;
+  constexpr int NCH = Gm::kChunks;
+  constexpr int RB = Gm::kRowBytes;
   constexpr int kQpb = kRows / G;  // positions per block
-  __shared__ __attribute__((aligned(16))) char sK[kBN * Gm::kKStride];
-  __shared__ __attribute__((aligned(16))) char sV[D * Gm::kVStride];
-  __shared__ int sPos[kBN];
+  __shared__ __attribute__((aligned(1024))) char sK0[Gm::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sK1[Gm::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sV0[Gm::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sV1[Gm::kTileBytes];
+  __shared__ int sPos0[kBN];
+  __shared__ int sPos1[kBN];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, col = lane & 31, half = lane >> 5;
 
-  // ---- block -> (sequence, KV head, query tile), XCD-aware ---------------------------------
-  const int n_qt = (a.m + kQpb - 1) / kQpb;
-  const int n_blocks = a.nb * a.Hkv * n_qt;
-  const int per_xcd = (n_blocks + kXcds - 1) / kXcds;
-  const int logical = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
-  if (logical >= n_blocks) return;
-  const int qt = n_qt - 1 - logical % n_qt;  // most keys first
-  const int j = (logical / n_qt) % a.Hkv;
-  const int bi = logical / (n_qt * a.Hkv);
+  // ---- block -> work item ------------------------------------------------------------
+  const int n_ret_blocks = a.nb * a.Hr * a.n_qt * a.nsplit;
+  int x = blockIdx.x, split = 0, nsplit = 1, qt, bi, j, cls;
+  if (x < n_ret_blocks) {
+    split = x % a.nsplit;
+    x /= a.nsplit;
+    cls = x % a.Hr;
+    x /= a.Hr;
+    bi = x % a.nb;
+    qt = a.n_qt - 1 - x / a.nb;  // most keys first
+    j = a.ret_kv[cls];
+    nsplit = a.nsplit;
+  } else {
+    x -= n_ret_blocks;
+    cls = x % a.Hs;
+    x /= a.Hs;
+    bi = x % a.nb;
+    qt = a.n_qt - 1 - x / a.nb;
+    j = a.str_kv[cls];
+  }
+  const bool retrieval = blockIdx.x < (unsigned)n_ret_blocks;
   const int b = a.b0 + bi;
   const int c0 = a.c0[bi];
-  const int ci = a.cls_idx[j];
-  const bool retrieval = ci >= 0;
   const int S = a.S, R = a.R, SR = a.S + a.R;
-  constexpr int RB = Gm::kRowBytes;
 
-  const int ql0 = qt * kQpb;                        // first local position of the tile
-  const int ql1 = min(a.m, ql0 + kQpb) - 1;         // last valid local position
+  const int ql0 = qt * kQpb;                 // first local position of the tile
+  const int ql1 = min(a.m, ql0 + kQpb) - 1;  // last valid local position
   const int p_min = c0 + ql0, p_max = c0 + ql1;
 
-  // this lane's query row (same row in lanes col and col + 32)
+  // this lane's query row (the same row in lanes col and col + 32)
   const int row = wave * 32 + col;
   const int q_local = ql0 + row / G;
   const int g = row % G;
   const bool q_valid = q_local < a.m;
   const int p = c0 + (q_valid ? q_local : ql1);
 
-  // ---- Q^T operand: 16-byte slabs of this lane's query row ------------------------------
+  // ---- Q^T operand: 16-byte slabs of this lane's query row --------------------------
   bf16x8_t qf[Gm::kSlabs];
   {
     const int ql = q_valid ? q_local : ql1;
@@ -123,165 +152,120 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
       qf[k] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(qrow + (16 * k + 8 * half) * 2));
   }
 
-  // ---- key tiles: cache part, then chunk part -----------------------------------------
+  // ---- key tiles: cache part, then chunk part ------------------------------------------
   int n_cache_tiles;
   const char* cache_k;
   const char* cache_v;
   const int32_t* slots = nullptr;
   if (retrieval) {
     n_cache_tiles = (c0 + kBN - 1) / kBN;
-    const int64_t base = ((int64_t)b * a.Hr + ci) * a.cap * RB;
+    const int64_t base = ((int64_t)b * a.Hr + cls) * a.cap * RB;
     cache_k = (const char*)a.full_k + base;
     cache_v = (const char*)a.full_v + base;
   } else {
-    const int s = -ci - 1;
     n_cache_tiles = c0 > 0 ? (SR + kBN - 1) / kBN : 0;
-    const int64_t base = ((int64_t)b * a.Hs + s) * SR * RB;
+    const int64_t base = ((int64_t)b * a.Hs + cls) * SR * RB;
     cache_k = (const char*)a.str_k + base;
     cache_v = (const char*)a.str_v + base;
     slots = a.slot_pos + (int64_t)b * SR;
   }
   const int n_chunk_tiles = ql1 / kBN + 1;  // causal limit: no key after the last query
   const int n_tiles = n_cache_tiles + n_chunk_tiles;
+  const int t_begin = (int)((int64_t)n_tiles * split / nsplit);
+  const int t_end = (int)((int64_t)n_tiles * (split + 1) / nsplit);
   const char* chunk_k = (const char*)a.k + ((int64_t)bi * a.m * a.Hkv + j) * RB;
   const char* chunk_v = (const char*)a.v + ((int64_t)bi * a.m * a.Hkv + j) * RB;
   const int64_t chunk_stride = (int64_t)a.Hkv * RB;
 
-  // Returns the tile's kind, or -1 if no key of it is visible to any query of the block.
+  // kind of tile ti: 0 = every key visible to every query, 1 = masked, -1 = skipped
   auto classify = [&](int ti) -> int {
     if (ti < n_cache_tiles) {
-      if (retrieval) return (ti + 1) * kBN <= c0 ? kFull : kMasked;
-      // streaming cache: only sink slots can be visible once the window is past the cache
+      if (retrieval) return (ti + 1) * kBN <= c0 ? 0 : 1;
+      // streaming cache: once every window starts past the cache only sink slots count
       if (ti * kBN >= S && p_min - R + 1 > c0 - 1) return -1;
-      return kMasked;
+      return 1;
     }
-    const int k0 = c0 + (ti - n_cache_tiles) * kBN;             // first key position
-    const int k1 = min(c0 + a.m, k0 + kBN) - 1;                  // last valid key position
-    const bool all_rows = k0 + kBN - 1 <= c0 + a.m - 1;
-    if (retrieval) return (all_rows && k1 <= p_min) ? kFull : kMasked;
-    if (k0 >= S && k1 < p_min - R + 1) return -1;               // left of every window
-    return (all_rows && k1 <= p_min && k0 >= p_max - R + 1) ? kFull : kMasked;
+    const int k0 = c0 + (ti - n_cache_tiles) * kBN;  // first key position
+    const int k1 = min(c0 + a.m, k0 + kBN) - 1;       // last valid key position
+    const bool all_rows = k0 + kBN <= c0 + a.m;
+    if (retrieval) return (all_rows && k1 <= p_min) ? 0 : 1;
+    if (k0 >= S && k1 < p_min - R + 1) return -1;  // left of every window
+    return (all_rows && k1 <= p_min && k0 >= p_max - R + 1) ? 0 : 1;
   };
-
-  // ---- staging: global -> registers (next tile) -> LDS -------------------------------------
-  uint4 kreg[Gm::kKLoads];
-  uint4 vreg[Gm::kVTasks][2];
-  int pos_reg = kNoPos;
+  // key row r of tile ti: source rows (always finite data in bounds) and its position
   auto tile_row = [&](int ti, int r, const char*& kp, const char*& vp) -> int {
-    // key row r of tile ti: source pointers (always in bounds) and position
+    int src, pos;
     if (ti < n_cache_tiles) {
       const int idx = ti * kBN + r;
       if (retrieval) {
-        const int rr = idx < c0 ? idx : c0 - 1;
-        kp = cache_k + (int64_t)rr * RB;
-        vp = cache_v + (int64_t)rr * RB;
-        return idx < c0 ? idx : kNoPos;
+        src = idx < c0 ? idx : c0 - 1;
+        pos = idx < c0 ? idx : kNoPos;
+      } else {
+        const int t = idx < SR ? slots[idx] : -1;
+        src = t >= 0 ? idx : 0;  // empty slot: read slot 0 (filled once c > 0), weight 0
+        pos = t >= 0 ? t : kNoPos;
       }
-      const int rr = idx < SR ? idx : SR - 1;
-      kp = cache_k + (int64_t)rr * RB;
-      vp = cache_v + (int64_t)rr * RB;
-      const int t = idx < SR ? slots[idx] : -1;
-      return t >= 0 ? t : kNoPos;
+      kp = cache_k + (int64_t)src * RB;
+      vp = cache_v + (int64_t)src * RB;
+      return pos;
     }
     const int i = (ti - n_cache_tiles) * kBN + r;
-    const int ii = i < a.m ? i : a.m - 1;
-    kp = chunk_k + (int64_t)ii * chunk_stride;
-    vp = chunk_v + (int64_t)ii * chunk_stride;
+    src = i < a.m ? i : a.m - 1;
+    kp = chunk_k + (int64_t)src * chunk_stride;
+    vp = chunk_v + (int64_t)src * chunk_stride;
     return i < a.m ? c0 + i : kNoPos;
   };
-  auto load_tile = [&](int ti) {
+  // DMA of tile ti into one LDS buffer pair: wave w moves 1 KB blocks w*kDmaPerWave + i
+  auto issue = [&](int ti, char* sk, char* sv, int* sp) {
 #pragma unroll
-    for (int u = 0; u < Gm::kKLoads; ++u) {
-      const int idx = tid + u * kThreads;
-      const int r = idx / Gm::kChunks, c = idx % Gm::kChunks;
+    for (int i = 0; i < Gm::kDmaPerWave; ++i) {
+      const int kb = wave * Gm::kDmaPerWave + i;
+      const int r = kb * Gm::kRowsPerKb + lane / NCH;
+      const int c = (lane % NCH) ^ swz<NCH>(r);  // logical chunk landing at this lane's slot
       const char *kp, *vp;
       tile_row(ti, r, kp, vp);
-      kreg[u] = *(const uint4*)(kp + c * 16);
-    }
-#pragma unroll
-    for (int u = 0; u < Gm::kVTasks; ++u) {
-      const int idx = tid + u * kThreads;
-      const int pr = idx / Gm::kChunks, c = idx % Gm::kChunks;
-      const char *kp, *vp0, *vp1;
-      // rows of empty slots hold whatever the arena held: stage zeros, since their softmax
-      // weight 0 times a non-finite value would still poison the product
-      const bool ok0 = tile_row(ti, 2 * pr, kp, vp0) != kNoPos;
-      const bool ok1 = tile_row(ti, 2 * pr + 1, kp, vp1) != kNoPos;
-      const uint4 z = {0u, 0u, 0u, 0u};
-      const uint4 x0 = *(const uint4*)(vp0 + c * 16);
-      const uint4 x1 = *(const uint4*)(vp1 + c * 16);
-      vreg[u][0] = ok0 ? x0 : z;
-      vreg[u][1] = ok1 ? x1 : z;
+      __builtin_amdgcn_global_load_lds((const void*)(kp + c * 16), (lds_void_t*)(sk + kb * 1024),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vp + c * 16), (lds_void_t*)(sv + kb * 1024),
+                                       16, 0, 0);
     }
     if (tid < kBN) {
       const char *kp, *vp;
-      pos_reg = tile_row(ti, tid, kp, vp);
+      sp[tid] = tile_row(ti, tid, kp, vp);
     }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int u = 0; u < Gm::kKLoads; ++u) {
-      const int idx = tid + u * kThreads;
-      const int r = idx / Gm::kChunks, c = idx % Gm::kChunks;
-      *(uint4*)(sK + r * Gm::kKStride + c * 16) = kreg[u];
-    }
-#pragma unroll
-    for (int u = 0; u < Gm::kVTasks; ++u) {
-      const int idx = tid + u * kThreads;
-      const int pr = idx / Gm::kChunks, c = idx % Gm::kChunks;
-      const uint32_t w0[4] = {vreg[u][0].x, vreg[u][0].y, vreg[u][0].z, vreg[u][0].w};
-      const uint32_t w1[4] = {vreg[u][1].x, vreg[u][1].y, vreg[u][1].z, vreg[u][1].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // d = 8c + 2e (low halves) and 8c + 2e + 1 (high halves); keys 2pr, 2pr + 1
-        const uint32_t lo = (w0[e] & 0xFFFFu) | (w1[e] << 16);
-        const uint32_t hi = (w0[e] >> 16) | (w1[e] & 0xFFFF0000u);
-        *(uint32_t*)(sV + (8 * c + 2 * e) * Gm::kVStride + 4 * pr) = lo;
-        *(uint32_t*)(sV + (8 * c + 2 * e + 1) * Gm::kVStride + 4 * pr) = hi;
-      }
-    }
-    if (tid < kBN) sPos[tid] = pos_reg;
   };
 
-  // ---- accumulators ------------------------------------------------------------------
+  // ---- accumulators --------------------------------------------------------------
   f32x16_t o[Gm::kDBlocks];
 #pragma unroll
   for (int db = 0; db < Gm::kDBlocks; ++db) o[db] = f32x16_t{};
-  float m = kMInit;  // running maximum of this query (log2 units), shared by lanes col, col+32
+  float m = kMInit;    // running maximum of this query (log2 units), same in lanes col, col+32
   float thr = kMInit;  // raw-score threshold (m + kTau) / c2
-  float l = 0.f;     // partial softmax sum over this lane's keys
+  float l = 0.f;       // partial softmax sum over this lane's keys
   const float c2 = a.scale_log2, inv_c2 = 1.f / c2;
 
-  // first tile that has any visible key
-  int ti = 0;
-  while (ti < n_tiles && classify(ti) < 0) ++ti;
-  if (ti < n_tiles) load_tile(ti);
-  while (ti < n_tiles) {
-    const int kind = classify(ti);
-    store_tile();
-    __syncthreads();
-    int next = ti + 1;
-    while (next < n_tiles && classify(next) < 0) ++next;
-    if (next < n_tiles) load_tile(next);  // in flight during this tile's math
-
-    // S^T = K Q^T: two 32-key blocks, keys 8a + 4half + b of block blk in element 4a + b
+  auto compute = [&](int kind, const char* sk, const char* sv, const int* sp) {
+    // S^T = K Q^T: two 32-key blocks; element 4a + b holds key 8a + 4half + b of the block
     f32x16_t s[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       s[blk] = f32x16_t{};
-      const char* krow = sK + (blk * 32 + col) * Gm::kKStride + 8 * half * 2;
+      const int r = blk * 32 + col;
+      const char* krow = sk + r * RB;
+      const int sw = swz<NCH>(r);
 #pragma unroll
       for (int k = 0; k < Gm::kSlabs; ++k) {
-        const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, *(const uint4*)(krow + 32 * k));
+        const int c = (2 * k + half) ^ sw;
+        const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, *(const uint4*)(krow + c * 16));
         s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[k], s[blk], 0, 0, 0);
       }
     }
-    if (kind == kMasked) {
+    if (kind != 0) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
-          const int4 t4 = *(const int4*)(sPos + blk * 32 + 8 * a4 + 4 * half);
+          const int4 t4 = *(const int4*)(sp + blk * 32 + 8 * a4 + 4 * half);
           const int tt[4] = {t4.x, t4.y, t4.z, t4.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -309,42 +293,86 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
       m = mn;
       thr = (mn + kTau) * inv_c2;
     }
-    uint32_t ph[2][8], pl[2][8];  // P = hi + lo in bf16, pairs of consecutive elements
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int e = 0; e < 16; e += 2) {
-        const float p0 = fexp2(__builtin_fmaf(s[blk][e], c2, -m));
-        const float p1 = fexp2(__builtin_fmaf(s[blk][e + 1], c2, -m));
-        l += p0 + p1;
-        split_bf16(p0, p1, ph[blk][e / 2], pl[blk][e / 2]);
-      }
-    // O^T += V^T P^T over four 16-key slabs; slab k holds keys 16k + {4half..4half+3} and
-    // 16k + 8 + {4half..4half+3}, in that order, in both operands
+    // O^T += V^T P^T over four 16-key slabs; slab k holds keys 16k + {4half..4half+3} then
+    // 16k + 8 + {4half..4half+3} in both operands (elements 8(k&1) .. 8(k&1)+7 of block
+    // k>>1 of S^T). A transposed read gives lane l the four keys k0..k0+3 at
+    // d = 32db + (l & 31), with k0 = 16k + 8part + 4half. P = hi + lo is formed per slab,
+    // right before its products.
+    const int gi = lane >> 4, jj = lane & 15, e4 = jj >> 2, q4 = jj & 3;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int blk = k >> 1, e0 = (k & 1) * 4;
-      const uint4 hw = {ph[blk][e0], ph[blk][e0 + 1], ph[blk][e0 + 2], ph[blk][e0 + 3]};
-      const uint4 lw = {pl[blk][e0], pl[blk][e0 + 1], pl[blk][e0 + 2], pl[blk][e0 + 3]};
-      const bf16x8_t pfh = __builtin_bit_cast(bf16x8_t, hw);
-      const bf16x8_t pfl = __builtin_bit_cast(bf16x8_t, lw);
+      const int blk = k >> 1, e0 = (k & 1) * 8;
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float p0 = fexp2(__builtin_fmaf(s[blk][e0 + e], c2, -m));
+        const float p1 = fexp2(__builtin_fmaf(s[blk][e0 + e + 1], c2, -m));
+        l += p0 + p1;
+        split_bf16(p0, p1, hw[e / 2], lw[e / 2]);
+      }
+      const bf16x8_t pfh = __builtin_bit_cast(bf16x8_t, uint4{hw[0], hw[1], hw[2], hw[3]});
+      const bf16x8_t pfl = __builtin_bit_cast(bf16x8_t, uint4{lw[0], lw[1], lw[2], lw[3]});
 #pragma unroll
       for (int db = 0; db < Gm::kDBlocks; ++db) {
-        const char* vrow = sV + (db * 32 + col) * Gm::kVStride;
-        const uint2 v0 = *(const uint2*)(vrow + (16 * k + 4 * half) * 2);
-        const uint2 v1 = *(const uint2*)(vrow + (16 * k + 8 + 4 * half) * 2);
+        s16x4_t vt[2];
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {
+          const int r = 16 * k + 8 * part + 4 * (gi >> 1) + e4;
+          const int d = 32 * db + 16 * (gi & 1) + 4 * q4;
+          const int c = (d >> 3) ^ swz<NCH>(r);
+          vt[part] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4_t*)(sv + r * RB + c * 16 + (q4 & 1) * 8));
+        }
+        const uint2 v0 = __builtin_bit_cast(uint2, vt[0]);
+        const uint2 v1 = __builtin_bit_cast(uint2, vt[1]);
         const uint4 vw = {v0.x, v0.y, v1.x, v1.y};
         const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, vw);
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pfh, o[db], 0, 0, 0);
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pfl, o[db], 0, 0, 0);
       }
     }
+  };
+
+  // ---- tile loop: DMA of the next tile overlaps the math of this one -------------------
+  auto next_visible = [&](int ti) {
+    while (ti < t_end && classify(ti) < 0) ++ti;
+    return ti;
+  };
+  int ti = next_visible(t_begin);
+  if (ti < t_end) issue(ti, sK0, sV0, sPos0);
+  __syncthreads();
+  bool odd = false;
+  while (ti < t_end) {
+    const int next = next_visible(ti + 1);
+    const int kind = classify(ti);
+    if (!odd) {
+      if (next < t_end) issue(next, sK1, sV1, sPos1);
+      compute(kind, sK0, sV0, sPos0);
+    } else {
+      if (next < t_end) issue(next, sK0, sV0, sPos0);
+      compute(kind, sK1, sV1, sPos1);
+    }
     __syncthreads();
     ti = next;
+    odd = !odd;
   }
 
-  // ---- epilogue -------------------------------------------------------------------------
+  // ---- epilogue ---------------------------------------------------------------------
   const float lt = l + __shfl_xor(l, 32);
+  if (nsplit > 1) {  // fp32 partial of this key range
+    const int64_t item = ((int64_t)bi * a.Hr + cls) * a.n_qt + qt;
+    const int64_t prow = (item * nsplit + split) * kRows + row;
+#pragma unroll
+    for (int db = 0; db < Gm::kDBlocks; ++db)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int d = db * 32 + 8 * a4 + 4 * half;
+        *(float4*)(a.part_o + prow * D + d) =
+            float4{o[db][4 * a4], o[db][4 * a4 + 1], o[db][4 * a4 + 2], o[db][4 * a4 + 3]};
+      }
+    if (half == 0) *(float2*)(a.part_ml + prow * 2) = float2{m, lt};
+    return;
+  }
   if (!q_valid) return;
   const float inv = 1.f / lt;
   const int64_t orow = ((int64_t)bi * a.m + q_local) * a.Hq + j * G + g;
@@ -365,25 +393,114 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
   if (half == 0 && a.lse) a.lse[orow] = (m + __builtin_log2f(lt)) * kLn2;
 }
 
+// Merge of the key-range partials of the retrieval query tiles: one block per (item, 16
+// query rows); every thread owns D/16 output columns of one row. M = max_s m_s,
+// L = sum_s l_s exp2(m_s - M), out = sum_s O_s exp2(m_s - M) / L, lse = (M + log2 L) ln 2;
+// empty ranges (m = kMInit, l = 0) weigh zero.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeRows = kMergeThreads / 16;
+
 template <int D, int G>
-int launch_t(const PrefillArgs& a, void* stream) {
+__global__ void __launch_bounds__(kMergeThreads) prefill_merge_kernel(PrefillArgs a) {
   constexpr int kQpb = kRows / G;
-  const int64_t n_qt = (a.m + kQpb - 1) / kQpb;
-  const int64_t n_blocks = (int64_t)a.nb * a.Hkv * n_qt;
-  const int64_t grid = (n_blocks + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL((prefill_kernel<D, G>), dim3((unsigned)grid), dim3(kThreads), 0,
-                     (hipStream_t)stream, a);
-  return (int)hipGetLastError();
+  constexpr int kCols = D / 16;
+  const int tid = threadIdx.x;
+  const int64_t item = blockIdx.x / (kRows / kMergeRows);
+  const int row = (int)(blockIdx.x % (kRows / kMergeRows)) * kMergeRows + tid / 16;
+  const int d0 = (tid % 16) * kCols;
+  const int qt = (int)(item % a.n_qt);
+  const int cls = (int)((item / a.n_qt) % a.Hr);
+  const int bi = (int)(item / ((int64_t)a.n_qt * a.Hr));
+  const int q_local = qt * kQpb + row / G;
+  if (q_local >= a.m) return;
+  const int g = row % G;
+  const int j = a.ret_kv[cls];
+  const int ns = a.nsplit;
+  const int64_t prow0 = item * ns * kRows + row;
+
+  float M = kMInit;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_ml[(prow0 + (int64_t)s * kRows) * 2]);
+  float L = 0.f, O[kCols];
+#pragma unroll
+  for (int c = 0; c < kCols; ++c) O[c] = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const int64_t pr = prow0 + (int64_t)s * kRows;
+    const float2 ml = *(const float2*)(a.part_ml + pr * 2);
+    const float w = fexp2(ml.x - M);
+    L = __builtin_fmaf(w, ml.y, L);
+    const float4* src = (const float4*)(a.part_o + pr * D + d0);
+#pragma unroll
+    for (int c = 0; c < kCols / 4; ++c) {
+      const float4 v = src[c];
+      O[4 * c] = __builtin_fmaf(w, v.x, O[4 * c]);
+      O[4 * c + 1] = __builtin_fmaf(w, v.y, O[4 * c + 1]);
+      O[4 * c + 2] = __builtin_fmaf(w, v.z, O[4 * c + 2]);
+      O[4 * c + 3] = __builtin_fmaf(w, v.w, O[4 * c + 3]);
+    }
+  }
+  const float inv = 1.f / L;
+  const int64_t orow = ((int64_t)bi * a.m + q_local) * a.Hq + j * G + g;
+#pragma unroll
+  for (int c = 0; c < kCols; c += 2) {
+    if (a.out_f32) {
+      *(float2*)((float*)a.out + orow * D + d0 + c) = float2{O[c] * inv, O[c + 1] * inv};
+    } else {
+      *(uint32_t*)((uint16_t*)a.out + orow * D + d0 + c) = pack_bf16(O[c] * inv, O[c + 1] * inv);
+    }
+  }
+  if (tid % 16 == 0 && a.lse) a.lse[orow] = (M + __builtin_log2f(L)) * kLn2;
+}
+
+template <int D, int G>
+struct Variant {
+  static int resident_blocks() {
+    static int cached = 0;
+    if (cached) return cached;
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(&prefill_kernel<D, G>), kThreads, 0) !=
+            hipSuccess ||
+        cus <= 0 || per_cu <= 0) {
+      (void)hipGetLastError();
+      return 512;
+    }
+    cached = cus * per_cu;
+    return cached;
+  }
+  static int launch(const PrefillArgs& a, void* stream) {
+    const int64_t blocks = (int64_t)a.nb * a.n_qt * ((int64_t)a.Hr * a.nsplit + a.Hs);
+    hipLaunchKernelGGL((prefill_kernel<D, G>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                       (hipStream_t)stream, a);
+    if (a.nsplit > 1 && a.Hr > 0) {
+      const int64_t mblocks = (int64_t)a.nb * a.Hr * a.n_qt * (kRows / kMergeRows);
+      hipLaunchKernelGGL((prefill_merge_kernel<D, G>), dim3((unsigned)mblocks),
+                         dim3(kMergeThreads), 0, (hipStream_t)stream, a);
+    }
+    return (int)hipGetLastError();
+  }
+};
+
+template <int D, int G>
+int run(bool query, const PrefillArgs* a, void* stream) {
+  return query ? Variant<D, G>::resident_blocks() : Variant<D, G>::launch(*a, stream);
 }
 
 template <int D>
-int launch_g(const PrefillArgs& a, int group, void* stream) {
+int dispatch_g(int group, bool query, const PrefillArgs* a, void* stream) {
   switch (group) {
-    case 1: return launch_t<D, 1>(a, stream);
-    case 2: return launch_t<D, 2>(a, stream);
-    case 4: return launch_t<D, 4>(a, stream);
-    case 8: return launch_t<D, 8>(a, stream);
+    case 1: return run<D, 1>(query, a, stream);
+    case 2: return run<D, 2>(query, a, stream);
+    case 4: return run<D, 4>(query, a, stream);
+    case 8: return run<D, 8>(query, a, stream);
   }
+  return -1;
+}
+
+int dispatch(int head_dim, int group, bool query, const PrefillArgs* a, void* stream) {
+  if (head_dim == 128) return dispatch_g<128>(group, query, a, stream);
+  if (head_dim == 64) return dispatch_g<64>(group, query, a, stream);
   return -1;
 }
 
@@ -392,9 +509,11 @@ int launch_g(const PrefillArgs& a, int group, void* stream) {
 // Returns -1 for a variant that is not built (fp32 inputs), else a hipError_t value.
 int launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int group, void* stream) {
   if (dtype != DUO_BF16) return -1;
-  if (head_dim == 128) return launch_g<128>(a, group, stream);
-  if (head_dim == 64) return launch_g<64>(a, group, stream);
-  return -1;
+  return dispatch(head_dim, group, false, &a, stream);
+}
+
+int prefill_resident_blocks(int head_dim, int group) {
+  return dispatch(head_dim, group, true, nullptr, nullptr);
 }
 
 }  // namespace duo

@@ -69,6 +69,8 @@ typedef struct {
   float softmax_scale;     /* <= 0 selects 1/sqrt(head_dim) */
   int32_t max_splits;      /* split-K workspace per (sequence, query head), <= 1024;
                               0 selects 256 */
+  int32_t prefill_tiles;   /* prefill split-K workspace in tiles of 128 query rows,
+                              <= 65536; 0 selects 2048 */
   const uint8_t* retrieval_mask; /* host [num_layers][num_kv_heads], nonzero = retrieval;
                                     copied by duo_cache_create */
 } duo_config;
@@ -83,7 +85,7 @@ typedef struct {
   uint64_t str_v_off;
   uint64_t slot_pos_off;   /* int32 [L][B][S+R]: position held by each slot, -1 = empty */
   uint64_t seq_len_off;    /* int32 [L][B]: tokens appended so far */
-  uint64_t workspace_off;  /* split-K partials of the decode */
+  uint64_t workspace_off;  /* split-K partials of decode and prefill (shared) */
   uint64_t workspace_bytes;
 } duo_layout;
 
