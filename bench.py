@@ -2,7 +2,8 @@
 
 Decode leg (the headline): the Llama-3-8B-shaped GQA layer at a 128K context (32 query heads,
 8 KV heads, head_dim 128, bf16, 4 retrieval KV heads, sink 16 + recent 512). One step is, for
-each of ``--layers`` replica layers, one append of the new token followed by one decode. The
+each of ``--layers`` replica layers, one append of the new token and its decode (the fused
+``duo_decode_step``; ``--unfused`` times duo_kv_append + duo_attn_decode instead). The
 replica layers sit at distinct addresses so that the per-step K/V (>= 2 GB) cannot stay in
 the 256 MB Infinity Cache; the time per layer-step is the step time divided by the layers.
 
@@ -47,6 +48,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--splits", type=int, default=0, help="force decode splits (0 = automatic)")
+    p.add_argument("--unfused", action="store_true", help="time append + decode as two calls")
     return p.parse_args()
 
 
@@ -122,15 +124,20 @@ def decode_leg(args, torch, hsk, W, N):
     qstride = w.hq * w.d * 2
     kstride = w.hkv * w.d * 2
     qp, kp, vp, op = qs.data_ptr(), ks.data_ptr(), vs.data_ptr(), ctypes.c_void_p(out.data_ptr())
-    append, decode = lib.duo_kv_append, lib.duo_attn_decode
+    decode, decode_step = lib.duo_attn_decode, lib.duo_decode_step
 
     def step(s):
+        # one decoding step of every replica layer: append of the step's token fused with
+        # the attention (duo_decode_step)
         kk = ctypes.c_void_p(kp + s * kstride)
         vv = ctypes.c_void_p(vp + s * kstride)
         qq = ctypes.c_void_p(qp + s * qstride)
         for layer in range(L):
-            st = append(h, layer, -1, kk, vv, 1, stream)
-            st |= decode(h, layer, qq, op, None, stream)
+            if args.unfused:
+                st = lib.duo_kv_append(h, layer, -1, kk, vv, 1, stream)
+                st |= decode(h, layer, qq, op, None, stream)
+            else:
+                st = decode_step(h, layer, qq, kk, vv, op, None, stream)
             if st:
                 raise RuntimeError(f"libduo call failed: {N.status_string(st)}")
 

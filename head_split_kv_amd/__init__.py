@@ -118,6 +118,9 @@ class DuoCache:
     def attn_decode(self, layer, q, out=None, lse=None, stream=None):
         return duo_attn_decode(self, layer, q, out, lse, stream=stream)
 
+    def decode_step(self, layer, q, k, v, out=None, lse=None, stream=None):
+        return duo_decode_step(self, layer, q, k, v, out, lse, stream=stream)
+
     def attn_prefill(self, layer, q, k, v, seq=-1, out=None, lse=None, stream=None):
         return duo_attn_prefill(self, layer, seq, q, k, v, out, lse, stream=stream)
 
@@ -177,6 +180,28 @@ def duo_attn_decode(cache: DuoCache, layer: int, q: torch.Tensor, out=None, lse=
     check(lib().duo_attn_decode(cache.handle, layer, ctypes.c_void_p(q.data_ptr()),
                                 ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(lse_ptr),
                                 _stream(stream)), "duo_attn_decode")
+    return out
+
+
+def duo_decode_step(cache: DuoCache, layer: int, q: torch.Tensor, k: torch.Tensor,
+                    v: torch.Tensor, out=None, lse=None, stream=None):
+    """Append one token per sequence and decode it in one pass: q ``[B, Hq, d]``,
+    k, v ``[B, Hkv, d]`` -> out ``[B, Hq, d]`` (and lse ``[B, Hq]``)."""
+    _check_tensor(q, (cache.batch, cache.hq, cache.d), cache.dtype, cache.device, "q")
+    _check_tensor(k, (cache.batch, cache.hkv, cache.d), cache.dtype, cache.device, "k")
+    _check_tensor(v, (cache.batch, cache.hkv, cache.d), cache.dtype, cache.device, "v")
+    if out is None:
+        out = torch.empty((cache.batch, cache.hq, cache.d), dtype=cache.out_dtype,
+                          device=q.device)
+    _check_tensor(out, (cache.batch, cache.hq, cache.d), cache.out_dtype, cache.device, "out")
+    lse_ptr = None
+    if lse is not None:
+        _check_tensor(lse, (cache.batch, cache.hq), torch.float32, cache.device, "lse")
+        lse_ptr = lse.data_ptr()
+    check(lib().duo_decode_step(cache.handle, layer, ctypes.c_void_p(q.data_ptr()),
+                                ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+                                ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(lse_ptr),
+                                _stream(stream)), "duo_decode_step")
     return out
 
 

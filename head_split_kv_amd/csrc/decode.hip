@@ -183,37 +183,55 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
   const int wave = tid >> 6, lane = tid & 63, grp = lane / LPT, sub = lane % LPT;
 
   // ---- work item -------------------------------------------------------------------------
+  // In a fused step (a.new_k != null) the token at p = n - 1 is not in the cache yet: the
+  // cache rows of this item exclude it (and, on a streaming head, the slot it is about to
+  // take), and the one block that covers p reads its K/V from the input, then stores them.
+  const bool fused = a.new_k != nullptr;
   const int64_t n_ret_items = (int64_t)a.B * a.Hr * a.nsplit;
-  int b, j, split, nsplit;
+  int b, j, split, nsplit, cls;
   int64_t head_row0;  // first row of this head in its cache
   const char* kbase;
   const char* vbase;
-  int t0, t1;
+  int t0, t1, skip = -1, new_row = -1;  // new_row: cache row of the new token if this block has it
+  bool retrieval;
   if ((int64_t)blockIdx.x < n_ret_items) {
     const int64_t i = blockIdx.x;
     split = (int)(i % a.nsplit);
-    const int r = (int)((i / a.nsplit) % a.Hr);
+    cls = (int)((i / a.nsplit) % a.Hr);
     b = (int)(i / ((int64_t)a.nsplit * a.Hr));
-    j = a.ret_kv[r];
+    j = a.ret_kv[cls];
     nsplit = a.nsplit;
+    retrieval = true;
     const int n = a.n[b];
     const int chunk = (n + nsplit - 1) / nsplit;
     t0 = split * chunk;
-    t1 = min(n, t0 + chunk);
-    head_row0 = ((int64_t)b * a.Hr + r) * a.cap;
+    t1 = min(fused ? n - 1 : n, t0 + chunk);
+    if (fused && (n - 1) / chunk == split) new_row = n - 1;
+    head_row0 = ((int64_t)b * a.Hr + cls) * a.cap;
     kbase = (const char*)a.full_k;
     vbase = (const char*)a.full_v;
   } else {
     const int64_t i = blockIdx.x - n_ret_items;
-    const int s = (int)(i % a.Hs);
+    cls = (int)(i % a.Hs);
     b = (int)(i / a.Hs);
-    j = a.str_kv[s];
+    j = a.str_kv[cls];
     split = 0;
     nsplit = 1;
+    retrieval = false;
     const int n = a.n[b];
+    const int SR = a.S + a.R;
     t0 = 0;
-    t1 = min(n, a.S + a.R);
-    head_row0 = ((int64_t)b * a.Hs + s) * (a.S + a.R);
+    if (!fused) {
+      t1 = min(n, SR);
+    } else {
+      const int pnew = n - 1;
+      new_row = pnew < a.S ? pnew : a.S + (pnew - a.S) % a.R;
+      // before the ring wraps the new slot is the first unused one; afterwards it holds the
+      // evicted token p - R, which is outside the window
+      t1 = min(pnew, SR);
+      if (pnew >= SR) skip = new_row;
+    }
+    head_row0 = ((int64_t)b * a.Hs + cls) * (a.S + a.R);
     kbase = (const char*)a.str_k;
     vbase = (const char*)a.str_v;
   }
@@ -246,9 +264,8 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
     for (int e = 0; e < E; ++e) o[g][e] = 0.f;
   }
 
-  // One step: the tokens of this lane group's row (masked past the end of the item).
-  auto process = [&](const F& f, int cur) {
-    const bool valid = t0 + (cur * kWaves + wave) * kTpw + grp < t1;
+  // One step: the token of this lane group's row (masked when not valid).
+  auto process = [&](const F& f, bool valid) {
     float dz[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -296,16 +313,45 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
     load_frag<T, D, LPT>(f2, kbase, vbase, row_of(2), sub);
     if constexpr (NS == 4) load_frag<T, D, LPT>(f3, kbase, vbase, row_of(3), sub);
 
+    auto valid_at = [&](int it) {
+      const int t = t0 + (it * kWaves + wave) * kTpw + grp;
+      return t < t1 && t != skip;
+    };
     for (int it = 0; it < n_it; it += NS) {
-      process(f0, it);
+      process(f0, valid_at(it));
       load_frag<T, D, LPT>(f0, kbase, vbase, row_of(it + NS), sub);
-      process(f1, it + 1);
+      process(f1, valid_at(it + 1));
       load_frag<T, D, LPT>(f1, kbase, vbase, row_of(it + NS + 1), sub);
-      process(f2, it + 2);
+      process(f2, valid_at(it + 2));
       load_frag<T, D, LPT>(f2, kbase, vbase, row_of(it + NS + 2), sub);
       if constexpr (NS == 4) {
-        process(f3, it + 3);
+        process(f3, valid_at(it + 3));
         load_frag<T, D, LPT>(f3, kbase, vbase, row_of(it + NS + 3), sub);
+      }
+    }
+  }
+
+  // ---- fused step: the new token from the input, then its store into the cache -----------
+  if (new_row >= 0) {
+    const char* nk = (const char*)a.new_k + ((int64_t)b * a.Hkv + j) * RB;
+    const char* nv = (const char*)a.new_v + ((int64_t)b * a.Hkv + j) * RB;
+    F f;
+    load_frag<T, D, LPT>(f, nk, nv, 0, sub);
+    process(f, wave == 0 && grp == 0);
+    if (wave == 0) {
+      constexpr int kRowChunks = RB / 16;
+      for (int c = lane; c < 2 * kRowChunks; c += 64) {
+        const bool is_v = c >= kRowChunks;
+        const int cc = is_v ? c - kRowChunks : c;
+        const uint4 x = *(const uint4*)((is_v ? nv : nk) + cc * 16);
+        *(uint4*)(const_cast<char*>(is_v ? vbase : kbase) + (int64_t)new_row * RB + cc * 16) = x;
+      }
+      if (j == 0 && lane == 0) {  // one block per sequence updates the tables
+        const int n = a.n[b];
+        const int pnew = n - 1;
+        const int SR = a.S + a.R;
+        a.slot_pos[(int64_t)b * SR + (pnew < a.S ? pnew : a.S + (pnew - a.S) % a.R)] = pnew;
+        a.seq_len[b] = n;
       }
     }
   }

@@ -67,6 +67,68 @@ Workspace workspace(duo_cache* c) {
 
 }  // namespace
 
+namespace {
+
+// Shared by duo_attn_decode (k == v == null) and duo_decode_step.
+duo_status decode_impl(duo_cache* c, int32_t layer, const void* q, const void* k, const void* v,
+                       void* out, float* lse, void* stream) {
+  if (!layer_ok(c, layer) || !q || !out || !aligned16(q) || !aligned16(out) || !aligned4(lse))
+    return DUO_ERR_INVALID;
+  const bool fused = k != nullptr;
+  if (fused && (!v || !aligned16(k) || !aligned16(v))) return DUO_ERR_INVALID;
+  int32_t n_max = 0;
+  for (int32_t b = 0; b < c->cfg.batch; ++b) {
+    const int64_t n = (int64_t)len_of(c, layer, b) + (fused ? 1 : 0);
+    if (n < 1) return DUO_ERR_INVALID;
+    if (n > c->cfg.capacity) return DUO_ERR_CAPACITY;
+    n_max = std::max(n_max, (int32_t)n);
+  }
+  const LayerInfo& li = c->layers[layer];
+  const LayerPtrs p = layer_ptrs(c, layer);
+  const Workspace w = workspace(c);
+  DecodeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.out = out;
+  a.lse = lse;
+  a.full_k = p.full_k;
+  a.full_v = p.full_v;
+  a.str_k = p.str_k;
+  a.str_v = p.str_v;
+  for (int32_t b = 0; b < c->cfg.batch; ++b) a.n[b] = len_of(c, layer, b) + (fused ? 1 : 0);
+  a.part_o = w.part_o;
+  a.part_ml = w.part_ml;
+  a.new_k = k;
+  a.new_v = v;
+  a.slot_pos = p.slot_pos;
+  a.seq_len = p.seq_len;
+  a.B = c->cfg.batch;
+  a.Hq = c->cfg.num_q_heads;
+  a.Hkv = c->cfg.num_kv_heads;
+  a.Hr = li.n_ret;
+  a.Hs = li.n_str;
+  a.cap = c->cfg.capacity;
+  a.S = c->cfg.sink;
+  a.R = c->cfg.recent;
+  a.max_splits = c->cfg.max_splits;
+  const int group = c->cfg.num_q_heads / c->cfg.num_kv_heads;
+  a.nsplit = c->force_splits
+                 ? c->force_splits
+                 : choose_decode_splits(n_max, a.B, a.Hr, a.Hs, a.max_splits,
+                                        decode_resident_blocks(c->cfg.dtype, c->cfg.head_dim,
+                                                               group));
+  a.scale_log2 = (float)((double)c->scale * 1.4426950408889634);
+  a.out_f32 = c->cfg.out_dtype == DUO_F32;
+  std::memcpy(a.ret_kv, li.ret_kv, sizeof(a.ret_kv));
+  std::memcpy(a.str_kv, li.str_kv, sizeof(a.str_kv));
+  if (launch_decode(a, c->cfg.dtype, c->cfg.head_dim, group, stream) != 0) return DUO_ERR_HIP;
+  if (fused)
+    for (int32_t b = 0; b < c->cfg.batch; ++b) len_of(c, layer, b) += 1;
+  return DUO_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 duo_status duo_cache_reset(duo_cache* c, void* stream) {
@@ -123,50 +185,13 @@ duo_status duo_kv_append(duo_cache* c, int32_t layer, int32_t seq, const void* k
 
 duo_status duo_attn_decode(duo_cache* c, int32_t layer, const void* q, void* out, float* lse,
                            void* stream) {
-  if (!layer_ok(c, layer) || !q || !out || !aligned16(q) || !aligned16(out) || !aligned4(lse))
-    return DUO_ERR_INVALID;
-  int32_t n_max = 0;
-  for (int32_t b = 0; b < c->cfg.batch; ++b) {
-    const int32_t n = len_of(c, layer, b);
-    if (n < 1) return DUO_ERR_INVALID;
-    n_max = std::max(n_max, n);
-  }
-  const LayerInfo& li = c->layers[layer];
-  const LayerPtrs p = layer_ptrs(c, layer);
-  const Workspace w = workspace(c);
-  DecodeArgs a;
-  std::memset(&a, 0, sizeof(a));
-  a.q = q;
-  a.out = out;
-  a.lse = lse;
-  a.full_k = p.full_k;
-  a.full_v = p.full_v;
-  a.str_k = p.str_k;
-  a.str_v = p.str_v;
-  for (int32_t b = 0; b < c->cfg.batch; ++b) a.n[b] = len_of(c, layer, b);
-  a.part_o = w.part_o;
-  a.part_ml = w.part_ml;
-  a.B = c->cfg.batch;
-  a.Hq = c->cfg.num_q_heads;
-  a.Hkv = c->cfg.num_kv_heads;
-  a.Hr = li.n_ret;
-  a.Hs = li.n_str;
-  a.cap = c->cfg.capacity;
-  a.S = c->cfg.sink;
-  a.R = c->cfg.recent;
-  a.max_splits = c->cfg.max_splits;
-  const int group = c->cfg.num_q_heads / c->cfg.num_kv_heads;
-  a.nsplit = c->force_splits
-                 ? c->force_splits
-                 : choose_decode_splits(n_max, a.B, a.Hr, a.Hs, a.max_splits,
-                                        decode_resident_blocks(c->cfg.dtype, c->cfg.head_dim,
-                                                               group));
-  a.scale_log2 = (float)((double)c->scale * 1.4426950408889634);
-  a.out_f32 = c->cfg.out_dtype == DUO_F32;
-  std::memcpy(a.ret_kv, li.ret_kv, sizeof(a.ret_kv));
-  std::memcpy(a.str_kv, li.str_kv, sizeof(a.str_kv));
-  if (launch_decode(a, c->cfg.dtype, c->cfg.head_dim, group, stream) != 0) return DUO_ERR_HIP;
-  return DUO_OK;
+  return decode_impl(c, layer, q, nullptr, nullptr, out, lse, stream);
+}
+
+duo_status duo_decode_step(duo_cache* c, int32_t layer, const void* q, const void* k,
+                           const void* v, void* out, float* lse, void* stream) {
+  if (!k || !v) return DUO_ERR_INVALID;
+  return decode_impl(c, layer, q, k, v, out, lse, stream);
 }
 
 duo_status duo_attn_prefill(duo_cache* c, int32_t layer, int32_t seq, const void* q,

@@ -65,12 +65,16 @@ struct DecodeArgs {
   const void* str_v;
   float* part_o;           // [B][Hq][max_splits][D]
   float* part_ml;          // [B][Hq][max_splits][2]
+  const void* new_k;       // fused step: the appended token [B][Hkv][D], else null
+  const void* new_v;
+  int32_t* slot_pos;       // fused step: this layer's slot table [B][S+R] and lengths [B]
+  int32_t* seq_len;
   int32_t B, Hq, Hkv, Hr, Hs, cap, S, R, nsplit, max_splits;
   float scale_log2;        // softmax scale * log2(e)
   int32_t out_f32;
   uint8_t ret_kv[kMaxKvHeads];
   uint8_t str_kv[kMaxKvHeads];
-  int32_t n[kMaxBatch];    // current length of every sequence (host mirror)
+  int32_t n[kMaxBatch];    // length of every sequence, the fused step's token included
 };
 
 struct PrefillArgs {

@@ -131,6 +131,14 @@ duo_status duo_kv_append(duo_cache* cache, int32_t layer, int32_t seq, const voi
 duo_status duo_attn_decode(duo_cache* cache, int32_t layer, const void* q, void* out,
                            float* lse, void* stream);
 
+/* One decoding step with its append fused in (explainer, "Decoding Procedure" steps 1-5):
+ * the same result and cache state as duo_kv_append(cache, layer, -1, k, v, 1, stream)
+ * followed by duo_attn_decode(cache, layer, q, out, lse, stream), in one pass over the
+ * caches. k, v [B][Hkv][d] hold the step's token of every sequence; q, out, lse as in
+ * duo_attn_decode. DUO_ERR_CAPACITY if a sequence is full. */
+duo_status duo_decode_step(duo_cache* cache, int32_t layer, const void* q, const void* k,
+                           const void* v, void* out, float* lse, void* stream);
+
 /* Attention of one pre-filling chunk (explainer, "Chunked Pre-filling"). The chunk holds
  * positions c .. c+m-1 where c is the sequence's current length. Query p attends to every
  * t <= p on retrieval heads (full cache rows 0..c-1 plus the chunk, causally) and, on

@@ -173,6 +173,9 @@ def test_error_paths_leave_state_unchanged():
     # decode of empty sequences is rejected
     assert L.duo_attn_decode(fc.h, 0, p, p, None, None) == N.DUO_ERR_INVALID
     assert L.duo_attn_decode(fc.h, 0, mis, p, None, None) == N.DUO_ERR_INVALID
+    assert L.duo_decode_step(fc.h, 0, p, None, p, p, None, None) == N.DUO_ERR_INVALID
+    assert L.duo_decode_step(fc.h, 0, p, mis, p, p, None, None) == N.DUO_ERR_INVALID
+    assert L.duo_decode_step(fc.h, 5, p, p, p, p, None, None) == N.DUO_ERR_INVALID
     assert L.duo_attn_prefill(fc.h, 0, -1, p, p, p, 0, p, None, None) == N.DUO_OK
     assert L.duo_attn_prefill(fc.h, 0, 5, p, p, p, 4, p, None, None) == N.DUO_ERR_INVALID
     assert L.duo_attn_prefill(fc.h, 0, 0, p, mis, p, 4, p, None, None) == N.DUO_ERR_INVALID
