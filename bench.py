@@ -144,6 +144,9 @@ def decode_leg(args, torch, hsk, W, N):
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
+    # the library's kernel timers record a HIP event pair on this stream around every
+    # split attention kernel of the timed steps (the split merge kernel is outside the pair)
+    hsk.duo_timing_enable(cache, args.steps * L)
     tm = Timer(torch)
     tm.start()
     for s in range(args.warmup, total_steps):
@@ -151,6 +154,10 @@ def decode_leg(args, torch, hsk, W, N):
     total_ms = tm.stop_ms()
     torch.cuda.synchronize()
     ms_per_step = total_ms / args.steps
+    kern_ms, kern_n = hsk.duo_timing_read(cache, "decode")
+    hsk.duo_timing_enable(cache, 0)
+    assert kern_n == args.steps * L, kern_n
+    kern_us = kern_ms * 1e3 / kern_n
 
     # algorithmic bytes of one layer-step, averaged over the timed steps
     cfg1, _m = hsk.make_config(num_layers=1, batch=1, num_q_heads=w.hq, num_kv_heads=w.hkv,
@@ -163,8 +170,10 @@ def decode_leg(args, torch, hsk, W, N):
     step_bytes = sum(kv_bytes) / len(kv_bytes) + io_bytes
     us_layer = ms_per_step * 1e3 / L
     gbs = step_bytes / (us_layer * 1e-6) / 1e9
+    kern_gbs = step_bytes / (kern_us * 1e-6) / 1e9
 
-    # the decode kernel alone: back-to-back launches over all replica layers at the final length
+    # one duo_attn_decode call (split kernel + merge kernel), back-to-back over the replica
+    # layers at the final length
     reps = max(4, 64 // L)
     for layer in range(L):
         decode(h, layer, ctypes.c_void_p(qp), op, None, stream)
@@ -180,6 +189,7 @@ def decode_leg(args, torch, hsk, W, N):
     result = dict(
         workload=w, layers=L, ms_per_step=ms_per_step, us_layer=us_layer, gbs=gbs,
         step_bytes=step_bytes, dec_us=dec_ms * 1e3, dec_bytes=dec_bytes, dec_gbs=dec_gbs,
+        kern_us=kern_us, kern_gbs=kern_gbs, kern_n=kern_n,
         n_final=n_final, history=(n0, total_steps))
     del cache, qs, ks, vs
     torch.cuda.empty_cache()
@@ -227,11 +237,16 @@ def prefill_leg(args, torch, hsk, W, N):
 
     run_pass()
     torch.cuda.synchronize()
+    hsk.duo_timing_enable(cache, args.prefill_passes * (P // C))
     tm = Timer(torch)
     tm.start()
     for _ in range(args.prefill_passes):
         run_pass()
     pass_ms = tm.stop_ms() / args.prefill_passes
+    kern_ms, kern_n = hsk.duo_timing_read(cache, "prefill")
+    hsk.duo_timing_enable(cache, 0)
+    assert kern_n == args.prefill_passes * (P // C), kern_n
+    kern_ms_pass = kern_ms / args.prefill_passes
     attn = []
     for _ in range(args.prefill_passes):
         attn.append(run_pass(Timer(torch)))
@@ -247,7 +262,8 @@ def prefill_leg(args, torch, hsk, W, N):
     del cache, q, k, v, out
     torch.cuda.empty_cache()
     return dict(workload=w, pass_ms=pass_ms, attn_ms=attn_ms, flops=flops,
-                tflops=flops / (attn_ms * 1e-3) / 1e12,
+                tflops=flops / (attn_ms * 1e-3) / 1e12, kern_ms=kern_ms_pass,
+                kern_tflops=flops / (kern_ms_pass * 1e-3) / 1e12,
                 tflops_incl_append=flops / (pass_ms * 1e-3) / 1e12)
 
 
@@ -304,14 +320,16 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dec = decode_leg(args, torch, hsk, W, N)
-    log(f"decode: {dec['us_layer']:.2f} us/layer-step, {dec['gbs']:.0f} GB/s; kernel alone "
-        f"{dec['dec_us']:.2f} us = {dec['dec_gbs']:.0f} GB/s")
+    log(f"decode: {dec['us_layer']:.2f} us/layer-step, {dec['gbs']:.0f} GB/s; split kernel "
+        f"{dec['kern_us']:.2f} us = {dec['kern_gbs']:.0f} GB/s ({dec['kern_n']} launches timed); "
+        f"one duo_attn_decode call {dec['dec_us']:.2f} us = {dec['dec_gbs']:.0f} GB/s")
     pre = None
     if not args.no_prefill:
         try:
             pre = prefill_leg(args, torch, hsk, W, N)
             log(f"prefill: {pre['attn_ms']:.3f} ms attention for {pre['flops'] / 1e12:.3f} TFLOP "
-                f"= {pre['tflops']:.1f} TFLOP/s")
+                f"= {pre['tflops']:.1f} TFLOP/s; attention kernel {pre['kern_ms']:.3f} ms = "
+                f"{pre['kern_tflops']:.1f} TFLOP/s")
         except (RuntimeError, hsk.DuoError) as e:
             log(f"prefill leg skipped: {e}")
     probe = copy_probe(torch)
@@ -343,16 +361,17 @@ def main():
         },
         "us_per_layer_step": round(dec["us_layer"], 3),
         "hbm_frac": round(dec["gbs"] / HBM_PEAK_GBS, 4),
-        "decode_kernel_us": round(dec["dec_us"], 3),
+        "decode_call_us": round(dec["dec_us"], 3),
         "roofline": {
             "bound": "hbm",
-            "achieved": round(dec["dec_gbs"], 1),
+            "achieved": round(dec["kern_gbs"], 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(dec["dec_gbs"] / HBM_PEAK_GBS, 4),
+            "frac": round(dec["kern_gbs"] / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "decode_kernel (bf16, d=128, G=4)",
-            "algorithmic_bytes_per_launch": int(dec["dec_bytes"]),
+            "kernel": "decode_kernel<bf16, d128, G4> (split attention kernel of duo_decode_step)",
+            "kernel_us": round(dec["kern_us"], 3),
+            "algorithmic_bytes_per_launch": int(dec["step_bytes"]),
         },
         "hbm_copy_probe_GBps": round(probe, 1),
         "prefill": None if pre is None else {
@@ -360,10 +379,12 @@ def main():
             "attn_ms": round(pre["attn_ms"], 3),
             "ms_incl_append": round(pre["pass_ms"], 3),
             "tflops": round(pre["tflops"], 1),
-            "roofline": {"bound": "mfma", "achieved": round(pre["tflops"], 1),
+            "roofline": {"bound": "mfma", "achieved": round(pre["kern_tflops"], 1),
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(pre["tflops"] / BF16_PEAK_TFLOPS, 4),
+                         "frac": round(pre["kern_tflops"] / BF16_PEAK_TFLOPS, 4),
                          "traffic": committed_traffic("prefill.hip", "prefill_c2"),
+                         "kernel": "prefill_kernel<d128, G1> (8 launches per pass)",
+                         "kernel_ms_per_pass": round(pre["kern_ms"], 3),
                          "algorithmic_flops": int(pre["flops"])},
         },
         "cpu_baseline": None if cpu is None else {

@@ -248,5 +248,23 @@ def duo_set_decode_splits(cache: DuoCache, splits: int) -> None:
     check(lib().duo_set_decode_splits(cache.handle, splits), "duo_set_decode_splits")
 
 
+def duo_timing_enable(cache: DuoCache, max_records: int) -> None:
+    """Record HIP events around the attention kernel of the next ``max_records`` decode
+    calls and, separately, prefill calls (0 switches timing off)."""
+    check(lib().duo_timing_enable(cache.handle, max_records), "duo_timing_enable")
+
+
+def duo_timing_read(cache: DuoCache, kind: str = "decode"):
+    """(summed kernel milliseconds, recorded launches) of ``kind`` ("decode" or "prefill")
+    since the last read; waits for the last recorded launch."""
+    from ._native import TIMING_DECODE, TIMING_PREFILL
+    k = {"decode": TIMING_DECODE, "prefill": TIMING_PREFILL}[kind]
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_int32(0)
+    check(lib().duo_timing_read(cache.handle, k, ctypes.byref(ms), ctypes.byref(n)),
+          "duo_timing_read")
+    return ms.value, n.value
+
+
 def duo_status_string(status: int) -> str:
     return status_string(status)

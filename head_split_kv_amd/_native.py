@@ -17,8 +17,10 @@ EXPORTS = (
     "duo_layout_query", "duo_cache_create", "duo_cache_reset", "duo_cache_destroy",
     "duo_kv_append", "duo_attn_decode", "duo_decode_step", "duo_attn_prefill",
     "duo_slot_positions",
-    "duo_cache_lengths", "duo_kv_bytes", "duo_set_decode_splits", "duo_status_string",
+    "duo_cache_lengths", "duo_kv_bytes", "duo_set_decode_splits", "duo_timing_enable",
+    "duo_timing_read", "duo_status_string",
 )
+TIMING_DECODE, TIMING_PREFILL = 0, 1
 
 
 class DuoConfig(ctypes.Structure):
@@ -83,6 +85,8 @@ def lib() -> ctypes.CDLL:
         "duo_kv_bytes": (st, [P(DuoConfig), i32, P(i32), P(ctypes.c_uint64),
                               P(ctypes.c_uint64)]),
         "duo_set_decode_splits": (st, [vp, i32]),
+        "duo_timing_enable": (st, [vp, i32]),
+        "duo_timing_read": (st, [vp, i32, P(ctypes.c_double), P(i32)]),
         "duo_status_string": (ctypes.c_char_p, [st]),
     }
     for name, (res, args) in sig.items():

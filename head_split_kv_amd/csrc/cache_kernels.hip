@@ -101,6 +101,45 @@ int launch_append(const AppendArgs& a, int /*dtype*/, void* stream) {
   return (int)hipGetLastError();
 }
 
+int create_events(int n, std::vector<void*>* out) {
+  out->clear();
+  for (int i = 0; i < n; ++i) {
+    // timing only: no system-scope cache writeback and invalidation at each record, which
+    // would slow the kernels that follow and count in the measured pairs
+    hipEvent_t e;
+    const hipError_t rc = hipEventCreateWithFlags(&e, hipEventDisableSystemFence);
+    if (rc != hipSuccess) {
+      destroy_events(out);
+      return (int)rc;
+    }
+    out->push_back((void*)e);
+  }
+  return 0;
+}
+
+void destroy_events(std::vector<void*>* ev) {
+  for (void* e : *ev) (void)hipEventDestroy((hipEvent_t)e);
+  ev->clear();
+}
+
+int record_event(void* event, void* stream) {
+  return (int)hipEventRecord((hipEvent_t)event, (hipStream_t)stream);
+}
+
+int pairs_elapsed_ms(const std::vector<void*>& ev, int pairs, double* total_ms) {
+  *total_ms = 0.0;
+  if (pairs <= 0) return 0;
+  hipError_t rc = hipEventSynchronize((hipEvent_t)ev[2 * pairs - 1]);
+  if (rc != hipSuccess) return (int)rc;
+  for (int i = 0; i < pairs; ++i) {
+    float ms = 0.f;
+    rc = hipEventElapsedTime(&ms, (hipEvent_t)ev[2 * i], (hipEvent_t)ev[2 * i + 1]);
+    if (rc != hipSuccess) return (int)rc;
+    *total_ms += ms;
+  }
+  return 0;
+}
+
 int copy_d2h_sync(void* dst, const void* src, uint64_t bytes, void* stream) {
   hipError_t e = hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, (hipStream_t)stream);
   if (e != hipSuccess) return (int)e;

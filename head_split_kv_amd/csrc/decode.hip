@@ -534,10 +534,12 @@ struct Variant {
     return cached;
   }
 
-  static int launch(const DecodeArgs& a, void* stream) {
+  static int launch(const DecodeArgs& a, void* stream, const KernelMarks& marks) {
     const int64_t blocks = (int64_t)a.B * a.Hr * a.nsplit + (int64_t)a.B * a.Hs;
+    if (marks.begin) (void)hipEventRecord((hipEvent_t)marks.begin, (hipStream_t)stream);
     hipLaunchKernelGGL((decode_kernel<T, D, G, LPT, NS>), dim3((unsigned)blocks),
                        dim3(kThreads), 0, (hipStream_t)stream, a);
+    if (marks.end) (void)hipEventRecord((hipEvent_t)marks.end, (hipStream_t)stream);
     if (a.nsplit > 1 && a.Hr > 0) {
       const int64_t mblocks = (int64_t)a.B * a.Hr * G * (D / 64);
       hipLaunchKernelGGL((merge_kernel<T, D, G>), dim3((unsigned)mblocks),
@@ -548,41 +550,43 @@ struct Variant {
 };
 
 template <typename T, int D, int G>
-int run(bool query, const DecodeArgs* a, void* stream) {
-  return query ? Variant<T, D, G>::resident_blocks() : Variant<T, D, G>::launch(*a, stream);
+int run(bool query, const DecodeArgs* a, void* stream, const KernelMarks* marks) {
+  return query ? Variant<T, D, G>::resident_blocks()
+               : Variant<T, D, G>::launch(*a, stream, *marks);
 }
 
 template <typename T, int D>
-int dispatch_g(int group, bool query, const DecodeArgs* a, void* stream) {
+int dispatch_g(int group, bool query, const DecodeArgs* a, void* stream, const KernelMarks* m) {
   switch (group) {
-    case 1: return run<T, D, 1>(query, a, stream);
-    case 2: return run<T, D, 2>(query, a, stream);
-    case 4: return run<T, D, 4>(query, a, stream);
-    case 8: return run<T, D, 8>(query, a, stream);
+    case 1: return run<T, D, 1>(query, a, stream, m);
+    case 2: return run<T, D, 2>(query, a, stream, m);
+    case 4: return run<T, D, 4>(query, a, stream, m);
+    case 8: return run<T, D, 8>(query, a, stream, m);
   }
   return -1;
 }
 
 int dispatch(int dtype, int head_dim, int group, bool query, const DecodeArgs* a,
-             void* stream) {
+             void* stream, const KernelMarks* m) {
   if (dtype == DUO_BF16) {
-    if (head_dim == 128) return dispatch_g<uint16_t, 128>(group, query, a, stream);
-    if (head_dim == 64) return dispatch_g<uint16_t, 64>(group, query, a, stream);
+    if (head_dim == 128) return dispatch_g<uint16_t, 128>(group, query, a, stream, m);
+    if (head_dim == 64) return dispatch_g<uint16_t, 64>(group, query, a, stream, m);
   } else {
-    if (head_dim == 128) return dispatch_g<float, 128>(group, query, a, stream);
-    if (head_dim == 64) return dispatch_g<float, 64>(group, query, a, stream);
+    if (head_dim == 128) return dispatch_g<float, 128>(group, query, a, stream, m);
+    if (head_dim == 64) return dispatch_g<float, 64>(group, query, a, stream, m);
   }
   return -1;
 }
 
 }  // namespace
 
-int launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group, void* stream) {
-  return dispatch(dtype, head_dim, group, false, &a, stream);
+int launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group, void* stream,
+                  const KernelMarks& marks) {
+  return dispatch(dtype, head_dim, group, false, &a, stream, &marks);
 }
 
 int decode_resident_blocks(int dtype, int head_dim, int group) {
-  return dispatch(dtype, head_dim, group, true, nullptr, nullptr);
+  return dispatch(dtype, head_dim, group, true, nullptr, nullptr, nullptr);
 }
 
 }  // namespace duo

@@ -69,6 +69,18 @@ Workspace workspace(duo_cache* c) {
 
 namespace {
 
+// The next event pair of a kernel timer, or none when the timer is off or full.
+KernelMarks next_marks(duo_cache* c, int kind) {
+  KernelMarks m;
+  duo_cache::Timer& t = c->timers[kind];
+  if (2 * (t.used + 1) <= (int)t.ev.size()) {
+    m.begin = t.ev[2 * t.used];
+    m.end = t.ev[2 * t.used + 1];
+    ++t.used;
+  }
+  return m;
+}
+
 // Shared by duo_attn_decode (k == v == null) and duo_decode_step.
 duo_status decode_impl(duo_cache* c, int32_t layer, const void* q, const void* k, const void* v,
                        void* out, float* lse, void* stream) {
@@ -121,7 +133,9 @@ duo_status decode_impl(duo_cache* c, int32_t layer, const void* q, const void* k
   a.out_f32 = c->cfg.out_dtype == DUO_F32;
   std::memcpy(a.ret_kv, li.ret_kv, sizeof(a.ret_kv));
   std::memcpy(a.str_kv, li.str_kv, sizeof(a.str_kv));
-  if (launch_decode(a, c->cfg.dtype, c->cfg.head_dim, group, stream) != 0) return DUO_ERR_HIP;
+  if (launch_decode(a, c->cfg.dtype, c->cfg.head_dim, group, stream,
+                    next_marks(c, DUO_TIMING_DECODE)) != 0)
+    return DUO_ERR_HIP;
   if (fused)
     for (int32_t b = 0; b < c->cfg.batch; ++b) len_of(c, layer, b) += 1;
   return DUO_OK;
@@ -252,9 +266,34 @@ duo_status duo_attn_prefill(duo_cache* c, int32_t layer, int32_t seq, const void
   a.part_o = (float*)ws;
   a.part_ml = (float*)(ws + ((uint64_t)c->cfg.prefill_tiles * kPrefillRows * D * 4 + kAlign - 1) /
                                 kAlign * kAlign);
-  const int rc = launch_prefill(a, c->cfg.dtype, c->cfg.head_dim, group, stream);
+  if (c->cfg.dtype != DUO_BF16) return DUO_ERR_UNSUPPORTED;
+  const int rc = launch_prefill(a, c->cfg.dtype, c->cfg.head_dim, group, stream,
+                                next_marks(c, DUO_TIMING_PREFILL));
   if (rc == -1) return DUO_ERR_UNSUPPORTED;
   if (rc != 0) return DUO_ERR_HIP;
+  return DUO_OK;
+}
+
+duo_status duo_timing_enable(duo_cache* c, int32_t max_records) {
+  if (!c || max_records < 0 || max_records > kMaxTimingRecords) return DUO_ERR_INVALID;
+  for (duo_cache::Timer& t : c->timers) {
+    destroy_events(&t.ev);
+    t.used = 0;
+    if (max_records > 0 && create_events(2 * max_records, &t.ev) != 0) {
+      for (duo_cache::Timer& u : c->timers) destroy_events(&u.ev);
+      return DUO_ERR_HIP;
+    }
+  }
+  return DUO_OK;
+}
+
+duo_status duo_timing_read(duo_cache* c, int32_t kind, double* total_ms, int32_t* records) {
+  if (!c || kind < DUO_TIMING_DECODE || kind > DUO_TIMING_PREFILL || !total_ms || !records)
+    return DUO_ERR_INVALID;
+  duo_cache::Timer& t = c->timers[kind];
+  *records = t.used;
+  if (pairs_elapsed_ms(t.ev, t.used, total_ms) != 0) return DUO_ERR_HIP;
+  t.used = 0;
   return DUO_OK;
 }
 

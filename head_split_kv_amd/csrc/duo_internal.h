@@ -17,6 +17,7 @@ constexpr int kDefaultPrefillTiles = 2048;
 constexpr int kMaxPrefillTiles = 65536;
 constexpr int kPrefillRows = 128;  // query rows per prefill block (and per partial tile)
 constexpr uint64_t kAlign = 256;
+constexpr int kMaxTimingRecords = 1 << 16;  // event pairs per kernel timer
 
 // Per-layer head partition. For KV head j: cls_idx[j] >= 0 is its index among the layer's
 // retrieval heads; cls_idx[j] < 0 encodes streaming index -(cls_idx[j] + 1).
@@ -101,11 +102,28 @@ struct PrefillArgs {
   int32_t c0[kMaxBatch];  // chunk start (current length) of each sequence b0 .. b0+nb-1
 };
 
+// A pair of HIP events (hipEvent_t, or null) that a launcher records on its stream right
+// before and right after the main kernel of its family (kernel timing).
+struct KernelMarks {
+  void* begin = nullptr;
+  void* end = nullptr;
+};
+
 // Launchers (one translation unit per kernel family). They return a hipError_t value as int.
 int launch_reset(const ResetArgs& a, void* stream);
 int launch_append(const AppendArgs& a, int dtype, void* stream);
-int launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group, void* stream);
-int launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int group, void* stream);
+int launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group, void* stream,
+                  const KernelMarks& marks);
+int launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int group, void* stream,
+                   const KernelMarks& marks);
+
+// HIP events of the kernel timers (cache_kernels.hip); hipError_t values as int.
+int create_events(int n, std::vector<void*>* out);
+void destroy_events(std::vector<void*>* ev);
+int record_event(void* event, void* stream);
+// Sum of the elapsed times of the pairs (ev[2i], ev[2i+1]), i < pairs, after waiting for
+// the last one.
+int pairs_elapsed_ms(const std::vector<void*>& ev, int pairs, double* total_ms);
 // Decode blocks of this variant that are resident on the device at once (512 if unknown).
 int decode_resident_blocks(int dtype, int head_dim, int group);
 // Prefill blocks of this variant that are resident on the device at once (512 if unknown).
@@ -134,4 +152,12 @@ struct duo_cache {
   int32_t force_splits = 0;
   int esize = 0;
   float scale = 0.f;
+  // kernel timers, indexed by duo_timing_kind: 2 * capacity events and the pairs used
+  struct Timer {
+    std::vector<void*> ev;
+    int32_t used = 0;
+  } timers[2];
+  ~duo_cache() {
+    for (Timer& t : timers) duo::destroy_events(&t.ev);
+  }
 };

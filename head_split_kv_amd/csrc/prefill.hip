@@ -469,10 +469,12 @@ struct Variant {
     cached = cus * per_cu;
     return cached;
   }
-  static int launch(const PrefillArgs& a, void* stream) {
+  static int launch(const PrefillArgs& a, void* stream, const KernelMarks& marks) {
     const int64_t blocks = (int64_t)a.nb * a.n_qt * ((int64_t)a.Hr * a.nsplit + a.Hs);
+    if (marks.begin) (void)hipEventRecord((hipEvent_t)marks.begin, (hipStream_t)stream);
     hipLaunchKernelGGL((prefill_kernel<D, G>), dim3((unsigned)blocks), dim3(kThreads), 0,
                        (hipStream_t)stream, a);
+    if (marks.end) (void)hipEventRecord((hipEvent_t)marks.end, (hipStream_t)stream);
     if (a.nsplit > 1 && a.Hr > 0) {
       const int64_t mblocks = (int64_t)a.nb * a.Hr * a.n_qt * (kRows / kMergeRows);
       hipLaunchKernelGGL((prefill_merge_kernel<D, G>), dim3((unsigned)mblocks),
@@ -483,37 +485,39 @@ struct Variant {
 };
 
 template <int D, int G>
-int run(bool query, const PrefillArgs* a, void* stream) {
-  return query ? Variant<D, G>::resident_blocks() : Variant<D, G>::launch(*a, stream);
+int run(bool query, const PrefillArgs* a, void* stream, const KernelMarks* m) {
+  return query ? Variant<D, G>::resident_blocks() : Variant<D, G>::launch(*a, stream, *m);
 }
 
 template <int D>
-int dispatch_g(int group, bool query, const PrefillArgs* a, void* stream) {
+int dispatch_g(int group, bool query, const PrefillArgs* a, void* stream, const KernelMarks* m) {
   switch (group) {
-    case 1: return run<D, 1>(query, a, stream);
-    case 2: return run<D, 2>(query, a, stream);
-    case 4: return run<D, 4>(query, a, stream);
-    case 8: return run<D, 8>(query, a, stream);
+    case 1: return run<D, 1>(query, a, stream, m);
+    case 2: return run<D, 2>(query, a, stream, m);
+    case 4: return run<D, 4>(query, a, stream, m);
+    case 8: return run<D, 8>(query, a, stream, m);
   }
   return -1;
 }
 
-int dispatch(int head_dim, int group, bool query, const PrefillArgs* a, void* stream) {
-  if (head_dim == 128) return dispatch_g<128>(group, query, a, stream);
-  if (head_dim == 64) return dispatch_g<64>(group, query, a, stream);
+int dispatch(int head_dim, int group, bool query, const PrefillArgs* a, void* stream,
+             const KernelMarks* m) {
+  if (head_dim == 128) return dispatch_g<128>(group, query, a, stream, m);
+  if (head_dim == 64) return dispatch_g<64>(group, query, a, stream, m);
   return -1;
 }
 
 }  // namespace
 
 // Returns -1 for a variant that is not built (fp32 inputs), else a hipError_t value.
-int launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int group, void* stream) {
+int launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int group, void* stream,
+                   const KernelMarks& marks) {
   if (dtype != DUO_BF16) return -1;
-  return dispatch(head_dim, group, false, &a, stream);
+  return dispatch(head_dim, group, false, &a, stream, &marks);
 }
 
 int prefill_resident_blocks(int head_dim, int group) {
-  return dispatch(head_dim, group, true, nullptr, nullptr);
+  return dispatch(head_dim, group, true, nullptr, nullptr, nullptr);
 }
 
 }  // namespace duo

@@ -169,6 +169,21 @@ duo_status duo_kv_bytes(const duo_config* cfg, int32_t layer, const int32_t* seq
  * on it beyond floating-point rounding. Host only. */
 duo_status duo_set_decode_splits(duo_cache* cache, int32_t splits);
 
+/* Kernel timers (a measurement aid, off by default). duo_timing_enable(cache, n) creates n
+ * HIP event pairs per kind on the current device (n <= 65536; n = 0 switches timing off and
+ * frees the events) and resets the counts; DUO_ERR_HIP if an event cannot be created. While
+ * on, each duo_attn_decode / duo_decode_step records one pair on its stream immediately
+ * before and after its split attention kernel (the split merge kernel is outside the pair),
+ * and each duo_attn_prefill one pair around its attention kernel (the merge outside), until
+ * n pairs of that kind are used; later calls run unrecorded. duo_timing_read waits for the
+ * last recorded event of `kind`, writes the summed elapsed time of its pairs in
+ * milliseconds and their count, and resets that count so the pairs are reused. Calls that
+ * overlap on several streams still record, but then a pair spans whatever else the device
+ * ran between its two events. */
+typedef enum { DUO_TIMING_DECODE = 0, DUO_TIMING_PREFILL = 1 } duo_timing_kind;
+duo_status duo_timing_enable(duo_cache* cache, int32_t max_records);
+duo_status duo_timing_read(duo_cache* cache, int32_t kind, double* total_ms, int32_t* records);
+
 /* Static text for a status code. */
 const char* duo_status_string(duo_status status);
 

@@ -183,6 +183,16 @@ def test_error_paths_leave_state_unchanged():
     assert L.duo_set_decode_splits(fc.h, -1) == N.DUO_ERR_INVALID
     assert L.duo_set_decode_splits(fc.h, 257) == N.DUO_ERR_INVALID
     assert L.duo_set_decode_splits(fc.h, 7) == N.DUO_OK
+    # kernel timers: argument checks only (creating events needs a device)
+    ms, cnt = ctypes.c_double(1.0), ctypes.c_int32(5)
+    assert L.duo_timing_enable(fc.h, -1) == N.DUO_ERR_INVALID
+    assert L.duo_timing_enable(fc.h, (1 << 16) + 1) == N.DUO_ERR_INVALID
+    assert L.duo_timing_enable(None, 4) == N.DUO_ERR_INVALID
+    assert L.duo_timing_enable(fc.h, 0) == N.DUO_OK  # off: nothing to create
+    assert L.duo_timing_read(fc.h, 2, ctypes.byref(ms), ctypes.byref(cnt)) == N.DUO_ERR_INVALID
+    assert L.duo_timing_read(fc.h, 0, None, ctypes.byref(cnt)) == N.DUO_ERR_INVALID
+    assert L.duo_timing_read(fc.h, 1, ctypes.byref(ms), ctypes.byref(cnt)) == N.DUO_OK
+    assert (ms.value, cnt.value) == (0.0, 0)
     assert np.array_equal(fc.lengths(), before)
     assert L.duo_cache_destroy(None) == N.DUO_OK
     fc.close()
