@@ -264,7 +264,7 @@ duo_status duo_attn_prefill(duo_cache* c, int32_t layer, int32_t seq, const void
   const uint64_t D = c->cfg.head_dim;
   char* ws = c->arena + c->lay.workspace_off;
   a.part_o = (float*)ws;
-  a.part_ml = (float*)(ws + ((uint64_t)c->cfg.prefill_tiles * kPrefillRows * D * 4 + kAlign - 1) /
+  a.part_ml = (float*)(ws + ((uint64_t)c->cfg.prefill_tiles * kPrefillTileRows * D * 4 + kAlign - 1) /
                                 kAlign * kAlign);
   if (c->cfg.dtype != DUO_BF16) return DUO_ERR_UNSUPPORTED;
   const int rc = launch_prefill(a, c->cfg.dtype, c->cfg.head_dim, group, stream,

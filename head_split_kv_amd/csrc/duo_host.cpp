@@ -92,8 +92,8 @@ duo_status build_layout(const duo_config* cfg, duo_layout* lay, std::vector<Laye
   out.workspace_off = off;
   const uint64_t ptiles = cfg->prefill_tiles ? cfg->prefill_tiles : kDefaultPrefillTiles;
   const uint64_t ws_decode = align_up(B * Hq * splits * D * 4) + align_up(B * Hq * splits * 2 * 4);
-  const uint64_t ws_prefill = align_up(ptiles * kPrefillRows * D * 4) +
-                              align_up(ptiles * kPrefillRows * 2 * 4);
+  const uint64_t ws_prefill = align_up(ptiles * kPrefillTileRows * D * 4) +
+                              align_up(ptiles * kPrefillTileRows * 2 * 4);
   const uint64_t ws = ws_decode > ws_prefill ? ws_decode : ws_prefill;
   out.workspace_bytes = ws;
   off = align_up(off + ws);
@@ -143,7 +143,8 @@ int choose_prefill_splits(int32_t nb, int32_t m, int32_t c_max, int32_t c_sum, i
   int64_t s = (t_ret_max + target - 1) / target;
   if (s > 32) s = 32;
   const int64_t items = (int64_t)nb * n_ret * n_qt;
-  if (s * items > prefill_tiles) s = prefill_tiles / items;
+  const int64_t capacity = (int64_t)prefill_tiles * kPrefillTileRows / kPrefillRows;
+  if (s * items > capacity) s = capacity / items;
   if (s < 1) s = 1;
   return (int)s;
 }

@@ -15,7 +15,8 @@ constexpr int kDefaultSplits = 256;
 constexpr int kMaxSplits = 1024;
 constexpr int kDefaultPrefillTiles = 2048;
 constexpr int kMaxPrefillTiles = 65536;
-constexpr int kPrefillRows = 128;  // query rows per prefill block (and per partial tile)
+constexpr int kPrefillRows = 128;      // query rows per prefill block (and per partial tile)
+constexpr int kPrefillTileRows = 128;  // rows of the workspace unit counted by prefill_tiles
 constexpr uint64_t kAlign = 256;
 constexpr int kMaxTimingRecords = 1 << 16;  // event pairs per kernel timer
 

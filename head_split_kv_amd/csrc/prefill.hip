@@ -90,12 +90,20 @@ __device__ __forceinline__ int swz(int r) {
   else return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
 }
 
+// Maximum and sum over the lane pair (l, l ^ 32) that shares one query row.
+__device__ __forceinline__ float max_pair32(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+__device__ __forceinline__ float sum_pair32(float x) { return x + __shfl_xor(x, 32); }
+
 template <int D, int G>
 __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
   using Gm = Geo<D>;
   constexpr int NCH = Gm::kChunks;
   constexpr int RB = Gm::kRowBytes;
   constexpr int kQpb = kRows / G;  // positions per block
+  constexpr int kDma = Gm::kDmaPerWave;
+  constexpr int kHalfSlabs = Gm::kSlabs / 2;  // QK^T K-slabs of the next tile per PV step
+  // Two K buffers, two V buffers (+ key positions): in the iteration of tile i the waves read
+  // V(i) and K(i+1) while the DMA fills V(i+1) and K(i+2) into the other buffers.
   __shared__ __attribute__((aligned(1024))) char sK0[Gm::kTileBytes];
   __shared__ __attribute__((aligned(1024))) char sK1[Gm::kTileBytes];
   __shared__ __attribute__((aligned(1024))) char sV0[Gm::kTileBytes];
@@ -141,6 +149,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
   const int g = row % G;
   const bool q_valid = q_local < a.m;
   const int p = c0 + (q_valid ? q_local : ql1);
+  // first key of this query's window (every key on a retrieval head)
+  const int win_lo = retrieval ? -0x7FFFFFFF : p - a.R + 1;
 
   // ---- Q^T operand: 16-byte slabs of this lane's query row --------------------------
   bf16x8_t qf[Gm::kSlabs];
@@ -153,10 +163,10 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
   }
 
   // ---- key tiles: cache part, then chunk part ------------------------------------------
+  const int filled = retrieval ? c0 : min(c0, SR);  // cache rows holding a token
   int n_cache_tiles;
   const char* cache_k;
   const char* cache_v;
-  const int32_t* slots = nullptr;
   if (retrieval) {
     n_cache_tiles = (c0 + kBN - 1) / kBN;
     const int64_t base = ((int64_t)b * a.Hr + cls) * a.cap * RB;
@@ -167,7 +177,6 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
     const int64_t base = ((int64_t)b * a.Hs + cls) * SR * RB;
     cache_k = (const char*)a.str_k + base;
     cache_v = (const char*)a.str_v + base;
-    slots = a.slot_pos + (int64_t)b * SR;
   }
   const int n_chunk_tiles = ql1 / kBN + 1;  // causal limit: no key after the last query
   const int n_tiles = n_cache_tiles + n_chunk_tiles;
@@ -192,47 +201,70 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
     if (k0 >= S && k1 < p_min - R + 1) return -1;  // left of every window
     return (all_rows && k1 <= p_min && k0 >= p_max - R + 1) ? 0 : 1;
   };
-  // key row r of tile ti: source rows (always finite data in bounds) and its position
-  auto tile_row = [&](int ti, int r, const char*& kp, const char*& vp) -> int {
-    int src, pos;
+  auto next_visible = [&](int ti) {
+    while (ti < t_end && classify(ti) < 0) ++ti;
+    return ti;
+  };
+
+  // Position of key row r of tile ti (kNoPos for an empty slot or padding). A streaming
+  // cache slot holds the latest token t < c0 that maps to it: t = idx below S, else the
+  // largest t <= c0 - 1 with t = idx (mod R) (the ring's slot map, inverted).
+  auto key_pos = [&](int ti, int r) -> int {
     if (ti < n_cache_tiles) {
       const int idx = ti * kBN + r;
-      if (retrieval) {
-        src = idx < c0 ? idx : c0 - 1;
-        pos = idx < c0 ? idx : kNoPos;
-      } else {
-        const int t = idx < SR ? slots[idx] : -1;
-        src = t >= 0 ? idx : 0;  // empty slot: read slot 0 (filled once c > 0), weight 0
-        pos = t >= 0 ? t : kNoPos;
-      }
-      kp = cache_k + (int64_t)src * RB;
-      vp = cache_v + (int64_t)src * RB;
-      return pos;
+      if (idx >= filled) return kNoPos;
+      if (retrieval || idx < S) return idx;
+      const int last = c0 - 1;
+      return last - (last - idx) % R;
     }
     const int i = (ti - n_cache_tiles) * kBN + r;
-    src = i < a.m ? i : a.m - 1;
-    kp = chunk_k + (int64_t)src * chunk_stride;
-    vp = chunk_v + (int64_t)src * chunk_stride;
     return i < a.m ? c0 + i : kNoPos;
   };
-  // DMA of tile ti into one LDS buffer pair: wave w moves 1 KB blocks w*kDmaPerWave + i
-  auto issue = [&](int ti, char* sk, char* sv, int* sp) {
+
+  // Per-lane DMA geometry: for 1 KB block i of this wave, the tile row this lane copies and
+  // the byte offset of the logical chunk that lands in this lane's (swizzled) LDS slot.
+  auto dma_row = [&](int i) { return (wave * kDma + i) * Gm::kRowsPerKb + lane / NCH; };
+  auto dma_col = [&](int i) { return ((lane % NCH) ^ swz<NCH>(dma_row(i))) * 16; };
+  // Source of tile ti: base pointers, row stride, first source row and the number of rows
+  // that hold data (later rows are clamped onto the last one, or onto row 0 for empty
+  // streaming slots: finite data in bounds whose weight is zero).
+  auto tile_src = [&](int ti, const char*& kb, const char*& vb, int64_t& stride, int& row0,
+                      int& nrows) {
+    if (ti < n_cache_tiles) {
+      kb = cache_k;
+      vb = cache_v;
+      stride = RB;
+      row0 = ti * kBN;
+      nrows = filled - row0;
+    } else {
+      kb = chunk_k;
+      vb = chunk_v;
+      stride = chunk_stride;
+      row0 = (ti - n_cache_tiles) * kBN;
+      nrows = a.m - row0;
+    }
+  };
+  auto src_row = [&](int r, int row0, int nrows) {
+    return r < nrows ? row0 + r : (nrows > 0 ? row0 + nrows - 1 : 0);
+  };
+  // One tensor of tile ti into LDS (rows past the data clamped).
+  auto issue_one = [&](int ti, bool is_v, char* dst) {
+    const char *kb, *vb;
+    int64_t stride;
+    int row0, nrows;
+    tile_src(ti, kb, vb, stride, row0, nrows);
+    const char* src = is_v ? vb : kb;
 #pragma unroll
-    for (int i = 0; i < Gm::kDmaPerWave; ++i) {
-      const int kb = wave * Gm::kDmaPerWave + i;
-      const int r = kb * Gm::kRowsPerKb + lane / NCH;
-      const int c = (lane % NCH) ^ swz<NCH>(r);  // logical chunk landing at this lane's slot
-      const char *kp, *vp;
-      tile_row(ti, r, kp, vp);
-      __builtin_amdgcn_global_load_lds((const void*)(kp + c * 16), (lds_void_t*)(sk + kb * 1024),
-                                       16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vp + c * 16), (lds_void_t*)(sv + kb * 1024),
-                                       16, 0, 0);
+    for (int i = 0; i < kDma; ++i) {
+      const int sr = src_row(dma_row(i), row0, nrows);
+      __builtin_amdgcn_global_load_lds((const void*)(src + sr * stride + dma_col(i)),
+                                       (lds_void_t*)(dst + (wave * kDma + i) * 1024), 16, 0, 0);
     }
-    if (tid < kBN) {
-      const char *kp, *vp;
-      sp[tid] = tile_row(ti, tid, kp, vp);
-    }
+  };
+  auto issue_k = [&](int ti, char* sk) { issue_one(ti, false, sk); };
+  auto issue_v = [&](int ti, char* sv, int* sp) {
+    issue_one(ti, true, sv);
+    if (tid < kBN) sp[tid] = key_pos(ti, tid);
   };
 
   // ---- accumulators --------------------------------------------------------------
@@ -244,22 +276,27 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
   float l = 0.f;       // partial softmax sum over this lane's keys
   const float c2 = a.scale_log2, inv_c2 = 1.f / c2;
 
-  auto compute = [&](int kind, const char* sk, const char* sv, const int* sp) {
-    // S^T = K Q^T: two 32-key blocks; element 4a + b holds key 8a + 4half + b of the block
-    f32x16_t s[2];
+  // QK^T K-slabs [k0, k0 + n) of 32-key block blk of a tile: S^T += K Q^T (keys as MFMA
+  // rows); element 4a + b of s[blk] holds key 8a + 4half + b of the block.
+  // The first part of a block (k0 == 0) starts from a zero accumulator.
+  auto qk_part = [&](f32x16_t& s, const char* sk, int blk, int k0) {
+    const int r = blk * 32 + col;
+    const char* krow = sk + r * RB;
+    const int sw = swz<NCH>(r);
+    bf16x8_t kf[kHalfSlabs];
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      s[blk] = f32x16_t{};
-      const int r = blk * 32 + col;
-      const char* krow = sk + r * RB;
-      const int sw = swz<NCH>(r);
+    for (int k = 0; k < kHalfSlabs; ++k)
+      kf[k] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(krow + ((2 * (k0 + k) + half) ^ sw) * 16));
 #pragma unroll
-      for (int k = 0; k < Gm::kSlabs; ++k) {
-        const int c = (2 * k + half) ^ sw;
-        const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, *(const uint4*)(krow + c * 16));
-        s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[k], s[blk], 0, 0, 0);
-      }
-    }
+    for (int k = 0; k < kHalfSlabs; ++k)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[k], qf[k0 + k],
+                                                  (k0 == 0 && k == 0) ? f32x16_t{} : s, 0, 0, 0);
+  };
+
+  // One pipelined iteration: softmax and PV of the current tile (scores sc, V in sv, key
+  // positions in sp) interleaved with the scores of the next tile (K in skn) into sn.
+  auto iterate = [&](f32x16_t (&sc)[2], f32x16_t (&sn)[2], int kind, const char* skn,
+                     const char* sv, const int* sp) {
     if (kind != 0) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
@@ -270,20 +307,22 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int t = tt[e];
-            const bool vis = t <= p && (retrieval || t < S || t >= p - R + 1);
-            if (!vis) s[blk][4 * a4 + e] = kNegInf;
+            const bool vis = (t <= p) & ((t < S) | (t >= win_lo));
+            sc[blk][4 * a4 + e] = vis ? sc[blk][4 * a4 + e] : kNegInf;
           }
         }
     }
-    // online softmax (row statistics over this lane and lane ^ 32)
+    // online softmax statistics (row over this lane and lane ^ 32); the rescale branch is
+    // taken by the whole wave when any row's maximum moves (al = 1 for the others)
     float mx = kNegInf;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[blk][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    if (mx > thr) {
-      const float mn = mx * c2;
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[blk][e]);
+    mx = max_pair32(mx);
+    const bool up = mx > thr;
+    if (__builtin_amdgcn_ballot_w64(up)) {
+      const float mn = up ? mx * c2 : m;
       const float al = fexp2(m - mn);
       l *= al;
 #pragma unroll
@@ -291,13 +330,13 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[db][e] *= al;
       m = mn;
-      thr = (mn + kTau) * inv_c2;
+      thr = up ? (mn + kTau) * inv_c2 : thr;
     }
-    // O^T += V^T P^T over four 16-key slabs; slab k holds keys 16k + {4half..4half+3} then
+    // PV over four 16-key slabs; slab k holds keys 16k + {4half..4half+3} then
     // 16k + 8 + {4half..4half+3} in both operands (elements 8(k&1) .. 8(k&1)+7 of block
     // k>>1 of S^T). A transposed read gives lane l the four keys k0..k0+3 at
-    // d = 32db + (l & 31), with k0 = 16k + 8part + 4half. P = hi + lo is formed per slab,
-    // right before its products.
+    // d = 32db + (l & 31), with k0 = 16k + 8part + 4half. Each slab step also advances a
+    // quarter of the next tile's scores.
     const int gi = lane >> 4, jj = lane & 15, e4 = jj >> 2, q4 = jj & 3;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -305,13 +344,14 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
       uint32_t hw[4], lw[4];
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        const float p0 = fexp2(__builtin_fmaf(s[blk][e0 + e], c2, -m));
-        const float p1 = fexp2(__builtin_fmaf(s[blk][e0 + e + 1], c2, -m));
+        const float p0 = fexp2(__builtin_fmaf(sc[blk][e0 + e], c2, -m));
+        const float p1 = fexp2(__builtin_fmaf(sc[blk][e0 + e + 1], c2, -m));
         l += p0 + p1;
         split_bf16(p0, p1, hw[e / 2], lw[e / 2]);
       }
       const bf16x8_t pfh = __builtin_bit_cast(bf16x8_t, uint4{hw[0], hw[1], hw[2], hw[3]});
       const bf16x8_t pfl = __builtin_bit_cast(bf16x8_t, uint4{lw[0], lw[1], lw[2], lw[3]});
+      bf16x8_t vf[Gm::kDBlocks];
 #pragma unroll
       for (int db = 0; db < Gm::kDBlocks; ++db) {
         s16x4_t vt[2];
@@ -325,40 +365,63 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
         }
         const uint2 v0 = __builtin_bit_cast(uint2, vt[0]);
         const uint2 v1 = __builtin_bit_cast(uint2, vt[1]);
-        const uint4 vw = {v0.x, v0.y, v1.x, v1.y};
-        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, vw);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pfh, o[db], 0, 0, 0);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pfl, o[db], 0, 0, 0);
+        vf[db] = __builtin_bit_cast(bf16x8_t, uint4{v0.x, v0.y, v1.x, v1.y});
       }
+      __builtin_amdgcn_s_setprio(1);
+      qk_part(sn[k >> 1], skn, k >> 1, (k & 1) * kHalfSlabs);
+#pragma unroll
+      for (int db = 0; db < Gm::kDBlocks; ++db)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pfh, o[db], 0, 0, 0);
+#pragma unroll
+      for (int db = 0; db < Gm::kDBlocks; ++db)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pfl, o[db], 0, 0, 0);
+      __builtin_amdgcn_s_setprio(0);
     }
   };
 
-  // ---- tile loop: DMA of the next tile overlaps the math of this one -------------------
-  auto next_visible = [&](int ti) {
-    while (ti < t_end && classify(ti) < 0) ++ti;
-    return ti;
-  };
-  int ti = next_visible(t_begin);
-  if (ti < t_end) issue(ti, sK0, sV0, sPos0);
-  __syncthreads();
-  bool odd = false;
-  while (ti < t_end) {
-    const int next = next_visible(ti + 1);
-    const int kind = classify(ti);
-    if (!odd) {
-      if (next < t_end) issue(next, sK1, sV1, sPos1);
-      compute(kind, sK0, sV0, sPos0);
-    } else {
-      if (next < t_end) issue(next, sK0, sV0, sPos0);
-      compute(kind, sK1, sV1, sPos1);
-    }
+  // ---- tile loop ------------------------------------------------------------------
+  // Prologue: K, V of the first visible tile and K of the second; scores of the first.
+  // Iteration i (tiles cur = t_i, nxt = t_i+1, nn = t_i+2): DMA of K(nn) into the K buffer
+  // of cur and of V(nxt) into the other V buffer, then iterate(); the barrier at its end
+  // makes both DMAs visible and frees the buffers read in it. Past the last tile the
+  // "next" scores are computed from a stale buffer and discarded.
+  f32x16_t sA[2], sB[2];
+  int cur = next_visible(t_begin);
+  if (cur < t_end) {
+    int nxt = next_visible(cur + 1);
+    issue_k(cur, sK0);
+    issue_v(cur, sV0, sPos0);
+    if (nxt < t_end) issue_k(nxt, sK1);
     __syncthreads();
-    ti = next;
-    odd = !odd;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) qk_part(sA[q >> 1], sK0, q >> 1, (q & 1) * kHalfSlabs);
+    int kind = classify(cur);
+    while (true) {
+      // even iteration: scores of cur in sA, V(cur) in sV0, K(nxt) in sK1
+      int nn = nxt < t_end ? next_visible(nxt + 1) : t_end;
+      if (nn < t_end) issue_k(nn, sK0);
+      if (nxt < t_end) issue_v(nxt, sV1, sPos1);
+      iterate(sA, sB, kind, sK1, sV0, sPos0);
+      __syncthreads();
+      if (nxt >= t_end) break;
+      cur = nxt;
+      nxt = nn;
+      kind = classify(cur);
+      // odd iteration: scores of cur in sB, V(cur) in sV1, K(nxt) in sK0
+      nn = nxt < t_end ? next_visible(nxt + 1) : t_end;
+      if (nn < t_end) issue_k(nn, sK1);
+      if (nxt < t_end) issue_v(nxt, sV0, sPos0);
+      iterate(sB, sA, kind, sK0, sV1, sPos1);
+      __syncthreads();
+      if (nxt >= t_end) break;
+      cur = nxt;
+      nxt = nn;
+      kind = classify(cur);
+    }
   }
 
   // ---- epilogue ---------------------------------------------------------------------
-  const float lt = l + __shfl_xor(l, 32);
+  const float lt = sum_pair32(l);
   if (nsplit > 1) {  // fp32 partial of this key range
     const int64_t item = ((int64_t)bi * a.Hr + cls) * a.n_qt + qt;
     const int64_t prow = (item * nsplit + split) * kRows + row;
