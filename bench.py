@@ -165,7 +165,7 @@ def decode_leg(args, torch, hsk, W, N):
                                retrieval_mask=[mask])
     kv_bytes = []
     for s in range(args.warmup, total_steps):
-        kv_bytes.append(hsk.duo_kv_bytes(cfg1, 0, [n0 + s + 1])[1])
+        kv_bytes.append(hsk.duo_kv_bytes(cfg1, [n0 + s + 1], 0)[1])
     io_bytes = 2 * w.hq * w.d * 2 + 2 * 2 * w.hkv * w.d * 2  # q in, out, new K/V in + stored
     step_bytes = sum(kv_bytes) / len(kv_bytes) + io_bytes
     us_layer = ms_per_step * 1e3 / L
@@ -184,7 +184,7 @@ def decode_leg(args, torch, hsk, W, N):
             decode(h, layer, ctypes.c_void_p(qp), op, None, stream)
     dec_ms = tm.stop_ms() / (reps * L)
     n_final = n0 + total_steps
-    dec_bytes = hsk.duo_kv_bytes(cfg1, 0, [n_final])[1] + 2 * w.hq * w.d * 2
+    dec_bytes = hsk.duo_kv_bytes(cfg1, [n_final], 0)[1] + 2 * w.hq * w.d * 2
     dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
     result = dict(
         workload=w, layers=L, ms_per_step=ms_per_step, us_layer=us_layer, gbs=gbs,

@@ -49,13 +49,13 @@ def duo_layout_query(cfg: DuoConfig) -> DuoLayout:
     return lay
 
 
-def duo_kv_bytes(cfg: DuoConfig, layer: int, seq_lens: Sequence[int]):
+def duo_kv_bytes(cfg: DuoConfig, seq_lens: Sequence[int], layer: int):
     """(full-attention bytes, split-layout bytes) one layer holds for these lengths."""
     lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
     full = ctypes.c_uint64()
     duo = ctypes.c_uint64()
-    check(lib().duo_kv_bytes(ctypes.byref(cfg), layer,
-                             lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+    check(lib().duo_kv_bytes(ctypes.byref(cfg),
+                             lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), layer,
                              ctypes.byref(full), ctypes.byref(duo)), "duo_kv_bytes")
     return full.value, duo.value
 
@@ -91,10 +91,9 @@ class DuoCache:
         off = (-self._arena_raw.data_ptr()) % 256
         self.arena = self._arena_raw[off:off + nbytes]
         h = ctypes.c_void_p()
-        check(lib().duo_cache_create(ctypes.byref(self.cfg), ctypes.c_void_p(self.arena.data_ptr()),
-                                     nbytes, ctypes.byref(h)), "duo_cache_create")
+        check(lib().duo_cache_init(ctypes.byref(self.cfg), ctypes.c_void_p(self.arena.data_ptr()),
+                                   nbytes, _stream(stream), ctypes.byref(h)), "duo_cache_init")
         self.handle = h
-        duo_cache_reset(self, stream)
 
     @property
     def retrieval_mask(self) -> np.ndarray:
@@ -130,6 +129,9 @@ class DuoCache:
     def lengths(self):
         return duo_cache_lengths(self)
 
+    def set_lengths(self, lens, stream=None):
+        return duo_cache_set_lengths(self, lens, stream)
+
 
 def _check_tensor(t: torch.Tensor, shape, dtype, device, name):
     if not isinstance(t, torch.Tensor):
@@ -149,6 +151,13 @@ def _check_tensor(t: torch.Tensor, shape, dtype, device, name):
 
 def duo_cache_reset(cache: DuoCache, stream=None) -> None:
     check(lib().duo_cache_reset(cache.handle, _stream(stream)), "duo_cache_reset")
+
+
+def duo_cache_set_lengths(cache: DuoCache, lens, stream=None) -> None:
+    """Set every length (int ``[L, B]``) and rebuild the slot tables to match."""
+    a = np.ascontiguousarray(np.asarray(lens, dtype=np.int32).reshape(cache.num_layers, cache.batch))
+    check(lib().duo_cache_set_lengths(cache.handle, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                      _stream(stream)), "duo_cache_set_lengths")
 
 
 def duo_kv_append(cache: DuoCache, layer: int, seq: int, k: torch.Tensor, v: torch.Tensor,

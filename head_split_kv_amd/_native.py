@@ -14,7 +14,8 @@ DUO_F32, DUO_BF16 = 0, 1
 
 # Every symbol include/duo.h declares.
 EXPORTS = (
-    "duo_layout_query", "duo_cache_create", "duo_cache_reset", "duo_cache_destroy",
+    "duo_layout_query", "duo_cache_create", "duo_cache_init", "duo_cache_reset",
+    "duo_cache_set_lengths", "duo_cache_destroy",
     "duo_kv_append", "duo_attn_decode", "duo_decode_step", "duo_attn_prefill",
     "duo_slot_positions",
     "duo_cache_lengths", "duo_kv_bytes", "duo_set_decode_splits", "duo_timing_enable",
@@ -74,7 +75,9 @@ def lib() -> ctypes.CDLL:
     sig = {
         "duo_layout_query": (st, [P(DuoConfig), P(DuoLayout)]),
         "duo_cache_create": (st, [P(DuoConfig), vp, ctypes.c_uint64, P(vp)]),
+        "duo_cache_init": (st, [P(DuoConfig), vp, ctypes.c_uint64, vp, P(vp)]),
         "duo_cache_reset": (st, [vp, vp]),
+        "duo_cache_set_lengths": (st, [vp, P(i32), vp]),
         "duo_cache_destroy": (st, [vp]),
         "duo_kv_append": (st, [vp, i32, i32, vp, vp, i32, vp]),
         "duo_attn_decode": (st, [vp, i32, vp, vp, vp, vp]),
@@ -82,7 +85,7 @@ def lib() -> ctypes.CDLL:
         "duo_attn_prefill": (st, [vp, i32, i32, vp, vp, vp, i32, vp, vp, vp]),
         "duo_slot_positions": (st, [vp, i32, P(i32), vp]),
         "duo_cache_lengths": (st, [vp, P(i32)]),
-        "duo_kv_bytes": (st, [P(DuoConfig), i32, P(i32), P(ctypes.c_uint64),
+        "duo_kv_bytes": (st, [P(DuoConfig), P(i32), i32, P(ctypes.c_uint64),
                               P(ctypes.c_uint64)]),
         "duo_set_decode_splits": (st, [vp, i32]),
         "duo_timing_enable": (st, [vp, i32]),

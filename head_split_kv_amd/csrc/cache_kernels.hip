@@ -29,6 +29,21 @@ __device__ __forceinline__ bool survives(int32_t t, int32_t n_end, int32_t S, in
   return t < S || t >= n_end - R;
 }
 
+// Lengths of one layer set to n[b], with the slot table rebuilt to match: slot s holds the
+// latest token t < n that maps to it (t = s for a sink slot; for a ring slot, the latest
+// t <= n - 1 with t = s (mod R), which is one of the last R tokens), or -1.
+__global__ void __launch_bounds__(kThreads) set_lengths_kernel(SetLenArgs a) {
+  const int32_t SR = a.S + a.R;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)a.B * SR) return;
+  const int32_t b = (int32_t)(i / SR), s = (int32_t)(i % SR), n = a.n[b];
+  int32_t pos = -1;
+  if (s < a.S) pos = s < n ? s : -1;
+  else if (n - 1 >= s) pos = s + a.R * ((n - 1 - s) / a.R);
+  a.slot_pos[i] = pos;
+  if (s == 0) a.seq_len[b] = n;
+}
+
 // One thread moves one 16-byte chunk of one K or V row. Work index (outer to inner):
 // tensor (K, V), sequence, token, KV head, chunk; consecutive threads read consecutive
 // bytes of the input. The extra nb*m work items at the end write the slot table.
@@ -138,6 +153,13 @@ int pairs_elapsed_ms(const std::vector<void*>& ev, int pairs, double* total_ms) 
     *total_ms += ms;
   }
   return 0;
+}
+
+int launch_set_lengths(const SetLenArgs& a, void* stream) {
+  const int64_t work = (int64_t)a.B * (a.S + a.R);
+  hipLaunchKernelGGL(set_lengths_kernel, dim3((unsigned)((work + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, (hipStream_t)stream, a);
+  return (int)hipGetLastError();
 }
 
 int copy_d2h_sync(void* dst, const void* src, uint64_t bytes, void* stream) {

@@ -159,6 +159,41 @@ duo_status duo_cache_reset(duo_cache* c, void* stream) {
   return DUO_OK;
 }
 
+duo_status duo_cache_init(const duo_config* cfg, void* arena, uint64_t arena_bytes,
+                          void* stream, duo_cache** out) {
+  duo_cache* c = nullptr;
+  const duo_status st = duo_cache_create(cfg, arena, arena_bytes, &c);
+  if (st != DUO_OK) return st;
+  const duo_status rs = duo_cache_reset(c, stream);
+  if (rs != DUO_OK) {
+    duo_cache_destroy(c);
+    return rs;
+  }
+  *out = c;
+  return DUO_OK;
+}
+
+duo_status duo_cache_set_lengths(duo_cache* c, const int32_t* lens, void* stream) {
+  if (!c || !lens) return DUO_ERR_INVALID;
+  const int32_t L = c->cfg.num_layers, B = c->cfg.batch;
+  for (int64_t i = 0; i < (int64_t)L * B; ++i)
+    if (lens[i] < 0 || lens[i] > c->cfg.capacity) return DUO_ERR_INVALID;
+  for (int32_t layer = 0; layer < L; ++layer) {
+    const LayerPtrs p = layer_ptrs(c, layer);
+    SetLenArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.slot_pos = p.slot_pos;
+    a.seq_len = p.seq_len;
+    a.B = B;
+    a.S = c->cfg.sink;
+    a.R = c->cfg.recent;
+    std::memcpy(a.n, lens + (int64_t)layer * B, sizeof(int32_t) * B);
+    if (launch_set_lengths(a, stream) != 0) return DUO_ERR_HIP;
+    std::memcpy(&len_of(c, layer, 0), lens + (int64_t)layer * B, sizeof(int32_t) * B);
+  }
+  return DUO_OK;
+}
+
 duo_status duo_kv_append(duo_cache* c, int32_t layer, int32_t seq, const void* k,
                          const void* v, int32_t n_new, void* stream) {
   if (!layer_ok(c, layer) || seq < -1 || seq >= c->cfg.batch || n_new < 0)

@@ -201,7 +201,7 @@ duo_status duo_cache_lengths(const duo_cache* cache, int32_t* host_out) {
   return DUO_OK;
 }
 
-duo_status duo_kv_bytes(const duo_config* cfg, int32_t layer, const int32_t* seq_lens,
+duo_status duo_kv_bytes(const duo_config* cfg, const int32_t* seq_lens, int32_t layer,
                         uint64_t* full_attn_bytes, uint64_t* duo_bytes) {
   duo_status st = check_config(cfg);
   if (st != DUO_OK) return st;

@@ -42,6 +42,13 @@ struct ResetArgs {
   int64_t n_len;
 };
 
+struct SetLenArgs {
+  int32_t* slot_pos;  // this layer: [B][S+R]
+  int32_t* seq_len;   // this layer: [B]
+  int32_t B, S, R;
+  int32_t n[kMaxBatch];
+};
+
 struct AppendArgs {
   const void* k;  // [nb][m][Hkv][D]
   const void* v;
@@ -113,6 +120,7 @@ struct KernelMarks {
 // Launchers (one translation unit per kernel family). They return a hipError_t value as int.
 int launch_reset(const ResetArgs& a, void* stream);
 int launch_append(const AppendArgs& a, int dtype, void* stream);
+int launch_set_lengths(const SetLenArgs& a, void* stream);
 int launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group, void* stream,
                   const KernelMarks& marks);
 int launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int group, void* stream,

@@ -209,13 +209,17 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
   // Position of key row r of tile ti (kNoPos for an empty slot or padding). A streaming
   // cache slot holds the latest token t < c0 that maps to it: t = idx below S, else the
   // largest t <= c0 - 1 with t = idx (mod R) (the ring's slot map, inverted).
+  // With bm = (c0 - 1 - S) mod R (once per block), (c0 - 1 - idx) mod R = bm - (idx - S),
+  // plus R when negative, for a ring slot idx in [S, S + R).
+  const int ring_bm = (!retrieval && c0 > S) ? (c0 - 1 - S) % R : 0;
   auto key_pos = [&](int ti, int r) -> int {
     if (ti < n_cache_tiles) {
       const int idx = ti * kBN + r;
       if (idx >= filled) return kNoPos;
       if (retrieval || idx < S) return idx;
-      const int last = c0 - 1;
-      return last - (last - idx) % R;
+      int back = ring_bm - (idx - S);
+      back += back < 0 ? R : 0;
+      return c0 - 1 - back;
     }
     const int i = (ti - n_cache_tiles) * kBN + r;
     return i < a.m ? c0 + i : kNoPos;
@@ -261,11 +265,13 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
                                        (lds_void_t*)(dst + (wave * kDma + i) * 1024), 16, 0, 0);
     }
   };
-  auto issue_k = [&](int ti, char* sk) { issue_one(ti, false, sk); };
-  auto issue_v = [&](int ti, char* sv, int* sp) {
-    issue_one(ti, true, sv);
+  // Key positions of a tile (LDS, for the masks). Written before the iteration's DMAs are
+  // issued: any wait on a vector load in between would also wait for those.
+  auto write_pos = [&](int ti, int* sp) {
     if (tid < kBN) sp[tid] = key_pos(ti, tid);
   };
+  auto issue_k = [&](int ti, char* sk) { issue_one(ti, false, sk); };
+  auto issue_v = [&](int ti, char* sv) { issue_one(ti, true, sv); };
 
   // ---- accumulators --------------------------------------------------------------
   f32x16_t o[Gm::kDBlocks];
@@ -367,7 +373,6 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
         const uint2 v1 = __builtin_bit_cast(uint2, vt[1]);
         vf[db] = __builtin_bit_cast(bf16x8_t, uint4{v0.x, v0.y, v1.x, v1.y});
       }
-      __builtin_amdgcn_s_setprio(1);
       qk_part(sn[k >> 1], skn, k >> 1, (k & 1) * kHalfSlabs);
 #pragma unroll
       for (int db = 0; db < Gm::kDBlocks; ++db)
@@ -375,7 +380,6 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int db = 0; db < Gm::kDBlocks; ++db)
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pfl, o[db], 0, 0, 0);
-      __builtin_amdgcn_s_setprio(0);
     }
   };
 
@@ -389,8 +393,9 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
   int cur = next_visible(t_begin);
   if (cur < t_end) {
     int nxt = next_visible(cur + 1);
+    write_pos(cur, sPos0);
     issue_k(cur, sK0);
-    issue_v(cur, sV0, sPos0);
+    issue_v(cur, sV0);
     if (nxt < t_end) issue_k(nxt, sK1);
     __syncthreads();
 #pragma unroll
@@ -399,8 +404,9 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
     while (true) {
       // even iteration: scores of cur in sA, V(cur) in sV0, K(nxt) in sK1
       int nn = nxt < t_end ? next_visible(nxt + 1) : t_end;
+      if (nxt < t_end) write_pos(nxt, sPos1);
       if (nn < t_end) issue_k(nn, sK0);
-      if (nxt < t_end) issue_v(nxt, sV1, sPos1);
+      if (nxt < t_end) issue_v(nxt, sV1);
       iterate(sA, sB, kind, sK1, sV0, sPos0);
       __syncthreads();
       if (nxt >= t_end) break;
@@ -409,8 +415,9 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
       kind = classify(cur);
       // odd iteration: scores of cur in sB, V(cur) in sV1, K(nxt) in sK0
       nn = nxt < t_end ? next_visible(nxt + 1) : t_end;
+      if (nxt < t_end) write_pos(nxt, sPos0);
       if (nn < t_end) issue_k(nn, sK1);
-      if (nxt < t_end) issue_v(nxt, sV0, sPos0);
+      if (nxt < t_end) issue_v(nxt, sV0);
       iterate(sB, sA, kind, sK0, sV1, sPos1);
       __syncthreads();
       if (nxt >= t_end) break;

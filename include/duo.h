@@ -104,6 +104,17 @@ duo_status duo_layout_query(const duo_config* cfg, duo_layout* out);
 duo_status duo_cache_create(const duo_config* cfg, void* arena, uint64_t arena_bytes,
                             duo_cache** out);
 
+/* duo_cache_create followed by duo_cache_reset on `stream`: a ready, empty cache. */
+duo_status duo_cache_init(const duo_config* cfg, void* arena, uint64_t arena_bytes,
+                          void* stream, duo_cache** out);
+
+/* Set the length of every sequence of every layer, int32 [L][B] (0 <= len <= capacity;
+ * otherwise DUO_ERR_INVALID and nothing changes), for caches whose rows were filled outside
+ * the library. Each layer's slot table is rebuilt to match the lengths: slot s holds the
+ * latest token t < n with slot(t) = s, or -1 (explainer, "Decoding Procedure", step 4). The
+ * K/V rows are not touched. Enqueues one small kernel per layer on `stream`. */
+duo_status duo_cache_set_lengths(duo_cache* cache, const int32_t* lens, void* stream);
+
 /* Empty every sequence of every layer: lengths 0, slot table -1.
  * Enqueues one fill kernel on `stream` (no memset node, so it can be graph-captured). */
 duo_status duo_cache_reset(duo_cache* cache, void* stream);
@@ -161,7 +172,7 @@ duo_status duo_cache_lengths(const duo_cache* cache, int32_t* host_out);
  * (H_r * n + H_s * min(n, S + R)) * d * 2 * element size, summed over sequences (explainer,
  * "Decoding Procedure", memory formula). The second figure is also the K/V bytes one decode
  * step of that layer reads. Host only. */
-duo_status duo_kv_bytes(const duo_config* cfg, int32_t layer, const int32_t* seq_lens,
+duo_status duo_kv_bytes(const duo_config* cfg, const int32_t* seq_lens, int32_t layer,
                         uint64_t* full_attn_bytes, uint64_t* duo_bytes);
 
 /* Override the number of context splits per retrieval head used by duo_attn_decode

@@ -94,7 +94,7 @@ def test_kv_bytes_match_oracle_memory_model(layer):
     for dtype, es in ((torch.bfloat16, 2), (torch.float32, 4)):
         cfg, mask = cfg_of(dtype=dtype, out_dtype=torch.float32)
         lens = [0, 7, 3000]
-        full, duo = hsk.duo_kv_bytes(cfg, layer, lens)
+        full, duo = hsk.duo_kv_bytes(cfg, lens, layer)
         hr = int(mask[layer].sum())
         hs = 2 - hr
         want_duo = sum(2 * O.duo_kv_elements_layer(hr, hs, n, 4, 16, 128) * es for n in lens)
@@ -110,7 +110,7 @@ def test_kv_bytes_at_workload_shapes():
         cfg, _ = hsk.make_config(num_layers=1, batch=1, num_q_heads=w.hq, num_kv_heads=w.hkv,
                                  head_dim=w.d, sink=w.sink, recent=w.recent, capacity=w.capacity,
                                  retrieval_mask=W.retrieval_mask(w))
-        full, duo = hsk.duo_kv_bytes(cfg, 0, [w.context])
+        full, duo = hsk.duo_kv_bytes(cfg, [w.context], 0)
         assert abs(full / duo - ratio) < 1e-9
 
 
@@ -183,6 +183,13 @@ def test_error_paths_leave_state_unchanged():
     assert L.duo_set_decode_splits(fc.h, -1) == N.DUO_ERR_INVALID
     assert L.duo_set_decode_splits(fc.h, 257) == N.DUO_ERR_INVALID
     assert L.duo_set_decode_splits(fc.h, 7) == N.DUO_OK
+    # lengths: out of range or missing -> INVALID, nothing launched
+    bad = (ctypes.c_int32 * 6)(0, 1001, 0, 0, 0, 0)  # [L=2][B=3], capacity 1000
+    assert L.duo_cache_set_lengths(fc.h, bad, None) == N.DUO_ERR_INVALID
+    neg = (ctypes.c_int32 * 6)(0, 0, -1, 0, 0, 0)
+    assert L.duo_cache_set_lengths(fc.h, neg, None) == N.DUO_ERR_INVALID
+    assert L.duo_cache_set_lengths(fc.h, None, None) == N.DUO_ERR_INVALID
+    assert L.duo_cache_init(None, p, 0, None, None) == N.DUO_ERR_INVALID
     # kernel timers: argument checks only (creating events needs a device)
     ms, cnt = ctypes.c_double(1.0), ctypes.c_int32(5)
     assert L.duo_timing_enable(fc.h, -1) == N.DUO_ERR_INVALID
