@@ -91,7 +91,8 @@ class Timer:
 def decode_leg(args, torch, hsk, W, N):
     w = W.workload(args.workload)
     L = args.layers
-    total_steps = args.warmup + args.steps
+    # warm-up, the timed steps, then as many again timed one by one for the spread
+    total_steps = args.warmup + 2 * args.steps
     n0 = w.context
     cap = n0 + total_steps
     mask = W.retrieval_mask(w)[0]
@@ -144,27 +145,41 @@ def decode_leg(args, torch, hsk, W, N):
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
-    # the library's kernel timers record a HIP event pair on this stream around every
-    # split attention kernel of the timed steps (the split merge kernel is outside the pair)
-    hsk.duo_timing_enable(cache, args.steps * L)
     tm = Timer(torch)
     tm.start()
-    for s in range(args.warmup, total_steps):
+    for s in range(args.warmup, args.warmup + args.steps):
         step(s)
     total_ms = tm.stop_ms()
     torch.cuda.synchronize()
     ms_per_step = total_ms / args.steps
+
+    # Second timed pass over the next `steps` steps: the library's kernel timers record a HIP
+    # event pair on this stream around every split attention kernel (the split merge kernel
+    # is outside the pair), and every step sits between its own pair of events for the
+    # spread. Kept out of the pass above: the extra event records cost about 2 us per step.
+    hsk.duo_timing_enable(cache, args.steps * L)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i, s in enumerate(range(args.warmup + args.steps, total_steps)):
+        evs[i][0].record()
+        step(s)
+        evs[i][1].record()
+    torch.cuda.synchronize()
     kern_ms, kern_n = hsk.duo_timing_read(cache, "decode")
     hsk.duo_timing_enable(cache, 0)
     assert kern_n == args.steps * L, kern_n
     kern_us = kern_ms * 1e3 / kern_n
+    import numpy as np
+    per_step_us = np.array([a.elapsed_time(b) * 1e3 / L for a, b in evs])
+    pct = {f"p{q}": float(np.percentile(per_step_us, q)) for q in (10, 50, 90)}
 
-    # algorithmic bytes of one layer-step, averaged over the timed steps
+    # algorithmic bytes of one layer-step, averaged over the timed steps (the second pass,
+    # 100 tokens longer, differs by less than 0.1 %)
     cfg1, _m = hsk.make_config(num_layers=1, batch=1, num_q_heads=w.hq, num_kv_heads=w.hkv,
                                head_dim=w.d, sink=w.sink, recent=w.recent, capacity=cap,
                                retrieval_mask=[mask])
     kv_bytes = []
-    for s in range(args.warmup, total_steps):
+    for s in range(args.warmup, args.warmup + args.steps):
         kv_bytes.append(hsk.duo_kv_bytes(cfg1, [n0 + s + 1], 0)[1])
     io_bytes = 2 * w.hq * w.d * 2 + 2 * 2 * w.hkv * w.d * 2  # q in, out, new K/V in + stored
     step_bytes = sum(kv_bytes) / len(kv_bytes) + io_bytes
@@ -189,7 +204,7 @@ def decode_leg(args, torch, hsk, W, N):
     result = dict(
         workload=w, layers=L, ms_per_step=ms_per_step, us_layer=us_layer, gbs=gbs,
         step_bytes=step_bytes, dec_us=dec_ms * 1e3, dec_bytes=dec_bytes, dec_gbs=dec_gbs,
-        kern_us=kern_us, kern_gbs=kern_gbs, kern_n=kern_n,
+        kern_us=kern_us, kern_gbs=kern_gbs, kern_n=kern_n, step_pct=pct,
         n_final=n_final, history=(n0, total_steps))
     del cache, qs, ks, vs
     torch.cuda.empty_cache()
@@ -237,20 +252,22 @@ def prefill_leg(args, torch, hsk, W, N):
 
     run_pass()
     torch.cuda.synchronize()
-    hsk.duo_timing_enable(cache, args.prefill_passes * (P // C))
     tm = Timer(torch)
     tm.start()
     for _ in range(args.prefill_passes):
         run_pass()
     pass_ms = tm.stop_ms() / args.prefill_passes
-    kern_ms, kern_n = hsk.duo_timing_read(cache, "prefill")
-    hsk.duo_timing_enable(cache, 0)
-    assert kern_n == args.prefill_passes * (P // C), kern_n
-    kern_ms_pass = kern_ms / args.prefill_passes
+    # attention calls alone (events around each call), with the kernel timers around each
+    # attention kernel launch
+    hsk.duo_timing_enable(cache, args.prefill_passes * (P // C))
     attn = []
     for _ in range(args.prefill_passes):
         attn.append(run_pass(Timer(torch)))
     attn_ms = sum(attn) / len(attn)
+    kern_ms, kern_n = hsk.duo_timing_read(cache, "prefill")
+    hsk.duo_timing_enable(cache, 0)
+    assert kern_n == args.prefill_passes * (P // C), kern_n
+    kern_ms_pass = kern_ms / args.prefill_passes
     # algorithmic flops: 4 d per visible (query, key) pair; query p sees p + 1 keys on a
     # retrieval head and min(p + 1, S + R) on a streaming head
     S, R = w.sink, w.recent
@@ -307,6 +324,26 @@ def cpu_baseline(args, W, w, n):
     return dict(sec_per_step=sec, calls=calls, threads=threads)
 
 
+def cpu_prefill_sample(args, W):
+    """The float64 oracle pre-filling a sample of the 32K MHA prompt on the host's cores: the
+    last 64 queries of the third 4K chunk (positions 12,224..12,287), all 32 heads."""
+    from oracle import duo_oracle as O
+    w = W.workload("c2")
+    mask = W.retrieval_mask(w)[0]
+    start, m = 12224, 64
+    k = W.tokens(w, "k", 0, 0, 0, start + m)
+    v = W.tokens(w, "v", 0, 0, 0, start + m)
+    q = W.tokens(w, "q", 0, 0, start, start + m)
+    t = time.time()
+    O.prefill_chunk(q, k, v, start, mask, w.sink, w.recent)
+    sec = time.time() - t
+    S, R = w.sink, w.recent
+    hr = int(mask.sum())
+    pairs = sum(hr * (p + 1) + (w.hkv - hr) * min(p + 1, S + R) for p in range(start, start + m))
+    flops = 4 * w.d * pairs * (w.hq // w.hkv)
+    return dict(sec=sec, flops=flops, tflops=flops / sec / 1e12)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -334,10 +371,12 @@ def main():
             log(f"prefill leg skipped: {e}")
     probe = copy_probe(torch)
     w = dec["workload"]
-    cpu = None
+    cpu = cpu_pre = None
     if not args.no_cpu:
         cpu = cpu_baseline(args, W, w, w.context)
         log(f"oracle: {cpu['sec_per_step']:.3f} s per decode step on {cpu['threads']} threads")
+        cpu_pre = cpu_prefill_sample(args, W)
+        log(f"oracle prefill sample: {cpu_pre['sec']:.2f} s, {cpu_pre['tflops'] * 1e3:.3f} GFLOP/s")
     traffic = committed_traffic("decode.hip", f"decode_{args.workload}")
     out = {
         "metric": METRIC,
@@ -360,6 +399,7 @@ def main():
             "context": w.context, "replica_layers": dec["layers"], "global_batch": 1,
         },
         "us_per_layer_step": round(dec["us_layer"], 3),
+        "us_per_layer_step_spread": {k: round(v, 3) for k, v in dec["step_pct"].items()},
         "hbm_frac": round(dec["gbs"] / HBM_PEAK_GBS, 4),
         "decode_call_us": round(dec["dec_us"], 3),
         "roofline": {
@@ -386,6 +426,12 @@ def main():
                          "kernel": "prefill_kernel<d128, G1> (8 launches per pass)",
                          "kernel_ms_per_pass": round(pre["kern_ms"], 3),
                          "algorithmic_flops": int(pre["flops"])},
+        },
+        "cpu_prefill_baseline": None if cpu is None else {
+            "value": round(cpu_pre["tflops"], 6), "unit": "TFLOP/s", "cores": cpu["threads"],
+            "kind": "oracle",
+            "sample": f"float64 oracle prefill of 64 queries (positions 12224..12287) x 32 heads "
+                      f"of the 32K MHA prompt, {cpu_pre['sec']:.2f} s",
         },
         "cpu_baseline": None if cpu is None else {
             "value": round(dec["dec_bytes"] / cpu["sec_per_step"] / 1e9, 3),
