@@ -61,6 +61,27 @@ def visible_mask(q_pos, k_pos, retrieval: bool, sink: int, recent: int) -> np.nd
     return causal & ((t < sink) | (t >= p - recent + 1))
 
 
+def chunk_visible_mask(q_pos, k_pos, start: int, retrieval: bool, sink: int,
+                       recent: int) -> np.ndarray:
+    """The chunk-granular reading of chunked pre-filling, for a chunk starting at ``start``.
+
+    Explainer, "Chunked Pre-filling" (Figure 5): after each chunk the streaming heads' cache is
+    pruned to the sinks and the most recent tokens, and the next chunk attends to that pruned
+    cache together with itself. Reading: a streaming head's query p in the chunk sees the
+    tokens the cache holds when the chunk starts (t < start with t < S or t >= start - R, the
+    same set as ``streaming_valid_tokens(start)``) and the chunk's tokens t in [start, p];
+    a retrieval head keeps the causal mask. Unlike ``visible_mask`` this depends on where
+    the chunks start.
+    """
+    p = np.asarray(q_pos, dtype=np.int64)[:, None]
+    t = np.asarray(k_pos, dtype=np.int64)[None, :]
+    causal = (t <= p) & (t >= 0)
+    if retrieval:
+        return causal
+    held = (t >= 0) & (t < start) & ((t < sink) | (t >= start - recent))
+    return held | ((t >= start) & (t <= p))
+
+
 # --------------------------------------------------------------------------------------------
 # Attention
 # --------------------------------------------------------------------------------------------
@@ -90,7 +111,7 @@ def masked_softmax_attention(q, k, v, mask, scale):
     return out, lse
 
 
-def attention(q, k, v, q_pos, k_pos, retrieval, sink, recent, scale=None):
+def attention(q, k, v, q_pos, k_pos, retrieval, sink, recent, scale=None, chunk_start=None):
     """All heads of one layer and one sequence.
 
     ``q [P, Hq, d]``, ``k, v [T, Hkv, d]``, ``q_pos [P]``, ``k_pos [T]``,
@@ -101,6 +122,8 @@ def attention(q, k, v, q_pos, k_pos, retrieval, sink, recent, scale=None):
     which is the concatenation of step 5 undone by the head permutation of "Head Reordering
     Preprocessing" (heads are permutation-invariant there). No KV head is repeated for GQA:
     each query head reads its own group's K and V (OpenReview thread, GQA compatibility).
+    With ``chunk_start`` set, streaming heads use ``chunk_visible_mask`` for a chunk that
+    starts there instead of the per-query Lambda mask.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -118,7 +141,8 @@ def attention(q, k, v, q_pos, k_pos, retrieval, sink, recent, scale=None):
         j = kv_head_of(h, G)
         r = bool(retrieval[j])
         if r not in masks:
-            masks[r] = visible_mask(q_pos, k_pos, r, sink, recent)
+            masks[r] = (visible_mask(q_pos, k_pos, r, sink, recent) if chunk_start is None else
+                        chunk_visible_mask(q_pos, k_pos, chunk_start, r, sink, recent))
         out[:, h, :], lse[:, h] = masked_softmax_attention(q[:, h, :], k[:, j, :], v[:, j, :],
                                                            masks[r], scale)
     return out, lse
@@ -141,7 +165,8 @@ def decode_step(q, k_hist, v_hist, retrieval, sink, recent, scale=None):
     return out[0], lse[0]
 
 
-def prefill_chunk(q, k_hist, v_hist, start, retrieval, sink, recent, scale=None):
+def prefill_chunk(q, k_hist, v_hist, start, retrieval, sink, recent, scale=None,
+                  chunk_granular=False):
     """Chunked pre-filling of positions ``start .. start+m-1`` for one sequence.
 
     ``q [m, Hq, d]``; ``k_hist, v_hist [start+m, Hkv, d]`` (all earlier tokens plus the
@@ -151,12 +176,14 @@ def prefill_chunk(q, k_hist, v_hist, start, retrieval, sink, recent, scale=None)
     chunk causally. Reading: streaming heads apply the same per-query Lambda mask as in
     decoding, so the result does not depend on the chunk size and equals token-by-token
     decoding; the pruned cache after each chunk still holds every key this mask can reach.
+    ``chunk_granular=True`` takes the other reading instead (``chunk_visible_mask``).
     """
     m = np.asarray(q).shape[0]
     T = start + m
     assert k_hist.shape[0] >= T
     return attention(q, k_hist[:T], v_hist[:T], np.arange(start, T), np.arange(T),
-                     retrieval, sink, recent, scale)
+                     retrieval, sink, recent, scale,
+                     chunk_start=start if chunk_granular else None)
 
 
 # --------------------------------------------------------------------------------------------

@@ -208,6 +208,8 @@ def pin_fig5_worked_example():
     assert rows[0][0] == "sink=1"
     assert head["recent"] == "2" and head["chunk"] == "4"
     for kind, d in rows[1:]:
+        if not kind.startswith("after="):
+            continue
         n = int(kind.split("=")[1])
         want = sorted(int(x) for x in d["cache"].split(","))
         assert sorted(O.streaming_valid_tokens(n, S, R).tolist()) == want
@@ -217,6 +219,67 @@ def pin_fig5_worked_example():
     # the ring convention places them as [0, 3, 2] and [0, 7, 6]
     assert list(O.slot_table(4, S, R)) == [0, 3, 2]
     assert list(O.slot_table(8, S, R)) == [0, 7, 6]
+
+
+def pin_chunk_granular_fig5():
+    """Chunk-granular reading: the second chunk of Figure 5 sees the pruned cache {0, 2, 3}
+    plus its own tokens up to the query."""
+    rows = _read_golden("chunked_prefill_fig5.txt")
+    att = [d for kind, d in rows if kind == "attend"]
+    assert len(att) == 1
+    start = int(att[0]["start"])
+    held = [int(x) for x in att[0]["held"].split(",")]
+    S, R, chunk = 1, 2, 4
+    assert sorted(sim_chunked_cache(start, S, R, chunk)) == held
+    q_pos = np.arange(start, start + chunk)
+    m = O.chunk_visible_mask(q_pos, np.arange(start + chunk), start, False, S, R)
+    for i, p in enumerate(q_pos):
+        assert sorted(np.nonzero(m[i])[0].tolist()) == held + list(range(start, p + 1))
+    assert np.array_equal(O.chunk_visible_mask(q_pos, np.arange(8), start, True, S, R),
+                          O.visible_mask(q_pos, np.arange(8), True, S, R))
+
+
+def pin_chunk_granular_gather():
+    """Chunk-granular prefill equals plain attention over the gathered keys [pruned cache ;
+    chunk] with a causal mask on the chunk part, the pruned cache taken from the chunked
+    cache simulation (chunks of the same size before this one)."""
+    rng = np.random.default_rng(11)
+    for (S, R, chunk, n_chunks, G) in [(2, 5, 4, 4, 1), (1, 2, 4, 2, 2), (0, 3, 7, 3, 1), (3, 9, 5, 4, 4)]:
+        T = chunk * n_chunks
+        d = 8
+        q = rand(rng, T, G, d)
+        k = rand(rng, T, 1, d)
+        v = rand(rng, T, 1, d)
+        for c in range(n_chunks):
+            start = c * chunk
+            held = sorted(sim_chunked_cache(start, S, R, chunk))
+            out, lse = O.prefill_chunk(q[start:start + chunk], k, v, start, [0], S, R,
+                                       chunk_granular=True)
+            for i in range(chunk):
+                keys = held + list(range(start, start + i + 1))
+                for h in range(G):
+                    z = (k[keys, 0] @ q[start + i, h]) / math.sqrt(d)
+                    w = np.exp(z - z.max())
+                    ref = (w @ v[keys, 0]) / w.sum()
+                    assert np.allclose(out[i, h], ref, rtol=0, atol=1e-12), (S, R, chunk, c, i)
+                    assert abs(lse[i, h] - (z.max() + math.log(w.sum()))) < 1e-12
+
+
+def pin_chunk_granular_short_is_full():
+    """While the chunk starts within the first S+R tokens the pruned cache is the whole
+    prefix, so the chunk-granular streaming head is causal attention."""
+    rng = np.random.default_rng(12)
+    S, R, d = 2, 6, 8
+    T = 20
+    q = rand(rng, T, 1, d)
+    k = rand(rng, T, 1, d)
+    v = rand(rng, T, 1, d)
+    ref = _sdpa_causal(q, k, v)
+    for start in (0, 3, S + R):
+        out, _ = O.prefill_chunk(q[start:], k, v, start, [0], S, R, chunk_granular=True)
+        assert np.allclose(out, ref[start:], rtol=0, atol=1e-12), start
+    out, _ = O.prefill_chunk(q[S + R + 1:], k, v, S + R + 1, [0], S, R, chunk_granular=True)
+    assert not np.allclose(out, ref[S + R + 1:])
 
 
 def pin_memory_numbers():
@@ -320,7 +383,8 @@ PINS = [pin_cache_policy, pin_streaming_rows, pin_decode_scalar_bruteforce,
         pin_all_retrieval_is_causal_attention, pin_short_streaming_is_full,
         pin_no_sink_is_sliding_window, pin_fig5_worked_example, pin_memory_numbers,
         pin_memory_formula_by_count, pin_chunk_invariance_and_decode_equivalence,
-        pin_head_permutation, pin_gqa_equals_repeated_mha, pin_lambda_mask_literal]
+        pin_head_permutation, pin_gqa_equals_repeated_mha, pin_lambda_mask_literal,
+        pin_chunk_granular_fig5, pin_chunk_granular_gather, pin_chunk_granular_short_is_full]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -373,6 +437,15 @@ def _softmax_unmasked_den(q, k, v, mask, scale):
     return (w @ np.asarray(v)) / den, (m + np.log(den))[:, 0]
 
 
+def _chunk_held_one_short(q_pos, k_pos, start, retrieval, sink, recent):
+    p = np.asarray(q_pos)[:, None]
+    t = np.asarray(k_pos)[None, :]
+    if retrieval:
+        return (t <= p) & (t >= 0)
+    held = (t >= 0) & (t < start) & ((t < sink) | (t >= start - recent + 1))
+    return held | ((t >= start) & (t <= p))
+
+
 _ORIG_MSA = O.masked_softmax_attention
 
 MUTANTS = {
@@ -393,6 +466,9 @@ MUTANTS = {
                       lambda Hr, Hs, L, S, R, d: (Hr * L + Hs * (S + R)) * d),
     "budget_weights_r": ("budget_ratio", lambda r, L, S, R: (r * L + r * min(L, S + R)) / L),
     "full_kv_no_factor2": ("full_kv_elements", lambda D, H, L, d: D * H * L * d),
+    "chunk_held_one_short": ("chunk_visible_mask", _chunk_held_one_short),
+    "chunk_window_per_query": ("chunk_visible_mask",
+                               lambda q, k, st, r, S, R: O.visible_mask(q, k, r, S, R)),
 }
 
 
