@@ -8,7 +8,9 @@ replica layers sit at distinct addresses so that the per-step K/V (>= 2 GB) cann
 the 256 MB Infinity Cache; the time per layer-step is the step time divided by the layers.
 
 Prefill leg: the Llama-2-7B-shaped MHA layer (32 heads, 8 retrieval) pre-filling a 32K
-prompt in 4K-token chunks (prefill attention of each chunk, then its append).
+prompt in 4K-token chunks (prefill attention of each chunk, then its append), once with the
+per-query sink + recent mask on streaming heads and once with chunk-granular streaming heads
+(the pruned cache before the chunk plus the chunk; ``--prefill-modes`` picks either).
 
 Prints one JSON line. ``value`` is the decode K/V bandwidth in GB/s (algorithmic bytes: the
 K/V rows the method must read, plus q, out and the appended token). Inputs are resident in
@@ -45,6 +47,8 @@ def parse():
     p.add_argument("--workload", default="c3", help="decode workload key (c2, c3, c5, c5q)")
     p.add_argument("--prefill-passes", type=int, default=3)
     p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--prefill-modes", default="window,chunk",
+                   help="streaming-head prefill modes to time: window, chunk or both")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--splits", type=int, default=0, help="force decode splits (0 = automatic)")
@@ -211,7 +215,7 @@ def decode_leg(args, torch, hsk, W, N):
     return result
 
 
-def prefill_leg(args, torch, hsk, W, N):
+def prefill_leg(args, torch, hsk, W, N, mode="window"):
     w = W.workload("c2")
     mask = W.retrieval_mask(w)[0]
     dev = torch.device("cuda")
@@ -219,7 +223,7 @@ def prefill_leg(args, torch, hsk, W, N):
     cache = hsk.DuoCache(num_layers=1, batch=1, num_q_heads=w.hq, num_kv_heads=w.hkv,
                          head_dim=w.d, sink=w.sink, recent=w.recent, capacity=P,
                          retrieval_mask=[mask], dtype=torch.bfloat16, out_dtype=torch.bfloat16,
-                         device=dev)
+                         streaming_prefill=mode, device=dev)
     q = torch.from_numpy(W.tokens(w, "q", 0, 0, 0, P)).to(dev).to(torch.bfloat16)
     k = torch.from_numpy(W.tokens(w, "k", 0, 0, 0, P)).to(dev).to(torch.bfloat16)
     v = torch.from_numpy(W.tokens(w, "v", 0, 0, 0, P)).to(dev).to(torch.bfloat16)
@@ -269,12 +273,16 @@ def prefill_leg(args, torch, hsk, W, N):
     assert kern_n == args.prefill_passes * (P // C), kern_n
     kern_ms_pass = kern_ms / args.prefill_passes
     # algorithmic flops: 4 d per visible (query, key) pair; query p sees p + 1 keys on a
-    # retrieval head and min(p + 1, S + R) on a streaming head
+    # retrieval head and, on a streaming head, min(p + 1, S + R) (window mode) or the
+    # min(c, S + R) held tokens plus p - c + 1 chunk tokens (chunk mode, chunk starting at c)
     S, R = w.sink, w.recent
     hr = int(mask.sum())
     hs = w.hkv - hr
     pairs_ret = P * (P + 1) // 2
-    pairs_str = sum(min(p + 1, S + R) for p in range(P))
+    if mode == "chunk":
+        pairs_str = sum(min(p - p % C, S + R) + p % C + 1 for p in range(P))
+    else:
+        pairs_str = sum(min(p + 1, S + R) for p in range(P))
     flops = 4 * w.d * (hr * pairs_ret + hs * pairs_str) * (w.hq // w.hkv)
     del cache, q, k, v, out
     torch.cuda.empty_cache()
@@ -360,8 +368,9 @@ def main():
     log(f"decode: {dec['us_layer']:.2f} us/layer-step, {dec['gbs']:.0f} GB/s; split kernel "
         f"{dec['kern_us']:.2f} us = {dec['kern_gbs']:.0f} GB/s ({dec['kern_n']} launches timed); "
         f"one duo_attn_decode call {dec['dec_us']:.2f} us = {dec['dec_gbs']:.0f} GB/s")
+    modes = set(args.prefill_modes.split(","))
     pre = None
-    if not args.no_prefill:
+    if not args.no_prefill and "window" in modes:
         try:
             pre = prefill_leg(args, torch, hsk, W, N)
             log(f"prefill: {pre['attn_ms']:.3f} ms attention for {pre['flops'] / 1e12:.3f} TFLOP "
@@ -369,6 +378,16 @@ def main():
                 f"{pre['kern_tflops']:.1f} TFLOP/s")
         except (RuntimeError, hsk.DuoError) as e:
             log(f"prefill leg skipped: {e}")
+    pre_chunk = None
+    if not args.no_prefill and "chunk" in modes:
+        try:
+            pre_chunk = prefill_leg(args, torch, hsk, W, N, mode="chunk")
+            log(f"prefill, chunk-granular streaming heads: {pre_chunk['attn_ms']:.3f} ms attention "
+                f"for {pre_chunk['flops'] / 1e12:.3f} TFLOP = {pre_chunk['tflops']:.1f} TFLOP/s; "
+                f"attention kernel {pre_chunk['kern_ms']:.3f} ms = "
+                f"{pre_chunk['kern_tflops']:.1f} TFLOP/s")
+        except (RuntimeError, hsk.DuoError) as e:
+            log(f"chunk-mode prefill leg skipped: {e}")
     probe = copy_probe(torch)
     w = dec["workload"]
     cpu = cpu_pre = None
@@ -426,6 +445,17 @@ def main():
                          "kernel": "prefill_kernel<d128, G1> (8 launches per pass)",
                          "kernel_ms_per_pass": round(pre["kern_ms"], 3),
                          "algorithmic_flops": int(pre["flops"])},
+        },
+        "prefill_chunk_mode": None if pre_chunk is None else {
+            "workload": f"{pre_chunk['workload'].name}: 32K prompt in 4K chunks, streaming heads "
+                        f"over the pruned cache plus the chunk",
+            "attn_ms": round(pre_chunk["attn_ms"], 3),
+            "ms_incl_append": round(pre_chunk["pass_ms"], 3),
+            "tflops": round(pre_chunk["tflops"], 1),
+            "kernel_ms_per_pass": round(pre_chunk["kern_ms"], 3),
+            "kernel_tflops": round(pre_chunk["kern_tflops"], 1),
+            "frac": round(pre_chunk["kern_tflops"] / BF16_PEAK_TFLOPS, 4),
+            "algorithmic_flops": int(pre_chunk["flops"]),
         },
         "cpu_prefill_baseline": None if cpu is None else {
             "value": round(cpu_pre["tflops"], 6), "unit": "TFLOP/s", "cores": cpu["threads"],

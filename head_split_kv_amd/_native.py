@@ -22,6 +22,7 @@ EXPORTS = (
     "duo_timing_read", "duo_status_string",
 )
 TIMING_DECODE, TIMING_PREFILL = 0, 1
+PREFILL_WINDOW, PREFILL_CHUNK = 0, 1
 
 
 class DuoConfig(ctypes.Structure):
@@ -40,6 +41,7 @@ class DuoConfig(ctypes.Structure):
         ("max_splits", ctypes.c_int32),
         ("prefill_tiles", ctypes.c_int32),
         ("retrieval_mask", ctypes.POINTER(ctypes.c_uint8)),
+        ("streaming_prefill", ctypes.c_int32),
     ]
 
 

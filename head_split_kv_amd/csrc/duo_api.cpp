@@ -281,6 +281,7 @@ duo_status duo_attn_prefill(duo_cache* c, int32_t layer, int32_t seq, const void
   a.R = c->cfg.recent;
   a.scale_log2 = (float)((double)c->scale * 1.4426950408889634);
   a.out_f32 = c->cfg.out_dtype == DUO_F32;
+  a.chunk_mode = c->cfg.streaming_prefill == DUO_PREFILL_CHUNK;
   std::memcpy(a.cls_idx, li.cls_idx, sizeof(a.cls_idx));
   std::memcpy(a.ret_kv, li.ret_kv, sizeof(a.ret_kv));
   std::memcpy(a.str_kv, li.str_kv, sizeof(a.str_kv));
@@ -295,7 +296,8 @@ duo_status duo_attn_prefill(duo_cache* c, int32_t layer, int32_t seq, const void
   a.n_qt = (n_chunk + qpb - 1) / qpb;
   a.nsplit = choose_prefill_splits(nb, n_chunk, c_max, c_sum, a.Hr, a.Hs, a.S, a.R, group,
                                    c->cfg.prefill_tiles,
-                                   prefill_resident_blocks(c->cfg.head_dim, group));
+                                   prefill_resident_blocks(c->cfg.head_dim, group),
+                                   a.chunk_mode != 0);
   const uint64_t D = c->cfg.head_dim;
   char* ws = c->arena + c->lay.workspace_off;
   a.part_o = (float*)ws;

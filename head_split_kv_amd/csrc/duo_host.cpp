@@ -32,6 +32,8 @@ duo_status check_config(const duo_config* cfg) {
   if (cfg->max_splits < 0 || cfg->max_splits > kMaxSplits) return DUO_ERR_INVALID;
   if (cfg->prefill_tiles < 0 || cfg->prefill_tiles > kMaxPrefillTiles) return DUO_ERR_INVALID;
   if (!cfg->retrieval_mask) return DUO_ERR_INVALID;
+  if (cfg->streaming_prefill != DUO_PREFILL_WINDOW && cfg->streaming_prefill != DUO_PREFILL_CHUNK)
+    return DUO_ERR_INVALID;
   if (element_size(cfg->dtype) == 0 || element_size(cfg->out_dtype) == 0)
     return DUO_ERR_INVALID;
   if (!(std::isfinite(cfg->softmax_scale))) return DUO_ERR_INVALID;
@@ -122,8 +124,9 @@ int choose_decode_splits(int32_t n_max, int32_t batch, int32_t n_ret, int32_t n_
 
 int choose_prefill_splits(int32_t nb, int32_t m, int32_t c_max, int32_t c_sum, int32_t n_ret,
                           int32_t n_str, int32_t sink, int32_t recent, int32_t group,
-                          int32_t prefill_tiles, int32_t resident_blocks) {
-  // Retrieval query tiles see the whole cache prefix, streaming ones a constant window.
+                          int32_t prefill_tiles, int32_t resident_blocks, bool chunk_mode) {
+  // Retrieval query tiles see the whole cache prefix, streaming ones a constant window
+  // (or, chunk-granular, the S + R cache rows and the chunk up to the tile).
   // Cut the retrieval key ranges so that the heaviest piece is about the size of a
   // streaming tile or of 1/2 of a resident round's share of the work, whichever is larger.
   constexpr int64_t kBN = 64;
@@ -136,6 +139,7 @@ int choose_prefill_splits(int32_t nb, int32_t m, int32_t c_max, int32_t c_sum, i
   const int64_t sr = (int64_t)sink + recent;
   int64_t t_str = (c_max > 0 ? (sr + kBN - 1) / kBN : 0) + (recent + qpb + kBN - 1) / kBN + 1;
   if (t_str > (m + kBN - 1) / kBN + (sr + kBN - 1) / kBN) t_str = (m + kBN - 1) / kBN + (sr + kBN - 1) / kBN;
+  if (chunk_mode) t_str = (c_max > 0 ? (sr + kBN - 1) / kBN : 0) + chunk_tiles_avg;
   const int64_t work = (int64_t)nb * n_qt * ((int64_t)n_ret * t_ret_avg + (int64_t)n_str * t_str);
   int64_t target = work / (2 * (int64_t)(resident_blocks > 0 ? resident_blocks : 512));
   if (target < t_str) target = t_str;

@@ -104,6 +104,7 @@ struct PrefillArgs {
   int32_t nsplit;           // key-range splits of every retrieval query tile
   float scale_log2;
   int32_t out_f32;
+  int32_t chunk_mode;       // streaming heads see the whole cache plus the chunk causally
   int16_t cls_idx[kMaxKvHeads];
   uint8_t ret_kv[kMaxKvHeads];
   uint8_t str_kv[kMaxKvHeads];
@@ -146,7 +147,7 @@ int choose_decode_splits(int32_t n_max, int32_t batch, int32_t n_ret, int32_t n_
                          int32_t max_splits, int32_t resident_blocks);
 int choose_prefill_splits(int32_t nb, int32_t m, int32_t c_max, int32_t c_sum, int32_t n_ret,
                           int32_t n_str, int32_t sink, int32_t recent, int32_t group,
-                          int32_t prefill_tiles, int32_t resident_blocks);
+                          int32_t prefill_tiles, int32_t resident_blocks, bool chunk_mode);
 
 }  // namespace duo
 

@@ -4,7 +4,9 @@
 // t <= p on a retrieval head (full-cache rows 0..c-1, then the chunk) and, on a streaming
 // head, to the keys t <= p with t < S or t >= p - R + 1 (the sink + ring slots held before
 // the chunk, then the chunk) (explainer, "Chunked Pre-filling" and "The Full and Streaming
-// Attention Masks"). The cache is only read; the caller appends the chunk afterwards.
+// Attention Masks"). In chunk mode a streaming head sees every token its cache holds before
+// the chunk and the chunk causally, the cache being pruned between chunks only (the same
+// subsection, Figure 5). The cache is only read; the caller appends the chunk afterwards.
 //
 // One block = 4 waves = 128 query rows of one (sequence, KV head): 128 / G positions times
 // the G query heads of the group, so every K/V tile staged in LDS serves the whole group
@@ -135,6 +137,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
     j = a.str_kv[cls];
   }
   const bool retrieval = blockIdx.x < (unsigned)n_ret_blocks;
+  // every held key is visible (retrieval, or a streaming head in chunk mode): causal only
+  const bool causal_only = retrieval || a.chunk_mode != 0;
   const int b = a.b0 + bi;
   const int c0 = a.c0[bi];
   const int S = a.S, R = a.R, SR = a.S + a.R;
@@ -150,7 +154,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
   const bool q_valid = q_local < a.m;
   const int p = c0 + (q_valid ? q_local : ql1);
   // first key of this query's window (every key on a retrieval head)
-  const int win_lo = retrieval ? -0x7FFFFFFF : p - a.R + 1;
+  const int win_lo = causal_only ? -0x7FFFFFFF : p - a.R + 1;
 
   // ---- Q^T operand: 16-byte slabs of this lane's query row --------------------------
   bf16x8_t qf[Gm::kSlabs];
@@ -189,7 +193,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
   // kind of tile ti: 0 = every key visible to every query, 1 = masked, -1 = skipped
   auto classify = [&](int ti) -> int {
     if (ti < n_cache_tiles) {
-      if (retrieval) return (ti + 1) * kBN <= c0 ? 0 : 1;
+      if (ti * kBN >= filled) return -1;  // empty slots only
+      if (causal_only) return (ti + 1) * kBN <= filled ? 0 : 1;
       // streaming cache: once every window starts past the cache only sink slots count
       if (ti * kBN >= S && p_min - R + 1 > c0 - 1) return -1;
       return 1;
@@ -197,7 +202,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
     const int k0 = c0 + (ti - n_cache_tiles) * kBN;  // first key position
     const int k1 = min(c0 + a.m, k0 + kBN) - 1;       // last valid key position
     const bool all_rows = k0 + kBN <= c0 + a.m;
-    if (retrieval) return (all_rows && k1 <= p_min) ? 0 : 1;
+    if (causal_only) return (all_rows && k1 <= p_min) ? 0 : 1;
     if (k0 >= S && k1 < p_min - R + 1) return -1;  // left of every window
     return (all_rows && k1 <= p_min && k0 >= p_max - R + 1) ? 0 : 1;
   };

@@ -51,6 +51,13 @@ typedef enum {
 
 typedef enum { DUO_F32 = 0, DUO_BF16 = 1 } duo_dtype;
 
+/* Streaming-head visibility during chunked pre-filling (explainer, "Chunked Pre-filling").
+ * WINDOW: query p sees the t <= p with t < S or t >= p - R + 1, the same Lambda mask as
+ * decoding. CHUNK: query p of a chunk starting at c sees every token the streaming cache
+ * holds at c (the sinks and the R tokens before c) and the chunk's tokens t <= p, the cache
+ * being pruned only between chunks. Both agree while c + (position in chunk) < S + R. */
+typedef enum { DUO_PREFILL_WINDOW = 0, DUO_PREFILL_CHUNK = 1 } duo_prefill_mode;
+
 /* Cache configuration. head_dim is 64 or 128; G = num_q_heads / num_kv_heads is 1, 2, 4 or
  * 8; sink >= 0 and recent >= 1 (explainer, "The Full and Streaming Attention Masks": the
  * streaming mask keeps the first `sink` tokens and the `recent` most recent ones, the query's
@@ -73,6 +80,7 @@ typedef struct {
                               <= 65536; 0 selects 2048 */
   const uint8_t* retrieval_mask; /* host [num_layers][num_kv_heads], nonzero = retrieval;
                                     copied by duo_cache_create */
+  int32_t streaming_prefill; /* duo_prefill_mode of streaming heads in duo_attn_prefill */
 } duo_config;
 
 /* Byte offsets inside the caller's arena (all 256-byte aligned). Inside each cache region
@@ -154,8 +162,10 @@ duo_status duo_decode_step(duo_cache* cache, int32_t layer, const void* q, const
  * positions c .. c+m-1 where c is the sequence's current length. Query p attends to every
  * t <= p on retrieval heads (full cache rows 0..c-1 plus the chunk, causally) and, on
  * streaming heads, to the t <= p with t < S or t >= p - R + 1 (sinks and ring before the
- * chunk, plus the chunk). The cache is not modified: the caller then appends the same k, v
- * with duo_kv_append. Layouts as in the header comment; n_chunk = 0 is a no-op. */
+ * chunk, plus the chunk) under DUO_PREFILL_WINDOW, or to every token the streaming cache
+ * holds plus the chunk's t <= p under DUO_PREFILL_CHUNK (cfg.streaming_prefill). The cache is
+ * not modified: the caller then appends the same k, v with duo_kv_append. Layouts as in the
+ * header comment; n_chunk = 0 is a no-op. */
 duo_status duo_attn_prefill(duo_cache* cache, int32_t layer, int32_t seq, const void* q,
                             const void* k, const void* v, int32_t n_chunk, void* out,
                             float* lse, void* stream);

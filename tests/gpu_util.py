@@ -21,7 +21,7 @@ def to_dev(x: np.ndarray, dtype: torch.dtype, device="cuda") -> torch.Tensor:
 
 
 def make_cache(w: W.Workload, out_dtype=torch.float32, max_splits=0, capacity=None,
-               layers=None):
+               layers=None, streaming_prefill="window"):
     import head_split_kv_amd as hsk
     mask = W.retrieval_mask(w)
     if layers is not None:
@@ -29,7 +29,8 @@ def make_cache(w: W.Workload, out_dtype=torch.float32, max_splits=0, capacity=No
     return hsk.DuoCache(num_layers=mask.shape[0], batch=w.batch, num_q_heads=w.hq,
                         num_kv_heads=w.hkv, head_dim=w.d, sink=w.sink, recent=w.recent,
                         capacity=capacity or w.capacity, retrieval_mask=mask,
-                        dtype=torch_dtype(w.dtype), out_dtype=out_dtype, max_splits=max_splits)
+                        dtype=torch_dtype(w.dtype), out_dtype=out_dtype, max_splits=max_splits,
+                        streaming_prefill=streaming_prefill)
 
 
 def fill(cache, w: W.Workload, layer: int, lens, chunk: int = 1 << 16, mask_layer=None):

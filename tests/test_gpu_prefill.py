@@ -16,15 +16,18 @@ pytestmark = pytest.mark.gpu
 
 
 def run_prefill(w, lens, chunk, layer=0, check_rows=None, cache=None, seqwise=False,
-                out_dtype=torch.float32, rng_seed=0):
+                out_dtype=torch.float32, rng_seed=0, mode="window"):
     """Prefill prompts of lengths ``lens`` in chunks of ``chunk``; returns the outputs.
+
+    ``mode`` is the streaming-head prefill mode: "window" (per-query sink + recent mask) or
+    "chunk" (the pruned cache before the chunk plus the chunk causally).
 
     ``check_rows``: None = every row, int = that many random rows per chunk and sequence.
     With ``seqwise`` every sequence is prefilled by its own calls (ragged prompts);
     otherwise all sequences share the chunk calls (equal lengths).
     """
     if cache is None:
-        cache = make_cache(w, out_dtype=out_dtype, capacity=max(lens) + 1)
+        cache = make_cache(w, out_dtype=out_dtype, capacity=max(lens) + 1, streaming_prefill=mode)
     dt = torch_dtype(w.dtype)
     mask = W.retrieval_mask(w)[layer]
     rng = np.random.default_rng(rng_seed)
@@ -62,7 +65,8 @@ def run_prefill(w, lens, chunk, layer=0, check_rows=None, cache=None, seqwise=Fa
             else:
                 rows = np.unique(rng.integers(c0, c1, size=min(check_rows, c1 - c0)))
             qa = W.tokens(w, "q", layer, s, 0, c1)[rows]
-            ref, ref_lse = O.attention(qa, kh, vh, rows, np.arange(c1), mask, w.sink, w.recent)
+            ref, ref_lse = O.attention(qa, kh, vh, rows, np.arange(c1), mask, w.sink, w.recent,
+                                       chunk_start=c0 if mode == "chunk" else None)
             assert_close(got[si][rows - c0], ref, f"chunk [{c0},{c1}) seq {s} out")
             assert_close(got_lse[si][rows - c0], ref_lse, f"chunk [{c0},{c1}) seq {s} lse")
     return outs, lses, cache

@@ -73,6 +73,17 @@ def test_config_checks(bad, status):
     assert N.lib().duo_layout_query(ctypes.byref(cfg2), ctypes.byref(lay)) == N.DUO_ERR_UNSUPPORTED
 
 
+def test_streaming_prefill_mode_checked():
+    lay = N.DuoLayout()
+    for mode, status in ((N.PREFILL_WINDOW, N.DUO_OK), (N.PREFILL_CHUNK, N.DUO_OK),
+                         (2, N.DUO_ERR_INVALID), (-1, N.DUO_ERR_INVALID)):
+        cfg, _keep = cfg_of()
+        cfg.streaming_prefill = mode
+        assert N.lib().duo_layout_query(ctypes.byref(cfg), ctypes.byref(lay)) == status, mode
+    with pytest.raises(ValueError):
+        cfg_of(streaming_prefill="sliding")
+
+
 def test_layout_covers_the_split_caches():
     cfg, mask = cfg_of()
     lay = hsk.duo_layout_query(cfg)
