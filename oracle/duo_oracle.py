@@ -255,3 +255,85 @@ def budget_ratio(retrieval_fraction: float, length: int, sink: int, recent: int)
     """
     r = retrieval_fraction
     return (r * length + (1.0 - r) * min(length, sink + recent)) / length
+
+
+# --------------------------------------------------------------------------------------------
+# From trained gates to the deployed head split
+# --------------------------------------------------------------------------------------------
+
+def retrieval_count(n_heads: int, ratio: float) -> int:
+    """Number of retrieval heads for a target retrieval ratio over ``n_heads`` KV heads.
+
+    Explainer, "Binarization: From Continuous Gates to Hard Assignments": the threshold is set
+    so that a target fraction of the heads (25 % for the MHA model, 50 % for the GQA models)
+    become retrieval heads. Reading: the count nearest to ratio * n_heads, halves rounded up,
+    clamped to [0, n_heads], the product being taken in double precision (so 0.7 * 5, which
+    rounds to 3.5, gives 4).
+    """
+    if not (0.0 <= ratio <= 1.0):
+        raise ValueError("ratio must lie in [0, 1]")
+    return max(0, min(n_heads, int(math.floor(ratio * n_heads + 0.5))))
+
+
+def binarize_gates(alpha, ratio: float):
+    """Hard retrieval/streaming assignment from the gate values ``alpha [L][H_kv]``.
+
+    Explainer, same section, Equation 4: head (i, j) keeps full attention when its gate
+    exceeds a threshold tau, and streaming attention otherwise, with tau placed at the
+    quantile that leaves the target fraction of all heads of the model as retrieval heads.
+
+    Reading: the quantile runs over every KV head of every layer together. Heads are ranked
+    by decreasing gate value; equal values are ranked by layer, then head, ascending (the
+    pages leave ties open). The first ``retrieval_count`` heads of that ranking are the
+    retrieval heads, and tau is the gate of the first head left out (-inf when every head is
+    kept), so that "alpha > tau" is exactly the retrieval set whenever no other head shares
+    tau's value. Returns ``(mask uint8 [L][H_kv], tau)``.
+    """
+    a = np.asarray(alpha, dtype=np.float64)
+    if a.ndim != 2 or not np.all(np.isfinite(a)):
+        raise ValueError("alpha must be a finite [layers][kv_heads] array")
+    L, H = a.shape
+    k = retrieval_count(L * H, ratio)
+    ranking = sorted(((layer, head) for layer in range(L) for head in range(H)),
+                     key=lambda lh: (-a[lh], lh[0], lh[1]))
+    mask = np.zeros((L, H), dtype=np.uint8)
+    for lh in ranking[:k]:
+        mask[lh] = 1
+    tau = a[ranking[k]] if k < L * H else -math.inf
+    return mask, float(tau)
+
+
+def head_order(mask_layer) -> np.ndarray:
+    """Native KV head at each position of the reordered layout of one layer.
+
+    Explainer, "Head Reordering Preprocessing": the projection weights are permuted so that
+    the retrieval heads take the first H_r head slots and the streaming heads the remaining
+    H_s. Reading: each class keeps its native order (a stable partition).
+    """
+    m = np.asarray(mask_layer).astype(bool)
+    return np.array([j for j in range(m.size) if m[j]] + [j for j in range(m.size) if not m[j]],
+                    dtype=np.int64)
+
+
+def query_head_order(kv_order, group: int) -> np.ndarray:
+    """Native query head at each reordered query position: the G query heads of a KV head
+    move with it, in their own order (same section; the same permutation must hold across Q,
+    K and V, and a KV head serves the contiguous group of ``kv_head_of``)."""
+    return np.array([j * group + g for j in kv_order for g in range(group)], dtype=np.int64)
+
+
+def reorder_output_rows(w, order, rows_per_head: int) -> np.ndarray:
+    """Rows of a Q, K or V projection weight ``[heads * rows_per_head][hidden]`` with head
+    blocks in the reordered layout: block i of the result is block ``order[i]`` of ``w``."""
+    w = np.asarray(w)
+    return np.concatenate([w[h * rows_per_head:(h + 1) * rows_per_head] for h in order], axis=0)
+
+
+def reorder_input_cols(w, order, cols_per_head: int) -> np.ndarray:
+    """Columns of the output projection ``[hidden][heads * cols_per_head]`` permuted the same
+    way, so that it reads the concatenated head outputs of the reordered layout (explainer,
+    same section: reordering the heads and the output projection together leaves the layer's
+    output unchanged)."""
+    w = np.asarray(w)
+    return np.concatenate([w[:, h * cols_per_head:(h + 1) * cols_per_head] for h in order],
+                          axis=1)

@@ -379,12 +379,119 @@ def pin_lambda_mask_literal():
                           np.tril(np.ones((7, 7), dtype=bool)))
 
 
+def pin_retrieval_count_nearest():
+    """The retrieval count is the integer nearest ratio * N (the product rounded to double,
+    halves up), by search over every count; the pages' two budgets give 256 of the 1,024 Llama-2-7B heads and 128 of the
+    32 x 8 Llama-3-8B KV heads."""
+    from fractions import Fraction
+    for n in range(0, 13):
+        for ratio in (0.0, 0.1, 0.25, 1 / 3, 0.5, 0.7, 0.75, 0.9, 1.0):
+            target = Fraction(ratio * n)  # the product as rounded to double
+            best = min(range(n + 1), key=lambda c: (abs(Fraction(c) - target), -c))
+            assert O.retrieval_count(n, ratio) == best, (n, ratio)
+    assert O.retrieval_count(32 * 32, 0.25) == 256
+    assert O.retrieval_count(32 * 8, 0.5) == 128
+
+
+def _gates(rng, L, H, levels):
+    return rng.integers(0, levels, size=(L, H)) / float(levels)  # exact, with ties
+
+
+def pin_binarize_bruteforce():
+    """Among all head subsets of the retrieval count, the chosen set has the largest gate sum
+    and, among those, the lexicographically first (layer, head) list: the stated tie-break."""
+    import itertools
+    rng = np.random.default_rng(31)
+    for (L, H) in [(1, 4), (2, 3), (3, 2), (2, 4)]:
+        for levels in (3, 8, 1000):
+            a = _gates(rng, L, H, levels)
+            for ratio in (0.25, 0.5, 0.7, 1 / 3):
+                mask, tau = O.binarize_gates(a, ratio)
+                n = L * H
+                k = O.retrieval_count(n, ratio)
+                flat = a.reshape(-1)
+                best = None
+                for sub in itertools.combinations(range(n), k):
+                    key = (-sum(flat[list(sub)]), sub)
+                    if best is None or key < best:
+                        best = key
+                want = np.zeros(n, dtype=np.uint8)
+                want[list(best[1])] = 1
+                assert np.array_equal(mask.reshape(-1), want), (L, H, levels, ratio)
+
+
+def pin_binarize_equation4():
+    """With distinct gates the assignment is Equation 4 itself: retrieval iff alpha > tau,
+    exactly the target count of heads. The result depends on the gates' order only, and a
+    larger ratio keeps every head a smaller one kept."""
+    rng = np.random.default_rng(32)
+    for (L, H) in [(32, 32), (32, 8), (5, 7)]:
+        a = rng.random((L, H))
+        prev = None
+        for ratio in (0.0, 0.1, 0.25, 0.5, 0.75, 1.0):
+            mask, tau = O.binarize_gates(a, ratio)
+            assert np.array_equal(mask, (a > tau).astype(np.uint8)), (L, H, ratio)
+            assert int(mask.sum()) == O.retrieval_count(L * H, ratio)
+            m2, _ = O.binarize_gates(3.0 * a ** 3 - 1.0, ratio)
+            assert np.array_equal(m2, mask)
+            if prev is not None:
+                assert np.all(mask >= prev)
+            prev = mask
+    m, _ = O.binarize_gates(rng.random((32, 32)), 0.25)
+    assert m.sum() == 256
+    m, _ = O.binarize_gates(rng.random((32, 8)), 0.5)
+    assert m.sum() == 128
+
+
+def pin_head_reordering_preserves_layer():
+    """Reordering Q/K/V output rows and the output projection's input columns by the head
+    order leaves an attention layer's output unchanged, and puts the H_r retrieval heads
+    first: projection, per-head attention with the reordered mask, output projection."""
+    rng = np.random.default_rng(33)
+    for (Hkv, G, mask_row) in [(4, 2, [0, 1, 0, 1]), (3, 1, [1, 0, 1]), (4, 4, [0, 0, 1, 0])]:
+        d, hidden, T, S, R = 8, 24, 14, 2, 4
+        Hq = Hkv * G
+        x = rng.standard_normal((T, hidden))
+        wq = rng.standard_normal((Hq * d, hidden))
+        wk = rng.standard_normal((Hkv * d, hidden))
+        wv = rng.standard_normal((Hkv * d, hidden))
+        wo = rng.standard_normal((hidden, Hq * d))
+        mask = np.array(mask_row, dtype=np.uint8)
+
+        def layer(wq, wk, wv, wo, mask):
+            q = (x @ wq.T).reshape(T, Hq, d)
+            k = (x @ wk.T).reshape(T, Hkv, d)
+            v = (x @ wv.T).reshape(T, Hkv, d)
+            heads, _ = O.attention(q, k, v, np.arange(T), np.arange(T), mask, S, R)
+            return heads.reshape(T, Hq * d) @ wo.T, q
+
+        ref, q_ref = layer(wq, wk, wv, wo, mask)
+        kv_order = O.head_order(mask)
+        q_order = O.query_head_order(kv_order, G)
+        assert sorted(kv_order.tolist()) == list(range(Hkv))
+        assert sorted(q_order.tolist()) == list(range(Hq))
+        mask2 = mask[kv_order]
+        hr = int(mask.sum())
+        assert mask2.tolist() == [1] * hr + [0] * (Hkv - hr)
+        got, q_got = layer(O.reorder_output_rows(wq, q_order, d),
+                           O.reorder_output_rows(wk, kv_order, d),
+                           O.reorder_output_rows(wv, kv_order, d),
+                           O.reorder_input_cols(wo, q_order, d), mask2)
+        assert np.allclose(got, ref, rtol=0, atol=1e-9)
+        assert np.array_equal(q_got, q_ref[:, q_order])
+        # stable inside each class
+        assert list(kv_order[:hr]) == sorted(kv_order[:hr])
+        assert list(kv_order[hr:]) == sorted(kv_order[hr:])
+
+
 PINS = [pin_cache_policy, pin_streaming_rows, pin_decode_scalar_bruteforce,
         pin_all_retrieval_is_causal_attention, pin_short_streaming_is_full,
         pin_no_sink_is_sliding_window, pin_fig5_worked_example, pin_memory_numbers,
         pin_memory_formula_by_count, pin_chunk_invariance_and_decode_equivalence,
         pin_head_permutation, pin_gqa_equals_repeated_mha, pin_lambda_mask_literal,
-        pin_chunk_granular_fig5, pin_chunk_granular_gather, pin_chunk_granular_short_is_full]
+        pin_chunk_granular_fig5, pin_chunk_granular_gather, pin_chunk_granular_short_is_full,
+        pin_retrieval_count_nearest, pin_binarize_bruteforce, pin_binarize_equation4,
+        pin_head_reordering_preserves_layer]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -446,7 +553,31 @@ def _chunk_held_one_short(q_pos, k_pos, start, retrieval, sink, recent):
     return held | ((t >= start) & (t <= p))
 
 
+def _binarize_ties_high_first(alpha, ratio):
+    a = np.asarray(alpha, dtype=np.float64)
+    L, H = a.shape
+    k = O.retrieval_count(L * H, ratio)
+    ranking = sorted(((i, j) for i in range(L) for j in range(H)), key=lambda lh: (-a[lh], -lh[0], -lh[1]))
+    mask = np.zeros((L, H), dtype=np.uint8)
+    for lh in ranking[:k]:
+        mask[lh] = 1
+    return mask, float(a[ranking[k]]) if k < L * H else -math.inf
+
+
+def _binarize_tau_last_kept(alpha, ratio):
+    mask, _ = _ORIG_BIN(alpha, ratio)
+    a = np.asarray(alpha, dtype=np.float64)
+    return mask, float(a[mask == 1].min()) if mask.any() else float(a.max())
+
+
+def _binarize_per_layer(alpha, ratio):
+    a = np.asarray(alpha, dtype=np.float64)
+    rows = [_ORIG_BIN(a[i:i + 1], ratio) for i in range(a.shape[0])]
+    return np.concatenate([r[0] for r in rows]), min(r[1] for r in rows)
+
+
 _ORIG_MSA = O.masked_softmax_attention
+_ORIG_BIN = O.binarize_gates
 
 MUTANTS = {
     "window_too_wide": ("visible_mask", _window_too_wide),
@@ -469,6 +600,14 @@ MUTANTS = {
     "chunk_held_one_short": ("chunk_visible_mask", _chunk_held_one_short),
     "chunk_window_per_query": ("chunk_visible_mask",
                                lambda q, k, st, r, S, R: O.visible_mask(q, k, r, S, R)),
+    "count_floor": ("retrieval_count", lambda n, r: int(math.floor(r * n))),
+    "binarize_ties_high_first": ("binarize_gates", _binarize_ties_high_first),
+    "binarize_tau_last_kept": ("binarize_gates", _binarize_tau_last_kept),
+    "binarize_per_layer": ("binarize_gates", _binarize_per_layer),
+    "head_order_streaming_first": ("head_order",
+                                   lambda m: np.argsort(np.asarray(m) != 0, kind="stable")),
+    "query_order_interleaved": ("query_head_order",
+                                lambda o, G: np.array([g * len(o) + j for j in o for g in range(G)])),
 }
 
 
