@@ -292,6 +292,73 @@ def prefill_leg(args, torch, hsk, W, N, mode="window"):
                 tflops_incl_append=flops / (pass_ms * 1e-3) / 1e12)
 
 
+def reorder_leg(args, torch, hsk, N):
+    """One-time head reordering of a Llama-3-8B-shaped model's attention projections: gates
+    of 32 layers x 8 KV heads binarized at 50 %, then every layer's Q, K, V rows and output
+    projection columns permuted on the GPU (128 launches, 2.68 GB of bf16 weights, each byte
+    read and written once)."""
+    import numpy as np
+    L, Hkv, G, d, hidden = 32, 8, 4, 128, 4096
+    Hq = Hkv * G
+    rng = np.random.default_rng(5)
+    alpha = np.clip(rng.normal(0.3, 0.3, (L, Hkv)), 0, 1).astype(np.float32)
+    mask, _, n_ret = hsk.duo_binarize_gates(alpha, 0.5)
+    orders = [hsk.duo_head_order(mask[layer], G) for layer in range(L)]
+    shapes = [(Hq * d, hidden), (Hkv * d, hidden), (Hkv * d, hidden), (hidden, Hq * d)]
+    src = [[torch.randn(s, device="cuda", dtype=torch.bfloat16) for s in shapes] for _ in range(L)]
+    dst = [[torch.empty_like(t) for t in layer] for layer in src]
+    # the first pass goes through the binding (its checks), the timed ones through the C
+    # calls with prepared arguments
+    for layer in range(L):
+        kv_o, q_o = orders[layer]
+        for t, (o, nb, bb, order) in enumerate([(1, Hq, d * hidden * 2, q_o),
+                                                (1, Hkv, d * hidden * 2, kv_o),
+                                                (1, Hkv, d * hidden * 2, kv_o),
+                                                (hidden, Hq, d * 2, q_o)]):
+            hsk.duo_permute_blocks(src[layer][t], dst[layer][t], o, nb, bb, order)
+    lib = hsk.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P32 = ctypes.POINTER(ctypes.c_int32)
+    keep = [(np.ascontiguousarray(kv, dtype=np.int32), np.ascontiguousarray(q, dtype=np.int32))
+            for kv, q in orders]
+    calls = []
+    for layer in range(L):
+        kv_o, q_o = (a.ctypes.data_as(P32) for a in keep[layer])
+        for t, (o, nb, bb, order) in enumerate([(1, Hq, d * hidden * 2, q_o),
+                                                (1, Hkv, d * hidden * 2, kv_o),
+                                                (1, Hkv, d * hidden * 2, kv_o),
+                                                (hidden, Hq, d * 2, q_o)]):
+            calls.append((ctypes.c_void_p(src[layer][t].data_ptr()),
+                          ctypes.c_void_p(dst[layer][t].data_ptr()), o, nb, bb, order, t))
+
+    def run(only=None):
+        for s_, d_, o, nb, bb, order, t in calls:
+            if only is None or t == only:
+                st = lib.duo_permute_blocks(s_, d_, o, nb, bb, order, stream)
+                if st:
+                    raise RuntimeError(f"permute failed: {N.status_string(st)}")
+
+    run()
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    reps = 5
+    tm.start()
+    for _ in range(reps):
+        run()
+    ms = tm.stop_ms() / reps
+    nbytes = sum(t.numel() * 2 for layer in src for t in layer)
+    # the output projection alone (column blocks of 256 bytes), timed the same way
+    tm.start()
+    for _ in range(reps):
+        run(only=3)
+    ms_o = tm.stop_ms() / reps
+    o_bytes = sum(layer[3].numel() * 2 for layer in src)
+    del src, dst
+    torch.cuda.empty_cache()
+    return dict(ms=ms, bytes=nbytes, gbs=2 * nbytes / (ms * 1e-3) / 1e9, n_ret=n_ret,
+                o_gbs=2 * o_bytes / (ms_o * 1e-3) / 1e9)
+
+
 def copy_probe(torch):
     """Achievable HBM bandwidth of a plain device copy (read + write bytes)."""
     n = 1 << 30
@@ -388,6 +455,9 @@ def main():
                 f"{pre_chunk['kern_tflops']:.1f} TFLOP/s")
         except (RuntimeError, hsk.DuoError) as e:
             log(f"chunk-mode prefill leg skipped: {e}")
+    reo = reorder_leg(args, torch, hsk, N)
+    log(f"reorder: {reo['ms']:.3f} ms for {reo['bytes'] / 1e9:.2f} GB of projections = "
+        f"{reo['gbs']:.0f} GB/s (read + write); output projections alone {reo['o_gbs']:.0f} GB/s")
     probe = copy_probe(torch)
     w = dec["workload"]
     cpu = cpu_pre = None
@@ -433,6 +503,14 @@ def main():
             "algorithmic_bytes_per_launch": int(dec["step_bytes"]),
         },
         "hbm_copy_probe_GBps": round(probe, 1),
+        "head_reorder": {
+            "workload": "Llama-3-8B-shaped attention projections, 32 layers (Q, K, V rows and "
+                        "output-projection columns, bf16), heads ordered by gates binarized at "
+                        f"50 % ({reo['n_ret']} of 256 KV heads retrieval)",
+            "ms": round(reo["ms"], 3), "bytes": int(reo["bytes"]),
+            "GBps": round(reo["gbs"], 1), "frac": round(reo["gbs"] / HBM_PEAK_GBS, 4),
+            "output_projection_GBps": round(reo["o_gbs"], 1),
+        },
         "prefill": None if pre is None else {
             "workload": f"{pre['workload'].name}: 32K prompt in 4K chunks",
             "attn_ms": round(pre["attn_ms"], 3),

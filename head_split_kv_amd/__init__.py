@@ -287,5 +287,78 @@ def duo_timing_read(cache: DuoCache, kind: str = "decode"):
     return ms.value, n.value
 
 
+def duo_binarize_gates(alpha, ratio: float):
+    """Retrieval mask (uint8 ``[L, H_kv]``), threshold tau and retrieval count from the trained
+    gates ``alpha [L, H_kv]`` for a target retrieval ratio (the quantile runs over all heads;
+    equal gates go to the lower (layer, head))."""
+    a = np.ascontiguousarray(np.asarray(alpha, dtype=np.float32))
+    if a.ndim != 2:
+        raise ValueError("alpha must be [layers, kv_heads]")
+    mask = np.empty(a.shape, dtype=np.uint8)
+    tau = ctypes.c_float()
+    n = ctypes.c_int32()
+    check(lib().duo_binarize_gates(a.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), a.shape[0],
+                                   a.shape[1], float(ratio),
+                                   mask.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
+                                   ctypes.byref(tau), ctypes.byref(n)), "duo_binarize_gates")
+    return mask, tau.value, n.value
+
+
+def duo_head_order(mask_layer, group: int = 1):
+    """(kv_order, q_order): native KV / query head at each slot of the reordered layout of one
+    layer, retrieval heads first."""
+    m = np.ascontiguousarray(np.asarray(mask_layer, dtype=np.uint8).reshape(-1))
+    kv = np.empty(m.size, dtype=np.int32)
+    q = np.empty(m.size * group, dtype=np.int32)
+    check(lib().duo_head_order(m.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)), m.size, group,
+                               kv.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                               q.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))),
+          "duo_head_order")
+    return kv, q
+
+
+def duo_permute_blocks(src: torch.Tensor, dst: torch.Tensor, outer: int, n_blocks: int,
+                       block_bytes: int, order, stream=None) -> None:
+    """``dst[o][i] = src[o][order[i]]`` over blocks of ``block_bytes`` bytes (device tensors)."""
+    for t in (src, dst):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError("src and dst must be contiguous device tensors")
+    if src.numel() * src.element_size() != outer * n_blocks * block_bytes or \
+            dst.numel() * dst.element_size() != outer * n_blocks * block_bytes:
+        raise ValueError("tensor sizes do not match outer * n_blocks * block_bytes")
+    o = np.ascontiguousarray(np.asarray(order, dtype=np.int32).reshape(-1))
+    if o.size != n_blocks:
+        raise ValueError("order must have n_blocks entries")
+    check(lib().duo_permute_blocks(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                   outer, n_blocks, block_bytes,
+                                   o.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                   _stream(stream)), "duo_permute_blocks")
+
+
+def reorder_output_rows(w: torch.Tensor, order, rows_per_head: int, stream=None) -> torch.Tensor:
+    """A Q, K or V projection weight ``[heads * rows_per_head, hidden]`` with its head blocks
+    in ``order`` (block i of the result is block ``order[i]`` of ``w``)."""
+    heads = len(order)
+    if w.dim() != 2 or w.shape[0] != heads * rows_per_head:
+        raise ValueError("w must be [heads * rows_per_head, hidden]")
+    w = w.contiguous()
+    out = torch.empty_like(w)
+    duo_permute_blocks(w, out, 1, heads, rows_per_head * w.shape[1] * w.element_size(), order,
+                       stream)
+    return out
+
+
+def reorder_input_cols(w: torch.Tensor, order, cols_per_head: int, stream=None) -> torch.Tensor:
+    """The output projection ``[hidden, heads * cols_per_head]`` with its per-head column
+    blocks in ``order``."""
+    heads = len(order)
+    if w.dim() != 2 or w.shape[1] != heads * cols_per_head:
+        raise ValueError("w must be [hidden, heads * cols_per_head]")
+    w = w.contiguous()
+    out = torch.empty_like(w)
+    duo_permute_blocks(w, out, w.shape[0], heads, cols_per_head * w.element_size(), order, stream)
+    return out
+
+
 def duo_status_string(status: int) -> str:
     return status_string(status)

@@ -19,7 +19,8 @@ EXPORTS = (
     "duo_kv_append", "duo_attn_decode", "duo_decode_step", "duo_attn_prefill",
     "duo_slot_positions",
     "duo_cache_lengths", "duo_kv_bytes", "duo_set_decode_splits", "duo_timing_enable",
-    "duo_timing_read", "duo_status_string",
+    "duo_timing_read", "duo_binarize_gates", "duo_head_order", "duo_permute_blocks",
+    "duo_status_string",
 )
 TIMING_DECODE, TIMING_PREFILL = 0, 1
 PREFILL_WINDOW, PREFILL_CHUNK = 0, 1
@@ -92,6 +93,10 @@ def lib() -> ctypes.CDLL:
         "duo_set_decode_splits": (st, [vp, i32]),
         "duo_timing_enable": (st, [vp, i32]),
         "duo_timing_read": (st, [vp, i32, P(ctypes.c_double), P(i32)]),
+        "duo_binarize_gates": (st, [P(ctypes.c_float), i32, i32, ctypes.c_double,
+                                    P(ctypes.c_uint8), P(ctypes.c_float), P(i32)]),
+        "duo_head_order": (st, [P(ctypes.c_uint8), i32, i32, P(i32), P(i32)]),
+        "duo_permute_blocks": (st, [vp, vp, ctypes.c_int64, i32, ctypes.c_int64, P(i32), vp]),
         "duo_status_string": (ctypes.c_char_p, [st]),
     }
     for name, (res, args) in sig.items():

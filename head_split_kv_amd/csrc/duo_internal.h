@@ -127,6 +127,18 @@ int launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group, void*
 int launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int group, void* stream,
                    const KernelMarks& marks);
 
+// Block permutation (reorder.hip): dst[o][i] = src[o][order[i]], blocks of 16-byte chunks.
+constexpr int kMaxPermuteBlocks = 1024;
+struct PermuteArgs {
+  const void* src;
+  void* dst;
+  uint32_t n_chunks;        // outer * n_blocks * chunks_per_block (< 2^31)
+  uint32_t chunks_per_block;
+  uint32_t n_blocks;
+  uint16_t order[kMaxPermuteBlocks];
+};
+int launch_permute(const PermuteArgs& a, void* stream);
+
 // HIP events of the kernel timers (cache_kernels.hip); hipError_t values as int.
 int create_events(int n, std::vector<void*>* out);
 void destroy_events(std::vector<void*>* ev);

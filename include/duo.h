@@ -205,6 +205,46 @@ typedef enum { DUO_TIMING_DECODE = 0, DUO_TIMING_PREFILL = 1 } duo_timing_kind;
 duo_status duo_timing_enable(duo_cache* cache, int32_t max_records);
 duo_status duo_timing_read(duo_cache* cache, int32_t kind, double* total_ms, int32_t* records);
 
+/* ---- From trained gates to the deployed head split (one-time preprocessing) ---- */
+
+/* Retrieval/streaming assignment of every KV head of a model from its trained gates
+ * (explainer, "Binarization: From Continuous Gates to Hard Assignments", Equation 4: full
+ * attention iff the gate exceeds a threshold tau placed at the quantile that keeps a target
+ * fraction of the heads). alpha: host float [n_layers][n_kv_heads], finite. The quantile runs
+ * over all heads together: the n = floor(ratio * n_layers * n_kv_heads + 0.5) heads (product
+ * in double precision) ranked first by decreasing gate, equal gates ranked by (layer, head)
+ * ascending, get mask_out = 1 (retrieval), the others 0 (streaming). mask_out: host uint8
+ * [n_layers][n_kv_heads], the layout of duo_config.retrieval_mask. tau_out (may be NULL): the
+ * gate of the first head left out, -inf when every head is kept; with distinct gates the mask
+ * is exactly alpha > tau. n_retrieval_out (may be NULL): n. Host only. DUO_ERR_INVALID for a
+ * null alpha or mask_out, sizes below 1, a non-finite gate or ratio outside [0, 1]. */
+duo_status duo_binarize_gates(const float* alpha, int32_t n_layers, int32_t n_kv_heads,
+                              double ratio, uint8_t* mask_out, float* tau_out,
+                              int32_t* n_retrieval_out);
+
+/* Head order of one layer after reordering (explainer, "Head Reordering Preprocessing": the
+ * retrieval heads take the first H_r head slots of the Q, K and V projections, the streaming
+ * heads the rest). mask: host uint8 [n_kv_heads], nonzero = retrieval. kv_order_out[i]: the
+ * native KV head placed at slot i, retrieval heads first, each class in native order.
+ * q_order_out (may be NULL) [n_kv_heads * group]: the native query head at each query slot,
+ * the group's query heads moving with their KV head (head h belongs to KV head h / group).
+ * Host only. DUO_ERR_INVALID for null pointers, n_kv_heads outside 1..1024 or group < 1. */
+duo_status duo_head_order(const uint8_t* mask, int32_t n_kv_heads, int32_t group,
+                          int32_t* kv_order_out, int32_t* q_order_out);
+
+/* Reorder equal blocks of a device tensor on `stream` (the weight permutation of the same
+ * section): dst[o][i] = src[o][order[i]] for o < outer and i < n_blocks, every block
+ * block_bytes long. The rows of a Q, K or V projection [heads * head_dim][hidden] are outer
+ * = 1, one block of head_dim * hidden elements per head; the columns of the output projection
+ * [hidden][heads * head_dim] are outer = hidden, one block of head_dim elements per head.
+ * order: host int32 [n_blocks], a permutation of 0..n_blocks-1 (copied into the launch).
+ * src and dst: device memory, 16-byte aligned, not overlapping; block_bytes a positive
+ * multiple of 16; n_blocks 1..1024; outer * n_blocks * block_bytes / 16 below 2^31. outer = 0
+ * is a no-op. DUO_ERR_INVALID otherwise (nothing is launched), DUO_ERR_HIP if the launch
+ * fails. */
+duo_status duo_permute_blocks(const void* src, void* dst, int64_t outer, int32_t n_blocks,
+                              int64_t block_bytes, const int32_t* order, void* stream);
+
 /* Static text for a status code. */
 const char* duo_status_string(duo_status status);
 
