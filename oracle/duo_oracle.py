@@ -148,6 +148,26 @@ def attention(q, k, v, q_pos, k_pos, retrieval, sink, recent, scale=None, chunk_
     return out, lse
 
 
+def gate_mixed_attention(q, k, v, q_pos, k_pos, alpha, sink, recent, scale=None):
+    """Attention of the identification phase: for KV head j with gate ``alpha[j]``, each of
+    its query heads returns alpha_j * full_attn + (1 - alpha_j) * streaming_attn.
+
+    Explainer, "Gate Parameterization" (the mixing equation) and "The Full and Streaming
+    Attention Masks": full_attn is softmax attention under the causal mask and
+    streaming_attn the same under the Lambda mask, over the same keys; the two normalized
+    outputs are blended, not their logits or weights. Shapes as in ``attention``;
+    ``alpha [Hkv]``. Returns ``out [P, Hq, d]``.
+    """
+    Hkv = np.asarray(k).shape[1]
+    full, _ = attention(q, k, v, q_pos, k_pos, np.ones(Hkv, dtype=np.uint8), sink, recent, scale)
+    stream, _ = attention(q, k, v, q_pos, k_pos, np.zeros(Hkv, dtype=np.uint8), sink, recent,
+                          scale)
+    a = np.asarray(alpha, dtype=np.float64)
+    G = np.asarray(q).shape[1] // Hkv
+    w = np.array([a[kv_head_of(h, G)] for h in range(np.asarray(q).shape[1])])[None, :, None]
+    return w * full + (1.0 - w) * stream
+
+
 def decode_step(q, k_hist, v_hist, retrieval, sink, recent, scale=None):
     """Decode one token for one sequence.
 

@@ -484,6 +484,40 @@ def pin_head_reordering_preserves_layer():
         assert list(kv_order[hr:]) == sorted(kv_order[hr:])
 
 
+def pin_gate_mixed_bruteforce():
+    """Scalar loops over tiny inputs: per query head, two separately normalized softmax
+    averages (causal keys; sink + recent keys) blended by the KV head's gate. Gate 1 is
+    causal attention, gate 0 is the Lambda-masked attention of a streaming head, and while
+    every query is within S + R tokens the gate does not matter."""
+    rng = np.random.default_rng(41)
+    T, Hkv, G, d, S, R = 11, 2, 2, 4, 2, 3
+    q, k, v = rand(rng, T, Hkv * G, d), rand(rng, T, Hkv, d), rand(rng, T, Hkv, d)
+    alpha = np.array([0.3, 0.85])
+    pos = np.arange(T)
+    out = O.gate_mixed_attention(q, k, v, pos, pos, alpha, S, R)
+    for p in range(T):
+        for h in range(Hkv * G):
+            j = h // G
+            parts = []
+            for keys in (list(range(p + 1)),
+                         [t for t in range(p + 1) if t < S or t >= p - R + 1]):
+                z = [sum(q[p, h, c] * k[t, j, c] for c in range(d)) / math.sqrt(d) for t in keys]
+                mz = max(z)
+                w = [math.exp(x - mz) for x in z]
+                parts.append([sum(w[i] * v[t, j, c] for i, t in enumerate(keys)) / sum(w)
+                              for c in range(d)])
+            want = [alpha[j] * parts[0][c] + (1 - alpha[j]) * parts[1][c] for c in range(d)]
+            assert np.allclose(out[p, h], want, rtol=0, atol=1e-12), (p, h)
+    full, _ = O.attention(q, k, v, pos, pos, [1, 1], S, R)
+    stream, _ = O.attention(q, k, v, pos, pos, [0, 0], S, R)
+    assert np.allclose(O.gate_mixed_attention(q, k, v, pos, pos, [1, 1], S, R), full, atol=1e-14)
+    assert np.allclose(O.gate_mixed_attention(q, k, v, pos, pos, [0, 0], S, R), stream, atol=1e-14)
+    short = np.arange(S + R)
+    a = O.gate_mixed_attention(q[:S + R], k[:S + R], v[:S + R], short, short, [0.1, 0.9], S, R)
+    assert np.allclose(a, _sdpa_causal(q[:S + R], np.repeat(k[:S + R], G, axis=1),
+                                       np.repeat(v[:S + R], G, axis=1)), atol=1e-12)
+
+
 PINS = [pin_cache_policy, pin_streaming_rows, pin_decode_scalar_bruteforce,
         pin_all_retrieval_is_causal_attention, pin_short_streaming_is_full,
         pin_no_sink_is_sliding_window, pin_fig5_worked_example, pin_memory_numbers,
@@ -491,7 +525,7 @@ PINS = [pin_cache_policy, pin_streaming_rows, pin_decode_scalar_bruteforce,
         pin_head_permutation, pin_gqa_equals_repeated_mha, pin_lambda_mask_literal,
         pin_chunk_granular_fig5, pin_chunk_granular_gather, pin_chunk_granular_short_is_full,
         pin_retrieval_count_nearest, pin_binarize_bruteforce, pin_binarize_equation4,
-        pin_head_reordering_preserves_layer]
+        pin_head_reordering_preserves_layer, pin_gate_mixed_bruteforce]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -576,8 +610,30 @@ def _binarize_per_layer(alpha, ratio):
     return np.concatenate([r[0] for r in rows]), min(r[1] for r in rows)
 
 
+def _mixed_unnormalized(q, k, v, q_pos, k_pos, alpha, sink, recent, scale=None):
+    """Blends the unnormalized sums and normalizes once (a plausible fused-kernel mistake)."""
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    P, Hq, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    sc = 1 / math.sqrt(d) if scale is None else scale
+    out = np.empty((P, Hq, d))
+    for h in range(Hq):
+        j = h // G
+        z = sc * (q[:, h] @ k[:, j].T)
+        num, den = 0, 0
+        for r, wgt in ((True, alpha[j]), (False, 1 - alpha[j])):
+            m = O.visible_mask(q_pos, k_pos, r, sink, recent)
+            e = np.where(m, np.exp(z - z.max(axis=1, keepdims=True)), 0)
+            num = num + wgt * (e @ v[:, j])
+            den = den + wgt * e.sum(axis=1, keepdims=True)
+        out[:, h] = num / den
+    return out
+
+
 _ORIG_MSA = O.masked_softmax_attention
 _ORIG_BIN = O.binarize_gates
+_ORIG_MIX = O.gate_mixed_attention
 
 MUTANTS = {
     "window_too_wide": ("visible_mask", _window_too_wide),
@@ -606,6 +662,10 @@ MUTANTS = {
     "binarize_per_layer": ("binarize_gates", _binarize_per_layer),
     "head_order_streaming_first": ("head_order",
                                    lambda m: np.argsort(np.asarray(m) != 0, kind="stable")),
+    "mixed_alpha_swapped": ("gate_mixed_attention",
+                            lambda q, k, v, qp, kp, a, S, R, scale=None: _ORIG_MIX(
+                                q, k, v, qp, kp, 1 - np.asarray(a), S, R, scale)),
+    "mixed_unnormalized_blend": ("gate_mixed_attention", _mixed_unnormalized),
     "query_order_interleaved": ("query_head_order",
                                 lambda o, G: np.array([g * len(o) + j for j in o for g in range(G)])),
 }
