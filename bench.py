@@ -10,7 +10,13 @@ the 256 MB Infinity Cache; the time per layer-step is the step time divided by t
 Prefill leg: the Llama-2-7B-shaped MHA layer (32 heads, 8 retrieval) pre-filling a 32K
 prompt in 4K-token chunks (prefill attention of each chunk, then its append), once with the
 per-query sink + recent mask on streaming heads and once with chunk-granular streaming heads
-(the pruned cache before the chunk plus the chunk; ``--prefill-modes`` picks either).
+(the pruned cache before the chunk plus the chunk; ``--prefill-modes`` picks the legs).
+
+Gate-mixed leg: the identification-phase attention of the same MHA layer over one 32K-token
+sequence processed whole (every head blends its causal and sink + recent outputs).
+
+Head-reorder leg: the one-time permutation of a Llama-3-8B-shaped model's attention
+projections (2.68 GB) after binarizing its gates.
 
 Prints one JSON line. ``value`` is the decode K/V bandwidth in GB/s (algorithmic bytes: the
 K/V rows the method must read, plus q, out and the appended token). Inputs are resident in
@@ -47,8 +53,9 @@ def parse():
     p.add_argument("--workload", default="c3", help="decode workload key (c2, c3, c5, c5q)")
     p.add_argument("--prefill-passes", type=int, default=3)
     p.add_argument("--no-prefill", action="store_true")
-    p.add_argument("--prefill-modes", default="window,chunk",
-                   help="streaming-head prefill modes to time: window, chunk or both")
+    p.add_argument("--prefill-modes", default="window,chunk,mixed",
+                   help="prefill legs to time: window (per-query sink + recent mask), chunk "
+                        "(chunk-granular streaming heads), mixed (gate-mixed attention)")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--splits", type=int, default=0, help="force decode splits (0 = automatic)")
@@ -292,6 +299,59 @@ def prefill_leg(args, torch, hsk, W, N, mode="window"):
                 tflops_incl_append=flops / (pass_ms * 1e-3) / 1e12)
 
 
+def gate_mixed_leg(args, torch, hsk, W, N):
+    """Identification-phase attention: a Llama-2-7B-shaped MHA layer (32 heads, d 128, sink 16
+    + recent 512) over one 32,768-token sequence processed whole, every head blending its
+    causal and sink + recent outputs by a gate drawn in [0, 1]."""
+    import numpy as np
+    w = W.workload("c2")
+    T, H, d = w.prefill_len, w.hq, w.d
+    dev = torch.device("cuda")
+    cache = hsk.DuoCache(num_layers=1, batch=1, num_q_heads=H, num_kv_heads=H, head_dim=d,
+                         sink=w.sink, recent=w.recent, capacity=T,
+                         retrieval_mask=[np.ones(H, dtype=np.uint8)], dtype=torch.bfloat16,
+                         out_dtype=torch.bfloat16, device=dev)
+    q, k, v = (torch.from_numpy(W.tokens(w, t, 0, 0, 0, T)).to(dev).to(torch.bfloat16)
+               for t in "qkv")
+    out = torch.empty_like(q)
+    alpha = np.random.default_rng(91).random(H).astype(np.float32)
+    lib = N.lib()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    pa = alpha.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    args_ = (cache.handle, 0, 0, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+             ctypes.c_void_p(v.data_ptr()), T)
+
+    def mixed():
+        st = lib.duo_attn_gate_mixed(*args_, pa, ctypes.c_void_p(out.data_ptr()), stream)
+        if st:
+            raise RuntimeError(f"gate-mixed failed: {N.status_string(st)}")
+
+    def full():
+        st = lib.duo_attn_prefill(*args_, ctypes.c_void_p(out.data_ptr()), None, stream)
+        if st:
+            raise RuntimeError(f"prefill failed: {N.status_string(st)}")
+
+    reps = max(2, args.prefill_passes)
+    res = {}
+    for name, fn in (("mixed", mixed), ("full", full)):
+        fn()
+        torch.cuda.synchronize()
+        tm = Timer(torch)
+        tm.start()
+        for _ in range(reps):
+            fn()
+        res[name] = tm.stop_ms() / reps
+    S, R = w.sink, w.recent
+    pairs_full = T * (T + 1) // 2
+    pairs_str = sum(min(p + 1, S + R) for p in range(T))
+    flops = 4 * d * H * (pairs_full + pairs_str)
+    del cache, q, k, v, out
+    torch.cuda.empty_cache()
+    return dict(workload=w, ms=res["mixed"], full_ms=res["full"], flops=flops,
+                tflops=flops / (res["mixed"] * 1e-3) / 1e12,
+                full_tflops=4 * d * H * pairs_full / (res["full"] * 1e-3) / 1e12)
+
+
 def reorder_leg(args, torch, hsk, N):
     """One-time head reordering of a Llama-3-8B-shaped model's attention projections: gates
     of 32 layers x 8 KV heads binarized at 50 %, then every layer's Q, K, V rows and output
@@ -455,6 +515,12 @@ def main():
                 f"{pre_chunk['kern_tflops']:.1f} TFLOP/s")
         except (RuntimeError, hsk.DuoError) as e:
             log(f"chunk-mode prefill leg skipped: {e}")
+    mix = None
+    if not args.no_prefill and "mixed" in modes:
+        mix = gate_mixed_leg(args, torch, hsk, W, N)
+        log(f"gate-mixed: {mix['ms']:.3f} ms for {mix['flops'] / 1e12:.3f} TFLOP = "
+            f"{mix['tflops']:.1f} TFLOP/s; the causal pass alone {mix['full_ms']:.3f} ms = "
+            f"{mix['full_tflops']:.1f} TFLOP/s")
     reo = reorder_leg(args, torch, hsk, N)
     log(f"reorder: {reo['ms']:.3f} ms for {reo['bytes'] / 1e9:.2f} GB of projections = "
         f"{reo['gbs']:.0f} GB/s (read + write); output projections alone {reo['o_gbs']:.0f} GB/s")
@@ -503,6 +569,16 @@ def main():
             "algorithmic_bytes_per_launch": int(dec["step_bytes"]),
         },
         "hbm_copy_probe_GBps": round(probe, 1),
+        "gate_mixed": None if mix is None else {
+            "workload": "identification-phase attention: Llama-2-7B-shaped MHA layer, one "
+                        "32,768-token sequence processed whole, every head blending causal and "
+                        "sink 16 + recent 512 outputs by its gate",
+            "ms": round(mix["ms"], 3), "tflops": round(mix["tflops"], 1),
+            "frac": round(mix["tflops"] / BF16_PEAK_TFLOPS, 4),
+            "algorithmic_flops": int(mix["flops"]),
+            "causal_pass_alone_ms": round(mix["full_ms"], 3),
+            "causal_pass_alone_tflops": round(mix["full_tflops"], 1),
+        },
         "head_reorder": {
             "workload": "Llama-3-8B-shaped attention projections, 32 layers (Q, K, V rows and "
                         "output-projection columns, bf16), heads ordered by gates binarized at "

@@ -135,6 +135,9 @@ class DuoCache:
     def attn_prefill(self, layer, q, k, v, seq=-1, out=None, lse=None, stream=None):
         return duo_attn_prefill(self, layer, seq, q, k, v, out, lse, stream=stream)
 
+    def attn_gate_mixed(self, layer, q, k, v, alpha, seq=-1, out=None, stream=None):
+        return duo_attn_gate_mixed(self, layer, seq, q, k, v, alpha, out, stream=stream)
+
     def slot_positions(self, layer, stream=None):
         return duo_slot_positions(self, layer, stream)
 
@@ -246,6 +249,30 @@ def duo_attn_prefill(cache: DuoCache, layer: int, seq: int, q: torch.Tensor, k: 
                                  ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
                                  m, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(lse_ptr),
                                  _stream(stream)), "duo_attn_prefill")
+    return out
+
+
+def duo_attn_gate_mixed(cache: DuoCache, layer: int, seq: int, q: torch.Tensor, k: torch.Tensor,
+                        v: torch.Tensor, alpha, out=None, stream=None):
+    """Gate-mixed attention of one chunk, ``alpha[j] * full + (1 - alpha[j]) * streaming`` per
+    KV head j (every KV head of the layer must keep a full cache). Shapes as in
+    ``duo_attn_prefill``; ``alpha`` has one gate per KV head. Does not modify the cache."""
+    m = q.shape[1] if seq < 0 else q.shape[0]
+    lead = (cache.batch, m) if seq < 0 else (m,)
+    _check_tensor(q, lead + (cache.hq, cache.d), cache.dtype, cache.device, "q")
+    _check_tensor(k, lead + (cache.hkv, cache.d), cache.dtype, cache.device, "k")
+    _check_tensor(v, lead + (cache.hkv, cache.d), cache.dtype, cache.device, "v")
+    if out is None:
+        out = torch.empty(lead + (cache.hq, cache.d), dtype=cache.out_dtype, device=q.device)
+    _check_tensor(out, lead + (cache.hq, cache.d), cache.out_dtype, cache.device, "out")
+    a = np.ascontiguousarray(np.asarray(alpha, dtype=np.float32).reshape(-1))
+    if a.size != cache.hkv:
+        raise ValueError(f"alpha must hold {cache.hkv} gates")
+    check(lib().duo_attn_gate_mixed(cache.handle, layer, seq, ctypes.c_void_p(q.data_ptr()),
+                                    ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+                                    m, a.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+                                    ctypes.c_void_p(out.data_ptr()), _stream(stream)),
+          "duo_attn_gate_mixed")
     return out
 
 

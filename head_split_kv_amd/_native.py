@@ -17,6 +17,7 @@ EXPORTS = (
     "duo_layout_query", "duo_cache_create", "duo_cache_init", "duo_cache_reset",
     "duo_cache_set_lengths", "duo_cache_destroy",
     "duo_kv_append", "duo_attn_decode", "duo_decode_step", "duo_attn_prefill",
+    "duo_attn_gate_mixed",
     "duo_slot_positions",
     "duo_cache_lengths", "duo_kv_bytes", "duo_set_decode_splits", "duo_timing_enable",
     "duo_timing_read", "duo_binarize_gates", "duo_head_order", "duo_permute_blocks",
@@ -86,6 +87,7 @@ def lib() -> ctypes.CDLL:
         "duo_attn_decode": (st, [vp, i32, vp, vp, vp, vp]),
         "duo_decode_step": (st, [vp, i32, vp, vp, vp, vp, vp, vp]),
         "duo_attn_prefill": (st, [vp, i32, i32, vp, vp, vp, i32, vp, vp, vp]),
+        "duo_attn_gate_mixed": (st, [vp, i32, i32, vp, vp, vp, i32, P(ctypes.c_float), vp, vp]),
         "duo_slot_positions": (st, [vp, i32, P(i32), vp]),
         "duo_cache_lengths": (st, [vp, P(i32)]),
         "duo_kv_bytes": (st, [P(DuoConfig), P(i32), i32, P(ctypes.c_uint64),

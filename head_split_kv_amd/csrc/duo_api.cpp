@@ -243,12 +243,12 @@ duo_status duo_decode_step(duo_cache* c, int32_t layer, const void* q, const voi
   return decode_impl(c, layer, q, k, v, out, lse, stream);
 }
 
-duo_status duo_attn_prefill(duo_cache* c, int32_t layer, int32_t seq, const void* q,
-                            const void* k, const void* v, int32_t n_chunk, void* out,
-                            float* lse, void* stream) {
-  if (!layer_ok(c, layer) || seq < -1 || seq >= c->cfg.batch || n_chunk < 0)
-    return DUO_ERR_INVALID;
-  if (n_chunk == 0) return DUO_OK;
+namespace {
+
+// Checks and launch arguments of one prefill chunk (shared by duo_attn_prefill and
+// duo_attn_gate_mixed). Returns DUO_OK with `a` filled, or the error to report.
+duo_status prefill_args(duo_cache* c, int32_t layer, int32_t seq, const void* q, const void* k,
+                        const void* v, int32_t n_chunk, void* out, float* lse, PrefillArgs& a) {
   if (!q || !k || !v || !out || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
       !aligned16(out) || !aligned4(lse))
     return DUO_ERR_INVALID;
@@ -257,7 +257,6 @@ duo_status duo_attn_prefill(duo_cache* c, int32_t layer, int32_t seq, const void
     if ((int64_t)len_of(c, layer, b) + n_chunk > c->cfg.capacity) return DUO_ERR_CAPACITY;
   const LayerInfo& li = c->layers[layer];
   const LayerPtrs p = layer_ptrs(c, layer);
-  PrefillArgs a;
   std::memset(&a, 0, sizeof(a));
   a.q = q;
   a.k = k;
@@ -303,12 +302,59 @@ duo_status duo_attn_prefill(duo_cache* c, int32_t layer, int32_t seq, const void
   a.part_o = (float*)ws;
   a.part_ml = (float*)(ws + ((uint64_t)c->cfg.prefill_tiles * kPrefillTileRows * D * 4 + kAlign - 1) /
                                 kAlign * kAlign);
+  a.full_heads = li.n_ret;
   if (c->cfg.dtype != DUO_BF16) return DUO_ERR_UNSUPPORTED;
-  const int rc = launch_prefill(a, c->cfg.dtype, c->cfg.head_dim, group, stream,
-                                next_marks(c, DUO_TIMING_PREFILL));
-  if (rc == -1) return DUO_ERR_UNSUPPORTED;
-  if (rc != 0) return DUO_ERR_HIP;
   return DUO_OK;
+}
+
+duo_status launch_status(int rc) {
+  if (rc == -1) return DUO_ERR_UNSUPPORTED;
+  return rc != 0 ? DUO_ERR_HIP : DUO_OK;
+}
+
+}  // namespace
+
+duo_status duo_attn_prefill(duo_cache* c, int32_t layer, int32_t seq, const void* q,
+                            const void* k, const void* v, int32_t n_chunk, void* out,
+                            float* lse, void* stream) {
+  if (!layer_ok(c, layer) || seq < -1 || seq >= c->cfg.batch || n_chunk < 0)
+    return DUO_ERR_INVALID;
+  if (n_chunk == 0) return DUO_OK;
+  PrefillArgs a;
+  const duo_status st = prefill_args(c, layer, seq, q, k, v, n_chunk, out, lse, a);
+  if (st != DUO_OK) return st;
+  const int group = c->cfg.num_q_heads / c->cfg.num_kv_heads;
+  return launch_status(launch_prefill(a, c->cfg.dtype, c->cfg.head_dim, group, stream,
+                                      next_marks(c, DUO_TIMING_PREFILL)));
+}
+
+duo_status duo_attn_gate_mixed(duo_cache* c, int32_t layer, int32_t seq, const void* q,
+                               const void* k, const void* v, int32_t n_chunk,
+                               const float* alpha, void* out, void* stream) {
+  if (!layer_ok(c, layer) || seq < -1 || seq >= c->cfg.batch || n_chunk < 0 || !alpha)
+    return DUO_ERR_INVALID;
+  const LayerInfo& li = c->layers[layer];
+  if (li.n_ret != c->cfg.num_kv_heads) return DUO_ERR_INVALID;  // every head needs a full cache
+  for (int32_t j = 0; j < c->cfg.num_kv_heads; ++j)
+    if (!(alpha[j] >= 0.f && alpha[j] <= 1.f)) return DUO_ERR_INVALID;
+  if (n_chunk == 0) return DUO_OK;
+  PrefillArgs a;
+  duo_status st = prefill_args(c, layer, seq, q, k, v, n_chunk, out, nullptr, a);
+  if (st != DUO_OK) return st;
+  const int group = c->cfg.num_q_heads / c->cfg.num_kv_heads;
+  // full attention of every head into out (the layer is all retrieval heads)
+  a.chunk_mode = 0;
+  st = launch_status(launch_prefill(a, c->cfg.dtype, c->cfg.head_dim, group, stream, {}));
+  if (st != DUO_OK) return st;
+  // sink + recent attention of every head over the same full caches, blended into out
+  PrefillArgs s = a;
+  s.Hr = 0;
+  s.Hs = c->cfg.num_kv_heads;
+  for (int32_t j = 0; j < s.Hs; ++j) s.str_kv[j] = (uint8_t)j;
+  s.nsplit = 1;
+  s.mixed = 1;
+  for (int32_t j = 0; j < s.Hs; ++j) s.alpha[j] = alpha[j];
+  return launch_status(launch_prefill(s, c->cfg.dtype, c->cfg.head_dim, group, stream, {}));
 }
 
 duo_status duo_timing_enable(duo_cache* c, int32_t max_records) {

@@ -105,6 +105,11 @@ struct PrefillArgs {
   float scale_log2;
   int32_t out_f32;
   int32_t chunk_mode;       // streaming heads see the whole cache plus the chunk causally
+  // Gate-mixed pass (its own kernel variant): streaming blocks read the full caches under
+  // the sink + recent window and write alpha[j] * out + (1 - alpha[j]) * result.
+  int32_t mixed;
+  int32_t full_heads;       // full caches per sequence of this layer
+  float alpha[kMaxKvHeads];
   int16_t cls_idx[kMaxKvHeads];
   uint8_t ret_kv[kMaxKvHeads];
   uint8_t str_kv[kMaxKvHeads];

@@ -96,7 +96,9 @@ __device__ __forceinline__ int swz(int r) {
 __device__ __forceinline__ float max_pair32(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
 __device__ __forceinline__ float sum_pair32(float x) { return x + __shfl_xor(x, 32); }
 
-template <int D, int G>
+// kMix: the streaming pass of gate-mixed attention (full-cache source, blended output); a
+// separate instantiation so that the ordinary kernel carries none of it.
+template <int D, int G, bool kMix>
 __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
   using Gm = Geo<D>;
   constexpr int NCH = Gm::kChunks;
@@ -139,6 +141,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
   const bool retrieval = blockIdx.x < (unsigned)n_ret_blocks;
   // every held key is visible (retrieval, or a streaming head in chunk mode): causal only
   const bool causal_only = retrieval || a.chunk_mode != 0;
+  // the cache part is a full cache, row r holding position r (otherwise the ring)
+  const bool full_src = retrieval || kMix;
   const int b = a.b0 + bi;
   const int c0 = a.c0[bi];
   const int S = a.S, R = a.R, SR = a.S + a.R;
@@ -167,13 +171,15 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
   }
 
   // ---- key tiles: cache part, then chunk part ------------------------------------------
-  const int filled = retrieval ? c0 : min(c0, SR);  // cache rows holding a token
+  const int filled = full_src ? c0 : min(c0, SR);  // cache rows holding a token
   int n_cache_tiles;
   const char* cache_k;
   const char* cache_v;
-  if (retrieval) {
+  if (full_src) {
     n_cache_tiles = (c0 + kBN - 1) / kBN;
-    const int64_t base = ((int64_t)b * a.Hr + cls) * a.cap * RB;
+    const int64_t base = (kMix && !retrieval)
+                             ? ((int64_t)b * a.full_heads + a.cls_idx[j]) * a.cap * RB
+                             : ((int64_t)b * a.Hr + cls) * a.cap * RB;
     cache_k = (const char*)a.full_k + base;
     cache_v = (const char*)a.full_v + base;
   } else {
@@ -195,6 +201,10 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
     if (ti < n_cache_tiles) {
       if (ti * kBN >= filled) return -1;  // empty slots only
       if (causal_only) return (ti + 1) * kBN <= filled ? 0 : 1;
+      if (kMix) {  // window over full-cache rows: skip rows left of every window
+        const int k1 = min(filled, (ti + 1) * kBN) - 1;
+        return (ti * kBN >= S && k1 < p_min - R + 1) ? -1 : 1;
+      }
       // streaming cache: once every window starts past the cache only sink slots count
       if (ti * kBN >= S && p_min - R + 1 > c0 - 1) return -1;
       return 1;
@@ -216,12 +226,12 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
   // largest t <= c0 - 1 with t = idx (mod R) (the ring's slot map, inverted).
   // With bm = (c0 - 1 - S) mod R (once per block), (c0 - 1 - idx) mod R = bm - (idx - S),
   // plus R when negative, for a ring slot idx in [S, S + R).
-  const int ring_bm = (!retrieval && c0 > S) ? (c0 - 1 - S) % R : 0;
+  const int ring_bm = (!full_src && c0 > S) ? (c0 - 1 - S) % R : 0;
   auto key_pos = [&](int ti, int r) -> int {
     if (ti < n_cache_tiles) {
       const int idx = ti * kBN + r;
       if (idx >= filled) return kNoPos;
-      if (retrieval || idx < S) return idx;
+      if (full_src || idx < S) return idx;
       int back = ring_bm - (idx - S);
       back += back < 0 ? R : 0;
       return c0 - 1 - back;
@@ -451,13 +461,33 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
   if (!q_valid) return;
   const float inv = 1.f / lt;
   const int64_t orow = ((int64_t)bi * a.m + q_local) * a.Hq + j * G + g;
+  // gate-mixed output: out (already holding the full-attention result) keeps weight alpha
+  const float keep = kMix ? a.alpha[j] : 0.f;
+  const float mine = 1.f - keep;
 #pragma unroll
   for (int db = 0; db < Gm::kDBlocks; ++db)
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4) {
       const int d = db * 32 + 8 * a4 + 4 * half;
-      const float v0 = o[db][4 * a4] * inv, v1 = o[db][4 * a4 + 1] * inv;
-      const float v2 = o[db][4 * a4 + 2] * inv, v3 = o[db][4 * a4 + 3] * inv;
+      float v0 = o[db][4 * a4] * inv, v1 = o[db][4 * a4 + 1] * inv;
+      float v2 = o[db][4 * a4 + 2] * inv, v3 = o[db][4 * a4 + 3] * inv;
+      if constexpr (kMix) {
+        float p0, p1, p2, p3;
+        if (a.out_f32) {
+          const float4 pv = *(const float4*)((const float*)a.out + orow * D + d);
+          p0 = pv.x, p1 = pv.y, p2 = pv.z, p3 = pv.w;
+        } else {
+          const uint2 pw = *(const uint2*)((const uint16_t*)a.out + orow * D + d);
+          p0 = __builtin_bit_cast(float, pw.x << 16);
+          p1 = __builtin_bit_cast(float, pw.x & 0xFFFF0000u);
+          p2 = __builtin_bit_cast(float, pw.y << 16);
+          p3 = __builtin_bit_cast(float, pw.y & 0xFFFF0000u);
+        }
+        v0 = __builtin_fmaf(keep, p0, mine * v0);
+        v1 = __builtin_fmaf(keep, p1, mine * v1);
+        v2 = __builtin_fmaf(keep, p2, mine * v2);
+        v3 = __builtin_fmaf(keep, p3, mine * v3);
+      }
       if (a.out_f32) {
         *(float4*)((float*)a.out + orow * D + d) = float4{v0, v1, v2, v3};
       } else {
@@ -535,7 +565,7 @@ struct Variant {
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&prefill_kernel<D, G>), kThreads, 0) !=
+            &per_cu, reinterpret_cast<const void*>(&prefill_kernel<D, G, false>), kThreads, 0) !=
             hipSuccess ||
         cus <= 0 || per_cu <= 0) {
       (void)hipGetLastError();
@@ -547,8 +577,12 @@ struct Variant {
   static int launch(const PrefillArgs& a, void* stream, const KernelMarks& marks) {
     const int64_t blocks = (int64_t)a.nb * a.n_qt * ((int64_t)a.Hr * a.nsplit + a.Hs);
     if (marks.begin) (void)hipEventRecord((hipEvent_t)marks.begin, (hipStream_t)stream);
-    hipLaunchKernelGGL((prefill_kernel<D, G>), dim3((unsigned)blocks), dim3(kThreads), 0,
-                       (hipStream_t)stream, a);
+    if (a.mixed)
+      hipLaunchKernelGGL((prefill_kernel<D, G, true>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                         (hipStream_t)stream, a);
+    else
+      hipLaunchKernelGGL((prefill_kernel<D, G, false>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                         (hipStream_t)stream, a);
     if (marks.end) (void)hipEventRecord((hipEvent_t)marks.end, (hipStream_t)stream);
     if (a.nsplit > 1 && a.Hr > 0) {
       const int64_t mblocks = (int64_t)a.nb * a.Hr * a.n_qt * (kRows / kMergeRows);

@@ -170,6 +170,22 @@ duo_status duo_attn_prefill(duo_cache* cache, int32_t layer, int32_t seq, const 
                             const void* k, const void* v, int32_t n_chunk, void* out,
                             float* lse, void* stream);
 
+/* Gate-mixed attention of one chunk, the attention of the retrieval-head identification phase
+ * (explainer, "Gate Parameterization"): every query head h of KV head j = h / G returns
+ * alpha[j] * full_attn + (1 - alpha[j]) * streaming_attn, where full_attn is softmax attention
+ * over the t <= p (full cache rows 0..c-1, then the chunk) and streaming_attn the same over the
+ * t <= p with t < S or t >= p - R + 1 (explainer, "The Full and Streaming Attention Masks").
+ * The two outputs are normalized separately, then blended. Every KV head of `layer` must be a
+ * retrieval head (each keeps its full history); alpha: host float [num_kv_heads] in [0, 1].
+ * q, k, v, out and the chunk positions as in duo_attn_prefill (no lse); the cache is not
+ * modified. Runs as two launches on `stream`: full attention into out, then the windowed
+ * attention blended into it (with a bf16 out the full result is rounded once before the blend).
+ * DUO_ERR_INVALID for a layer with streaming heads, a gate outside [0, 1] or the argument
+ * errors of duo_attn_prefill; DUO_ERR_CAPACITY as there. */
+duo_status duo_attn_gate_mixed(duo_cache* cache, int32_t layer, int32_t seq, const void* q,
+                               const void* k, const void* v, int32_t n_chunk,
+                               const float* alpha, void* out, void* stream);
+
 /* Copy the slot table of one layer, int32 [B][S+R], to host memory. Synchronizes `stream`. */
 duo_status duo_slot_positions(duo_cache* cache, int32_t layer, int32_t* host_out,
                               void* stream);
