@@ -357,3 +357,70 @@ def reorder_input_cols(w, order, cols_per_head: int) -> np.ndarray:
     w = np.asarray(w)
     return np.concatenate([w[:, h * cols_per_head:(h + 1) * cols_per_head] for h in order],
                           axis=1)
+
+
+# --------------------------------------------------------------------------------------------
+# 4-bit retrieval caches
+# --------------------------------------------------------------------------------------------
+#
+# Explainer, "Combination with Quantization" and the OpenReview reply on KV quantization:
+# DuoAttention's full caches combine with 4-bit KV quantization (per-channel, as in KIVI).
+# The pages fix the bit width only. Readings taken here, each a plain choice:
+#   * asymmetric 4-bit codes 0..15 with a float32 scale and zero point (zero = the minimum);
+#   * keys per channel over aligned groups of KV4_GROUP tokens (positions g*64 .. g*64+63),
+#     values per token over the channels;
+#   * the tokens of the last, incomplete group are kept exactly (bf16) until it completes;
+#   * the code decision is taken in float32: c = rint((x - zero) / scale) clamped to 0..15,
+#     with scale = (max - min) / 15 and c = 0 when scale is 0 (IEEE float32 division,
+#     round half to even), so that any float32 implementation takes the same decision;
+#   * a stored token reads back as c * scale + zero.
+
+KV4_GROUP = 64
+
+
+def kv4_codes(x, axis: int):
+    """4-bit codes of a float32 block over ``axis`` (the reduction axis of min and max).
+    Returns ``(codes uint8, scale float32, zero float32)``, scale and zero reduced."""
+    x = np.asarray(x, dtype=np.float32)
+    mn = x.min(axis=axis, keepdims=True)
+    mx = x.max(axis=axis, keepdims=True)
+    scale = (mx - mn) / np.float32(15.0)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        c = np.rint((x - mn) / scale)
+    c = np.where(scale == 0, np.float32(0.0), c)
+    codes = np.clip(c, 0, 15).astype(np.uint8)
+    return codes, np.squeeze(scale, axis), np.squeeze(mn, axis)
+
+
+def kv4_history(x_hist, n: int, is_key: bool) -> np.ndarray:
+    """What a 4-bit full cache reads back for tokens 0..n-1 of one head, ``x_hist [>=n, d]``
+    (float64 of the stored values): complete groups dequantized (keys per channel over the
+    group, values per token), the incomplete last group exact."""
+    x = np.asarray(x_hist, dtype=np.float32)[:n]
+    out = x.astype(np.float64).copy()
+    full = (n // KV4_GROUP) * KV4_GROUP
+    for g0 in range(0, full, KV4_GROUP):
+        blk = x[g0:g0 + KV4_GROUP]
+        if is_key:
+            codes, scale, zero = kv4_codes(blk, axis=0)  # per channel: over the group's tokens
+            out[g0:g0 + KV4_GROUP] = (codes.astype(np.float64) * scale.astype(np.float64)[None, :]
+                                      + zero.astype(np.float64)[None, :])
+        else:
+            codes, scale, zero = kv4_codes(blk, axis=1)  # per token: over the channels
+            out[g0:g0 + KV4_GROUP] = (codes.astype(np.float64) * scale.astype(np.float64)[:, None]
+                                      + zero.astype(np.float64)[:, None])
+    return out
+
+
+def decode_step_kv4(q, k_hist, v_hist, retrieval, sink, recent, scale=None):
+    """``decode_step`` with the retrieval heads' full caches stored in 4 bits: every
+    retrieval KV head attends over ``kv4_history`` of its keys and values; streaming heads
+    (constant-size caches, kept exact) as before."""
+    k = np.asarray(k_hist, dtype=np.float64).copy()
+    v = np.asarray(v_hist, dtype=np.float64).copy()
+    n = k.shape[0]
+    for j in range(k.shape[1]):
+        if retrieval[j]:
+            k[:, j] = kv4_history(k_hist[:, j], n, True)
+            v[:, j] = kv4_history(v_hist[:, j], n, False)
+    return decode_step(q, k, v, retrieval, sink, recent, scale)

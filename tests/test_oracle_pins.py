@@ -518,6 +518,98 @@ def pin_gate_mixed_bruteforce():
                                        np.repeat(v[:S + R], G, axis=1)), atol=1e-12)
 
 
+def _bf16_grid(rng, *shape):
+    """float32 values that bf16 represents exactly."""
+    x = rng.standard_normal(shape).astype(np.float32)
+    return (x.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)
+
+
+def pin_kv4_nearest_level():
+    """Every code is the nearest of the 16 levels zero + c * scale (up to float32 rounding of
+    the quotient), the block's minimum and maximum take codes 0 and 15, and the error is at
+    most half a step; checked against a search over all 16 levels in float64."""
+    rng = np.random.default_rng(51)
+    for shape, axis in (((64, 16), 0), ((8, 128), 1), ((64, 3), 0)):
+        x = _bf16_grid(rng, *shape)
+        codes, scale, zero = O.kv4_codes(x, axis)
+        s = np.expand_dims(scale.astype(np.float64), axis)
+        z = np.expand_dims(zero.astype(np.float64), axis)
+        levels = z[..., None] + s[..., None] * np.arange(16)
+        dist = np.abs(x.astype(np.float64)[..., None] - levels)
+        best = dist.min(axis=-1)
+        got = np.take_along_axis(dist, codes[..., None].astype(np.int64), -1)[..., 0]
+        assert np.all(got <= best + 1e-6 * s), shape
+        assert np.all(got <= 0.5 * s * (1 + 1e-6)), shape
+        assert np.array_equal(np.take_along_axis(codes, np.expand_dims(x.argmin(axis), axis), axis),
+                              np.zeros_like(np.expand_dims(x.argmin(axis), axis), dtype=np.uint8))
+        assert np.all(np.take_along_axis(codes, np.expand_dims(x.argmax(axis), axis), axis) == 15)
+
+
+def pin_kv4_axes_and_exact_grids():
+    """Keys are quantized per channel (over tokens), values per token (over channels): a key
+    block whose every channel is constant, or a value block whose every token is constant,
+    reads back exactly; so does a block whose levels are 16 evenly spaced dyadic values from
+    min to max along the quantization axis."""
+    rng = np.random.default_rng(52)
+    G, d = O.KV4_GROUP, 16
+    kc = np.tile(_bf16_grid(rng, 1, d), (G, 1))          # channel-constant keys
+    vc = np.tile(_bf16_grid(rng, G, 1), (1, d))          # token-constant values
+    assert np.array_equal(O.kv4_history(kc, G, True), kc.astype(np.float64))
+    assert np.array_equal(O.kv4_history(vc, G, False), vc.astype(np.float64))
+    step = 2.0 ** rng.integers(-6, 0, size=d)
+    base = np.round(rng.standard_normal(d) * 8) / 8
+    kidx = np.stack([rng.permutation(np.resize(np.arange(16), G)) for _ in range(d)], axis=1)
+    kg = (base[None, :] + kidx * step[None, :]).astype(np.float32)
+    assert np.array_equal(O.kv4_history(kg, G, True), kg.astype(np.float64))
+    vidx = np.stack([rng.permutation(np.resize(np.arange(16), d)) for _ in range(G)], axis=0)
+    vg = (np.float32(-1.5) + vidx * 0.25).astype(np.float32)
+    assert np.array_equal(O.kv4_history(vg, G, False), vg.astype(np.float64))
+
+
+def pin_kv4_groups_and_residual():
+    """Groups are the aligned positions g*64 .. g*64+63: a group reads back the same whatever
+    the other groups hold; tokens after the last complete group (and every token of a
+    sequence shorter than one group) read back exactly."""
+    rng = np.random.default_rng(53)
+    G = O.KV4_GROUP
+    for is_key in (True, False):
+        x = _bf16_grid(rng, 3 * G + 17, 8)
+        h = O.kv4_history(x, x.shape[0], is_key)
+        assert np.array_equal(h[3 * G:], x[3 * G:].astype(np.float64))
+        assert not np.array_equal(h[:3 * G], x[:3 * G].astype(np.float64))
+        y = x.copy()
+        y[G:2 * G] = _bf16_grid(rng, G, 8)
+        hy = O.kv4_history(y, y.shape[0], is_key)
+        assert np.array_equal(hy[:G], h[:G]) and np.array_equal(hy[2 * G:], h[2 * G:])
+        for n in (1, G - 1):
+            assert np.array_equal(O.kv4_history(x, n, is_key), x[:n].astype(np.float64))
+        assert np.array_equal(O.kv4_history(x, 2 * G, is_key)[:G], h[:G])
+
+
+def pin_kv4_decode():
+    """Quantization touches retrieval heads only, and a history on the exact grids decodes
+    exactly as the unquantized one; on general data the output moves by no more than the
+    quantization error allows."""
+    rng = np.random.default_rng(54)
+    G = O.KV4_GROUP
+    n, Hkv, Gq, d, S, R = 2 * G + 5, 2, 2, 16, 2, 8
+    q = _bf16_grid(rng, Hkv * Gq, d)
+    k = _bf16_grid(rng, n, Hkv, d)
+    v = _bf16_grid(rng, n, Hkv, d)
+    a, _ = O.decode_step(q, k, v, [0, 0], S, R)
+    b, _ = O.decode_step_kv4(q, k, v, [0, 0], S, R)
+    assert np.array_equal(a, b)
+    a, _ = O.decode_step(q, k, v, [1, 0], S, R)
+    b, _ = O.decode_step_kv4(q, k, v, [1, 0], S, R)
+    assert np.array_equal(a[Gq:], b[Gq:]) and 0 < np.abs(a[:Gq] - b[:Gq]).max() < 0.5
+    # channel-constant keys and token-constant values are exact in 4 bits
+    k2 = np.repeat(_bf16_grid(rng, 1, Hkv, d), n, axis=0)
+    v2 = np.repeat(_bf16_grid(rng, n, Hkv, 1), d, axis=2)
+    a, _ = O.decode_step(q, k2, v2, [1, 1], S, R)
+    b, _ = O.decode_step_kv4(q, k2, v2, [1, 1], S, R)
+    assert np.allclose(a, b, rtol=0, atol=1e-12)
+
+
 PINS = [pin_cache_policy, pin_streaming_rows, pin_decode_scalar_bruteforce,
         pin_all_retrieval_is_causal_attention, pin_short_streaming_is_full,
         pin_no_sink_is_sliding_window, pin_fig5_worked_example, pin_memory_numbers,
@@ -525,7 +617,8 @@ PINS = [pin_cache_policy, pin_streaming_rows, pin_decode_scalar_bruteforce,
         pin_head_permutation, pin_gqa_equals_repeated_mha, pin_lambda_mask_literal,
         pin_chunk_granular_fig5, pin_chunk_granular_gather, pin_chunk_granular_short_is_full,
         pin_retrieval_count_nearest, pin_binarize_bruteforce, pin_binarize_equation4,
-        pin_head_reordering_preserves_layer, pin_gate_mixed_bruteforce]
+        pin_head_reordering_preserves_layer, pin_gate_mixed_bruteforce, pin_kv4_nearest_level,
+        pin_kv4_axes_and_exact_grids, pin_kv4_groups_and_residual, pin_kv4_decode]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -631,6 +724,42 @@ def _mixed_unnormalized(q, k, v, q_pos, k_pos, alpha, sink, recent, scale=None):
     return out
 
 
+def _kv4_codes_variant(floor=False, levels=15):
+    def f(x, axis):
+        x = np.asarray(x, dtype=np.float32)
+        mn = x.min(axis=axis, keepdims=True)
+        mx = x.max(axis=axis, keepdims=True)
+        scale = (mx - mn) / np.float32(levels)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            r = (x - mn) / scale
+            c = np.floor(r) if floor else np.rint(r)
+        c = np.where(scale == 0, np.float32(0.0), c)
+        return np.clip(c, 0, 15).astype(np.uint8), np.squeeze(scale, axis), np.squeeze(mn, axis)
+    return f
+
+
+def _kv4_history_variant(swap_axes=False, quantize_tail=False, misaligned=False):
+    def f(x_hist, n, is_key):
+        x = np.asarray(x_hist, dtype=np.float32)[:n]
+        out = x.astype(np.float64).copy()
+        G = O.KV4_GROUP
+        starts = list(range(0, (n // G) * G, G))
+        if misaligned:
+            starts = list(range(n % G, n - G + 1, G))
+        if quantize_tail and n % G:
+            starts.append((n // G) * G)
+        for g0 in starts:
+            blk = x[g0:g0 + G]
+            per_channel = is_key != swap_axes
+            codes, scale, zero = O.kv4_codes(blk, axis=0 if per_channel else 1)
+            if per_channel:
+                out[g0:g0 + len(blk)] = codes * scale.astype(np.float64)[None] + zero[None]
+            else:
+                out[g0:g0 + len(blk)] = codes * scale.astype(np.float64)[:, None] + zero[:, None]
+        return out
+    return f
+
+
 _ORIG_MSA = O.masked_softmax_attention
 _ORIG_BIN = O.binarize_gates
 _ORIG_MIX = O.gate_mixed_attention
@@ -662,6 +791,11 @@ MUTANTS = {
     "binarize_per_layer": ("binarize_gates", _binarize_per_layer),
     "head_order_streaming_first": ("head_order",
                                    lambda m: np.argsort(np.asarray(m) != 0, kind="stable")),
+    "kv4_floor": ("kv4_codes", _kv4_codes_variant(floor=True)),
+    "kv4_sixteen_steps": ("kv4_codes", _kv4_codes_variant(levels=16)),
+    "kv4_axes_swapped": ("kv4_history", _kv4_history_variant(swap_axes=True)),
+    "kv4_tail_quantized": ("kv4_history", _kv4_history_variant(quantize_tail=True)),
+    "kv4_groups_misaligned": ("kv4_history", _kv4_history_variant(misaligned=True)),
     "mixed_alpha_swapped": ("gate_mixed_attention",
                             lambda q, k, v, qp, kp, a, S, R, scale=None: _ORIG_MIX(
                                 q, k, v, qp, kp, 1 - np.asarray(a), S, R, scale)),
