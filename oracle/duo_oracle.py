@@ -367,15 +367,15 @@ def reorder_input_cols(w, order, cols_per_head: int) -> np.ndarray:
 # DuoAttention's full caches combine with 4-bit KV quantization (per-channel, as in KIVI).
 # The pages fix the bit width only. Readings taken here, each a plain choice:
 #   * asymmetric 4-bit codes 0..15 with a float32 scale and zero point (zero = the minimum);
-#   * keys per channel over aligned groups of KV4_GROUP tokens (positions g*64 .. g*64+63),
-#     values per token over the channels;
+#   * keys per channel over aligned groups of KV4_GROUP = 128 tokens (positions g*128 ..
+#     g*128+127), values per token over the channels;
 #   * the tokens of the last, incomplete group are kept exactly (bf16) until it completes;
 #   * the code decision is taken in float32: c = rint((x - zero) / scale) clamped to 0..15,
 #     with scale = (max - min) / 15 and c = 0 when scale is 0 (IEEE float32 division,
 #     round half to even), so that any float32 implementation takes the same decision;
 #   * a stored token reads back as c * scale + zero.
 
-KV4_GROUP = 64
+KV4_GROUP = 128
 
 
 def kv4_codes(x, axis: int):

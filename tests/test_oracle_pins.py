@@ -567,7 +567,7 @@ def pin_kv4_axes_and_exact_grids():
 
 
 def pin_kv4_groups_and_residual():
-    """Groups are the aligned positions g*64 .. g*64+63: a group reads back the same whatever
+    """Groups are the aligned positions g*128 .. g*128+127: a group reads back the same whatever
     the other groups hold; tokens after the last complete group (and every token of a
     sequence shorter than one group) read back exactly."""
     rng = np.random.default_rng(53)
