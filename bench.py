@@ -57,6 +57,7 @@ def parse():
                    help="prefill legs to time: window (per-query sink + recent mask), chunk "
                         "(chunk-granular streaming heads), mixed (gate-mixed attention)")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-kv4", action="store_true", help="skip the 4-bit full-cache decode leg")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--splits", type=int, default=0, help="force decode splits (0 = automatic)")
     p.add_argument("--unfused", action="store_true", help="time append + decode as two calls")
@@ -99,7 +100,7 @@ class Timer:
         return self.a.elapsed_time(self.b)
 
 
-def decode_leg(args, torch, hsk, W, N):
+def decode_leg(args, torch, hsk, W, N, kv_bits=0):
     w = W.workload(args.workload)
     L = args.layers
     # warm-up, the timed steps, then as many again timed one by one for the spread
@@ -111,7 +112,8 @@ def decode_leg(args, torch, hsk, W, N):
     cache = hsk.DuoCache(num_layers=L, batch=1, num_q_heads=w.hq, num_kv_heads=w.hkv,
                          head_dim=w.d, sink=w.sink, recent=w.recent, capacity=cap,
                          retrieval_mask=[mask] * L, dtype=torch.bfloat16,
-                         out_dtype=torch.bfloat16, device=dev, max_splits=1024)
+                         out_dtype=torch.bfloat16, device=dev, max_splits=1024,
+                         kv_bits=kv_bits)
     if args.splits:
         hsk.duo_set_decode_splits(cache, args.splits)
     t = time.time()
@@ -128,7 +130,8 @@ def decode_leg(args, torch, hsk, W, N):
     vs = torch.from_numpy(W.tokens(w, "v", 0, 0, n0, n0 + total_steps)).to(dev).to(torch.bfloat16)
     out = torch.empty((1, w.hq, w.d), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
-    log(f"decode leg: {w.name}, {L} replica layers filled to {n0} tokens in {time.time() - t:.1f}s")
+    log(f"decode leg{' (4-bit full caches)' if kv_bits == 4 else ''}: {w.name}, {L} replica "
+        f"layers filled to {n0} tokens in {time.time() - t:.1f}s")
 
     lib = N.lib()
     h = cache.handle
@@ -188,7 +191,7 @@ def decode_leg(args, torch, hsk, W, N):
     # 100 tokens longer, differs by less than 0.1 %)
     cfg1, _m = hsk.make_config(num_layers=1, batch=1, num_q_heads=w.hq, num_kv_heads=w.hkv,
                                head_dim=w.d, sink=w.sink, recent=w.recent, capacity=cap,
-                               retrieval_mask=[mask])
+                               retrieval_mask=[mask], kv_bits=kv_bits)
     kv_bytes = []
     for s in range(args.warmup, args.warmup + args.steps):
         kv_bytes.append(hsk.duo_kv_bytes(cfg1, [n0 + s + 1], 0)[1])
@@ -495,6 +498,13 @@ def main():
     log(f"decode: {dec['us_layer']:.2f} us/layer-step, {dec['gbs']:.0f} GB/s; split kernel "
         f"{dec['kern_us']:.2f} us = {dec['kern_gbs']:.0f} GB/s ({dec['kern_n']} launches timed); "
         f"one duo_attn_decode call {dec['dec_us']:.2f} us = {dec['dec_gbs']:.0f} GB/s")
+    dec4 = None
+    if not args.no_kv4:
+        dec4 = decode_leg(args, torch, hsk, W, N, kv_bits=4)
+        log(f"decode, 4-bit full caches: {dec4['us_layer']:.2f} us/layer-step "
+            f"({dec['us_layer'] / dec4['us_layer']:.2f}x the bf16 step), {dec4['gbs']:.0f} GB/s of "
+            f"stored bytes; split kernel {dec4['kern_us']:.2f} us = {dec4['kern_gbs']:.0f} GB/s; "
+            f"one duo_attn_decode call {dec4['dec_us']:.2f} us")
     modes = set(args.prefill_modes.split(","))
     pre = None
     if not args.no_prefill and "window" in modes:
@@ -569,6 +579,20 @@ def main():
             "algorithmic_bytes_per_launch": int(dec["step_bytes"]),
         },
         "hbm_copy_probe_GBps": round(probe, 1),
+        "decode_kv4": None if dec4 is None else {
+            "workload": "the same 128K GQA decode with 4-bit full caches (keys per channel over "
+                        "128-token groups, values per token, bf16 residual group)",
+            "us_per_layer_step": round(dec4["us_layer"], 3),
+            "speedup_vs_bf16_step": round(dec["us_layer"] / dec4["us_layer"], 3),
+            "GBps": round(dec4["gbs"], 1),
+            "stored_bytes_per_layer_step": int(dec4["step_bytes"]),
+            "decode_call_us": round(dec4["dec_us"], 3),
+            "roofline": {"bound": "hbm", "achieved": round(dec4["kern_gbs"], 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(dec4["kern_gbs"] / HBM_PEAK_GBS, 4),
+                         "kernel": "decode_q4_kernel<d128, G4> (split attention kernel)",
+                         "kernel_us": round(dec4["kern_us"], 3)},
+        },
         "gate_mixed": None if mix is None else {
             "workload": "identification-phase attention: Llama-2-7B-shaped MHA layer, one "
                         "32,768-token sequence processed whole, every head blending causal and "

@@ -35,12 +35,13 @@ def make_config(*, num_layers: int, batch: int, num_q_heads: int, num_kv_heads: 
                 head_dim: int, sink: int, recent: int, capacity: int,
                 retrieval_mask, dtype: torch.dtype = torch.bfloat16,
                 out_dtype: Optional[torch.dtype] = None, softmax_scale: float = 0.0,
-                max_splits: int = 0, prefill_tiles: int = 0, streaming_prefill: str = "window"):
+                max_splits: int = 0, prefill_tiles: int = 0, streaming_prefill: str = "window",
+                kv_bits: int = 0):
     """Build a ``DuoConfig``; returns ``(cfg, mask_array)`` (keep the array alive).
 
     ``streaming_prefill`` is ``"window"`` (streaming heads use the per-query sink + recent
     mask during pre-filling) or ``"chunk"`` (they see the whole pruned cache before the chunk
-    plus the chunk causally)."""
+    plus the chunk causally). ``kv_bits=4`` stores the full (retrieval) caches in 4 bits."""
     if streaming_prefill not in _PREFILL_MODES:
         raise ValueError(f"streaming_prefill must be 'window' or 'chunk', not {streaming_prefill!r}")
     mask = np.ascontiguousarray(np.asarray(retrieval_mask, dtype=np.uint8)
@@ -49,7 +50,7 @@ def make_config(*, num_layers: int, batch: int, num_q_heads: int, num_kv_heads: 
                     capacity, _dt(dtype), _dt(out_dtype or dtype), float(softmax_scale),
                     max_splits, prefill_tiles,
                     mask.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
-                    _PREFILL_MODES[streaming_prefill])
+                    _PREFILL_MODES[streaming_prefill], int(kv_bits))
     return cfg, mask
 
 
@@ -83,14 +84,16 @@ class DuoCache:
                  head_dim: int, sink: int, recent: int, capacity: int, retrieval_mask,
                  dtype: torch.dtype = torch.bfloat16, out_dtype: Optional[torch.dtype] = None,
                  softmax_scale: float = 0.0, max_splits: int = 0, prefill_tiles: int = 0,
-                 streaming_prefill: str = "window", device="cuda", stream=None):
+                 streaming_prefill: str = "window", kv_bits: int = 0, device="cuda",
+                 stream=None):
         self.cfg, self._mask = make_config(
             num_layers=num_layers, batch=batch, num_q_heads=num_q_heads,
             num_kv_heads=num_kv_heads, head_dim=head_dim, sink=sink, recent=recent,
             capacity=capacity, retrieval_mask=retrieval_mask, dtype=dtype, out_dtype=out_dtype,
             softmax_scale=softmax_scale, max_splits=max_splits, prefill_tiles=prefill_tiles,
-            streaming_prefill=streaming_prefill)
+            streaming_prefill=streaming_prefill, kv_bits=kv_bits)
         self.streaming_prefill = streaming_prefill
+        self.kv_bits = kv_bits
         self.layout = duo_layout_query(self.cfg)
         self.dtype = dtype
         self.out_dtype = out_dtype or dtype

@@ -25,6 +25,7 @@ EXPORTS = (
 )
 TIMING_DECODE, TIMING_PREFILL = 0, 1
 PREFILL_WINDOW, PREFILL_CHUNK = 0, 1
+KV4_GROUP = 128
 
 
 class DuoConfig(ctypes.Structure):
@@ -44,6 +45,7 @@ class DuoConfig(ctypes.Structure):
         ("prefill_tiles", ctypes.c_int32),
         ("retrieval_mask", ctypes.POINTER(ctypes.c_uint8)),
         ("streaming_prefill", ctypes.c_int32),
+        ("kv_bits", ctypes.c_int32),
     ]
 
 

@@ -17,7 +17,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libduo.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["cache_kernels.hip", "decode.hip", "prefill.hip", "reorder.hip"]
+HIP_SOURCES = ["cache_kernels.hip", "decode.hip", "prefill.hip", "reorder.hip", "kv4.hip"]
 CXX_SOURCES = ["duo_host.cpp", "duo_api.cpp", "preprocess.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

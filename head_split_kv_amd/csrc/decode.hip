@@ -435,6 +435,468 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
   }
 }
 
+// ---- 4-bit full caches -------------------------------------------------------------------
+// Complete groups of kQ4Group tokens of a retrieval head hold 4-bit codes, and both products
+// of a group run on MFMA (v_mfma_f32_16x16x32_f16): the logits S = Q' K^T of the G query heads
+// (rows, padded to 16) against 16 tokens, and O^T += V^T P'^T over 32 tokens for 16 channels.
+// Keys share per-channel (scale s_c, zero z_c) in a group, so S = sum_c (q_c s_c) k_c +
+// sum_c q_c z_c: the scales are folded into the query operand once per group and the zero
+// term is a per-row bias. Values carry per-token (s_t, z_t): O = sum_t (p_t s_t) v_t +
+// sum_t p_t z_t, the scales folded into the weights and the zero term one sum per row.
+// Codes become fp16 operands with no conversion: masked in place, a code c reads as the fp16
+// denormal c 2^-24 (or 16 c 2^-24 for a high nibble), exact and taken as such by the matrix
+// unit; the partner operand carries 1/16 where the nibble was high and the products are
+// scaled back by 2^24 (also exact). Masking takes the elements of a word in the order
+// 0, 4, 1, 5, 2, 6, 3, 7, which the partner operand follows. A wave streams whole groups in
+// steps of 32 tokens with the next step's codes and the next group's key parameters in
+// flight. Codes are stored in operand order (layout in duo.h): the KC key words of one token
+// that a lane needs are contiguous, and so are the D / 16 value words of one channel residue
+// and step, so every load moves whole lines. The incomplete last group (bf16
+// residual rows) and the streaming heads take the bf16 path over the 4 waves of one block.
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Eight codes (byte i: element 2i in the low nibble, 2i + 1 in the high one) as fp16
+// denormals: operand slot e holds element kCodeOrder[e] times 2^-24, times 16 in the slots
+// where kCodeHigh is set.
+constexpr int kCodeOrder[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+constexpr bool kCodeHigh[8] = {false, false, true, true, false, false, true, true};
+// slot of element x: 2 (x mod 4) + x / 4, the inverse of kCodeOrder
+constexpr float kTwo24 = 16777216.f;
+__device__ __forceinline__ half8_t codes_to_f16(uint32_t w) {
+  const uint32_t w8 = w >> 8;
+  const u32x4_t r = {w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu, w8 & 0x00F000F0u};
+  return __builtin_bit_cast(half8_t, r);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+  return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+
+// Maximum over each aligned group of 16 lanes (DPP, like group_sum<16>).
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp<0xB1>(x));
+  x = fmaxf(x, dpp<0x4E>(x));
+  x = fmaxf(x, dpp<0x141>(x));
+  x = fmaxf(x, dpp<0x128>(x));
+  return x;
+}
+
+// Order this wave's LDS writes before its following LDS reads (no other wave is involved).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int D, int G, int LPT, int NS>
+__global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
+  using T = uint16_t;
+  using Geo = RowGeom<T, D, LPT>;
+  using F = Frag<T, D, LPT>;
+  constexpr int kCpl = Geo::kCpl;
+  constexpr int kTpw = 64 / LPT;
+  constexpr int kTpb = kWaves * kTpw;
+  constexpr int RB = D * 2;
+  constexpr int CBY = D / 2;   // code bytes of one key token row
+  constexpr int KC = D / 32;   // 32-channel k-chunks of the logit product
+  constexpr int CBK = D / 16;  // 16-channel blocks of the value product
+  constexpr int kStep = 32;    // tokens per wave step
+  constexpr int kSteps = kQ4Group / kStep;
+  static_assert(G <= 16 && kSteps % 2 == 0, "query rows must fit the 16-row tile");
+
+  __shared__ float s_o[2 * kWaves][G][D];  // partials: bf16 path per wave, then MFMA path
+  __shared__ float s_m[2 * kWaves][G];
+  __shared__ float s_l[2 * kWaves][G];
+  __shared__ __attribute__((aligned(16))) uint16_t s_q[G][D];
+  __shared__ __attribute__((aligned(16))) _Float16 s_p[kWaves][16][kStep];  // P'^T per wave
+  __shared__ float s_x[kWaves][16];  // per-row scalars moved from the S to the O^T layout
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, grp = lane / LPT, sub = lane % LPT;
+  const int col = lane & 15;              // MFMA column: token of S, query of O^T
+  const int srow0 = 4 * (lane >> 4);      // first S row (query) held by this lane
+
+  // ---- work item -------------------------------------------------------------------------
+  const int64_t n_ret_items = (int64_t)a.B * a.Hr * a.nsplit;
+  const bool ret = (int64_t)blockIdx.x < n_ret_items;
+  int b, j, split, nsplit, n;
+  const char* kq = nullptr;  // retrieval head: K region (codes, parameters, residual)
+  const char* vq = nullptr;
+  const char* kbase;         // bf16 rows: the residual group, or the streaming slots
+  const char* vbase;
+  if (ret) {
+    const int64_t i = blockIdx.x;
+    split = (int)(i % a.nsplit);
+    const int cls = (int)((i / a.nsplit) % a.Hr);
+    b = (int)(i / ((int64_t)a.nsplit * a.Hr));
+    j = a.ret_kv[cls];
+    nsplit = a.nsplit;
+    n = a.n[b];
+    const int64_t head = ((int64_t)b * a.Hr + cls) * a.q4_stride;
+    kq = (const char*)a.full_k + head;
+    vq = (const char*)a.full_v + head;
+    kbase = kq + a.q4_resid;
+    vbase = vq + a.q4_resid;
+  } else {
+    const int64_t i = blockIdx.x - n_ret_items;
+    const int cls = (int)(i % a.Hs);
+    b = (int)(i / a.Hs);
+    j = a.str_kv[cls];
+    split = 0;
+    nsplit = 1;
+    const int SR = a.S + a.R;
+    n = min(a.n[b], SR);
+    const int64_t row0 = ((int64_t)b * a.Hs + cls) * SR;
+    kbase = (const char*)a.str_k + row0 * RB;
+    vbase = (const char*)a.str_v + row0 * RB;
+  }
+  const int h0 = j * G;
+  {
+    const uint32_t* qw = (const uint32_t*)((const char*)a.q + ((int64_t)b * a.Hq + h0) * RB);
+    for (int w = tid; w < G * D / 2; w += kThreads) reinterpret_cast<uint32_t*>(&s_q[0][0])[w] = qw[w];
+  }
+  __syncthreads();
+  const float c2 = a.scale_log2;
+  const float inv_c2 = 1.f / c2;
+
+  // ---- quantized groups on MFMA ------------------------------------------------------------
+  // S-layout state of rows srow0 + i: running maximum (log2 units), its raw-dot threshold,
+  // weight sum and value-zero sum. Rows past G never move their maximum (threshold +inf)
+  // and weigh exp2(x - 1e30) = 0.
+  float mq[4], thq[4], lq[4], zq[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool live = srow0 + i < G;
+    mq[i] = live ? kMInit : 1e30f;
+    thq[i] = live ? kMInit : __builtin_inff();
+    lq[i] = zq[i] = 0.f;
+  }
+  const float c2s = c2 * kTwo24;          // logit (log2 units) per unit of the raw product
+  const float inv_c2s = 1.f / c2s;
+  f32x4_t oacc[CBK];  // O^T: lane holds channels 16 cb + srow0 + i of query col
+#pragma unroll
+  for (int cb = 0; cb < CBK; ++cb) oacc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int ng = ret ? n / kQ4Group : 0;
+  const int n_split = ng > split ? (ng - 1 - split) / nsplit + 1 : 0;  // groups of the split
+  const int n_wave = n_split > wave ? (n_split - 1 - wave) / kWaves + 1 : 0;
+  if (n_wave > 0) {
+    auto group_of = [&](int i) {
+      return split + nsplit * (wave + kWaves * (i < n_wave ? i : n_wave - 1));
+    };
+    const float* kpar = (const float*)(kq + a.q4_params);    // [group][2][D]
+    const float2* vpar = (const float2*)(vq + a.q4_params);  // [token]
+    // key scale and zero of this lane's A-operand channels 32 kc + 8 (lane / 16) + e
+    float4 ps[KC][2], pz[KC][2];
+    auto load_params = [&](int gi) {
+      const float* p = kpar + (int64_t)group_of(gi) * 2 * D;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const int ch = 32 * kc + 8 * (lane >> 4);
+        ps[kc][0] = *(const float4*)(p + ch);
+        ps[kc][1] = *(const float4*)(p + ch + 4);
+        pz[kc][0] = *(const float4*)(p + D + ch);
+        pz[kc][1] = *(const float4*)(p + D + ch + 4);
+      }
+    };
+    half8_t qa[KC];
+    f32x4_t bias4;
+    auto fold = [&]() {
+      float bp = 0.f;  // this lane's part of row col's bias
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const float sv[8] = {ps[kc][0].x, ps[kc][0].y, ps[kc][0].z, ps[kc][0].w,
+                             ps[kc][1].x, ps[kc][1].y, ps[kc][1].z, ps[kc][1].w};
+        const float zv[8] = {pz[kc][0].x, pz[kc][0].y, pz[kc][0].z, pz[kc][0].w,
+                             pz[kc][1].x, pz[kc][1].y, pz[kc][1].z, pz[kc][1].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int x = kCodeOrder[e];  // channel 32 kc + 8 (lane / 16) + x in operand slot e
+          const int ch = 32 * kc + 8 * (lane >> 4) + x;
+          const float qf = col < G ? bf16_bits_to_f32(s_q[col < G ? col : 0][ch]) : 0.f;
+          qa[kc][e] = (_Float16)(qf * sv[x] * (kCodeHigh[e] ? 0.0625f : 1.f));
+          bp = __builtin_fmaf(qf, zv[x], bp);
+        }
+      }
+      bp += __shfl_xor(bp, 16);
+      bp += __shfl_xor(bp, 32);
+      // the product accumulates in units of 2^-24: the bias enters in the same units
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bias4[i] = __shfl(bp, srow0 + i) * (1.f / kTwo24);
+    };
+    struct Ld {
+      uint32_t k[2][KC];  // key code words of the two 16-token tiles
+      uint32_t v[CBK];    // value code words of the channel blocks
+      float2 vp[2];       // value scale and zero of token col of each tile
+    };
+    auto load_step = [&](Ld& f, int gi, int st) {
+      const int gg = group_of(gi);
+      const int64_t t0 = (int64_t)gg * kQ4Group + st * kStep;
+      const int j = lane >> 4;
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+        // token t0 + 16 tau + col: words KC j .. KC j + KC - 1 of its row
+        const char* kr = kq + (t0 + 16 * tau + col) * CBY + j * KC * 4;
+        if constexpr (KC == 4) {
+          const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kr));
+          f.k[tau][0] = x.x; f.k[tau][1] = x.y; f.k[tau][2] = x.z; f.k[tau][3] = x.w;
+        } else {
+          const u32x2_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(kr));
+          f.k[tau][0] = x.x; f.k[tau][1] = x.y;
+        }
+        f.vp[tau] = vpar[t0 + 16 * tau + col];
+      }
+      // channel residue col, step st, slice j: CBK words (channel blocks 0..CBK-1)
+      const char* vr = vq + (int64_t)gg * kQ4Group * CBY + (((col * 4 + st) * 4 + j) * CBK) * 4;
+#pragma unroll
+      for (int h = 0; h < CBK / 4; ++h) {
+        const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vr) + h);
+        f.v[4 * h] = x.x; f.v[4 * h + 1] = x.y; f.v[4 * h + 2] = x.z; f.v[4 * h + 3] = x.w;
+      }
+    };
+    auto step = [&](const Ld& f) {
+      f32x4_t sacc[2];
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+        sacc[tau] = bias4;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+          sacc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kc], codes_to_f16(f.k[tau][kc]),
+                                                            sacc[tau], 0, 0, 0);
+      }
+      // online softmax of rows srow0 + i over the 32 tokens (rows >= G stay empty)
+      float bm[4];
+      bool need = false;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        bm[i] = row16_max(fmaxf(sacc[0][i], sacc[1][i]));
+        need |= bm[i] > thq[i];
+      }
+      if (__ballot(need) != 0) {  // rare: move the running maxima, rescale the state
+        float al[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          al[i] = 1.f;
+          if (bm[i] > thq[i]) {
+            const float mn = bm[i] * c2s;
+            al[i] = fexp2(mq[i] - mn);
+            lq[i] *= al[i];
+            zq[i] *= al[i];
+            mq[i] = mn;
+            thq[i] = (mn + kTau) * inv_c2s;
+          }
+        }
+        if (col == 0)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s_x[wave][srow0 + i] = al[i];
+        wave_lds_sync();
+        const float alc = s_x[wave][col];
+#pragma unroll
+        for (int cb = 0; cb < CBK; ++cb) oacc[cb] *= alc;
+        wave_lds_sync();
+      }
+      // token col of each tile goes to operand slot kCodeSlot[col % 8] of its 8 tokens,
+      // with 1/16 where that slot reads a high nibble (the odd tokens)
+      const int pslot = (col & ~7) + 2 * (col & 3) + ((col >> 2) & 1);
+      const float oddf = (col & 1) ? 0.0625f : 1.f;
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+        const float2 vpt = f.vp[tau];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = fexp2(__builtin_fmaf(sacc[tau][i], c2s, -mq[i]));
+          lq[i] += p;
+          zq[i] = __builtin_fmaf(p, vpt.y, zq[i]);
+          s_p[wave][srow0 + i][16 * tau + pslot] = (_Float16)(p * vpt.x * oddf);
+        }
+      }
+      wave_lds_sync();
+      const half8_t pb = *(const half8_t*)&s_p[wave][col][8 * (lane >> 4)];
+#pragma unroll
+      for (int cb = 0; cb < CBK; ++cb)
+        oacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_to_f16(f.v[cb]), pb, oacc[cb],
+                                                          0, 0, 0);
+      wave_lds_sync();
+    };
+
+    Ld f0, f1;
+    load_params(0);
+    load_step(f0, 0, 0);
+    for (int gi = 0; gi < n_wave; ++gi) {
+      fold();
+      load_params(gi + 1);  // clamped past the last group
+      for (int st = 0; st < kSteps; st += 2) {
+        load_step(f1, gi, st + 1);
+        step(f0);
+        if (st + 2 < kSteps) load_step(f0, gi, st + 2);
+        else load_step(f0, gi + 1, 0);  // clamped past the last group
+        step(f1);
+      }
+    }
+  }
+  // MFMA partial: row totals over the 16 columns; O^T column col gets its row's value-zero sum
+  {
+    float addr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lq[i] = group_sum<16>(lq[i]);
+      addr[i] = group_sum<16>(zq[i]);
+    }
+    if (col == 0)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_x[wave][srow0 + i] = addr[i];
+    wave_lds_sync();
+    const float add = s_x[wave][col];
+    if (col < G) {
+#pragma unroll
+      for (int cb = 0; cb < CBK; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          s_o[kWaves + wave][col][16 * cb + srow0 + i] = __builtin_fmaf(oacc[cb][i], kTwo24, add);
+    }
+    if (col == 0)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (srow0 + i < G) {
+          s_m[kWaves + wave][srow0 + i] = mq[i];
+          s_l[kWaves + wave][srow0 + i] = lq[i];
+        }
+  }
+
+  // ---- bf16 rows: the residual group (its split only) or the streaming slots ---------------
+  float m[G], thr[G], l[G], o[G][Geo::kE];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = kMInit;
+    thr[g] = kMInit;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < Geo::kE; ++e) o[g][e] = 0.f;
+  }
+  const int t1 = ret ? ((ng % nsplit) == split ? n - ng * kQ4Group : 0) : n;
+  if (t1 > 0) {
+    QRegs<T, D, G, LPT> q;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int c = 0; c < kCpl; ++c) q.q[g][c] = *(const uint4*)&s_q[g][(sub + LPT * c) * 8];
+    auto process = [&](const F& f, bool valid) {
+      float dz[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        dz[g] = group_sum<LPT>(dot_partial<T, D, G, LPT>(f, q, g));
+        dz[g] = valid ? dz[g] : kNegInf;
+      }
+      bool need = false;
+#pragma unroll
+      for (int g = 0; g < G; ++g) need |= dz[g] > thr[g];
+      if (need) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          if (dz[g] > thr[g]) {
+            const float mn = dz[g] * c2;
+            const float al = fexp2(m[g] - mn);
+            l[g] *= al;
+#pragma unroll
+            for (int e = 0; e < Geo::kE; ++e) o[g][e] *= al;
+            m[g] = mn;
+            thr[g] = (mn + kTau) * inv_c2;
+          }
+        }
+      }
+      float p[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        p[g] = fexp2(__builtin_fmaf(dz[g], c2, -m[g]));
+        l[g] += p[g];
+      }
+      accumulate_pv<T, D, G, LPT>(f, p, o);
+    };
+    const int n_it = (t1 + kTpb - 1) / kTpb;
+    auto row_of = [&](int it) -> int64_t {
+      const int t = it * kTpb + wave * kTpw + grp;
+      return (int64_t)(t < t1 ? t : t1 - 1);
+    };
+    auto valid_at = [&](int it) { return it * kTpb + wave * kTpw + grp < t1; };
+    F g0, g1, g2;
+    load_frag<T, D, LPT>(g0, kbase, vbase, row_of(0), sub);
+    load_frag<T, D, LPT>(g1, kbase, vbase, row_of(1), sub);
+    load_frag<T, D, LPT>(g2, kbase, vbase, row_of(2), sub);
+    for (int it = 0; it < n_it; it += 3) {
+      process(g0, valid_at(it));
+      load_frag<T, D, LPT>(g0, kbase, vbase, row_of(it + 3), sub);
+      process(g1, valid_at(it + 1));
+      load_frag<T, D, LPT>(g1, kbase, vbase, row_of(it + 4), sub);
+      process(g2, valid_at(it + 2));
+      load_frag<T, D, LPT>(g2, kbase, vbase, row_of(it + 5), sub);
+    }
+  }
+  // lane groups of this wave -> s_*[wave]
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float mx = m[g];
+    if constexpr (LPT == 8) mx = fmaxf(mx, dpp<0x128>(mx));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float sc = fexp2(m[g] - mx);
+    float lg = l[g] * sc;
+    if constexpr (LPT == 8) lg += dpp<0x128>(lg);
+    lg += __shfl_xor(lg, 16);
+    lg += __shfl_xor(lg, 32);
+#pragma unroll
+    for (int e = 0; e < Geo::kE; ++e) {
+      float x = o[g][e] * sc;
+      if constexpr (LPT == 8) x += dpp<0x128>(x);
+      x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      o[g][e] = x;
+    }
+    if (grp == 0) {
+#pragma unroll
+      for (int c = 0; c < kCpl; ++c)
+#pragma unroll
+        for (int e = 0; e < Geo::kEpc; ++e)
+          s_o[wave][g][Geo::elem_d(sub, c, e)] = o[g][c * Geo::kEpc + e];
+      if (sub == 0) {
+        s_m[wave][g] = mx;
+        s_l[wave][g] = lg;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- merge the 2 x 4 partials; finish or write this split's partial ---------------------
+  for (int idx = tid; idx < G * D; idx += kThreads) {
+    const int g = idx / D, d = idx % D;
+    float M = kMInit;
+#pragma unroll
+    for (int w = 0; w < 2 * kWaves; ++w) M = fmaxf(M, s_m[w][g]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < 2 * kWaves; ++w) {
+      const float sc = fexp2(s_m[w][g] - M);
+      L += s_l[w][g] * sc;
+      O += s_o[w][g][d] * sc;
+    }
+    const int h = h0 + g;
+    if (nsplit == 1) {
+      const int64_t oi = ((int64_t)b * a.Hq + h) * D + d;
+      store_out<T>(a.out, oi, O / L, a.out_f32);
+      if (d == 0 && a.lse) a.lse[(int64_t)b * a.Hq + h] = (M + __builtin_log2f(L)) * kLn2;
+    } else {
+      const int64_t pi = ((int64_t)b * a.Hq + h) * a.max_splits + split;
+      a.part_o[pi * D + d] = O;
+      if (d == 0) {
+        a.part_ml[pi * 2 + 0] = M;
+        a.part_ml[pi * 2 + 1] = L;
+      }
+    }
+  }
+}
+
 // Merge of the context splits of one retrieval query head (sequence b, head h) over 64
 // output columns: M = max_s m_s, L = sum_s l_s exp2(m_s - M), out = sum_s o_s exp2(m_s - M)
 // / L, lse = (M + log2 L) ln 2. Each of the 8 waves takes every 8th split with an online
@@ -537,8 +999,18 @@ struct Variant {
   static int launch(const DecodeArgs& a, void* stream, const KernelMarks& marks) {
     const int64_t blocks = (int64_t)a.B * a.Hr * a.nsplit + (int64_t)a.B * a.Hs;
     if (marks.begin) (void)hipEventRecord((hipEvent_t)marks.begin, (hipStream_t)stream);
-    hipLaunchKernelGGL((decode_kernel<T, D, G, LPT, NS>), dim3((unsigned)blocks),
-                       dim3(kThreads), 0, (hipStream_t)stream, a);
+    if constexpr (sizeof(T) == 2) {
+      if (a.q4)
+        hipLaunchKernelGGL((decode_q4_kernel<D, G, LPT, 4>), dim3((unsigned)blocks),
+                           dim3(kThreads), 0, (hipStream_t)stream, a);
+      else
+        hipLaunchKernelGGL((decode_kernel<T, D, G, LPT, NS>), dim3((unsigned)blocks),
+                           dim3(kThreads), 0, (hipStream_t)stream, a);
+    } else {
+      if (a.q4) return -1;
+      hipLaunchKernelGGL((decode_kernel<T, D, G, LPT, NS>), dim3((unsigned)blocks),
+                         dim3(kThreads), 0, (hipStream_t)stream, a);
+    }
     if (marks.end) (void)hipEventRecord((hipEvent_t)marks.end, (hipStream_t)stream);
     if (a.nsplit > 1 && a.Hr > 0) {
       const int64_t mblocks = (int64_t)a.B * a.Hr * G * (D / 64);

@@ -133,6 +133,13 @@ duo_status decode_impl(duo_cache* c, int32_t layer, const void* q, const void* k
   a.out_f32 = c->cfg.out_dtype == DUO_F32;
   std::memcpy(a.ret_kv, li.ret_kv, sizeof(a.ret_kv));
   std::memcpy(a.str_kv, li.str_kv, sizeof(a.str_kv));
+  if (c->cfg.kv_bits == 4) {
+    const Q4Geom g = q4_geom(c->cfg.capacity, c->cfg.head_dim);
+    a.q4 = 1;
+    a.q4_stride = (int64_t)g.stride;
+    a.q4_params = (int64_t)g.codes;
+    a.q4_resid = (int64_t)(g.codes + g.params);
+  }
   if (launch_decode(a, c->cfg.dtype, c->cfg.head_dim, group, stream,
                     next_marks(c, DUO_TIMING_DECODE)) != 0)
     return DUO_ERR_HIP;
@@ -226,8 +233,23 @@ duo_status duo_kv_append(duo_cache* c, int32_t layer, int32_t seq, const void* k
   a.R = c->cfg.recent;
   a.row_bytes = c->cfg.head_dim * c->esize;
   std::memcpy(a.cls_idx, li.cls_idx, sizeof(a.cls_idx));
+  std::memcpy(a.ret_kv, li.ret_kv, sizeof(a.ret_kv));
   for (int32_t i = 0; i < nb; ++i) a.n_old[i] = len_of(c, layer, b0 + i);
+  const bool q4 = c->cfg.kv_bits == 4;
+  if (q4) {
+    const Q4Geom g = q4_geom(c->cfg.capacity, c->cfg.head_dim);
+    a.q4 = 1;
+    a.q4_stride = (int64_t)g.stride;
+    a.q4_params = (int64_t)g.codes;
+    a.q4_resid = (int64_t)(g.codes + g.params);
+    for (int32_t i = 0; i < nb; ++i) {
+      const int32_t n0 = a.n_old[i], n1 = n0 + n_new;
+      const int32_t first_new = n0 / kQ4Group + (n0 % kQ4Group != 0 ? 1 : 0);
+      a.q4_mid = std::max(a.q4_mid, n1 / kQ4Group - first_new);
+    }
+  }
   if (launch_append(a, c->cfg.dtype, stream) != 0) return DUO_ERR_HIP;
+  if (q4 && a.Hr > 0 && launch_append_kv4(a, c->cfg.head_dim, stream) != 0) return DUO_ERR_HIP;
   for (int32_t b = b0; b < b0 + nb; ++b) len_of(c, layer, b) += n_new;
   return DUO_OK;
 }
@@ -240,6 +262,14 @@ duo_status duo_attn_decode(duo_cache* c, int32_t layer, const void* q, void* out
 duo_status duo_decode_step(duo_cache* c, int32_t layer, const void* q, const void* k,
                            const void* v, void* out, float* lse, void* stream) {
   if (!k || !v) return DUO_ERR_INVALID;
+  if (c && c->cfg.kv_bits == 4) {
+    // 4-bit full caches: the append (which may complete a group) runs first, then the decode
+    if (!layer_ok(c, layer) || !q || !out || !aligned16(q) || !aligned16(out) || !aligned4(lse))
+      return DUO_ERR_INVALID;
+    const duo_status st = duo_kv_append(c, layer, -1, k, v, 1, stream);
+    if (st != DUO_OK) return st;
+    return decode_impl(c, layer, q, nullptr, nullptr, out, lse, stream);
+  }
   return decode_impl(c, layer, q, k, v, out, lse, stream);
 }
 
@@ -249,6 +279,7 @@ namespace {
 // duo_attn_gate_mixed). Returns DUO_OK with `a` filled, or the error to report.
 duo_status prefill_args(duo_cache* c, int32_t layer, int32_t seq, const void* q, const void* k,
                         const void* v, int32_t n_chunk, void* out, float* lse, PrefillArgs& a) {
+  if (c->cfg.kv_bits == 4 && c->layers[layer].n_ret > 0) return DUO_ERR_UNSUPPORTED;
   if (!q || !k || !v || !out || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
       !aligned16(out) || !aligned4(lse))
     return DUO_ERR_INVALID;

@@ -34,6 +34,7 @@ duo_status check_config(const duo_config* cfg) {
   if (!cfg->retrieval_mask) return DUO_ERR_INVALID;
   if (cfg->streaming_prefill != DUO_PREFILL_WINDOW && cfg->streaming_prefill != DUO_PREFILL_CHUNK)
     return DUO_ERR_INVALID;
+  if (cfg->kv_bits != 0 && cfg->kv_bits != 16 && cfg->kv_bits != 4) return DUO_ERR_INVALID;
   if (element_size(cfg->dtype) == 0 || element_size(cfg->out_dtype) == 0)
     return DUO_ERR_INVALID;
   if (!(std::isfinite(cfg->softmax_scale))) return DUO_ERR_INVALID;
@@ -42,6 +43,7 @@ duo_status check_config(const duo_config* cfg) {
   const int g = cfg->num_q_heads / cfg->num_kv_heads;
   if (g != 1 && g != 2 && g != 4 && g != 8) return DUO_ERR_UNSUPPORTED;
   if (cfg->out_dtype != DUO_F32 && cfg->out_dtype != cfg->dtype) return DUO_ERR_UNSUPPORTED;
+  if (cfg->kv_bits == 4 && cfg->dtype != DUO_BF16) return DUO_ERR_UNSUPPORTED;
   return DUO_OK;
 }
 
@@ -72,7 +74,9 @@ duo_status build_layout(const duo_config* cfg, duo_layout* lay, std::vector<Laye
     }
     info.n_ret = nr;
     info.n_str = ns;
-    const long double fb = (long double)B * nr * cap * D * es;
+    const long double per_head = cfg->kv_bits == 4 ? (long double)q4_geom(cap, D).stride
+                                                   : (long double)cap * D * es;
+    const long double fb = (long double)B * nr * per_head;
     const long double sb = (long double)B * ns * SR * D * es;
     full_total += fb;
     str_total += sb;
@@ -221,7 +225,15 @@ duo_status duo_kv_bytes(const duo_config* cfg, const int32_t* seq_lens, int32_t 
     if (seq_lens[b] < 0) return DUO_ERR_INVALID;
     const uint64_t n = (uint64_t)seq_lens[b];
     full += 2 * (nr + ns) * n * D * es;
-    duo_b += 2 * (nr * n + ns * (n < SR ? n : SR)) * D * es;
+    duo_b += 2 * ns * (n < SR ? n : SR) * D * es;
+    if (cfg->kv_bits == 4) {
+      // complete groups: K and V codes (d / 2 bytes each per token), the keys' per-channel
+      // scale and zero per group, the values' per-token scale and zero; then the residual
+      const uint64_t g = n / kQ4Group, t = g * kQ4Group;
+      duo_b += nr * (t * D + g * 2 * D * 4 + t * 2 * 4 + 2 * (n - t) * D * es);
+    } else {
+      duo_b += 2 * nr * n * D * es;
+    }
   }
   *full_attn_bytes = full;
   *duo_bytes = duo_b;

@@ -20,6 +20,26 @@ constexpr int kPrefillTileRows = 128;  // rows of the workspace unit counted by 
 constexpr uint64_t kAlign = 256;
 constexpr int kMaxTimingRecords = 1 << 16;  // event pairs per kernel timer
 
+// Byte geometry of one retrieval head's K (or V) region in a 4-bit cache: codes, then the
+// parameter block, then the residual group in bf16 (layout in duo.h).
+constexpr int kQ4Group = DUO_KV4_GROUP;
+struct Q4Geom {
+  uint64_t codes;   // bytes of codes (128 G rows of D / 2)
+  uint64_t params;  // bytes of the parameter block
+  uint64_t resid;   // bytes of the residual group
+  uint64_t stride;  // bytes per head
+};
+inline Q4Geom q4_geom(uint64_t cap, uint64_t D) {
+  const uint64_t groups = (cap + kQ4Group - 1) / kQ4Group;
+  Q4Geom g;
+  g.codes = groups * kQ4Group * D / 2;
+  const uint64_t kp = groups * 2 * D * 4, vp = groups * kQ4Group * 2 * 4;
+  g.params = kp > vp ? kp : vp;
+  g.resid = (uint64_t)kQ4Group * D * 2;
+  g.stride = g.codes + g.params + g.resid;
+  return g;
+}
+
 // Per-layer head partition. For KV head j: cls_idx[j] >= 0 is its index among the layer's
 // retrieval heads; cls_idx[j] < 0 encodes streaming index -(cls_idx[j] + 1).
 struct LayerInfo {
@@ -60,7 +80,11 @@ struct AppendArgs {
   int32_t* seq_len;   // this layer: [B]
   int32_t b0, nb, m, Hkv, Hr, Hs, cap, S, R;
   int32_t row_bytes;  // D * element size
+  int32_t q4;         // 4-bit full caches: append_kernel leaves retrieval heads to kv4
+  int64_t q4_stride, q4_params, q4_resid;  // Q4Geom: head stride, parameter and residual offsets
+  int32_t q4_mid;     // complete groups of the widest sequence that need no residual rows
   int16_t cls_idx[kMaxKvHeads];
+  uint8_t ret_kv[kMaxKvHeads];
   int32_t n_old[kMaxBatch];  // lengths before the append, for sequences b0 .. b0+nb-1
 };
 
@@ -81,6 +105,8 @@ struct DecodeArgs {
   int32_t B, Hq, Hkv, Hr, Hs, cap, S, R, nsplit, max_splits;
   float scale_log2;        // softmax scale * log2(e)
   int32_t out_f32;
+  int32_t q4;              // full caches in 4 bits (Q4Geom offsets below); no fused step
+  int64_t q4_stride, q4_params, q4_resid;
   uint8_t ret_kv[kMaxKvHeads];
   uint8_t str_kv[kMaxKvHeads];
   int32_t n[kMaxBatch];    // length of every sequence, the fused step's token included
@@ -126,6 +152,7 @@ struct KernelMarks {
 // Launchers (one translation unit per kernel family). They return a hipError_t value as int.
 int launch_reset(const ResetArgs& a, void* stream);
 int launch_append(const AppendArgs& a, int dtype, void* stream);
+int launch_append_kv4(const AppendArgs& a, int head_dim, void* stream);
 int launch_set_lengths(const SetLenArgs& a, void* stream);
 int launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group, void* stream,
                   const KernelMarks& marks);

@@ -81,7 +81,27 @@ typedef struct {
   const uint8_t* retrieval_mask; /* host [num_layers][num_kv_heads], nonzero = retrieval;
                                     copied by duo_cache_create */
   int32_t streaming_prefill; /* duo_prefill_mode of streaming heads in duo_attn_prefill */
+  int32_t kv_bits;         /* 0 or 16: full caches in dtype. 4: full (retrieval) caches in
+                              4 bits, see below (bf16 only); streaming caches keep dtype */
 } duo_config;
+
+/* 4-bit full caches (cfg.kv_bits = 4; explainer, "Combination with Quantization": the full
+ * caches pair with 4-bit per-channel KV quantization). Codes c in 0..15 read back as
+ * c * scale + zero with float32 scale = (max - min) / 15 and zero = min, the code being
+ * rint((x - min) / scale) in float32 (0 when scale = 0). Keys: per channel over aligned
+ * groups of 128 tokens (positions 128 g .. 128 g + 127). Values: per token over the channels.
+ * The tokens of the last, incomplete group stay in dtype in a residual block until the group
+ * completes. Per retrieval head, with G = ceil(capacity / 128) and P = max(8 d, 1024) G:
+ *   K region: codes [128 G][d / 8] 32-bit words, then P bytes holding float32 [G][2][d]
+ *             (scale row, zero row), then the residual [128][d] in dtype (row t % 128);
+ *   V region: codes [G][d * 128 / 8] words, then P bytes holding float32 [128 G][2] (scale,
+ *             zero per token), then the residual [128][d].
+ * A code word holds 8 codes, element e in bits 4e .. 4e + 3. Key row t: the word in slot
+ * (d / 32) j + k holds channels 32 k + 8 j .. + 7 of token t. Value group g: word
+ * (((c % 16) 4 + s) 4 + j) (d / 16) + c / 16 holds channel c of tokens 128 g + 32 s + 8 j .. + 7.
+ * duo_attn_decode and duo_decode_step (run as append + decode) read them; duo_attn_prefill
+ * and duo_attn_gate_mixed return DUO_ERR_UNSUPPORTED on a 4-bit cache. */
+#define DUO_KV4_GROUP 128
 
 /* Byte offsets inside the caller's arena (all 256-byte aligned). Inside each cache region
  * the layers follow one another in order, each starting on a 256-byte boundary. */
@@ -196,8 +216,11 @@ duo_status duo_cache_lengths(const duo_cache* cache, int32_t* host_out);
 /* KV bytes one layer holds for sequences of the given lengths (int32 [B]): under full
  * attention (every KV head keeps every token) and under the split layout
  * (H_r * n + H_s * min(n, S + R)) * d * 2 * element size, summed over sequences (explainer,
- * "Decoding Procedure", memory formula). The second figure is also the K/V bytes one decode
- * step of that layer reads. Host only. */
+ * "Decoding Procedure", memory formula). With 4-bit full caches the retrieval term is, per
+ * head, the codes of the 128 floor(n / 128) grouped tokens (d bytes per token for K and V),
+ * their parameters (8 d bytes per key group, 8 bytes per value token) and the residual tokens
+ * in dtype. The second figure is also the K/V bytes one decode step of that layer reads.
+ * Host only. */
 duo_status duo_kv_bytes(const duo_config* cfg, const int32_t* seq_lens, int32_t layer,
                         uint64_t* full_attn_bytes, uint64_t* duo_bytes);
 

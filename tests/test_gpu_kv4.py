@@ -1,0 +1,254 @@
+"""4-bit full caches (cfg.kv_bits = 4) on the GPU against the CPU oracle.
+
+Append: the stored codes, float32 scales and zeros, and the bf16 residual rows are compared
+bit for bit with the oracle's kv4_codes, through the byte layout documented in duo.h.
+Decode: outputs against decode_step_kv4 (retrieval heads attend over what the 4-bit caches
+read back), |gpu - ref| <= 2e-3 + 1e-2 |ref|.
+"""
+import numpy as np
+import pytest
+import torch
+
+import head_split_kv_amd as hsk
+import workloads as W
+from oracle import duo_oracle as O
+
+from gpu_util import assert_close, step_inputs, to_dev, torch_dtype
+
+pytestmark = pytest.mark.gpu
+
+QG = O.KV4_GROUP
+
+
+def kv4_cache(w, capacity, out_dtype=torch.float32, mask=None):
+    mask = W.retrieval_mask(w) if mask is None else mask
+    return hsk.DuoCache(num_layers=mask.shape[0], batch=w.batch, num_q_heads=w.hq,
+                        num_kv_heads=w.hkv, head_dim=w.d, sink=w.sink, recent=w.recent,
+                        capacity=capacity, retrieval_mask=mask, dtype=torch.bfloat16,
+                        out_dtype=out_dtype, kv_bits=4)
+
+
+def geom(cap, D):
+    groups = -(-cap // QG)
+    codes = groups * QG * D // 2
+    params = max(groups * 2 * D * 4, groups * QG * 2 * 4)
+    resid = QG * D * 2
+    return codes, params, resid, codes + params + resid
+
+
+def head_region(cache, is_v, b, r):
+    """Raw bytes of retrieval head r of sequence b (layer 0) as a numpy uint8 array."""
+    codes, params, resid, stride = geom(cache.capacity, cache.d)
+    hr = int(cache.retrieval_mask[0].sum())
+    off = (cache.layout.full_v_off if is_v else cache.layout.full_k_off) + (b * hr + r) * stride
+    return cache.arena[off:off + stride].cpu().numpy(), codes, params
+
+
+def nibbles(words):
+    """uint32 words -> their 8 codes each (element e in bits 4e .. 4e + 3)."""
+    w = np.asarray(words, dtype=np.uint32)
+    return ((w[..., None] >> (4 * np.arange(8, dtype=np.uint32))) & 15).astype(np.uint8)
+
+
+def unpack_keys(code_bytes, rows, D):
+    """Key codes [rows][D]: row words in slot KC j + kc hold channels 32 kc + 8 j .. + 7."""
+    KC = D // 32
+    w = code_bytes[:rows * D // 2].view(np.uint32).reshape(rows, D // 8)
+    out = np.empty((rows, D), dtype=np.uint8)
+    for slot in range(D // 8):
+        c0 = 32 * (slot % KC) + 8 * (slot // KC)
+        out[:, c0:c0 + 8] = nibbles(w[:, slot])
+    return out
+
+
+def unpack_values(code_bytes, groups, D):
+    """Value codes [groups * QG][D]: word (((c % 16) 4 + s) 4 + j) (D / 16) + c / 16 of a group
+    holds channel c of tokens 32 s + 8 j .. + 7."""
+    CBK = D // 16
+    w = code_bytes[:groups * QG * D // 2].view(np.uint32).reshape(groups, 16, 4, 4, CBK)
+    out = np.empty((groups, QG, D), dtype=np.uint8)
+    for cl in range(16):
+        for s in range(4):
+            for j in range(4):
+                for cb in range(CBK):
+                    t0 = 32 * s + 8 * j
+                    out[:, t0:t0 + 8, 16 * cb + cl] = nibbles(w[:, cl, s, j, cb])
+    return out.reshape(groups * QG, D)
+
+
+def check_stored(cache, w, lens):
+    """Every retrieval head of every sequence: complete groups' codes and parameters equal
+    the oracle's, residual rows equal the input bits."""
+    D = w.d
+    ret = np.nonzero(cache.retrieval_mask[0])[0]
+    for b, n in enumerate(lens):
+        ng = n // QG
+        for r, j in enumerate(ret):
+            for is_v in (False, True):
+                x = W.tokens(w, "v" if is_v else "k", 0, b, 0, n)[:, j].astype(np.float32)
+                raw, codes_b, params_b = head_region(cache, is_v, b, r)
+                codes = unpack_values(raw, ng, D) if is_v else unpack_keys(raw, ng * QG, D)
+                par = raw[codes_b:codes_b + params_b].view(np.float32)
+                for g in range(ng):
+                    blk = x[g * QG:(g + 1) * QG]
+                    c, s, z = O.kv4_codes(blk, axis=1 if is_v else 0)
+                    assert np.array_equal(codes[g * QG:(g + 1) * QG], c), (b, j, is_v, g)
+                    if is_v:
+                        got = par[2 * g * QG:2 * (g + 1) * QG].reshape(QG, 2)
+                    else:
+                        got = par[g * 2 * D:(g + 1) * 2 * D].reshape(2, D).T
+                    assert np.array_equal(got[:, 0].view(np.uint32), s.view(np.uint32)), (b, j, is_v, g)
+                    assert np.array_equal(got[:, 1].view(np.uint32), z.view(np.uint32)), (b, j, is_v, g)
+                res = raw[codes_b + params_b:].view(np.uint16).reshape(QG, D)
+                want = (x[ng * QG:n].view(np.uint32) >> 16).astype(np.uint16)
+                got_rows = res[np.arange(ng * QG, n) % QG]
+                assert np.array_equal(got_rows, want), (b, j, is_v, "residual")
+
+
+def append_tokens(cache, w, b, t0, t1):
+    dt = torch_dtype(w.dtype)
+    k = to_dev(W.tokens(w, "k", 0, b, t0, t1), dt)
+    v = to_dev(W.tokens(w, "v", 0, b, t0, t1), dt)
+    cache.kv_append(0, k, v, seq=b)
+
+
+def test_kv4_append_patterns_bit_exact():
+    """Bulk appends, single tokens across a group boundary, chunks that complete a group
+    holding residual rows and leave a new tail, and ragged sequences."""
+    w = W.Workload("kv4-append", 1, 3, 8, 4, 128, "bf16", 4, 32, 0, 0, 2,
+                   fixed_mask=((0, 2),), seed=101)
+    cache = kv4_cache(w, 1200)
+    lens = [0, 0, 0]
+    plan = [(0, 300), (1, 1), (2, 128), (0, 1), (0, 83), (1, 126), (1, 1), (1, 1), (2, 257),
+            (0, 5), (1, 500), (2, 1)]
+    for b, m in plan:
+        append_tokens(cache, w, b, lens[b], lens[b] + m)
+        lens[b] += m
+        torch.cuda.synchronize()
+        check_stored(cache, w, lens)
+    assert list(cache.lengths()[0]) == lens
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_kv4_append_batch_calls(d):
+    """Appends to every sequence at once (seq = -1), chunk sizes that straddle groups."""
+    w = W.Workload("kv4-append-batch", 1, 2, 4, 2, d, "bf16", 2, 16, 0, 0, 1,
+                   fixed_mask=((1,),), seed=103)
+    cache = kv4_cache(w, 1000)
+    dt = torch_dtype(w.dtype)
+    n = 0
+    for m in (1, 126, 2, 127, 128, 300, 1):
+        k = to_dev(np.stack([W.tokens(w, "k", 0, b, n, n + m) for b in range(2)]), dt)
+        v = to_dev(np.stack([W.tokens(w, "v", 0, b, n, n + m) for b in range(2)]), dt)
+        cache.kv_append(0, k, v)
+        n += m
+        torch.cuda.synchronize()
+        check_stored(cache, w, [n, n])
+
+
+def run_decode_kv4(w, lens0, steps, check_steps=None, splits=None, out_dtype=torch.float32,
+                   fused=False, heads=None):
+    cache = kv4_cache(w, max(lens0) + steps, out_dtype=out_dtype)
+    for b, n in enumerate(lens0):
+        for t0 in range(0, n, 1 << 16):
+            append_tokens(cache, w, b, t0, min(n, t0 + (1 << 16)))
+    if splits is not None:
+        hsk.duo_set_decode_splits(cache, splits)
+    mask = W.retrieval_mask(w)[0]
+    lens = list(lens0)
+    for s in range(steps):
+        q, k, v, qh = step_inputs(w, 0, lens)
+        lse = torch.empty((w.batch, w.hq), dtype=torch.float32, device="cuda")
+        if fused:
+            out = cache.decode_step(0, q, k[:, 0], v[:, 0], lse=lse)
+        else:
+            cache.kv_append(0, k, v)
+            out = cache.attn_decode(0, q, lse=lse)
+        lens = [n + 1 for n in lens]
+        if check_steps is not None and s not in check_steps:
+            continue
+        torch.cuda.synchronize()
+        got, got_lse = out.float().cpu().numpy(), lse.cpu().numpy()
+        for b, n in enumerate(lens):
+            kh, vh = W.tokens(w, "k", 0, b, 0, n), W.tokens(w, "v", 0, b, 0, n)
+            if heads is None:
+                ref, ref_lse = O.decode_step_kv4(qh[b], kh, vh, mask, w.sink, w.recent)
+                assert_close(got[b], ref, f"step {s} seq {b} n {n} out")
+                assert_close(got_lse[b], ref_lse, f"step {s} seq {b} n {n} lse")
+            else:
+                G = w.group
+                for j in heads:
+                    hq = slice(j * G, (j + 1) * G)
+                    ref, ref_lse = O.decode_step_kv4(qh[b][hq], kh[:, j:j + 1], vh[:, j:j + 1],
+                                                     mask[j:j + 1], w.sink, w.recent)
+                    assert_close(got[b][hq], ref, f"step {s} seq {b} kv {j}")
+                    assert_close(got_lse[b][hq], ref_lse, f"step {s} seq {b} kv {j} lse")
+    return cache
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_kv4_decode_variants(d, G):
+    """Every (head_dim, group) variant; a context crossing several groups, steps across the
+    next group boundary (the completing append re-quantizes the residual)."""
+    w = W.Workload("kv4-variant", 1, 2, 2 * G, 2, d, "bf16", 4, 32, 0, 0, 1,
+                   fixed_mask=((0,),), seed=105 + G)
+    run_decode_kv4(w, [3 * QG - 2, 2 * QG + 40], 4)
+
+
+@pytest.mark.parametrize("n0", [1, QG - 1, QG, QG + 1, 5 * QG + 17])
+def test_kv4_decode_lengths(n0):
+    """Contexts inside the first group (residual only), at group edges and past several."""
+    w = W.Workload("kv4-len", 1, 1, 16, 4, 128, "bf16", 16, 64, 0, 0, 2,
+                   fixed_mask=((1, 2),), seed=107)
+    run_decode_kv4(w, [n0], 3)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 16])
+def test_kv4_decode_split_counts(splits):
+    """Groups dealt to 1..16 splits (some with no group, the residual on split ng mod s)."""
+    w = W.Workload("kv4-splits", 1, 1, 32, 8, 128, "bf16", 16, 64, 0, 0, 4, seed=109)
+    run_decode_kv4(w, [9 * QG + 50], 2, splits=splits)
+
+
+def test_kv4_decode_ragged_batch_bf16_out_and_streaming_only():
+    w = W.Workload("kv4-ragged", 1, 3, 32, 8, 128, "bf16", 16, 64, 0, 0, 4, seed=111)
+    run_decode_kv4(w, [700, 129, 1500], 2, out_dtype=torch.bfloat16)
+    w2 = W.Workload("kv4-streaming", 1, 2, 8, 2, 128, "bf16", 4, 32, 0, 0, 0,
+                    fixed_mask=((),), seed=113)
+    run_decode_kv4(w2, [300, 40], 2)
+
+
+def test_kv4_decode_step_from_empty():
+    """duo_decode_step on a 4-bit cache from an empty cache through two group completions,
+    every step checked."""
+    w = W.Workload("kv4-step", 1, 1, 8, 2, 64, "bf16", 4, 16, 0, 0, 1,
+                   fixed_mask=((1,),), seed=115)
+    run_decode_kv4(w, [0], 2 * QG + 5, fused=True, check_steps=set(range(0, 2 * QG + 5, 7)) |
+                   {QG - 1, QG, 2 * QG - 1, 2 * QG})
+
+
+def test_kv4_rejects_prefill_and_gate_mixed():
+    w = W.Workload("kv4-reject", 1, 1, 8, 2, 128, "bf16", 4, 32, 0, 0, 1,
+                   fixed_mask=((0,),), seed=117)
+    cache = kv4_cache(w, 256)
+    dt = torch_dtype(w.dtype)
+    q, k, v = (to_dev(W.tokens(w, t, 0, 0, 0, 16)[None], dt) for t in "qkv")
+    with pytest.raises(hsk.DuoError) as e:
+        cache.attn_prefill(0, q, k, v)
+    assert e.value.status == hsk.DUO_ERR_UNSUPPORTED
+    w2 = W.Workload("kv4-reject2", 1, 1, 8, 2, 128, "bf16", 4, 32, 0, 0, 2,
+                    fixed_mask=((0, 1),), seed=117)
+    cache2 = kv4_cache(w2, 256)
+    with pytest.raises(hsk.DuoError) as e:
+        cache2.attn_gate_mixed(0, q, k, v, [0.5, 0.5])
+    assert e.value.status == hsk.DUO_ERR_UNSUPPORTED
+    assert cache.lengths()[0][0] == 0 and cache2.lengths()[0][0] == 0
+
+
+@pytest.mark.timeout(900)
+def test_kv4_decode_gqa_128k():
+    """Llama-3-8B-shaped GQA layer at a 128K context in 4 bits (the benchmark's shape): the
+    steps cross the group boundary at 131,072 tokens."""
+    w = W.workload("c3")
+    run_decode_kv4(w, [w.context - 2], 4)

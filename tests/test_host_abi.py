@@ -73,6 +73,51 @@ def test_config_checks(bad, status):
     assert N.lib().duo_layout_query(ctypes.byref(cfg2), ctypes.byref(lay)) == N.DUO_ERR_UNSUPPORTED
 
 
+def test_kv_bits_checked_and_kv4_layout():
+    import torch
+    lay = N.DuoLayout()
+    for bits, status in ((0, N.DUO_OK), (16, N.DUO_OK), (4, N.DUO_OK), (8, N.DUO_ERR_INVALID),
+                         (-4, N.DUO_ERR_INVALID)):
+        cfg, _keep = cfg_of()
+        cfg.kv_bits = bits
+        assert N.lib().duo_layout_query(ctypes.byref(cfg), ctypes.byref(lay)) == status, bits
+    cfg, _keep = cfg_of(dtype=torch.float32, kv_bits=4)
+    assert N.lib().duo_layout_query(ctypes.byref(cfg), ctypes.byref(lay)) == N.DUO_ERR_UNSUPPORTED
+    # the 4-bit full caches are sized by the documented per-head geometry
+    cfg4, _k4 = cfg_of(kv_bits=4)
+    cfg16, _k16 = cfg_of()
+    l4, l16 = N.DuoLayout(), N.DuoLayout()
+    assert N.lib().duo_layout_query(ctypes.byref(cfg4), ctypes.byref(l4)) == N.DUO_OK
+    assert N.lib().duo_layout_query(ctypes.byref(cfg16), ctypes.byref(l16)) == N.DUO_OK
+    cap, D, G = 1000, 128, N.KV4_GROUP
+    groups = -(-cap // G)
+    stride = groups * G * D // 2 + max(groups * 2 * D * 4, groups * G * 8) + G * D * 2
+    per_layer = [3 * 1 * stride, 3 * 1 * stride]  # batch 3, one retrieval head per layer
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert l4.full_v_off - l4.full_k_off == al(sum(al(x) for x in per_layer))
+    assert l4.arena_bytes < l16.arena_bytes
+
+
+def test_kv4_bytes_model():
+    """Per retrieval head: d bytes of K and V codes per grouped token, 8 d bytes of key
+    parameters per group, 8 bytes of value parameters per grouped token, residual tokens at
+    4 d bytes (bf16 K and V); streaming heads unchanged."""
+    cfg, _keep = cfg_of(kv_bits=4)
+    full, duo = ctypes.c_uint64(), ctypes.c_uint64()
+    D, G, S, R = 128, N.KV4_GROUP, 4, 16
+    for lens in ([0, 1, 127], [128, 129, 999], [256, 500, 1000]):
+        ln = np.array(lens, dtype=np.int32)
+        assert N.lib().duo_kv_bytes(ctypes.byref(cfg), ln.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                    0, ctypes.byref(full), ctypes.byref(duo)) == N.DUO_OK
+        want = 0
+        for n in lens:
+            g, t = n // G, (n // G) * G
+            want += t * D + g * 8 * D + t * 8 + (n - t) * 4 * D  # one retrieval head
+            want += 2 * min(n, S + R) * D * 2                    # one streaming head
+        assert duo.value == want, lens
+        assert full.value == sum(2 * 2 * n * D * 2 for n in lens)
+
+
 def test_streaming_prefill_mode_checked():
     lay = N.DuoLayout()
     for mode, status in ((N.PREFILL_WINDOW, N.DUO_OK), (N.PREFILL_CHUNK, N.DUO_OK),
