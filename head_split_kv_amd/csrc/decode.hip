@@ -520,9 +520,14 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
   const int srow0 = 4 * (lane >> 4);      // first S row (query) held by this lane
 
   // ---- work item -------------------------------------------------------------------------
+  // In a fused step (a.new_k != null) the token at p = a.n[b] - 1 is not in the cache yet and
+  // completes no group: the block that reads the residual (or the streaming slots) also takes
+  // it from the input and then stores it, as in decode_kernel.
+  const bool fused = a.new_k != nullptr;
   const int64_t n_ret_items = (int64_t)a.B * a.Hr * a.nsplit;
   const bool ret = (int64_t)blockIdx.x < n_ret_items;
-  int b, j, split, nsplit, n;
+  int b, j, split, nsplit, n;  // n: tokens in the cache
+  int new_row = -1, skip = -1;
   const char* kq = nullptr;  // retrieval head: K region (codes, parameters, residual)
   const char* vq = nullptr;
   const char* kbase;         // bf16 rows: the residual group, or the streaming slots
@@ -534,7 +539,8 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
     b = (int)(i / ((int64_t)a.nsplit * a.Hr));
     j = a.ret_kv[cls];
     nsplit = a.nsplit;
-    n = a.n[b];
+    n = fused ? a.n[b] - 1 : a.n[b];
+    if (fused && (n / kQ4Group) % nsplit == split) new_row = n % kQ4Group;
     const int64_t head = ((int64_t)b * a.Hr + cls) * a.q4_stride;
     kq = (const char*)a.full_k + head;
     vq = (const char*)a.full_v + head;
@@ -548,7 +554,14 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
     split = 0;
     nsplit = 1;
     const int SR = a.S + a.R;
-    n = min(a.n[b], SR);
+    if (!fused) {
+      n = min(a.n[b], SR);
+    } else {
+      const int pnew = a.n[b] - 1;
+      new_row = pnew < a.S ? pnew : a.S + (pnew - a.S) % a.R;
+      n = min(pnew, SR);
+      if (pnew >= SR) skip = new_row;  // the evicted token p - R, outside the window
+    }
     const int64_t row0 = ((int64_t)b * a.Hs + cls) * SR;
     kbase = (const char*)a.str_k + row0 * RB;
     vbase = (const char*)a.str_v + row0 * RB;
@@ -777,7 +790,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
     for (int e = 0; e < Geo::kE; ++e) o[g][e] = 0.f;
   }
   const int t1 = ret ? ((ng % nsplit) == split ? n - ng * kQ4Group : 0) : n;
-  if (t1 > 0) {
+  if (t1 > 0 || new_row >= 0) {
     QRegs<T, D, G, LPT> q;
 #pragma unroll
     for (int g = 0; g < G; ++g)
@@ -820,18 +833,46 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
       const int t = it * kTpb + wave * kTpw + grp;
       return (int64_t)(t < t1 ? t : t1 - 1);
     };
-    auto valid_at = [&](int it) { return it * kTpb + wave * kTpw + grp < t1; };
-    F g0, g1, g2;
-    load_frag<T, D, LPT>(g0, kbase, vbase, row_of(0), sub);
-    load_frag<T, D, LPT>(g1, kbase, vbase, row_of(1), sub);
-    load_frag<T, D, LPT>(g2, kbase, vbase, row_of(2), sub);
-    for (int it = 0; it < n_it; it += 3) {
-      process(g0, valid_at(it));
-      load_frag<T, D, LPT>(g0, kbase, vbase, row_of(it + 3), sub);
-      process(g1, valid_at(it + 1));
-      load_frag<T, D, LPT>(g1, kbase, vbase, row_of(it + 4), sub);
-      process(g2, valid_at(it + 2));
-      load_frag<T, D, LPT>(g2, kbase, vbase, row_of(it + 5), sub);
+    auto valid_at = [&](int it) {
+      const int t = it * kTpb + wave * kTpw + grp;
+      return t < t1 && t != skip;
+    };
+    if (t1 > 0) {
+      F g0, g1, g2;
+      load_frag<T, D, LPT>(g0, kbase, vbase, row_of(0), sub);
+      load_frag<T, D, LPT>(g1, kbase, vbase, row_of(1), sub);
+      load_frag<T, D, LPT>(g2, kbase, vbase, row_of(2), sub);
+      for (int it = 0; it < n_it; it += 3) {
+        process(g0, valid_at(it));
+        load_frag<T, D, LPT>(g0, kbase, vbase, row_of(it + 3), sub);
+        process(g1, valid_at(it + 1));
+        load_frag<T, D, LPT>(g1, kbase, vbase, row_of(it + 4), sub);
+        process(g2, valid_at(it + 2));
+        load_frag<T, D, LPT>(g2, kbase, vbase, row_of(it + 5), sub);
+      }
+    }
+    // fused step: the new token from the input, then its store (residual row or ring slot)
+    if (new_row >= 0) {
+      const char* nk = (const char*)a.new_k + ((int64_t)b * a.Hkv + j) * RB;
+      const char* nv = (const char*)a.new_v + ((int64_t)b * a.Hkv + j) * RB;
+      F f;
+      load_frag<T, D, LPT>(f, nk, nv, 0, sub);
+      process(f, wave == 0 && grp == 0);
+      if (wave == 0) {
+        constexpr int kRowChunks = RB / 16;
+        for (int c = lane; c < 2 * kRowChunks; c += 64) {
+          const bool is_v = c >= kRowChunks;
+          const int cc = is_v ? c - kRowChunks : c;
+          const uint4 x = *(const uint4*)((is_v ? nv : nk) + cc * 16);
+          *(uint4*)(const_cast<char*>(is_v ? vbase : kbase) + (int64_t)new_row * RB + cc * 16) = x;
+        }
+        if (j == 0 && lane == 0) {  // one block per sequence updates the tables
+          const int pnew = a.n[b] - 1;
+          const int SR = a.S + a.R;
+          a.slot_pos[(int64_t)b * SR + (pnew < a.S ? pnew : a.S + (pnew - a.S) % a.R)] = pnew;
+          a.seq_len[b] = a.n[b];
+        }
+      }
     }
   }
   // lane groups of this wave -> s_*[wave]

@@ -262,13 +262,19 @@ duo_status duo_attn_decode(duo_cache* c, int32_t layer, const void* q, void* out
 duo_status duo_decode_step(duo_cache* c, int32_t layer, const void* q, const void* k,
                            const void* v, void* out, float* lse, void* stream) {
   if (!k || !v) return DUO_ERR_INVALID;
-  if (c && c->cfg.kv_bits == 4) {
-    // 4-bit full caches: the append (which may complete a group) runs first, then the decode
-    if (!layer_ok(c, layer) || !q || !out || !aligned16(q) || !aligned16(out) || !aligned4(lse))
-      return DUO_ERR_INVALID;
-    const duo_status st = duo_kv_append(c, layer, -1, k, v, 1, stream);
-    if (st != DUO_OK) return st;
-    return decode_impl(c, layer, q, nullptr, nullptr, out, lse, stream);
+  if (c && c->cfg.kv_bits == 4 && layer_ok(c, layer)) {
+    // 4-bit full caches: a token that completes a group of some sequence needs the group's
+    // quantization, so that step runs as append + decode; otherwise the token only lands in
+    // the bf16 residual and the step is fused like the bf16 one
+    bool completes = false;
+    for (int32_t b = 0; b < c->cfg.batch; ++b)
+      completes |= (len_of(c, layer, b) + 1) % kQ4Group == 0;
+    if (completes) {
+      if (!q || !out || !aligned16(q) || !aligned16(out) || !aligned4(lse)) return DUO_ERR_INVALID;
+      const duo_status st = duo_kv_append(c, layer, -1, k, v, 1, stream);
+      if (st != DUO_OK) return st;
+      return decode_impl(c, layer, q, nullptr, nullptr, out, lse, stream);
+    }
   }
   return decode_impl(c, layer, q, k, v, out, lse, stream);
 }
