@@ -645,14 +645,19 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
       uint32_t v[CBK];    // value code words of the channel blocks
       float2 vp[2];       // value scale and zero of token col of each tile
     };
+    // past this wave's last group the look-ahead reads the first KB of the parameter region
+    // instead (cached, and the values are never used), so it costs no HBM traffic
+    const char* dummy = (const char*)kpar;
     auto load_step = [&](Ld& f, int gi, int st) {
+      const bool real = gi < n_wave;
       const int gg = group_of(gi);
       const int64_t t0 = (int64_t)gg * kQ4Group + st * kStep;
       const int j = lane >> 4;
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau) {
         // token t0 + 16 tau + col: words KC j .. KC j + KC - 1 of its row
-        const char* kr = kq + (t0 + 16 * tau + col) * CBY + j * KC * 4;
+        const int64_t koff = (t0 + 16 * tau + col) * CBY + j * KC * 4;
+        const char* kr = real ? kq + koff : dummy + (koff & 1023);
         if constexpr (KC == 4) {
           const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kr));
           f.k[tau][0] = x.x; f.k[tau][1] = x.y; f.k[tau][2] = x.z; f.k[tau][3] = x.w;
@@ -660,10 +665,12 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
           const u32x2_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(kr));
           f.k[tau][0] = x.x; f.k[tau][1] = x.y;
         }
-        f.vp[tau] = vpar[t0 + 16 * tau + col];
+        const int64_t tok = t0 + 16 * tau + col;
+        f.vp[tau] = real ? vpar[tok] : *(const float2*)(dummy + ((tok * 8) & 1023));
       }
       // channel residue col, step st, slice j: CBK words (channel blocks 0..CBK-1)
-      const char* vr = vq + (int64_t)gg * kQ4Group * CBY + (((col * 4 + st) * 4 + j) * CBK) * 4;
+      const int64_t voff = (int64_t)gg * kQ4Group * CBY + (((col * 4 + st) * 4 + j) * CBK) * 4;
+      const char* vr = real ? vq + voff : dummy + (voff & 1023);
 #pragma unroll
       for (int h = 0; h < CBK / 4; ++h) {
         const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vr) + h);
