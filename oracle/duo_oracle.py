@@ -366,25 +366,34 @@ def reorder_input_cols(w, order, cols_per_head: int) -> np.ndarray:
 # Explainer, "Combination with Quantization" and the OpenReview reply on KV quantization:
 # DuoAttention's full caches combine with 4-bit KV quantization (per-channel, as in KIVI).
 # The pages fix the bit width only. Readings taken here, each a plain choice:
-#   * asymmetric 4-bit codes 0..15 with a float32 scale and zero point (zero = the minimum);
+#   * asymmetric 4-bit codes 0..15 with a scale and zero point stored in bfloat16 (round to
+#     nearest even of the float32 scale (max - min) / 15 and of the minimum);
 #   * keys per channel over aligned groups of KV4_GROUP = 128 tokens (positions g*128 ..
 #     g*128+127), values per token over the channels;
 #   * the tokens of the last, incomplete group are kept exactly (bf16) until it completes;
-#   * the code decision is taken in float32: c = rint((x - zero) / scale) clamped to 0..15,
-#     with scale = (max - min) / 15 and c = 0 when scale is 0 (IEEE float32 division,
-#     round half to even), so that any float32 implementation takes the same decision;
-#   * a stored token reads back as c * scale + zero.
+#   * the code decision is taken in float32 against the stored values: c = rint((x - zero) /
+#     scale) clamped to 0..15, and c = 0 when scale is 0 (IEEE float32 division, round half to
+#     even), so that any float32 implementation takes the same decision;
+#   * a stored token reads back as c * scale + zero with the stored scale and zero.
 
 KV4_GROUP = 128
 
 
+def to_bf16(x) -> np.ndarray:
+    """float32 values rounded to the nearest bfloat16 (ties to even), returned as float32."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32)
+
+
 def kv4_codes(x, axis: int):
     """4-bit codes of a float32 block over ``axis`` (the reduction axis of min and max).
-    Returns ``(codes uint8, scale float32, zero float32)``, scale and zero reduced."""
+    Returns ``(codes uint8, scale, zero)``: the stored bfloat16 scale and zero (as float32),
+    reduced over ``axis``."""
     x = np.asarray(x, dtype=np.float32)
-    mn = x.min(axis=axis, keepdims=True)
+    mn = to_bf16(x.min(axis=axis, keepdims=True))
     mx = x.max(axis=axis, keepdims=True)
-    scale = (mx - mn) / np.float32(15.0)
+    scale = to_bf16((mx - x.min(axis=axis, keepdims=True)) / np.float32(15.0))
     with np.errstate(divide="ignore", invalid="ignore"):
         c = np.rint((x - mn) / scale)
     c = np.where(scale == 0, np.float32(0.0), c)

@@ -525,9 +525,11 @@ def _bf16_grid(rng, *shape):
 
 
 def pin_kv4_nearest_level():
-    """Every code is the nearest of the 16 levels zero + c * scale (up to float32 rounding of
-    the quotient), the block's minimum and maximum take codes 0 and 15, and the error is at
-    most half a step; checked against a search over all 16 levels in float64."""
+    """Every code is the nearest of the 16 stored levels zero + c * scale (up to float32
+    rounding of the quotient), found by search over all 16 levels in float64; the error is at
+    most half a step inside the levels' span, and beyond it no more than the bfloat16 rounding
+    of the minimum and of the step moved the span; the stored scale and zero are the
+    bfloat16 roundings of (max - min) / 15 and of the minimum."""
     rng = np.random.default_rng(51)
     for shape, axis in (((64, 16), 0), ((8, 128), 1), ((64, 3), 0)):
         x = _bf16_grid(rng, *shape)
@@ -539,10 +541,14 @@ def pin_kv4_nearest_level():
         best = dist.min(axis=-1)
         got = np.take_along_axis(dist, codes[..., None].astype(np.int64), -1)[..., 0]
         assert np.all(got <= best + 1e-6 * s), shape
-        assert np.all(got <= 0.5 * s * (1 + 1e-6)), shape
-        assert np.array_equal(np.take_along_axis(codes, np.expand_dims(x.argmin(axis), axis), axis),
-                              np.zeros_like(np.expand_dims(x.argmin(axis), axis), dtype=np.uint8))
-        assert np.all(np.take_along_axis(codes, np.expand_dims(x.argmax(axis), axis), axis) == 15)
+        mn = x.min(axis=axis, keepdims=True).astype(np.float64)
+        mx = x.max(axis=axis, keepdims=True).astype(np.float64)
+        slack = np.maximum(np.maximum(z - mn, 0), np.maximum(mx - (z + 15 * s), 0))
+        assert np.all(got <= 0.5 * s * (1 + 1e-6) + slack), shape
+        assert np.all(np.abs(z - mn) <= np.abs(mn) * 2.0 ** -8), shape
+        assert np.all(np.abs(s - (mx - mn) / 15) <= (mx - mn) / 15 * 2.0 ** -8 + 1e-30), shape
+        # bfloat16 values: the low 16 bits of the float32 are zero
+        assert not np.any(scale.view(np.uint32) & 0xFFFF) and not np.any(zero.view(np.uint32) & 0xFFFF)
 
 
 def pin_kv4_axes_and_exact_grids():
