@@ -448,8 +448,9 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
 // unit; the partner operand carries 1/16 where the nibble was high and the products are
 // scaled back by 2^24 (also exact). Masking takes the elements of a word in the order
 // 0, 4, 1, 5, 2, 6, 3, 7, which the partner operand follows. A wave streams whole groups in
-// steps of 32 tokens with the next step's codes and the next group's key parameters in
-// flight. Codes are stored in operand order (layout in duo.h): the KC key words of one token
+// steps of 32 tokens, one register slot per step, each refilled with the same step of the next
+// group as soon as it is used: three steps of codes and the next group's (bf16) key parameters
+// are in flight (a wave moves the bytes it has in flight per memory latency). Codes are stored in operand order (layout in duo.h): the KC key words of one token
 // that a lane needs are contiguous, and so are the D / 16 value words of one channel residue
 // and step, so every load moves whole lines. The incomplete last group (bf16
 // residual rows) and the streaming heads take the bf16 path over the 4 waves of one block.
@@ -515,7 +516,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
   __shared__ float s_x[kWaves][16];  // per-row scalars moved from the S to the O^T layout
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, grp = lane / LPT, sub = lane % LPT;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, grp = lane / LPT, sub = lane % LPT;
   const int col = lane & 15;              // MFMA column: token of S, query of O^T
   const int srow0 = 4 * (lane >> 4);      // first S row (query) held by this lane
 
@@ -600,36 +601,44 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
     auto group_of = [&](int i) {
       return split + nsplit * (wave + kWaves * (i < n_wave ? i : n_wave - 1));
     };
-    const float* kpar = (const float*)(kq + a.q4_params);    // [group][2][D]
-    const float2* vpar = (const float2*)(vq + a.q4_params);  // [token]
-    // key scale and zero of this lane's A-operand channels 32 kc + 8 (lane / 16) + e
-    float4 ps[KC][2], pz[KC][2];
+    const uint16_t* kpar = (const uint16_t*)(kq + a.q4_params);  // bf16 [group][2][D]
+    const uint32_t* vpar = (const uint32_t*)(vq + a.q4_params);  // [token]: bf16 scale | zero
+    // bf16 key scale and zero of this lane's A-operand channels 32 kc + 8 (lane / 16) + e
+    uint4 ps[KC], pz[KC];
     auto load_params = [&](int gi) {
-      const float* p = kpar + (int64_t)group_of(gi) * 2 * D;
+      const uint16_t* p = kpar + (int64_t)group_of(gi) * 2 * D;
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
         const int ch = 32 * kc + 8 * (lane >> 4);
-        ps[kc][0] = *(const float4*)(p + ch);
-        ps[kc][1] = *(const float4*)(p + ch + 4);
-        pz[kc][0] = *(const float4*)(p + D + ch);
-        pz[kc][1] = *(const float4*)(p + D + ch + 4);
+        ps[kc] = *(const uint4*)(p + ch);
+        pz[kc] = *(const uint4*)(p + D + ch);
       }
     };
     half8_t qa[KC];
     f32x4_t bias4;
     auto fold = [&]() {
       float bp = 0.f;  // this lane's part of row col's bias
+      const float qlive = col < G ? 1.f : 0.f;  // rows past G carry a zero query
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        const float sv[8] = {ps[kc][0].x, ps[kc][0].y, ps[kc][0].z, ps[kc][0].w,
-                             ps[kc][1].x, ps[kc][1].y, ps[kc][1].z, ps[kc][1].w};
-        const float zv[8] = {pz[kc][0].x, pz[kc][0].y, pz[kc][0].z, pz[kc][0].w,
-                             pz[kc][1].x, pz[kc][1].y, pz[kc][1].z, pz[kc][1].w};
+        // channels 32 kc + 8 (lane / 16) + 0..7 of query col, one 16-byte read
+        const uint4 qv = *(const uint4*)&s_q[col < G ? col : 0][32 * kc + 8 * (lane >> 4)];
+        const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
+        const uint32_t sw[4] = {ps[kc].x, ps[kc].y, ps[kc].z, ps[kc].w};
+        const uint32_t zw[4] = {pz[kc].x, pz[kc].y, pz[kc].z, pz[kc].w};
+        float sv[8], zv[8];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          sv[2 * h] = __builtin_bit_cast(float, sw[h] << 16);
+          sv[2 * h + 1] = __builtin_bit_cast(float, sw[h] & 0xFFFF0000u);
+          zv[2 * h] = __builtin_bit_cast(float, zw[h] << 16);
+          zv[2 * h + 1] = __builtin_bit_cast(float, zw[h] & 0xFFFF0000u);
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int x = kCodeOrder[e];  // channel 32 kc + 8 (lane / 16) + x in operand slot e
-          const int ch = 32 * kc + 8 * (lane >> 4) + x;
-          const float qf = col < G ? bf16_bits_to_f32(s_q[col < G ? col : 0][ch]) : 0.f;
+          const float qf =
+              qlive * __builtin_bit_cast(float, (x & 1) ? qw[x >> 1] & 0xFFFF0000u : qw[x >> 1] << 16);
           qa[kc][e] = (_Float16)(qf * sv[x] * (kCodeHigh[e] ? 0.0625f : 1.f));
           bp = __builtin_fmaf(qf, zv[x], bp);
         }
@@ -643,13 +652,16 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
     struct Ld {
       uint32_t k[2][KC];  // key code words of the two 16-token tiles
       uint32_t v[CBK];    // value code words of the channel blocks
-      float2 vp[2];       // value scale and zero of token col of each tile
+      uint32_t vp[2];     // bf16 value scale and zero of token col of each tile
     };
-    // past this wave's last group the look-ahead reads the first KB of the parameter region
-    // instead (cached, and the values are never used), so it costs no HBM traffic
-    const char* dummy = (const char*)kpar;
+    // Past this wave's last group the look-ahead reads the first KB of the region's parameter
+    // block instead (cached, and the values are never used), so it costs no HBM traffic. The
+    // choice is an offset mask, not a branch: a branch would split the loop body and let the
+    // compiler move the last uses of a slot below its reload.
+    const int64_t q4p = a.q4_params;
+    auto pick = [](int64_t off, int64_t keep, int64_t alt) { return (off & keep) | (alt & ~keep); };
     auto load_step = [&](Ld& f, int gi, int st) {
-      const bool real = gi < n_wave;
+      const int64_t keep = gi < n_wave ? -1 : 0;  // wave-uniform
       const int gg = group_of(gi);
       const int64_t t0 = (int64_t)gg * kQ4Group + st * kStep;
       const int j = lane >> 4;
@@ -657,7 +669,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
       for (int tau = 0; tau < 2; ++tau) {
         // token t0 + 16 tau + col: words KC j .. KC j + KC - 1 of its row
         const int64_t koff = (t0 + 16 * tau + col) * CBY + j * KC * 4;
-        const char* kr = real ? kq + koff : dummy + (koff & 1023);
+        const char* kr = kq + pick(koff, keep, q4p + (koff & 1023));
         if constexpr (KC == 4) {
           const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kr));
           f.k[tau][0] = x.x; f.k[tau][1] = x.y; f.k[tau][2] = x.z; f.k[tau][3] = x.w;
@@ -665,12 +677,12 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
           const u32x2_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(kr));
           f.k[tau][0] = x.x; f.k[tau][1] = x.y;
         }
-        const int64_t tok = t0 + 16 * tau + col;
-        f.vp[tau] = real ? vpar[tok] : *(const float2*)(dummy + ((tok * 8) & 1023));
+        const int64_t poff = (t0 + 16 * tau + col) * 4;
+        f.vp[tau] = *(const uint32_t*)(vq + q4p + pick(poff, keep, poff & 1023));
       }
       // channel residue col, step st, slice j: CBK words (channel blocks 0..CBK-1)
       const int64_t voff = (int64_t)gg * kQ4Group * CBY + (((col * 4 + st) * 4 + j) * CBK) * 4;
-      const char* vr = real ? vq + voff : dummy + (voff & 1023);
+      const char* vr = vq + pick(voff, keep, q4p + (voff & 1023));
 #pragma unroll
       for (int h = 0; h < CBK / 4; ++h) {
         const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vr) + h);
@@ -688,17 +700,20 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
                                                             sacc[tau], 0, 0, 0);
       }
       // online softmax of rows srow0 + i over the 32 tokens (rows >= G stay empty)
+      // the common case compares each raw product with its row's threshold; only when one
+      // passes it does the wave take the row maxima over the 16 columns
       float bm[4];
       bool need = false;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        bm[i] = row16_max(fmaxf(sacc[0][i], sacc[1][i]));
+        bm[i] = fmaxf(sacc[0][i], sacc[1][i]);
         need |= bm[i] > thq[i];
       }
       if (__ballot(need) != 0) {  // rare: move the running maxima, rescale the state
         float al[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+          bm[i] = row16_max(bm[i]);
           al[i] = 1.f;
           if (bm[i] > thq[i]) {
             const float mn = bm[i] * c2s;
@@ -724,13 +739,14 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
       const float oddf = (col & 1) ? 0.0625f : 1.f;
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau) {
-        const float2 vpt = f.vp[tau];
+        const float vs = __builtin_bit_cast(float, f.vp[tau] << 16) * oddf;
+        const float vz = __builtin_bit_cast(float, f.vp[tau] & 0xFFFF0000u);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float p = fexp2(__builtin_fmaf(sacc[tau][i], c2s, -mq[i]));
           lq[i] += p;
-          zq[i] = __builtin_fmaf(p, vpt.y, zq[i]);
-          s_p[wave][srow0 + i][16 * tau + pslot] = (_Float16)(p * vpt.x * oddf);
+          zq[i] = __builtin_fmaf(p, vz, zq[i]);
+          s_p[wave][srow0 + i][16 * tau + pslot] = (_Float16)(p * vs);
         }
       }
       wave_lds_sync();
@@ -742,19 +758,32 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
       wave_lds_sync();
     };
 
-    Ld f0, f1;
+    // one register slot per step of a group: slot s is refilled with step s of the next
+    // group right after use, so three steps of loads stay in flight
+    static_assert(kSteps == 4, "one register slot per step of a group");
+    Ld f0, f1, f2, f3;
     load_params(0);
     load_step(f0, 0, 0);
+    load_step(f1, 0, 1);
+    load_step(f2, 0, 2);
+    load_step(f3, 0, 3);
     for (int gi = 0; gi < n_wave; ++gi) {
       fold();
       load_params(gi + 1);  // clamped past the last group
-      for (int st = 0; st < kSteps; st += 2) {
-        load_step(f1, gi, st + 1);
-        step(f0);
-        if (st + 2 < kSteps) load_step(f0, gi, st + 2);
-        else load_step(f0, gi + 1, 0);  // clamped past the last group
-        step(f1);
-      }
+      // the barriers keep each slot's last use ahead of its reload, so the reload lands in
+      // the same registers (no loop-carried copy, which would wait for the load)
+      step(f0);
+      __builtin_amdgcn_sched_barrier(0);
+      load_step(f0, gi + 1, 0);
+      step(f1);
+      __builtin_amdgcn_sched_barrier(0);
+      load_step(f1, gi + 1, 1);
+      step(f2);
+      __builtin_amdgcn_sched_barrier(0);
+      load_step(f2, gi + 1, 2);
+      step(f3);
+      __builtin_amdgcn_sched_barrier(0);
+      load_step(f3, gi + 1, 3);
     }
   }
   // MFMA partial: row totals over the 16 columns; O^T column col gets its row's value-zero sum

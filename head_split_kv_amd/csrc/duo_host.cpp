@@ -228,9 +228,9 @@ duo_status duo_kv_bytes(const duo_config* cfg, const int32_t* seq_lens, int32_t 
     duo_b += 2 * ns * (n < SR ? n : SR) * D * es;
     if (cfg->kv_bits == 4) {
       // complete groups: K and V codes (d / 2 bytes each per token), the keys' per-channel
-      // scale and zero per group, the values' per-token scale and zero; then the residual
+      // bf16 scale and zero per group, the values' per-token bf16 pair; then the residual
       const uint64_t g = n / kQ4Group, t = g * kQ4Group;
-      duo_b += nr * (t * D + g * 2 * D * 4 + t * 2 * 4 + 2 * (n - t) * D * es);
+      duo_b += nr * (t * D + g * 2 * D * 2 + t * 4 + 2 * (n - t) * D * es);
     } else {
       duo_b += 2 * nr * n * D * es;
     }

@@ -33,7 +33,7 @@ inline Q4Geom q4_geom(uint64_t cap, uint64_t D) {
   const uint64_t groups = (cap + kQ4Group - 1) / kQ4Group;
   Q4Geom g;
   g.codes = groups * kQ4Group * D / 2;
-  const uint64_t kp = groups * 2 * D * 4, vp = groups * kQ4Group * 2 * 4;
+  const uint64_t kp = groups * 2 * D * 2, vp = groups * kQ4Group * 4;  // bf16 parameters
   g.params = kp > vp ? kp : vp;
   g.resid = (uint64_t)kQ4Group * D * 2;
   g.stride = g.codes + g.params + g.resid;

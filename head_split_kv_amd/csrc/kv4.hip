@@ -2,9 +2,10 @@
 // heads' full caches in 4 bits). Keys are quantized per channel over aligned groups of
 // kQ4Group tokens, values per token, both only when their group is complete, the codes
 // stored in the operand layouts of the decode kernel (below). Until a group is complete the
-// group's tokens wait in a bf16 residual block (row t % kQ4Group). Code of x in a block with
-// minimum mn and maximum mx: scale = (mx - mn) / 15, c = rint((x - mn) / scale) clamped to
-// 0..15 (0 when scale is 0), all in IEEE float32, so the decision is reproducible.
+// group's tokens wait in a bf16 residual block (row t % kQ4Group). Parameters of a block with
+// minimum mn and maximum mx: scale = bf16((mx - mn) / 15) and zero = bf16(mn), stored; the code
+// of x is rint((x - zero) / scale) clamped to 0..15 (0 when scale is 0), in IEEE float32
+// against the stored values, so the decision is reproducible.
 //
 // Blocks per (sequence, retrieval head): block 0 is the edge block. It completes the first
 // group if that group already had residual rows (reading them), then, after a barrier,
@@ -25,6 +26,12 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __builtin_bit_cast(float, (uint32_t)h << 16);
 }
 
+// float32 -> bfloat16 bits, round to nearest even (the stored scale and zero)
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
 __device__ __forceinline__ uint32_t code_of(float x, float mn, float scale) {
   if (scale == 0.f) return 0u;
   const float r = __builtin_rintf((x - mn) / scale);
@@ -40,10 +47,11 @@ __device__ __forceinline__ uint32_t code_of(float x, float mn, float scale) {
 static_assert(kG == 128, "four 32-token steps per group");
 
 // Quantize the group staged in s (rows 0..kG-1, bf16) as keys: per channel over the rows.
-// codes: the group's first code row; params: float32 [2][D] (scale row, zero row); sk: the
-// same in LDS for the code pass.
+// codes: the group's first code row; params: bf16 [2][D] (scale row, zero row); sk: the
+// stored values (as float) in LDS for the code pass, which decides against them.
 template <int D>
-__device__ void quantize_keys(const uint16_t (*s)[D], uint8_t* codes, float* params, float* sk) {
+__device__ void quantize_keys(const uint16_t (*s)[D], uint8_t* codes, uint16_t* params,
+                              float* sk) {
   const int c = threadIdx.x;
   if (c < D) {
     float mn = bf16_to_f32(s[0][c]), mx = mn;
@@ -52,11 +60,11 @@ __device__ void quantize_keys(const uint16_t (*s)[D], uint8_t* codes, float* par
       mn = fminf(mn, x);
       mx = fmaxf(mx, x);
     }
-    const float scale = (mx - mn) / 15.f;
-    params[c] = scale;
-    params[D + c] = mn;
-    sk[c] = scale;
-    sk[D + c] = mn;
+    const uint16_t sb = f32_to_bf16_bits((mx - mn) / 15.f), zb = f32_to_bf16_bits(mn);
+    params[c] = sb;
+    params[D + c] = zb;
+    sk[c] = bf16_to_f32(sb);
+    sk[D + c] = bf16_to_f32(zb);
   }
   __syncthreads();
   constexpr int KC = D / 32, W = D / 8;
@@ -73,10 +81,10 @@ __device__ void quantize_keys(const uint16_t (*s)[D], uint8_t* codes, float* par
 }
 
 // Quantize the staged group as values: per token over the channels (one wave per token for
-// the minimum and maximum). params: float32 [kG][2] (scale, zero) of the group's tokens; sp:
-// the same in LDS for the code pass.
+// the minimum and maximum). params: one word per token of the group, bf16 scale in the low
+// half and bf16 zero in the high half; sp: the stored values (as float) in LDS.
 template <int D>
-__device__ void quantize_values(const uint16_t (*s)[D], uint8_t* codes, float* params,
+__device__ void quantize_values(const uint16_t (*s)[D], uint8_t* codes, uint32_t* params,
                                 float* sp) {
   constexpr int kPer = D / 64;  // channels per lane: lane, lane + 64
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -97,12 +105,11 @@ __device__ void quantize_values(const uint16_t (*s)[D], uint8_t* codes, float* p
       mn = fminf(mn, __shfl_xor(mn, off));
       mx = fmaxf(mx, __shfl_xor(mx, off));
     }
-    const float scale = (mx - mn) / 15.f;
+    const uint16_t sb = f32_to_bf16_bits((mx - mn) / 15.f), zb = f32_to_bf16_bits(mn);
     if (lane == 0) {
-      params[2 * r] = scale;
-      params[2 * r + 1] = mn;
-      sp[2 * r] = scale;
-      sp[2 * r + 1] = mn;
+      params[r] = (uint32_t)sb | ((uint32_t)zb << 16);
+      sp[2 * r] = bf16_to_f32(sb);
+      sp[2 * r + 1] = bf16_to_f32(zb);
     }
   }
   __syncthreads();
@@ -163,9 +170,9 @@ __global__ void __launch_bounds__(kThreads) kv4_append_kernel(AppendArgs a) {
       char* base = (char*)(is_v ? a.full_v : a.full_k) + head;
       uint8_t* codes = (uint8_t*)base + (int64_t)g * kG * (D / 2);
       if (is_v)
-        quantize_values<D>(s, codes, (float*)(base + a.q4_params) + (int64_t)g * kG * 2, sp);
+        quantize_values<D>(s, codes, (uint32_t*)(base + a.q4_params) + (int64_t)g * kG, sp);
       else
-        quantize_keys<D>(s, codes, (float*)(base + a.q4_params) + (int64_t)g * 2 * D, sp);
+        quantize_keys<D>(s, codes, (uint16_t*)(base + a.q4_params) + (int64_t)g * 2 * D, sp);
       __syncthreads();
     }
   };

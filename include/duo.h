@@ -87,20 +87,22 @@ typedef struct {
 
 /* 4-bit full caches (cfg.kv_bits = 4; explainer, "Combination with Quantization": the full
  * caches pair with 4-bit per-channel KV quantization). Codes c in 0..15 read back as
- * c * scale + zero with float32 scale = (max - min) / 15 and zero = min, the code being
- * rint((x - min) / scale) in float32 (0 when scale = 0). Keys: per channel over aligned
+ * c * scale + zero with scale = bf16((max - min) / 15) and zero = bf16(min) as stored (bf16
+ * round to nearest even), the code being rint((x - zero) / scale) in float32 against the
+ * stored values, clamped to 0..15 (0 when scale = 0). Keys: per channel over aligned
  * groups of 128 tokens (positions 128 g .. 128 g + 127). Values: per token over the channels.
  * The tokens of the last, incomplete group stay in dtype in a residual block until the group
- * completes. Per retrieval head, with G = ceil(capacity / 128) and P = max(8 d, 1024) G:
- *   K region: codes [128 G][d / 8] 32-bit words, then P bytes holding float32 [G][2][d]
- *             (scale row, zero row), then the residual [128][d] in dtype (row t % 128);
- *   V region: codes [G][d * 128 / 8] words, then P bytes holding float32 [128 G][2] (scale,
- *             zero per token), then the residual [128][d].
+ * completes. Per retrieval head, with G = ceil(capacity / 128) and P = max(4 d, 512) G:
+ *   K region: codes [128 G][d / 8] 32-bit words, then P bytes holding bf16 [G][2][d] (scale
+ *             row, zero row), then the residual [128][d] in dtype (row t % 128);
+ *   V region: codes [G][d * 128 / 8] words, then P bytes holding one word per token [128 G]
+ *             (bf16 scale in the low half, bf16 zero in the high half), then the residual.
  * A code word holds 8 codes, element e in bits 4e .. 4e + 3. Key row t: the word in slot
  * (d / 32) j + k holds channels 32 k + 8 j .. + 7 of token t. Value group g: word
  * (((c % 16) 4 + s) 4 + j) (d / 16) + c / 16 holds channel c of tokens 128 g + 32 s + 8 j .. + 7.
- * duo_attn_decode and duo_decode_step (run as append + decode) read them; duo_attn_prefill
- * and duo_attn_gate_mixed return DUO_ERR_UNSUPPORTED on a 4-bit cache. */
+ * duo_kv_append, duo_attn_decode and duo_decode_step handle them (a step whose token completes
+ * a group of some sequence runs as append + decode); duo_attn_prefill and duo_attn_gate_mixed
+ * return DUO_ERR_UNSUPPORTED on a 4-bit cache. */
 #define DUO_KV4_GROUP 128
 
 /* Byte offsets inside the caller's arena (all 256-byte aligned). Inside each cache region
@@ -218,7 +220,7 @@ duo_status duo_cache_lengths(const duo_cache* cache, int32_t* host_out);
  * (H_r * n + H_s * min(n, S + R)) * d * 2 * element size, summed over sequences (explainer,
  * "Decoding Procedure", memory formula). With 4-bit full caches the retrieval term is, per
  * head, the codes of the 128 floor(n / 128) grouped tokens (d bytes per token for K and V),
- * their parameters (8 d bytes per key group, 8 bytes per value token) and the residual tokens
+ * their parameters (4 d bytes per key group, 4 bytes per value token) and the residual tokens
  * in dtype. The second figure is also the K/V bytes one decode step of that layer reads.
  * Host only. */
 duo_status duo_kv_bytes(const duo_config* cfg, const int32_t* seq_lens, int32_t layer,

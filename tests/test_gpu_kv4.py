@@ -31,7 +31,7 @@ def kv4_cache(w, capacity, out_dtype=torch.float32, mask=None):
 def geom(cap, D):
     groups = -(-cap // QG)
     codes = groups * QG * D // 2
-    params = max(groups * 2 * D * 4, groups * QG * 2 * 4)
+    params = max(groups * 2 * D * 2, groups * QG * 4)
     resid = QG * D * 2
     return codes, params, resid, codes + params + resid
 
@@ -88,17 +88,18 @@ def check_stored(cache, w, lens):
                 x = W.tokens(w, "v" if is_v else "k", 0, b, 0, n)[:, j].astype(np.float32)
                 raw, codes_b, params_b = head_region(cache, is_v, b, r)
                 codes = unpack_values(raw, ng, D) if is_v else unpack_keys(raw, ng * QG, D)
-                par = raw[codes_b:codes_b + params_b].view(np.float32)
+                par = raw[codes_b:codes_b + params_b]
                 for g in range(ng):
                     blk = x[g * QG:(g + 1) * QG]
                     c, s, z = O.kv4_codes(blk, axis=1 if is_v else 0)
                     assert np.array_equal(codes[g * QG:(g + 1) * QG], c), (b, j, is_v, g)
-                    if is_v:
-                        got = par[2 * g * QG:2 * (g + 1) * QG].reshape(QG, 2)
-                    else:
-                        got = par[g * 2 * D:(g + 1) * 2 * D].reshape(2, D).T
-                    assert np.array_equal(got[:, 0].view(np.uint32), s.view(np.uint32)), (b, j, is_v, g)
-                    assert np.array_equal(got[:, 1].view(np.uint32), z.view(np.uint32)), (b, j, is_v, g)
+                    hi16 = lambda f: (f.view(np.uint32) >> 16).astype(np.uint16)  # noqa: E731
+                    if is_v:  # one word per token: bf16 scale low, bf16 zero high
+                        got = par.view(np.uint16)[2 * g * QG:2 * (g + 1) * QG].reshape(QG, 2)
+                    else:     # bf16 [2][D] per group
+                        got = par.view(np.uint16)[g * 2 * D:(g + 1) * 2 * D].reshape(2, D).T
+                    assert np.array_equal(got[:, 0], hi16(s)), (b, j, is_v, g)
+                    assert np.array_equal(got[:, 1], hi16(z)), (b, j, is_v, g)
                 res = raw[codes_b + params_b:].view(np.uint16).reshape(QG, D)
                 want = (x[ng * QG:n].view(np.uint32) >> 16).astype(np.uint16)
                 got_rows = res[np.arange(ng * QG, n) % QG]

@@ -91,7 +91,7 @@ def test_kv_bits_checked_and_kv4_layout():
     assert N.lib().duo_layout_query(ctypes.byref(cfg16), ctypes.byref(l16)) == N.DUO_OK
     cap, D, G = 1000, 128, N.KV4_GROUP
     groups = -(-cap // G)
-    stride = groups * G * D // 2 + max(groups * 2 * D * 4, groups * G * 8) + G * D * 2
+    stride = groups * G * D // 2 + max(groups * 2 * D * 2, groups * G * 4) + G * D * 2
     per_layer = [3 * 1 * stride, 3 * 1 * stride]  # batch 3, one retrieval head per layer
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     assert l4.full_v_off - l4.full_k_off == al(sum(al(x) for x in per_layer))
@@ -99,8 +99,8 @@ def test_kv_bits_checked_and_kv4_layout():
 
 
 def test_kv4_bytes_model():
-    """Per retrieval head: d bytes of K and V codes per grouped token, 8 d bytes of key
-    parameters per group, 8 bytes of value parameters per grouped token, residual tokens at
+    """Per retrieval head: d bytes of K and V codes per grouped token, 4 d bytes of key
+    parameters per group, 4 bytes of value parameters per grouped token, residual tokens at
     4 d bytes (bf16 K and V); streaming heads unchanged."""
     cfg, _keep = cfg_of(kv_bits=4)
     full, duo = ctypes.c_uint64(), ctypes.c_uint64()
@@ -112,7 +112,7 @@ def test_kv4_bytes_model():
         want = 0
         for n in lens:
             g, t = n // G, (n // G) * G
-            want += t * D + g * 8 * D + t * 8 + (n - t) * 4 * D  # one retrieval head
+            want += t * D + g * 4 * D + t * 4 + (n - t) * 4 * D  # one retrieval head
             want += 2 * min(n, S + R) * D * 2                    # one streaming head
         assert duo.value == want, lens
         assert full.value == sum(2 * 2 * n * D * 2 for n in lens)
