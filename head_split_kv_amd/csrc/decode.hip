@@ -437,12 +437,14 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
 
 // ---- 4-bit full caches -------------------------------------------------------------------
 // Complete groups of kQ4Group tokens of a retrieval head hold 4-bit codes, and both products
-// of a group run on MFMA (v_mfma_f32_16x16x32_f16): the logits S = Q' K^T of the G query heads
-// (rows, padded to 16) against 16 tokens, and O^T += V^T P'^T over 32 tokens for 16 channels.
-// Keys share per-channel (scale s_c, zero z_c) in a group, so S = sum_c (q_c s_c) k_c +
-// sum_c q_c z_c: the scales are folded into the query operand once per group and the zero
-// term is a per-row bias. Values carry per-token (s_t, z_t): O = sum_t (p_t s_t) v_t +
-// sum_t p_t z_t, the scales folded into the weights and the zero term one sum per row.
+// of a group run on MFMA (v_mfma_f32_16x16x32_f16): the logits, transposed, S^T = K Q'^T of 16
+// tokens against the G query heads (columns, padded to 16), and O^T += V^T P'^T over 32
+// tokens for 16 channels. Keys share per-channel (scale s_c, zero z_c) in a group, so
+// S = sum_c (q_c s_c) k_c + sum_c q_c z_c: the scales are folded into the query operand once
+// per group and the zero term is a per-column bias. Values carry per-token (s_t, z_t):
+// O = sum_t (p_t s_t) v_t + sum_t p_t z_t, the scales folded into the weights and the zero
+// term one sum per query. In the transposed layout a lane's logits are the weights its value
+// operand needs, so the softmax stays in registers.
 // Codes become fp16 operands with no conversion: masked in place, a code c reads as the fp16
 // denormal c 2^-24 (or 16 c 2^-24 for a high nibble), exact and taken as such by the matrix
 // unit; the partner operand carries 1/16 where the nibble was high and the products are
@@ -450,13 +452,13 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
 // 0, 4, 1, 5, 2, 6, 3, 7, which the partner operand follows. A wave streams whole groups in
 // steps of 32 tokens, one register slot per step, each refilled with the same step of the next
 // group as soon as it is used: three steps of codes and the next group's (bf16) key parameters
-// are in flight (a wave moves the bytes it has in flight per memory latency). Codes are stored in operand order (layout in duo.h): the KC key words of one token
-// that a lane needs are contiguous, and so are the D / 16 value words of one channel residue
-// and step, so every load moves whole lines. The incomplete last group (bf16
-// residual rows) and the streaming heads take the bf16 path over the 4 waves of one block.
+// are in flight (a wave moves the bytes it has in flight per memory latency). Codes are stored
+// in operand order (layout in duo.h): the KC key words of one token that a lane needs are
+// contiguous, and a wave's value words of a step are D / 64 contiguous KB, so every load
+// instruction reads one contiguous KB. The incomplete last group (bf16 residual rows) and the streaming
+// heads take the bf16 path over the 4 waves of one block.
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void lds_void_t;
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // Eight codes (byte i: element 2i in the low nibble, 2i + 1 in the high one) as fp16
@@ -464,7 +466,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // where kCodeHigh is set.
 constexpr int kCodeOrder[8] = {0, 4, 1, 5, 2, 6, 3, 7};
 constexpr bool kCodeHigh[8] = {false, false, true, true, false, false, true, true};
-// slot of element x: 2 (x mod 4) + x / 4, the inverse of kCodeOrder
+// (element x sits in slot 2 (x mod 4) + x / 4, the inverse of kCodeOrder)
 constexpr float kTwo24 = 16777216.f;
 __device__ __forceinline__ half8_t codes_to_f16(uint32_t w) {
   const uint32_t w8 = w >> 8;
@@ -472,25 +474,11 @@ __device__ __forceinline__ half8_t codes_to_f16(uint32_t w) {
   return __builtin_bit_cast(half8_t, r);
 }
 
-__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
-  return __builtin_bit_cast(float, (uint32_t)h << 16);
-}
+constexpr int kBfStages = 6;  // bf16 row fragments in flight in decode_q4_kernel
 
-// Maximum over each aligned group of 16 lanes (DPP, like group_sum<16>).
-__device__ __forceinline__ float row16_max(float x) {
-  x = fmaxf(x, dpp<0xB1>(x));
-  x = fmaxf(x, dpp<0x4E>(x));
-  x = fmaxf(x, dpp<0x141>(x));
-  x = fmaxf(x, dpp<0x128>(x));
-  return x;
-}
-
-// Order this wave's LDS writes before its following LDS reads (no other wave is involved).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
+// What a wave's look-ahead reads when it has no group there: always-valid memory that stays
+// in cache (the values are never used). 16 KB covers every offset a look-ahead adds.
+__device__ __attribute__((aligned(256))) uint32_t g_q4_idle[4096];
 
 template <int D, int G, int LPT, int NS>
 __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
@@ -512,13 +500,10 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
   __shared__ float s_m[2 * kWaves][G];
   __shared__ float s_l[2 * kWaves][G];
   __shared__ __attribute__((aligned(16))) uint16_t s_q[G][D];
-  __shared__ __attribute__((aligned(16))) _Float16 s_p[kWaves][16][kStep];  // P'^T per wave
-  __shared__ float s_x[kWaves][16];  // per-row scalars moved from the S to the O^T layout
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, grp = lane / LPT, sub = lane % LPT;
-  const int col = lane & 15;              // MFMA column: token of S, query of O^T
-  const int srow0 = 4 * (lane >> 4);      // first S row (query) held by this lane
+  const int col = lane & 15;              // MFMA column: the query of S^T and of O^T
 
   // ---- work item -------------------------------------------------------------------------
   // In a fused step (a.new_k != null) the token at p = a.n[b] - 1 is not in the cache yet and
@@ -568,108 +553,103 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
     vbase = (const char*)a.str_v + row0 * RB;
   }
   const int h0 = j * G;
-  {
-    const uint32_t* qw = (const uint32_t*)((const char*)a.q + ((int64_t)b * a.Hq + h0) * RB);
-    for (int w = tid; w < G * D / 2; w += kThreads) reinterpret_cast<uint32_t*>(&s_q[0][0])[w] = qw[w];
-  }
-  __syncthreads();
   const float c2 = a.scale_log2;
   const float inv_c2 = 1.f / c2;
 
   // ---- quantized groups on MFMA ------------------------------------------------------------
-  // S-layout state of rows srow0 + i: running maximum (log2 units), its raw-dot threshold,
-  // weight sum and value-zero sum. Rows past G never move their maximum (threshold +inf)
-  // and weigh exp2(x - 1e30) = 0.
-  float mq[4], thq[4], lq[4], zq[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bool live = srow0 + i < G;
-    mq[i] = live ? kMInit : 1e30f;
-    thq[i] = live ? kMInit : __builtin_inff();
-    lq[i] = zq[i] = 0.f;
-  }
+  // The logits come transposed, S^T = K' Q'^T: lane (col, jj = lane / 16) holds query col's
+  // logits of tokens 4 jj + i (tile 0) and 16 + 4 jj + i (tile 1), i = 0..3, of a 32-token
+  // step, which are the very weights its B operand of the value product takes (the value
+  // codes are stored in that token order), so P' never leaves the lane. State of query col,
+  // per lane: running maximum (log2 units, equal in the 4 lanes of col), its raw-product
+  // threshold, and this lane's parts of the weight sum and the value-zero sum. Columns past G
+  // carry a zero query, never move their maximum (threshold +inf) and weigh
+  // exp2(x - 1e30) = 0.
+  const int jj = lane >> 4;
+  const bool live = col < G;
+  float mq = live ? kMInit : 1e30f;
+  float thq = live ? kMInit : __builtin_inff();
+  float lq = 0.f, zq = 0.f;
   const float c2s = c2 * kTwo24;          // logit (log2 units) per unit of the raw product
   const float inv_c2s = 1.f / c2s;
-  f32x4_t oacc[CBK];  // O^T: lane holds channels 16 cb + srow0 + i of query col
+  f32x4_t oacc[CBK];  // O^T: lane holds channels 16 cb + 4 jj + i of query col
 #pragma unroll
   for (int cb = 0; cb < CBK; ++cb) oacc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int ng = ret ? n / kQ4Group : 0;
   const int n_split = ng > split ? (ng - 1 - split) / nsplit + 1 : 0;  // groups of the split
   const int n_wave = n_split > wave ? (n_split - 1 - wave) / kWaves + 1 : 0;
-  if (n_wave > 0) {
+  {
     auto group_of = [&](int i) {
       return split + nsplit * (wave + kWaves * (i < n_wave ? i : n_wave - 1));
     };
     const uint16_t* kpar = (const uint16_t*)(kq + a.q4_params);  // bf16 [group][2][D]
-    const uint32_t* vpar = (const uint32_t*)(vq + a.q4_params);  // [token]: bf16 scale | zero
-    // bf16 key scale and zero of this lane's A-operand channels 32 kc + 8 (lane / 16) + e
+    // bf16 key scale and zero of this lane's operand channels 32 kc + 8 jj + e
     uint4 ps[KC], pz[KC];
+    const char* idle = (const char*)g_q4_idle;
     auto load_params = [&](int gi) {
       const uint16_t* p = kpar + (int64_t)group_of(gi) * 2 * D;
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        const int ch = 32 * kc + 8 * (lane >> 4);
+        const int ch = 32 * kc + 8 * jj;
         ps[kc] = *(const uint4*)(p + ch);
         pz[kc] = *(const uint4*)(p + D + ch);
       }
     };
-    half8_t qa[KC];
-    f32x4_t bias4;
+    half8_t qa[KC];  // B operand: Q'^T, channel slots of query col
+    float bias;      // key-zero term of query col, in units of the raw product
     auto fold = [&]() {
-      float bp = 0.f;  // this lane's part of row col's bias
-      const float qlive = col < G ? 1.f : 0.f;  // rows past G carry a zero query
+      float bp = 0.f;  // this lane's part of query col's bias
+      const float qlive = live ? 1.f : 0.f;
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        // channels 32 kc + 8 (lane / 16) + 0..7 of query col, one 16-byte read
-        const uint4 qv = *(const uint4*)&s_q[col < G ? col : 0][32 * kc + 8 * (lane >> 4)];
+        // channels 32 kc + 8 jj + 0..7 of query col, one 16-byte read
+        const uint4 qv = *(const uint4*)&s_q[live ? col : 0][32 * kc + 8 * jj];
         const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
         const uint32_t sw[4] = {ps[kc].x, ps[kc].y, ps[kc].z, ps[kc].w};
         const uint32_t zw[4] = {pz[kc].x, pz[kc].y, pz[kc].z, pz[kc].w};
-        float sv[8], zv[8];
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          sv[2 * h] = __builtin_bit_cast(float, sw[h] << 16);
-          sv[2 * h + 1] = __builtin_bit_cast(float, sw[h] & 0xFFFF0000u);
-          zv[2 * h] = __builtin_bit_cast(float, zw[h] << 16);
-          zv[2 * h + 1] = __builtin_bit_cast(float, zw[h] & 0xFFFF0000u);
-        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int x = kCodeOrder[e];  // channel 32 kc + 8 (lane / 16) + x in operand slot e
-          const float qf =
-              qlive * __builtin_bit_cast(float, (x & 1) ? qw[x >> 1] & 0xFFFF0000u : qw[x >> 1] << 16);
-          qa[kc][e] = (_Float16)(qf * sv[x] * (kCodeHigh[e] ? 0.0625f : 1.f));
-          bp = __builtin_fmaf(qf, zv[x], bp);
+          const int x = kCodeOrder[e];  // channel 32 kc + 8 jj + x in operand slot e
+          const uint32_t hq = (x & 1) ? qw[x >> 1] & 0xFFFF0000u : qw[x >> 1] << 16;
+          const uint32_t hs = (x & 1) ? sw[x >> 1] & 0xFFFF0000u : sw[x >> 1] << 16;
+          const uint32_t hz = (x & 1) ? zw[x >> 1] & 0xFFFF0000u : zw[x >> 1] << 16;
+          const float qf = qlive * __builtin_bit_cast(float, hq);
+          qa[kc][e] = (_Float16)(qf * __builtin_bit_cast(float, hs) *
+                                 (kCodeHigh[e] ? 0.0625f : 1.f));
+          bp = __builtin_fmaf(qf, __builtin_bit_cast(float, hz), bp);
         }
       }
       bp += __shfl_xor(bp, 16);
       bp += __shfl_xor(bp, 32);
-      // the product accumulates in units of 2^-24: the bias enters in the same units
-#pragma unroll
-      for (int i = 0; i < 4; ++i) bias4[i] = __shfl(bp, srow0 + i) * (1.f / kTwo24);
+      bias = bp * (1.f / kTwo24);  // the product accumulates in units of 2^-24
     };
     struct Ld {
       uint32_t k[2][KC];  // key code words of the two 16-token tiles
       uint32_t v[CBK];    // value code words of the channel blocks
-      uint32_t vp[2];     // bf16 value scale and zero of token col of each tile
+      u32x4_t vp[2];      // bf16 value scale | zero of tokens 16 tau + 4 jj + 0..3
     };
-    // Past this wave's last group the look-ahead reads the first KB of the region's parameter
-    // block instead (cached, and the values are never used), so it costs no HBM traffic. The
-    // choice is an offset mask, not a branch: a branch would split the loop body and let the
-    // compiler move the last uses of a slot below its reload.
+    // Loads address a wave-uniform group base plus a constant 32-bit lane offset plus an
+    // immediate for the step and tile. Past this wave's last group the look-ahead reads the
+    // idle buffer instead (cached), so it costs no HBM traffic. The choice is a select of the
+    // base and of the lane offset, not a branch: a branch would split the loop body and let
+    // the compiler move the last uses of a slot below its reload.
     const int64_t q4p = a.q4_params;
-    auto pick = [](int64_t off, int64_t keep, int64_t alt) { return (off & keep) | (alt & ~keep); };
+    const uint32_t lk = col * CBY + jj * KC * 4;          // token col's key words of slice jj
+    const uint32_t lv = lane * 16;                         // this lane's 16 bytes of each KB
+    const uint32_t lp = 16 * jj;                           // value parameters of tokens 4 jj ..
+    const uint32_t lk_d = lk & 1023;
     auto load_step = [&](Ld& f, int gi, int st) {
-      const int64_t keep = gi < n_wave ? -1 : 0;  // wave-uniform
-      const int gg = group_of(gi);
-      const int64_t t0 = (int64_t)gg * kQ4Group + st * kStep;
-      const int j = lane >> 4;
+      const bool real = gi < n_wave;  // wave-uniform
+      const int64_t gg = group_of(gi);
+      const char* kb = real ? kq + gg * kQ4Group * CBY : idle;
+      const char* vb = real ? vq + gg * kQ4Group * CBY : idle;
+      const char* pb = real ? vq + q4p + gg * kQ4Group * 4 : idle;
+      const uint32_t ok = real ? lk : lk_d;
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau) {
-        // token t0 + 16 tau + col: words KC j .. KC j + KC - 1 of its row
-        const int64_t koff = (t0 + 16 * tau + col) * CBY + j * KC * 4;
-        const char* kr = kq + pick(koff, keep, q4p + (koff & 1023));
+        // token 32 st + 16 tau + col: words KC jj .. KC jj + KC - 1 of its row
+        const char* kr = kb + ok + (st * kStep + 16 * tau) * CBY;
         if constexpr (KC == 4) {
           const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kr));
           f.k[tau][0] = x.x; f.k[tau][1] = x.y; f.k[tau][2] = x.z; f.k[tau][3] = x.w;
@@ -677,15 +657,16 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
           const u32x2_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(kr));
           f.k[tau][0] = x.x; f.k[tau][1] = x.y;
         }
-        const int64_t poff = (t0 + 16 * tau + col) * 4;
-        f.vp[tau] = *(const uint32_t*)(vq + q4p + pick(poff, keep, poff & 1023));
+        // parameters of tokens 32 st + 16 tau + 4 jj .. + 3
+        f.vp[tau] = *(const u32x4_t*)(pb + lp + (st * kStep + 16 * tau) * 4);
       }
-      // channel residue col, step st, slice j: CBK words (channel blocks 0..CBK-1)
-      const int64_t voff = (int64_t)gg * kQ4Group * CBY + (((col * 4 + st) * 4 + j) * CBK) * 4;
-      const char* vr = vq + pick(voff, keep, q4p + (voff & 1023));
+      // step st: CBK / 4 contiguous KB, word w of this lane's 16 bytes in KB h is channel
+      // block 4 h + w
+      const char* vr = vb + lv + st * (CBK / 4) * 1024;
 #pragma unroll
       for (int h = 0; h < CBK / 4; ++h) {
-        const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vr) + h);
+        const u32x4_t x =
+            __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vr + h * 1024));
         f.v[4 * h] = x.x; f.v[4 * h + 1] = x.y; f.v[4 * h + 2] = x.z; f.v[4 * h + 3] = x.w;
       }
     };
@@ -693,80 +674,73 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
       f32x4_t sacc[2];
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau) {
-        sacc[tau] = bias4;
+        sacc[tau] = f32x4_t{bias, bias, bias, bias};
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc)
-          sacc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kc], codes_to_f16(f.k[tau][kc]),
+          sacc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_to_f16(f.k[tau][kc]), qa[kc],
                                                             sacc[tau], 0, 0, 0);
       }
-      // online softmax of rows srow0 + i over the 32 tokens (rows >= G stay empty)
-      // the common case compares each raw product with its row's threshold; only when one
-      // passes it does the wave take the row maxima over the 16 columns
-      float bm[4];
-      bool need = false;
+      // online softmax of query col over the 32 tokens: the common case compares the lane's
+      // largest raw product with the threshold; only when one passes it does the wave take
+      // the maxima over the 4 lanes of each column and rescale
+      float lm = sacc[0][0];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        bm[i] = fmaxf(sacc[0][i], sacc[1][i]);
-        need |= bm[i] > thq[i];
-      }
-      if (__ballot(need) != 0) {  // rare: move the running maxima, rescale the state
-        float al[4];
+      for (int i = 1; i < 4; ++i) lm = fmaxf(lm, sacc[0][i]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          bm[i] = row16_max(bm[i]);
-          al[i] = 1.f;
-          if (bm[i] > thq[i]) {
-            const float mn = bm[i] * c2s;
-            al[i] = fexp2(mq[i] - mn);
-            lq[i] *= al[i];
-            zq[i] *= al[i];
-            mq[i] = mn;
-            thq[i] = (mn + kTau) * inv_c2s;
-          }
-        }
-        if (col == 0)
+      for (int i = 0; i < 4; ++i) lm = fmaxf(lm, sacc[1][i]);
+      if (__ballot(lm > thq) != 0) {  // rare
+        float cm = fmaxf(lm, __shfl_xor(lm, 16));
+        cm = fmaxf(cm, __shfl_xor(cm, 32));
+        if (cm > thq) {
+          const float mn = cm * c2s;
+          const float al = fexp2(mq - mn);
+          lq *= al;
+          zq *= al;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) s_x[wave][srow0 + i] = al[i];
-        wave_lds_sync();
-        const float alc = s_x[wave][col];
-#pragma unroll
-        for (int cb = 0; cb < CBK; ++cb) oacc[cb] *= alc;
-        wave_lds_sync();
-      }
-      // token col of each tile goes to operand slot kCodeSlot[col % 8] of its 8 tokens,
-      // with 1/16 where that slot reads a high nibble (the odd tokens)
-      const int pslot = (col & ~7) + 2 * (col & 3) + ((col >> 2) & 1);
-      const float oddf = (col & 1) ? 0.0625f : 1.f;
-#pragma unroll
-      for (int tau = 0; tau < 2; ++tau) {
-        const float vs = __builtin_bit_cast(float, f.vp[tau] << 16) * oddf;
-        const float vz = __builtin_bit_cast(float, f.vp[tau] & 0xFFFF0000u);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = fexp2(__builtin_fmaf(sacc[tau][i], c2s, -mq[i]));
-          lq[i] += p;
-          zq[i] = __builtin_fmaf(p, vz, zq[i]);
-          s_p[wave][srow0 + i][16 * tau + pslot] = (_Float16)(p * vs);
+          for (int cb = 0; cb < CBK; ++cb) oacc[cb] *= al;
+          mq = mn;
+          thq = (mn + kTau) * inv_c2s;
         }
       }
-      wave_lds_sync();
-      const half8_t pb = *(const half8_t*)&s_p[wave][col][8 * (lane >> 4)];
+      // element x of a value word is token 16 (x / 4) + 4 jj + x % 4 and sits in operand slot
+      // 2 (x % 4) + x / 4, with 1/16 for the odd (high-nibble) elements
+      half8_t pb;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const int tau = x >> 2, i = x & 3;
+        const uint32_t w = f.vp[tau][i];
+        const float p = fexp2(__builtin_fmaf(sacc[tau][i], c2s, -mq));
+        lq += p;
+        zq = __builtin_fmaf(p, __builtin_bit_cast(float, w & 0xFFFF0000u), zq);
+        pb[2 * i + tau] =
+            (_Float16)(p * __builtin_bit_cast(float, w << 16) * ((x & 1) ? 0.0625f : 1.f));
+      }
 #pragma unroll
       for (int cb = 0; cb < CBK; ++cb)
         oacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_to_f16(f.v[cb]), pb, oacc[cb],
                                                           0, 0, 0);
-      wave_lds_sync();
     };
 
     // one register slot per step of a group: slot s is refilled with step s of the next
     // group right after use, so three steps of loads stay in flight
     static_assert(kSteps == 4, "one register slot per step of a group");
+    // The query first, on a quiet memory system (fetched together with every wave's first
+    // group, it waited behind that burst and the compute started later), then the first
+    // group's loads.
+    {
+      const uint32_t* qw = (const uint32_t*)((const char*)a.q + ((int64_t)b * a.Hq + h0) * RB);
+      for (int w = tid; w < G * D / 2; w += kThreads)
+        reinterpret_cast<uint32_t*>(&s_q[0][0])[w] = qw[w];
+    }
+    __syncthreads();
     Ld f0, f1, f2, f3;
-    load_params(0);
-    load_step(f0, 0, 0);
-    load_step(f1, 0, 1);
-    load_step(f2, 0, 2);
-    load_step(f3, 0, 3);
+    if (n_wave > 0) {
+      load_params(0);
+      load_step(f0, 0, 0);
+      load_step(f1, 0, 1);
+      load_step(f2, 0, 2);
+      load_step(f3, 0, 3);
+    }
     for (int gi = 0; gi < n_wave; ++gi) {
       fold();
       load_params(gi + 1);  // clamped past the last group
@@ -786,33 +760,24 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
       load_step(f3, gi + 1, 3);
     }
   }
-  // MFMA partial: row totals over the 16 columns; O^T column col gets its row's value-zero sum
+  // MFMA partial of query col: sums over the 4 lanes of the column; every channel of O^T gets
+  // the column's value-zero sum
   {
-    float addr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lq[i] = group_sum<16>(lq[i]);
-      addr[i] = group_sum<16>(zq[i]);
-    }
-    if (col == 0)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s_x[wave][srow0 + i] = addr[i];
-    wave_lds_sync();
-    const float add = s_x[wave][col];
-    if (col < G) {
+    lq += __shfl_xor(lq, 16);
+    lq += __shfl_xor(lq, 32);
+    zq += __shfl_xor(zq, 16);
+    zq += __shfl_xor(zq, 32);
+    if (live) {
 #pragma unroll
       for (int cb = 0; cb < CBK; ++cb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          s_o[kWaves + wave][col][16 * cb + srow0 + i] = __builtin_fmaf(oacc[cb][i], kTwo24, add);
+          s_o[kWaves + wave][col][16 * cb + 4 * jj + i] = __builtin_fmaf(oacc[cb][i], kTwo24, zq);
+      if (jj == 0) {
+        s_m[kWaves + wave][col] = mq;
+        s_l[kWaves + wave][col] = lq;
+      }
     }
-    if (col == 0)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (srow0 + i < G) {
-          s_m[kWaves + wave][srow0 + i] = mq[i];
-          s_l[kWaves + wave][srow0 + i] = lq[i];
-        }
   }
 
   // ---- bf16 rows: the residual group (its split only) or the streaming slots ---------------
@@ -874,17 +839,19 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
       return t < t1 && t != skip;
     };
     if (t1 > 0) {
-      F g0, g1, g2;
-      load_frag<T, D, LPT>(g0, kbase, vbase, row_of(0), sub);
-      load_frag<T, D, LPT>(g1, kbase, vbase, row_of(1), sub);
-      load_frag<T, D, LPT>(g2, kbase, vbase, row_of(2), sub);
-      for (int it = 0; it < n_it; it += 3) {
-        process(g0, valid_at(it));
-        load_frag<T, D, LPT>(g0, kbase, vbase, row_of(it + 3), sub);
-        process(g1, valid_at(it + 1));
-        load_frag<T, D, LPT>(g1, kbase, vbase, row_of(it + 4), sub);
-        process(g2, valid_at(it + 2));
-        load_frag<T, D, LPT>(g2, kbase, vbase, row_of(it + 5), sub);
+      // kBfStages row fragments in flight: this path runs after the MFMA loop, whose
+      // registers are free by then, and its blocks (a streaming head's S + R slots over 4
+      // waves) wait on memory once per kBfStages iterations
+      F g[kBfStages];
+#pragma unroll
+      for (int st = 0; st < kBfStages; ++st)
+        load_frag<T, D, LPT>(g[st], kbase, vbase, row_of(st), sub);
+      for (int it = 0; it < n_it; it += kBfStages) {
+#pragma unroll
+        for (int st = 0; st < kBfStages; ++st) {
+          process(g[st], valid_at(it + st));
+          load_frag<T, D, LPT>(g[st], kbase, vbase, row_of(it + st + kBfStages), sub);
+        }
       }
     }
     // fused step: the new token from the input, then its store (residual row or ring slot)
@@ -911,9 +878,11 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
       }
     }
   }
-  // lane groups of this wave -> s_*[wave]
+  // lane groups of this wave -> s_*[wave]; a block with no bf16 rows (nearly every retrieval
+  // block) skips the reduction and merges its MFMA partials alone
+  const bool bf16_rows = t1 > 0 || new_row >= 0;  // block-uniform
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
+  for (int g = 0; g < G && bf16_rows; ++g) {
     float mx = m[g];
     if constexpr (LPT == 8) mx = fmaxf(mx, dpp<0x128>(mx));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -948,12 +917,11 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
   // ---- merge the 2 x 4 partials; finish or write this split's partial ---------------------
   for (int idx = tid; idx < G * D; idx += kThreads) {
     const int g = idx / D, d = idx % D;
+    const int w0 = bf16_rows ? 0 : kWaves;
     float M = kMInit;
-#pragma unroll
-    for (int w = 0; w < 2 * kWaves; ++w) M = fmaxf(M, s_m[w][g]);
+    for (int w = w0; w < 2 * kWaves; ++w) M = fmaxf(M, s_m[w][g]);
     float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int w = 0; w < 2 * kWaves; ++w) {
+    for (int w = w0; w < 2 * kWaves; ++w) {
       const float sc = fexp2(s_m[w][g] - M);
       L += s_l[w][g] * sc;
       O += s_o[w][g][d] * sc;

@@ -42,8 +42,10 @@ __device__ __forceinline__ uint32_t code_of(float x, float mn, float scale) {
 // word holds 8 codes, element e in bits 4e .. 4e + 3.
 //   Keys: per token row, D / 8 words; the word in slot KC j + kc (KC = D / 32) holds channels
 //         32 kc + 8 j .. + 7, so the KC words one lane needs for a token are contiguous.
-//   Values: per group, word ((c % 16) 4 + s) 4 + j) (D / 16) + c / 16 holds channel c for tokens
-//         32 s + 8 j .. + 7, so the D / 16 words one lane needs for a step are contiguous.
+//   Values: per group, word ((s (D / 64) + h) 64 + l) 4 + w, with l = 16 j + (c % 16) and
+//         c / 16 = 4 h + w, holds channel c; its element e is token 32 s + 16 (e / 4) + 4 j +
+//         e % 4 (the tokens whose logits lane l of the transposed logit tile holds). A wave's
+//         value load for step s reads 1 KB contiguous per h.
 static_assert(kG == 128, "four 32-token steps per group");
 
 // Quantize the group staged in s (rows 0..kG-1, bf16) as keys: per channel over the rows.
@@ -113,17 +115,18 @@ __device__ void quantize_values(const uint16_t (*s)[D], uint8_t* codes, uint32_t
     }
   }
   __syncthreads();
-  constexpr int CBK = D / 16;
+  constexpr int kHalves = D / 64;  // 16-byte loads per lane and step
   uint32_t* cw = (uint32_t*)codes;
   for (int w = threadIdx.x; w < D * kG / 8; w += kThreads) {
-    int x = w / CBK;
-    const int cb = w % CBK, j = x % 4;
-    x /= 4;
-    const int st = x % 4, c = 16 * cb + x / 4, t0 = 32 * st + 8 * j;
+    const int l = (w >> 2) & 63, x = w >> 8;
+    const int h = x % kHalves, st = x / kHalves, j = l >> 4;
+    const int c = 16 * (4 * h + (w & 3)) + (l & 15), t0 = 32 * st + 4 * j;
     uint32_t word = 0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      word |= code_of(bf16_to_f32(s[t0 + e][c]), sp[2 * (t0 + e) + 1], sp[2 * (t0 + e)]) << (4 * e);
+    for (int e = 0; e < 8; ++e) {
+      const int t = t0 + 16 * (e >> 2) + (e & 3);
+      word |= code_of(bf16_to_f32(s[t][c]), sp[2 * t + 1], sp[2 * t]) << (4 * e);
+    }
     cw[w] = word;
   }
 }

@@ -99,7 +99,8 @@ typedef struct {
  *             (bf16 scale in the low half, bf16 zero in the high half), then the residual.
  * A code word holds 8 codes, element e in bits 4e .. 4e + 3. Key row t: the word in slot
  * (d / 32) j + k holds channels 32 k + 8 j .. + 7 of token t. Value group g: word
- * (((c % 16) 4 + s) 4 + j) (d / 16) + c / 16 holds channel c of tokens 128 g + 32 s + 8 j .. + 7.
+ * ((s (d / 64) + h) 64 + 16 j + c % 16) 4 + w, with c / 16 = 4 h + w, holds channel c; its
+ * element e is token 128 g + 32 s + 16 (e / 4) + 4 j + e % 4.
  * duo_kv_append, duo_attn_decode and duo_decode_step handle them (a step whose token completes
  * a group of some sequence runs as append + decode); duo_attn_prefill and duo_attn_gate_mixed
  * return DUO_ERR_UNSUPPORTED on a 4-bit cache. */

@@ -62,17 +62,20 @@ def unpack_keys(code_bytes, rows, D):
 
 
 def unpack_values(code_bytes, groups, D):
-    """Value codes [groups * QG][D]: word (((c % 16) 4 + s) 4 + j) (D / 16) + c / 16 of a group
-    holds channel c of tokens 32 s + 8 j .. + 7."""
-    CBK = D // 16
-    w = code_bytes[:groups * QG * D // 2].view(np.uint32).reshape(groups, 16, 4, 4, CBK)
+    """Value codes [groups * QG][D]: word ((s (D / 64) + h) 64 + 16 j + c % 16) 4 + w of a group,
+    with c / 16 = 4 h + w, holds channel c; its element e is token 32 s + 16 (e / 4) + 4 j +
+    e % 4."""
+    halves = D // 64
+    w = code_bytes[:groups * QG * D // 2].view(np.uint32).reshape(groups, 4, halves, 4, 16, 4)
     out = np.empty((groups, QG, D), dtype=np.uint8)
-    for cl in range(16):
-        for s in range(4):
+    e = np.arange(8)
+    for s in range(4):
+        for h in range(halves):
             for j in range(4):
-                for cb in range(CBK):
-                    t0 = 32 * s + 8 * j
-                    out[:, t0:t0 + 8, 16 * cb + cl] = nibbles(w[:, cl, s, j, cb])
+                toks = 32 * s + 16 * (e // 4) + 4 * j + e % 4
+                for cl in range(16):
+                    for ww in range(4):
+                        out[:, toks, 16 * (4 * h + ww) + cl] = nibbles(w[:, s, h, j, cl, ww])
     return out.reshape(groups * QG, D)
 
 
