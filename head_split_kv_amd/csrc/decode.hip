@@ -42,6 +42,35 @@ __device__ __forceinline__ float dpp(float x) {
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Butterflies across the 16-lane rows on the VALU (no LDS): v_permlane16_swap (32_swap) with
+// x in both operands returns x and its partner at lane ^ 16 (^ 32), in an order that depends
+// on the row, so the sum (maximum) of the two results is the butterfly, the same on both
+// partners.
+__device__ __forceinline__ float xor16_sum(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const unsigned r0 = r[0], r1 = r[1];  // (bit_cast of a vector element misreads element 1)
+  return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const unsigned r0 = r[0], r1 = r[1];  // (bit_cast of a vector element misreads element 1)
+  return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ float xor16_max(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const unsigned r0 = r[0], r1 = r[1];  // (bit_cast of a vector element misreads element 1)
+  return fmaxf(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const unsigned r0 = r[0], r1 = r[1];  // (bit_cast of a vector element misreads element 1)
+  return fmaxf(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   uint32_t u = __builtin_bit_cast(uint32_t, f);
   u += 0x7FFFu + ((u >> 16) & 1u);
@@ -377,19 +406,19 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
   for (int g = 0; g < G; ++g) {
     float mx = m[g];
     if constexpr (LPT == 8) mx = fmaxf(mx, dpp<0x128>(mx));  // row_ror:8 -> lane ^ 8
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = xor16_max(mx);
+    mx = xor32_max(mx);
     const float sc = fexp2(m[g] - mx);
     float lg = l[g] * sc;
     if constexpr (LPT == 8) lg += dpp<0x128>(lg);
-    lg += __shfl_xor(lg, 16);
-    lg += __shfl_xor(lg, 32);
+    lg = xor16_sum(lg);
+    lg = xor32_sum(lg);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       float x = o[g][e] * sc;
       if constexpr (LPT == 8) x += dpp<0x128>(x);
-      x += __shfl_xor(x, 16);
-      x += __shfl_xor(x, 32);
+      x = xor16_sum(x);
+      x = xor32_sum(x);
       o[g][e] = x;
     }
     if (grp == 0) {
@@ -620,8 +649,8 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
           bp = __builtin_fmaf(qf, __builtin_bit_cast(float, hz), bp);
         }
       }
-      bp += __shfl_xor(bp, 16);
-      bp += __shfl_xor(bp, 32);
+      bp = xor16_sum(bp);
+      bp = xor32_sum(bp);
       bias = bp * (1.f / kTwo24);  // the product accumulates in units of 2^-24
     };
     struct Ld {
@@ -689,8 +718,8 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) lm = fmaxf(lm, sacc[1][i]);
       if (__ballot(lm > thq) != 0) {  // rare
-        float cm = fmaxf(lm, __shfl_xor(lm, 16));
-        cm = fmaxf(cm, __shfl_xor(cm, 32));
+        float cm = xor16_max(lm);
+        cm = xor32_max(cm);
         if (cm > thq) {
           const float mn = cm * c2s;
           const float al = fexp2(mq - mn);
@@ -763,10 +792,10 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
   // MFMA partial of query col: sums over the 4 lanes of the column; every channel of O^T gets
   // the column's value-zero sum
   {
-    lq += __shfl_xor(lq, 16);
-    lq += __shfl_xor(lq, 32);
-    zq += __shfl_xor(zq, 16);
-    zq += __shfl_xor(zq, 32);
+    lq = xor16_sum(lq);
+    lq = xor32_sum(lq);
+    zq = xor16_sum(zq);
+    zq = xor32_sum(zq);
     if (live) {
 #pragma unroll
       for (int cb = 0; cb < CBK; ++cb)
@@ -885,19 +914,19 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
   for (int g = 0; g < G && bf16_rows; ++g) {
     float mx = m[g];
     if constexpr (LPT == 8) mx = fmaxf(mx, dpp<0x128>(mx));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = xor16_max(mx);
+    mx = xor32_max(mx);
     const float sc = fexp2(m[g] - mx);
     float lg = l[g] * sc;
     if constexpr (LPT == 8) lg += dpp<0x128>(lg);
-    lg += __shfl_xor(lg, 16);
-    lg += __shfl_xor(lg, 32);
+    lg = xor16_sum(lg);
+    lg = xor32_sum(lg);
 #pragma unroll
     for (int e = 0; e < Geo::kE; ++e) {
       float x = o[g][e] * sc;
       if constexpr (LPT == 8) x += dpp<0x128>(x);
-      x += __shfl_xor(x, 16);
-      x += __shfl_xor(x, 32);
+      x = xor16_sum(x);
+      x = xor32_sum(x);
       o[g][e] = x;
     }
     if (grp == 0) {
