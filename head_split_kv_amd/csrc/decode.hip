@@ -18,6 +18,8 @@
 // retrieval head by a second, small kernel with the log-sum-exp weights exp2(m_i - m).
 #include <hip/hip_runtime.h>
 
+#include <cstring>
+
 #include "duo_internal.h"
 
 namespace duo {
@@ -541,8 +543,8 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
   const bool fused = a.new_k != nullptr;
   const int64_t n_ret_items = (int64_t)a.B * a.Hr * a.nsplit;
   const bool ret = (int64_t)blockIdx.x < n_ret_items;
-  int b, j, split, nsplit, n;  // n: tokens in the cache
-  int new_row = -1, skip = -1;
+  int b, j, split, nsplit, n;  // n: tokens in the cache (streaming: slots of this block)
+  int new_row = -1, skip = -1, r0 = 0;  // r0: first bf16 row of this block
   const char* kq = nullptr;  // retrieval head: K region (codes, parameters, residual)
   const char* vq = nullptr;
   const char* kbase;         // bf16 rows: the residual group, or the streaming slots
@@ -562,21 +564,28 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
     kbase = kq + a.q4_resid;
     vbase = vq + a.q4_resid;
   } else {
+    // a streaming head's window is cut over a.nss blocks; the last one takes the fused
+    // step's token
     const int64_t i = blockIdx.x - n_ret_items;
-    const int cls = (int)(i % a.Hs);
-    b = (int)(i / a.Hs);
+    nsplit = a.nss;
+    split = (int)(i % nsplit);
+    const int cls = (int)((i / nsplit) % a.Hs);
+    b = (int)(i / ((int64_t)nsplit * a.Hs));
     j = a.str_kv[cls];
-    split = 0;
-    nsplit = 1;
     const int SR = a.S + a.R;
+    int nw;  // held slots of the window
     if (!fused) {
-      n = min(a.n[b], SR);
+      nw = min(a.n[b], SR);
     } else {
       const int pnew = a.n[b] - 1;
-      new_row = pnew < a.S ? pnew : a.S + (pnew - a.S) % a.R;
-      n = min(pnew, SR);
-      if (pnew >= SR) skip = new_row;  // the evicted token p - R, outside the window
+      const int slot = pnew < a.S ? pnew : a.S + (pnew - a.S) % a.R;
+      nw = min(pnew, SR);
+      if (pnew >= SR) skip = slot;  // the evicted token p - R, outside the window
+      if (split == nsplit - 1) new_row = slot;
     }
+    const int per = (nw + nsplit - 1) / nsplit;
+    r0 = min(nw, split * per);
+    n = min(nw, r0 + per) - r0;
     const int64_t row0 = ((int64_t)b * a.Hs + cls) * SR;
     kbase = (const char*)a.str_k + row0 * RB;
     vbase = (const char*)a.str_v + row0 * RB;
@@ -605,13 +614,16 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
 #pragma unroll
   for (int cb = 0; cb < CBK; ++cb) oacc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // Groups of a retrieval head: chunks of kWaves consecutive groups are dealt round-robin
+  // to the splits, and wave w of a split takes group w of each of its chunks, so the blocks
+  // of a head read neighbouring groups at any time.
   const int ng = ret ? n / kQ4Group : 0;
-  const int n_split = ng > split ? (ng - 1 - split) / nsplit + 1 : 0;  // groups of the split
-  const int n_wave = n_split > wave ? (n_split - 1 - wave) / kWaves + 1 : 0;
+  const int n_wave =
+      ng > kWaves * split + wave ? (ng - 1 - kWaves * split - wave) / (kWaves * nsplit) + 1 : 0;
+  auto group_of = [&](int i) {  // clamped past the last group
+    return (split + nsplit * (i < n_wave ? i : n_wave - 1)) * kWaves + wave;
+  };
   {
-    auto group_of = [&](int i) {
-      return split + nsplit * (wave + kWaves * (i < n_wave ? i : n_wave - 1));
-    };
     const uint16_t* kpar = (const uint16_t*)(kq + a.q4_params);  // bf16 [group][2][D]
     // bf16 key scale and zero of this lane's operand channels 32 kc + 8 jj + e
     uint4 ps[KC], pz[KC];
@@ -861,11 +873,11 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
     const int n_it = (t1 + kTpb - 1) / kTpb;
     auto row_of = [&](int it) -> int64_t {
       const int t = it * kTpb + wave * kTpw + grp;
-      return (int64_t)(t < t1 ? t : t1 - 1);
+      return (int64_t)r0 + (t < t1 ? t : t1 - 1);
     };
     auto valid_at = [&](int it) {
       const int t = it * kTpb + wave * kTpw + grp;
-      return t < t1 && t != skip;
+      return t < t1 && r0 + t != skip;
     };
     if (t1 > 0) {
       // kBfStages row fragments in flight: this path runs after the MFMA loop, whose
@@ -971,7 +983,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
   }
 }
 
-// Merge of the context splits of one retrieval query head (sequence b, head h) over 64
+// Merge of the context splits of one query head (sequence b, head h) over 64
 // output columns: M = max_s m_s, L = sum_s l_s exp2(m_s - M), out = sum_s o_s exp2(m_s - M)
 // / L, lse = (M + log2 L) ln 2. Each of the 8 waves takes every 8th split with an online
 // log-sum-exp, issuing the loads of kMergeBatch splits together, and the waves combine
@@ -988,12 +1000,18 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(DecodeArgs a) {
   constexpr int kSlices = D / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int slice = blockIdx.x % kSlices;
-  const int qi = blockIdx.x / kSlices;  // (b, retrieval index, g)
+  // (b, retrieval index, g) of the split retrieval heads, then (b, streaming index, g) of the
+  // split streaming heads
+  const int n_ret_q = a.nsplit > 1 ? a.B * a.Hr * G : 0;
+  int qi = blockIdx.x / kSlices;
+  const bool ret = qi < n_ret_q;
+  if (!ret) qi -= n_ret_q;
+  const int Hc = ret ? a.Hr : a.Hs;
   const int g = qi % G;
-  const int r = (qi / G) % a.Hr;
-  const int b = qi / (G * a.Hr);
-  const int h = a.ret_kv[r] * G + g;
-  const int nsplit = a.nsplit;
+  const int r = (qi / G) % Hc;
+  const int b = qi / (G * Hc);
+  const int h = (ret ? a.ret_kv[r] : a.str_kv[r]) * G + g;
+  const int nsplit = ret ? a.nsplit : a.nss;
   const int64_t p0 = ((int64_t)b * a.Hq + h) * a.max_splits;
   const int d = slice * 64 + lane;
   const float* po = a.part_o + p0 * D + d;
@@ -1052,26 +1070,28 @@ struct Variant {
   static constexpr int LPT = lanes_per_token<T, D, G>();
   static constexpr int NS = stages<T, D, G>();
 
-  // Decode blocks that fit on the device at once, queried once per process.
-  static int resident_blocks() {
-    static int cached = 0;
-    if (cached) return cached;
+  // Decode blocks that fit on the device at once (of the 4-bit kernel when q4), queried
+  // once per process.
+  static int resident_blocks(bool q4) {
+    static int cached[2] = {0, 0};
+    if (cached[q4]) return cached[q4];
+    const void* fn = reinterpret_cast<const void*>(&decode_kernel<T, D, G, LPT, NS>);
+    if constexpr (sizeof(T) == 2)
+      if (q4) fn = reinterpret_cast<const void*>(&decode_q4_kernel<D, G, LPT, 4>);
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(&decode_kernel<T, D, G, LPT, NS>), kThreads,
-            0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0) != hipSuccess ||
         cus <= 0 || per_cu <= 0) {
       (void)hipGetLastError();
       return 512;
     }
-    cached = cus * per_cu;
-    return cached;
+    cached[q4] = cus * per_cu;
+    return cached[q4];
   }
 
   static int launch(const DecodeArgs& a, void* stream, const KernelMarks& marks) {
-    const int64_t blocks = (int64_t)a.B * a.Hr * a.nsplit + (int64_t)a.B * a.Hs;
+    const int64_t blocks = (int64_t)a.B * a.Hr * a.nsplit + (int64_t)a.B * a.Hs * a.nss;
     if (marks.begin) (void)hipEventRecord((hipEvent_t)marks.begin, (hipStream_t)stream);
     if constexpr (sizeof(T) == 2) {
       if (a.q4)
@@ -1086,8 +1106,10 @@ struct Variant {
                          dim3(kThreads), 0, (hipStream_t)stream, a);
     }
     if (marks.end) (void)hipEventRecord((hipEvent_t)marks.end, (hipStream_t)stream);
-    if (a.nsplit > 1 && a.Hr > 0) {
-      const int64_t mblocks = (int64_t)a.B * a.Hr * G * (D / 64);
+    // split heads (retrieval heads when nsplit > 1, streaming heads when nss > 1)
+    const int64_t mheads = (a.nsplit > 1 ? (int64_t)a.Hr : 0) + (a.nss > 1 ? (int64_t)a.Hs : 0);
+    if (mheads > 0) {
+      const int64_t mblocks = (int64_t)a.B * mheads * G * (D / 64);
       hipLaunchKernelGGL((merge_kernel<T, D, G>), dim3((unsigned)mblocks),
                          dim3(kMergeThreads), 0, (hipStream_t)stream, a);
     }
@@ -1097,7 +1119,7 @@ struct Variant {
 
 template <typename T, int D, int G>
 int run(bool query, const DecodeArgs* a, void* stream, const KernelMarks* marks) {
-  return query ? Variant<T, D, G>::resident_blocks()
+  return query ? Variant<T, D, G>::resident_blocks(a != nullptr && a->q4 != 0)
                : Variant<T, D, G>::launch(*a, stream, *marks);
 }
 
@@ -1131,8 +1153,11 @@ int launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group, void*
   return dispatch(dtype, head_dim, group, false, &a, stream, &marks);
 }
 
-int decode_resident_blocks(int dtype, int head_dim, int group) {
-  return dispatch(dtype, head_dim, group, true, nullptr, nullptr, nullptr);
+int decode_resident_blocks(int dtype, int head_dim, int group, bool q4) {
+  DecodeArgs probe;  // only q4 is read
+  std::memset(&probe, 0, sizeof(probe));
+  probe.q4 = q4 ? 1 : 0;
+  return dispatch(dtype, head_dim, group, true, &probe, nullptr, nullptr);
 }
 
 }  // namespace duo

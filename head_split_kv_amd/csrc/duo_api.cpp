@@ -124,16 +124,24 @@ duo_status decode_impl(duo_cache* c, int32_t layer, const void* q, const void* k
   a.R = c->cfg.recent;
   a.max_splits = c->cfg.max_splits;
   const int group = c->cfg.num_q_heads / c->cfg.num_kv_heads;
+  const bool q4 = c->cfg.kv_bits == 4;
+  // 4-bit caches: a streaming head's window is cut over up to 8 blocks of ~128 slots, so that
+  // it is done long before the retrieval groups
+  a.nss = 1;
+  if (q4 && a.Hs > 0) {
+    const int32_t rows = std::min(n_max, c->cfg.sink + c->cfg.recent);
+    a.nss = std::max(1, std::min({8, (rows + 127) / 128, (int)c->cfg.max_splits}));
+  }
   a.nsplit = c->force_splits
                  ? c->force_splits
-                 : choose_decode_splits(n_max, a.B, a.Hr, a.Hs, a.max_splits,
+                 : choose_decode_splits(n_max, a.B, a.Hr, a.Hs * a.nss, a.max_splits,
                                         decode_resident_blocks(c->cfg.dtype, c->cfg.head_dim,
-                                                               group));
+                                                               group, q4));
   a.scale_log2 = (float)((double)c->scale * 1.4426950408889634);
   a.out_f32 = c->cfg.out_dtype == DUO_F32;
   std::memcpy(a.ret_kv, li.ret_kv, sizeof(a.ret_kv));
   std::memcpy(a.str_kv, li.str_kv, sizeof(a.str_kv));
-  if (c->cfg.kv_bits == 4) {
+  if (q4) {
     const Q4Geom g = q4_geom(c->cfg.capacity, c->cfg.head_dim);
     a.q4 = 1;
     a.q4_stride = (int64_t)g.stride;

@@ -105,8 +105,9 @@ struct DecodeArgs {
   int32_t B, Hq, Hkv, Hr, Hs, cap, S, R, nsplit, max_splits;
   float scale_log2;        // softmax scale * log2(e)
   int32_t out_f32;
-  int32_t q4;              // full caches in 4 bits (Q4Geom offsets below); no fused step
+  int32_t q4;              // full caches in 4 bits (Q4Geom offsets below)
   int64_t q4_stride, q4_params, q4_resid;
+  int32_t nss;             // blocks per streaming head (4-bit kernel; 1 otherwise)
   uint8_t ret_kv[kMaxKvHeads];
   uint8_t str_kv[kMaxKvHeads];
   int32_t n[kMaxBatch];    // length of every sequence, the fused step's token included
@@ -178,8 +179,9 @@ int record_event(void* event, void* stream);
 // Sum of the elapsed times of the pairs (ev[2i], ev[2i+1]), i < pairs, after waiting for
 // the last one.
 int pairs_elapsed_ms(const std::vector<void*>& ev, int pairs, double* total_ms);
-// Decode blocks of this variant that are resident on the device at once (512 if unknown).
-int decode_resident_blocks(int dtype, int head_dim, int group);
+// Decode blocks of this variant (the 4-bit kernel when q4) that are resident on the device
+// at once (512 if unknown).
+int decode_resident_blocks(int dtype, int head_dim, int group, bool q4);
 // Prefill blocks of this variant that are resident on the device at once (512 if unknown).
 int prefill_resident_blocks(int head_dim, int group);
 

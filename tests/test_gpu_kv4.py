@@ -215,6 +215,17 @@ def test_kv4_decode_split_counts(splits):
     run_decode_kv4(w, [9 * QG + 50], 2, splits=splits)
 
 
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("n0", [300, 1000])
+def test_kv4_decode_streaming_slices(fused, n0):
+    """A streaming window of 4 + 500 slots is cut over several blocks (merged like retrieval
+    splits): before the ring wraps and after, the fused step's token taken by the last block
+    and the evicted slot skipped by every block."""
+    w = W.Workload("kv4-slices", 1, 1, 16, 4, 64, "bf16", 4, 500, 0, 0, 2,
+                   fixed_mask=((1, 2),), seed=119)
+    run_decode_kv4(w, [n0], 3, fused=fused)
+
+
 def test_kv4_decode_ragged_batch_bf16_out_and_streaming_only():
     w = W.Workload("kv4-ragged", 1, 3, 32, 8, 128, "bf16", 16, 64, 0, 0, 4, seed=111)
     run_decode_kv4(w, [700, 129, 1500], 2, out_dtype=torch.bfloat16)
