@@ -139,8 +139,10 @@ duo_status decode_impl(duo_cache* c, int32_t layer, const void* q, const void* k
                                                                group, q4));
   a.scale_log2 = (float)((double)c->scale * 1.4426950408889634);
   a.out_f32 = c->cfg.out_dtype == DUO_F32;
-  std::memcpy(a.ret_kv, li.ret_kv, sizeof(a.ret_kv));
-  std::memcpy(a.str_kv, li.str_kv, sizeof(a.str_kv));
+  for (int k = 0; k < kMaxKvHeads; ++k) {
+    a.ret_kv[k] = li.ret_kv[k];
+    a.str_kv[k] = li.str_kv[k];
+  }
   if (q4) {
     const Q4Geom g = q4_geom(c->cfg.capacity, c->cfg.head_dim);
     a.q4 = 1;

@@ -108,8 +108,10 @@ struct DecodeArgs {
   int32_t q4;              // full caches in 4 bits (Q4Geom offsets below)
   int64_t q4_stride, q4_params, q4_resid;
   int32_t nss;             // blocks per streaming head (4-bit kernel; 1 otherwise)
-  uint8_t ret_kv[kMaxKvHeads];
-  uint8_t str_kv[kMaxKvHeads];
+  // KV head of each retrieval / streaming index, as 32-bit words: a block reads its entry with
+  // a scalar load (a byte would take a vector load, whose latency delays every first load)
+  int32_t ret_kv[kMaxKvHeads];
+  int32_t str_kv[kMaxKvHeads];
   int32_t n[kMaxBatch];    // length of every sequence, the fused step's token included
 };
 
