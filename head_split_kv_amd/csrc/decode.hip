@@ -537,27 +537,42 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
   const int col = lane & 15;              // MFMA column: the query of S^T and of O^T
 
   // ---- work item -------------------------------------------------------------------------
-  // In a fused step (a.new_k != null) the token at p = a.n[b] - 1 is not in the cache yet and
-  // completes no group: the block that reads the residual (or the streaming slots) also takes
-  // it from the input and then stores it, as in decode_kernel.
+  // Blocks: the quantized groups of every (sequence, retrieval head) over a.nsplit splits;
+  // one block per (sequence, retrieval head) for its bf16 residual rows, which starts
+  // reading them at once instead of after some split's groups; then the streaming windows,
+  // each over a.nss blocks. A retrieval head's partials are its nsplit splits plus the
+  // residual block's. In a fused step (a.new_k != null) the token at p = a.n[b] - 1 is not
+  // in the cache yet and completes no group: the residual block (or the last block of the
+  // streaming window) also takes it from the input and then stores it, as in decode_kernel.
   const bool fused = a.new_k != nullptr;
   const int64_t n_ret_items = (int64_t)a.B * a.Hr * a.nsplit;
+  const int64_t n_res_items = (int64_t)a.B * a.Hr;
   const bool ret = (int64_t)blockIdx.x < n_ret_items;
-  int b, j, split, nsplit, n;  // n: tokens in the cache (streaming: slots of this block)
+  const bool res = !ret && (int64_t)blockIdx.x < n_ret_items + n_res_items;
+  int b, j, split, nsplit, nparts, n;  // n: tokens in the cache (streaming: slots of this block)
   int new_row = -1, skip = -1, r0 = 0;  // r0: first bf16 row of this block
   const char* kq = nullptr;  // retrieval head: K region (codes, parameters, residual)
   const char* vq = nullptr;
   const char* kbase;         // bf16 rows: the residual group, or the streaming slots
   const char* vbase;
-  if (ret) {
-    const int64_t i = blockIdx.x;
-    split = (int)(i % a.nsplit);
-    const int cls = (int)((i / a.nsplit) % a.Hr);
-    b = (int)(i / ((int64_t)a.nsplit * a.Hr));
+  if (ret || res) {
+    int cls;
+    if (ret) {
+      const int64_t i = blockIdx.x;
+      split = (int)(i % a.nsplit);
+      cls = (int)((i / a.nsplit) % a.Hr);
+      b = (int)(i / ((int64_t)a.nsplit * a.Hr));
+    } else {
+      const int64_t i = blockIdx.x - n_ret_items;
+      split = a.nsplit;  // the partial after the splits'
+      cls = (int)(i % a.Hr);
+      b = (int)(i / a.Hr);
+    }
     j = a.ret_kv[cls];
     nsplit = a.nsplit;
+    nparts = a.nsplit + 1;
     n = fused ? a.n[b] - 1 : a.n[b];
-    if (fused && (n / kQ4Group) % nsplit == split) new_row = n % kQ4Group;
+    if (res && fused) new_row = n % kQ4Group;
     const int64_t head = ((int64_t)b * a.Hr + cls) * a.q4_stride;
     kq = (const char*)a.full_k + head;
     vq = (const char*)a.full_v + head;
@@ -566,8 +581,8 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
   } else {
     // a streaming head's window is cut over a.nss blocks; the last one takes the fused
     // step's token
-    const int64_t i = blockIdx.x - n_ret_items;
-    nsplit = a.nss;
+    const int64_t i = blockIdx.x - n_ret_items - n_res_items;
+    nsplit = nparts = a.nss;
     split = (int)(i % nsplit);
     const int cls = (int)((i / nsplit) % a.Hs);
     b = (int)(i / ((int64_t)nsplit * a.Hs));
@@ -831,7 +846,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < Geo::kE; ++e) o[g][e] = 0.f;
   }
-  const int t1 = ret ? ((ng % nsplit) == split ? n - ng * kQ4Group : 0) : n;
+  const int t1 = ret ? 0 : (res ? n % kQ4Group : n);
   if (t1 > 0 || new_row >= 0) {
     QRegs<T, D, G, LPT> q;
 #pragma unroll
@@ -968,7 +983,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
       O += s_o[w][g][d] * sc;
     }
     const int h = h0 + g;
-    if (nsplit == 1) {
+    if (nparts == 1) {
       const int64_t oi = ((int64_t)b * a.Hq + h) * D + d;
       store_out<T>(a.out, oi, O / L, a.out_f32);
       if (d == 0 && a.lse) a.lse[(int64_t)b * a.Hq + h] = (M + __builtin_log2f(L)) * kLn2;
@@ -1002,7 +1017,8 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(DecodeArgs a) {
   const int slice = blockIdx.x % kSlices;
   // (b, retrieval index, g) of the split retrieval heads, then (b, streaming index, g) of the
   // split streaming heads
-  const int n_ret_q = a.nsplit > 1 ? a.B * a.Hr * G : 0;
+  const int ret_parts = a.nsplit + (a.q4 ? 1 : 0);  // 4-bit: plus the residual block's
+  const int n_ret_q = ret_parts > 1 ? a.B * a.Hr * G : 0;
   int qi = blockIdx.x / kSlices;
   const bool ret = qi < n_ret_q;
   if (!ret) qi -= n_ret_q;
@@ -1011,7 +1027,7 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(DecodeArgs a) {
   const int r = (qi / G) % Hc;
   const int b = qi / (G * Hc);
   const int h = (ret ? a.ret_kv[r] : a.str_kv[r]) * G + g;
-  const int nsplit = ret ? a.nsplit : a.nss;
+  const int nsplit = ret ? ret_parts : a.nss;
   const int64_t p0 = ((int64_t)b * a.Hq + h) * a.max_splits;
   const int d = slice * 64 + lane;
   const float* po = a.part_o + p0 * D + d;
@@ -1091,7 +1107,8 @@ struct Variant {
   }
 
   static int launch(const DecodeArgs& a, void* stream, const KernelMarks& marks) {
-    const int64_t blocks = (int64_t)a.B * a.Hr * a.nsplit + (int64_t)a.B * a.Hs * a.nss;
+    const int64_t blocks = (int64_t)a.B * a.Hr * a.nsplit + (a.q4 ? (int64_t)a.B * a.Hr : 0) +
+                           (int64_t)a.B * a.Hs * a.nss;
     if (marks.begin) (void)hipEventRecord((hipEvent_t)marks.begin, (hipStream_t)stream);
     if constexpr (sizeof(T) == 2) {
       if (a.q4)
@@ -1107,7 +1124,8 @@ struct Variant {
     }
     if (marks.end) (void)hipEventRecord((hipEvent_t)marks.end, (hipStream_t)stream);
     // split heads (retrieval heads when nsplit > 1, streaming heads when nss > 1)
-    const int64_t mheads = (a.nsplit > 1 ? (int64_t)a.Hr : 0) + (a.nss > 1 ? (int64_t)a.Hs : 0);
+    const int ret_parts = a.nsplit + (a.q4 ? 1 : 0);
+    const int64_t mheads = (ret_parts > 1 ? (int64_t)a.Hr : 0) + (a.nss > 1 ? (int64_t)a.Hs : 0);
     if (mheads > 0) {
       const int64_t mblocks = (int64_t)a.B * mheads * G * (D / 64);
       hipLaunchKernelGGL((merge_kernel<T, D, G>), dim3((unsigned)mblocks),

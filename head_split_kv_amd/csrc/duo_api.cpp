@@ -132,9 +132,12 @@ duo_status decode_impl(duo_cache* c, int32_t layer, const void* q, const void* k
     const int32_t rows = std::min(n_max, c->cfg.sink + c->cfg.recent);
     a.nss = std::max(1, std::min({8, (rows + 127) / 128, (int)c->cfg.max_splits}));
   }
+  // 4-bit caches: one more block and one more partial per retrieval head (its residual rows)
+  const int32_t split_cap = q4 ? a.max_splits - 1 : a.max_splits;
   a.nsplit = c->force_splits
-                 ? c->force_splits
-                 : choose_decode_splits(n_max, a.B, a.Hr, a.Hs * a.nss, a.max_splits,
+                 ? std::min(c->force_splits, split_cap)
+                 : choose_decode_splits(n_max, a.B, a.Hr, a.Hs * a.nss + (q4 ? a.Hr : 0),
+                                        split_cap,
                                         decode_resident_blocks(c->cfg.dtype, c->cfg.head_dim,
                                                                group, q4));
   a.scale_log2 = (float)((double)c->scale * 1.4426950408889634);

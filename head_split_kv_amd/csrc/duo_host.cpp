@@ -44,6 +44,8 @@ duo_status check_config(const duo_config* cfg) {
   if (g != 1 && g != 2 && g != 4 && g != 8) return DUO_ERR_UNSUPPORTED;
   if (cfg->out_dtype != DUO_F32 && cfg->out_dtype != cfg->dtype) return DUO_ERR_UNSUPPORTED;
   if (cfg->kv_bits == 4 && cfg->dtype != DUO_BF16) return DUO_ERR_UNSUPPORTED;
+  // a 4-bit retrieval head decodes into its splits' partials plus one for the residual rows
+  if (cfg->kv_bits == 4 && cfg->max_splits == 1) return DUO_ERR_INVALID;
   return DUO_OK;
 }
 

@@ -75,7 +75,9 @@ typedef struct {
   int32_t out_dtype;       /* duo_dtype of out */
   float softmax_scale;     /* <= 0 selects 1/sqrt(head_dim) */
   int32_t max_splits;      /* split-K workspace per (sequence, query head), <= 1024;
-                              0 selects 256 */
+                              0 selects 256; with kv_bits = 4 not 1 (a retrieval head then
+                              uses up to max_splits - 1 context splits plus one partial for
+                              its residual rows) */
   int32_t prefill_tiles;   /* prefill split-K workspace in tiles of 128 query rows,
                               <= 65536; 0 selects 2048 */
   const uint8_t* retrieval_mask; /* host [num_layers][num_kv_heads], nonzero = retrieval;
@@ -228,8 +230,8 @@ duo_status duo_kv_bytes(const duo_config* cfg, const int32_t* seq_lens, int32_t 
                         uint64_t* full_attn_bytes, uint64_t* duo_bytes);
 
 /* Override the number of context splits per retrieval head used by duo_attn_decode
- * (0 = automatic from the lengths; otherwise 1..cfg.max_splits). The result does not depend
- * on it beyond floating-point rounding. Host only. */
+ * (0 = automatic from the lengths; otherwise 1..cfg.max_splits, capped at max_splits - 1 on
+ * a 4-bit cache). The result does not depend on it beyond floating-point rounding. Host only. */
 duo_status duo_set_decode_splits(duo_cache* cache, int32_t splits);
 
 /* Kernel timers (a measurement aid, off by default). duo_timing_enable(cache, n) creates n

@@ -83,6 +83,10 @@ def test_kv_bits_checked_and_kv4_layout():
         assert N.lib().duo_layout_query(ctypes.byref(cfg), ctypes.byref(lay)) == status, bits
     cfg, _keep = cfg_of(dtype=torch.float32, kv_bits=4)
     assert N.lib().duo_layout_query(ctypes.byref(cfg), ctypes.byref(lay)) == N.DUO_ERR_UNSUPPORTED
+    # a 4-bit retrieval head needs a partial for its residual rows besides its context splits
+    for ms, status in ((1, N.DUO_ERR_INVALID), (2, N.DUO_OK), (0, N.DUO_OK)):
+        cfg, _keep = cfg_of(kv_bits=4, max_splits=ms)
+        assert N.lib().duo_layout_query(ctypes.byref(cfg), ctypes.byref(lay)) == status, ms
     # the 4-bit full caches are sized by the documented per-head geometry
     cfg4, _k4 = cfg_of(kv_bits=4)
     cfg16, _k16 = cfg_of()
