@@ -630,13 +630,22 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
   for (int cb = 0; cb < CBK; ++cb) oacc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // Groups of a retrieval head: chunks of kWaves consecutive groups are dealt round-robin
-  // to the splits, and wave w of a split takes group w of each of its chunks, so the blocks
-  // of a head read neighbouring groups at any time.
+  // to the splits, and wave w of a split takes group w of each of its chunks (wave gw of the
+  // head takes groups i W + gw), so the blocks of a head read neighbouring groups at any
+  // time. The ng - q W groups left over after q whole rounds go by steps when there are
+  // enough waves: the four waves of block k each take one 32-token step of leftover group
+  // k, instead of a few waves taking a whole extra group and ending last.
   const int ng = ret ? n / kQ4Group : 0;
-  const int n_wave =
-      ng > kWaves * split + wave ? (ng - 1 - kWaves * split - wave) / (kWaves * nsplit) + 1 : 0;
+  const int W = kWaves * nsplit, gw = kWaves * split + wave;
+  const int q_rounds = ng / W, rem = ng - q_rounds * W;
+  const bool by_steps = 4 * rem <= W;
+  const int n_full = q_rounds + (!by_steps && gw < rem ? 1 : 0);  // whole groups of the wave
+  const int t_step = by_steps && gw < 4 * rem ? gw % kSteps : -1;   // its leftover step, if any
+  const int t_group = q_rounds * W + gw / kSteps;
+  const int n_wave = n_full + (t_step >= 0 ? 1 : 0);
   auto group_of = [&](int i) {  // clamped past the last group
-    return (split + nsplit * (i < n_wave ? i : n_wave - 1)) * kWaves + wave;
+    const int ii = i < n_wave ? i : n_wave - 1;
+    return ii == n_full && t_step >= 0 ? t_group : ii * W + gw;
   };
   {
     const uint16_t* kpar = (const uint16_t*)(kq + a.q4_params);  // bf16 [group][2][D]
@@ -696,7 +705,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
     const uint32_t lp = 16 * jj;                           // value parameters of tokens 4 jj ..
     const uint32_t lk_d = lk & 1023;
     auto load_step = [&](Ld& f, int gi, int st) {
-      const bool real = gi < n_wave;  // wave-uniform
+      const bool real = gi < n_full || (gi == n_full && st == t_step);  // wave-uniform
       const int64_t gg = group_of(gi);
       const char* kb = real ? kq + gg * kQ4Group * CBY : idle;
       const char* vb = real ? vq + gg * kQ4Group * CBY : idle;
@@ -797,7 +806,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
       load_step(f2, 0, 2);
       load_step(f3, 0, 3);
     }
-    for (int gi = 0; gi < n_wave; ++gi) {
+    for (int gi = 0; gi < n_full; ++gi) {
       fold();
       load_params(gi + 1);  // clamped past the last group
       // the barriers keep each slot's last use ahead of its reload, so the reload lands in
@@ -814,6 +823,11 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
       step(f3);
       __builtin_amdgcn_sched_barrier(0);
       load_step(f3, gi + 1, 3);
+    }
+    if (t_step >= 0) {  // the leftover step, already in its slot (the others read the idle buffer)
+      fold();
+      const Ld& ft = t_step == 0 ? f0 : t_step == 1 ? f1 : t_step == 2 ? f2 : f3;
+      step(ft);
     }
   }
   // MFMA partial of query col: sums over the 4 lanes of the column; every channel of O^T gets
