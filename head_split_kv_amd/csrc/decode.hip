@@ -486,8 +486,8 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
 // are in flight (a wave moves the bytes it has in flight per memory latency). Codes are stored
 // in operand order (layout in duo.h): the KC key words of one token that a lane needs are
 // contiguous, and a wave's value words of a step are D / 64 contiguous KB, so every load
-// instruction reads one contiguous KB. The incomplete last group (bf16 residual rows) and the streaming
-// heads take the bf16 path over the 4 waves of one block.
+// instruction reads one contiguous KB. The incomplete last group (bf16 residual rows) and the
+// streaming heads take the bf16 path, in blocks of their own.
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));

@@ -210,7 +210,8 @@ def test_kv4_decode_lengths(n0):
 
 @pytest.mark.parametrize("splits", [1, 2, 3, 7, 16])
 def test_kv4_decode_split_counts(splits):
-    """Groups dealt to 1..16 splits (some with no group, the residual on split ng mod s)."""
+    """Groups dealt to 1..16 splits: some splits with no group, leftover groups by steps (1
+    and 2 splits) or whole (3 and more), the residual rows in a block of their own."""
     w = W.Workload("kv4-splits", 1, 1, 32, 8, 128, "bf16", 16, 64, 0, 0, 4, seed=109)
     run_decode_kv4(w, [9 * QG + 50], 2, splits=splits)
 
