@@ -590,6 +590,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(dec4["kern_gbs"], 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(dec4["kern_gbs"] / HBM_PEAK_GBS, 4),
+                         "traffic": committed_traffic("decode.hip", f"decode_kv4_{args.workload}"),
                          "kernel": "decode_q4_kernel<d128, G4> (split attention kernel)",
                          "kernel_us": round(dec4["kern_us"], 3)},
         },
