@@ -107,7 +107,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
   constexpr int RB = Gm::kRowBytes;
   constexpr int kQpb = kRows / G;  // positions per block
   constexpr int kDma = Gm::kDmaPerWave;
-  constexpr int kHalfSlabs = Gm::kSlabs / 2;  // QK^T K-slabs of the next tile per PV step
+  constexpr int kHalfSlabs = Gm::kSlabs / 2;  // QK^T K-slabs per quarter of a tile's scores
   // Two K buffers, two V buffers (+ key positions): in the iteration of tile i the waves read
   // V(i) and K(i+1) while the DMA fills V(i+1) and K(i+2) into the other buffers.
   __shared__ __attribute__((aligned(1024))) char sK0[Gm::kTileBytes];
@@ -316,8 +316,12 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
                                                   (k0 == 0 && k == 0) ? f32x16_t{} : s, 0, 0, 0);
   };
 
-  // One pipelined iteration: softmax and PV of the current tile (scores sc, V in sv, key
-  // positions in sp) interleaved with the scores of the next tile (K in skn) into sn.
+  // One iteration: softmax and PV of the current tile (scores sc, V in sv, key positions in
+  // sp), then the scores of the next tile (K in skn) into sn. Every group of MFMAs runs with
+  // the LDS reads of the next group's operands in flight (two register sets, the issue order
+  // fixed by scheduling barriers); the scores are computed after PV rather than under it so
+  // that the current scores are dead by then, which keeps both operand sets in registers
+  // without spills.
   auto iterate = [&](f32x16_t (&sc)[2], f32x16_t (&sn)[2], int kind, const char* skn,
                      const char* sv, const int* sp) {
     if (kind != 0) {
@@ -358,23 +362,9 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
     // PV over four 16-key slabs; slab k holds keys 16k + {4half..4half+3} then
     // 16k + 8 + {4half..4half+3} in both operands (elements 8(k&1) .. 8(k&1)+7 of block
     // k>>1 of S^T). A transposed read gives lane l the four keys k0..k0+3 at
-    // d = 32db + (l & 31), with k0 = 16k + 8part + 4half. Each slab step also advances a
-    // quarter of the next tile's scores.
+    // d = 32db + (l & 31), with k0 = 16k + 8part + 4half.
     const int gi = lane >> 4, jj = lane & 15, e4 = jj >> 2, q4 = jj & 3;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int blk = k >> 1, e0 = (k & 1) * 8;
-      uint32_t hw[4], lw[4];
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const float p0 = fexp2(__builtin_fmaf(sc[blk][e0 + e], c2, -m));
-        const float p1 = fexp2(__builtin_fmaf(sc[blk][e0 + e + 1], c2, -m));
-        l += p0 + p1;
-        split_bf16(p0, p1, hw[e / 2], lw[e / 2]);
-      }
-      const bf16x8_t pfh = __builtin_bit_cast(bf16x8_t, uint4{hw[0], hw[1], hw[2], hw[3]});
-      const bf16x8_t pfl = __builtin_bit_cast(bf16x8_t, uint4{lw[0], lw[1], lw[2], lw[3]});
-      bf16x8_t vf[Gm::kDBlocks];
+    auto load_vt = [&](bf16x8_t (&vf)[Gm::kDBlocks], int k) {
 #pragma unroll
       for (int db = 0; db < Gm::kDBlocks; ++db) {
         s16x4_t vt[2];
@@ -390,13 +380,61 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
         const uint2 v1 = __builtin_bit_cast(uint2, vt[1]);
         vf[db] = __builtin_bit_cast(bf16x8_t, uint4{v0.x, v0.y, v1.x, v1.y});
       }
-      qk_part(sn[k >> 1], skn, k >> 1, (k & 1) * kHalfSlabs);
+    };
+    // K operands of quarter q of the next tile's scores (32-key block q >> 1, K-slabs
+    // (q & 1) kHalfSlabs ..)
+    auto load_k = [&](bf16x8_t (&kf)[kHalfSlabs], int q) {
+      const int r = (q >> 1) * 32 + col;
+      const char* krow = skn + r * RB;
+      const int sw = swz<NCH>(r);
+#pragma unroll
+      for (int k = 0; k < kHalfSlabs; ++k)
+        kf[k] = __builtin_bit_cast(
+            bf16x8_t, *(const uint4*)(krow + ((2 * ((q & 1) * kHalfSlabs + k) + half) ^ sw) * 16));
+    };
+    bf16x8_t vA[Gm::kDBlocks], vB[Gm::kDBlocks];
+    bf16x8_t kA[kHalfSlabs], kB[kHalfSlabs];
+    load_vt(vA, 0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int blk = k >> 1, e0 = (k & 1) * 8;
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float p0 = fexp2(__builtin_fmaf(sc[blk][e0 + e], c2, -m));
+        const float p1 = fexp2(__builtin_fmaf(sc[blk][e0 + e + 1], c2, -m));
+        l += p0 + p1;
+        split_bf16(p0, p1, hw[e / 2], lw[e / 2]);
+      }
+      const bf16x8_t pfh = __builtin_bit_cast(bf16x8_t, uint4{hw[0], hw[1], hw[2], hw[3]});
+      const bf16x8_t pfl = __builtin_bit_cast(bf16x8_t, uint4{lw[0], lw[1], lw[2], lw[3]});
+      bf16x8_t (&vf)[Gm::kDBlocks] = (k & 1) ? vB : vA;
+      bf16x8_t (&vn)[Gm::kDBlocks] = (k & 1) ? vA : vB;
+      // the next slab's operands (after the last slab, the first K operands of the next
+      // tile's scores) in flight under these MFMAs
+      if (k < 3) load_vt(vn, k + 1);
+      else load_k(kA, 0);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int db = 0; db < Gm::kDBlocks; ++db)
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pfh, o[db], 0, 0, 0);
 #pragma unroll
       for (int db = 0; db < Gm::kDBlocks; ++db)
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pfl, o[db], 0, 0, 0);
+    }
+    // scores of the next tile, the K operands of each quarter read under the previous one's
+    // MFMAs
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      bf16x8_t (&kf)[kHalfSlabs] = (q & 1) ? kB : kA;
+      bf16x8_t (&kn)[kHalfSlabs] = (q & 1) ? kA : kB;
+      if (q < 3) load_k(kn, q + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      const int k0 = (q & 1) * kHalfSlabs;
+#pragma unroll
+      for (int k = 0; k < kHalfSlabs; ++k)
+        sn[q >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            kf[k], qf[k0 + k], (k0 == 0 && k == 0) ? f32x16_t{} : sn[q >> 1], 0, 0, 0);
     }
   };
 
