@@ -98,6 +98,19 @@ __device__ __forceinline__ int swz(int r) {
 __device__ __forceinline__ float max_pair32(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
 __device__ __forceinline__ float sum_pair32(float x) { return x + __shfl_xor(x, 32); }
 
+// Wait until at most N of this wave's vector memory operations are in flight and its LDS
+// operations are done, then join the block's barrier. The K/V tiles arrive in LDS by DMA
+// (global_load_lds), whose completions the vector memory counter tracks in issue order, so
+// waiting for all but the last N DMAs leaves the most recent batch in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // s_waitcnt fields: vmcnt low bits 3:0 and high bits 15:14, expcnt 6:4 (7: no wait),
+  // lgkmcnt 11:8 (0: wait for all)
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
+  __builtin_amdgcn_s_barrier();
+}
+
 // kMix: the streaming pass of gate-mixed attention (full-cache source, blended output); a
 // separate instantiation so that the ordinary kernel carries none of it.
 template <int D, int G, bool kMix>
@@ -413,7 +426,6 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
       // the next slab's operands (after the last slab, the first K operands of the next
       // tile's scores) in flight under these MFMAs
       if (k < 3) load_vt(vn, k + 1);
-      else load_k(kA, 0);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int db = 0; db < Gm::kDBlocks; ++db)
@@ -422,8 +434,11 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
       for (int db = 0; db < Gm::kDBlocks; ++db)
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pfl, o[db], 0, 0, 0);
     }
-    // scores of the next tile, the K operands of each quarter read under the previous one's
-    // MFMAs
+    // K(next) came by DMA in the previous iteration: wait for it (this iteration's two
+    // batches stay in flight), then the scores of the next tile, the K operands of each
+    // quarter read under the previous one's MFMAs
+    wait_vm_barrier<2 * kDma>();
+    load_k(kA, 0);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       bf16x8_t (&kf)[kHalfSlabs] = (q & 1) ? kB : kA;
@@ -440,10 +455,13 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
 
   // ---- tile loop ------------------------------------------------------------------
   // Prologue: K, V of the first visible tile and K of the second; scores of the first.
-  // Iteration i (tiles cur = t_i, nxt = t_i+1, nn = t_i+2): DMA of K(nn) into the K buffer
-  // of cur and of V(nxt) into the other V buffer, then iterate(); the barrier at its end
-  // makes both DMAs visible and frees the buffers read in it. Past the last tile the
-  // "next" scores are computed from a stale buffer and discarded.
+  // Iteration i (tiles cur = t_i, nxt = t_i+1, nn = t_i+2): DMA of V(nxt) into the other V
+  // buffer and of K(nn) into the K buffer of cur, then iterate(). Its barrier before the
+  // scores waits for K(nxt), issued one iteration earlier; the barrier at its end waits for
+  // V(nxt) and frees the buffers read in it, while K(nn) stays in flight. So every wait
+  // leaves the latest batch in flight, and the counts are constant: past the last tile the
+  // batches still go out (in-bounds rows, never read) and the "next" scores are computed
+  // from a stale buffer and discarded.
   f32x16_t sA[2], sB[2];
   int cur = next_visible(t_begin);
   if (cur < t_end) {
@@ -460,10 +478,10 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
       // even iteration: scores of cur in sA, V(cur) in sV0, K(nxt) in sK1
       int nn = nxt < t_end ? next_visible(nxt + 1) : t_end;
       if (nxt < t_end) write_pos(nxt, sPos1);
-      if (nn < t_end) issue_k(nn, sK0);
-      if (nxt < t_end) issue_v(nxt, sV1);
+      issue_v(nxt, sV1);
+      issue_k(nn, sK0);
       iterate(sA, sB, kind, sK1, sV0, sPos0);
-      __syncthreads();
+      wait_vm_barrier<kDma>();  // V(nxt) in LDS; K(nn) stays in flight
       if (nxt >= t_end) break;
       cur = nxt;
       nxt = nn;
@@ -471,15 +489,16 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
       // odd iteration: scores of cur in sB, V(cur) in sV1, K(nxt) in sK0
       nn = nxt < t_end ? next_visible(nxt + 1) : t_end;
       if (nxt < t_end) write_pos(nxt, sPos0);
-      if (nn < t_end) issue_k(nn, sK1);
-      if (nxt < t_end) issue_v(nxt, sV0);
+      issue_v(nxt, sV0);
+      issue_k(nn, sK1);
       iterate(sB, sA, kind, sK0, sV1, sPos1);
-      __syncthreads();
+      wait_vm_barrier<kDma>();
       if (nxt >= t_end) break;
       cur = nxt;
       nxt = nn;
       kind = classify(cur);
     }
+    wait_vm_barrier<0>();  // no DMA into this block's LDS outlives the loop
   }
 
   // ---- epilogue ---------------------------------------------------------------------
