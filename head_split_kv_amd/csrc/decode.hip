@@ -209,8 +209,14 @@ constexpr int lanes_per_token() {
   return (words8 > 200 && chunks >= 16) ? 16 : 8;
 }
 
+// The leading scalar arguments repeat a.nsplit, a.Hr, a.Hs, a.B, a.nss and whether the step
+// is fused (a.new_k != null). They arrive preloaded in SGPRs (the library's build asks for six
+// preloaded argument dwords), so a block decodes its work item without a memory round trip
+// and its first argument loads (lengths, head tables, pointers) go out together.
 template <typename T, int D, int G, int LPT, int NS>
-__global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(kThreads, 2)
+    decode_kernel(int32_t lead_nsplit, int32_t lead_hr, int32_t lead_hs, int32_t lead_b,
+                  int32_t lead_nss, int32_t lead_fused, DecodeArgs a) {
   using Geo = RowGeom<T, D, LPT>;
   using F = Frag<T, D, LPT>;
   constexpr int kTpw = 64 / LPT;        // tokens per wave per step
@@ -231,30 +237,33 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
   // In a fused step (a.new_k != null) the token at p = n - 1 is not in the cache yet: the
   // cache rows of this item exclude it (and, on a streaming head, the slot it is about to
   // take), and the one block that covers p reads its K/V from the input, then stores them.
-  const bool fused = a.new_k != nullptr;
-  const int64_t n_ret_items = (int64_t)a.B * a.Hr * a.nsplit;
+  const bool fused = lead_fused != 0;
+  // 32-bit work-item arithmetic (blocks < 2^32; a 64-bit division is a long software
+  // sequence on the path to the first loads)
+  const uint32_t bid = blockIdx.x;
+  const uint32_t n_ret_items = (uint32_t)lead_b * lead_hr * lead_nsplit;
   int b, j, split, nsplit, cls;
   int64_t head_row0;  // first row of this head in its cache
   const char* kbase;
   const char* vbase;
   int t1, skip = -1, new_row = -1;  // new_row: cache row of the new token if this block has it
-  if ((int64_t)blockIdx.x < n_ret_items) {
-    const int64_t i = blockIdx.x;
-    split = (int)(i % a.nsplit);
-    cls = (int)((i / a.nsplit) % a.Hr);
-    b = (int)(i / ((int64_t)a.nsplit * a.Hr));
+  if (bid < n_ret_items) {
+    const uint32_t q = bid / (uint32_t)lead_nsplit;
+    split = (int)(bid - q * (uint32_t)lead_nsplit);
+    cls = (int)(q % (uint32_t)lead_hr);
+    b = (int)(q / (uint32_t)lead_hr);
     j = a.ret_kv[cls];
-    nsplit = a.nsplit;
+    nsplit = lead_nsplit;
     const int n = a.n[b];
     t1 = fused ? n - 1 : n;
     if (fused && ((n - 1) / kTile) % nsplit == split) new_row = n - 1;
-    head_row0 = ((int64_t)b * a.Hr + cls) * a.cap;
+    head_row0 = ((int64_t)b * lead_hr + cls) * a.cap;
     kbase = (const char*)a.full_k;
     vbase = (const char*)a.full_v;
   } else {
-    const int64_t i = blockIdx.x - n_ret_items;
-    cls = (int)(i % a.Hs);
-    b = (int)(i / a.Hs);
+    const uint32_t i = bid - n_ret_items;
+    cls = (int)(i % (uint32_t)lead_hs);
+    b = (int)(i / (uint32_t)lead_hs);
     j = a.str_kv[cls];
     split = 0;
     nsplit = 1;
@@ -270,7 +279,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
       t1 = min(pnew, SR);
       if (pnew >= SR) skip = new_row;
     }
-    head_row0 = ((int64_t)b * a.Hs + cls) * (a.S + a.R);
+    head_row0 = ((int64_t)b * lead_hs + cls) * (a.S + a.R);
     kbase = (const char*)a.str_k;
     vbase = (const char*)a.str_v;
   }
@@ -511,8 +520,11 @@ constexpr int kBfStages = 6;  // bf16 row fragments in flight in decode_q4_kerne
 // in cache (the values are never used). 16 KB covers every offset a look-ahead adds.
 __device__ __attribute__((aligned(256))) uint32_t g_q4_idle[4096];
 
+// Leading arguments as for decode_kernel.
 template <int D, int G, int LPT, int NS>
-__global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(kThreads, 2)
+    decode_q4_kernel(int32_t lead_nsplit, int32_t lead_hr, int32_t lead_hs, int32_t lead_b,
+                     int32_t lead_nss, int32_t lead_fused, DecodeArgs a) {
   using T = uint16_t;
   using Geo = RowGeom<T, D, LPT>;
   using F = Frag<T, D, LPT>;
@@ -537,18 +549,20 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
   const int col = lane & 15;              // MFMA column: the query of S^T and of O^T
 
   // ---- work item -------------------------------------------------------------------------
-  // Blocks: the quantized groups of every (sequence, retrieval head) over a.nsplit splits;
+  // Blocks: the quantized groups of every (sequence, retrieval head) over lead_nsplit splits;
   // one block per (sequence, retrieval head) for its bf16 residual rows, which starts
   // reading them at once instead of after some split's groups; then the streaming windows,
-  // each over a.nss blocks. A retrieval head's partials are its nsplit splits plus the
+  // each over lead_nss blocks. A retrieval head's partials are its nsplit splits plus the
   // residual block's. In a fused step (a.new_k != null) the token at p = a.n[b] - 1 is not
   // in the cache yet and completes no group: the residual block (or the last block of the
   // streaming window) also takes it from the input and then stores it, as in decode_kernel.
-  const bool fused = a.new_k != nullptr;
-  const int64_t n_ret_items = (int64_t)a.B * a.Hr * a.nsplit;
-  const int64_t n_res_items = (int64_t)a.B * a.Hr;
-  const bool ret = (int64_t)blockIdx.x < n_ret_items;
-  const bool res = !ret && (int64_t)blockIdx.x < n_ret_items + n_res_items;
+  const bool fused = lead_fused != 0;
+  // 32-bit work-item arithmetic, as in decode_kernel
+  const uint32_t bid = blockIdx.x;
+  const uint32_t n_ret_items = (uint32_t)lead_b * lead_hr * lead_nsplit;
+  const uint32_t n_res_items = (uint32_t)lead_b * lead_hr;
+  const bool ret = bid < n_ret_items;
+  const bool res = !ret && bid < n_ret_items + n_res_items;
   int b, j, split, nsplit, nparts, n;  // n: tokens in the cache (streaming: slots of this block)
   int new_row = -1, skip = -1, r0 = 0;  // r0: first bf16 row of this block
   const char* kq = nullptr;  // retrieval head: K region (codes, parameters, residual)
@@ -558,34 +572,35 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
   if (ret || res) {
     int cls;
     if (ret) {
-      const int64_t i = blockIdx.x;
-      split = (int)(i % a.nsplit);
-      cls = (int)((i / a.nsplit) % a.Hr);
-      b = (int)(i / ((int64_t)a.nsplit * a.Hr));
+      const uint32_t q = bid / (uint32_t)lead_nsplit;
+      split = (int)(bid - q * (uint32_t)lead_nsplit);
+      cls = (int)(q % (uint32_t)lead_hr);
+      b = (int)(q / (uint32_t)lead_hr);
     } else {
-      const int64_t i = blockIdx.x - n_ret_items;
-      split = a.nsplit;  // the partial after the splits'
-      cls = (int)(i % a.Hr);
-      b = (int)(i / a.Hr);
+      const uint32_t i = bid - n_ret_items;
+      split = lead_nsplit;  // the partial after the splits'
+      cls = (int)(i % (uint32_t)lead_hr);
+      b = (int)(i / (uint32_t)lead_hr);
     }
     j = a.ret_kv[cls];
-    nsplit = a.nsplit;
-    nparts = a.nsplit + 1;
+    nsplit = lead_nsplit;
+    nparts = lead_nsplit + 1;
     n = fused ? a.n[b] - 1 : a.n[b];
     if (res && fused) new_row = n % kQ4Group;
-    const int64_t head = ((int64_t)b * a.Hr + cls) * a.q4_stride;
+    const int64_t head = ((int64_t)b * lead_hr + cls) * a.q4_stride;
     kq = (const char*)a.full_k + head;
     vq = (const char*)a.full_v + head;
     kbase = kq + a.q4_resid;
     vbase = vq + a.q4_resid;
   } else {
-    // a streaming head's window is cut over a.nss blocks; the last one takes the fused
+    // a streaming head's window is cut over lead_nss blocks; the last one takes the fused
     // step's token
-    const int64_t i = blockIdx.x - n_ret_items - n_res_items;
-    nsplit = nparts = a.nss;
-    split = (int)(i % nsplit);
-    const int cls = (int)((i / nsplit) % a.Hs);
-    b = (int)(i / ((int64_t)nsplit * a.Hs));
+    const uint32_t i = bid - n_ret_items - n_res_items;
+    nsplit = nparts = lead_nss;
+    const uint32_t q = i / (uint32_t)nsplit;
+    split = (int)(i - q * (uint32_t)nsplit);
+    const int cls = (int)(q % (uint32_t)lead_hs);
+    b = (int)(q / (uint32_t)lead_hs);
     j = a.str_kv[cls];
     const int SR = a.S + a.R;
     int nw;  // held slots of the window
@@ -601,7 +616,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_q4_kernel(DecodeArgs a) {
     const int per = (nw + nsplit - 1) / nsplit;
     r0 = min(nw, split * per);
     n = min(nw, r0 + per) - r0;
-    const int64_t row0 = ((int64_t)b * a.Hs + cls) * SR;
+    const int64_t row0 = ((int64_t)b * lead_hs + cls) * SR;
     kbase = (const char*)a.str_k + row0 * RB;
     vbase = (const char*)a.str_v + row0 * RB;
   }
@@ -1022,8 +1037,11 @@ constexpr int kMergeWaves = 8;
 constexpr int kMergeThreads = kMergeWaves * 64;
 constexpr int kMergeBatch = 16;
 
+// Leading arguments as for decode_kernel, the last one a.q4.
 template <typename T, int D, int G>
-__global__ void __launch_bounds__(kMergeThreads) merge_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(kMergeThreads)
+    merge_kernel(int32_t lead_nsplit, int32_t lead_hr, int32_t lead_hs, int32_t lead_b,
+                 int32_t lead_nss, int32_t lead_q4, DecodeArgs a) {
   __shared__ float s_m[kMergeWaves], s_l[kMergeWaves];
   __shared__ float s_o[kMergeWaves][64];
   constexpr int kSlices = D / 64;
@@ -1031,17 +1049,17 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(DecodeArgs a) {
   const int slice = blockIdx.x % kSlices;
   // (b, retrieval index, g) of the split retrieval heads, then (b, streaming index, g) of the
   // split streaming heads
-  const int ret_parts = a.nsplit + (a.q4 ? 1 : 0);  // 4-bit: plus the residual block's
-  const int n_ret_q = ret_parts > 1 ? a.B * a.Hr * G : 0;
+  const int ret_parts = lead_nsplit + (lead_q4 ? 1 : 0);  // 4-bit: plus the residual block's
+  const int n_ret_q = ret_parts > 1 ? lead_b * lead_hr * G : 0;
   int qi = blockIdx.x / kSlices;
   const bool ret = qi < n_ret_q;
   if (!ret) qi -= n_ret_q;
-  const int Hc = ret ? a.Hr : a.Hs;
+  const int Hc = ret ? lead_hr : lead_hs;
   const int g = qi % G;
   const int r = (qi / G) % Hc;
   const int b = qi / (G * Hc);
   const int h = (ret ? a.ret_kv[r] : a.str_kv[r]) * G + g;
-  const int nsplit = ret ? ret_parts : a.nss;
+  const int nsplit = ret ? ret_parts : lead_nss;
   const int64_t p0 = ((int64_t)b * a.Hq + h) * a.max_splits;
   const int d = slice * 64 + lane;
   const float* po = a.part_o + p0 * D + d;
@@ -1127,14 +1145,17 @@ struct Variant {
     if constexpr (sizeof(T) == 2) {
       if (a.q4)
         hipLaunchKernelGGL((decode_q4_kernel<D, G, LPT, 4>), dim3((unsigned)blocks),
-                           dim3(kThreads), 0, (hipStream_t)stream, a);
+                           dim3(kThreads), 0, (hipStream_t)stream, a.nsplit, a.Hr, a.Hs, a.B, a.nss,
+                           a.new_k != nullptr ? 1 : 0, a);
       else
         hipLaunchKernelGGL((decode_kernel<T, D, G, LPT, NS>), dim3((unsigned)blocks),
-                           dim3(kThreads), 0, (hipStream_t)stream, a);
+                           dim3(kThreads), 0, (hipStream_t)stream, a.nsplit, a.Hr, a.Hs, a.B, a.nss,
+                           a.new_k != nullptr ? 1 : 0, a);
     } else {
       if (a.q4) return -1;
       hipLaunchKernelGGL((decode_kernel<T, D, G, LPT, NS>), dim3((unsigned)blocks),
-                         dim3(kThreads), 0, (hipStream_t)stream, a);
+                         dim3(kThreads), 0, (hipStream_t)stream, a.nsplit, a.Hr, a.Hs, a.B, a.nss,
+                           a.new_k != nullptr ? 1 : 0, a);
     }
     if (marks.end) (void)hipEventRecord((hipEvent_t)marks.end, (hipStream_t)stream);
     // split heads (retrieval heads when nsplit > 1, streaming heads when nss > 1)
@@ -1143,7 +1164,8 @@ struct Variant {
     if (mheads > 0) {
       const int64_t mblocks = (int64_t)a.B * mheads * G * (D / 64);
       hipLaunchKernelGGL((merge_kernel<T, D, G>), dim3((unsigned)mblocks),
-                         dim3(kMergeThreads), 0, (hipStream_t)stream, a);
+                         dim3(kMergeThreads), 0, (hipStream_t)stream, a.nsplit, a.Hr, a.Hs, a.B, a.nss,
+                           a.q4, a);
     }
     return (int)hipGetLastError();
   }
