@@ -182,7 +182,7 @@ int record_event(void* event, void* stream);
 // the last one.
 int pairs_elapsed_ms(const std::vector<void*>& ev, int pairs, double* total_ms);
 // Decode blocks of this variant (the 4-bit kernel when q4) that are resident on the device
-// at once (512 if unknown).
+// at once, counting at most two per CU (512 if unknown): the size of one round of splits.
 int decode_resident_blocks(int dtype, int head_dim, int group, bool q4);
 // Prefill blocks of this variant that are resident on the device at once (512 if unknown).
 int prefill_resident_blocks(int head_dim, int group);
