@@ -61,7 +61,23 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--splits", type=int, default=0, help="force decode splits (0 = automatic)")
     p.add_argument("--unfused", action="store_true", help="time append + decode as two calls")
-    return p.parse_args()
+    p.add_argument("--legs", default="decode,kv4,c4,prefill,reorder,probe,cpu",
+                   help="legs to run: decode (the headline, always run), kv4 (4-bit full "
+                        "caches), c4 (32 layers x batch 8, ragged), prefill (the legs of "
+                        "--prefill-modes), reorder, probe (read and copy bandwidth), cpu "
+                        "(the oracle on the host)")
+    a = p.parse_args()
+    legs = set(a.legs.split(","))
+    unknown = legs - {"decode", "kv4", "c4", "prefill", "reorder", "probe", "cpu"}
+    if unknown:
+        p.error(f"unknown legs {sorted(unknown)}")
+    a.no_kv4 = a.no_kv4 or "kv4" not in legs
+    a.no_prefill = a.no_prefill or "prefill" not in legs
+    a.no_cpu = a.no_cpu or "cpu" not in legs
+    a.no_c4 = "c4" not in legs
+    a.no_reorder = "reorder" not in legs
+    a.no_probe = "probe" not in legs
+    return a
 
 
 def source_sha(name: str) -> str:
@@ -422,6 +438,130 @@ def reorder_leg(args, torch, hsk, N):
                 o_gbs=2 * o_bytes / (ms_o * 1e-3) / 1e9)
 
 
+def c4_leg(args, torch, hsk, N):
+    """Full-depth GQA decode: 32 layers of the Llama-3-8B-shaped head layout (32 q / 8 kv
+    heads, d 128, bf16, sink 16 + recent 512, per-layer retrieval masks at 50 %), batch 8 with
+    ragged contexts drawn in [16K, 32K]. One step is the fused append + decode
+    (duo_decode_step) of every layer for all 8 sequences: one whole-model attention step.
+    K/V/q come from a seeded device generator (torch.randn, seed 4000 + 64 layer + b for the
+    fill; the step tokens from seed 4999), rounded once to bf16."""
+    import numpy as np
+    import workloads as W
+    w = W.workload("c4")
+    lens0 = [int(x) for x in W.initial_lengths(w)]
+    masks = W.retrieval_mask(w)
+    L, B = w.layers, w.batch
+    total_steps = args.warmup + 2 * args.steps
+    cap = max(lens0) + total_steps
+    dev = torch.device("cuda")
+    cache = hsk.DuoCache(num_layers=L, batch=B, num_q_heads=w.hq, num_kv_heads=w.hkv,
+                         head_dim=w.d, sink=w.sink, recent=w.recent, capacity=cap,
+                         retrieval_mask=masks, dtype=torch.bfloat16, out_dtype=torch.bfloat16,
+                         device=dev, max_splits=1024)
+    gen = torch.Generator(device=dev)
+    t = time.time()
+    for layer in range(L):
+        for b, n in enumerate(lens0):
+            gen.manual_seed(4000 + 64 * layer + b)
+            k = torch.randn((n, w.hkv, w.d), generator=gen, device=dev).to(torch.bfloat16)
+            v = torch.randn((n, w.hkv, w.d), generator=gen, device=dev).to(torch.bfloat16)
+            cache.kv_append(layer, k, v, seq=b)
+            del k, v
+    gen.manual_seed(4999)
+    qs = torch.randn((total_steps, B, w.hq, w.d), generator=gen, device=dev).to(torch.bfloat16)
+    ks = torch.randn((total_steps, B, w.hkv, w.d), generator=gen, device=dev).to(torch.bfloat16)
+    vs = torch.randn((total_steps, B, w.hkv, w.d), generator=gen, device=dev).to(torch.bfloat16)
+    out = torch.empty((B, w.hq, w.d), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    log(f"c4 leg: {L} layers x batch {B}, lengths {lens0}, filled in {time.time() - t:.1f}s")
+    lib = N.lib()
+    h = cache.handle
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    qstride, kstride = B * w.hq * w.d * 2, B * w.hkv * w.d * 2
+    qp, kp, vp, op = qs.data_ptr(), ks.data_ptr(), vs.data_ptr(), ctypes.c_void_p(out.data_ptr())
+    decode_step = lib.duo_decode_step
+
+    def step(s):
+        qq = ctypes.c_void_p(qp + s * qstride)
+        kk = ctypes.c_void_p(kp + s * kstride)
+        vv = ctypes.c_void_p(vp + s * kstride)
+        for layer in range(L):
+            st = decode_step(h, layer, qq, kk, vv, op, None, stream)
+            if st:
+                raise RuntimeError(f"libduo call failed: {N.status_string(st)}")
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    tm.start()
+    for s in range(args.warmup, args.warmup + args.steps):
+        step(s)
+    ms_per_step = tm.stop_ms() / args.steps
+    # second pass: kernel timers around every split attention kernel, events around each step
+    hsk.duo_timing_enable(cache, args.steps * L)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i, s in enumerate(range(args.warmup + args.steps, total_steps)):
+        evs[i][0].record()
+        step(s)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    kern_ms, kern_n = hsk.duo_timing_read(cache, "decode")
+    hsk.duo_timing_enable(cache, 0)
+    assert kern_n == args.steps * L, kern_n
+    kern_ms_step = kern_ms / args.steps
+    per_step = np.array([a.elapsed_time(b) for a, b in evs])
+    pct = {f"p{q}": float(np.percentile(per_step, q)) for q in (10, 50, 90)}
+    # algorithmic bytes of a whole-model step (every layer, every sequence), averaged over the
+    # first pass's steps; the second pass is args.steps tokens longer (< 0.1 % more bytes)
+    cfg, _m = hsk.make_config(num_layers=L, batch=B, num_q_heads=w.hq, num_kv_heads=w.hkv,
+                              head_dim=w.d, sink=w.sink, recent=w.recent, capacity=cap,
+                              retrieval_mask=masks)
+    io_layer = 2 * B * w.hq * w.d * 2 + 2 * 2 * B * w.hkv * w.d * 2
+    tot = []
+    for s in range(args.warmup, args.warmup + args.steps):
+        lens = [n + s + 1 for n in lens0]
+        tot.append(sum(hsk.duo_kv_bytes(cfg, lens, layer)[1] for layer in range(L)) + L * io_layer)
+    step_bytes = float(np.mean(tot))
+    full_bytes = sum(hsk.duo_kv_bytes(cfg, [n + args.warmup + 1 for n in lens0], layer)[0]
+                     for layer in range(L))
+    del cache, qs, ks, vs
+    torch.cuda.empty_cache()
+    return dict(workload=w, lens0=lens0, ms_per_step=ms_per_step, step_bytes=step_bytes,
+                gbs=step_bytes / (ms_per_step * 1e-3) / 1e9, kern_ms_step=kern_ms_step,
+                kern_gbs=step_bytes / (kern_ms_step * 1e-3) / 1e9, step_pct=pct,
+                full_bytes=full_bytes)
+
+
+def read_probe(torch, hsk):
+    """Read bandwidth of a plain streaming-read kernel (duo_read_probe): 8 buffers of the 128K
+    decode layer's size (270 MB, 2.16 GB in all, so the Infinity Cache cannot hold them) read
+    round-robin, and one 2 GiB buffer, at several grid sizes; the best rate of each."""
+    res = {}
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for name, nbytes, nbuf in (("270MB", 269_573_120, 8), ("2GiB", 1 << 31, 1)):
+        bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(nbuf)]
+        best = None
+        for blocks in (512, 1024, 2048, 4096):
+            for bf in bufs:
+                hsk.duo_read_probe(bf, flag, blocks)
+            torch.cuda.synchronize()
+            tm = Timer(torch)
+            reps = 4 * nbuf if nbuf > 1 else 6
+            tm.start()
+            for i in range(reps):
+                hsk.duo_read_probe(bufs[i % nbuf], flag, blocks)
+            us = tm.stop_ms() * 1e3 / reps
+            gbs = nbytes / (us * 1e-6) / 1e9
+            if best is None or gbs > best[0]:
+                best = (gbs, us, blocks)
+        res[name] = {"GBps": round(best[0], 1), "us": round(best[1], 3), "blocks": best[2]}
+        del bufs
+        torch.cuda.empty_cache()
+    return res
+
+
 def copy_probe(torch):
     """Achievable HBM bandwidth of a plain device copy (read + write bytes)."""
     n = 1 << 30
@@ -438,15 +578,30 @@ def copy_probe(torch):
     return 2 * n / (ms * 1e-3) / 1e9
 
 
+def blas_threads() -> int:
+    """Threads numpy's BLAS runs with (the oracle's matrix products are its only parallel
+    part)."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def host_cores() -> dict:
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        aff = None
+    return {"cpu_count": os.cpu_count(), "affinity_cpus": aff, "blas_threads": blas_threads(),
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
 def cpu_baseline(args, W, w, n):
     """The float64 oracle decoding one step of the same layer on the host's cores."""
     import numpy as np
     from oracle import duo_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    threads = blas_threads()
     mask = W.retrieval_mask(w)[0]
     k = W.tokens(w, "k", 0, 0, 0, n)
     v = W.tokens(w, "v", 0, 0, 0, n)
@@ -506,35 +661,41 @@ def main():
             f"stored bytes; split kernel {dec4['kern_us']:.2f} us = {dec4['kern_gbs']:.0f} GB/s; "
             f"one duo_attn_decode call {dec4['dec_us']:.2f} us")
     modes = set(args.prefill_modes.split(","))
+    # a failing leg ends the run with an error (no leg is dropped from the line silently)
     pre = None
     if not args.no_prefill and "window" in modes:
-        try:
-            pre = prefill_leg(args, torch, hsk, W, N)
-            log(f"prefill: {pre['attn_ms']:.3f} ms attention for {pre['flops'] / 1e12:.3f} TFLOP "
-                f"= {pre['tflops']:.1f} TFLOP/s; attention kernel {pre['kern_ms']:.3f} ms = "
-                f"{pre['kern_tflops']:.1f} TFLOP/s")
-        except (RuntimeError, hsk.DuoError) as e:
-            log(f"prefill leg skipped: {e}")
+        pre = prefill_leg(args, torch, hsk, W, N)
+        log(f"prefill: {pre['attn_ms']:.3f} ms attention for {pre['flops'] / 1e12:.3f} TFLOP "
+            f"= {pre['tflops']:.1f} TFLOP/s; attention kernel {pre['kern_ms']:.3f} ms = "
+            f"{pre['kern_tflops']:.1f} TFLOP/s")
     pre_chunk = None
     if not args.no_prefill and "chunk" in modes:
-        try:
-            pre_chunk = prefill_leg(args, torch, hsk, W, N, mode="chunk")
-            log(f"prefill, chunk-granular streaming heads: {pre_chunk['attn_ms']:.3f} ms attention "
-                f"for {pre_chunk['flops'] / 1e12:.3f} TFLOP = {pre_chunk['tflops']:.1f} TFLOP/s; "
-                f"attention kernel {pre_chunk['kern_ms']:.3f} ms = "
-                f"{pre_chunk['kern_tflops']:.1f} TFLOP/s")
-        except (RuntimeError, hsk.DuoError) as e:
-            log(f"chunk-mode prefill leg skipped: {e}")
+        pre_chunk = prefill_leg(args, torch, hsk, W, N, mode="chunk")
+        log(f"prefill, chunk-granular streaming heads: {pre_chunk['attn_ms']:.3f} ms attention "
+            f"for {pre_chunk['flops'] / 1e12:.3f} TFLOP = {pre_chunk['tflops']:.1f} TFLOP/s; "
+            f"attention kernel {pre_chunk['kern_ms']:.3f} ms = "
+            f"{pre_chunk['kern_tflops']:.1f} TFLOP/s")
     mix = None
     if not args.no_prefill and "mixed" in modes:
         mix = gate_mixed_leg(args, torch, hsk, W, N)
         log(f"gate-mixed: {mix['ms']:.3f} ms for {mix['flops'] / 1e12:.3f} TFLOP = "
             f"{mix['tflops']:.1f} TFLOP/s; the causal pass alone {mix['full_ms']:.3f} ms = "
             f"{mix['full_tflops']:.1f} TFLOP/s")
-    reo = reorder_leg(args, torch, hsk, N)
-    log(f"reorder: {reo['ms']:.3f} ms for {reo['bytes'] / 1e9:.2f} GB of projections = "
-        f"{reo['gbs']:.0f} GB/s (read + write); output projections alone {reo['o_gbs']:.0f} GB/s")
-    probe = copy_probe(torch)
+    c4 = None
+    if not args.no_c4:
+        c4 = c4_leg(args, torch, hsk, N)
+        log(f"c4: {c4['ms_per_step'] * 1e3:.1f} us per whole-model step, {c4['gbs']:.0f} GB/s; "
+            f"split kernels {c4['kern_ms_step'] * 1e3:.1f} us per step = {c4['kern_gbs']:.0f} GB/s")
+    reo = None
+    if not args.no_reorder:
+        reo = reorder_leg(args, torch, hsk, N)
+        log(f"reorder: {reo['ms']:.3f} ms for {reo['bytes'] / 1e9:.2f} GB of projections = "
+            f"{reo['gbs']:.0f} GB/s (read + write); output projections alone {reo['o_gbs']:.0f} GB/s")
+    probe = rprobe = None
+    if not args.no_probe:
+        probe = copy_probe(torch)
+        rprobe = read_probe(torch, hsk)
+        log(f"probes: device copy {probe:.0f} GB/s (read + write); streaming read {rprobe}")
     w = dec["workload"]
     cpu = cpu_pre = None
     if not args.no_cpu:
@@ -542,6 +703,7 @@ def main():
         log(f"oracle: {cpu['sec_per_step']:.3f} s per decode step on {cpu['threads']} threads")
         cpu_pre = cpu_prefill_sample(args, W)
         log(f"oracle prefill sample: {cpu_pre['sec']:.2f} s, {cpu_pre['tflops'] * 1e3:.3f} GFLOP/s")
+    cores = host_cores()
     traffic = committed_traffic("decode.hip", f"decode_{args.workload}")
     out = {
         "metric": METRIC,
@@ -578,7 +740,29 @@ def main():
             "kernel_us": round(dec["kern_us"], 3),
             "algorithmic_bytes_per_launch": int(dec["step_bytes"]),
         },
-        "hbm_copy_probe_GBps": round(probe, 1),
+        "hbm_copy_probe_GBps": None if probe is None else round(probe, 1),
+        "hbm_read_probe": None if rprobe is None else dict(
+            rprobe, what="duo_read_probe: non-temporal 16-byte loads and nothing else, best of "
+                         "512..4096 blocks; 270MB = 8 buffers of the 128K layer's K/V size read "
+                         "round-robin (2.16 GB, beyond the Infinity Cache), 2GiB = one buffer"),
+        "c4": None if c4 is None else {
+            "workload": f"{c4['workload'].name}: 32 layers x batch 8, ragged contexts "
+                        f"{min(c4['lens0'])}..{max(c4['lens0'])} (seeded), 32 q / 8 kv heads, "
+                        f"d=128, bf16, per-layer retrieval masks at 50 %, sink 16 + recent 512; "
+                        f"step = append+decode of every layer (one whole-model attention step)",
+            "initial_lengths": c4["lens0"],
+            "us_per_model_step": round(c4["ms_per_step"] * 1e3, 2),
+            "us_per_model_step_spread": {k: round(v * 1e3, 2) for k, v in c4["step_pct"].items()},
+            "GBps": round(c4["gbs"], 1),
+            "hbm_frac": round(c4["gbs"] / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes_per_model_step": int(c4["step_bytes"]),
+            "full_attention_kv_bytes": int(c4["full_bytes"]),
+            "roofline": {"bound": "hbm", "achieved": round(c4["kern_gbs"], 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(c4["kern_gbs"] / HBM_PEAK_GBS, 4),
+                         "kernel": "decode_kernel<bf16, d128, G4>, 32 launches per step",
+                         "kernel_us_per_model_step": round(c4["kern_ms_step"] * 1e3, 2)},
+        },
         "decode_kv4": None if dec4 is None else {
             "workload": "the same 128K GQA decode with 4-bit full caches (keys per channel over "
                         "128-token groups, values per token, bf16 residual group)",
@@ -604,7 +788,7 @@ def main():
             "causal_pass_alone_ms": round(mix["full_ms"], 3),
             "causal_pass_alone_tflops": round(mix["full_tflops"], 1),
         },
-        "head_reorder": {
+        "head_reorder": None if reo is None else {
             "workload": "Llama-3-8B-shaped attention projections, 32 layers (Q, K, V rows and "
                         "output-projection columns, bf16), heads ordered by gates binarized at "
                         f"50 % ({reo['n_ret']} of 256 KV heads retrieval)",
@@ -638,7 +822,7 @@ def main():
         },
         "cpu_prefill_baseline": None if cpu is None else {
             "value": round(cpu_pre["tflops"], 6), "unit": "TFLOP/s", "cores": cpu["threads"],
-            "kind": "oracle",
+            "kind": "oracle", "host": cores,
             "sample": f"float64 oracle prefill of 64 queries (positions 12224..12287) x 32 heads "
                       f"of the 32K MHA prompt, {cpu_pre['sec']:.2f} s",
         },
@@ -646,6 +830,7 @@ def main():
             "value": round(dec["dec_bytes"] / cpu["sec_per_step"] / 1e9, 3),
             "unit": "GB/s",
             "cores": cpu["threads"],
+            "host": cores,
             "kind": "oracle",
             "sample": f"{cpu['calls']} float64 oracle decode step(s) of one {w.name} layer at "
                       f"{w.context} tokens (all 32 query heads), {cpu['sec_per_step']:.2f} s each",

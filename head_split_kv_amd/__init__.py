@@ -317,6 +317,20 @@ def duo_timing_read(cache: DuoCache, kind: str = "decode"):
     return ms.value, n.value
 
 
+def duo_read_probe(src: torch.Tensor, flag: torch.Tensor, blocks: int = 0, stream=None) -> None:
+    """Measurement aid: read every byte of the device tensor ``src`` once with the decode
+    kernels' non-temporal loads (``flag``: a device int32 tensor of at least one element)."""
+    for t in (src, flag):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError("src and flag must be contiguous device tensors")
+    if flag.numel() * flag.element_size() < 4:
+        raise ValueError("flag must hold at least 4 bytes")
+    check(lib().duo_read_probe(ctypes.c_void_p(src.data_ptr()),
+                               src.numel() * src.element_size(),
+                               ctypes.c_void_p(flag.data_ptr()), int(blocks), _stream(stream)),
+          "duo_read_probe")
+
+
 def duo_binarize_gates(alpha, ratio: float):
     """Retrieval mask (uint8 ``[L, H_kv]``), threshold tau and retrieval count from the trained
     gates ``alpha [L, H_kv]`` for a target retrieval ratio (the quantile runs over all heads;

@@ -20,7 +20,7 @@ EXPORTS = (
     "duo_attn_gate_mixed",
     "duo_slot_positions",
     "duo_cache_lengths", "duo_kv_bytes", "duo_set_decode_splits", "duo_timing_enable",
-    "duo_timing_read", "duo_binarize_gates", "duo_head_order", "duo_permute_blocks",
+    "duo_timing_read", "duo_read_probe", "duo_binarize_gates", "duo_head_order", "duo_permute_blocks",
     "duo_status_string",
 )
 TIMING_DECODE, TIMING_PREFILL = 0, 1
@@ -97,6 +97,7 @@ def lib() -> ctypes.CDLL:
         "duo_set_decode_splits": (st, [vp, i32]),
         "duo_timing_enable": (st, [vp, i32]),
         "duo_timing_read": (st, [vp, i32, P(ctypes.c_double), P(i32)]),
+        "duo_read_probe": (st, [vp, ctypes.c_uint64, vp, i32, vp]),
         "duo_binarize_gates": (st, [P(ctypes.c_float), i32, i32, ctypes.c_double,
                                     P(ctypes.c_uint8), P(ctypes.c_float), P(i32)]),
         "duo_head_order": (st, [P(ctypes.c_uint8), i32, i32, P(i32), P(i32)]),

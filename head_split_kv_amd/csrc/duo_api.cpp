@@ -353,7 +353,6 @@ duo_status prefill_args(duo_cache* c, int32_t layer, int32_t seq, const void* q,
   a.part_ml = (float*)(ws + ((uint64_t)c->cfg.prefill_tiles * kPrefillTileRows * D * 4 + kAlign - 1) /
                                 kAlign * kAlign);
   a.full_heads = li.n_ret;
-  if (c->cfg.dtype != DUO_BF16) return DUO_ERR_UNSUPPORTED;
   return DUO_OK;
 }
 
@@ -428,6 +427,14 @@ duo_status duo_timing_read(duo_cache* c, int32_t kind, double* total_ms, int32_t
   if (pairs_elapsed_ms(t.ev, t.used, total_ms) != 0) return DUO_ERR_HIP;
   t.used = 0;
   return DUO_OK;
+}
+
+duo_status duo_read_probe(const void* src, uint64_t bytes, uint32_t* flag, int32_t blocks,
+                          void* stream) {
+  if (!src || !flag || !aligned16(src) || !aligned4(flag) || bytes == 0 || bytes % 16 != 0 ||
+      blocks < 0 || blocks > (1 << 20))
+    return DUO_ERR_INVALID;
+  return launch_read_probe(src, bytes, flag, blocks, stream) != 0 ? DUO_ERR_HIP : DUO_OK;
 }
 
 duo_status duo_slot_positions(duo_cache* c, int32_t layer, int32_t* host_out, void* stream) {

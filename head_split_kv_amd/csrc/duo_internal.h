@@ -174,6 +174,9 @@ struct PermuteArgs {
 };
 int launch_permute(const PermuteArgs& a, void* stream);
 
+// Streaming-read probe (probe.hip); blocks <= 0 selects two per compute unit.
+int launch_read_probe(const void* src, uint64_t bytes, uint32_t* flag, int blocks, void* stream);
+
 // HIP events of the kernel timers (cache_kernels.hip); hipError_t values as int.
 int create_events(int n, std::vector<void*>* out);
 void destroy_events(std::vector<void*>* ev);

@@ -615,6 +615,262 @@ __global__ void __launch_bounds__(kMergeThreads) prefill_merge_kernel(PrefillArg
   if (tid % 16 == 0 && a.lse) a.lse[orow] = (M + __builtin_log2f(L)) * kLn2;
 }
 
+// ---- fp32 inputs ------------------------------------------------------------------------
+// The same attention for float32 q, k, v and caches, on v_mfma_f32_16x16x4_f32 with fp32
+// accumulation. One block = 4 waves = 64 query rows of one (sequence, KV head), 16 per wave;
+// K and V tiles of 32 keys are staged in LDS by plain 16-byte loads, rows padded by 4 words
+// so that both read patterns below hit 64 distinct banks. Per tile a wave computes
+// S^T = K Q^T (keys as MFMA rows; lane l holds query l % 16 against keys 4 (l / 16) + v of
+// each 16-key block), an online softmax in fp32 (log2 domain), and O^T += V^T P^T where the
+// k index of step s of a 16-key block is key 4 (l / 16) + s, so that every lane's B operand
+// is one of its own softmax weights and P never leaves the lane. Tile classes and masks are
+// those of the bf16 kernel. No split-K: every block covers the whole key range of its query
+// rows.
+constexpr int kF32Rows = 64;  // query rows per block
+constexpr int kF32BN = 32;    // keys per tile
+
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+template <int D, int G>
+__global__ void __launch_bounds__(kThreads, 2) prefill_f32_kernel(PrefillArgs a, int n_qt) {
+  constexpr int LD = D + 4;  // padded LDS row, in floats
+  constexpr int kQpb = kF32Rows / G;
+  constexpr int kSteps = D / 4;    // k steps of S^T over the head dimension
+  constexpr int kDBlocks = D / 16;  // 16-wide d blocks of O^T
+  __shared__ __attribute__((aligned(16))) float sK[kF32BN * LD];
+  __shared__ __attribute__((aligned(16))) float sV[kF32BN * LD];
+  __shared__ int sPos[kF32BN];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, qi = lane & 15, kq = lane >> 4;
+
+  // ---- block -> work item (retrieval items first, most keys first) ----------------------
+  const int n_ret_blocks = a.nb * a.Hr * n_qt;
+  int x = blockIdx.x, qt, bi, j, cls;
+  const bool retrieval = x < n_ret_blocks;
+  if (retrieval) {
+    cls = x % a.Hr;
+    x /= a.Hr;
+    bi = x % a.nb;
+    qt = n_qt - 1 - x / a.nb;
+    j = a.ret_kv[cls];
+  } else {
+    x -= n_ret_blocks;
+    cls = x % a.Hs;
+    x /= a.Hs;
+    bi = x % a.nb;
+    qt = n_qt - 1 - x / a.nb;
+    j = a.str_kv[cls];
+  }
+  const bool mixed = a.mixed != 0;
+  const bool causal_only = retrieval || a.chunk_mode != 0;
+  const bool full_src = retrieval || mixed;
+  const int b = a.b0 + bi;
+  const int c0 = a.c0[bi];
+  const int S = a.S, R = a.R, SR = a.S + a.R;
+  const int ql0 = qt * kQpb;
+  const int ql1 = min(a.m, ql0 + kQpb) - 1;
+  const int p_min = c0 + ql0, p_max = c0 + ql1;
+
+  // this lane's query row
+  const int row = wave * 16 + qi;
+  const int q_local = ql0 + row / G;
+  const int g = row % G;
+  const bool q_valid = q_local < a.m;
+  const int p = c0 + (q_valid ? q_local : ql1);
+  const int win_lo = causal_only ? -0x7FFFFFFF : p - R + 1;
+
+  // B operand of S^T: element kq of each 4-wide slice of this lane's query row
+  float qv[kSteps];
+  {
+    const int ql = q_valid ? q_local : ql1;
+    const float* qrow = (const float*)a.q + (((int64_t)bi * a.m + ql) * a.Hq + j * G + g) * D;
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) qv[s] = qrow[4 * s + kq];
+  }
+
+  // ---- key tiles: cache part, then chunk part ------------------------------------------
+  const int filled = full_src ? c0 : min(c0, SR);
+  int n_cache_tiles;
+  const float* cache_k;
+  const float* cache_v;
+  if (full_src) {
+    n_cache_tiles = (c0 + kF32BN - 1) / kF32BN;
+    const int64_t base = (mixed && !retrieval)
+                             ? ((int64_t)b * a.full_heads + a.cls_idx[j]) * a.cap * D
+                             : ((int64_t)b * a.Hr + cls) * a.cap * D;
+    cache_k = (const float*)a.full_k + base;
+    cache_v = (const float*)a.full_v + base;
+  } else {
+    n_cache_tiles = c0 > 0 ? (SR + kF32BN - 1) / kF32BN : 0;
+    const int64_t base = ((int64_t)b * a.Hs + cls) * SR * D;
+    cache_k = (const float*)a.str_k + base;
+    cache_v = (const float*)a.str_v + base;
+  }
+  const int n_tiles = n_cache_tiles + ql1 / kF32BN + 1;
+  const float* chunk_k = (const float*)a.k + ((int64_t)bi * a.m * a.Hkv + j) * D;
+  const float* chunk_v = (const float*)a.v + ((int64_t)bi * a.m * a.Hkv + j) * D;
+  const int64_t chunk_stride = (int64_t)a.Hkv * D;
+
+  // skipped (-1) or computed (masked from the key positions) tile
+  auto visible_tile = [&](int ti) -> bool {
+    if (ti < n_cache_tiles) {
+      if (ti * kF32BN >= filled) return false;
+      if (causal_only) return true;
+      if (mixed) {
+        const int k1 = min(filled, (ti + 1) * kF32BN) - 1;
+        return !(ti * kF32BN >= S && k1 < p_min - R + 1);
+      }
+      return !(ti * kF32BN >= S && p_min - R + 1 > c0 - 1);
+    }
+    const int k0 = c0 + (ti - n_cache_tiles) * kF32BN;
+    const int k1 = min(c0 + a.m, k0 + kF32BN) - 1;
+    if (causal_only) return true;
+    return !(k0 >= S && k1 < p_min - R + 1);
+  };
+  const int ring_bm = (!full_src && c0 > S) ? (c0 - 1 - S) % R : 0;
+  auto key_pos = [&](int ti, int r) -> int {
+    if (ti < n_cache_tiles) {
+      const int idx = ti * kF32BN + r;
+      if (idx >= filled) return kNoPos;
+      if (full_src || idx < S) return idx;
+      int back = ring_bm - (idx - S);
+      back += back < 0 ? R : 0;
+      return c0 - 1 - back;
+    }
+    const int i = (ti - n_cache_tiles) * kF32BN + r;
+    return i < a.m ? c0 + i : kNoPos;
+  };
+
+  f32x4_t o[kDBlocks];
+#pragma unroll
+  for (int db = 0; db < kDBlocks; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = kMInit, l = 0.f;
+  const float c2 = a.scale_log2;
+
+  for (int ti = 0; ti < n_tiles; ++ti) {
+    if (!visible_tile(ti)) continue;  // uniform over the block
+    // ---- stage the tile (rows past the data clamped onto the last one, or row 0) --------
+    const float* kb;
+    const float* vb;
+    int64_t stride;
+    int row0, nrows;
+    if (ti < n_cache_tiles) {
+      kb = cache_k, vb = cache_v, stride = D, row0 = ti * kF32BN, nrows = filled - row0;
+    } else {
+      kb = chunk_k, vb = chunk_v, stride = chunk_stride, row0 = (ti - n_cache_tiles) * kF32BN;
+      nrows = a.m - row0;
+    }
+    __syncthreads();  // the previous tile's LDS reads are done
+    constexpr int kChunks = kF32BN * D / 4;  // 16-byte chunks per tensor
+#pragma unroll
+    for (int c = tid; c < kChunks; c += kThreads) {
+      const int r = c / (D / 4), c4 = c % (D / 4);
+      const int sr = r < nrows ? row0 + r : (nrows > 0 ? row0 + nrows - 1 : 0);
+      const float4 kx = *(const float4*)(kb + sr * stride + 4 * c4);
+      const float4 vx = *(const float4*)(vb + sr * stride + 4 * c4);
+      *(float4*)(sK + r * LD + 4 * c4) = kx;
+      *(float4*)(sV + r * LD + 4 * c4) = vx;
+    }
+    if (tid < kF32BN) sPos[tid] = key_pos(ti, tid);
+    __syncthreads();
+
+    // ---- S^T = K Q^T: two 16-key blocks ------------------------------------------------
+    f32x4_t s[2];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      s[kb2] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const float* krow = sK + (16 * kb2 + qi) * LD + kq;
+#pragma unroll
+      for (int st = 0; st < kSteps; ++st)
+        s[kb2] = __builtin_amdgcn_mfma_f32_16x16x4f32(krow[4 * st], qv[st], s[kb2], 0, 0, 0);
+    }
+    // ---- masks and online softmax (this query's 32 scores over the 4 lanes qi + 16 kq) ----
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int t = sPos[16 * kb2 + 4 * kq + v];
+        const bool vis = (t <= p) & ((t < S) | (t >= win_lo));
+        s[kb2][v] = vis ? s[kb2][v] * c2 : kNegInf;
+        mx = fmaxf(mx, s[kb2][v]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(m, mx);
+    const float al = fexp2(m - mn);
+    m = mn;
+    l *= al;
+#pragma unroll
+    for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) o[db][v] *= al;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        s[kb2][v] = fexp2(s[kb2][v] - m);
+        l += s[kb2][v];
+      }
+    // ---- O^T += V^T P^T: step st of block kb2 takes key 16 kb2 + 4 kq + st -------------
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const float* vrow = sV + (16 * kb2 + 4 * kq + st) * LD + qi;
+#pragma unroll
+        for (int db = 0; db < kDBlocks; ++db)
+          o[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(vrow[16 * db], s[kb2][st], o[db], 0, 0, 0);
+      }
+  }
+
+  // ---- epilogue: lane (qi, kq) holds d = 16 db + 4 kq .. + 3 of its query ------------------
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (!q_valid) return;
+  const float inv = 1.f / l;
+  const int64_t orow = ((int64_t)bi * a.m + q_local) * a.Hq + j * G + g;
+  float* orow_p = (float*)a.out + orow * D;
+  const float keep = mixed ? a.alpha[j] : 0.f;
+  const float mine = 1.f - keep;
+#pragma unroll
+  for (int db = 0; db < kDBlocks; ++db) {
+    const int d = 16 * db + 4 * kq;
+    float4 r = float4{o[db][0] * inv, o[db][1] * inv, o[db][2] * inv, o[db][3] * inv};
+    if (mixed) {
+      const float4 pv = *(const float4*)(orow_p + d);
+      r = float4{__builtin_fmaf(keep, pv.x, mine * r.x), __builtin_fmaf(keep, pv.y, mine * r.y),
+                 __builtin_fmaf(keep, pv.z, mine * r.z), __builtin_fmaf(keep, pv.w, mine * r.w)};
+    }
+    *(float4*)(orow_p + d) = r;
+  }
+  if (kq == 0 && a.lse && !mixed) a.lse[orow] = (m + __builtin_log2f(l)) * kLn2;
+}
+
+template <int D, int G>
+int launch_f32(const PrefillArgs& args, void* stream, const KernelMarks& marks) {
+  const int n_qt = (args.m + kF32Rows / G - 1) / (kF32Rows / G);
+  const int64_t blocks = (int64_t)args.nb * n_qt * ((int64_t)args.Hr + args.Hs);
+  if (blocks == 0) return 0;
+  if (marks.begin) (void)hipEventRecord((hipEvent_t)marks.begin, (hipStream_t)stream);
+  hipLaunchKernelGGL((prefill_f32_kernel<D, G>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                     (hipStream_t)stream, args, n_qt);
+  if (marks.end) (void)hipEventRecord((hipEvent_t)marks.end, (hipStream_t)stream);
+  return (int)hipGetLastError();
+}
+
+template <int D>
+int dispatch_f32(int group, const PrefillArgs& a, void* stream, const KernelMarks& m) {
+  switch (group) {
+    case 1: return launch_f32<D, 1>(a, stream, m);
+    case 2: return launch_f32<D, 2>(a, stream, m);
+    case 4: return launch_f32<D, 4>(a, stream, m);
+    case 8: return launch_f32<D, 8>(a, stream, m);
+  }
+  return -1;
+}
+
 template <int D, int G>
 struct Variant {
   static int resident_blocks() {
@@ -677,10 +933,14 @@ int dispatch(int head_dim, int group, bool query, const PrefillArgs* a, void* st
 
 }  // namespace
 
-// Returns -1 for a variant that is not built (fp32 inputs), else a hipError_t value.
+// Returns -1 for a variant that is not built, else a hipError_t value.
 int launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int group, void* stream,
                    const KernelMarks& marks) {
-  if (dtype != DUO_BF16) return -1;
+  if (dtype == DUO_F32) {
+    if (head_dim == 128) return dispatch_f32<128>(group, a, stream, marks);
+    if (head_dim == 64) return dispatch_f32<64>(group, a, stream, marks);
+    return -1;
+  }
   return dispatch(head_dim, group, false, &a, stream, &marks);
 }
 

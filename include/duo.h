@@ -249,6 +249,17 @@ typedef enum { DUO_TIMING_DECODE = 0, DUO_TIMING_PREFILL = 1 } duo_timing_kind;
 duo_status duo_timing_enable(duo_cache* cache, int32_t max_records);
 duo_status duo_timing_read(duo_cache* cache, int32_t kind, double* total_ms, int32_t* records);
 
+/* Streaming-read probe (a measurement aid; no passage of the pages defines it). Reads `bytes`
+ * bytes at `src` once with the non-temporal 16-byte loads the decode kernels use, in a grid
+ * of `blocks` blocks of 256 threads (0: two per compute unit), and stores at most one word at
+ * `flag` (device memory, 4 bytes; written only for an improbable XOR of the data, so that the
+ * loads stay live). Timed with events around it, it gives the rate a plain read-only kernel
+ * reaches on the device, reported beside the decode kernels' bandwidth and the spec peak.
+ * src: device memory, 16-byte aligned; bytes: a multiple of 16. DUO_ERR_INVALID otherwise
+ * (nothing is launched), DUO_ERR_HIP if the launch fails. */
+duo_status duo_read_probe(const void* src, uint64_t bytes, uint32_t* flag, int32_t blocks,
+                          void* stream);
+
 /* ---- From trained gates to the deployed head split (one-time preprocessing) ---- */
 
 /* Retrieval/streaming assignment of every KV head of a model from its trained gates

@@ -17,14 +17,29 @@ from gpu_util import assert_close, make_cache, to_dev, torch_dtype
 pytestmark = pytest.mark.gpu
 
 
-def all_retrieval(name, batch, hq, hkv, d, S, R, seed, **kw):
-    return W.Workload(name, 1, batch, hq, hkv, d, "bf16", S, R, 0, 0, hkv,
+def all_retrieval(name, batch, hq, hkv, d, S, R, seed, dtype="bf16", **kw):
+    return W.Workload(name, 1, batch, hq, hkv, d, dtype, S, R, 0, 0, hkv,
                       fixed_mask=(tuple(range(hkv)),), seed=seed, **kw)
 
 
+def mixed_check_rows(c0, c1, group, n_random, rng, head_rows=4096):
+    """Positions a full-size chunk [c0, c1) is checked at: every position below ``head_rows``
+    (the first keys of the sequence, where few are visible), the first and last position of
+    every query tile of 128 / group positions, and ``n_random`` random positions."""
+    qpb = 128 // group
+    starts = np.arange(c0, c1, qpb)
+    ends = np.minimum(starts + qpb, c1) - 1
+    head = np.arange(c0, min(c1, head_rows))
+    rnd = rng.integers(c0, c1, size=min(n_random, c1 - c0))
+    return np.unique(np.concatenate([head, starts, ends, rnd]))
+
+
 def run_mixed(w, lens, chunk, alpha, check_rows=None, out_dtype=torch.float32, seqwise=False,
-              rng_seed=0):
-    """Gate-mixed attention of prompts in chunks (appending each chunk after its call)."""
+              rng_seed=0, edges=False):
+    """Gate-mixed attention of prompts in chunks (appending each chunk after its call).
+    ``check_rows``: None = every row, int = that many random rows per chunk (with ``edges``,
+    the rows of ``mixed_check_rows``). The oracle runs over blocks of the sorted rows with the
+    keys up to each block's last position (later keys are masked for every one of them)."""
     cache = make_cache(w, out_dtype=out_dtype, capacity=max(lens) + 1)
     dt = torch_dtype(w.dtype)
     rng = np.random.default_rng(rng_seed)
@@ -48,11 +63,19 @@ def run_mixed(w, lens, chunk, alpha, check_rows=None, out_dtype=torch.float32, s
         for si, s in enumerate(seqs):
             outs[s][c0:c1] = got[si]
             kh, vh = W.tokens(w, "k", 0, s, 0, c1), W.tokens(w, "v", 0, s, 0, c1)
-            rows = (np.arange(c0, c1) if check_rows is None else
-                    np.unique(rng.integers(c0, c1, size=min(check_rows, c1 - c0))))
-            qa = W.tokens(w, "q", 0, s, 0, c1)[rows]
-            ref = O.gate_mixed_attention(qa, kh, vh, rows, np.arange(c1), alpha, w.sink, w.recent)
-            assert_close(got[si][rows - c0], ref, f"chunk [{c0},{c1}) seq {s}")
+            if check_rows is None:
+                rows = np.arange(c0, c1)
+            elif edges:
+                rows = mixed_check_rows(c0, c1, w.group, check_rows, rng)
+            else:
+                rows = np.unique(rng.integers(c0, c1, size=min(check_rows, c1 - c0)))
+            qall = W.tokens(w, "q", 0, s, 0, c1)
+            for i in range(0, len(rows), 256):
+                blk = rows[i:i + 256]
+                t1 = int(blk[-1]) + 1
+                ref = O.gate_mixed_attention(qall[blk], kh[:t1], vh[:t1], blk, np.arange(t1),
+                                             alpha, w.sink, w.recent)
+                assert_close(got[si][blk - c0], ref, f"chunk [{c0},{c1}) seq {s} rows {blk[0]}..")
     return outs, cache
 
 
@@ -109,11 +132,20 @@ def test_gate_mixed_rejects_streaming_layers_and_bad_gates():
         assert e.value.status == hsk.DUO_ERR_INVALID
 
 
+@pytest.mark.timeout(600)
 def test_gate_mixed_mha_32k_whole_sequence():
     """Identification-phase shape: a Llama-2-7B-shaped MHA layer (32 heads, d 128, sink 16 +
-    recent 512) over one 32,768-token sequence processed whole, gates drawn in [0, 1]; 64
-    sampled query rows, all 32 heads (the launch configuration the benchmark times)."""
+    recent 512) over one 32,768-token sequence processed whole, gates drawn in [0, 1] (the
+    launch configuration the benchmark times), all 32 heads: every row of the first 4,096
+    positions, the first and last row of every 128-row query tile, and 64 random rows."""
     base = W.workload("c2")
     w = all_retrieval("mixed-c2", 1, 32, 32, 128, 16, 512, seed=base.seed)
     alpha = np.random.default_rng(91).random(32).astype(np.float32)
-    run_mixed(w, [32768], 32768, alpha, check_rows=64)
+    run_mixed(w, [32768], 32768, alpha, check_rows=64, edges=True)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_gate_mixed_f32(d):
+    """float32 inputs: chunks over a growing full cache, gates across [0, 1]."""
+    w = all_retrieval("mixed-f32", 2, 8, 2, d, 4, 32, seed=93, dtype="f32")
+    run_mixed(w, [300, 300], 90, np.array([0.3, 1.0], dtype=np.float32))

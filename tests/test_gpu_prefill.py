@@ -15,16 +15,35 @@ from gpu_util import assert_close, make_cache, to_dev, torch_dtype
 pytestmark = pytest.mark.gpu
 
 
+def edge_rows(c0, c1, group, n_random, rng):
+    """Query positions a full-size prefill chunk [c0, c1) is checked at: every position of a
+    chunk that starts the sequence (where few keys are visible), otherwise the first and last
+    position of every query tile of 128 / group positions (the tiles the kernel works in,
+    counted from the chunk start; their rows meet the split key ranges' edges) plus
+    ``n_random`` random positions."""
+    if c0 == 0:
+        return np.arange(c0, c1)
+    qpb = 128 // group
+    starts = np.arange(c0, c1, qpb)
+    ends = np.minimum(starts + qpb, c1) - 1
+    rnd = rng.integers(c0, c1, size=min(n_random, c1 - c0))
+    return np.unique(np.concatenate([starts, ends, rnd]))
+
+
 def run_prefill(w, lens, chunk, layer=0, check_rows=None, cache=None, seqwise=False,
-                out_dtype=torch.float32, rng_seed=0, mode="window"):
+                out_dtype=torch.float32, rng_seed=0, mode="window", edges=False,
+                max_abs=None):
     """Prefill prompts of lengths ``lens`` in chunks of ``chunk``; returns the outputs.
 
     ``mode`` is the streaming-head prefill mode: "window" (per-query sink + recent mask) or
     "chunk" (the pruned cache before the chunk plus the chunk causally).
 
-    ``check_rows``: None = every row, int = that many random rows per chunk and sequence.
+    ``check_rows``: None = every row, int = that many random rows per chunk and sequence
+    (with ``edges``: every row of the first chunk, the first and last row of every query
+    tile of the others, plus that many random rows; see ``edge_rows``).
     With ``seqwise`` every sequence is prefilled by its own calls (ragged prompts);
-    otherwise all sequences share the chunk calls (equal lengths).
+    otherwise all sequences share the chunk calls (equal lengths). ``max_abs``: a tighter
+    bound on the largest absolute error of every chunk (fp32 inputs).
     """
     if cache is None:
         cache = make_cache(w, out_dtype=out_dtype, capacity=max(lens) + 1, streaming_prefill=mode)
@@ -62,13 +81,17 @@ def run_prefill(w, lens, chunk, layer=0, check_rows=None, cache=None, seqwise=Fa
             vh = W.tokens(w, "v", layer, s, 0, c1)
             if check_rows is None:
                 rows = np.arange(c0, c1)
+            elif edges:
+                rows = edge_rows(c0, c1, w.group, check_rows, rng)
             else:
                 rows = np.unique(rng.integers(c0, c1, size=min(check_rows, c1 - c0)))
             qa = W.tokens(w, "q", layer, s, 0, c1)[rows]
             ref, ref_lse = O.attention(qa, kh, vh, rows, np.arange(c1), mask, w.sink, w.recent,
                                        chunk_start=c0 if mode == "chunk" else None)
-            assert_close(got[si][rows - c0], ref, f"chunk [{c0},{c1}) seq {s} out")
+            err = assert_close(got[si][rows - c0], ref, f"chunk [{c0},{c1}) seq {s} out")
             assert_close(got_lse[si][rows - c0], ref_lse, f"chunk [{c0},{c1}) seq {s} lse")
+            if max_abs is not None:
+                assert err <= max_abs, f"chunk [{c0},{c1}) seq {s}: max abs err {err:.3e}"
     return outs, lses, cache
 
 
@@ -127,14 +150,53 @@ def test_prefill_equals_decode_sequence():
     assert np.max(np.abs(outs[0] - dec)) < 4e-3
 
 
+@pytest.mark.timeout(600)
 def test_prefill_c2_mha_32k_in_4k_chunks():
     """Llama-2-7B-shaped MHA layer: 32,768-token prompt in 8 chunks of 4,096 (the launch
-    configuration of the benchmark); 64 sampled query rows per chunk, all 32 heads."""
+    configuration of the benchmark), all 32 heads: every row of the first chunk, the first
+    and last row of every 128-row query tile of the other chunks, and 64 random rows."""
     w = W.workload("c2")
-    run_prefill(w, [w.prefill_len], w.prefill_chunk, check_rows=64)
+    run_prefill(w, [w.prefill_len], w.prefill_chunk, check_rows=64, edges=True)
 
 
 def test_prefill_gqa_8k_in_2k_chunks():
-    """Llama-3-8B-shaped GQA layer, 8,192-token prompt in 2,048-token chunks."""
+    """Llama-3-8B-shaped GQA layer, 8,192-token prompt in 2,048-token chunks: every row of the
+    first chunk, tile edges and 64 random rows of the others."""
     w = W.workload("c3").with_(context=8192)
-    run_prefill(w, [8192], 2048, check_rows=64)
+    run_prefill(w, [8192], 2048, check_rows=64, edges=True)
+
+
+# ---- fp32 inputs (v_mfma_f32_16x16x4_f32 path) ----------------------------------------------
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_prefill_f32_variants(d, G):
+    """Every built (head_dim, group) variant with float32 inputs; chunks that straddle the
+    sink and the window, 64-row query tiles and 32-key tiles."""
+    w = W.Workload("prefill-f32-variant", 1, 2, 2 * G, 2, d, "f32", 4, 32, 0, 0, 1,
+                   fixed_mask=((1,),), seed=61 + G)
+    run_prefill(w, [300, 300], 70, max_abs=1e-4)
+
+
+@pytest.mark.parametrize("chunk", [1, 64, 1024])
+def test_prefill_f32_tiny_gqa_1024(chunk):
+    """The tiny GQA layer (8 q / 2 kv heads, d 64, float32, KV head 0 retrieval, sink 4 +
+    recent 32): a 1,024-token prompt in chunks of 1, 64 and 1,024, every row checked, at the
+    float32 bar of 1e-4."""
+    w = W.workload("c1")
+    run_prefill(w, [1024], chunk, max_abs=1e-4)
+
+
+@pytest.mark.parametrize("S,R", [(0, 1), (16, 64), (70, 5)])
+def test_prefill_f32_sink_recent_ragged(S, R):
+    """float32 inputs: S/R around the 32-key tile, ragged prompts in per-sequence calls."""
+    w = W.Workload("prefill-f32-sr", 1, 3, 8, 4, 128, "f32", S, R, 0, 0, 2,
+                   fixed_mask=((0, 3),), seed=63)
+    run_prefill(w, [260, 37, 129], 50, seqwise=True, max_abs=1e-4)
+
+
+def test_prefill_f32_chunk_mode():
+    """float32 inputs with chunk-granular streaming heads."""
+    w = W.Workload("prefill-f32-chunk", 1, 2, 8, 2, 64, "f32", 4, 28, 0, 0, 1,
+                   fixed_mask=((0,),), seed=65)
+    run_prefill(w, [300, 300], 70, mode="chunk", max_abs=1e-4)

@@ -263,3 +263,18 @@ def test_error_paths_leave_state_unchanged():
     assert np.array_equal(fc.lengths(), before)
     assert L.duo_cache_destroy(None) == N.DUO_OK
     fc.close()
+
+
+def test_read_probe_rejects_bad_arguments():
+    """The streaming-read probe checks its arguments before launching anything."""
+    L = N.lib()
+    vp = ctypes.c_void_p
+    big = vp(1 << 40)
+    flag = vp((1 << 40) + 4096)
+    assert L.duo_read_probe(None, 1024, flag, 0, None) == N.DUO_ERR_INVALID
+    assert L.duo_read_probe(big, 1024, None, 0, None) == N.DUO_ERR_INVALID
+    assert L.duo_read_probe(vp((1 << 40) + 8), 1024, flag, 0, None) == N.DUO_ERR_INVALID
+    assert L.duo_read_probe(big, 1000, flag, 0, None) == N.DUO_ERR_INVALID
+    assert L.duo_read_probe(big, 0, flag, 0, None) == N.DUO_ERR_INVALID
+    assert L.duo_read_probe(big, 1024, flag, -1, None) == N.DUO_ERR_INVALID
+    assert L.duo_read_probe(big, 1024, vp((1 << 40) + 4098), 0, None) == N.DUO_ERR_INVALID
