@@ -210,6 +210,22 @@ def duo_attn_decode(cache: DuoCache, layer: int, q: torch.Tensor, out=None, lse=
     return out
 
 
+def duo_attn_decode_noalloc(cache: DuoCache, layer: int, q: torch.Tensor, out: torch.Tensor,
+                            lse=None, stream=None):
+    """``duo_attn_decode`` whose split-K partials live in the library's static device scratch
+    (no allocation in the call); ``out`` must be given."""
+    _check_tensor(q, (cache.batch, cache.hq, cache.d), cache.dtype, cache.device, "q")
+    _check_tensor(out, (cache.batch, cache.hq, cache.d), cache.out_dtype, cache.device, "out")
+    lse_ptr = None
+    if lse is not None:
+        _check_tensor(lse, (cache.batch, cache.hq), torch.float32, cache.device, "lse")
+        lse_ptr = lse.data_ptr()
+    check(lib().duo_attn_decode_noalloc(cache.handle, layer, ctypes.c_void_p(q.data_ptr()),
+                                        ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(lse_ptr),
+                                        _stream(stream)), "duo_attn_decode_noalloc")
+    return out
+
+
 def duo_decode_step(cache: DuoCache, layer: int, q: torch.Tensor, k: torch.Tensor,
                     v: torch.Tensor, out=None, lse=None, stream=None):
     """Append one token per sequence and decode it in one pass: q ``[B, Hq, d]``,

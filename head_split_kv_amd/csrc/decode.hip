@@ -19,6 +19,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstring>
+#include <mutex>
 
 #include "duo_internal.h"
 
@@ -1208,6 +1209,30 @@ int dispatch(int dtype, int head_dim, int group, bool query, const DecodeArgs* a
 int launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group, void* stream,
                   const KernelMarks& marks) {
   return dispatch(dtype, head_dim, group, false, &a, stream, &marks);
+}
+
+// Split-K partials of duo_attn_decode_noalloc: a file-scope device array, one copy per GPU
+// the library runs on, held until the process ends. On the host `scratch` names a stand-in,
+// not the device copy, so host code never passes it to a kernel: its device address is looked
+// up once per device with hipGetSymbolAddress (with that device current) and kept here.
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+int static_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t rc = hipGetDevice(&dev);
+  if (rc != hipSuccess) return (int)rc;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    rc = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (rc != hipSuccess) return (int)rc;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return 0;
 }
 
 int decode_resident_blocks(int dtype, int head_dim, int group, bool q4) {

@@ -81,9 +81,17 @@ KernelMarks next_marks(duo_cache* c, int kind) {
   return m;
 }
 
-// Shared by duo_attn_decode (k == v == null) and duo_decode_step.
+// Bytes of split-K partials for `stride` partials per (sequence, query head): o [B][Hq]
+// [stride][D] floats, then, 256-byte aligned, (m, l) [B][Hq][stride][2].
+uint64_t partial_bytes(const duo_cache* c, uint64_t stride) {
+  const uint64_t rows = (uint64_t)c->cfg.batch * c->cfg.num_q_heads * stride;
+  return (rows * c->cfg.head_dim * 4 + kAlign - 1) / kAlign * kAlign + rows * 2 * 4;
+}
+
+// Shared by duo_attn_decode (k == v == null), duo_decode_step and, with use_static,
+// duo_attn_decode_noalloc (partials in the static scratch instead of the arena's workspace).
 duo_status decode_impl(duo_cache* c, int32_t layer, const void* q, const void* k, const void* v,
-                       void* out, float* lse, void* stream) {
+                       void* out, float* lse, void* stream, bool use_static = false) {
   if (!layer_ok(c, layer) || !q || !out || !aligned16(q) || !aligned16(out) || !aligned4(lse))
     return DUO_ERR_INVALID;
   const bool fused = k != nullptr;
@@ -140,6 +148,24 @@ duo_status decode_impl(duo_cache* c, int32_t layer, const void* q, const void* k
                                         split_cap,
                                         decode_resident_blocks(c->cfg.dtype, c->cfg.head_dim,
                                                                group, q4));
+  if (use_static) {
+    // partials per (sequence, query head): the splits (plus the residual's on a 4-bit
+    // cache) or a 4-bit streaming window's blocks; fewer splits until they fit the scratch
+    const int32_t extra = q4 ? 1 : 0;
+    int32_t stride = std::max(a.nsplit + extra, a.nss);
+    while (stride > 1 && partial_bytes(c, stride) > kScratchBytes) --stride;
+    const bool fits = partial_bytes(c, stride) <= kScratchBytes;
+    if (q4 && (stride < 2 || !fits)) return DUO_ERR_CAPACITY;
+    if (!fits) stride = 1;  // one split per head: outputs are written directly, no partials
+    a.nsplit = std::max(1, std::min(a.nsplit, stride - extra));
+    a.nss = std::min(a.nss, stride);
+    void* base = nullptr;
+    if (static_scratch(&base) != 0) return DUO_ERR_HIP;
+    const uint64_t rows = (uint64_t)a.B * a.Hq * stride;
+    a.max_splits = stride;
+    a.part_o = (float*)base;
+    a.part_ml = (float*)((char*)base + (rows * c->cfg.head_dim * 4 + kAlign - 1) / kAlign * kAlign);
+  }
   a.scale_log2 = (float)((double)c->scale * 1.4426950408889634);
   a.out_f32 = c->cfg.out_dtype == DUO_F32;
   for (int k = 0; k < kMaxKvHeads; ++k) {
@@ -270,6 +296,11 @@ duo_status duo_kv_append(duo_cache* c, int32_t layer, int32_t seq, const void* k
 duo_status duo_attn_decode(duo_cache* c, int32_t layer, const void* q, void* out, float* lse,
                            void* stream) {
   return decode_impl(c, layer, q, nullptr, nullptr, out, lse, stream);
+}
+
+duo_status duo_attn_decode_noalloc(duo_cache* c, int32_t layer, const void* q, void* out,
+                                   float* lse, void* stream) {
+  return decode_impl(c, layer, q, nullptr, nullptr, out, lse, stream, true);
 }
 
 duo_status duo_decode_step(duo_cache* c, int32_t layer, const void* q, const void* k,

@@ -184,6 +184,12 @@ int record_event(void* event, void* stream);
 // Sum of the elapsed times of the pairs (ev[2i], ev[2i+1]), i < pairs, after waiting for
 // the last one.
 int pairs_elapsed_ms(const std::vector<void*>& ev, int pairs, double* total_ms);
+// Static split-K scratch of duo_attn_decode_noalloc (decode.hip): its size, and the device
+// address of the current device's copy, looked up on the first call on each device (a
+// hipError_t value as int).
+constexpr uint64_t kScratchBytes = 8ull << 20;
+constexpr int kMaxDevices = 64;
+int static_scratch(void** ptr);
 // Decode blocks of this variant (the 4-bit kernel when q4) that are resident on the device
 // at once, counting at most two per CU (512 if unknown): the size of one round of splits.
 int decode_resident_blocks(int dtype, int head_dim, int group, bool q4);

@@ -175,6 +175,20 @@ duo_status duo_kv_append(duo_cache* cache, int32_t layer, int32_t seq, const voi
 duo_status duo_attn_decode(duo_cache* cache, int32_t layer, const void* q, void* out,
                            float* lse, void* stream);
 
+/* duo_attn_decode for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Same arguments, layouts and
+ * result (within floating-point rounding of the split count), but the split-K partials live in
+ * a static device array of the library (8 MiB per GPU it runs on, kept until the process
+ * ends) instead of the cache's workspace; the call itself allocates and frees nothing. The
+ * split count is capped so that batch * num_q_heads * parts * (head_dim + 2) * 4 bytes fit in
+ * the array (parts = splits, plus one for a 4-bit cache's residual rows); DUO_ERR_CAPACITY when
+ * not even the least a 4-bit cache needs (two parts) fits, nothing launched. Every call on one
+ * GPU shares that GPU's array and nothing in it needs to start at zero, but calls that overlap
+ * on one GPU (other streams, other caches) race on it. The first call on each device looks the
+ * array's device address up (DUO_ERR_HIP if that fails). */
+duo_status duo_attn_decode_noalloc(duo_cache* cache, int32_t layer, const void* q, void* out,
+                                   float* lse, void* stream);
+
 /* One decoding step with its append fused in (explainer, "Decoding Procedure" steps 1-5):
  * the same result and cache state as duo_kv_append(cache, layer, -1, k, v, 1, stream)
  * followed by duo_attn_decode(cache, layer, q, out, lse, stream), in one pass over the
