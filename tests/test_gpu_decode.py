@@ -224,3 +224,44 @@ def test_decode_c5_1m_context(key, history_1m):
             assert_close(got[hq], ref, f"{key} step {s} kv {j}")
             assert_close(got_lse[hq], ref_lse, f"{key} step {s} kv {j} lse")
         _progress(f"{key}: step {s} checked")
+
+
+def test_decode_split_merge_reads_only_its_own_call():
+    """Back-to-back calls that share the cache's split-K workspace, at automatic, 48 and 3
+    splits: every call's outputs match the oracle, so no merge reads a partial left by the
+    call before. The queries alternate between unrelated draws (one scaled by -3) and two
+    layers of different lengths, so stale partials would be far off."""
+    import head_split_kv_amd as hsk
+    w = W.Workload("decode-fused-merge", 2, 2, 32, 8, 128, "bf16", 16, 64, 0, 1, 4, seed=111)
+    lens_by_layer = [[20000, 3000], [9000, 15000]]
+    cache = make_cache(w, capacity=20001, layers=2)
+    for layer in range(2):
+        fill(cache, w, layer, lens_by_layer[layer])
+    masks = W.retrieval_mask(w)
+    hist = {}
+    for layer in range(2):
+        q, k, v, _ = step_inputs(w, layer, lens_by_layer[layer])
+        cache.kv_append(layer, k, v)
+        hist[layer] = [(W.tokens(w, "k", layer, b, 0, n + 1), W.tokens(w, "v", layer, b, 0, n + 1))
+                       for b, n in enumerate(lens_by_layer[layer])]
+    rng = np.random.default_rng(5)
+    for splits in (0, 48, 3):
+        hsk.duo_set_decode_splits(cache, splits)
+        for rep in range(4):
+            layer = rep % 2
+            qh = rng.standard_normal((w.batch, w.hq, w.d)).astype(np.float32)
+            qh = W.bf16_round(qh * (1.0 if rep < 2 else -3.0))
+            out = cache.attn_decode(layer, to_dev(qh, torch.bfloat16))
+            got = out.float().cpu().numpy()
+            for b in range(w.batch):
+                kh, vh = hist[layer][b]
+                ref, _ = O.decode_step(qh[b], kh, vh, masks[layer], w.sink, w.recent)
+                assert_close(got[b], ref, f"splits {splits} call {rep} layer {layer} seq {b}")
+
+
+def test_decode_wide_grid():
+    """A batch whose blocks cannot all be resident at once (16 sequences x 4 retrieval heads x
+    64 forced splits): the splits run in several rounds and their merge still matches the
+    oracle."""
+    w = W.Workload("decode-wide", 1, 16, 32, 8, 128, "bf16", 16, 64, 0, 2, 4, seed=113)
+    run_decode(w, [3000 + 97 * b for b in range(16)], 2, splits=64)
