@@ -255,10 +255,17 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
     return i < a.m ? c0 + i : kNoPos;
   };
 
-  // Per-lane DMA geometry: for 1 KB block i of this wave, the tile row this lane copies and
-  // the byte offset of the logical chunk that lands in this lane's (swizzled) LDS slot.
-  auto dma_row = [&](int i) { return (wave * kDma + i) * Gm::kRowsPerKb + lane / NCH; };
-  auto dma_col = [&](int i) { return ((lane % NCH) ^ swz<NCH>(dma_row(i))) * 16; };
+  // Per-lane DMA geometry, fixed for the block: for 1 KB block i of this wave, the tile row
+  // this lane copies and the byte offset of the logical chunk that lands in this lane's
+  // (swizzled) LDS slot. The wave index is made explicitly uniform so that every LDS
+  // destination is scalar arithmetic.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  int dma_r[kDma], dma_c[kDma];
+#pragma unroll
+  for (int i = 0; i < kDma; ++i) {
+    dma_r[i] = (wave_u * kDma + i) * Gm::kRowsPerKb + lane / NCH;
+    dma_c[i] = ((lane % NCH) ^ swz<NCH>(dma_r[i])) * 16;
+  }
   // Source of tile ti: base pointers, row stride, first source row and the number of rows
   // that hold data (later rows are clamped onto the last one, or onto row 0 for empty
   // streaming slots: finite data in bounds whose weight is zero).
@@ -278,21 +285,27 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
       nrows = a.m - row0;
     }
   };
-  auto src_row = [&](int r, int row0, int nrows) {
-    return r < nrows ? row0 + r : (nrows > 0 ? row0 + nrows - 1 : 0);
-  };
-  // One tensor of tile ti into LDS (rows past the data clamped).
+  // One tensor of tile ti into LDS (rows past the data clamped onto the last one; a batch
+  // past the last tile reads row 0 and is never used). The tile's first row is a uniform
+  // base and each lane adds a 32-bit offset of one 24-bit multiply-add (tile rows < 64,
+  // row strides < 2^24), so issuing a DMA costs about two VALU operations.
   auto issue_one = [&](int ti, bool is_v, char* dst) {
     const char *kb, *vb;
     int64_t stride;
     int row0, nrows;
     tile_src(ti, kb, vb, stride, row0, nrows);
-    const char* src = is_v ? vb : kb;
+    if (nrows <= 0) {
+      row0 = 0;
+      nrows = 1;
+    }
+    const char* base = (is_v ? vb : kb) + (int64_t)row0 * stride;
+    const uint32_t st = (uint32_t)stride;
 #pragma unroll
     for (int i = 0; i < kDma; ++i) {
-      const int sr = src_row(dma_row(i), row0, nrows);
-      __builtin_amdgcn_global_load_lds((const void*)(src + sr * stride + dma_col(i)),
-                                       (lds_void_t*)(dst + (wave * kDma + i) * 1024), 16, 0, 0);
+      const uint32_t r = (uint32_t)min(dma_r[i], nrows - 1);
+      const uint32_t off = __umul24(r, st) + (uint32_t)dma_c[i];
+      __builtin_amdgcn_global_load_lds((const void*)(base + off),
+                                       (lds_void_t*)(dst + (wave_u * kDma + i) * 1024), 16, 0, 0);
     }
   };
   // Key positions of a tile (LDS, for the masks). Written before the iteration's DMAs are
