@@ -29,10 +29,11 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
 ]
-# Per-source extra flags. decode.hip: the leading scalar kernel arguments (the work-item
-# decomposition) arrive preloaded in SGPRs on gfx950, so a block's first argument loads do not
-# wait on an earlier one.
-HIP_EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=6"]}
+# Per-source extra flags. decode.hip: the leading scalar kernel arguments arrive preloaded in
+# SGPRs on gfx950 (up to 16 dwords): the decode kernels' work-item decomposition, so that a
+# block's first argument loads do not wait on an earlier one, and every argument of the split
+# merge kernel.
+HIP_EXTRA = {"decode.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include")]
 
 

@@ -1034,37 +1034,35 @@ __global__ void __launch_bounds__(kThreads, 2)
 // log-sum-exp, issuing the loads of kMergeBatch splits together, and the waves combine
 // through LDS; with up to 128 splits every wave waits on memory once. Empty splits
 // (m = kMInit, l = 0) weigh zero. A separate launch: the partials need no fences.
+// Its arguments are 14 dwords of leading scalars, all preloaded into SGPRs (16 user SGPRs,
+// two of them the argument pointer; the build asks for the preload in this file), and the
+// grid is (G x 64-column slices, KV head, sequence), so a block reaches its first partial
+// load with no memory access and no division. ret_mask bit j marks KV head j as retrieval (it
+// merges ret_parts partials, a streaming head str_parts); blocks of heads with a single part
+// return at once.
 constexpr int kMergeWaves = 8;
 constexpr int kMergeThreads = kMergeWaves * 64;
 constexpr int kMergeBatch = 16;
 
-// Leading arguments as for decode_kernel, the last one a.q4.
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool OutF32>
 __global__ void __launch_bounds__(kMergeThreads)
-    merge_kernel(int32_t lead_nsplit, int32_t lead_hr, int32_t lead_hs, int32_t lead_b,
-                 int32_t lead_nss, int32_t lead_q4, DecodeArgs a) {
+    merge_kernel(uint64_t ret_mask, int32_t ret_parts, int32_t str_parts, int32_t Hq,
+                 int32_t max_splits, const float* part_o, const float* part_ml, void* out,
+                 float* lse) {
   __shared__ float s_m[kMergeWaves], s_l[kMergeWaves];
   __shared__ float s_o[kMergeWaves][64];
   constexpr int kSlices = D / 64;
+  const int j = blockIdx.y;
+  const int nsplit = ((ret_mask >> j) & 1) ? ret_parts : str_parts;
+  if (nsplit <= 1) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int slice = blockIdx.x % kSlices;
-  // (b, retrieval index, g) of the split retrieval heads, then (b, streaming index, g) of the
-  // split streaming heads
-  const int ret_parts = lead_nsplit + (lead_q4 ? 1 : 0);  // 4-bit: plus the residual block's
-  const int n_ret_q = ret_parts > 1 ? lead_b * lead_hr * G : 0;
-  int qi = blockIdx.x / kSlices;
-  const bool ret = qi < n_ret_q;
-  if (!ret) qi -= n_ret_q;
-  const int Hc = ret ? lead_hr : lead_hs;
-  const int g = qi % G;
-  const int r = (qi / G) % Hc;
-  const int b = qi / (G * Hc);
-  const int h = (ret ? a.ret_kv[r] : a.str_kv[r]) * G + g;
-  const int nsplit = ret ? ret_parts : lead_nss;
-  const int64_t p0 = ((int64_t)b * a.Hq + h) * a.max_splits;
+  const int g = blockIdx.x / kSlices, slice = blockIdx.x % kSlices;
+  const int b = blockIdx.z;
+  const int h = j * G + g;
+  const int64_t p0 = ((int64_t)b * Hq + h) * max_splits;
   const int d = slice * 64 + lane;
-  const float* po = a.part_o + p0 * D + d;
-  const float2* pml = reinterpret_cast<const float2*>(a.part_ml) + p0;
+  const float* po = part_o + p0 * D + d;
+  const float2* pml = reinterpret_cast<const float2*>(part_ml) + p0;
 
   float M = kMInit, L = 0.f, O = 0.f;
   for (int s0 = wave; s0 < nsplit; s0 += kMergeWaves * kMergeBatch) {
@@ -1109,9 +1107,8 @@ __global__ void __launch_bounds__(kMergeThreads)
     Lt = __builtin_fmaf(sc, s_l[w], Lt);
     Ot = __builtin_fmaf(sc, s_o[w][lane], Ot);
   }
-  store_out<T>(a.out, ((int64_t)b * a.Hq + h) * D + d, Ot / Lt, a.out_f32);
-  if (slice == 0 && lane == 0 && a.lse)
-    a.lse[(int64_t)b * a.Hq + h] = (Mt + __builtin_log2f(Lt)) * kLn2;
+  store_out<T>(out, ((int64_t)b * Hq + h) * D + d, Ot / Lt, OutF32);
+  if (slice == 0 && lane == 0 && lse) lse[(int64_t)b * Hq + h] = (Mt + __builtin_log2f(Lt)) * kLn2;
 }
 
 template <typename T, int D, int G>
@@ -1119,11 +1116,9 @@ struct Variant {
   static constexpr int LPT = lanes_per_token<T, D, G>();
   static constexpr int NS = stages<T, D, G>();
 
-  // Decode blocks to size one round of splits for (of the 4-bit kernel when q4), queried once
-  // per process: the blocks that fit on the device at once, counting at most two per CU. Two
-  // waves per SIMD already keep enough bytes in flight to cover the memory latency; where
-  // more fit (the G = 1 kernel fits four), more and shorter splits only add start-up and
-  // partials (the 32K MHA layer: 26.8 us with 125 splits, 24.6 us with 61).
+  // Decode blocks that fit on the device at once (of the 4-bit kernel when q4), counting at
+  // most two per CU, queried once per process. The host sizes one round of splits from it
+  // (two blocks per CU for a batch, one for a single sequence).
   static int resident_blocks(bool q4) {
     static int cached[2] = {0, 0};
     if (cached[q4]) return cached[q4];
@@ -1164,12 +1159,18 @@ struct Variant {
     if (marks.end) (void)hipEventRecord((hipEvent_t)marks.end, (hipStream_t)stream);
     // split heads (retrieval heads when nsplit > 1, streaming heads when nss > 1)
     const int ret_parts = a.nsplit + (a.q4 ? 1 : 0);
-    const int64_t mheads = (ret_parts > 1 ? (int64_t)a.Hr : 0) + (a.nss > 1 ? (int64_t)a.Hs : 0);
-    if (mheads > 0) {
-      const int64_t mblocks = (int64_t)a.B * mheads * G * (D / 64);
-      hipLaunchKernelGGL((merge_kernel<T, D, G>), dim3((unsigned)mblocks),
-                         dim3(kMergeThreads), 0, (hipStream_t)stream, a.nsplit, a.Hr, a.Hs, a.B, a.nss,
-                           a.q4, a);
+    if ((ret_parts > 1 && a.Hr > 0) || (a.nss > 1 && a.Hs > 0)) {
+      uint64_t ret_mask = 0;
+      for (int r = 0; r < a.Hr; ++r) ret_mask |= 1ull << a.ret_kv[r];
+      const dim3 grid(G * (D / 64), a.Hkv, a.B);
+      if (a.out_f32)
+        hipLaunchKernelGGL((merge_kernel<T, D, G, true>), grid, dim3(kMergeThreads), 0,
+                           (hipStream_t)stream, ret_mask, ret_parts, a.nss, a.Hq, a.max_splits,
+                           (const float*)a.part_o, (const float*)a.part_ml, a.out, a.lse);
+      else
+        hipLaunchKernelGGL((merge_kernel<T, D, G, false>), grid, dim3(kMergeThreads), 0,
+                           (hipStream_t)stream, ret_mask, ret_parts, a.nss, a.Hq, a.max_splits,
+                           (const float*)a.part_o, (const float*)a.part_ml, a.out, a.lse);
     }
     return (int)hipGetLastError();
   }
