@@ -421,10 +421,15 @@ def kv4_history(x_hist, n: int, is_key: bool) -> np.ndarray:
     return out
 
 
-def decode_step_kv4(q, k_hist, v_hist, retrieval, sink, recent, scale=None):
+def decode_step_kv4(q, k_hist, v_hist, retrieval, sink, recent, scale=None, rope_theta=None):
     """``decode_step`` with the retrieval heads' full caches stored in 4 bits: every
     retrieval KV head attends over ``kv4_history`` of its keys and values; streaming heads
-    (constant-size caches, kept exact) as before."""
+    (constant-size caches, kept exact) as before.
+
+    With ``rope_theta`` the keys of every head are pre-RoPE: the 4-bit codes are taken of the
+    keys as given, and each key that attention reads (dequantized on retrieval heads, exact on
+    streaming heads) is rotated at its own position by ``rope`` (see below); ``q`` is the
+    query after its own rotation."""
     k = np.asarray(k_hist, dtype=np.float64).copy()
     v = np.asarray(v_hist, dtype=np.float64).copy()
     n = k.shape[0]
@@ -432,4 +437,42 @@ def decode_step_kv4(q, k_hist, v_hist, retrieval, sink, recent, scale=None):
         if retrieval[j]:
             k[:, j] = kv4_history(k_hist[:, j], n, True)
             v[:, j] = kv4_history(v_hist[:, j], n, False)
+    if rope_theta:
+        k = rope(k, np.arange(n), rope_theta)
     return decode_step(q, k, v, retrieval, sink, recent, scale)
+
+
+# --------------------------------------------------------------------------------------------
+# Pre-RoPE keys in 4-bit caches
+# --------------------------------------------------------------------------------------------
+#
+# OpenReview thread, the authors' reply on combining DuoAttention with KV quantization: their
+# 4-bit results quantize the keys before the rotary position embedding (RoPE) is applied. The
+# pages name the technique only. Readings taken here:
+#   * the caller appends every key of the layer before RoPE and passes each query after RoPE
+#     at its own position (its usual form); attention rotates each key at its own position t:
+#     after dequantization on a retrieval head, the exact stored key on a streaming head (at
+#     its original position, as for the caller-rotated keys of the other caches);
+#   * RoPE in its rotate-half form: channel i < d/2 pairs with channel i + d/2, and the pair
+#     turns by the angle t * theta^(-2i/d), angles taken exactly (here in float64).
+
+def rope_angles(pos, d: int, theta: float) -> np.ndarray:
+    """float64 ``[len(pos), d/2]``: the angle of channel pair i at position t,
+    t * theta**(-2 i / d)."""
+    i = np.arange(d // 2, dtype=np.float64)
+    inv = np.power(float(theta), -2.0 * i / d)
+    return np.asarray(pos, dtype=np.float64)[:, None] * inv[None, :]
+
+
+def rope(x, pos, theta: float) -> np.ndarray:
+    """Rows ``x [n, ..., d]`` rotated at positions ``pos [n]``: channels (i, i + d/2) of row t
+    turn by ``rope_angles`` (x_i cos - x_{i+d/2} sin, x_i sin + x_{i+d/2} cos)."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    h = d // 2
+    a = rope_angles(pos, d, theta)
+    shape = (x.shape[0],) + (1,) * (x.ndim - 2) + (h,)
+    c = np.cos(a).reshape(shape)
+    s = np.sin(a).reshape(shape)
+    x1, x2 = x[..., :h], x[..., h:]
+    return np.concatenate([x1 * c - x2 * s, x1 * s + x2 * c], axis=-1)

@@ -616,6 +616,64 @@ def pin_kv4_decode():
     assert np.allclose(a, b, rtol=0, atol=1e-12)
 
 
+def pin_rope_complex_form():
+    """RoPE equals multiplying the complex channels z_i = x_i + i x_{i+d/2} by
+    exp(i t theta^(-2i/d)), written here with complex arithmetic and the exponent as
+    exp(-(2i/d) ln theta); it keeps norms and is the identity at position 0."""
+    rng = np.random.default_rng(61)
+    for d, theta in ((8, 10000.0), (16, 500000.0), (128, 500000.0)):
+        n = 9
+        x = rng.standard_normal((n, 3, d))
+        pos = np.array([0, 1, 2, 7, 100, 4097, 131071, 1 << 20, 3 * (1 << 19) + 5])
+        h = d // 2
+        w = np.exp(-(2.0 * np.arange(h) / d) * math.log(theta))
+        z = (x[..., :h] + 1j * x[..., h:]) * np.exp(1j * pos[:, None, None] * w[None, None, :])
+        want = np.concatenate([z.real, z.imag], axis=-1)
+        got = O.rope(x, pos, theta)
+        assert np.allclose(got, want, rtol=0, atol=1e-9)
+        assert np.allclose(np.linalg.norm(got, axis=-1), np.linalg.norm(x, axis=-1), atol=1e-9)
+        assert np.array_equal(O.rope(x[:1], [0], theta), x[:1])
+
+
+def pin_rope_relative_positions():
+    """A rotated query and key score depends on the positions only through their difference."""
+    rng = np.random.default_rng(62)
+    d, theta = 32, 10000.0
+    q = rng.standard_normal((1, d))
+    k = rng.standard_normal((1, d))
+    for s_, t, u in ((3, 11, 5), (0, 0, 12345), (700, 20, 1 << 16)):
+        a = O.rope(q, [s_], theta) @ O.rope(k, [t], theta).T
+        b = O.rope(q, [s_ + u], theta) @ O.rope(k, [t + u], theta).T
+        assert abs(a[0, 0] - b[0, 0]) < 1e-9
+    assert not np.allclose(O.rope(k, [5], theta), k)
+
+
+def pin_kv4_rope_decode():
+    """With pre-RoPE keys, keys that are exact in 4 bits (constant over each group's tokens,
+    per channel) decode as plain attention over keys rotated at their positions by the
+    complex form, the quantized and the residual tokens alike; streaming heads rotate their
+    exact keys the same way, and the rotation changes the result."""
+    rng = np.random.default_rng(63)
+    G = O.KV4_GROUP
+    n, Hkv, Gq, d, S, R, theta = 2 * G + 7, 2, 2, 16, 2, 8, 10000.0
+    q = _bf16_grid(rng, Hkv * Gq, d)
+    base = _bf16_grid(rng, 3, Hkv, d)
+    k = np.concatenate([np.repeat(base[0:1], G, 0), np.repeat(base[1:2], G, 0),
+                        np.repeat(base[2:3], n - 2 * G, 0)]) + 0.0
+    k[2 * G:] = _bf16_grid(rng, n - 2 * G, Hkv, d)  # the residual tokens need not be constant
+    v = np.repeat(_bf16_grid(rng, n, Hkv, 1), d, axis=2)
+    h = d // 2
+    w = np.exp(-(2.0 * np.arange(h) / d) * math.log(theta))
+    z = (k[..., :h] + 1j * k[..., h:]) * np.exp(1j * np.arange(n)[:, None, None] * w)
+    krot = np.concatenate([z.real, z.imag], axis=-1)
+    for mask in ([1, 0], [1, 1], [0, 1]):
+        a, _ = O.decode_step(q, krot, v, mask, S, R)
+        b, _ = O.decode_step_kv4(q, k, v, mask, S, R, rope_theta=theta)
+        assert np.allclose(a, b, rtol=0, atol=1e-9), mask
+        c, _ = O.decode_step_kv4(q, k, v, mask, S, R)
+        assert np.abs(b - c).max() > 1e-3
+
+
 PINS = [pin_cache_policy, pin_streaming_rows, pin_decode_scalar_bruteforce,
         pin_all_retrieval_is_causal_attention, pin_short_streaming_is_full,
         pin_no_sink_is_sliding_window, pin_fig5_worked_example, pin_memory_numbers,
@@ -624,7 +682,8 @@ PINS = [pin_cache_policy, pin_streaming_rows, pin_decode_scalar_bruteforce,
         pin_chunk_granular_fig5, pin_chunk_granular_gather, pin_chunk_granular_short_is_full,
         pin_retrieval_count_nearest, pin_binarize_bruteforce, pin_binarize_equation4,
         pin_head_reordering_preserves_layer, pin_gate_mixed_bruteforce, pin_kv4_nearest_level,
-        pin_kv4_axes_and_exact_grids, pin_kv4_groups_and_residual, pin_kv4_decode]
+        pin_kv4_axes_and_exact_grids, pin_kv4_groups_and_residual, pin_kv4_decode,
+        pin_rope_complex_form, pin_rope_relative_positions, pin_kv4_rope_decode]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -766,6 +825,35 @@ def _kv4_history_variant(swap_axes=False, quantize_tail=False, misaligned=False)
     return f
 
 
+def _rope_variant(interleaved=False, sign=1.0, exponent=2.0, offset=0):
+    def f(x, pos, theta):
+        x = np.asarray(x, dtype=np.float64)
+        d = x.shape[-1]
+        h = d // 2
+        inv = np.power(float(theta), -exponent * np.arange(h) / d)
+        a = sign * (np.asarray(pos, dtype=np.float64) + offset)[:, None] * inv[None, :]
+        shape = (x.shape[0],) + (1,) * (x.ndim - 2) + (h,)
+        c, s_ = np.cos(a).reshape(shape), np.sin(a).reshape(shape)
+        if interleaved:
+            x1, x2 = x[..., 0::2], x[..., 1::2]
+            out = np.empty_like(x)
+            out[..., 0::2] = x1 * c - x2 * s_
+            out[..., 1::2] = x1 * s_ + x2 * c
+            return out
+        x1, x2 = x[..., :h], x[..., h:]
+        return np.concatenate([x1 * c - x2 * s_, x1 * s_ + x2 * c], axis=-1)
+    return f
+
+
+def _kv4_rope_before_quant(q, k_hist, v_hist, retrieval, sink, recent, scale=None,
+                           rope_theta=None):
+    k = np.asarray(k_hist, dtype=np.float64)
+    if rope_theta:
+        k = O.rope(k, np.arange(k.shape[0]), rope_theta).astype(np.float32)
+    return _ORIG_KV4(q, k, v_hist, retrieval, sink, recent, scale)
+
+
+_ORIG_KV4 = O.decode_step_kv4
 _ORIG_MSA = O.masked_softmax_attention
 _ORIG_BIN = O.binarize_gates
 _ORIG_MIX = O.gate_mixed_attention
@@ -806,6 +894,11 @@ MUTANTS = {
                             lambda q, k, v, qp, kp, a, S, R, scale=None: _ORIG_MIX(
                                 q, k, v, qp, kp, 1 - np.asarray(a), S, R, scale)),
     "mixed_unnormalized_blend": ("gate_mixed_attention", _mixed_unnormalized),
+    "rope_interleaved_pairs": ("rope", _rope_variant(interleaved=True)),
+    "rope_negative_angle": ("rope", _rope_variant(sign=-1.0)),
+    "rope_exponent_halved": ("rope", _rope_variant(exponent=1.0)),
+    "rope_position_plus_one": ("rope", _rope_variant(offset=1)),
+    "kv4_rope_before_quantization": ("decode_step_kv4", _kv4_rope_before_quant),
     "query_order_interleaved": ("query_head_order",
                                 lambda o, G: np.array([g * len(o) + j for j in o for g in range(G)])),
 }
