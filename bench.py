@@ -36,6 +36,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "decode-attn KV GB/s (% HBM peak) + µs/layer-step at 128K ctx; prefill TFLOP/s"
+ROPE_THETA = 500000.0  # RoPE base of the Llama-3-8B-shaped workload's pre-RoPE 4-bit leg
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 
@@ -61,16 +62,17 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--splits", type=int, default=0, help="force decode splits (0 = automatic)")
     p.add_argument("--unfused", action="store_true", help="time append + decode as two calls")
-    p.add_argument("--legs", default="decode,kv4,c4,prefill,reorder,probe,cpu",
+    p.add_argument("--legs", default="decode,kv4,kv4rope,c4,prefill,reorder,probe,cpu",
                    help="legs to run: decode (the headline, always run), kv4 (4-bit full "
-                        "caches), c4 (32 layers x batch 8, ragged), prefill (the legs of "
+                        "caches), kv4rope (4-bit with pre-RoPE keys), c4 (32 layers x batch 8, ragged), prefill (the legs of "
                         "--prefill-modes), reorder, probe (read and copy bandwidth), cpu "
                         "(the oracle on the host)")
     a = p.parse_args()
     legs = set(a.legs.split(","))
-    unknown = legs - {"decode", "kv4", "c4", "prefill", "reorder", "probe", "cpu"}
+    unknown = legs - {"decode", "kv4", "kv4rope", "c4", "prefill", "reorder", "probe", "cpu"}
     if unknown:
         p.error(f"unknown legs {sorted(unknown)}")
+    a.no_kv4rope = a.no_kv4 or "kv4rope" not in legs
     a.no_kv4 = a.no_kv4 or "kv4" not in legs
     a.no_prefill = a.no_prefill or "prefill" not in legs
     a.no_cpu = a.no_cpu or "cpu" not in legs
@@ -116,7 +118,7 @@ class Timer:
         return self.a.elapsed_time(self.b)
 
 
-def decode_leg(args, torch, hsk, W, N, kv_bits=0):
+def decode_leg(args, torch, hsk, W, N, kv_bits=0, rope_theta=0.0):
     w = W.workload(args.workload)
     L = args.layers
     # warm-up, the timed steps, then as many again timed one by one for the spread
@@ -129,7 +131,7 @@ def decode_leg(args, torch, hsk, W, N, kv_bits=0):
                          head_dim=w.d, sink=w.sink, recent=w.recent, capacity=cap,
                          retrieval_mask=[mask] * L, dtype=torch.bfloat16,
                          out_dtype=torch.bfloat16, device=dev, max_splits=1024,
-                         kv_bits=kv_bits)
+                         kv_bits=kv_bits, rope_theta=rope_theta)
     if args.splits:
         hsk.duo_set_decode_splits(cache, args.splits)
     t = time.time()
@@ -146,7 +148,8 @@ def decode_leg(args, torch, hsk, W, N, kv_bits=0):
     vs = torch.from_numpy(W.tokens(w, "v", 0, 0, n0, n0 + total_steps)).to(dev).to(torch.bfloat16)
     out = torch.empty((1, w.hq, w.d), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
-    log(f"decode leg{' (4-bit full caches)' if kv_bits == 4 else ''}: {w.name}, {L} replica "
+    kind = " (4-bit full caches" + (", pre-RoPE keys)" if rope_theta else ")") if kv_bits == 4 else ""
+    log(f"decode leg{kind}: {w.name}, {L} replica "
         f"layers filled to {n0} tokens in {time.time() - t:.1f}s")
 
     lib = N.lib()
@@ -660,6 +663,13 @@ def main():
             f"({dec['us_layer'] / dec4['us_layer']:.2f}x the bf16 step), {dec4['gbs']:.0f} GB/s of "
             f"stored bytes; split kernel {dec4['kern_us']:.2f} us = {dec4['kern_gbs']:.0f} GB/s; "
             f"one duo_attn_decode call {dec4['dec_us']:.2f} us")
+    dec4r = None
+    if not args.no_kv4rope:
+        dec4r = decode_leg(args, torch, hsk, W, N, kv_bits=4, rope_theta=ROPE_THETA)
+        log(f"decode, 4-bit full caches with pre-RoPE keys: {dec4r['us_layer']:.2f} "
+            f"us/layer-step, {dec4r['gbs']:.0f} GB/s of stored bytes; split kernel "
+            f"{dec4r['kern_us']:.2f} us = {dec4r['kern_gbs']:.0f} GB/s; one duo_attn_decode "
+            f"call {dec4r['dec_us']:.2f} us")
     modes = set(args.prefill_modes.split(","))
     # a failing leg ends the run with an error (no leg is dropped from the line silently)
     pre = None
@@ -777,6 +787,21 @@ def main():
                          "traffic": committed_traffic("decode.hip", f"decode_kv4_{args.workload}"),
                          "kernel": "decode_q4_kernel<d128, G4> (split attention kernel)",
                          "kernel_us": round(dec4["kern_us"], 3)},
+        },
+        "decode_kv4_rope": None if dec4r is None else {
+            "workload": "the same 4-bit decode with pre-RoPE keys (base 500,000): retrieval "
+                        "keys turned at their positions after dequantization, streaming keys "
+                        "turned when appended",
+            "us_per_layer_step": round(dec4r["us_layer"], 3),
+            "GBps": round(dec4r["gbs"], 1),
+            "stored_bytes_per_layer_step": int(dec4r["step_bytes"]),
+            "decode_call_us": round(dec4r["dec_us"], 3),
+            "roofline": {"bound": "hbm", "achieved": round(dec4r["kern_gbs"], 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(dec4r["kern_gbs"] / HBM_PEAK_GBS, 4),
+                         "traffic": None,
+                         "kernel": "decode_q4_kernel<d128, G4, pre-RoPE> (split attention kernel)",
+                         "kernel_us": round(dec4r["kern_us"], 3)},
         },
         "gate_mixed": None if mix is None else {
             "workload": "identification-phase attention: Llama-2-7B-shaped MHA layer, one "

@@ -46,13 +46,14 @@ class DuoConfig(ctypes.Structure):
         ("retrieval_mask", ctypes.POINTER(ctypes.c_uint8)),
         ("streaming_prefill", ctypes.c_int32),
         ("kv_bits", ctypes.c_int32),
+        ("rope_theta", ctypes.c_float),
     ]
 
 
 class DuoLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "arena_bytes", "full_k_off", "full_v_off", "str_k_off", "str_v_off", "slot_pos_off",
-        "seq_len_off", "workspace_off", "workspace_bytes")]
+        "seq_len_off", "workspace_off", "workspace_bytes", "rope_off", "rope_bytes")]
 
 
 class DuoError(RuntimeError):

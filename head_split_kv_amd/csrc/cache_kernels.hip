@@ -44,6 +44,40 @@ __global__ void __launch_bounds__(kThreads) set_lengths_kernel(SetLenArgs a) {
   if (s == 0) a.seq_len[b] = n;
 }
 
+// RopeGeom tables, one work item per (row, pair) of tau (rows 0..127) and base (rows 128..),
+// then the padding words of tau16: angles and their cos/sin in float64, rounded to float32
+// (base) or through float32 to fp16 (tau16).
+__global__ void __launch_bounds__(kThreads)
+    rope_table_kernel(uint32_t* tau16, float* base, int32_t D, int32_t nbase, double theta) {
+  const int half = D / 2;
+  const int64_t n_val = (int64_t)(kQ4Group + nbase) * half;
+  const int64_t total = n_val + kQ4Group * 4;
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < total;
+       u += (int64_t)gridDim.x * blockDim.x) {
+    if (u >= n_val) {
+      const int64_t k = u - n_val;
+      tau16[(k / 4) * (half + 4) + half + k % 4] = 0u;
+      continue;
+    }
+    const int64_t r = u / half;
+    const int i = (int)(u % half);
+    const double f = pow(theta, -2.0 * i / D);
+    const bool is_tau = r < kQ4Group;
+    const double ang = (is_tau ? (double)r : (double)kQ4Group * (double)(r - kQ4Group)) * f;
+    double sn, cs;
+    sincos(ang, &sn, &cs);
+    if (is_tau) {
+      uint16_t* row = (uint16_t*)(tau16 + r * (half + 4));
+      const int at = (i / 8) * 16 + 2 * (i % 4) + (i % 8) / 4;  // pair 8 b + w (+ 4): word w, half
+      row[at] = __builtin_bit_cast(uint16_t, (_Float16)(float)cs);
+      row[at + 8] = __builtin_bit_cast(uint16_t, (_Float16)(float)sn);
+    } else {
+      base[((r - kQ4Group) * half + i) * 2] = (float)cs;
+      base[((r - kQ4Group) * half + i) * 2 + 1] = (float)sn;
+    }
+  }
+}
+
 // One thread moves one 16-byte chunk of one K or V row. Work index (outer to inner):
 // tensor (K, V), sequence, token, KV head, chunk; consecutive threads read consecutive
 // bytes of the input. The extra nb*m work items at the end write the slot table.
@@ -107,6 +141,15 @@ int launch_reset(const ResetArgs& a, void* stream) {
   const int64_t work = a.n_slot > a.n_len ? a.n_slot : a.n_len;
   hipLaunchKernelGGL(reset_kernel, dim3(grid_for(work)), dim3(kThreads), 0,
                      (hipStream_t)stream, a);
+  return (int)hipGetLastError();
+}
+
+int launch_rope_tables(char* tables, int32_t D, int32_t nbase, double theta, void* stream) {
+  const RopeGeom g = rope_geom((uint64_t)(nbase - 1) * kQ4Group, (uint64_t)D);
+  const int64_t work = (int64_t)(kQ4Group + nbase) * (D / 2) + kQ4Group * 4;
+  hipLaunchKernelGGL(rope_table_kernel, dim3(grid_for(work)), dim3(kThreads), 0,
+                     (hipStream_t)stream, (uint32_t*)(tables + g.tau16),
+                     (float*)(tables + g.base), D, nbase, theta);
   return (int)hipGetLastError();
 }
 

@@ -499,6 +499,7 @@ __global__ void __launch_bounds__(kThreads, 2)
 // instruction reads one contiguous KB. The incomplete last group (bf16 residual rows) and the
 // streaming heads take the bf16 path, in blocks of their own.
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -521,9 +522,18 @@ constexpr int kBfStages = 6;  // bf16 row fragments in flight in decode_q4_kerne
 // in cache (the values are never used). 16 KB covers every offset a look-ahead adds.
 __device__ __attribute__((aligned(256))) uint32_t g_q4_idle[4096];
 
+// Pre-RoPE keys (kRope; a.rope_base and a.rope_tau16 set): a key of position t = 128 g + tau
+// is attended turned by RoPE at t, R(t) = R(128 g) R(tau) pair by pair, so a query q meets it
+// as R(-128 g) q . R(tau) k. Per group the query is turned by -128 g (float32 tables, fp16
+// operand) and the scales are no longer folded into it: each dequantized key c s + z is
+// formed in packed fp16 (a code OR 0x6400 reads as 1024 + c, exact, minus 1024) and turned
+// by tau from an fp16 table in LDS, and the MFMA takes the turned keys as its A operand in
+// real units. The bf16 rows (the residual group, streaming slots at the positions they hold,
+// a fused step's token) are turned in float32 and dotted with the query in float32; every
+// cache keeps the keys as given.
 // Leading arguments as for decode_kernel.
-template <int D, int G, int LPT, int NS>
-__global__ void __launch_bounds__(kThreads, 2)
+template <int D, int G, int LPT, int NS, bool kRope>
+__global__ void __launch_bounds__(kThreads, kRope ? 1 : 2)
     decode_q4_kernel(int32_t lead_nsplit, int32_t lead_hr, int32_t lead_hs, int32_t lead_b,
                      int32_t lead_nss, int32_t lead_fused, DecodeArgs a) {
   using T = uint16_t;
@@ -539,11 +549,13 @@ __global__ void __launch_bounds__(kThreads, 2)
   constexpr int kStep = 32;    // tokens per wave step
   constexpr int kSteps = kQ4Group / kStep;
   static_assert(G <= 16 && kSteps % 2 == 0, "query rows must fit the 16-row tile");
+  constexpr int kRotRow = D / 2 + 4;  // words of one tau16 row
 
   __shared__ float s_o[2 * kWaves][G][D];  // partials: bf16 path per wave, then MFMA path
   __shared__ float s_m[2 * kWaves][G];
   __shared__ float s_l[2 * kWaves][G];
   __shared__ __attribute__((aligned(16))) uint16_t s_q[G][D];
+  __shared__ __attribute__((aligned(16))) uint32_t s_rot[kRope ? kQ4Group * kRotRow : 4];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, grp = lane / LPT, sub = lane % LPT;
@@ -639,7 +651,9 @@ __global__ void __launch_bounds__(kThreads, 2)
   float mq = live ? kMInit : 1e30f;
   float thq = live ? kMInit : __builtin_inff();
   float lq = 0.f, zq = 0.f;
-  const float c2s = c2 * kTwo24;          // logit (log2 units) per unit of the raw product
+  // logit (log2 units) per unit of the raw product (codes read as multiples of 2^-24, or the
+  // turned keys in real units)
+  const float c2s = kRope ? c2 : c2 * kTwo24;
   const float inv_c2s = 1.f / c2s;
   f32x4_t oacc[CBK];  // O^T: lane holds channels 16 cb + 4 jj + i of query col
 #pragma unroll
@@ -667,6 +681,8 @@ __global__ void __launch_bounds__(kThreads, 2)
     const uint16_t* kpar = (const uint16_t*)(kq + a.q4_params);  // bf16 [group][2][D]
     // bf16 key scale and zero of this lane's operand channels 32 kc + 8 jj + e
     uint4 ps[KC], pz[KC];
+    // kRope: (cos, sin) of the group's base angle 128 g f_i of pairs 32 kh + 8 jj + 2 k, + 1
+    [[maybe_unused]] float4 bq[KC / 2][4];
     const char* idle = (const char*)g_q4_idle;
     auto load_params = [&](int gi) {
       const uint16_t* p = kpar + (int64_t)group_of(gi) * 2 * D;
@@ -676,10 +692,62 @@ __global__ void __launch_bounds__(kThreads, 2)
         ps[kc] = *(const uint4*)(p + ch);
         pz[kc] = *(const uint4*)(p + D + ch);
       }
+      if constexpr (kRope) {
+        const float4* bp = (const float4*)(a.rope_base + (int64_t)group_of(gi) * D);
+#pragma unroll
+        for (int kh = 0; kh < KC / 2; ++kh)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) bq[kh][k] = bp[(32 * kh + 8 * jj) / 2 + k];
+      }
     };
     half8_t qa[KC];  // B operand: Q'^T, channel slots of query col
     float bias;      // key-zero term of query col, in units of the raw product
+    // kRope: fp16 (scale, scale) and (zero, zero) of the channels of slot pair j of chunk kc
+    // (elements j and j + 4; the scale over 16 where the nibbles are high)
+    [[maybe_unused]] half2_t rs[KC][4], rz[KC][4];
     auto fold = [&]() {
+      if constexpr (kRope) {
+        // the query turned by -128 g: (q_i c + q_i' s, q_i' c - q_i s) for pair (i, i' = i + D/2)
+        const float qlive = live ? 1.f : 0.f;
+#pragma unroll
+        for (int kh = 0; kh < KC / 2; ++kh) {
+          const uint4 q1 = *(const uint4*)&s_q[live ? col : 0][32 * kh + 8 * jj];
+          const uint4 q2 = *(const uint4*)&s_q[live ? col : 0][32 * (kh + KC / 2) + 8 * jj];
+          const uint32_t w1[4] = {q1.x, q1.y, q1.z, q1.w}, w2[4] = {q2.x, q2.y, q2.z, q2.w};
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            const float a1 = qlive * __builtin_bit_cast(
+                                         float, (x & 1) ? w1[x >> 1] & 0xFFFF0000u : w1[x >> 1] << 16);
+            const float a2 = qlive * __builtin_bit_cast(
+                                         float, (x & 1) ? w2[x >> 1] & 0xFFFF0000u : w2[x >> 1] << 16);
+            const float4 bv = bq[kh][x >> 1];
+            const float cb = (x & 1) ? bv.z : bv.x, sb = (x & 1) ? bv.w : bv.y;
+            const int e = 2 * (x & 3) + (x >> 2);  // operand slot of element x
+            qa[kh][e] = (_Float16)__builtin_fmaf(a1, cb, a2 * sb);
+            qa[kh + KC / 2][e] = (_Float16)__builtin_fmaf(a2, cb, -a1 * sb);
+          }
+        }
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          const uint32_t sw[4] = {ps[kc].x, ps[kc].y, ps[kc].z, ps[kc].w};
+          const uint32_t zw[4] = {pz[kc].x, pz[kc].y, pz[kc].z, pz[kc].w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            // elements j and j + 4 sit in words j / 2 and j / 2 + 2, half j % 2
+            const uint32_t s0 = (j & 1) ? sw[j >> 1] & 0xFFFF0000u : sw[j >> 1] << 16;
+            const uint32_t s1 = (j & 1) ? sw[2 + (j >> 1)] & 0xFFFF0000u : sw[2 + (j >> 1)] << 16;
+            const uint32_t z0 = (j & 1) ? zw[j >> 1] & 0xFFFF0000u : zw[j >> 1] << 16;
+            const uint32_t z1 = (j & 1) ? zw[2 + (j >> 1)] & 0xFFFF0000u : zw[2 + (j >> 1)] << 16;
+            const float hs = (j & 1) ? 0.0625f : 1.f;
+            rs[kc][j] = half2_t{(_Float16)(__builtin_bit_cast(float, s0) * hs),
+                                (_Float16)(__builtin_bit_cast(float, s1) * hs)};
+            rz[kc][j] = half2_t{(_Float16)__builtin_bit_cast(float, z0),
+                                (_Float16)__builtin_bit_cast(float, z1)};
+          }
+        }
+        bias = 0.f;
+        return;
+      }
       float bp = 0.f;  // this lane's part of query col's bias
       const float qlive = live ? 1.f : 0.f;
 #pragma unroll
@@ -751,15 +819,58 @@ __global__ void __launch_bounds__(kThreads, 2)
         f.v[4 * h] = x.x; f.v[4 * h + 1] = x.y; f.v[4 * h + 2] = x.z; f.v[4 * h + 3] = x.w;
       }
     };
-    auto step = [&](const Ld& f) {
+    auto step = [&](const Ld& f, int st) {
       f32x4_t sacc[2];
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau) {
         sacc[tau] = f32x4_t{bias, bias, bias, bias};
+        if constexpr (kRope) {
+          // token 32 st + 16 tau + col of the group: dequantize its channels in packed fp16,
+          // turn pair (i, i + D/2) by its angle, feed the turned keys
+          half2_t dq[KC][4];
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc)
-          sacc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_to_f16(f.k[tau][kc]), qa[kc],
-                                                            sacc[tau], 0, 0, 0);
+          for (int kc = 0; kc < KC; ++kc) {
+            const uint32_t w = f.k[tau][kc], w8 = w >> 8;
+            const uint32_t m[4] = {(w & 0x000F000Fu) | 0x64006400u, (w & 0x00F000F0u) | 0x64006400u,
+                                   (w8 & 0x000F000Fu) | 0x64006400u,
+                                   (w8 & 0x00F000F0u) | 0x64006400u};
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              dq[kc][j] = __builtin_elementwise_fma(
+                  __builtin_bit_cast(half2_t, m[j]) - half2_t{(_Float16)1024.f, (_Float16)1024.f},
+                  rs[kc][j], rz[kc][j]);
+          }
+          const uint32_t* rot = &s_rot[(st * kStep + 16 * tau + col) * kRotRow + 8 * jj];
+          half8_t ka[KC];
+#pragma unroll
+          for (int kh = 0; kh < KC / 2; ++kh) {
+            // words copied out of the vectors first: hipcc 7.2 takes element 0 for every j
+            // when __builtin_bit_cast is given a vector element directly
+            const u32x4_t cv = *(const u32x4_t*)(rot + 32 * kh);
+            const u32x4_t sv = *(const u32x4_t*)(rot + 32 * kh + 4);
+            const uint32_t cw[4] = {cv.x, cv.y, cv.z, cv.w}, sw[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const half2_t c = __builtin_bit_cast(half2_t, cw[j]);
+              const half2_t sn = __builtin_bit_cast(half2_t, sw[j]);
+              const half2_t k1 = dq[kh][j], k2 = dq[kh + KC / 2][j];
+              const half2_t r1 = __builtin_elementwise_fma(k1, c, -(k2 * sn));
+              const half2_t r2 = __builtin_elementwise_fma(k1, sn, k2 * c);
+              ka[kh][2 * j] = r1.x;
+              ka[kh][2 * j + 1] = r1.y;
+              ka[kh + KC / 2][2 * j] = r2.x;
+              ka[kh + KC / 2][2 * j + 1] = r2.y;
+            }
+          }
+#pragma unroll
+          for (int kc = 0; kc < KC; ++kc)
+            sacc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[kc], qa[kc], sacc[tau], 0, 0, 0);
+        } else {
+#pragma unroll
+          for (int kc = 0; kc < KC; ++kc)
+            sacc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_to_f16(f.k[tau][kc]),
+                                                              qa[kc], sacc[tau], 0, 0, 0);
+        }
       }
       // online softmax of query col over the 32 tokens: the common case compares the lane's
       // largest raw product with the threshold; only when one passes it does the wave take
@@ -812,6 +923,11 @@ __global__ void __launch_bounds__(kThreads, 2)
       const uint32_t* qw = (const uint32_t*)((const char*)a.q + ((int64_t)b * a.Hq + h0) * RB);
       for (int w = tid; w < G * D / 2; w += kThreads)
         reinterpret_cast<uint32_t*>(&s_q[0][0])[w] = qw[w];
+      if constexpr (kRope) {  // the tau16 table, copied whole
+        const uint4* src = (const uint4*)a.rope_tau16;
+        for (int w = tid; w < kQ4Group * kRotRow / 4; w += kThreads)
+          reinterpret_cast<uint4*>(s_rot)[w] = src[w];
+      }
     }
     __syncthreads();
     Ld f0, f1, f2, f3;
@@ -827,23 +943,23 @@ __global__ void __launch_bounds__(kThreads, 2)
       load_params(gi + 1);  // clamped past the last group
       // the barriers keep each slot's last use ahead of its reload, so the reload lands in
       // the same registers (no loop-carried copy, which would wait for the load)
-      step(f0);
+      step(f0, 0);
       __builtin_amdgcn_sched_barrier(0);
       load_step(f0, gi + 1, 0);
-      step(f1);
+      step(f1, 1);
       __builtin_amdgcn_sched_barrier(0);
       load_step(f1, gi + 1, 1);
-      step(f2);
+      step(f2, 2);
       __builtin_amdgcn_sched_barrier(0);
       load_step(f2, gi + 1, 2);
-      step(f3);
+      step(f3, 3);
       __builtin_amdgcn_sched_barrier(0);
       load_step(f3, gi + 1, 3);
     }
     if (t_step >= 0) {  // the leftover step, already in its slot (the others read the idle buffer)
       fold();
       const Ld& ft = t_step == 0 ? f0 : t_step == 1 ? f1 : t_step == 2 ? f2 : f3;
-      step(ft);
+      step(ft, t_step);
     }
   }
   // MFMA partial of query col: sums over the 4 lanes of the column; every channel of O^T gets
@@ -877,19 +993,96 @@ __global__ void __launch_bounds__(kThreads, 2)
     for (int e = 0; e < Geo::kE; ++e) o[g][e] = 0.f;
   }
   const int t1 = ret ? 0 : (res ? n % kQ4Group : n);
+  // kRope: rows are turned at their positions in float32 and dotted with the query in
+  // float32. Position of bf16 row r of this block: residual row r is 128 (n / 128) + r; a
+  // streaming slot s holds s if s < S, else the latest position p <= nl with slot(p) = s,
+  // nl the last position in the cache (before a fused step's token).
+  [[maybe_unused]] const int str_nl = fused ? a.n[b] - 2 : a.n[b] - 1;
+  [[maybe_unused]] auto pos_of = [&](int64_t r64) -> int {
+    const int r = (int)r64;
+    if (res) return (n / kQ4Group) * kQ4Group + r;
+    return r < a.S ? r : r + a.R * ((str_nl - r) / a.R);
+  };
+  // (cos, sin) of the base angle 128 (p / 128) f_i of this lane's pairs i = 8 (sub mod D/16)
+  // + 2 k, + 1
+  [[maybe_unused]] auto load_base = [&](float4 (&bb)[4], int p) {
+    const float4* bp = (const float4*)(a.rope_base + (int64_t)(p / kQ4Group) * D +
+                                       16 * (sub & (D / 16 - 1)));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) bb[k] = bp[k];
+  };
+  // Logits of query g against the row's key turned at p (base angles bb, the rest tk = p mod
+  // 128 from the LDS table), summed over the row's LPT lanes. The partner channels of pair i
+  // sit in the same lane (two chunks per lane) or in lane sub ^ D/16 of the row's lane group
+  // (one chunk per lane).
+  [[maybe_unused]] auto rope_logits = [&](const F& f, const float4 (&bb)[4], int tk,
+                                          const QRegs<T, D, G, LPT>& q, float (&dz)[G]) {
+    const uint32_t* row = &s_rot[tk * kRotRow + 8 * (sub & (D / 16 - 1))];
+    // words copied out of the vectors first: hipcc 7.2 takes element 0 for every index when
+    // __builtin_bit_cast is given a vector element directly
+    const u32x4_t cv = *(const u32x4_t*)row, sv = *(const u32x4_t*)(row + 4);
+    const uint32_t cw[4] = {cv.x, cv.y, cv.z, cv.w}, sw[4] = {sv.x, sv.y, sv.z, sv.w};
+    float cs[8], sn[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float4 bv = bb[e >> 1];
+      const float cb = (e & 1) ? bv.z : bv.x, sb = (e & 1) ? bv.w : bv.y;
+      const float ct = (float)__builtin_bit_cast(half2_t, cw[e & 3])[e >> 2];
+      const float st = (float)__builtin_bit_cast(half2_t, sw[e & 3])[e >> 2];
+      cs[e] = __builtin_fmaf(cb, ct, -sb * st);
+      sn[e] = __builtin_fmaf(sb, ct, cb * st);
+    }
+    auto elem = [](uint32_t w, int h) {
+      return __builtin_bit_cast(float, h ? w & 0xFFFF0000u : w << 16);
+    };
+    float kr[kCpl][8];  // the turned key, this lane's chunks
+    if constexpr (kCpl == 2) {
+      const uint32_t x1[4] = {f.k[0].x, f.k[0].y, f.k[0].z, f.k[0].w};
+      const uint32_t x2[4] = {f.k[1].x, f.k[1].y, f.k[1].z, f.k[1].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float a1 = elem(x1[e >> 1], e & 1), a2 = elem(x2[e >> 1], e & 1);
+        kr[0][e] = __builtin_fmaf(a1, cs[e], -a2 * sn[e]);
+        kr[1][e] = __builtin_fmaf(a1, sn[e], a2 * cs[e]);
+      }
+    } else {
+      static_assert(kCpl == 1 && LPT == D / 8, "one chunk per lane: partner lane sub ^ D/16");
+      const bool first = sub < D / 16;
+      const uint32_t x[4] = {f.k[0].x, f.k[0].y, f.k[0].z, f.k[0].w};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t pw = (uint32_t)__shfl_xor((int)x[w], D / 16);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int e = 2 * w + h;
+          const float xv = elem(x[w], h), pv = elem(pw, h);
+          kr[0][e] = first ? __builtin_fmaf(xv, cs[e], -pv * sn[e])
+                           : __builtin_fmaf(pv, sn[e], xv * cs[e]);
+        }
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float acc = 0.f;
+#pragma unroll
+      for (int c = 0; c < kCpl; ++c) {
+        const uint32_t qw[4] = {q.q[g][c].x, q.q[g][c].y, q.q[g][c].z, q.q[g][c].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(kr[c][e], elem(qw[e >> 1], e & 1), acc);
+      }
+      dz[g] = group_sum<LPT>(acc);
+    }
+  };
   if (t1 > 0 || new_row >= 0) {
     QRegs<T, D, G, LPT> q;
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
       for (int c = 0; c < kCpl; ++c) q.q[g][c] = *(const uint4*)&s_q[g][(sub + LPT * c) * 8];
-    auto process = [&](const F& f, bool valid) {
-      float dz[G];
+    // online softmax and P V of one row given its logits
+    auto update = [&](const F& f, float (&dz)[G], bool valid) {
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        dz[g] = group_sum<LPT>(dot_partial<T, D, G, LPT>(f, q, g));
-        dz[g] = valid ? dz[g] : kNegInf;
-      }
+      for (int g = 0; g < G; ++g) dz[g] = valid ? dz[g] : kNegInf;
       bool need = false;
 #pragma unroll
       for (int g = 0; g < G; ++g) need |= dz[g] > thr[g];
@@ -915,6 +1108,12 @@ __global__ void __launch_bounds__(kThreads, 2)
       }
       accumulate_pv<T, D, G, LPT>(f, p, o);
     };
+    auto process = [&](const F& f, bool valid) {
+      float dz[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) dz[g] = group_sum<LPT>(dot_partial<T, D, G, LPT>(f, q, g));
+      update(f, dz, valid);
+    };
     const int n_it = (t1 + kTpb - 1) / kTpb;
     auto row_of = [&](int it) -> int64_t {
       const int t = it * kTpb + wave * kTpw + grp;
@@ -929,13 +1128,23 @@ __global__ void __launch_bounds__(kThreads, 2)
       // registers are free by then, and its blocks (a streaming head's S + R slots over 4
       // waves) wait on memory once per kBfStages iterations
       F g[kBfStages];
+      [[maybe_unused]] float4 gb[kRope ? kBfStages : 1][4];  // kRope: each row's base angles
 #pragma unroll
-      for (int st = 0; st < kBfStages; ++st)
+      for (int st = 0; st < kBfStages; ++st) {
         load_frag<T, D, LPT>(g[st], kbase, vbase, row_of(st), sub);
+        if constexpr (kRope) load_base(gb[st], pos_of(row_of(st)));
+      }
       for (int it = 0; it < n_it; it += kBfStages) {
 #pragma unroll
         for (int st = 0; st < kBfStages; ++st) {
-          process(g[st], valid_at(it + st));
+          if constexpr (kRope) {
+            float dz[G];
+            rope_logits(g[st], gb[st], pos_of(row_of(it + st)) % kQ4Group, q, dz);
+            update(g[st], dz, valid_at(it + st));
+            load_base(gb[st], pos_of(row_of(it + st + kBfStages)));
+          } else {
+            process(g[st], valid_at(it + st));
+          }
           load_frag<T, D, LPT>(g[st], kbase, vbase, row_of(it + st + kBfStages), sub);
         }
       }
@@ -946,7 +1155,16 @@ __global__ void __launch_bounds__(kThreads, 2)
       const char* nv = (const char*)a.new_v + ((int64_t)b * a.Hkv + j) * RB;
       F f;
       load_frag<T, D, LPT>(f, nk, nv, 0, sub);
-      process(f, wave == 0 && grp == 0);
+      if constexpr (kRope) {
+        const int pnew = a.n[b] - 1;
+        float4 bb[4];
+        load_base(bb, pnew);
+        float dz[G];
+        rope_logits(f, bb, pnew % kQ4Group, q, dz);
+        update(f, dz, wave == 0 && grp == 0);
+      } else {
+        process(f, wave == 0 && grp == 0);
+      }
       if (wave == 0) {
         constexpr int kRowChunks = RB / 16;
         for (int c = lane; c < 2 * kRowChunks; c += 64) {
@@ -1116,25 +1334,32 @@ struct Variant {
   static constexpr int LPT = lanes_per_token<T, D, G>();
   static constexpr int NS = stages<T, D, G>();
 
-  // Decode blocks that fit on the device at once (of the 4-bit kernel when q4), counting at
-  // most two per CU, queried once per process. The host sizes one round of splits from it
-  // (two blocks per CU for a batch, one for a single sequence).
-  static int resident_blocks(bool q4) {
-    static int cached[2] = {0, 0};
-    if (cached[q4]) return cached[q4];
-    const void* fn = reinterpret_cast<const void*>(&decode_kernel<T, D, G, LPT, NS>);
-    if constexpr (sizeof(T) == 2)
-      if (q4) fn = reinterpret_cast<const void*>(&decode_q4_kernel<D, G, LPT, 4>);
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0) != hipSuccess ||
-        cus <= 0 || per_cu <= 0) {
-      (void)hipGetLastError();
-      return 512;
+  // Decode blocks that fit on the device at once (of the 4-bit kernel when q4, its pre-RoPE
+  // form when rope), counting at most max_per_cu per CU; the occupancy is queried once per
+  // process. The host sizes one round of splits from it (two blocks per CU for a batch, one
+  // for a single sequence).
+  static int resident_blocks(bool q4, bool rope, int max_per_cu) {
+    static int cus_cached = 0, per_cu_cached[3] = {0, 0, 0};
+    const int kind = q4 ? (rope ? 2 : 1) : 0;
+    if (!per_cu_cached[kind]) {
+      const void* fn = reinterpret_cast<const void*>(&decode_kernel<T, D, G, LPT, NS>);
+      if constexpr (sizeof(T) == 2) {
+        if (kind == 1) fn = reinterpret_cast<const void*>(&decode_q4_kernel<D, G, LPT, 4, false>);
+        if (kind == 2) fn = reinterpret_cast<const void*>(&decode_q4_kernel<D, G, LPT, 4, true>);
+      }
+      int dev = 0, cus = 0, per_cu = 0;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+          hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0) != hipSuccess ||
+          cus <= 0 || per_cu <= 0) {
+        (void)hipGetLastError();
+        return 512;
+      }
+      cus_cached = cus;
+      per_cu_cached[kind] = per_cu;
     }
-    cached[q4] = cus * (per_cu < 2 ? per_cu : 2);
-    return cached[q4];
+    const int per_cu = per_cu_cached[kind];
+    return cus_cached * (per_cu < max_per_cu ? per_cu : max_per_cu);
   }
 
   static int launch(const DecodeArgs& a, void* stream, const KernelMarks& marks) {
@@ -1142,8 +1367,12 @@ struct Variant {
                            (int64_t)a.B * a.Hs * a.nss;
     if (marks.begin) (void)hipEventRecord((hipEvent_t)marks.begin, (hipStream_t)stream);
     if constexpr (sizeof(T) == 2) {
-      if (a.q4)
-        hipLaunchKernelGGL((decode_q4_kernel<D, G, LPT, 4>), dim3((unsigned)blocks),
+      if (a.q4 && a.rope_base)
+        hipLaunchKernelGGL((decode_q4_kernel<D, G, LPT, 4, true>), dim3((unsigned)blocks),
+                           dim3(kThreads), 0, (hipStream_t)stream, a.nsplit, a.Hr, a.Hs, a.B, a.nss,
+                           a.new_k != nullptr ? 1 : 0, a);
+      else if (a.q4)
+        hipLaunchKernelGGL((decode_q4_kernel<D, G, LPT, 4, false>), dim3((unsigned)blocks),
                            dim3(kThreads), 0, (hipStream_t)stream, a.nsplit, a.Hr, a.Hs, a.B, a.nss,
                            a.new_k != nullptr ? 1 : 0, a);
       else
@@ -1178,7 +1407,9 @@ struct Variant {
 
 template <typename T, int D, int G>
 int run(bool query, const DecodeArgs* a, void* stream, const KernelMarks* marks) {
-  return query ? Variant<T, D, G>::resident_blocks(a != nullptr && a->q4 != 0)
+  // a query reads a->q4, whether a->rope_base is set and the per-CU cap in a->nsplit
+  return query ? Variant<T, D, G>::resident_blocks(a->q4 != 0, a->rope_base != nullptr,
+                                                   a->nsplit)
                : Variant<T, D, G>::launch(*a, stream, *marks);
 }
 
@@ -1236,10 +1467,14 @@ int static_scratch(void** ptr) {
   return 0;
 }
 
-int decode_resident_blocks(int dtype, int head_dim, int group, bool q4) {
-  DecodeArgs probe;  // only q4 is read
+int decode_resident_blocks(int dtype, int head_dim, int group, bool q4, bool rope,
+                           int max_per_cu) {
+  static const float marker = 0.f;
+  DecodeArgs probe;  // only q4, rope_base (null or not) and nsplit (the per-CU cap) are read
   std::memset(&probe, 0, sizeof(probe));
   probe.q4 = q4 ? 1 : 0;
+  probe.rope_base = rope ? &marker : nullptr;
+  probe.nsplit = max_per_cu;
   return dispatch(dtype, head_dim, group, true, &probe, nullptr, nullptr);
 }
 

@@ -27,6 +27,24 @@ int32_t& len_of(duo_cache* c, int32_t layer, int32_t b) {
   return c->lens[(size_t)layer * c->cfg.batch + b];
 }
 
+// The pre-RoPE cos/sin tables (RopeGeom) of a cache, or nulls when its keys are appended as
+// attended.
+struct RopePtrs {
+  const float* base = nullptr;
+  const uint32_t* tau16 = nullptr;
+};
+
+RopePtrs rope_ptrs(const duo_cache* c) {
+  RopePtrs r;
+  if (c->cfg.rope_theta > 0.f) {
+    const RopeGeom g = rope_geom(c->cfg.capacity, c->cfg.head_dim);
+    const char* t = c->arena + c->lay.rope_off;
+    r.base = (const float*)(t + g.base);
+    r.tau16 = (const uint32_t*)(t + g.tau16);
+  }
+  return r;
+}
+
 struct LayerPtrs {
   char* full_k;
   char* full_v;
@@ -149,8 +167,9 @@ duo_status decode_impl(duo_cache* c, int32_t layer, const void* q, const void* k
   // 56-63 splits (one per CU) against 51.2-52.3 us with 126-127, its 4-bit cache 22.6 against
   // 23.3 us; the 32 layers of 8 ragged sequences 2,355 us at two blocks per CU against
   // 2,477 us at one.
-  int32_t resident = decode_resident_blocks(c->cfg.dtype, c->cfg.head_dim, group, q4);
-  if (a.B == 1) resident = std::max(1, resident / 2);
+  const RopePtrs rp = rope_ptrs(c);
+  const int32_t resident = decode_resident_blocks(c->cfg.dtype, c->cfg.head_dim, group, q4,
+                                                  rp.base != nullptr, a.B == 1 ? 1 : 2);
   a.nsplit = c->force_splits
                  ? std::min(c->force_splits, split_cap)
                  : choose_decode_splits(n_max, a.B, a.Hr, a.Hs * a.nss + (q4 ? a.Hr : 0),
@@ -185,6 +204,8 @@ duo_status decode_impl(duo_cache* c, int32_t layer, const void* q, const void* k
     a.q4_stride = (int64_t)g.stride;
     a.q4_params = (int64_t)g.codes;
     a.q4_resid = (int64_t)(g.codes + g.params);
+    a.rope_base = rp.base;
+    a.rope_tau16 = rp.tau16;
   }
   if (launch_decode(a, c->cfg.dtype, c->cfg.head_dim, group, stream,
                     next_marks(c, DUO_TIMING_DECODE)) != 0)
@@ -208,6 +229,11 @@ duo_status duo_cache_reset(duo_cache* c, void* stream) {
   a.seq_len = (int32_t*)(c->arena + c->lay.seq_len_off);
   a.n_len = (int64_t)(L * B);
   if (launch_reset(a, stream) != 0) return DUO_ERR_HIP;
+  if (c->cfg.rope_theta > 0.f &&
+      launch_rope_tables(c->arena + c->lay.rope_off, c->cfg.head_dim,
+                         rope_geom(c->cfg.capacity, c->cfg.head_dim).nbase,
+                         (double)c->cfg.rope_theta, stream) != 0)
+    return DUO_ERR_HIP;
   std::fill(c->lens.begin(), c->lens.end(), 0);
   return DUO_OK;
 }

@@ -38,6 +38,7 @@ duo_status check_config(const duo_config* cfg) {
   if (element_size(cfg->dtype) == 0 || element_size(cfg->out_dtype) == 0)
     return DUO_ERR_INVALID;
   if (!(std::isfinite(cfg->softmax_scale))) return DUO_ERR_INVALID;
+  if (!(std::isfinite(cfg->rope_theta))) return DUO_ERR_INVALID;
   // Built variants: head_dim 64/128, group 1/2/4/8, out either fp32 or the input dtype.
   if (cfg->head_dim != 64 && cfg->head_dim != 128) return DUO_ERR_UNSUPPORTED;
   const int g = cfg->num_q_heads / cfg->num_kv_heads;
@@ -46,6 +47,8 @@ duo_status check_config(const duo_config* cfg) {
   if (cfg->kv_bits == 4 && cfg->dtype != DUO_BF16) return DUO_ERR_UNSUPPORTED;
   // a 4-bit retrieval head decodes into its splits' partials plus one for the residual rows
   if (cfg->kv_bits == 4 && cfg->max_splits == 1) return DUO_ERR_INVALID;
+  // pre-RoPE keys: the rotation is built into the 4-bit caches' append and decode only
+  if (cfg->rope_theta > 0.f && cfg->kv_bits != 4) return DUO_ERR_UNSUPPORTED;
   return DUO_OK;
 }
 
@@ -105,6 +108,11 @@ duo_status build_layout(const duo_config* cfg, duo_layout* lay, std::vector<Laye
   const uint64_t ws = ws_decode > ws_prefill ? ws_decode : ws_prefill;
   out.workspace_bytes = ws;
   off = align_up(off + ws);
+  if (cfg->rope_theta > 0.f) {
+    out.rope_off = off;
+    out.rope_bytes = rope_geom(cap, D).bytes;
+    off = align_up(off + out.rope_bytes);
+  }
   out.arena_bytes = off;
   if (lay) *lay = out;
   return DUO_OK;

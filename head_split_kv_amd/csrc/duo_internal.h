@@ -40,6 +40,28 @@ inline Q4Geom q4_geom(uint64_t cap, uint64_t D) {
   return g;
 }
 
+// cos/sin tables of a cache with pre-RoPE keys (cfg.rope_theta > 0), at layout.rope_off;
+// f_i = theta^(-2 i / D) is the frequency of channel pair (i, i + D / 2):
+//   tau16: [128] rows of D / 2 + 4 words, the decode kernel's LDS image: for each block of 8
+//          pairs b, 4 words of fp16 (cos, cos) then 4 of (sin, sin) of pairs (8 b + w, 8 b + w + 4)
+//          at angle tau f_i (w = 0..3), then 4 padding words that keep the LDS reads of
+//          neighbouring rows on different banks;
+//   base:  float [nbase][D / 2][2], (cos, sin) of 128 g f_i, nbase = cap / 128 + 1.
+// A position t turns by base[t / 128] composed with tau[t % 128].
+struct RopeGeom {
+  uint64_t tau16, base, bytes;  // offsets from layout.rope_off, total bytes
+  int32_t nbase;
+};
+inline RopeGeom rope_geom(uint64_t cap, uint64_t D) {
+  auto up = [](uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; };
+  RopeGeom g;
+  g.nbase = (int32_t)(cap / kQ4Group + 1);
+  g.tau16 = 0;
+  g.base = up((uint64_t)kQ4Group * (D / 2 + 4) * 4);
+  g.bytes = g.base + up((uint64_t)g.nbase * D * 4);
+  return g;
+}
+
 // Per-layer head partition. For KV head j: cls_idx[j] >= 0 is its index among the layer's
 // retrieval heads; cls_idx[j] < 0 encodes streaming index -(cls_idx[j] + 1).
 struct LayerInfo {
@@ -108,6 +130,8 @@ struct DecodeArgs {
   int32_t q4;              // full caches in 4 bits (Q4Geom offsets below)
   int64_t q4_stride, q4_params, q4_resid;
   int32_t nss;             // blocks per streaming head (4-bit kernel; 1 otherwise)
+  const float* rope_base;      // pre-RoPE keys (4-bit kernel): RopeGeom base and tau16
+  const uint32_t* rope_tau16;  // tables, else null
   // KV head of each retrieval / streaming index, as 32-bit words: a block reads its entry with
   // a scalar load (a byte would take a vector load, whose latency delays every first load)
   int32_t ret_kv[kMaxKvHeads];
@@ -154,6 +178,8 @@ struct KernelMarks {
 
 // Launchers (one translation unit per kernel family). They return a hipError_t value as int.
 int launch_reset(const ResetArgs& a, void* stream);
+// Fills the RopeGeom tables at `tables` for head dimension D and base theta.
+int launch_rope_tables(char* tables, int32_t D, int32_t nbase, double theta, void* stream);
 int launch_append(const AppendArgs& a, int dtype, void* stream);
 int launch_append_kv4(const AppendArgs& a, int head_dim, void* stream);
 int launch_set_lengths(const SetLenArgs& a, void* stream);
@@ -190,9 +216,11 @@ int pairs_elapsed_ms(const std::vector<void*>& ev, int pairs, double* total_ms);
 constexpr uint64_t kScratchBytes = 8ull << 20;
 constexpr int kMaxDevices = 64;
 int static_scratch(void** ptr);
-// Decode blocks of this variant (the 4-bit kernel when q4) that are resident on the device
-// at once, counting at most two per CU (512 if unknown): the size of one round of splits.
-int decode_resident_blocks(int dtype, int head_dim, int group, bool q4);
+// Decode blocks of this variant (the 4-bit kernel when q4, its pre-RoPE form when rope) that
+// are resident on the device at once, counting at most max_per_cu (1 or 2) per CU (512 if
+// unknown): the size of one round of splits.
+int decode_resident_blocks(int dtype, int head_dim, int group, bool q4, bool rope,
+                           int max_per_cu);
 // Prefill blocks of this variant that are resident on the device at once (512 if unknown).
 int prefill_resident_blocks(int head_dim, int group);
 

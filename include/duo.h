@@ -85,6 +85,8 @@ typedef struct {
   int32_t streaming_prefill; /* duo_prefill_mode of streaming heads in duo_attn_prefill */
   int32_t kv_bits;         /* 0 or 16: full caches in dtype. 4: full (retrieval) caches in
                               4 bits, see below (bf16 only); streaming caches keep dtype */
+  float rope_theta;        /* > 0 (kv_bits = 4 only): keys are appended before RoPE with
+                              this base, see below; <= 0: keys are appended as attended */
 } duo_config;
 
 /* 4-bit full caches (cfg.kv_bits = 4; explainer, "Combination with Quantization": the full
@@ -108,6 +110,17 @@ typedef struct {
  * return DUO_ERR_UNSUPPORTED on a 4-bit cache. */
 #define DUO_KV4_GROUP 128
 
+/* Pre-RoPE keys (cfg.rope_theta > 0 with kv_bits = 4; OpenReview thread, the authors'
+ * reply on combining DuoAttention with KV quantization: their 4-bit keys are
+ * quantized before the rotary position embedding). The caller passes every key of the layer before RoPE, to
+ * duo_kv_append and duo_decode_step alike, and every query after its own rotation; attention
+ * scores each key at its own position t. RoPE here is the rotate-half form: channel i < d/2
+ * pairs with channel i + d/2 and the pair turns by the angle t * theta^(-2i/d). Every cache
+ * keeps the keys as given: a retrieval head's codes, scales and zeros are taken of them, and
+ * decoding rotates each dequantized key, each residual row and each streaming slot at the
+ * position it holds. Values are never rotated. The cos/sin tables live in the arena (layout.rope_off) and are
+ * written by duo_cache_reset. */
+
 /* Byte offsets inside the caller's arena (all 256-byte aligned). Inside each cache region
  * the layers follow one another in order, each starting on a 256-byte boundary. */
 typedef struct {
@@ -120,6 +133,9 @@ typedef struct {
   uint64_t seq_len_off;    /* int32 [L][B]: tokens appended so far */
   uint64_t workspace_off;  /* split-K partials of decode and prefill (shared) */
   uint64_t workspace_bytes;
+  uint64_t rope_off;       /* cfg.rope_theta > 0: the cos/sin tables (library-private
+                              contents), rope_bytes long; 0 bytes otherwise */
+  uint64_t rope_bytes;
 } duo_layout;
 
 typedef struct duo_cache duo_cache; /* opaque host object; owns no device memory */
@@ -148,8 +164,9 @@ duo_status duo_cache_init(const duo_config* cfg, void* arena, uint64_t arena_byt
  * K/V rows are not touched. Enqueues one small kernel per layer on `stream`. */
 duo_status duo_cache_set_lengths(duo_cache* cache, const int32_t* lens, void* stream);
 
-/* Empty every sequence of every layer: lengths 0, slot table -1.
- * Enqueues one fill kernel on `stream` (no memset node, so it can be graph-captured). */
+/* Empty every sequence of every layer: lengths 0, slot table -1; with cfg.rope_theta > 0
+ * also (re)write the cos/sin tables at layout.rope_off. Enqueues one fill kernel on `stream`
+ * (two with the tables; no memset node, so it can be graph-captured). */
 duo_status duo_cache_reset(duo_cache* cache, void* stream);
 
 /* Free the host object (not the arena). NULL is accepted. */

@@ -20,12 +20,12 @@ pytestmark = pytest.mark.gpu
 QG = O.KV4_GROUP
 
 
-def kv4_cache(w, capacity, out_dtype=torch.float32, mask=None):
+def kv4_cache(w, capacity, out_dtype=torch.float32, mask=None, rope_theta=0.0):
     mask = W.retrieval_mask(w) if mask is None else mask
     return hsk.DuoCache(num_layers=mask.shape[0], batch=w.batch, num_q_heads=w.hq,
                         num_kv_heads=w.hkv, head_dim=w.d, sink=w.sink, recent=w.recent,
                         capacity=capacity, retrieval_mask=mask, dtype=torch.bfloat16,
-                        out_dtype=out_dtype, kv_bits=4)
+                        out_dtype=out_dtype, kv_bits=4, rope_theta=rope_theta)
 
 
 def geom(cap, D):
@@ -151,8 +151,8 @@ def test_kv4_append_batch_calls(d):
 
 
 def run_decode_kv4(w, lens0, steps, check_steps=None, splits=None, out_dtype=torch.float32,
-                   fused=False, heads=None):
-    cache = kv4_cache(w, max(lens0) + steps, out_dtype=out_dtype)
+                   fused=False, heads=None, rope_theta=None):
+    cache = kv4_cache(w, max(lens0) + steps, out_dtype=out_dtype, rope_theta=rope_theta or 0.0)
     for b, n in enumerate(lens0):
         for t0 in range(0, n, 1 << 16):
             append_tokens(cache, w, b, t0, min(n, t0 + (1 << 16)))
@@ -176,7 +176,8 @@ def run_decode_kv4(w, lens0, steps, check_steps=None, splits=None, out_dtype=tor
         for b, n in enumerate(lens):
             kh, vh = W.tokens(w, "k", 0, b, 0, n), W.tokens(w, "v", 0, b, 0, n)
             if heads is None:
-                ref, ref_lse = O.decode_step_kv4(qh[b], kh, vh, mask, w.sink, w.recent)
+                ref, ref_lse = O.decode_step_kv4(qh[b], kh, vh, mask, w.sink, w.recent,
+                                                 rope_theta=rope_theta)
                 assert_close(got[b], ref, f"step {s} seq {b} n {n} out")
                 assert_close(got_lse[b], ref_lse, f"step {s} seq {b} n {n} lse")
             else:
@@ -184,7 +185,8 @@ def run_decode_kv4(w, lens0, steps, check_steps=None, splits=None, out_dtype=tor
                 for j in heads:
                     hq = slice(j * G, (j + 1) * G)
                     ref, ref_lse = O.decode_step_kv4(qh[b][hq], kh[:, j:j + 1], vh[:, j:j + 1],
-                                                     mask[j:j + 1], w.sink, w.recent)
+                                                     mask[j:j + 1], w.sink, w.recent,
+                                                     rope_theta=rope_theta)
                     assert_close(got[b][hq], ref, f"step {s} seq {b} kv {j}")
                     assert_close(got_lse[b][hq], ref_lse, f"step {s} seq {b} kv {j} lse")
     return cache
@@ -268,3 +270,138 @@ def test_kv4_decode_gqa_128k():
     steps cross the group boundary at 131,072 tokens."""
     w = W.workload("c3")
     run_decode_kv4(w, [w.context - 2], 4)
+
+
+# ---- pre-RoPE keys (cfg.rope_theta > 0) ---------------------------------------------------
+# Keys are appended before RoPE, queries are taken as already turned; the oracle turns each
+# key at its position after dequantization (decode_step_kv4 with rope_theta).
+
+THETA = 10000.0
+
+
+def streaming_keys(cache, b, s):
+    """bf16 slots [S + R][D] of streaming head index s of sequence b (layer 0) as float32."""
+    lay, D, SR = cache.layout, cache.d, cache.sink + cache.recent
+    hs = int((1 - cache.retrieval_mask[0]).sum())
+    off = lay.str_k_off + ((b * hs + s) * SR) * D * 2
+    raw = cache.arena[off:off + SR * D * 2].cpu().numpy().view(np.uint16).astype(np.uint32)
+    return (raw << 16).view(np.float32).reshape(SR, D)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_kv4_rope_tables(d):
+    """The cos/sin tables duo_cache_reset writes at layout.rope_off, against the oracle's
+    angles: tau16 (fp16 pairs (8 b + w, 8 b + w + 4) of cos then sin of tau f_i, rows of
+    d/2 + 4 words) and the base rows (float32 (cos, sin) of 128 g f_i)."""
+    theta, cap = 500000.0, 3000
+    w = W.Workload("kv4-rope-tables", 1, 1, 4, 2, d, "bf16", 4, 32, 0, 0, 1,
+                   fixed_mask=((0,),), seed=243)
+    cache = kv4_cache(w, cap, rope_theta=theta)
+    torch.cuda.synchronize()
+    lay = cache.layout
+    raw = cache.arena[lay.rope_off:lay.rope_off + lay.rope_bytes].cpu().numpy()
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    half, nbase = d // 2, cap // QG + 1
+    ob = al(QG * (half + 4) * 4)
+    base = raw[ob:ob + nbase * d * 4].view(np.float32).reshape(nbase, half, 2)
+    ang_t = O.rope_angles(np.arange(QG), d, theta)
+    ang_b = O.rope_angles(QG * np.arange(nbase), d, theta)
+    assert np.abs(base[..., 0] - np.cos(ang_b)).max() < 1e-6
+    assert np.abs(base[..., 1] - np.sin(ang_b)).max() < 1e-6
+    t16 = raw[:QG * (half + 4) * 4].view(np.float16).reshape(QG, 2 * (half + 4))
+    i = np.arange(half)
+    at = (i // 8) * 16 + 2 * (i % 4) + (i % 8) // 4
+    assert np.abs(t16[:, at].astype(np.float64) - np.cos(ang_t)).max() <= 2.0 ** -11
+    assert np.abs(t16[:, at + 8].astype(np.float64) - np.sin(ang_t)).max() <= 2.0 ** -11
+    assert np.all(t16[:, 2 * half:] == 0)
+    cache.close()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("path", ["residual", "groups", "streaming"])
+def test_kv4_rope_each_path(d, path):
+    """Each path alone with pre-RoPE keys: only bf16 residual rows (99 + 1 tokens), only
+    complete groups (255 + 1 tokens), only streaming heads."""
+    mask = ((),) if path == "streaming" else ((0, 1),)
+    w = W.Workload("kv4-rope-path", 1, 1, 4, 2, d, "bf16", 4, 32, 0, 0, 0 if mask == ((),) else 2,
+                   fixed_mask=mask, seed=241)
+    n0 = {"residual": 99, "groups": 255, "streaming": 200}[path]
+    run_decode_kv4(w, [n0], 1, rope_theta=THETA)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_kv4_rope_decode_variants(d, G):
+    """Every (head_dim, group) variant with pre-RoPE keys: the MFMA path (dequantize, turn
+    by the offset in the group, the query turned by the group base), the residual rows and
+    the streaming heads, steps across a group boundary."""
+    w = W.Workload("kv4-rope-variant", 1, 2, 2 * G, 2, d, "bf16", 4, 32, 0, 0, 1,
+                   fixed_mask=((0,),), seed=205 + G)
+    run_decode_kv4(w, [3 * QG - 2, 2 * QG + 40], 4, rope_theta=THETA)
+
+
+def test_kv4_rope_append_keeps_keys_as_given():
+    """With pre-RoPE keys every cache keeps the keys as given: the retrieval caches hold the
+    oracle's codes of them, and every streaming slot the input bits of its position."""
+    w = W.Workload("kv4-rope-append", 1, 2, 8, 4, 128, "bf16", 4, 64, 0, 0, 2,
+                   fixed_mask=((0, 2),), seed=211)
+    cache = kv4_cache(w, 3000, rope_theta=500000.0)
+    lens = [2500, 300]
+    for b, n in enumerate(lens):
+        append_tokens(cache, w, b, 0, n - 7)
+        for t in range(n - 7, n):  # single-token appends through the ring
+            append_tokens(cache, w, b, t, t + 1)
+    torch.cuda.synchronize()
+    check_stored(cache, w, lens)
+    str_heads = np.nonzero(1 - cache.retrieval_mask[0])[0]
+    for b, n in enumerate(lens):
+        table = O.slot_table(n, w.sink, w.recent)
+        for s, j in enumerate(str_heads):
+            got = streaming_keys(cache, b, s)
+            kh = W.tokens(w, "k", 0, b, 0, n)[:, j].astype(np.float32)
+            ok = table >= 0
+            assert np.array_equal(got[ok], kh[table[ok]]), (b, j)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_kv4_rope_streaming_ring_and_fused(fused):
+    """Streaming windows cut over several blocks before and after the ring wraps, each slot
+    turned at the position it holds; the fused step's token is turned at its own position
+    and stored as given (later steps read it back)."""
+    w = W.Workload("kv4-rope-ring", 1, 1, 16, 4, 128, "bf16", 4, 500, 0, 0, 2,
+                   fixed_mask=((1, 2),), seed=219)
+    run_decode_kv4(w, [1000], 6, fused=fused, rope_theta=THETA)
+    run_decode_kv4(w, [300], 3, fused=fused, rope_theta=THETA)
+
+
+def test_kv4_rope_ragged_batch_splits_bf16_out():
+    w = W.Workload("kv4-rope-ragged", 1, 3, 32, 8, 128, "bf16", 16, 64, 0, 0, 4, seed=223)
+    run_decode_kv4(w, [700, 129, 1500], 2, out_dtype=torch.bfloat16, rope_theta=500000.0)
+    w2 = W.Workload("kv4-rope-splits", 1, 1, 32, 8, 128, "bf16", 16, 64, 0, 0, 4, seed=227)
+    for splits in (1, 3, 16):
+        run_decode_kv4(w2, [9 * QG + 50], 1, splits=splits, rope_theta=THETA)
+
+
+def test_kv4_rope_step_from_empty():
+    """duo_decode_step with pre-RoPE keys from an empty cache through two group
+    completions (append + decode), every few steps checked."""
+    w = W.Workload("kv4-rope-step", 1, 1, 8, 2, 64, "bf16", 4, 16, 0, 0, 1,
+                   fixed_mask=((1,),), seed=229)
+    run_decode_kv4(w, [0], 2 * QG + 5, fused=True, rope_theta=THETA,
+                   check_steps=set(range(0, 2 * QG + 5, 9)) | {QG - 1, QG, 2 * QG - 1, 2 * QG})
+
+
+def test_kv4_rope_far_positions():
+    """Positions near 20,000 with base 10,000: the group base angles are far from zero (the
+    lowest pair turns by about 3,000 full turns)."""
+    w = W.Workload("kv4-rope-far", 1, 1, 8, 2, 128, "bf16", 16, 64, 0, 0, 1,
+                   fixed_mask=((0,),), seed=231)
+    run_decode_kv4(w, [20000 - 3], 4, rope_theta=THETA)
+
+
+@pytest.mark.timeout(900)
+def test_kv4_rope_gqa_128k():
+    """The Llama-3-8B-shaped GQA layer at a 128K context in 4 bits with pre-RoPE keys (base
+    500,000, as that model's): steps across the group boundary at 131,072 tokens."""
+    w = W.workload("c3")
+    run_decode_kv4(w, [w.context - 2], 4, rope_theta=500000.0)

@@ -102,6 +102,34 @@ def test_kv_bits_checked_and_kv4_layout():
     assert l4.arena_bytes < l16.arena_bytes
 
 
+def test_rope_theta_checked_and_rope_layout():
+    """Pre-RoPE keys are built for 4-bit caches only; their cos/sin tables follow the
+    workspace: tau16 [128][d/2 + 4] words and the base rows [cap / 128 + 1] of (cos, sin)
+    float pairs per channel pair, each 256-byte aligned."""
+    lay = N.DuoLayout()
+    for bits, theta, status in ((4, 10000.0, N.DUO_OK), (4, 0.0, N.DUO_OK), (4, -1.0, N.DUO_OK),
+                                (0, 10000.0, N.DUO_ERR_UNSUPPORTED),
+                                (16, 500000.0, N.DUO_ERR_UNSUPPORTED),
+                                (4, float("nan"), N.DUO_ERR_INVALID),
+                                (4, float("inf"), N.DUO_ERR_INVALID)):
+        cfg, _keep = cfg_of(kv_bits=bits)
+        cfg.rope_theta = theta
+        assert N.lib().duo_layout_query(ctypes.byref(cfg), ctypes.byref(lay)) == status, (bits, theta)
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    for D, cap in ((128, 1000), (64, 1024), (128, 131072 + 5)):
+        cfg, _keep = cfg_of(kv_bits=4, head_dim=D, capacity=cap, rope_theta=500000.0)
+        plain, _k2 = cfg_of(kv_bits=4, head_dim=D, capacity=cap)
+        lr, lp = N.DuoLayout(), N.DuoLayout()
+        assert N.lib().duo_layout_query(ctypes.byref(cfg), ctypes.byref(lr)) == N.DUO_OK
+        assert N.lib().duo_layout_query(ctypes.byref(plain), ctypes.byref(lp)) == N.DUO_OK
+        assert lp.rope_bytes == 0 and lp.rope_off == 0
+        want = al(128 * (D // 2 + 4) * 4) + al((cap // 128 + 1) * D * 4)
+        assert lr.rope_bytes == want, D
+        assert lr.rope_off == al(lr.workspace_off + lr.workspace_bytes)
+        assert lr.arena_bytes == al(lr.rope_off + lr.rope_bytes)
+        assert lr.arena_bytes == lp.arena_bytes + al(want)
+
+
 def test_kv4_bytes_model():
     """Per retrieval head: d bytes of K and V codes per grouped token, 4 d bytes of key
     parameters per group, 4 bytes of value parameters per grouped token, residual tokens at
