@@ -20,14 +20,14 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _pair(w, lens, kv_bits=0, splits=0):
+def _pair(w, lens, kv_bits=0, splits=0, rope_theta=0.0):
     """A filled cache after one appended step, and the step's query."""
     import head_split_kv_amd as hsk
     mask = W.retrieval_mask(w)
     cache = hsk.DuoCache(num_layers=1, batch=w.batch, num_q_heads=w.hq, num_kv_heads=w.hkv,
                          head_dim=w.d, sink=w.sink, recent=w.recent, capacity=max(lens) + 1,
                          retrieval_mask=mask, dtype=torch.bfloat16, out_dtype=torch.float32,
-                         kv_bits=kv_bits, max_splits=0)
+                         kv_bits=kv_bits, max_splits=0, rope_theta=rope_theta)
     fill(cache, w, 0, lens)
     q, k, v, _ = step_inputs(w, 0, lens)
     cache.kv_append(0, k, v)
@@ -74,14 +74,20 @@ def test_noalloc_matches_decode_on_calls_in_a_row():
 
 
 def test_noalloc_4bit_cache_and_capacity():
-    """A 4-bit cache (partials of the splits and of the residual rows), then a smaller bf16
-    call; and a 4-bit cache too wide for the scratch (512 sequences x 16 query heads x 2
+    """A 4-bit cache (partials of the splits and of the residual rows), the same with
+    pre-RoPE keys, then a smaller bf16 call; and a 4-bit cache too wide for the scratch (512 sequences x 16 query heads x 2
     partials x 130 floats > 8 MiB), which is rejected before anything is launched."""
     w = W.Workload("noalloc-q4", 1, 2, 16, 4, 128, "bf16", 16, 64, 0, 1, 2, seed=107)
     cache, q = _pair(w, [5000, 1300], kv_bits=4)
     out, lse, ref, ref_lse = _both(cache, q)
     assert_close(out, ref, "4-bit out")
     assert_close(lse, ref_lse, "4-bit lse")
+    cache.close()
+    # the same with pre-RoPE keys (the kernel's rotating form), then smaller again
+    cache, q = _pair(w, [3000, 700], kv_bits=4, rope_theta=500000.0)
+    out, lse, ref, ref_lse = _both(cache, q)
+    assert_close(out, ref, "4-bit pre-RoPE out")
+    assert_close(lse, ref_lse, "4-bit pre-RoPE lse")
     cache.close()
     w2 = W.Workload("noalloc-small", 1, 1, 8, 2, 128, "bf16", 4, 32, 0, 1, 1,
                     fixed_mask=((0,),), seed=109)
