@@ -360,19 +360,21 @@ def reorder_input_cols(w, order, cols_per_head: int) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------------------------
-# 4-bit retrieval caches
+# 4-bit (and 8-bit) retrieval caches
 # --------------------------------------------------------------------------------------------
 #
 # Explainer, "Combination with Quantization" and the OpenReview reply on KV quantization:
-# DuoAttention's full caches combine with 4-bit KV quantization (per-channel, as in KIVI).
-# The pages fix the bit width only. Readings taken here, each a plain choice:
-#   * asymmetric 4-bit codes 0..15 with a scale and zero point stored in bfloat16 (round to
-#     nearest even of the float32 scale (max - min) / 15 and of the minimum);
+# DuoAttention's full caches combine with 4-bit KV quantization (per-channel, as in KIVI);
+# the explainer's "Category 3: KV Cache Quantization" names 4-bit or 8-bit storage. The pages
+# fix the bit width only. Readings taken here, each a plain choice (L = 2^bits - 1 levels
+# above zero: 15 for 4 bits, 255 for 8):
+#   * asymmetric codes 0..L with a scale and zero point stored in bfloat16 (round to
+#     nearest even of the float32 scale (max - min) / L and of the minimum);
 #   * keys per channel over aligned groups of KV4_GROUP = 128 tokens (positions g*128 ..
 #     g*128+127), values per token over the channels;
 #   * the tokens of the last, incomplete group are kept exactly (bf16) until it completes;
 #   * the code decision is taken in float32 against the stored values: c = rint((x - zero) /
-#     scale) clamped to 0..15, and c = 0 when scale is 0 (IEEE float32 division, round half to
+#     scale) clamped to 0..L, and c = 0 when scale is 0 (IEEE float32 division, round half to
 #     even), so that any float32 implementation takes the same decision;
 #   * a stored token reads back as c * scale + zero with the stored scale and zero.
 
@@ -386,45 +388,47 @@ def to_bf16(x) -> np.ndarray:
     return u.astype(np.uint32).view(np.float32)
 
 
-def kv4_codes(x, axis: int):
-    """4-bit codes of a float32 block over ``axis`` (the reduction axis of min and max).
-    Returns ``(codes uint8, scale, zero)``: the stored bfloat16 scale and zero (as float32),
-    reduced over ``axis``."""
+def kv4_codes(x, axis: int, bits: int = 4):
+    """``bits``-bit codes (4 or 8) of a float32 block over ``axis`` (the reduction axis of
+    min and max). Returns ``(codes uint8, scale, zero)``: the stored bfloat16 scale and zero
+    (as float32), reduced over ``axis``."""
+    levels = np.float32((1 << bits) - 1)
     x = np.asarray(x, dtype=np.float32)
     mn = to_bf16(x.min(axis=axis, keepdims=True))
     mx = x.max(axis=axis, keepdims=True)
-    scale = to_bf16((mx - x.min(axis=axis, keepdims=True)) / np.float32(15.0))
+    scale = to_bf16((mx - x.min(axis=axis, keepdims=True)) / levels)
     with np.errstate(divide="ignore", invalid="ignore"):
         c = np.rint((x - mn) / scale)
     c = np.where(scale == 0, np.float32(0.0), c)
-    codes = np.clip(c, 0, 15).astype(np.uint8)
+    codes = np.clip(c, 0, levels).astype(np.uint8)
     return codes, np.squeeze(scale, axis), np.squeeze(mn, axis)
 
 
-def kv4_history(x_hist, n: int, is_key: bool) -> np.ndarray:
-    """What a 4-bit full cache reads back for tokens 0..n-1 of one head, ``x_hist [>=n, d]``
-    (float64 of the stored values): complete groups dequantized (keys per channel over the
-    group, values per token), the incomplete last group exact."""
+def kv4_history(x_hist, n: int, is_key: bool, bits: int = 4) -> np.ndarray:
+    """What a ``bits``-bit full cache reads back for tokens 0..n-1 of one head,
+    ``x_hist [>=n, d]`` (float64 of the stored values): complete groups dequantized (keys per
+    channel over the group, values per token), the incomplete last group exact."""
     x = np.asarray(x_hist, dtype=np.float32)[:n]
     out = x.astype(np.float64).copy()
     full = (n // KV4_GROUP) * KV4_GROUP
     for g0 in range(0, full, KV4_GROUP):
         blk = x[g0:g0 + KV4_GROUP]
         if is_key:
-            codes, scale, zero = kv4_codes(blk, axis=0)  # per channel: over the group's tokens
+            codes, scale, zero = kv4_codes(blk, axis=0, bits=bits)  # per channel
             out[g0:g0 + KV4_GROUP] = (codes.astype(np.float64) * scale.astype(np.float64)[None, :]
                                       + zero.astype(np.float64)[None, :])
         else:
-            codes, scale, zero = kv4_codes(blk, axis=1)  # per token: over the channels
+            codes, scale, zero = kv4_codes(blk, axis=1, bits=bits)  # per token
             out[g0:g0 + KV4_GROUP] = (codes.astype(np.float64) * scale.astype(np.float64)[:, None]
                                       + zero.astype(np.float64)[:, None])
     return out
 
 
-def decode_step_kv4(q, k_hist, v_hist, retrieval, sink, recent, scale=None, rope_theta=None):
-    """``decode_step`` with the retrieval heads' full caches stored in 4 bits: every
-    retrieval KV head attends over ``kv4_history`` of its keys and values; streaming heads
-    (constant-size caches, kept exact) as before.
+def decode_step_kv4(q, k_hist, v_hist, retrieval, sink, recent, scale=None, rope_theta=None,
+                    bits: int = 4):
+    """``decode_step`` with the retrieval heads' full caches stored in ``bits`` bits (4 or 8):
+    every retrieval KV head attends over ``kv4_history`` of its keys and values; streaming
+    heads (constant-size caches, kept exact) as before.
 
     With ``rope_theta`` the keys of every head are pre-RoPE: the 4-bit codes are taken of the
     keys as given, and each key that attention reads (dequantized on retrieval heads, exact on
@@ -435,8 +439,8 @@ def decode_step_kv4(q, k_hist, v_hist, retrieval, sink, recent, scale=None, rope
     n = k.shape[0]
     for j in range(k.shape[1]):
         if retrieval[j]:
-            k[:, j] = kv4_history(k_hist[:, j], n, True)
-            v[:, j] = kv4_history(v_hist[:, j], n, False)
+            k[:, j] = kv4_history(k_hist[:, j], n, True, bits)
+            v[:, j] = kv4_history(v_hist[:, j], n, False, bits)
     if rope_theta:
         k = rope(k, np.arange(n), rope_theta)
     return decode_step(q, k, v, retrieval, sink, recent, scale)

@@ -525,28 +525,31 @@ def _bf16_grid(rng, *shape):
 
 
 def pin_kv4_nearest_level():
-    """Every code is the nearest of the 16 stored levels zero + c * scale (up to float32
-    rounding of the quotient), found by search over all 16 levels in float64; the error is at
-    most half a step inside the levels' span, and beyond it no more than the bfloat16 rounding
-    of the minimum and of the step moved the span; the stored scale and zero are the
-    bfloat16 roundings of (max - min) / 15 and of the minimum."""
+    """For 4 and 8 bits (L = 15, 255): every code is the nearest of the L + 1 stored levels
+    zero + c * scale (up to float32 rounding of the quotient), found by search over all
+    levels in float64; the error is at most half a step inside the levels' span, and beyond
+    it no more than the bfloat16 rounding of the minimum and of the step moved the span; the
+    stored scale and zero are the bfloat16 roundings of (max - min) / L and of the minimum."""
     rng = np.random.default_rng(51)
-    for shape, axis in (((64, 16), 0), ((8, 128), 1), ((64, 3), 0)):
+    for bits, shape, axis in ((4, (64, 16), 0), (4, (8, 128), 1), (4, (64, 3), 0),
+                              (8, (128, 16), 0), (8, (8, 128), 1), (8, (300, 3), 0)):
+        L = (1 << bits) - 1
         x = _bf16_grid(rng, *shape)
-        codes, scale, zero = O.kv4_codes(x, axis)
+        codes, scale, zero = O.kv4_codes(x, axis, bits=bits)
+        assert codes.max() <= L
         s = np.expand_dims(scale.astype(np.float64), axis)
         z = np.expand_dims(zero.astype(np.float64), axis)
-        levels = z[..., None] + s[..., None] * np.arange(16)
+        levels = z[..., None] + s[..., None] * np.arange(L + 1)
         dist = np.abs(x.astype(np.float64)[..., None] - levels)
         best = dist.min(axis=-1)
         got = np.take_along_axis(dist, codes[..., None].astype(np.int64), -1)[..., 0]
         assert np.all(got <= best + 1e-6 * s), shape
         mn = x.min(axis=axis, keepdims=True).astype(np.float64)
         mx = x.max(axis=axis, keepdims=True).astype(np.float64)
-        slack = np.maximum(np.maximum(z - mn, 0), np.maximum(mx - (z + 15 * s), 0))
+        slack = np.maximum(np.maximum(z - mn, 0), np.maximum(mx - (z + L * s), 0))
         assert np.all(got <= 0.5 * s * (1 + 1e-6) + slack), shape
         assert np.all(np.abs(z - mn) <= np.abs(mn) * 2.0 ** -8), shape
-        assert np.all(np.abs(s - (mx - mn) / 15) <= (mx - mn) / 15 * 2.0 ** -8 + 1e-30), shape
+        assert np.all(np.abs(s - (mx - mn) / L) <= (mx - mn) / L * 2.0 ** -8 + 1e-30), shape
         # bfloat16 values: the low 16 bits of the float32 are zero
         assert not np.any(scale.view(np.uint32) & 0xFFFF) and not np.any(zero.view(np.uint32) & 0xFFFF)
 
@@ -554,22 +557,27 @@ def pin_kv4_nearest_level():
 def pin_kv4_axes_and_exact_grids():
     """Keys are quantized per channel (over tokens), values per token (over channels): a key
     block whose every channel is constant, or a value block whose every token is constant,
-    reads back exactly; so does a block whose levels are 16 evenly spaced dyadic values from
-    min to max along the quantization axis."""
+    reads back exactly; so does a block whose values lie on L + 1 evenly spaced dyadic levels
+    from min to max along the quantization axis (both ends present), for 4 and 8 bits."""
     rng = np.random.default_rng(52)
     G, d = O.KV4_GROUP, 16
-    kc = np.tile(_bf16_grid(rng, 1, d), (G, 1))          # channel-constant keys
-    vc = np.tile(_bf16_grid(rng, G, 1), (1, d))          # token-constant values
-    assert np.array_equal(O.kv4_history(kc, G, True), kc.astype(np.float64))
-    assert np.array_equal(O.kv4_history(vc, G, False), vc.astype(np.float64))
-    step = 2.0 ** rng.integers(-6, 0, size=d)
-    base = np.round(rng.standard_normal(d) * 8) / 8
-    kidx = np.stack([rng.permutation(np.resize(np.arange(16), G)) for _ in range(d)], axis=1)
-    kg = (base[None, :] + kidx * step[None, :]).astype(np.float32)
-    assert np.array_equal(O.kv4_history(kg, G, True), kg.astype(np.float64))
-    vidx = np.stack([rng.permutation(np.resize(np.arange(16), d)) for _ in range(G)], axis=0)
-    vg = (np.float32(-1.5) + vidx * 0.25).astype(np.float32)
-    assert np.array_equal(O.kv4_history(vg, G, False), vg.astype(np.float64))
+    for bits in (4, 8):
+        L = (1 << bits) - 1
+        kc = np.tile(_bf16_grid(rng, 1, d), (G, 1))          # channel-constant keys
+        vc = np.tile(_bf16_grid(rng, G, 1), (1, d))          # token-constant values
+        assert np.array_equal(O.kv4_history(kc, G, True, bits), kc.astype(np.float64))
+        assert np.array_equal(O.kv4_history(vc, G, False, bits), vc.astype(np.float64))
+
+        def grid_idx(m):  # m level indices in 0..L with both ends present
+            return rng.permutation(np.concatenate([[0, L], rng.integers(0, L + 1, m - 2)]))
+        step = 2.0 ** rng.integers(-6, 0, size=d)
+        base = np.round(rng.standard_normal(d) * 8) / 8
+        kidx = np.stack([grid_idx(G) for _ in range(d)], axis=1)
+        kg = (base[None, :] + kidx * step[None, :]).astype(np.float32)
+        assert np.array_equal(O.kv4_history(kg, G, True, bits), kg.astype(np.float64))
+        vidx = np.stack([grid_idx(d) for _ in range(G)], axis=0)
+        vg = (np.float32(-1.5) + vidx * 2.0 ** -6).astype(np.float32)
+        assert np.array_equal(O.kv4_history(vg, G, False, bits), vg.astype(np.float64))
 
 
 def pin_kv4_groups_and_residual():
@@ -578,18 +586,24 @@ def pin_kv4_groups_and_residual():
     sequence shorter than one group) read back exactly."""
     rng = np.random.default_rng(53)
     G = O.KV4_GROUP
-    for is_key in (True, False):
-        x = _bf16_grid(rng, 3 * G + 17, 8)
-        h = O.kv4_history(x, x.shape[0], is_key)
-        assert np.array_equal(h[3 * G:], x[3 * G:].astype(np.float64))
-        assert not np.array_equal(h[:3 * G], x[:3 * G].astype(np.float64))
-        y = x.copy()
-        y[G:2 * G] = _bf16_grid(rng, G, 8)
-        hy = O.kv4_history(y, y.shape[0], is_key)
-        assert np.array_equal(hy[:G], h[:G]) and np.array_equal(hy[2 * G:], h[2 * G:])
-        for n in (1, G - 1):
-            assert np.array_equal(O.kv4_history(x, n, is_key), x[:n].astype(np.float64))
-        assert np.array_equal(O.kv4_history(x, 2 * G, is_key)[:G], h[:G])
+    for bits in (4, 8):
+        for is_key in (True, False):
+            x = _bf16_grid(rng, 3 * G + 17, 8)
+            h = O.kv4_history(x, x.shape[0], is_key, bits)
+            assert np.array_equal(h[3 * G:], x[3 * G:].astype(np.float64))
+            assert not np.array_equal(h[:3 * G], x[:3 * G].astype(np.float64))
+            y = x.copy()
+            y[G:2 * G] = _bf16_grid(rng, G, 8)
+            hy = O.kv4_history(y, y.shape[0], is_key, bits)
+            assert np.array_equal(hy[:G], h[:G]) and np.array_equal(hy[2 * G:], h[2 * G:])
+            for n in (1, G - 1):
+                assert np.array_equal(O.kv4_history(x, n, is_key, bits), x[:n].astype(np.float64))
+            assert np.array_equal(O.kv4_history(x, 2 * G, is_key, bits)[:G], h[:G])
+        # 8 bits read back closer than 4 on general data
+        x = _bf16_grid(rng, 2 * G, 8)
+        e4 = np.abs(O.kv4_history(x, 2 * G, True, 4) - x).max()
+        e8 = np.abs(O.kv4_history(x, 2 * G, True, 8) - x).max()
+        assert e8 < e4 / 8
 
 
 def pin_kv4_decode():
@@ -602,18 +616,19 @@ def pin_kv4_decode():
     q = _bf16_grid(rng, Hkv * Gq, d)
     k = _bf16_grid(rng, n, Hkv, d)
     v = _bf16_grid(rng, n, Hkv, d)
-    a, _ = O.decode_step(q, k, v, [0, 0], S, R)
-    b, _ = O.decode_step_kv4(q, k, v, [0, 0], S, R)
-    assert np.array_equal(a, b)
-    a, _ = O.decode_step(q, k, v, [1, 0], S, R)
-    b, _ = O.decode_step_kv4(q, k, v, [1, 0], S, R)
-    assert np.array_equal(a[Gq:], b[Gq:]) and 0 < np.abs(a[:Gq] - b[:Gq]).max() < 0.5
-    # channel-constant keys and token-constant values are exact in 4 bits
-    k2 = np.repeat(_bf16_grid(rng, 1, Hkv, d), n, axis=0)
-    v2 = np.repeat(_bf16_grid(rng, n, Hkv, 1), d, axis=2)
-    a, _ = O.decode_step(q, k2, v2, [1, 1], S, R)
-    b, _ = O.decode_step_kv4(q, k2, v2, [1, 1], S, R)
-    assert np.allclose(a, b, rtol=0, atol=1e-12)
+    for bits, bound in ((4, 0.5), (8, 0.05)):
+        a, _ = O.decode_step(q, k, v, [0, 0], S, R)
+        b, _ = O.decode_step_kv4(q, k, v, [0, 0], S, R, bits=bits)
+        assert np.array_equal(a, b)
+        a, _ = O.decode_step(q, k, v, [1, 0], S, R)
+        b, _ = O.decode_step_kv4(q, k, v, [1, 0], S, R, bits=bits)
+        assert np.array_equal(a[Gq:], b[Gq:]) and 0 < np.abs(a[:Gq] - b[:Gq]).max() < bound
+        # channel-constant keys and token-constant values are exact
+        k2 = np.repeat(_bf16_grid(rng, 1, Hkv, d), n, axis=0)
+        v2 = np.repeat(_bf16_grid(rng, n, Hkv, 1), d, axis=2)
+        a, _ = O.decode_step(q, k2, v2, [1, 1], S, R)
+        b, _ = O.decode_step_kv4(q, k2, v2, [1, 1], S, R, bits=bits)
+        assert np.allclose(a, b, rtol=0, atol=1e-12)
 
 
 def pin_rope_complex_form():
@@ -789,22 +804,23 @@ def _mixed_unnormalized(q, k, v, q_pos, k_pos, alpha, sink, recent, scale=None):
     return out
 
 
-def _kv4_codes_variant(floor=False, levels=15):
-    def f(x, axis):
+def _kv4_codes_variant(floor=False, extra_level=False, ignore_bits=False):
+    def f(x, axis, bits=4):
+        L = 15 if ignore_bits else (1 << bits) - 1
         x = np.asarray(x, dtype=np.float32)
         mn = x.min(axis=axis, keepdims=True)
         mx = x.max(axis=axis, keepdims=True)
-        scale = (mx - mn) / np.float32(levels)
+        scale = (mx - mn) / np.float32(L + 1 if extra_level else L)
         with np.errstate(divide="ignore", invalid="ignore"):
             r = (x - mn) / scale
             c = np.floor(r) if floor else np.rint(r)
         c = np.where(scale == 0, np.float32(0.0), c)
-        return np.clip(c, 0, 15).astype(np.uint8), np.squeeze(scale, axis), np.squeeze(mn, axis)
+        return np.clip(c, 0, L).astype(np.uint8), np.squeeze(scale, axis), np.squeeze(mn, axis)
     return f
 
 
 def _kv4_history_variant(swap_axes=False, quantize_tail=False, misaligned=False):
-    def f(x_hist, n, is_key):
+    def f(x_hist, n, is_key, bits=4):
         x = np.asarray(x_hist, dtype=np.float32)[:n]
         out = x.astype(np.float64).copy()
         G = O.KV4_GROUP
@@ -816,7 +832,7 @@ def _kv4_history_variant(swap_axes=False, quantize_tail=False, misaligned=False)
         for g0 in starts:
             blk = x[g0:g0 + G]
             per_channel = is_key != swap_axes
-            codes, scale, zero = O.kv4_codes(blk, axis=0 if per_channel else 1)
+            codes, scale, zero = O.kv4_codes(blk, axis=0 if per_channel else 1, bits=bits)
             if per_channel:
                 out[g0:g0 + len(blk)] = codes * scale.astype(np.float64)[None] + zero[None]
             else:
@@ -846,11 +862,11 @@ def _rope_variant(interleaved=False, sign=1.0, exponent=2.0, offset=0):
 
 
 def _kv4_rope_before_quant(q, k_hist, v_hist, retrieval, sink, recent, scale=None,
-                           rope_theta=None):
+                           rope_theta=None, bits=4):
     k = np.asarray(k_hist, dtype=np.float64)
     if rope_theta:
         k = O.rope(k, np.arange(k.shape[0]), rope_theta).astype(np.float32)
-    return _ORIG_KV4(q, k, v_hist, retrieval, sink, recent, scale)
+    return _ORIG_KV4(q, k, v_hist, retrieval, sink, recent, scale, bits=bits)
 
 
 _ORIG_KV4 = O.decode_step_kv4
@@ -886,7 +902,8 @@ MUTANTS = {
     "head_order_streaming_first": ("head_order",
                                    lambda m: np.argsort(np.asarray(m) != 0, kind="stable")),
     "kv4_floor": ("kv4_codes", _kv4_codes_variant(floor=True)),
-    "kv4_sixteen_steps": ("kv4_codes", _kv4_codes_variant(levels=16)),
+    "kv4_sixteen_steps": ("kv4_codes", _kv4_codes_variant(extra_level=True)),
+    "kv8_levels_of_4_bits": ("kv4_codes", _kv4_codes_variant(ignore_bits=True)),
     "kv4_axes_swapped": ("kv4_history", _kv4_history_variant(swap_axes=True)),
     "kv4_tail_quantized": ("kv4_history", _kv4_history_variant(quantize_tail=True)),
     "kv4_groups_misaligned": ("kv4_history", _kv4_history_variant(misaligned=True)),
