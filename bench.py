@@ -62,17 +62,19 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--splits", type=int, default=0, help="force decode splits (0 = automatic)")
     p.add_argument("--unfused", action="store_true", help="time append + decode as two calls")
-    p.add_argument("--legs", default="decode,kv4,kv4rope,c4,prefill,reorder,probe,cpu",
+    p.add_argument("--legs", default="decode,kv4,kv4rope,kv8,c4,prefill,reorder,probe,cpu",
                    help="legs to run: decode (the headline, always run), kv4 (4-bit full "
-                        "caches), kv4rope (4-bit with pre-RoPE keys), c4 (32 layers x batch 8, ragged), prefill (the legs of "
+                        "caches), kv4rope (4-bit with pre-RoPE keys), kv8 (8-bit), c4 (32 layers x batch 8, ragged), prefill (the legs of "
                         "--prefill-modes), reorder, probe (read and copy bandwidth), cpu "
                         "(the oracle on the host)")
     a = p.parse_args()
     legs = set(a.legs.split(","))
-    unknown = legs - {"decode", "kv4", "kv4rope", "c4", "prefill", "reorder", "probe", "cpu"}
+    unknown = legs - {"decode", "kv4", "kv4rope", "kv8", "c4", "prefill", "reorder", "probe",
+                      "cpu"}
     if unknown:
         p.error(f"unknown legs {sorted(unknown)}")
     a.no_kv4rope = a.no_kv4 or "kv4rope" not in legs
+    a.no_kv8 = "kv8" not in legs
     a.no_kv4 = a.no_kv4 or "kv4" not in legs
     a.no_prefill = a.no_prefill or "prefill" not in legs
     a.no_cpu = a.no_cpu or "cpu" not in legs
@@ -148,7 +150,8 @@ def decode_leg(args, torch, hsk, W, N, kv_bits=0, rope_theta=0.0):
     vs = torch.from_numpy(W.tokens(w, "v", 0, 0, n0, n0 + total_steps)).to(dev).to(torch.bfloat16)
     out = torch.empty((1, w.hq, w.d), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
-    kind = " (4-bit full caches" + (", pre-RoPE keys)" if rope_theta else ")") if kv_bits == 4 else ""
+    kind = (f" ({kv_bits}-bit full caches" + (", pre-RoPE keys)" if rope_theta else ")")
+            if kv_bits in (4, 8) else "")
     log(f"decode leg{kind}: {w.name}, {L} replica "
         f"layers filled to {n0} tokens in {time.time() - t:.1f}s")
 
@@ -663,6 +666,13 @@ def main():
             f"({dec['us_layer'] / dec4['us_layer']:.2f}x the bf16 step), {dec4['gbs']:.0f} GB/s of "
             f"stored bytes; split kernel {dec4['kern_us']:.2f} us = {dec4['kern_gbs']:.0f} GB/s; "
             f"one duo_attn_decode call {dec4['dec_us']:.2f} us")
+    dec8 = None
+    if not args.no_kv8:
+        dec8 = decode_leg(args, torch, hsk, W, N, kv_bits=8)
+        log(f"decode, 8-bit full caches: {dec8['us_layer']:.2f} us/layer-step "
+            f"({dec['us_layer'] / dec8['us_layer']:.2f}x the bf16 step), {dec8['gbs']:.0f} GB/s of "
+            f"stored bytes; split kernel {dec8['kern_us']:.2f} us = {dec8['kern_gbs']:.0f} GB/s; "
+            f"one duo_attn_decode call {dec8['dec_us']:.2f} us")
     dec4r = None
     if not args.no_kv4rope:
         dec4r = decode_leg(args, torch, hsk, W, N, kv_bits=4, rope_theta=ROPE_THETA)
@@ -787,6 +797,21 @@ def main():
                          "traffic": committed_traffic("decode.hip", f"decode_kv4_{args.workload}"),
                          "kernel": "decode_q4_kernel<d128, G4> (split attention kernel)",
                          "kernel_us": round(dec4["kern_us"], 3)},
+        },
+        "decode_kv8": None if dec8 is None else {
+            "workload": "the same 128K GQA decode with 8-bit full caches (the 4-bit scheme with "
+                        "255 levels)",
+            "us_per_layer_step": round(dec8["us_layer"], 3),
+            "speedup_vs_bf16_step": round(dec["us_layer"] / dec8["us_layer"], 3),
+            "GBps": round(dec8["gbs"], 1),
+            "stored_bytes_per_layer_step": int(dec8["step_bytes"]),
+            "decode_call_us": round(dec8["dec_us"], 3),
+            "roofline": {"bound": "hbm", "achieved": round(dec8["kern_gbs"], 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(dec8["kern_gbs"] / HBM_PEAK_GBS, 4),
+                         "traffic": None,
+                         "kernel": "decode_q4_kernel<d128, G4, 8-bit> (split attention kernel)",
+                         "kernel_us": round(dec8["kern_us"], 3)},
         },
         "decode_kv4_rope": None if dec4r is None else {
             "workload": "the same 4-bit decode with pre-RoPE keys (base 500,000): retrieval "

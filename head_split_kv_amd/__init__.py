@@ -41,8 +41,8 @@ def make_config(*, num_layers: int, batch: int, num_q_heads: int, num_kv_heads: 
 
     ``streaming_prefill`` is ``"window"`` (streaming heads use the per-query sink + recent
     mask during pre-filling) or ``"chunk"`` (they see the whole pruned cache before the chunk
-    plus the chunk causally). ``kv_bits=4`` stores the full (retrieval) caches in 4 bits;
-    with it, ``rope_theta > 0`` takes keys before RoPE (base ``rope_theta``, rotate-half
+    plus the chunk causally). ``kv_bits=4`` (or 8) stores the full (retrieval) caches in 4
+    (8) bits; with it, ``rope_theta > 0`` takes keys before RoPE (base ``rope_theta``, rotate-half
     pairs) and queries after it, and attention turns each key at its position."""
     if streaming_prefill not in _PREFILL_MODES:
         raise ValueError(f"streaming_prefill must be 'window' or 'chunk', not {streaming_prefill!r}")

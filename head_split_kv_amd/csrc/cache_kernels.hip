@@ -115,7 +115,7 @@ __global__ void __launch_bounds__(kThreads) append_kernel(AppendArgs a) {
     const int32_t ci = a.cls_idx[j];
     char* dst;
     if (ci >= 0) {
-      if (a.q4) continue;  // 4-bit full caches: written by the kv4 append
+      if (a.qbits) continue;  // 4- or 8-bit full caches: written by the quantizing append
       dst = (char*)(tensor ? a.full_v : a.full_k) +
             (((int64_t)b * a.Hr + ci) * a.cap + t) * a.row_bytes + c * 16;
     } else {

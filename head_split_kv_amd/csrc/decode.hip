@@ -515,6 +515,17 @@ __device__ __forceinline__ half8_t codes_to_f16(uint32_t w) {
   const u32x4_t r = {w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu, w8 & 0x00F000F0u};
   return __builtin_bit_cast(half8_t, r);
 }
+// 8-bit caches: two words of four byte codes (w0 elements 0..3, w1 elements 4..7) as fp16
+// denormals c 2^-24 (c <= 255, exact), pair j of the operand holding elements j and j + 4: the
+// slot order of codes_to_f16, with no high nibbles.
+__device__ __forceinline__ uint32_t byte_pair(uint32_t w0, uint32_t w1, int j) {
+  return ((w0 >> (8 * j)) & 0xFFu) | (((w1 >> (8 * j)) & 0xFFu) << 16);
+}
+__device__ __forceinline__ half8_t bytes_to_f16(uint32_t w0, uint32_t w1) {
+  const u32x4_t r = {byte_pair(w0, w1, 0), byte_pair(w0, w1, 1), byte_pair(w0, w1, 2),
+                     byte_pair(w0, w1, 3)};
+  return __builtin_bit_cast(half8_t, r);
+}
 
 constexpr int kBfStages = 6;  // bf16 row fragments in flight in decode_q4_kernel
 
@@ -531,9 +542,12 @@ __device__ __attribute__((aligned(256))) uint32_t g_q4_idle[4096];
 // real units. The bf16 rows (the residual group, streaming slots at the positions they hold,
 // a fused step's token) are turned in float32 and dotted with the query in float32; every
 // cache keeps the keys as given.
+// 8-bit caches (BITS = 8) run the same kernel: a token's key codes and a step's value codes
+// take twice the words (bytes_to_f16 instead of codes_to_f16, same operand slots), and no
+// operand carries the 1/16 of high nibbles.
 // Leading arguments as for decode_kernel.
-template <int D, int G, int LPT, int NS, bool kRope>
-__global__ void __launch_bounds__(kThreads, kRope ? 1 : 2)
+template <int D, int G, int LPT, int NS, bool kRope, int BITS>
+__global__ void __launch_bounds__(kThreads, (kRope || BITS == 8) ? 1 : 2)
     decode_q4_kernel(int32_t lead_nsplit, int32_t lead_hr, int32_t lead_hs, int32_t lead_b,
                      int32_t lead_nss, int32_t lead_fused, DecodeArgs a) {
   using T = uint16_t;
@@ -543,9 +557,12 @@ __global__ void __launch_bounds__(kThreads, kRope ? 1 : 2)
   constexpr int kTpw = 64 / LPT;
   constexpr int kTpb = kWaves * kTpw;
   constexpr int RB = D * 2;
-  constexpr int CBY = D / 2;   // code bytes of one key token row
+  constexpr int CBY = D * BITS / 8;  // code bytes of one key token row
   constexpr int KC = D / 32;   // 32-channel k-chunks of the logit product
   constexpr int CBK = D / 16;  // 16-channel blocks of the value product
+  constexpr int KW = KC * BITS / 4;   // key code words of a lane per token
+  constexpr int VW = CBK * BITS / 4;  // value code words of a lane per step
+  static_assert(BITS == 4 || BITS == 8, "4- or 8-bit codes");
   constexpr int kStep = 32;    // tokens per wave step
   constexpr int kSteps = kQ4Group / kStep;
   static_assert(G <= 16 && kSteps % 2 == 0, "query rows must fit the 16-row tile");
@@ -738,7 +755,7 @@ __global__ void __launch_bounds__(kThreads, kRope ? 1 : 2)
             const uint32_t s1 = (j & 1) ? sw[2 + (j >> 1)] & 0xFFFF0000u : sw[2 + (j >> 1)] << 16;
             const uint32_t z0 = (j & 1) ? zw[j >> 1] & 0xFFFF0000u : zw[j >> 1] << 16;
             const uint32_t z1 = (j & 1) ? zw[2 + (j >> 1)] & 0xFFFF0000u : zw[2 + (j >> 1)] << 16;
-            const float hs = (j & 1) ? 0.0625f : 1.f;
+            const float hs = (BITS == 4 && (j & 1)) ? 0.0625f : 1.f;
             rs[kc][j] = half2_t{(_Float16)(__builtin_bit_cast(float, s0) * hs),
                                 (_Float16)(__builtin_bit_cast(float, s1) * hs)};
             rz[kc][j] = half2_t{(_Float16)__builtin_bit_cast(float, z0),
@@ -765,7 +782,7 @@ __global__ void __launch_bounds__(kThreads, kRope ? 1 : 2)
           const uint32_t hz = (x & 1) ? zw[x >> 1] & 0xFFFF0000u : zw[x >> 1] << 16;
           const float qf = qlive * __builtin_bit_cast(float, hq);
           qa[kc][e] = (_Float16)(qf * __builtin_bit_cast(float, hs) *
-                                 (kCodeHigh[e] ? 0.0625f : 1.f));
+                                 ((BITS == 4 && kCodeHigh[e]) ? 0.0625f : 1.f));
           bp = __builtin_fmaf(qf, __builtin_bit_cast(float, hz), bp);
         }
       }
@@ -774,8 +791,8 @@ __global__ void __launch_bounds__(kThreads, kRope ? 1 : 2)
       bias = bp * (1.f / kTwo24);  // the product accumulates in units of 2^-24
     };
     struct Ld {
-      uint32_t k[2][KC];  // key code words of the two 16-token tiles
-      uint32_t v[CBK];    // value code words of the channel blocks
+      uint32_t k[2][KW];  // key code words of the two 16-token tiles
+      uint32_t v[VW];     // value code words of the channel blocks
       u32x4_t vp[2];      // bf16 value scale | zero of tokens 16 tau + 4 jj + 0..3
     };
     // Loads address a wave-uniform group base plus a constant 32-bit lane offset plus an
@@ -784,7 +801,7 @@ __global__ void __launch_bounds__(kThreads, kRope ? 1 : 2)
     // base and of the lane offset, not a branch: a branch would split the loop body and let
     // the compiler move the last uses of a slot below its reload.
     const int64_t q4p = a.q4_params;
-    const uint32_t lk = col * CBY + jj * KC * 4;          // token col's key words of slice jj
+    const uint32_t lk = col * CBY + jj * KW * 4;          // token col's key words of slice jj
     const uint32_t lv = lane * 16;                         // this lane's 16 bytes of each KB
     const uint32_t lp = 16 * jj;                           // value parameters of tokens 4 jj ..
     const uint32_t lk_d = lk & 1023;
@@ -797,11 +814,16 @@ __global__ void __launch_bounds__(kThreads, kRope ? 1 : 2)
       const uint32_t ok = real ? lk : lk_d;
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau) {
-        // token 32 st + 16 tau + col: words KC jj .. KC jj + KC - 1 of its row
+        // token 32 st + 16 tau + col: words KW jj .. KW jj + KW - 1 of its row
         const char* kr = kb + ok + (st * kStep + 16 * tau) * CBY;
-        if constexpr (KC == 4) {
-          const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kr));
-          f.k[tau][0] = x.x; f.k[tau][1] = x.y; f.k[tau][2] = x.z; f.k[tau][3] = x.w;
+        if constexpr (KW >= 4) {
+#pragma unroll
+          for (int i = 0; i < KW / 4; ++i) {
+            const u32x4_t x =
+                __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kr + 16 * i));
+            f.k[tau][4 * i] = x.x; f.k[tau][4 * i + 1] = x.y;
+            f.k[tau][4 * i + 2] = x.z; f.k[tau][4 * i + 3] = x.w;
+          }
         } else {
           const u32x2_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(kr));
           f.k[tau][0] = x.x; f.k[tau][1] = x.y;
@@ -809,11 +831,11 @@ __global__ void __launch_bounds__(kThreads, kRope ? 1 : 2)
         // parameters of tokens 32 st + 16 tau + 4 jj .. + 3
         f.vp[tau] = *(const u32x4_t*)(pb + lp + (st * kStep + 16 * tau) * 4);
       }
-      // step st: CBK / 4 contiguous KB, word w of this lane's 16 bytes in KB h is channel
-      // block 4 h + w
-      const char* vr = vb + lv + st * (CBK / 4) * 1024;
+      // step st: VW / 4 contiguous KB, word w of this lane's 16 bytes in KB h is channel
+      // block 4 h + w (4 bits), or channel block 2 h + w / 2, tile w % 2 (8 bits)
+      const char* vr = vb + lv + st * (VW / 4) * 1024;
 #pragma unroll
-      for (int h = 0; h < CBK / 4; ++h) {
+      for (int h = 0; h < VW / 4; ++h) {
         const u32x4_t x =
             __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vr + h * 1024));
         f.v[4 * h] = x.x; f.v[4 * h + 1] = x.y; f.v[4 * h + 2] = x.z; f.v[4 * h + 3] = x.w;
@@ -830,10 +852,18 @@ __global__ void __launch_bounds__(kThreads, kRope ? 1 : 2)
           half2_t dq[KC][4];
 #pragma unroll
           for (int kc = 0; kc < KC; ++kc) {
-            const uint32_t w = f.k[tau][kc], w8 = w >> 8;
-            const uint32_t m[4] = {(w & 0x000F000Fu) | 0x64006400u, (w & 0x00F000F0u) | 0x64006400u,
-                                   (w8 & 0x000F000Fu) | 0x64006400u,
-                                   (w8 & 0x00F000F0u) | 0x64006400u};
+            uint32_t m[4];
+            if constexpr (BITS == 4) {
+              const uint32_t w = f.k[tau][kc], w8 = w >> 8;
+              m[0] = (w & 0x000F000Fu) | 0x64006400u;
+              m[1] = (w & 0x00F000F0u) | 0x64006400u;
+              m[2] = (w8 & 0x000F000Fu) | 0x64006400u;
+              m[3] = (w8 & 0x00F000F0u) | 0x64006400u;
+            } else {
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                m[j] = byte_pair(f.k[tau][2 * kc], f.k[tau][2 * kc + 1], j) | 0x64006400u;
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j)
               dq[kc][j] = __builtin_elementwise_fma(
@@ -867,9 +897,11 @@ __global__ void __launch_bounds__(kThreads, kRope ? 1 : 2)
             sacc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[kc], qa[kc], sacc[tau], 0, 0, 0);
         } else {
 #pragma unroll
-          for (int kc = 0; kc < KC; ++kc)
-            sacc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_to_f16(f.k[tau][kc]),
-                                                              qa[kc], sacc[tau], 0, 0, 0);
+          for (int kc = 0; kc < KC; ++kc) {
+            const half8_t ka = BITS == 4 ? codes_to_f16(f.k[tau][kc])
+                                         : bytes_to_f16(f.k[tau][2 * kc], f.k[tau][2 * kc + 1]);
+            sacc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qa[kc], sacc[tau], 0, 0, 0);
+          }
         }
       }
       // online softmax of query col over the 32 tokens: the common case compares the lane's
@@ -904,13 +936,15 @@ __global__ void __launch_bounds__(kThreads, kRope ? 1 : 2)
         const float p = fexp2(__builtin_fmaf(sacc[tau][i], c2s, -mq));
         lq += p;
         zq = __builtin_fmaf(p, __builtin_bit_cast(float, w & 0xFFFF0000u), zq);
-        pb[2 * i + tau] =
-            (_Float16)(p * __builtin_bit_cast(float, w << 16) * ((x & 1) ? 0.0625f : 1.f));
+        pb[2 * i + tau] = (_Float16)(p * __builtin_bit_cast(float, w << 16) *
+                                     ((BITS == 4 && (x & 1)) ? 0.0625f : 1.f));
       }
 #pragma unroll
-      for (int cb = 0; cb < CBK; ++cb)
-        oacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_to_f16(f.v[cb]), pb, oacc[cb],
-                                                          0, 0, 0);
+      for (int cb = 0; cb < CBK; ++cb) {
+        const half8_t va = BITS == 4 ? codes_to_f16(f.v[cb])
+                                     : bytes_to_f16(f.v[2 * cb], f.v[2 * cb + 1]);
+        oacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, oacc[cb], 0, 0, 0);
+      }
     };
 
     // one register slot per step of a group: slot s is refilled with step s of the next
@@ -1338,14 +1372,16 @@ struct Variant {
   // form when rope), counting at most max_per_cu per CU; the occupancy is queried once per
   // process. The host sizes one round of splits from it (two blocks per CU for a batch, one
   // for a single sequence).
-  static int resident_blocks(bool q4, bool rope, int max_per_cu) {
-    static int cus_cached = 0, per_cu_cached[3] = {0, 0, 0};
-    const int kind = q4 ? (rope ? 2 : 1) : 0;
+  static int resident_blocks(int qbits, bool rope, int max_per_cu) {
+    static int cus_cached = 0, per_cu_cached[5] = {0, 0, 0, 0, 0};
+    const int kind = qbits ? (qbits == 8 ? 3 : 1) + (rope ? 1 : 0) : 0;
     if (!per_cu_cached[kind]) {
       const void* fn = reinterpret_cast<const void*>(&decode_kernel<T, D, G, LPT, NS>);
       if constexpr (sizeof(T) == 2) {
-        if (kind == 1) fn = reinterpret_cast<const void*>(&decode_q4_kernel<D, G, LPT, 4, false>);
-        if (kind == 2) fn = reinterpret_cast<const void*>(&decode_q4_kernel<D, G, LPT, 4, true>);
+        if (kind == 1) fn = reinterpret_cast<const void*>(&decode_q4_kernel<D, G, LPT, 4, false, 4>);
+        if (kind == 2) fn = reinterpret_cast<const void*>(&decode_q4_kernel<D, G, LPT, 4, true, 4>);
+        if (kind == 3) fn = reinterpret_cast<const void*>(&decode_q4_kernel<D, G, LPT, 4, false, 8>);
+        if (kind == 4) fn = reinterpret_cast<const void*>(&decode_q4_kernel<D, G, LPT, 4, true, 8>);
       }
       int dev = 0, cus = 0, per_cu = 0;
       if (hipGetDevice(&dev) != hipSuccess ||
@@ -1363,31 +1399,40 @@ struct Variant {
   }
 
   static int launch(const DecodeArgs& a, void* stream, const KernelMarks& marks) {
-    const int64_t blocks = (int64_t)a.B * a.Hr * a.nsplit + (a.q4 ? (int64_t)a.B * a.Hr : 0) +
+    const int64_t blocks = (int64_t)a.B * a.Hr * a.nsplit + (a.qbits ? (int64_t)a.B * a.Hr : 0) +
                            (int64_t)a.B * a.Hs * a.nss;
     if (marks.begin) (void)hipEventRecord((hipEvent_t)marks.begin, (hipStream_t)stream);
     if constexpr (sizeof(T) == 2) {
-      if (a.q4 && a.rope_base)
-        hipLaunchKernelGGL((decode_q4_kernel<D, G, LPT, 4, true>), dim3((unsigned)blocks),
-                           dim3(kThreads), 0, (hipStream_t)stream, a.nsplit, a.Hr, a.Hs, a.B, a.nss,
-                           a.new_k != nullptr ? 1 : 0, a);
-      else if (a.q4)
-        hipLaunchKernelGGL((decode_q4_kernel<D, G, LPT, 4, false>), dim3((unsigned)blocks),
-                           dim3(kThreads), 0, (hipStream_t)stream, a.nsplit, a.Hr, a.Hs, a.B, a.nss,
-                           a.new_k != nullptr ? 1 : 0, a);
+      const dim3 grid((unsigned)blocks), block(kThreads);
+      hipStream_t st = (hipStream_t)stream;
+      const int fused = a.new_k != nullptr ? 1 : 0;
+      if (a.qbits == 4 && a.rope_base)
+        hipLaunchKernelGGL((decode_q4_kernel<D, G, LPT, 4, true, 4>), grid, block, 0, st,
+                           a.nsplit, a.Hr, a.Hs, a.B, a.nss, fused, a);
+      else if (a.qbits == 4)
+        hipLaunchKernelGGL((decode_q4_kernel<D, G, LPT, 4, false, 4>), grid, block, 0, st,
+                           a.nsplit, a.Hr, a.Hs, a.B, a.nss, fused, a);
+      else if (a.qbits == 8 && a.rope_base)
+        hipLaunchKernelGGL((decode_q4_kernel<D, G, LPT, 4, true, 8>), grid, block, 0, st,
+                           a.nsplit, a.Hr, a.Hs, a.B, a.nss, fused, a);
+      else if (a.qbits == 8)
+        hipLaunchKernelGGL((decode_q4_kernel<D, G, LPT, 4, false, 8>), grid, block, 0, st,
+                           a.nsplit, a.Hr, a.Hs, a.B, a.nss, fused, a);
+      else if (a.qbits)
+        return -1;
       else
         hipLaunchKernelGGL((decode_kernel<T, D, G, LPT, NS>), dim3((unsigned)blocks),
                            dim3(kThreads), 0, (hipStream_t)stream, a.nsplit, a.Hr, a.Hs, a.B, a.nss,
                            a.new_k != nullptr ? 1 : 0, a);
     } else {
-      if (a.q4) return -1;
+      if (a.qbits) return -1;
       hipLaunchKernelGGL((decode_kernel<T, D, G, LPT, NS>), dim3((unsigned)blocks),
                          dim3(kThreads), 0, (hipStream_t)stream, a.nsplit, a.Hr, a.Hs, a.B, a.nss,
                            a.new_k != nullptr ? 1 : 0, a);
     }
     if (marks.end) (void)hipEventRecord((hipEvent_t)marks.end, (hipStream_t)stream);
     // split heads (retrieval heads when nsplit > 1, streaming heads when nss > 1)
-    const int ret_parts = a.nsplit + (a.q4 ? 1 : 0);
+    const int ret_parts = a.nsplit + (a.qbits ? 1 : 0);
     if ((ret_parts > 1 && a.Hr > 0) || (a.nss > 1 && a.Hs > 0)) {
       uint64_t ret_mask = 0;
       for (int r = 0; r < a.Hr; ++r) ret_mask |= 1ull << a.ret_kv[r];
@@ -1407,8 +1452,8 @@ struct Variant {
 
 template <typename T, int D, int G>
 int run(bool query, const DecodeArgs* a, void* stream, const KernelMarks* marks) {
-  // a query reads a->q4, whether a->rope_base is set and the per-CU cap in a->nsplit
-  return query ? Variant<T, D, G>::resident_blocks(a->q4 != 0, a->rope_base != nullptr,
+  // a query reads a->qbits, whether a->rope_base is set and the per-CU cap in a->nsplit
+  return query ? Variant<T, D, G>::resident_blocks(a->qbits, a->rope_base != nullptr,
                                                    a->nsplit)
                : Variant<T, D, G>::launch(*a, stream, *marks);
 }
@@ -1467,12 +1512,12 @@ int static_scratch(void** ptr) {
   return 0;
 }
 
-int decode_resident_blocks(int dtype, int head_dim, int group, bool q4, bool rope,
+int decode_resident_blocks(int dtype, int head_dim, int group, int qbits, bool rope,
                            int max_per_cu) {
   static const float marker = 0.f;
-  DecodeArgs probe;  // only q4, rope_base (null or not) and nsplit (the per-CU cap) are read
+  DecodeArgs probe;  // only qbits, rope_base (null or not) and nsplit (the per-CU cap) are read
   std::memset(&probe, 0, sizeof(probe));
-  probe.q4 = q4 ? 1 : 0;
+  probe.qbits = qbits;
   probe.rope_base = rope ? &marker : nullptr;
   probe.nsplit = max_per_cu;
   return dispatch(dtype, head_dim, group, true, &probe, nullptr, nullptr);

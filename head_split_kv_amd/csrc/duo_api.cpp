@@ -150,16 +150,17 @@ duo_status decode_impl(duo_cache* c, int32_t layer, const void* q, const void* k
   a.R = c->cfg.recent;
   a.max_splits = c->cfg.max_splits;
   const int group = c->cfg.num_q_heads / c->cfg.num_kv_heads;
-  const bool q4 = c->cfg.kv_bits == 4;
-  // 4-bit caches: a streaming head's window is cut over up to 8 blocks of ~128 slots, so that
+  const int32_t qbits = (c->cfg.kv_bits == 4 || c->cfg.kv_bits == 8) ? c->cfg.kv_bits : 0;
+  const bool quant = qbits != 0;  // 4- or 8-bit full caches
+  // 4- and 8-bit caches: a streaming head's window is cut over up to 8 blocks of ~128 slots, so that
   // it is done long before the retrieval groups
   a.nss = 1;
-  if (q4 && a.Hs > 0) {
+  if (quant && a.Hs > 0) {
     const int32_t rows = std::min(n_max, c->cfg.sink + c->cfg.recent);
     a.nss = std::max(1, std::min({8, (rows + 127) / 128, (int)c->cfg.max_splits}));
   }
-  // 4-bit caches: one more block and one more partial per retrieval head (its residual rows)
-  const int32_t split_cap = q4 ? a.max_splits - 1 : a.max_splits;
+  // 4- and 8-bit caches: one more block and one more partial per retrieval head (its residual rows)
+  const int32_t split_cap = quant ? a.max_splits - 1 : a.max_splits;
   // One round of splits: two blocks per CU for a batch, whose sequences' unequal lengths then
   // share each CU (the second block takes up the bandwidth a short sequence's block leaves),
   // one block per CU for a single sequence, whose four waves then have the CU's memory
@@ -168,20 +169,20 @@ duo_status decode_impl(duo_cache* c, int32_t layer, const void* q, const void* k
   // 23.3 us; the 32 layers of 8 ragged sequences 2,355 us at two blocks per CU against
   // 2,477 us at one.
   const RopePtrs rp = rope_ptrs(c);
-  const int32_t resident = decode_resident_blocks(c->cfg.dtype, c->cfg.head_dim, group, q4,
+  const int32_t resident = decode_resident_blocks(c->cfg.dtype, c->cfg.head_dim, group, qbits,
                                                   rp.base != nullptr, a.B == 1 ? 1 : 2);
   a.nsplit = c->force_splits
                  ? std::min(c->force_splits, split_cap)
-                 : choose_decode_splits(n_max, a.B, a.Hr, a.Hs * a.nss + (q4 ? a.Hr : 0),
+                 : choose_decode_splits(n_max, a.B, a.Hr, a.Hs * a.nss + (quant ? a.Hr : 0),
                                         split_cap, resident);
   if (use_static) {
-    // partials per (sequence, query head): the splits (plus the residual's on a 4-bit
-    // cache) or a 4-bit streaming window's blocks; fewer splits until they fit the scratch
-    const int32_t extra = q4 ? 1 : 0;
+    // partials per (sequence, query head): the splits (plus the residual's on a quantized
+    // cache) or a quantized cache's streaming window blocks; fewer splits until they fit the scratch
+    const int32_t extra = quant ? 1 : 0;
     int32_t stride = std::max(a.nsplit + extra, a.nss);
     while (stride > 1 && partial_bytes(c, stride) > kScratchBytes) --stride;
     const bool fits = partial_bytes(c, stride) <= kScratchBytes;
-    if (q4 && (stride < 2 || !fits)) return DUO_ERR_CAPACITY;
+    if (quant && (stride < 2 || !fits)) return DUO_ERR_CAPACITY;
     if (!fits) stride = 1;  // one split per head: outputs are written directly, no partials
     a.nsplit = std::max(1, std::min(a.nsplit, stride - extra));
     a.nss = std::min(a.nss, stride);
@@ -198,9 +199,9 @@ duo_status decode_impl(duo_cache* c, int32_t layer, const void* q, const void* k
     a.ret_kv[k] = li.ret_kv[k];
     a.str_kv[k] = li.str_kv[k];
   }
-  if (q4) {
-    const Q4Geom g = q4_geom(c->cfg.capacity, c->cfg.head_dim);
-    a.q4 = 1;
+  if (quant) {
+    const Q4Geom g = q4_geom(c->cfg.capacity, c->cfg.head_dim, qbits);
+    a.qbits = qbits;
     a.q4_stride = (int64_t)g.stride;
     a.q4_params = (int64_t)g.codes;
     a.q4_resid = (int64_t)(g.codes + g.params);
@@ -307,10 +308,10 @@ duo_status duo_kv_append(duo_cache* c, int32_t layer, int32_t seq, const void* k
   std::memcpy(a.cls_idx, li.cls_idx, sizeof(a.cls_idx));
   std::memcpy(a.ret_kv, li.ret_kv, sizeof(a.ret_kv));
   for (int32_t i = 0; i < nb; ++i) a.n_old[i] = len_of(c, layer, b0 + i);
-  const bool q4 = c->cfg.kv_bits == 4;
-  if (q4) {
-    const Q4Geom g = q4_geom(c->cfg.capacity, c->cfg.head_dim);
-    a.q4 = 1;
+  const bool quant = c->cfg.kv_bits == 4 || c->cfg.kv_bits == 8;
+  if (quant) {
+    const Q4Geom g = q4_geom(c->cfg.capacity, c->cfg.head_dim, c->cfg.kv_bits);
+    a.qbits = c->cfg.kv_bits;
     a.q4_stride = (int64_t)g.stride;
     a.q4_params = (int64_t)g.codes;
     a.q4_resid = (int64_t)(g.codes + g.params);
@@ -321,7 +322,7 @@ duo_status duo_kv_append(duo_cache* c, int32_t layer, int32_t seq, const void* k
     }
   }
   if (launch_append(a, c->cfg.dtype, stream) != 0) return DUO_ERR_HIP;
-  if (q4 && a.Hr > 0 && launch_append_kv4(a, c->cfg.head_dim, stream) != 0) return DUO_ERR_HIP;
+  if (quant && a.Hr > 0 && launch_append_kv4(a, c->cfg.head_dim, stream) != 0) return DUO_ERR_HIP;
   for (int32_t b = b0; b < b0 + nb; ++b) len_of(c, layer, b) += n_new;
   return DUO_OK;
 }
@@ -339,10 +340,10 @@ duo_status duo_attn_decode_noalloc(duo_cache* c, int32_t layer, const void* q, v
 duo_status duo_decode_step(duo_cache* c, int32_t layer, const void* q, const void* k,
                            const void* v, void* out, float* lse, void* stream) {
   if (!k || !v) return DUO_ERR_INVALID;
-  if (c && c->cfg.kv_bits == 4 && layer_ok(c, layer)) {
-    // 4-bit full caches: a token that completes a group of some sequence needs the group's
-    // quantization, so that step runs as append + decode; otherwise the token only lands in
-    // the bf16 residual and the step is fused like the bf16 one
+  if (c && (c->cfg.kv_bits == 4 || c->cfg.kv_bits == 8) && layer_ok(c, layer)) {
+    // 4- and 8-bit full caches: a token that completes a group of some sequence needs the
+    // group's quantization, so that step runs as append + decode; otherwise the token only
+    // lands in the bf16 residual and the step is fused like the bf16 one
     bool completes = false;
     for (int32_t b = 0; b < c->cfg.batch; ++b)
       completes |= (len_of(c, layer, b) + 1) % kQ4Group == 0;
@@ -362,7 +363,8 @@ namespace {
 // duo_attn_gate_mixed). Returns DUO_OK with `a` filled, or the error to report.
 duo_status prefill_args(duo_cache* c, int32_t layer, int32_t seq, const void* q, const void* k,
                         const void* v, int32_t n_chunk, void* out, float* lse, PrefillArgs& a) {
-  if (c->cfg.kv_bits == 4 && c->layers[layer].n_ret > 0) return DUO_ERR_UNSUPPORTED;
+  if ((c->cfg.kv_bits == 4 || c->cfg.kv_bits == 8) && c->layers[layer].n_ret > 0)
+    return DUO_ERR_UNSUPPORTED;
   if (!q || !k || !v || !out || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
       !aligned16(out) || !aligned4(lse))
     return DUO_ERR_INVALID;

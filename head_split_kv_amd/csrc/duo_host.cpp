@@ -34,7 +34,8 @@ duo_status check_config(const duo_config* cfg) {
   if (!cfg->retrieval_mask) return DUO_ERR_INVALID;
   if (cfg->streaming_prefill != DUO_PREFILL_WINDOW && cfg->streaming_prefill != DUO_PREFILL_CHUNK)
     return DUO_ERR_INVALID;
-  if (cfg->kv_bits != 0 && cfg->kv_bits != 16 && cfg->kv_bits != 4) return DUO_ERR_INVALID;
+  if (cfg->kv_bits != 0 && cfg->kv_bits != 16 && cfg->kv_bits != 4 && cfg->kv_bits != 8)
+    return DUO_ERR_INVALID;
   if (element_size(cfg->dtype) == 0 || element_size(cfg->out_dtype) == 0)
     return DUO_ERR_INVALID;
   if (!(std::isfinite(cfg->softmax_scale))) return DUO_ERR_INVALID;
@@ -44,11 +45,12 @@ duo_status check_config(const duo_config* cfg) {
   const int g = cfg->num_q_heads / cfg->num_kv_heads;
   if (g != 1 && g != 2 && g != 4 && g != 8) return DUO_ERR_UNSUPPORTED;
   if (cfg->out_dtype != DUO_F32 && cfg->out_dtype != cfg->dtype) return DUO_ERR_UNSUPPORTED;
-  if (cfg->kv_bits == 4 && cfg->dtype != DUO_BF16) return DUO_ERR_UNSUPPORTED;
-  // a 4-bit retrieval head decodes into its splits' partials plus one for the residual rows
-  if (cfg->kv_bits == 4 && cfg->max_splits == 1) return DUO_ERR_INVALID;
-  // pre-RoPE keys: the rotation is built into the 4-bit caches' append and decode only
-  if (cfg->rope_theta > 0.f && cfg->kv_bits != 4) return DUO_ERR_UNSUPPORTED;
+  const bool quantized = cfg->kv_bits == 4 || cfg->kv_bits == 8;
+  if (quantized && cfg->dtype != DUO_BF16) return DUO_ERR_UNSUPPORTED;
+  // a quantized retrieval head decodes into its splits' partials plus one for the residual rows
+  if (quantized && cfg->max_splits == 1) return DUO_ERR_INVALID;
+  // pre-RoPE keys: the rotation is built into the quantized caches' decode only
+  if (cfg->rope_theta > 0.f && !quantized) return DUO_ERR_UNSUPPORTED;
   return DUO_OK;
 }
 
@@ -79,8 +81,9 @@ duo_status build_layout(const duo_config* cfg, duo_layout* lay, std::vector<Laye
     }
     info.n_ret = nr;
     info.n_str = ns;
-    const long double per_head = cfg->kv_bits == 4 ? (long double)q4_geom(cap, D).stride
-                                                   : (long double)cap * D * es;
+    const long double per_head = (cfg->kv_bits == 4 || cfg->kv_bits == 8)
+                                     ? (long double)q4_geom(cap, D, cfg->kv_bits).stride
+                                     : (long double)cap * D * es;
     const long double fb = (long double)B * nr * per_head;
     const long double sb = (long double)B * ns * SR * D * es;
     full_total += fb;
@@ -237,11 +240,12 @@ duo_status duo_kv_bytes(const duo_config* cfg, const int32_t* seq_lens, int32_t 
     const uint64_t n = (uint64_t)seq_lens[b];
     full += 2 * (nr + ns) * n * D * es;
     duo_b += 2 * ns * (n < SR ? n : SR) * D * es;
-    if (cfg->kv_bits == 4) {
-      // complete groups: K and V codes (d / 2 bytes each per token), the keys' per-channel
-      // bf16 scale and zero per group, the values' per-token bf16 pair; then the residual
+    if (cfg->kv_bits == 4 || cfg->kv_bits == 8) {
+      // complete groups: K and V codes (d * bits / 8 bytes each per token), the keys'
+      // per-channel bf16 scale and zero per group, the values' per-token bf16 pair; then the
+      // residual
       const uint64_t g = n / kQ4Group, t = g * kQ4Group;
-      duo_b += nr * (t * D + g * 2 * D * 2 + t * 4 + 2 * (n - t) * D * es);
+      duo_b += nr * (t * D * cfg->kv_bits / 4 + g * 2 * D * 2 + t * 4 + 2 * (n - t) * D * es);
     } else {
       duo_b += 2 * nr * n * D * es;
     }

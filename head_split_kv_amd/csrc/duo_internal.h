@@ -20,19 +20,19 @@ constexpr int kPrefillTileRows = 128;  // rows of the workspace unit counted by 
 constexpr uint64_t kAlign = 256;
 constexpr int kMaxTimingRecords = 1 << 16;  // event pairs per kernel timer
 
-// Byte geometry of one retrieval head's K (or V) region in a 4-bit cache: codes, then the
-// parameter block, then the residual group in bf16 (layout in duo.h).
+// Byte geometry of one retrieval head's K (or V) region in a 4-bit or 8-bit cache: codes,
+// then the parameter block, then the residual group in bf16 (layout in duo.h).
 constexpr int kQ4Group = DUO_KV4_GROUP;
 struct Q4Geom {
-  uint64_t codes;   // bytes of codes (128 G rows of D / 2)
+  uint64_t codes;   // bytes of codes (128 G rows of D * bits / 8)
   uint64_t params;  // bytes of the parameter block
   uint64_t resid;   // bytes of the residual group
   uint64_t stride;  // bytes per head
 };
-inline Q4Geom q4_geom(uint64_t cap, uint64_t D) {
+inline Q4Geom q4_geom(uint64_t cap, uint64_t D, uint64_t bits) {
   const uint64_t groups = (cap + kQ4Group - 1) / kQ4Group;
   Q4Geom g;
-  g.codes = groups * kQ4Group * D / 2;
+  g.codes = groups * kQ4Group * D * bits / 8;
   const uint64_t kp = groups * 2 * D * 2, vp = groups * kQ4Group * 4;  // bf16 parameters
   g.params = kp > vp ? kp : vp;
   g.resid = (uint64_t)kQ4Group * D * 2;
@@ -102,7 +102,8 @@ struct AppendArgs {
   int32_t* seq_len;   // this layer: [B]
   int32_t b0, nb, m, Hkv, Hr, Hs, cap, S, R;
   int32_t row_bytes;  // D * element size
-  int32_t q4;         // 4-bit full caches: append_kernel leaves retrieval heads to kv4
+  int32_t qbits;      // 4- or 8-bit full caches (else 0): append_kernel leaves retrieval
+                      // heads to the quantizing append
   int64_t q4_stride, q4_params, q4_resid;  // Q4Geom: head stride, parameter and residual offsets
   int32_t q4_mid;     // complete groups of the widest sequence that need no residual rows
   int16_t cls_idx[kMaxKvHeads];
@@ -127,7 +128,7 @@ struct DecodeArgs {
   int32_t B, Hq, Hkv, Hr, Hs, cap, S, R, nsplit, max_splits;
   float scale_log2;        // softmax scale * log2(e)
   int32_t out_f32;
-  int32_t q4;              // full caches in 4 bits (Q4Geom offsets below)
+  int32_t qbits;           // full caches in 4 or 8 bits (Q4Geom offsets below), else 0
   int64_t q4_stride, q4_params, q4_resid;
   int32_t nss;             // blocks per streaming head (4-bit kernel; 1 otherwise)
   const float* rope_base;      // pre-RoPE keys (4-bit kernel): RopeGeom base and tau16
@@ -216,10 +217,10 @@ int pairs_elapsed_ms(const std::vector<void*>& ev, int pairs, double* total_ms);
 constexpr uint64_t kScratchBytes = 8ull << 20;
 constexpr int kMaxDevices = 64;
 int static_scratch(void** ptr);
-// Decode blocks of this variant (the 4-bit kernel when q4, its pre-RoPE form when rope) that
-// are resident on the device at once, counting at most max_per_cu (1 or 2) per CU (512 if
-// unknown): the size of one round of splits.
-int decode_resident_blocks(int dtype, int head_dim, int group, bool q4, bool rope,
+// Decode blocks of this variant (the quantized kernel of qbits 4 or 8, its pre-RoPE form when
+// rope) that are resident on the device at once, counting at most max_per_cu (1 or 2) per CU
+// (512 if unknown): the size of one round of splits.
+int decode_resident_blocks(int dtype, int head_dim, int group, int qbits, bool rope,
                            int max_per_cu);
 // Prefill blocks of this variant that are resident on the device at once (512 if unknown).
 int prefill_resident_blocks(int head_dim, int group);

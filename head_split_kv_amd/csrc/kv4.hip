@@ -1,11 +1,12 @@
-// Append into 4-bit full caches (explainer, "Combination with Quantization": the retrieval
-// heads' full caches in 4 bits). Keys are quantized per channel over aligned groups of
-// kQ4Group tokens, values per token, both only when their group is complete, the codes
-// stored in the operand layouts of the decode kernel (below). Until a group is complete the
-// group's tokens wait in a bf16 residual block (row t % kQ4Group). Parameters of a block with
-// minimum mn and maximum mx: scale = bf16((mx - mn) / 15) and zero = bf16(mn), stored; the code
-// of x is rint((x - zero) / scale) clamped to 0..15 (0 when scale is 0), in IEEE float32
-// against the stored values, so the decision is reproducible.
+// Append into 4-bit or 8-bit full caches (explainer, "Combination with Quantization": the
+// retrieval heads' full caches in 4 bits; "Category 3: KV Cache Quantization": 4 or 8 bits).
+// Keys are quantized per channel over aligned groups of kQ4Group tokens, values per token,
+// both only when their group is complete, the codes stored in the operand layouts of the
+// decode kernel (below). Until a group is complete the group's tokens wait in a bf16 residual
+// block (row t % kQ4Group). Parameters of a block with minimum mn and maximum mx, L = 15 (4
+// bits) or 255 (8 bits): scale = bf16((mx - mn) / L) and zero = bf16(mn), stored; the code of
+// x is rint((x - zero) / scale) clamped to 0..L (0 when scale is 0), in IEEE float32 against
+// the stored values, so the decision is reproducible.
 //
 // Blocks per (sequence, retrieval head): block 0 is the edge block. It completes the first
 // group if that group already had residual rows (reading them), then, after a barrier,
@@ -32,28 +33,38 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+template <int BITS>
 __device__ __forceinline__ uint32_t code_of(float x, float mn, float scale) {
+  constexpr float kLevels = (float)((1 << BITS) - 1);
   if (scale == 0.f) return 0u;
   const float r = __builtin_rintf((x - mn) / scale);
-  return (uint32_t)fminf(fmaxf(r, 0.f), 15.f);
+  return (uint32_t)fminf(fmaxf(r, 0.f), kLevels);
 }
 
-// Codes are stored in the operand layouts of the decode kernel's matrix products. A code
-// word holds 8 codes, element e in bits 4e .. 4e + 3.
-//   Keys: per token row, D / 8 words; the word in slot KC j + kc (KC = D / 32) holds channels
-//         32 kc + 8 j .. + 7, so the KC words one lane needs for a token are contiguous.
-//   Values: per group, word ((s (D / 64) + h) 64 + l) 4 + w, with l = 16 j + (c % 16) and
-//         c / 16 = 4 h + w, holds channel c; its element e is token 32 s + 16 (e / 4) + 4 j +
-//         e % 4 (the tokens whose logits lane l of the transposed logit tile holds). A wave's
-//         value load for step s reads 1 KB contiguous per h.
+// Codes are stored in the operand layouts of the decode kernel's matrix products. 4 bits: a
+// code word holds 8 codes, element e in bits 4e .. 4e + 3. 8 bits: a word holds 4 codes,
+// element e in byte e.
+//   Keys, 4 bits: per token row, D / 8 words; the word in slot KC j + kc (KC = D / 32) holds
+//         channels 32 kc + 8 j .. + 7, so the KC words one lane needs for a token are
+//         contiguous.
+//   Keys, 8 bits: per token row, D / 4 words; the word in slot 2 KC j + 2 kc + h holds
+//         channels 32 kc + 8 j + 4 h .. + 3 (the 2 KC words of a lane contiguous).
+//   Values, 4 bits: per group, word ((s (D / 64) + h) 64 + l) 4 + w, with l = 16 j + (c % 16)
+//         and c / 16 = 4 h + w, holds channel c; its element e is token 32 s + 16 (e / 4) +
+//         4 j + e % 4 (the tokens whose logits lane l of the transposed logit tile holds). A
+//         wave's value load for step s reads 1 KB contiguous per h.
+//   Values, 8 bits: per group, word ((s (D / 32) + h) 64 + l) 4 + u, with l = 16 j + (c % 16)
+//         and c / 16 = 2 h + u / 2, holds channel c; its element e is token 32 s +
+//         16 (u % 2) + 4 j + e. Again 1 KB contiguous per h and step.
 static_assert(kG == 128, "four 32-token steps per group");
 
 // Quantize the group staged in s (rows 0..kG-1, bf16) as keys: per channel over the rows.
 // codes: the group's first code row; params: bf16 [2][D] (scale row, zero row); sk: the
 // stored values (as float) in LDS for the code pass, which decides against them.
-template <int D>
+template <int D, int BITS>
 __device__ void quantize_keys(const uint16_t (*s)[D], uint8_t* codes, uint16_t* params,
                               float* sk) {
+  constexpr float kLevels = (float)((1 << BITS) - 1);
   const int c = threadIdx.x;
   if (c < D) {
     float mn = bf16_to_f32(s[0][c]), mx = mn;
@@ -62,22 +73,23 @@ __device__ void quantize_keys(const uint16_t (*s)[D], uint8_t* codes, uint16_t* 
       mn = fminf(mn, x);
       mx = fmaxf(mx, x);
     }
-    const uint16_t sb = f32_to_bf16_bits((mx - mn) / 15.f), zb = f32_to_bf16_bits(mn);
+    const uint16_t sb = f32_to_bf16_bits((mx - mn) / kLevels), zb = f32_to_bf16_bits(mn);
     params[c] = sb;
     params[D + c] = zb;
     sk[c] = bf16_to_f32(sb);
     sk[D + c] = bf16_to_f32(zb);
   }
   __syncthreads();
-  constexpr int KC = D / 32, W = D / 8;
+  constexpr int KC = D / 32, CPW = 32 / BITS, W = D / CPW;  // codes per word, words per row
   uint32_t* cw = (uint32_t*)codes;
   for (int w = threadIdx.x; w < kG * W; w += kThreads) {
     const int r = w / W, slot = w % W;
-    const int c0 = 32 * (slot % KC) + 8 * (slot / KC);
+    const int c0 = BITS == 4 ? 32 * (slot % KC) + 8 * (slot / KC)
+                             : 32 * ((slot % (2 * KC)) / 2) + 8 * (slot / (2 * KC)) + 4 * (slot % 2);
     uint32_t word = 0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      word |= code_of(bf16_to_f32(s[r][c0 + e]), sk[D + c0 + e], sk[c0 + e]) << (4 * e);
+    for (int e = 0; e < CPW; ++e)
+      word |= code_of<BITS>(bf16_to_f32(s[r][c0 + e]), sk[D + c0 + e], sk[c0 + e]) << (BITS * e);
     cw[(int64_t)r * W + slot] = word;
   }
 }
@@ -85,9 +97,10 @@ __device__ void quantize_keys(const uint16_t (*s)[D], uint8_t* codes, uint16_t* 
 // Quantize the staged group as values: per token over the channels (one wave per token for
 // the minimum and maximum). params: one word per token of the group, bf16 scale in the low
 // half and bf16 zero in the high half; sp: the stored values (as float) in LDS.
-template <int D>
+template <int D, int BITS>
 __device__ void quantize_values(const uint16_t (*s)[D], uint8_t* codes, uint32_t* params,
                                 float* sp) {
+  constexpr float kLevels = (float)((1 << BITS) - 1);
   constexpr int kPer = D / 64;  // channels per lane: lane, lane + 64
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int r = wave; r < kG; r += kThreads / 64) {
@@ -107,7 +120,7 @@ __device__ void quantize_values(const uint16_t (*s)[D], uint8_t* codes, uint32_t
       mn = fminf(mn, __shfl_xor(mn, off));
       mx = fmaxf(mx, __shfl_xor(mx, off));
     }
-    const uint16_t sb = f32_to_bf16_bits((mx - mn) / 15.f), zb = f32_to_bf16_bits(mn);
+    const uint16_t sb = f32_to_bf16_bits((mx - mn) / kLevels), zb = f32_to_bf16_bits(mn);
     if (lane == 0) {
       params[r] = (uint32_t)sb | ((uint32_t)zb << 16);
       sp[2 * r] = bf16_to_f32(sb);
@@ -115,23 +128,32 @@ __device__ void quantize_values(const uint16_t (*s)[D], uint8_t* codes, uint32_t
     }
   }
   __syncthreads();
-  constexpr int kHalves = D / 64;  // 16-byte loads per lane and step
+  constexpr int kChunks = D * BITS / 256;  // 16-byte loads per lane and step
   uint32_t* cw = (uint32_t*)codes;
-  for (int w = threadIdx.x; w < D * kG / 8; w += kThreads) {
-    const int l = (w >> 2) & 63, x = w >> 8;
-    const int h = x % kHalves, st = x / kHalves, j = l >> 4;
-    const int c = 16 * (4 * h + (w & 3)) + (l & 15), t0 = 32 * st + 4 * j;
+  for (int w = threadIdx.x; w < D * kG * BITS / 32; w += kThreads) {
+    const int u = w & 3, l = (w >> 2) & 63, x = w >> 8;
+    const int h = x % kChunks, st = x / kChunks, j = l >> 4;
     uint32_t word = 0;
+    if constexpr (BITS == 4) {
+      const int c = 16 * (4 * h + u) + (l & 15), t0 = 32 * st + 4 * j;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int t = t0 + 16 * (e >> 2) + (e & 3);
-      word |= code_of(bf16_to_f32(s[t][c]), sp[2 * t + 1], sp[2 * t]) << (4 * e);
+      for (int e = 0; e < 8; ++e) {
+        const int t = t0 + 16 * (e >> 2) + (e & 3);
+        word |= code_of<4>(bf16_to_f32(s[t][c]), sp[2 * t + 1], sp[2 * t]) << (4 * e);
+      }
+    } else {
+      const int c = 16 * (2 * h + (u >> 1)) + (l & 15), t0 = 32 * st + 16 * (u & 1) + 4 * j;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = t0 + e;
+        word |= code_of<8>(bf16_to_f32(s[t][c]), sp[2 * t + 1], sp[2 * t]) << (8 * e);
+      }
     }
     cw[w] = word;
   }
 }
 
-template <int D>
+template <int D, int BITS>
 __global__ void __launch_bounds__(kThreads) kv4_append_kernel(AppendArgs a) {
   __shared__ uint16_t s[kG][D];
   __shared__ float sp[kG > D ? 2 * kG : 2 * D];  // parameters of the group in LDS
@@ -171,11 +193,12 @@ __global__ void __launch_bounds__(kThreads) kv4_append_kernel(AppendArgs a) {
       stage(g, is_v != 0);
       __syncthreads();
       char* base = (char*)(is_v ? a.full_v : a.full_k) + head;
-      uint8_t* codes = (uint8_t*)base + (int64_t)g * kG * (D / 2);
+      uint8_t* codes = (uint8_t*)base + (int64_t)g * kG * (D * BITS / 8);
       if (is_v)
-        quantize_values<D>(s, codes, (uint32_t*)(base + a.q4_params) + (int64_t)g * kG, sp);
+        quantize_values<D, BITS>(s, codes, (uint32_t*)(base + a.q4_params) + (int64_t)g * kG, sp);
       else
-        quantize_keys<D>(s, codes, (uint16_t*)(base + a.q4_params) + (int64_t)g * 2 * D, sp);
+        quantize_keys<D, BITS>(s, codes, (uint16_t*)(base + a.q4_params) + (int64_t)g * 2 * D,
+                               sp);
       __syncthreads();
     }
   };
@@ -208,12 +231,16 @@ __global__ void __launch_bounds__(kThreads) kv4_append_kernel(AppendArgs a) {
 int launch_append_kv4(const AppendArgs& a, int head_dim, void* stream) {
   const int64_t blocks = (int64_t)a.nb * a.Hr * (1 + a.q4_mid);
   if (blocks == 0) return 0;
-  if (head_dim == 128)
-    hipLaunchKernelGGL(kv4_append_kernel<128>, dim3((unsigned)blocks), dim3(kThreads), 0,
-                       (hipStream_t)stream, a);
-  else if (head_dim == 64)
-    hipLaunchKernelGGL(kv4_append_kernel<64>, dim3((unsigned)blocks), dim3(kThreads), 0,
-                       (hipStream_t)stream, a);
+  const dim3 grid((unsigned)blocks), block(kThreads);
+  hipStream_t st = (hipStream_t)stream;
+  if (head_dim == 128 && a.qbits == 4)
+    hipLaunchKernelGGL((kv4_append_kernel<128, 4>), grid, block, 0, st, a);
+  else if (head_dim == 64 && a.qbits == 4)
+    hipLaunchKernelGGL((kv4_append_kernel<64, 4>), grid, block, 0, st, a);
+  else if (head_dim == 128 && a.qbits == 8)
+    hipLaunchKernelGGL((kv4_append_kernel<128, 8>), grid, block, 0, st, a);
+  else if (head_dim == 64 && a.qbits == 8)
+    hipLaunchKernelGGL((kv4_append_kernel<64, 8>), grid, block, 0, st, a);
   else
     return -1;
   return (int)hipGetLastError();

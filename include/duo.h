@@ -83,34 +83,43 @@ typedef struct {
   const uint8_t* retrieval_mask; /* host [num_layers][num_kv_heads], nonzero = retrieval;
                                     copied by duo_cache_create */
   int32_t streaming_prefill; /* duo_prefill_mode of streaming heads in duo_attn_prefill */
-  int32_t kv_bits;         /* 0 or 16: full caches in dtype. 4: full (retrieval) caches in
-                              4 bits, see below (bf16 only); streaming caches keep dtype */
-  float rope_theta;        /* > 0 (kv_bits = 4 only): keys are appended before RoPE with
-                              this base, see below; <= 0: keys are appended as attended */
+  int32_t kv_bits;         /* 0 or 16: full caches in dtype. 4 or 8: full (retrieval) caches
+                              in 4 or 8 bits, see below (bf16 only); streaming caches keep
+                              dtype */
+  float rope_theta;        /* > 0 (kv_bits = 4 or 8 only): keys are appended before RoPE
+                              with this base, see below; <= 0: keys are appended as
+                              attended */
 } duo_config;
 
-/* 4-bit full caches (cfg.kv_bits = 4; explainer, "Combination with Quantization": the full
- * caches pair with 4-bit per-channel KV quantization). Codes c in 0..15 read back as
- * c * scale + zero with scale = bf16((max - min) / 15) and zero = bf16(min) as stored (bf16
- * round to nearest even), the code being rint((x - zero) / scale) in float32 against the
- * stored values, clamped to 0..15 (0 when scale = 0). Keys: per channel over aligned
- * groups of 128 tokens (positions 128 g .. 128 g + 127). Values: per token over the channels.
- * The tokens of the last, incomplete group stay in dtype in a residual block until the group
- * completes. Per retrieval head, with G = ceil(capacity / 128) and P = max(4 d, 512) G:
- *   K region: codes [128 G][d / 8] 32-bit words, then P bytes holding bf16 [G][2][d] (scale
- *             row, zero row), then the residual [128][d] in dtype (row t % 128);
- *   V region: codes [G][d * 128 / 8] words, then P bytes holding one word per token [128 G]
- *             (bf16 scale in the low half, bf16 zero in the high half), then the residual.
- * A code word holds 8 codes, element e in bits 4e .. 4e + 3. Key row t: the word in slot
- * (d / 32) j + k holds channels 32 k + 8 j .. + 7 of token t. Value group g: word
+/* 4-bit and 8-bit full caches (cfg.kv_bits = 4 or 8; explainer, "Combination with
+ * Quantization": the full caches pair with 4-bit per-channel KV quantization; "Category 3: KV
+ * Cache Quantization": 4-bit or 8-bit storage). With L = 15 (4 bits) or 255 (8 bits), codes c
+ * in 0..L read back as c * scale + zero with scale = bf16((max - min) / L) and zero =
+ * bf16(min) as stored (bf16 round to nearest even), the code being rint((x - zero) / scale) in
+ * float32 against the stored values, clamped to 0..L (0 when scale = 0). Keys: per channel
+ * over aligned groups of 128 tokens (positions 128 g .. 128 g + 127). Values: per token over
+ * the channels. The tokens of the last, incomplete group stay in dtype in a residual block
+ * until the group completes. Per retrieval head, with G = ceil(capacity / 128), b the bits
+ * and P = max(4 d, 512) G:
+ *   K region: codes [128 G][d b / 32] 32-bit words, then P bytes holding bf16 [G][2][d]
+ *             (scale row, zero row), then the residual [128][d] in dtype (row t % 128);
+ *   V region: codes [G][d * 128 b / 32] words, then P bytes holding one word per token
+ *             [128 G] (bf16 scale in the low half, bf16 zero in the high half), then the
+ *             residual.
+ * 4 bits: a code word holds 8 codes, element e in bits 4e .. 4e + 3. Key row t: the word in
+ * slot (d / 32) j + k holds channels 32 k + 8 j .. + 7 of token t. Value group g: word
  * ((s (d / 64) + h) 64 + 16 j + c % 16) 4 + w, with c / 16 = 4 h + w, holds channel c; its
  * element e is token 128 g + 32 s + 16 (e / 4) + 4 j + e % 4.
+ * 8 bits: a code word holds 4 codes, element e in byte e. Key row t: the word in slot
+ * 2 (d / 32) j + 2 k + h holds channels 32 k + 8 j + 4 h .. + 3. Value group g: word
+ * ((s (d / 32) + h) 64 + 16 j + c % 16) 4 + u, with c / 16 = 2 h + u / 2, holds channel c;
+ * its element e is token 128 g + 32 s + 16 (u % 2) + 4 j + e.
  * duo_kv_append, duo_attn_decode and duo_decode_step handle them (a step whose token completes
  * a group of some sequence runs as append + decode); duo_attn_prefill and duo_attn_gate_mixed
- * return DUO_ERR_UNSUPPORTED on a 4-bit cache. */
+ * return DUO_ERR_UNSUPPORTED on a 4- or 8-bit cache. */
 #define DUO_KV4_GROUP 128
 
-/* Pre-RoPE keys (cfg.rope_theta > 0 with kv_bits = 4; OpenReview thread, the authors'
+/* Pre-RoPE keys (cfg.rope_theta > 0 with kv_bits = 4 or 8; OpenReview thread, the authors'
  * reply on combining DuoAttention with KV quantization: their 4-bit keys are
  * quantized before the rotary position embedding). The caller passes every key of the layer before RoPE, to
  * duo_kv_append and duo_decode_step alike, and every query after its own rotation; attention
@@ -198,8 +207,8 @@ duo_status duo_attn_decode(duo_cache* cache, int32_t layer, const void* q, void*
  * a static device array of the library (8 MiB per GPU it runs on, kept until the process
  * ends) instead of the cache's workspace; the call itself allocates and frees nothing. The
  * split count is capped so that batch * num_q_heads * parts * (head_dim + 2) * 4 bytes fit in
- * the array (parts = splits, plus one for a 4-bit cache's residual rows); DUO_ERR_CAPACITY when
- * not even the least a 4-bit cache needs (two parts) fits, nothing launched. Every call on one
+ * the array (parts = splits, plus one for a 4- or 8-bit cache's residual rows); DUO_ERR_CAPACITY
+ * when not even the least such a cache needs (two parts) fits, nothing launched. Every call on one
  * GPU shares that GPU's array and nothing in it needs to start at zero, but calls that overlap
  * on one GPU (other streams, other caches) race on it. The first call on each device looks the
  * array's device address up (DUO_ERR_HIP if that fails). */
@@ -252,8 +261,9 @@ duo_status duo_cache_lengths(const duo_cache* cache, int32_t* host_out);
 /* KV bytes one layer holds for sequences of the given lengths (int32 [B]): under full
  * attention (every KV head keeps every token) and under the split layout
  * (H_r * n + H_s * min(n, S + R)) * d * 2 * element size, summed over sequences (explainer,
- * "Decoding Procedure", memory formula). With 4-bit full caches the retrieval term is, per
- * head, the codes of the 128 floor(n / 128) grouped tokens (d bytes per token for K and V),
+ * "Decoding Procedure", memory formula). With 4- or 8-bit full caches the retrieval term is,
+ * per head, the codes of the 128 floor(n / 128) grouped tokens (d bits / 4 bytes per token
+ * for K and V),
  * their parameters (4 d bytes per key group, 4 bytes per value token) and the residual tokens
  * in dtype. The second figure is also the K/V bytes one decode step of that layer reads.
  * Host only. */
@@ -262,7 +272,7 @@ duo_status duo_kv_bytes(const duo_config* cfg, const int32_t* seq_lens, int32_t 
 
 /* Override the number of context splits per retrieval head used by duo_attn_decode
  * (0 = automatic from the lengths; otherwise 1..cfg.max_splits, capped at max_splits - 1 on
- * a 4-bit cache). The result does not depend on it beyond floating-point rounding. Host only. */
+ * a 4- or 8-bit cache). The result does not depend on it beyond floating-point rounding. Host only. */
 duo_status duo_set_decode_splits(duo_cache* cache, int32_t splits);
 
 /* Kernel timers (a measurement aid, off by default). duo_timing_enable(cache, n) creates n

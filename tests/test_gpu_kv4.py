@@ -1,9 +1,9 @@
-"""4-bit full caches (cfg.kv_bits = 4) on the GPU against the CPU oracle.
+"""4-bit and 8-bit full caches (cfg.kv_bits = 4 or 8) on the GPU against the CPU oracle.
 
-Append: the stored codes, float32 scales and zeros, and the bf16 residual rows are compared
+Append: the stored codes, bf16 scales and zeros, and the bf16 residual rows are compared
 bit for bit with the oracle's kv4_codes, through the byte layout documented in duo.h.
-Decode: outputs against decode_step_kv4 (retrieval heads attend over what the 4-bit caches
-read back), |gpu - ref| <= 2e-3 + 1e-2 |ref|.
+Decode: outputs against decode_step_kv4 (retrieval heads attend over what the quantized
+caches read back), |gpu - ref| <= 2e-3 + 1e-2 |ref|.
 """
 import numpy as np
 import pytest
@@ -20,17 +20,17 @@ pytestmark = pytest.mark.gpu
 QG = O.KV4_GROUP
 
 
-def kv4_cache(w, capacity, out_dtype=torch.float32, mask=None, rope_theta=0.0):
+def kv4_cache(w, capacity, out_dtype=torch.float32, mask=None, rope_theta=0.0, bits=4):
     mask = W.retrieval_mask(w) if mask is None else mask
     return hsk.DuoCache(num_layers=mask.shape[0], batch=w.batch, num_q_heads=w.hq,
                         num_kv_heads=w.hkv, head_dim=w.d, sink=w.sink, recent=w.recent,
                         capacity=capacity, retrieval_mask=mask, dtype=torch.bfloat16,
-                        out_dtype=out_dtype, kv_bits=4, rope_theta=rope_theta)
+                        out_dtype=out_dtype, kv_bits=bits, rope_theta=rope_theta)
 
 
-def geom(cap, D):
+def geom(cap, D, bits=4):
     groups = -(-cap // QG)
-    codes = groups * QG * D // 2
+    codes = groups * QG * D * bits // 8
     params = max(groups * 2 * D * 2, groups * QG * 4)
     resid = QG * D * 2
     return codes, params, resid, codes + params + resid
@@ -38,7 +38,7 @@ def geom(cap, D):
 
 def head_region(cache, is_v, b, r):
     """Raw bytes of retrieval head r of sequence b (layer 0) as a numpy uint8 array."""
-    codes, params, resid, stride = geom(cache.capacity, cache.d)
+    codes, params, resid, stride = geom(cache.capacity, cache.d, cache.kv_bits)
     hr = int(cache.retrieval_mask[0].sum())
     off = (cache.layout.full_v_off if is_v else cache.layout.full_k_off) + (b * hr + r) * stride
     return cache.arena[off:off + stride].cpu().numpy(), codes, params
@@ -50,21 +50,43 @@ def nibbles(words):
     return ((w[..., None] >> (4 * np.arange(8, dtype=np.uint32))) & 15).astype(np.uint8)
 
 
-def unpack_keys(code_bytes, rows, D):
-    """Key codes [rows][D]: row words in slot KC j + kc hold channels 32 kc + 8 j .. + 7."""
+def unpack_keys(code_bytes, rows, D, bits=4):
+    """Key codes [rows][D]. 4 bits: row words in slot KC j + kc hold channels 32 kc + 8 j ..
+    + 7. 8 bits: slot 2 KC j + 2 kc + h holds channels 32 kc + 8 j + 4 h .. + 3, one a byte."""
     KC = D // 32
-    w = code_bytes[:rows * D // 2].view(np.uint32).reshape(rows, D // 8)
     out = np.empty((rows, D), dtype=np.uint8)
-    for slot in range(D // 8):
-        c0 = 32 * (slot % KC) + 8 * (slot // KC)
-        out[:, c0:c0 + 8] = nibbles(w[:, slot])
+    if bits == 4:
+        w = code_bytes[:rows * D // 2].view(np.uint32).reshape(rows, D // 8)
+        for slot in range(D // 8):
+            c0 = 32 * (slot % KC) + 8 * (slot // KC)
+            out[:, c0:c0 + 8] = nibbles(w[:, slot])
+        return out
+    b = code_bytes[:rows * D].reshape(rows, D // 4, 4)
+    for slot in range(D // 4):
+        j, kc, h = slot // (2 * KC), (slot % (2 * KC)) // 2, slot % 2
+        c0 = 32 * kc + 8 * j + 4 * h
+        out[:, c0:c0 + 4] = b[:, slot]
     return out
 
 
-def unpack_values(code_bytes, groups, D):
-    """Value codes [groups * QG][D]: word ((s (D / 64) + h) 64 + 16 j + c % 16) 4 + w of a group,
-    with c / 16 = 4 h + w, holds channel c; its element e is token 32 s + 16 (e / 4) + 4 j +
-    e % 4."""
+def unpack_values(code_bytes, groups, D, bits=4):
+    """Value codes [groups * QG][D]. 4 bits: word ((s (D / 64) + h) 64 + 16 j + c % 16) 4 + w
+    of a group, with c / 16 = 4 h + w, holds channel c; its element e is token 32 s +
+    16 (e / 4) + 4 j + e % 4. 8 bits: word ((s (D / 32) + h) 64 + 16 j + c % 16) 4 + u, with
+    c / 16 = 2 h + u / 2, holds channel c; its byte e is token 32 s + 16 (u % 2) + 4 j + e."""
+    if bits == 8:
+        chunks = D // 32
+        b = code_bytes[:groups * QG * D].reshape(groups, 4, chunks, 4, 16, 4, 4)
+        out = np.empty((groups, QG, D), dtype=np.uint8)
+        for s_ in range(4):
+            for h in range(chunks):
+                for j in range(4):
+                    for cl in range(16):
+                        for u in range(4):
+                            c = 16 * (2 * h + u // 2) + cl
+                            t0 = 32 * s_ + 16 * (u % 2) + 4 * j
+                            out[:, t0:t0 + 4, c] = b[:, s_, h, j, cl, u]
+        return out.reshape(groups * QG, D)
     halves = D // 64
     w = code_bytes[:groups * QG * D // 2].view(np.uint32).reshape(groups, 4, halves, 4, 16, 4)
     out = np.empty((groups, QG, D), dtype=np.uint8)
@@ -82,7 +104,7 @@ def unpack_values(code_bytes, groups, D):
 def check_stored(cache, w, lens):
     """Every retrieval head of every sequence: complete groups' codes and parameters equal
     the oracle's, residual rows equal the input bits."""
-    D = w.d
+    D, bits = w.d, cache.kv_bits
     ret = np.nonzero(cache.retrieval_mask[0])[0]
     for b, n in enumerate(lens):
         ng = n // QG
@@ -90,11 +112,12 @@ def check_stored(cache, w, lens):
             for is_v in (False, True):
                 x = W.tokens(w, "v" if is_v else "k", 0, b, 0, n)[:, j].astype(np.float32)
                 raw, codes_b, params_b = head_region(cache, is_v, b, r)
-                codes = unpack_values(raw, ng, D) if is_v else unpack_keys(raw, ng * QG, D)
+                codes = (unpack_values(raw, ng, D, bits) if is_v
+                         else unpack_keys(raw, ng * QG, D, bits))
                 par = raw[codes_b:codes_b + params_b]
                 for g in range(ng):
                     blk = x[g * QG:(g + 1) * QG]
-                    c, s, z = O.kv4_codes(blk, axis=1 if is_v else 0)
+                    c, s, z = O.kv4_codes(blk, axis=1 if is_v else 0, bits=bits)
                     assert np.array_equal(codes[g * QG:(g + 1) * QG], c), (b, j, is_v, g)
                     hi16 = lambda f: (f.view(np.uint32) >> 16).astype(np.uint16)  # noqa: E731
                     if is_v:  # one word per token: bf16 scale low, bf16 zero high
@@ -151,8 +174,9 @@ def test_kv4_append_batch_calls(d):
 
 
 def run_decode_kv4(w, lens0, steps, check_steps=None, splits=None, out_dtype=torch.float32,
-                   fused=False, heads=None, rope_theta=None):
-    cache = kv4_cache(w, max(lens0) + steps, out_dtype=out_dtype, rope_theta=rope_theta or 0.0)
+                   fused=False, heads=None, rope_theta=None, bits=4):
+    cache = kv4_cache(w, max(lens0) + steps, out_dtype=out_dtype, rope_theta=rope_theta or 0.0,
+                      bits=bits)
     for b, n in enumerate(lens0):
         for t0 in range(0, n, 1 << 16):
             append_tokens(cache, w, b, t0, min(n, t0 + (1 << 16)))
@@ -177,7 +201,7 @@ def run_decode_kv4(w, lens0, steps, check_steps=None, splits=None, out_dtype=tor
             kh, vh = W.tokens(w, "k", 0, b, 0, n), W.tokens(w, "v", 0, b, 0, n)
             if heads is None:
                 ref, ref_lse = O.decode_step_kv4(qh[b], kh, vh, mask, w.sink, w.recent,
-                                                 rope_theta=rope_theta)
+                                                 rope_theta=rope_theta, bits=bits)
                 assert_close(got[b], ref, f"step {s} seq {b} n {n} out")
                 assert_close(got_lse[b], ref_lse, f"step {s} seq {b} n {n} lse")
             else:
@@ -186,7 +210,7 @@ def run_decode_kv4(w, lens0, steps, check_steps=None, splits=None, out_dtype=tor
                     hq = slice(j * G, (j + 1) * G)
                     ref, ref_lse = O.decode_step_kv4(qh[b][hq], kh[:, j:j + 1], vh[:, j:j + 1],
                                                      mask[j:j + 1], w.sink, w.recent,
-                                                     rope_theta=rope_theta)
+                                                     rope_theta=rope_theta, bits=bits)
                     assert_close(got[b][hq], ref, f"step {s} seq {b} kv {j}")
                     assert_close(got_lse[b][hq], ref_lse, f"step {s} seq {b} kv {j} lse")
     return cache
@@ -405,3 +429,67 @@ def test_kv4_rope_gqa_128k():
     500,000, as that model's): steps across the group boundary at 131,072 tokens."""
     w = W.workload("c3")
     run_decode_kv4(w, [w.context - 2], 4, rope_theta=500000.0)
+
+
+# ---- 8-bit caches (cfg.kv_bits = 8) --------------------------------------------------------
+
+def test_kv8_append_patterns_bit_exact():
+    """The 8-bit layouts bit for bit: bulk appends, single tokens across a group boundary,
+    chunks that complete a group holding residual rows, ragged sequences, both head dims."""
+    for d in (128, 64):
+        w = W.Workload("kv8-append", 1, 3, 8, 4, d, "bf16", 4, 32, 0, 0, 2,
+                       fixed_mask=((0, 2),), seed=301)
+        cache = kv4_cache(w, 1200, bits=8)
+        dt = torch_dtype(w.dtype)
+        lens = [0, 0, 0]
+        for b, chunks in enumerate(((300,), (127, 1, 1, 200), (1, 128, 500))):
+            for m in chunks:
+                k = to_dev(W.tokens(w, "k", 0, b, lens[b], lens[b] + m), dt)
+                v = to_dev(W.tokens(w, "v", 0, b, lens[b], lens[b] + m), dt)
+                cache.kv_append(0, k, v, seq=b)
+                lens[b] += m
+        torch.cuda.synchronize()
+        check_stored(cache, w, lens)
+        cache.close()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_kv8_decode_variants(d, G):
+    """Every (head_dim, group) variant of the 8-bit kernel, steps across a group boundary."""
+    w = W.Workload("kv8-variant", 1, 2, 2 * G, 2, d, "bf16", 4, 32, 0, 0, 1,
+                   fixed_mask=((0,),), seed=305 + G)
+    run_decode_kv4(w, [3 * QG - 2, 2 * QG + 40], 4, bits=8)
+
+
+@pytest.mark.parametrize("splits", [1, 3, 16])
+def test_kv8_decode_split_counts_and_streaming(splits):
+    w = W.Workload("kv8-splits", 1, 1, 32, 8, 128, "bf16", 16, 64, 0, 0, 4, seed=309)
+    run_decode_kv4(w, [9 * QG + 50], 2, splits=splits, bits=8)
+    w2 = W.Workload("kv8-slices", 1, 1, 16, 4, 64, "bf16", 4, 500, 0, 0, 2,
+                    fixed_mask=((1, 2),), seed=311)
+    run_decode_kv4(w2, [1000], 3, fused=splits == 3, bits=8)
+
+
+def test_kv8_ragged_bf16_out_and_step_from_empty():
+    w = W.Workload("kv8-ragged", 1, 3, 32, 8, 128, "bf16", 16, 64, 0, 0, 4, seed=313)
+    run_decode_kv4(w, [700, 129, 1500], 2, out_dtype=torch.bfloat16, bits=8)
+    w2 = W.Workload("kv8-step", 1, 1, 8, 2, 64, "bf16", 4, 16, 0, 0, 1,
+                    fixed_mask=((1,),), seed=315)
+    run_decode_kv4(w2, [0], QG + 5, fused=True, bits=8,
+                   check_steps=set(range(0, QG + 5, 9)) | {QG - 1, QG})
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_kv8_rope(d):
+    """8-bit caches with pre-RoPE keys: quantized groups, residual rows and streaming heads."""
+    w = W.Workload("kv8-rope", 1, 2, 8, 2, d, "bf16", 4, 32, 0, 0, 1,
+                   fixed_mask=((0,),), seed=317)
+    run_decode_kv4(w, [3 * QG - 2, 2 * QG + 40], 3, bits=8, rope_theta=THETA)
+
+
+@pytest.mark.timeout(900)
+def test_kv8_decode_gqa_128k():
+    """The Llama-3-8B-shaped GQA layer at a 128K context in 8 bits."""
+    w = W.workload("c3")
+    run_decode_kv4(w, [w.context - 2], 3, bits=8)

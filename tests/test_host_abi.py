@@ -76,13 +76,14 @@ def test_config_checks(bad, status):
 def test_kv_bits_checked_and_kv4_layout():
     import torch
     lay = N.DuoLayout()
-    for bits, status in ((0, N.DUO_OK), (16, N.DUO_OK), (4, N.DUO_OK), (8, N.DUO_ERR_INVALID),
-                         (-4, N.DUO_ERR_INVALID)):
+    for bits, status in ((0, N.DUO_OK), (16, N.DUO_OK), (4, N.DUO_OK), (8, N.DUO_OK),
+                         (2, N.DUO_ERR_INVALID), (-4, N.DUO_ERR_INVALID)):
         cfg, _keep = cfg_of()
         cfg.kv_bits = bits
         assert N.lib().duo_layout_query(ctypes.byref(cfg), ctypes.byref(lay)) == status, bits
-    cfg, _keep = cfg_of(dtype=torch.float32, kv_bits=4)
-    assert N.lib().duo_layout_query(ctypes.byref(cfg), ctypes.byref(lay)) == N.DUO_ERR_UNSUPPORTED
+    for bits in (4, 8):
+        cfg, _keep = cfg_of(dtype=torch.float32, kv_bits=bits)
+        assert N.lib().duo_layout_query(ctypes.byref(cfg), ctypes.byref(lay)) == N.DUO_ERR_UNSUPPORTED
     # a 4-bit retrieval head needs a partial for its residual rows besides its context splits
     for ms, status in ((1, N.DUO_ERR_INVALID), (2, N.DUO_OK), (0, N.DUO_OK)):
         cfg, _keep = cfg_of(kv_bits=4, max_splits=ms)
@@ -100,6 +101,13 @@ def test_kv_bits_checked_and_kv4_layout():
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     assert l4.full_v_off - l4.full_k_off == al(sum(al(x) for x in per_layer))
     assert l4.arena_bytes < l16.arena_bytes
+    # 8 bits: twice the code bytes, the same parameter block and residual
+    cfg8, _k8 = cfg_of(kv_bits=8)
+    l8 = N.DuoLayout()
+    assert N.lib().duo_layout_query(ctypes.byref(cfg8), ctypes.byref(l8)) == N.DUO_OK
+    stride8 = groups * G * D + max(groups * 2 * D * 2, groups * G * 4) + G * D * 2
+    assert l8.full_v_off - l8.full_k_off == al(2 * al(3 * stride8))
+    assert l4.arena_bytes < l8.arena_bytes < l16.arena_bytes
 
 
 def test_rope_theta_checked_and_rope_layout():
@@ -108,6 +116,7 @@ def test_rope_theta_checked_and_rope_layout():
     float pairs per channel pair, each 256-byte aligned."""
     lay = N.DuoLayout()
     for bits, theta, status in ((4, 10000.0, N.DUO_OK), (4, 0.0, N.DUO_OK), (4, -1.0, N.DUO_OK),
+                                (8, 10000.0, N.DUO_OK),
                                 (0, 10000.0, N.DUO_ERR_UNSUPPORTED),
                                 (16, 500000.0, N.DUO_ERR_UNSUPPORTED),
                                 (4, float("nan"), N.DUO_ERR_INVALID),
@@ -130,11 +139,12 @@ def test_rope_theta_checked_and_rope_layout():
         assert lr.arena_bytes == lp.arena_bytes + al(want)
 
 
-def test_kv4_bytes_model():
-    """Per retrieval head: d bytes of K and V codes per grouped token, 4 d bytes of key
-    parameters per group, 4 bytes of value parameters per grouped token, residual tokens at
-    4 d bytes (bf16 K and V); streaming heads unchanged."""
-    cfg, _keep = cfg_of(kv_bits=4)
+@pytest.mark.parametrize("bits", [4, 8])
+def test_kv4_bytes_model(bits):
+    """Per retrieval head: d bits / 4 bytes of K and V codes per grouped token, 4 d bytes of
+    key parameters per group, 4 bytes of value parameters per grouped token, residual tokens
+    at 4 d bytes (bf16 K and V); streaming heads unchanged."""
+    cfg, _keep = cfg_of(kv_bits=bits)
     full, duo = ctypes.c_uint64(), ctypes.c_uint64()
     D, G, S, R = 128, N.KV4_GROUP, 4, 16
     for lens in ([0, 1, 127], [128, 129, 999], [256, 500, 1000]):
@@ -144,8 +154,8 @@ def test_kv4_bytes_model():
         want = 0
         for n in lens:
             g, t = n // G, (n // G) * G
-            want += t * D + g * 4 * D + t * 4 + (n - t) * 4 * D  # one retrieval head
-            want += 2 * min(n, S + R) * D * 2                    # one streaming head
+            want += t * D * bits // 4 + g * 4 * D + t * 4 + (n - t) * 4 * D  # a retrieval head
+            want += 2 * min(n, S + R) * D * 2                               # a streaming head
         assert duo.value == want, lens
         assert full.value == sum(2 * 2 * n * D * 2 for n in lens)
 
