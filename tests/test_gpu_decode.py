@@ -226,6 +226,44 @@ def test_decode_c5_1m_context(key, history_1m):
         _progress(f"{key}: step {s} checked")
 
 
+@pytest.mark.timeout(900)
+def test_decode_c5_1m_context_kv4(history_1m):
+    """The 1,048,576-token layer at 50 % retrieval with 4-bit full caches: 2 steps, checked on
+    two retrieval KV heads and one streaming head against decode_step_kv4."""
+    import head_split_kv_amd as hsk
+    w = W.workload("c5")
+    kh, vh, qh = history_1m
+    mask = W.retrieval_mask(w)[0]
+    ret = [int(j) for j in np.nonzero(mask)[0]]
+    heads = [ret[0], ret[-1], int(np.nonzero(mask == 0)[0][0])]
+    n0 = w.context
+    cache = hsk.DuoCache(num_layers=1, batch=1, num_q_heads=w.hq, num_kv_heads=w.hkv,
+                         head_dim=w.d, sink=w.sink, recent=w.recent, capacity=n0 + 2,
+                         retrieval_mask=[mask], dtype=torch.bfloat16, out_dtype=torch.float32,
+                         kv_bits=4)
+    dt = torch.bfloat16
+    for t0 in range(0, n0, 1 << 17):
+        t1 = min(n0, t0 + (1 << 17))
+        cache.kv_append(0, to_dev(kh[t0:t1], dt), to_dev(vh[t0:t1], dt), seq=0)
+    _progress("c5 4-bit: filled")
+    G = w.group
+    for s in range(2):
+        p = n0 + s
+        cache.kv_append(0, to_dev(kh[p:p + 1][None], dt), to_dev(vh[p:p + 1][None], dt))
+        lse = torch.empty((1, w.hq), dtype=torch.float32, device="cuda")
+        out = cache.attn_decode(0, to_dev(qh[s:s + 1], dt), lse=lse)
+        got = out.float().cpu().numpy()[0]
+        got_lse = lse.cpu().numpy()[0]
+        for j in heads:
+            hq = slice(j * G, (j + 1) * G)
+            ref, ref_lse = O.decode_step_kv4(qh[s][hq], kh[:p + 1, j:j + 1], vh[:p + 1, j:j + 1],
+                                             mask[j:j + 1], w.sink, w.recent)
+            assert_close(got[hq], ref, f"c5 4-bit step {s} kv {j}")
+            assert_close(got_lse[hq], ref_lse, f"c5 4-bit step {s} kv {j} lse")
+        _progress(f"c5 4-bit: step {s} checked")
+    cache.close()
+
+
 def test_decode_split_merge_reads_only_its_own_call():
     """Back-to-back calls that share the cache's split-K workspace, at automatic, 48 and 3
     splits: every call's outputs match the oracle, so no merge reads a partial left by the
