@@ -446,6 +446,24 @@ def decode_step_kv4(q, k_hist, v_hist, retrieval, sink, recent, scale=None, rope
     return decode_step(q, k, v, retrieval, sink, recent, scale)
 
 
+def prefill_chunk_kv4(q, k_hist, v_hist, start, retrieval, sink, recent, scale=None,
+                      chunk_granular=False, bits: int = 4):
+    """``prefill_chunk`` over a cache whose retrieval heads are stored in ``bits`` bits (4 or
+    8). Reading (the pages pair quantized caches with serving the whole context, explainer,
+    "Combination with Quantization"): the chunk's queries see the cache as it stands before
+    the chunk, so a retrieval head's earlier tokens 0..start-1 read back as
+    ``kv4_history(.., start)`` (complete groups dequantized, the last incomplete group exact),
+    while the chunk's own keys and values are exact (they are not in the cache yet; the caller
+    appends them afterwards). Streaming heads are exact, as in decoding."""
+    k = np.asarray(k_hist, dtype=np.float64).copy()
+    v = np.asarray(v_hist, dtype=np.float64).copy()
+    for j in range(k.shape[1]):
+        if retrieval[j] and start > 0:
+            k[:start, j] = kv4_history(k_hist[:, j], start, True, bits)
+            v[:start, j] = kv4_history(v_hist[:, j], start, False, bits)
+    return prefill_chunk(q, k, v, start, retrieval, sink, recent, scale, chunk_granular)
+
+
 # --------------------------------------------------------------------------------------------
 # Pre-RoPE keys in 4-bit caches
 # --------------------------------------------------------------------------------------------

@@ -631,6 +631,43 @@ def pin_kv4_decode():
         assert np.allclose(a, b, rtol=0, atol=1e-12)
 
 
+def pin_kv4_prefill():
+    """Prefill over a quantized cache: with no earlier tokens it is plain prefill; its queries
+    see the earlier tokens as the quantized cache reads them back and the chunk exactly, so a
+    chunk that starts on a group boundary and completes no group ends on exactly the decode
+    step of its last token (whose cache holds the same groups); quantization touches retrieval
+    heads only; and on general data the earlier groups change the result."""
+    rng = np.random.default_rng(55)
+    G = O.KV4_GROUP
+    Hkv, Gq, d, S, R = 2, 2, 16, 2, 8
+    for bits in (4, 8):
+        m = 40
+        k = _bf16_grid(rng, 2 * G + m, Hkv, d)
+        v = _bf16_grid(rng, 2 * G + m, Hkv, d)
+        q = _bf16_grid(rng, m, Hkv * Gq, d)
+        a, la = O.prefill_chunk(q, k, v, 0, [1, 0], S, R)
+        b, lb = O.prefill_chunk_kv4(q, k, v, 0, [1, 0], S, R, bits=bits)
+        assert np.array_equal(a, b) and np.array_equal(la, lb)
+        start = 2 * G
+        c, lc = O.prefill_chunk_kv4(q, k, v, start, [1, 0], S, R, bits=bits)
+        e, le = O.decode_step_kv4(q[-1], k, v, [1, 0], S, R, bits=bits)
+        assert np.allclose(c[-1], e, rtol=0, atol=1e-12) and np.allclose(lc[-1], le, atol=1e-12)
+        f, lf = O.prefill_chunk(q, k, v, start, [1, 0], S, R)
+        assert np.array_equal(c[:, Gq:], f[:, Gq:])       # the streaming head: exact
+        assert np.abs(c[:, :Gq] - f[:, :Gq]).max() > 0     # the retrieval head: quantized
+        # the first query sees the quantized groups and itself only: brute force
+        kq = np.concatenate([O.kv4_history(k[:, 0], start, True, bits), k[start:start + 1, 0]])
+        vq = np.concatenate([O.kv4_history(v[:, 0], start, False, bits), v[start:start + 1, 0]])
+        z = kq @ q[0, 0].astype(np.float64) / math.sqrt(d)
+        p_ = np.exp(z - z.max())
+        assert np.allclose(c[0, 0], p_ @ vq / p_.sum(), rtol=0, atol=1e-12)
+        # a chunk at 100 that completes group 0: the cache before it holds no complete group,
+        # so nothing is quantized (the chunk's tokens are exact even where they complete it)
+        g, lg = O.prefill_chunk_kv4(q, k, v, 100, [1, 0], S, R, bits=bits)
+        h, lh = O.prefill_chunk(q, k, v, 100, [1, 0], S, R)
+        assert np.array_equal(g, h) and np.array_equal(lg, lh)
+
+
 def pin_rope_complex_form():
     """RoPE equals multiplying the complex channels z_i = x_i + i x_{i+d/2} by
     exp(i t theta^(-2i/d)), written here with complex arithmetic and the exponent as
@@ -698,6 +735,7 @@ PINS = [pin_cache_policy, pin_streaming_rows, pin_decode_scalar_bruteforce,
         pin_retrieval_count_nearest, pin_binarize_bruteforce, pin_binarize_equation4,
         pin_head_reordering_preserves_layer, pin_gate_mixed_bruteforce, pin_kv4_nearest_level,
         pin_kv4_axes_and_exact_grids, pin_kv4_groups_and_residual, pin_kv4_decode,
+        pin_kv4_prefill,
         pin_rope_complex_form, pin_rope_relative_positions, pin_kv4_rope_decode]
 
 
@@ -869,6 +907,18 @@ def _kv4_rope_before_quant(q, k_hist, v_hist, retrieval, sink, recent, scale=Non
     return _ORIG_KV4(q, k, v_hist, retrieval, sink, recent, scale, bits=bits)
 
 
+def _kv4_prefill_quantizes_chunk(q, k_hist, v_hist, start, retrieval, sink, recent, scale=None,
+                                 chunk_granular=False, bits=4):
+    m = np.asarray(q).shape[0]
+    k = np.asarray(k_hist, dtype=np.float64).copy()
+    v = np.asarray(v_hist, dtype=np.float64).copy()
+    for j in range(k.shape[1]):
+        if retrieval[j]:
+            k[:start + m, j] = O.kv4_history(k_hist[:, j], start + m, True, bits)
+            v[:start + m, j] = O.kv4_history(v_hist[:, j], start + m, False, bits)
+    return O.prefill_chunk(q, k, v, start, retrieval, sink, recent, scale, chunk_granular)
+
+
 _ORIG_KV4 = O.decode_step_kv4
 _ORIG_MSA = O.masked_softmax_attention
 _ORIG_BIN = O.binarize_gates
@@ -916,6 +966,7 @@ MUTANTS = {
     "rope_exponent_halved": ("rope", _rope_variant(exponent=1.0)),
     "rope_position_plus_one": ("rope", _rope_variant(offset=1)),
     "kv4_rope_before_quantization": ("decode_step_kv4", _kv4_rope_before_quant),
+    "kv4_prefill_quantizes_the_chunk": ("prefill_chunk_kv4", _kv4_prefill_quantizes_chunk),
     "query_order_interleaved": ("query_head_order",
                                 lambda o, G: np.array([g * len(o) + j for j in o for g in range(G)])),
 }
