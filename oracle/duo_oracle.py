@@ -446,21 +446,42 @@ def decode_step_kv4(q, k_hist, v_hist, retrieval, sink, recent, scale=None, rope
     return decode_step(q, k, v, retrieval, sink, recent, scale)
 
 
+def kv4_history_bf16(x_hist, n: int, is_key: bool, bits: int = 4) -> np.ndarray:
+    """``kv4_history`` read back in the cache dtype: every dequantized value is
+    ``to_bf16(float32(c * scale + zero))`` (c * scale is exact in float32: at most 8 + 8
+    significant bits; one float32 rounding for the sum, then round to nearest even), the
+    residual tokens exact as before."""
+    x = np.asarray(x_hist, dtype=np.float32)[:n]
+    out = x.astype(np.float64).copy()
+    full = (n // KV4_GROUP) * KV4_GROUP
+    for g0 in range(0, full, KV4_GROUP):
+        blk = x[g0:g0 + KV4_GROUP]
+        codes, scale, zero = kv4_codes(blk, axis=0 if is_key else 1, bits=bits)
+        c = codes.astype(np.float32)
+        if is_key:
+            y = c * scale[None, :] + zero[None, :]
+        else:
+            y = c * scale[:, None] + zero[:, None]
+        out[g0:g0 + KV4_GROUP] = to_bf16(y.astype(np.float32)).astype(np.float64)
+    return out
+
+
 def prefill_chunk_kv4(q, k_hist, v_hist, start, retrieval, sink, recent, scale=None,
                       chunk_granular=False, bits: int = 4):
     """``prefill_chunk`` over a cache whose retrieval heads are stored in ``bits`` bits (4 or
     8). Reading (the pages pair quantized caches with serving the whole context, explainer,
     "Combination with Quantization"): the chunk's queries see the cache as it stands before
     the chunk, so a retrieval head's earlier tokens 0..start-1 read back as
-    ``kv4_history(.., start)`` (complete groups dequantized, the last incomplete group exact),
-    while the chunk's own keys and values are exact (they are not in the cache yet; the caller
-    appends them afterwards). Streaming heads are exact, as in decoding."""
+    ``kv4_history_bf16(.., start)``: complete groups dequantized into the cache dtype, as a
+    dequantize-then-attend kernel computes them, the last incomplete group exact. The chunk's
+    own keys and values are exact (they are not in the cache yet; the caller appends them
+    afterwards). Streaming heads are exact, as in decoding."""
     k = np.asarray(k_hist, dtype=np.float64).copy()
     v = np.asarray(v_hist, dtype=np.float64).copy()
     for j in range(k.shape[1]):
         if retrieval[j] and start > 0:
-            k[:start, j] = kv4_history(k_hist[:, j], start, True, bits)
-            v[:start, j] = kv4_history(v_hist[:, j], start, False, bits)
+            k[:start, j] = kv4_history_bf16(k_hist[:, j], start, True, bits)
+            v[:start, j] = kv4_history_bf16(v_hist[:, j], start, False, bits)
     return prefill_chunk(q, k, v, start, retrieval, sink, recent, scale, chunk_granular)
 
 

@@ -632,11 +632,12 @@ def pin_kv4_decode():
 
 
 def pin_kv4_prefill():
-    """Prefill over a quantized cache: with no earlier tokens it is plain prefill; its queries
-    see the earlier tokens as the quantized cache reads them back and the chunk exactly, so a
-    chunk that starts on a group boundary and completes no group ends on exactly the decode
-    step of its last token (whose cache holds the same groups); quantization touches retrieval
-    heads only; and on general data the earlier groups change the result."""
+    """Prefill over a quantized cache: with no earlier tokens it is plain prefill; the bf16
+    read-back of the groups is the bf16 rounding of the exact dequantized values (within half
+    a bf16 step) and exact on the dyadic grids; a chunk that starts on a group boundary and
+    completes no group ends near the decode step of its last token (whose cache holds the same
+    groups, read back exactly); quantization touches retrieval heads only; a brute-force first
+    row; nothing is quantized when no group is complete before the chunk."""
     rng = np.random.default_rng(55)
     G = O.KV4_GROUP
     Hkv, Gq, d, S, R = 2, 2, 16, 2, 8
@@ -649,15 +650,30 @@ def pin_kv4_prefill():
         b, lb = O.prefill_chunk_kv4(q, k, v, 0, [1, 0], S, R, bits=bits)
         assert np.array_equal(a, b) and np.array_equal(la, lb)
         start = 2 * G
+        for is_key in (True, False):
+            xx = (k if is_key else v)[:, 1]
+            ex = O.kv4_history(xx, start, is_key, bits)
+            hb = O.kv4_history_bf16(xx, start, is_key, bits)
+            assert np.all(np.abs(hb - ex) <= 2.0 ** -8 * np.abs(ex) * (1 + 2.0 ** -20) + 1e-30)
+            assert not np.any(hb.astype(np.float32).view(np.uint32) & 0xFFFF)
+        kg = np.tile((np.float32(-1.5) + rng.integers(0, 16, (1, 1, d)) * 2.0 ** -4)
+                     .astype(np.float32), (start, 1, 1))
+        assert np.array_equal(O.kv4_history_bf16(kg[:, 0], start, True, bits),
+                              kg[:, 0].astype(np.float64))
         c, lc = O.prefill_chunk_kv4(q, k, v, start, [1, 0], S, R, bits=bits)
         e, le = O.decode_step_kv4(q[-1], k, v, [1, 0], S, R, bits=bits)
-        assert np.allclose(c[-1], e, rtol=0, atol=1e-12) and np.allclose(lc[-1], le, atol=1e-12)
+        assert np.allclose(c[-1], e, rtol=0, atol=2e-2) and np.allclose(lc[-1], le, atol=2e-2)
         f, lf = O.prefill_chunk(q, k, v, start, [1, 0], S, R)
         assert np.array_equal(c[:, Gq:], f[:, Gq:])       # the streaming head: exact
         assert np.abs(c[:, :Gq] - f[:, :Gq]).max() > 0     # the retrieval head: quantized
         # the first query sees the quantized groups and itself only: brute force
-        kq = np.concatenate([O.kv4_history(k[:, 0], start, True, bits), k[start:start + 1, 0]])
-        vq = np.concatenate([O.kv4_history(v[:, 0], start, False, bits), v[start:start + 1, 0]])
+        cs = [O.kv4_codes(k[g0:g0 + G, 0], 0, bits) for g0 in (0, G)]
+        kd = np.concatenate([O.to_bf16(c_.astype(np.float32) * s_ + z_) for c_, s_, z_ in cs])
+        cs = [O.kv4_codes(v[g0:g0 + G, 0], 1, bits) for g0 in (0, G)]
+        vd = np.concatenate([O.to_bf16(c_.astype(np.float32) * s_[:, None] + z_[:, None])
+                             for c_, s_, z_ in cs])
+        kq = np.concatenate([kd.astype(np.float64), k[start:start + 1, 0]])
+        vq = np.concatenate([vd.astype(np.float64), v[start:start + 1, 0]])
         z = kq @ q[0, 0].astype(np.float64) / math.sqrt(d)
         p_ = np.exp(z - z.max())
         assert np.allclose(c[0, 0], p_ @ vq / p_.sum(), rtol=0, atol=1e-12)
@@ -914,8 +930,8 @@ def _kv4_prefill_quantizes_chunk(q, k_hist, v_hist, start, retrieval, sink, rece
     v = np.asarray(v_hist, dtype=np.float64).copy()
     for j in range(k.shape[1]):
         if retrieval[j]:
-            k[:start + m, j] = O.kv4_history(k_hist[:, j], start + m, True, bits)
-            v[:start + m, j] = O.kv4_history(v_hist[:, j], start + m, False, bits)
+            k[:start + m, j] = O.kv4_history_bf16(k_hist[:, j], start + m, True, bits)
+            v[:start + m, j] = O.kv4_history_bf16(v_hist[:, j], start + m, False, bits)
     return O.prefill_chunk(q, k, v, start, retrieval, sink, recent, scale, chunk_granular)
 
 
