@@ -141,6 +141,11 @@ class DuoCache:
     def attn_prefill(self, layer, q, k, v, seq=-1, out=None, lse=None, stream=None):
         return duo_attn_prefill(self, layer, seq, q, k, v, out, lse, stream=stream)
 
+    def attn_prefill_staged(self, layer, q, k, v, seq=-1, out=None, lse=None, staging=None,
+                            stream=None):
+        return duo_attn_prefill_staged(self, layer, seq, q, k, v, out, lse, staging,
+                                       stream=stream)
+
     def attn_gate_mixed(self, layer, q, k, v, alpha, seq=-1, out=None, stream=None):
         return duo_attn_gate_mixed(self, layer, seq, q, k, v, alpha, out, stream=stream)
 
@@ -271,6 +276,45 @@ def duo_attn_prefill(cache: DuoCache, layer: int, seq: int, q: torch.Tensor, k: 
                                  ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
                                  m, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(lse_ptr),
                                  _stream(stream)), "duo_attn_prefill")
+    return out
+
+
+def duo_prefill_staging_bytes(cache: DuoCache, layer: int, seq: int = -1) -> int:
+    """Bytes of bf16 staging ``duo_attn_prefill_staged`` needs at the current lengths."""
+    n = ctypes.c_uint64()
+    check(lib().duo_prefill_staging_bytes(cache.handle, layer, seq, ctypes.byref(n)),
+          "duo_prefill_staging_bytes")
+    return n.value
+
+
+def duo_attn_prefill_staged(cache: DuoCache, layer: int, seq: int, q: torch.Tensor,
+                            k: torch.Tensor, v: torch.Tensor, out=None, lse=None, staging=None,
+                            stream=None):
+    """``duo_attn_prefill`` over a 4- or 8-bit cache: the retrieval heads' earlier tokens are
+    read back as bf16 rows into ``staging`` (a ``torch.uint8`` device tensor of at least
+    ``duo_prefill_staging_bytes`` bytes; allocated here when None), then the chunk attends.
+    Shapes as in ``duo_attn_prefill``."""
+    m = q.shape[1] if seq < 0 else q.shape[0]
+    lead = (cache.batch, m) if seq < 0 else (m,)
+    _check_tensor(q, lead + (cache.hq, cache.d), cache.dtype, cache.device, "q")
+    _check_tensor(k, lead + (cache.hkv, cache.d), cache.dtype, cache.device, "k")
+    _check_tensor(v, lead + (cache.hkv, cache.d), cache.dtype, cache.device, "v")
+    if out is None:
+        out = torch.empty(lead + (cache.hq, cache.d), dtype=cache.out_dtype, device=q.device)
+    _check_tensor(out, lead + (cache.hq, cache.d), cache.out_dtype, cache.device, "out")
+    lse_ptr = None
+    if lse is not None:
+        _check_tensor(lse, lead + (cache.hq,), torch.float32, cache.device, "lse")
+        lse_ptr = lse.data_ptr()
+    need = duo_prefill_staging_bytes(cache, layer, seq)
+    if staging is None:
+        staging = torch.empty(max(need, 16), dtype=torch.uint8, device=cache.device)
+    check(lib().duo_attn_prefill_staged(cache.handle, layer, seq, ctypes.c_void_p(q.data_ptr()),
+                                        ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+                                        m, ctypes.c_void_p(out.data_ptr()),
+                                        ctypes.c_void_p(lse_ptr),
+                                        ctypes.c_void_p(staging.data_ptr()), staging.numel(),
+                                        _stream(stream)), "duo_attn_prefill_staged")
     return out
 
 

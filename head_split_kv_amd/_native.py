@@ -17,7 +17,7 @@ EXPORTS = (
     "duo_layout_query", "duo_cache_create", "duo_cache_init", "duo_cache_reset",
     "duo_cache_set_lengths", "duo_cache_destroy",
     "duo_kv_append", "duo_attn_decode", "duo_attn_decode_noalloc", "duo_decode_step", "duo_attn_prefill",
-    "duo_attn_gate_mixed",
+    "duo_attn_prefill_staged", "duo_prefill_staging_bytes", "duo_attn_gate_mixed",
     "duo_slot_positions",
     "duo_cache_lengths", "duo_kv_bytes", "duo_set_decode_splits", "duo_timing_enable",
     "duo_timing_read", "duo_read_probe", "duo_binarize_gates", "duo_head_order", "duo_permute_blocks",
@@ -79,6 +79,7 @@ def lib() -> ctypes.CDLL:
     vp = ctypes.c_void_p
     i32 = ctypes.c_int32
     P = ctypes.POINTER
+    u64 = ctypes.c_uint64
     sig = {
         "duo_layout_query": (st, [P(DuoConfig), P(DuoLayout)]),
         "duo_cache_create": (st, [P(DuoConfig), vp, ctypes.c_uint64, P(vp)]),
@@ -91,6 +92,8 @@ def lib() -> ctypes.CDLL:
         "duo_attn_decode_noalloc": (st, [vp, i32, vp, vp, vp, vp]),
         "duo_decode_step": (st, [vp, i32, vp, vp, vp, vp, vp, vp]),
         "duo_attn_prefill": (st, [vp, i32, i32, vp, vp, vp, i32, vp, vp, vp]),
+        "duo_attn_prefill_staged": (st, [vp, i32, i32, vp, vp, vp, i32, vp, vp, vp, u64, vp]),
+        "duo_prefill_staging_bytes": (st, [vp, i32, i32, P(ctypes.c_uint64)]),
         "duo_attn_gate_mixed": (st, [vp, i32, i32, vp, vp, vp, i32, P(ctypes.c_float), vp, vp]),
         "duo_slot_positions": (st, [vp, i32, P(i32), vp]),
         "duo_cache_lengths": (st, [vp, P(i32)]),

@@ -361,9 +361,12 @@ namespace {
 
 // Checks and launch arguments of one prefill chunk (shared by duo_attn_prefill and
 // duo_attn_gate_mixed). Returns DUO_OK with `a` filled, or the error to report.
+// staged: the caller has a bf16 read-back of a quantized layer's retrieval caches to offer
+// (duo_attn_prefill_staged); otherwise prefill over a quantized layer is unsupported.
 duo_status prefill_args(duo_cache* c, int32_t layer, int32_t seq, const void* q, const void* k,
-                        const void* v, int32_t n_chunk, void* out, float* lse, PrefillArgs& a) {
-  if ((c->cfg.kv_bits == 4 || c->cfg.kv_bits == 8) && c->layers[layer].n_ret > 0)
+                        const void* v, int32_t n_chunk, void* out, float* lse, PrefillArgs& a,
+                        bool staged = false) {
+  if ((c->cfg.kv_bits == 4 || c->cfg.kv_bits == 8) && c->layers[layer].n_ret > 0 && !staged)
     return DUO_ERR_UNSUPPORTED;
   if (!q || !k || !v || !out || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
       !aligned16(out) || !aligned4(lse))
@@ -438,6 +441,67 @@ duo_status duo_attn_prefill(duo_cache* c, int32_t layer, int32_t seq, const void
   PrefillArgs a;
   const duo_status st = prefill_args(c, layer, seq, q, k, v, n_chunk, out, lse, a);
   if (st != DUO_OK) return st;
+  const int group = c->cfg.num_q_heads / c->cfg.num_kv_heads;
+  return launch_status(launch_prefill(a, c->cfg.dtype, c->cfg.head_dim, group, stream,
+                                      next_marks(c, DUO_TIMING_PREFILL)));
+}
+
+duo_status duo_prefill_staging_bytes(const duo_cache* c, int32_t layer, int32_t seq,
+                                     uint64_t* bytes) {
+  if (!layer_ok(c, layer) || seq < -1 || seq >= c->cfg.batch || !bytes) return DUO_ERR_INVALID;
+  *bytes = 0;
+  if (c->cfg.kv_bits != 4 && c->cfg.kv_bits != 8) return DUO_OK;
+  const int32_t b0 = seq < 0 ? 0 : seq, nb = seq < 0 ? c->cfg.batch : 1;
+  int32_t c_max = 0;
+  for (int32_t b = b0; b < b0 + nb; ++b)
+    c_max = std::max(c_max, c->lens[(size_t)layer * c->cfg.batch + b]);
+  *bytes = 2ull * nb * c->layers[layer].n_ret * (uint64_t)c_max * c->cfg.head_dim * 2;
+  return DUO_OK;
+}
+
+duo_status duo_attn_prefill_staged(duo_cache* c, int32_t layer, int32_t seq, const void* q,
+                                   const void* k, const void* v, int32_t n_chunk, void* out,
+                                   float* lse, void* staging, uint64_t staging_bytes,
+                                   void* stream) {
+  if (!layer_ok(c, layer) || seq < -1 || seq >= c->cfg.batch || n_chunk < 0)
+    return DUO_ERR_INVALID;
+  const bool quant = c->cfg.kv_bits == 4 || c->cfg.kv_bits == 8;
+  if (!quant) return duo_attn_prefill(c, layer, seq, q, k, v, n_chunk, out, lse, stream);
+  if (c->cfg.rope_theta > 0.f) return DUO_ERR_UNSUPPORTED;
+  uint64_t need = 0;
+  if (duo_prefill_staging_bytes(c, layer, seq, &need) != DUO_OK) return DUO_ERR_INVALID;
+  if (need > 0 && (!staging || !aligned16(staging) || staging_bytes < need)) return DUO_ERR_INVALID;
+  if (n_chunk == 0) return DUO_OK;
+  PrefillArgs a;
+  const duo_status st = prefill_args(c, layer, seq, q, k, v, n_chunk, out, lse, a, true);
+  if (st != DUO_OK) return st;
+  // the prefix of every retrieval head, read back as bf16 rows [nb][Hr][c_max][D] (K, then V)
+  int32_t c_max = 0;
+  for (int32_t i = 0; i < a.nb; ++i) c_max = std::max(c_max, a.c0[i]);
+  const uint64_t half = need / 2;
+  if (need > 0) {
+    const Q4Geom g = q4_geom(c->cfg.capacity, c->cfg.head_dim, c->cfg.kv_bits);
+    DequantArgs d;
+    std::memset(&d, 0, sizeof(d));
+    d.full_k = a.full_k;
+    d.full_v = a.full_v;
+    d.out_k = staging;
+    d.out_v = (char*)staging + half;
+    d.q4_stride = (int64_t)g.stride;
+    d.q4_params = (int64_t)g.codes;
+    d.q4_resid = (int64_t)(g.codes + g.params);
+    d.qbits = c->cfg.kv_bits;
+    d.b0 = a.b0;
+    d.nb = a.nb;
+    d.Hr = a.Hr;
+    d.cap_s = c_max;
+    std::memcpy(d.c0, a.c0, sizeof(d.c0));
+    if (launch_dequant_kv4(d, c->cfg.head_dim, stream) != 0) return DUO_ERR_HIP;
+  }
+  a.full_k = staging;
+  a.full_v = (char*)staging + half;
+  a.cap = c_max;
+  a.full_b0 = a.b0;
   const int group = c->cfg.num_q_heads / c->cfg.num_kv_heads;
   return launch_status(launch_prefill(a, c->cfg.dtype, c->cfg.head_dim, group, stream,
                                       next_marks(c, DUO_TIMING_PREFILL)));

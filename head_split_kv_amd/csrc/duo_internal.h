@@ -163,6 +163,8 @@ struct PrefillArgs {
   // the sink + recent window and write alpha[j] * out + (1 - alpha[j]) * result.
   int32_t mixed;
   int32_t full_heads;       // full caches per sequence of this layer
+  int32_t full_b0;          // sequence whose full caches start at full_k / full_v (0, or b0
+                            // when they are a staging copy of sequences b0 .. b0 + nb - 1)
   float alpha[kMaxKvHeads];
   int16_t cls_idx[kMaxKvHeads];
   uint8_t ret_kv[kMaxKvHeads];
@@ -183,6 +185,19 @@ int launch_reset(const ResetArgs& a, void* stream);
 int launch_rope_tables(char* tables, int32_t D, int32_t nbase, double theta, void* stream);
 int launch_append(const AppendArgs& a, int dtype, void* stream);
 int launch_append_kv4(const AppendArgs& a, int head_dim, void* stream);
+// Read-back of a layer's 4- or 8-bit retrieval caches into bf16 rows (kv4.hip): for each
+// sequence b0 + i and retrieval head r, tokens 0 .. c0[i] - 1 into out_k / out_v
+// [nb][Hr][cap_s][D], complete groups as bf16(float32(c * scale + zero)), residual rows copied.
+struct DequantArgs {
+  const void* full_k;  // this layer's quantized regions
+  const void* full_v;
+  void* out_k;         // staging rows, [nb][Hr][cap_s][D] bf16 each
+  void* out_v;
+  int64_t q4_stride, q4_params, q4_resid;  // Q4Geom of the regions
+  int32_t qbits, b0, nb, Hr, cap_s;
+  int32_t c0[kMaxBatch];
+};
+int launch_dequant_kv4(const DequantArgs& a, int head_dim, void* stream);
 int launch_set_lengths(const SetLenArgs& a, void* stream);
 int launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group, void* stream,
                   const KernelMarks& marks);

@@ -226,7 +226,108 @@ __global__ void __launch_bounds__(kThreads) kv4_append_kernel(AppendArgs a) {
   quantize(g);
 }
 
+// Read-back into bf16 rows (DequantArgs): one thread per (K or V, sequence, head, token, 8
+// channels), reading the codes through the layouts above. A value is c * scale + zero in
+// float32 (c * scale is exact: at most 8 + 8 significant bits; one rounding for the sum),
+// rounded to bf16 to nearest even.
+template <int D, int BITS>
+__global__ void __launch_bounds__(kThreads) kv4_dequant_kernel(DequantArgs a) {
+  constexpr int CH = D / 8, KC = D / 32;
+  const int64_t per_tensor = (int64_t)a.nb * a.Hr * a.cap_s * CH;
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < 2 * per_tensor;
+       u += (int64_t)gridDim.x * blockDim.x) {
+    const bool is_v = u >= per_tensor;
+    int64_t w = is_v ? u - per_tensor : u;
+    const int x = (int)(w % CH);
+    w /= CH;
+    const int t = (int)(w % a.cap_s);
+    w /= a.cap_s;
+    const int r = (int)(w % a.Hr);
+    const int bi = (int)(w / a.Hr);
+    const int n = a.c0[bi];
+    if (t >= n) continue;
+    const char* head = (const char*)(is_v ? a.full_v : a.full_k) +
+                       ((int64_t)(a.b0 + bi) * a.Hr + r) * a.q4_stride;
+    uint4* dst = (uint4*)((uint16_t*)(is_v ? a.out_v : a.out_k) +
+                          (((int64_t)bi * a.Hr + r) * a.cap_s + t) * D + 8 * x);
+    if (t >= (n / kG) * kG) {  // residual row
+      *dst = *(const uint4*)(head + a.q4_resid + (int64_t)(t % kG) * D * 2 + 16 * x);
+      continue;
+    }
+    const int g = t / kG, tt = t % kG, c0 = 8 * x;
+    float val[8];
+    if (!is_v) {  // per-channel scale and zero of the group
+      const uint16_t* par = (const uint16_t*)(head + a.q4_params) + (int64_t)g * 2 * D;
+      const uint4 sv = *(const uint4*)(par + c0), zv = *(const uint4*)(par + D + c0);
+      const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w}, zw[4] = {zv.x, zv.y, zv.z, zv.w};
+      const uint32_t* row = (const uint32_t*)(head + (int64_t)t * (D * BITS / 8));
+      const int k = c0 / 32, j = (c0 % 32) / 8;
+      uint32_t code[8];
+      if constexpr (BITS == 4) {
+        const uint32_t cw = row[KC * j + k];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) code[e] = (cw >> (4 * e)) & 15u;
+      } else {
+        const uint2 cw = *(const uint2*)(row + 2 * KC * j + 2 * k);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) code[e] = ((e < 4 ? cw.x : cw.y) >> (8 * (e & 3))) & 255u;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t sb = (e & 1) ? sw[e >> 1] >> 16 : sw[e >> 1] & 0xFFFFu;
+        const uint32_t zb = (e & 1) ? zw[e >> 1] >> 16 : zw[e >> 1] & 0xFFFFu;
+        val[e] = __builtin_fmaf((float)code[e], bf16_to_f32((uint16_t)sb), bf16_to_f32((uint16_t)zb));
+      }
+    } else {  // per-token scale and zero
+      const uint32_t pw = ((const uint32_t*)(head + a.q4_params))[t];
+      const float sc = bf16_to_f32((uint16_t)(pw & 0xFFFFu)), ze = bf16_to_f32((uint16_t)(pw >> 16));
+      const uint32_t* grp = (const uint32_t*)(head + (int64_t)g * kG * (D * BITS / 8));
+      const int st = tt / 32, rr = tt % 32, j = (rr % 16) / 4;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c = c0 + e, cb = c / 16, lane = 16 * j + c % 16;
+        uint32_t code;
+        if constexpr (BITS == 4) {
+          const int el = 4 * (rr / 16) + rr % 4;  // element of the token in its word
+          const uint32_t cw = grp[((st * (D / 64) + cb / 4) * 64 + lane) * 4 + cb % 4];
+          code = (cw >> (4 * el)) & 15u;
+        } else {
+          const int uu = 2 * (cb % 2) + rr / 16;
+          const uint32_t cw = grp[((st * (D / 32) + cb / 2) * 64 + lane) * 4 + uu];
+          code = (cw >> (8 * (rr % 4))) & 255u;
+        }
+        val[e] = __builtin_fmaf((float)code, sc, ze);
+      }
+    }
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = (uint32_t)f32_to_bf16_bits(val[2 * i]) | ((uint32_t)f32_to_bf16_bits(val[2 * i + 1]) << 16);
+    *dst = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
 }  // namespace
+
+int launch_dequant_kv4(const DequantArgs& a, int head_dim, void* stream) {
+  const int64_t work = 2 * (int64_t)a.nb * a.Hr * a.cap_s * (head_dim / 8);
+  if (work == 0) return 0;
+  int64_t blocks = (work + kThreads - 1) / kThreads;
+  if (blocks > 16384) blocks = 16384;
+  const dim3 grid((unsigned)blocks), block(kThreads);
+  hipStream_t st = (hipStream_t)stream;
+  if (head_dim == 128 && a.qbits == 4)
+    hipLaunchKernelGGL((kv4_dequant_kernel<128, 4>), grid, block, 0, st, a);
+  else if (head_dim == 64 && a.qbits == 4)
+    hipLaunchKernelGGL((kv4_dequant_kernel<64, 4>), grid, block, 0, st, a);
+  else if (head_dim == 128 && a.qbits == 8)
+    hipLaunchKernelGGL((kv4_dequant_kernel<128, 8>), grid, block, 0, st, a);
+  else if (head_dim == 64 && a.qbits == 8)
+    hipLaunchKernelGGL((kv4_dequant_kernel<64, 8>), grid, block, 0, st, a);
+  else
+    return -1;
+  return (int)hipGetLastError();
+}
 
 int launch_append_kv4(const AppendArgs& a, int head_dim, void* stream) {
   const int64_t blocks = (int64_t)a.nb * a.Hr * (1 + a.q4_mid);

@@ -193,8 +193,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
   if (full_src) {
     n_cache_tiles = (c0 + kBN - 1) / kBN;
     const int64_t base = (kMix && !retrieval)
-                             ? ((int64_t)b * a.full_heads + a.cls_idx[j]) * a.cap * RB
-                             : ((int64_t)b * a.Hr + cls) * a.cap * RB;
+                             ? ((int64_t)(b - a.full_b0) * a.full_heads + a.cls_idx[j]) * a.cap * RB
+                             : ((int64_t)(b - a.full_b0) * a.Hr + cls) * a.cap * RB;
     cache_k = (const char*)a.full_k + base;
     cache_v = (const char*)a.full_v + base;
   } else {
@@ -710,8 +710,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_f32_kernel(PrefillArgs a,
   if (full_src) {
     n_cache_tiles = (c0 + kF32BN - 1) / kF32BN;
     const int64_t base = (mixed && !retrieval)
-                             ? ((int64_t)b * a.full_heads + a.cls_idx[j]) * a.cap * D
-                             : ((int64_t)b * a.Hr + cls) * a.cap * D;
+                             ? ((int64_t)(b - a.full_b0) * a.full_heads + a.cls_idx[j]) * a.cap * D
+                             : ((int64_t)(b - a.full_b0) * a.Hr + cls) * a.cap * D;
     cache_k = (const float*)a.full_k + base;
     cache_v = (const float*)a.full_v + base;
   } else {

@@ -115,8 +115,9 @@ typedef struct {
  * ((s (d / 32) + h) 64 + 16 j + c % 16) 4 + u, with c / 16 = 2 h + u / 2, holds channel c;
  * its element e is token 128 g + 32 s + 16 (u % 2) + 4 j + e.
  * duo_kv_append, duo_attn_decode and duo_decode_step handle them (a step whose token completes
- * a group of some sequence runs as append + decode); duo_attn_prefill and duo_attn_gate_mixed
- * return DUO_ERR_UNSUPPORTED on a 4- or 8-bit cache. */
+ * a group of some sequence runs as append + decode); duo_attn_prefill_staged pre-fills over
+ * them; duo_attn_prefill and duo_attn_gate_mixed return DUO_ERR_UNSUPPORTED on a layer with
+ * 4- or 8-bit retrieval caches. */
 #define DUO_KV4_GROUP 128
 
 /* Pre-RoPE keys (cfg.rope_theta > 0 with kv_bits = 4 or 8; OpenReview thread, the authors'
@@ -234,6 +235,27 @@ duo_status duo_decode_step(duo_cache* cache, int32_t layer, const void* q, const
 duo_status duo_attn_prefill(duo_cache* cache, int32_t layer, int32_t seq, const void* q,
                             const void* k, const void* v, int32_t n_chunk, void* out,
                             float* lse, void* stream);
+
+/* duo_attn_prefill over a layer whose retrieval caches are in 4 or 8 bits (explainer,
+ * "Combination with Quantization": quantized caches serve the whole context). The retrieval
+ * heads' earlier tokens are first read back into `staging` as bf16 rows, complete groups as
+ * bf16(float32(c * scale + zero)) and residual rows as stored, [nb][Hr][c_max][d] for K then
+ * the same for V (nb = 1, or B when seq = -1; Hr the layer's retrieval heads; c_max the
+ * longest current length among the sequences); the chunk then attends as in duo_attn_prefill,
+ * its own keys and values exact. staging: caller-owned device memory, 16-byte aligned, at
+ * least duo_prefill_staging_bytes bytes (else DUO_ERR_INVALID); its contents are scratch.
+ * On a dtype cache this is duo_attn_prefill (staging unused). DUO_ERR_UNSUPPORTED with
+ * cfg.rope_theta > 0. */
+duo_status duo_attn_prefill_staged(duo_cache* cache, int32_t layer, int32_t seq, const void* q,
+                                   const void* k, const void* v, int32_t n_chunk, void* out,
+                                   float* lse, void* staging, uint64_t staging_bytes,
+                                   void* stream);
+
+/* Bytes of staging duo_attn_prefill_staged needs for this layer and seq (-1 = all sequences)
+ * at the cache's current lengths: 2 * nb * Hr * c_max * d * 2 on a 4- or 8-bit cache, 0
+ * otherwise. Host only. */
+duo_status duo_prefill_staging_bytes(const duo_cache* cache, int32_t layer, int32_t seq,
+                                     uint64_t* bytes);
 
 /* Gate-mixed attention of one chunk, the attention of the retrieval-head identification phase
  * (explainer, "Gate Parameterization"): every query head h of KV head j = h / G returns

@@ -303,6 +303,31 @@ def test_error_paths_leave_state_unchanged():
     fc.close()
 
 
+def test_prefill_staged_checks_before_launch():
+    """duo_prefill_staging_bytes: 0 on a dtype cache and on empty caches, argument checks;
+    duo_attn_prefill_staged: rejects bad arguments and pre-RoPE caches before launching."""
+    L = N.lib()
+    n = ctypes.c_uint64(7)
+    for bits in (0, 4, 8):
+        fc = FakeCache(kv_bits=bits)
+        assert L.duo_prefill_staging_bytes(fc.h, 0, -1, ctypes.byref(n)) == N.DUO_OK
+        assert n.value == 0
+        assert L.duo_prefill_staging_bytes(fc.h, 2, -1, ctypes.byref(n)) == N.DUO_ERR_INVALID
+        assert L.duo_prefill_staging_bytes(fc.h, 0, 3, ctypes.byref(n)) == N.DUO_ERR_INVALID
+        assert L.duo_prefill_staging_bytes(fc.h, 0, -1, None) == N.DUO_ERR_INVALID
+        p = ctypes.c_void_p(1 << 40)
+        assert L.duo_attn_prefill_staged(fc.h, 0, -2, p, p, p, 4, p, None, p, 0,
+                                         None) == N.DUO_ERR_INVALID
+        assert L.duo_attn_prefill_staged(fc.h, 0, -1, p, p, p, -1, p, None, p, 0,
+                                         None) == N.DUO_ERR_INVALID
+        fc.close()
+    fc = FakeCache(kv_bits=4, rope_theta=10000.0)
+    p = ctypes.c_void_p(1 << 40)
+    assert L.duo_attn_prefill_staged(fc.h, 0, -1, p, p, p, 4, p, None, p, 1 << 20,
+                                     None) == N.DUO_ERR_UNSUPPORTED
+    fc.close()
+
+
 def test_read_probe_rejects_bad_arguments():
     """The streaming-read probe checks its arguments before launching anything."""
     L = N.lib()
