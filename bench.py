@@ -54,9 +54,10 @@ def parse():
     p.add_argument("--workload", default="c3", help="decode workload key (c2, c3, c5, c5q)")
     p.add_argument("--prefill-passes", type=int, default=3)
     p.add_argument("--no-prefill", action="store_true")
-    p.add_argument("--prefill-modes", default="window,chunk,mixed",
+    p.add_argument("--prefill-modes", default="window,chunk,mixed,kv4",
                    help="prefill legs to time: window (per-query sink + recent mask), chunk "
-                        "(chunk-granular streaming heads), mixed (gate-mixed attention)")
+                        "(chunk-granular streaming heads), mixed (gate-mixed attention), kv4 "
+                        "(window mode over a 4-bit cache, staged)")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-kv4", action="store_true", help="skip the 4-bit full-cache decode leg")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -247,7 +248,10 @@ def decode_leg(args, torch, hsk, W, N, kv_bits=0, rope_theta=0.0):
     return result
 
 
-def prefill_leg(args, torch, hsk, W, N, mode="window"):
+def prefill_leg(args, torch, hsk, W, N, mode="window", kv_bits=0):
+    """The 32K MHA prompt in 4K chunks; with kv_bits 4 over a 4-bit cache
+    (duo_attn_prefill_staged: the retrieval prefix read back into bf16 staging, then the
+    prefill kernel; the kernel timers cover the prefill kernel alone)."""
     w = W.workload("c2")
     mask = W.retrieval_mask(w)[0]
     dev = torch.device("cuda")
@@ -255,7 +259,10 @@ def prefill_leg(args, torch, hsk, W, N, mode="window"):
     cache = hsk.DuoCache(num_layers=1, batch=1, num_q_heads=w.hq, num_kv_heads=w.hkv,
                          head_dim=w.d, sink=w.sink, recent=w.recent, capacity=P,
                          retrieval_mask=[mask], dtype=torch.bfloat16, out_dtype=torch.bfloat16,
-                         streaming_prefill=mode, device=dev)
+                         streaming_prefill=mode, device=dev, kv_bits=kv_bits)
+    staged = kv_bits in (4, 8)
+    staging = torch.empty(2 * int(mask.sum()) * P * w.d * 2 if staged else 16,
+                          dtype=torch.uint8, device=dev)
     q = torch.from_numpy(W.tokens(w, "q", 0, 0, 0, P)).to(dev).to(torch.bfloat16)
     k = torch.from_numpy(W.tokens(w, "k", 0, 0, 0, P)).to(dev).to(torch.bfloat16)
     v = torch.from_numpy(W.tokens(w, "v", 0, 0, 0, P)).to(dev).to(torch.bfloat16)
@@ -272,10 +279,16 @@ def prefill_leg(args, torch, hsk, W, N, mode="window"):
         for c0 in range(0, P, C):
             if timer_attn is not None:
                 timer_attn.start()
-            st = lib.duo_attn_prefill(h, 0, 0, ctypes.c_void_p(q.data_ptr() + c0 * rs),
-                                      ctypes.c_void_p(k.data_ptr() + c0 * ks),
-                                      ctypes.c_void_p(v.data_ptr() + c0 * ks), C,
-                                      ctypes.c_void_p(out.data_ptr() + c0 * rs), None, stream)
+            qq = ctypes.c_void_p(q.data_ptr() + c0 * rs)
+            kk = ctypes.c_void_p(k.data_ptr() + c0 * ks)
+            vv = ctypes.c_void_p(v.data_ptr() + c0 * ks)
+            oo = ctypes.c_void_p(out.data_ptr() + c0 * rs)
+            if staged:
+                st = lib.duo_attn_prefill_staged(h, 0, 0, qq, kk, vv, C, oo, None,
+                                                 ctypes.c_void_p(staging.data_ptr()),
+                                                 staging.numel(), stream)
+            else:
+                st = lib.duo_attn_prefill(h, 0, 0, qq, kk, vv, C, oo, None, stream)
             if timer_attn is not None:
                 attn_ms += timer_attn.stop_ms()
             if st:
@@ -316,7 +329,7 @@ def prefill_leg(args, torch, hsk, W, N, mode="window"):
     else:
         pairs_str = sum(min(p + 1, S + R) for p in range(P))
     flops = 4 * w.d * (hr * pairs_ret + hs * pairs_str) * (w.hq // w.hkv)
-    del cache, q, k, v, out
+    del cache, q, k, v, out, staging
     torch.cuda.empty_cache()
     return dict(workload=w, pass_ms=pass_ms, attn_ms=attn_ms, flops=flops,
                 tflops=flops / (attn_ms * 1e-3) / 1e12, kern_ms=kern_ms_pass,
@@ -695,6 +708,12 @@ def main():
             f"for {pre_chunk['flops'] / 1e12:.3f} TFLOP = {pre_chunk['tflops']:.1f} TFLOP/s; "
             f"attention kernel {pre_chunk['kern_ms']:.3f} ms = "
             f"{pre_chunk['kern_tflops']:.1f} TFLOP/s")
+    pre_kv4 = None
+    if not args.no_prefill and "kv4" in modes:
+        pre_kv4 = prefill_leg(args, torch, hsk, W, N, kv_bits=4)
+        log(f"prefill over a 4-bit cache: {pre_kv4['attn_ms']:.3f} ms attention (read-back "
+            f"included) = {pre_kv4['tflops']:.1f} TFLOP/s; attention kernel "
+            f"{pre_kv4['kern_ms']:.3f} ms = {pre_kv4['kern_tflops']:.1f} TFLOP/s")
     mix = None
     if not args.no_prefill and "mixed" in modes:
         mix = gate_mixed_leg(args, torch, hsk, W, N)
@@ -858,6 +877,16 @@ def main():
                          "kernel": "prefill_kernel<d128, G1> (8 launches per pass)",
                          "kernel_ms_per_pass": round(pre["kern_ms"], 3),
                          "algorithmic_flops": int(pre["flops"])},
+        },
+        "prefill_kv4": None if pre_kv4 is None else {
+            "workload": f"{pre_kv4['workload'].name}: 32K prompt in 4K chunks over 4-bit full "
+                        f"caches (retrieval prefix read back into bf16 staging per chunk)",
+            "attn_ms": round(pre_kv4["attn_ms"], 3),
+            "ms_incl_append": round(pre_kv4["pass_ms"], 3),
+            "tflops": round(pre_kv4["tflops"], 1),
+            "kernel_ms_per_pass": round(pre_kv4["kern_ms"], 3),
+            "kernel_tflops": round(pre_kv4["kern_tflops"], 1),
+            "frac": round(pre_kv4["kern_tflops"] / BF16_PEAK_TFLOPS, 4),
         },
         "prefill_chunk_mode": None if pre_chunk is None else {
             "workload": f"{pre_chunk['workload'].name}: 32K prompt in 4K chunks, streaming heads "
