@@ -828,14 +828,14 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(dec8["kern_gbs"], 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(dec8["kern_gbs"] / HBM_PEAK_GBS, 4),
-                         "traffic": None,
+                         "traffic": committed_traffic("decode.hip", f"decode_kv8_{args.workload}"),
                          "kernel": "decode_q4_kernel<d128, G4, 8-bit> (split attention kernel)",
                          "kernel_us": round(dec8["kern_us"], 3)},
         },
         "decode_kv4_rope": None if dec4r is None else {
-            "workload": "the same 4-bit decode with pre-RoPE keys (base 500,000): retrieval "
-                        "keys turned at their positions after dequantization, streaming keys "
-                        "turned when appended",
+            "workload": "the same 4-bit decode with pre-RoPE keys (base 500,000): every key "
+                        "turned at its own position inside the kernel, after dequantization on "
+                        "retrieval heads, as stored on streaming heads",
             "us_per_layer_step": round(dec4r["us_layer"], 3),
             "GBps": round(dec4r["gbs"], 1),
             "stored_bytes_per_layer_step": int(dec4r["step_bytes"]),
