@@ -446,13 +446,12 @@ def decode_step_kv4(q, k_hist, v_hist, retrieval, sink, recent, scale=None, rope
     return decode_step(q, k, v, retrieval, sink, recent, scale)
 
 
-def kv4_history_bf16(x_hist, n: int, is_key: bool, bits: int = 4) -> np.ndarray:
-    """``kv4_history`` read back in the cache dtype: every dequantized value is
-    ``to_bf16(float32(c * scale + zero))`` (c * scale is exact in float32: at most 8 + 8
-    significant bits; one float32 rounding for the sum, then round to nearest even), the
-    residual tokens exact as before."""
+def kv4_history_f32(x_hist, n: int, is_key: bool, bits: int = 4) -> np.ndarray:
+    """``kv4_history`` as a float32 dequantizer computes it: every dequantized value is
+    ``float32(c * scale + zero)`` (c * scale is exact in float32: at most 8 + 8 significant
+    bits; one float32 rounding for the sum), the residual tokens exact. float32 ``[n, d]``."""
     x = np.asarray(x_hist, dtype=np.float32)[:n]
-    out = x.astype(np.float64).copy()
+    out = x.copy()
     full = (n // KV4_GROUP) * KV4_GROUP
     for g0 in range(0, full, KV4_GROUP):
         blk = x[g0:g0 + KV4_GROUP]
@@ -462,12 +461,18 @@ def kv4_history_bf16(x_hist, n: int, is_key: bool, bits: int = 4) -> np.ndarray:
             y = c * scale[None, :] + zero[None, :]
         else:
             y = c * scale[:, None] + zero[:, None]
-        out[g0:g0 + KV4_GROUP] = to_bf16(y.astype(np.float32)).astype(np.float64)
+        out[g0:g0 + KV4_GROUP] = y.astype(np.float32)
     return out
 
 
+def kv4_history_bf16(x_hist, n: int, is_key: bool, bits: int = 4) -> np.ndarray:
+    """``kv4_history`` read back in the cache dtype: ``kv4_history_f32`` rounded to the nearest
+    bfloat16 (ties to even); the residual tokens, bf16 already, stay exact. float64 ``[n, d]``."""
+    return to_bf16(kv4_history_f32(x_hist, n, is_key, bits)).astype(np.float64)
+
+
 def prefill_chunk_kv4(q, k_hist, v_hist, start, retrieval, sink, recent, scale=None,
-                      chunk_granular=False, bits: int = 4):
+                      chunk_granular=False, bits: int = 4, rope_theta=None):
     """``prefill_chunk`` over a cache whose retrieval heads are stored in ``bits`` bits (4 or
     8). Reading (the pages pair quantized caches with serving the whole context, explainer,
     "Combination with Quantization"): the chunk's queries see the cache as it stands before
@@ -475,12 +480,27 @@ def prefill_chunk_kv4(q, k_hist, v_hist, start, retrieval, sink, recent, scale=N
     ``kv4_history_bf16(.., start)``: complete groups dequantized into the cache dtype, as a
     dequantize-then-attend kernel computes them, the last incomplete group exact. The chunk's
     own keys and values are exact (they are not in the cache yet; the caller appends them
-    afterwards). Streaming heads are exact, as in decoding."""
+    afterwards). Streaming heads are exact, as in decoding.
+
+    With ``rope_theta`` the cache holds pre-RoPE keys (the 4-bit reading of the OpenReview
+    thread, below) and ``k_hist`` holds every key as appended, before RoPE; ``q`` is the
+    chunk's queries after their own rotation. Reading: every key the chunk attends to is
+    turned at its own position and read in the cache dtype, as a kernel that stages the keys
+    for a bf16 prefill computes them: ``to_bf16(rope(x, t))`` of the float32 dequantized key
+    (``kv4_history_f32``) for a retrieval head's earlier tokens, and of the key as given for
+    the chunk's own keys and for every streaming head. Values are as without RoPE."""
     k = np.asarray(k_hist, dtype=np.float64).copy()
     v = np.asarray(v_hist, dtype=np.float64).copy()
+    if rope_theta:
+        pos = np.arange(k.shape[0])
+        k = to_bf16(rope(k, pos, rope_theta)).astype(np.float64)
     for j in range(k.shape[1]):
         if retrieval[j] and start > 0:
-            k[:start, j] = kv4_history_bf16(k_hist[:, j], start, True, bits)
+            if rope_theta:
+                kd = kv4_history_f32(k_hist[:, j], start, True, bits)
+                k[:start, j] = to_bf16(rope(kd, np.arange(start), rope_theta)).astype(np.float64)
+            else:
+                k[:start, j] = kv4_history_bf16(k_hist[:, j], start, True, bits)
             v[:start, j] = kv4_history_bf16(v_hist[:, j], start, False, bits)
     return prefill_chunk(q, k, v, start, retrieval, sink, recent, scale, chunk_granular)
 

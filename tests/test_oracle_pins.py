@@ -684,6 +684,65 @@ def pin_kv4_prefill():
         assert np.array_equal(g, h) and np.array_equal(lg, lh)
 
 
+def pin_kv4_prefill_rope():
+    """Prefill over a pre-RoPE quantized cache (keys appended before RoPE, queries after it):
+    every chunk query ends within the bound that the bf16 reading of its keys and values allows
+    of the decode step at its position, which turns every key exactly and reads the dequantized
+    keys and values unrounded. The chunk starts after the last complete group and completes
+    none, so both read the same groups. Per key element the two differ by at most half a bf16
+    step (2^-8 relative) plus a float32 rounding; a logit then moves by at most
+    delta = sigma (2^-8 + 2^-22) sum_i |q_i| |k_i|, the weights by a factor within
+    exp(+-2 delta), the output by (exp(2 delta) - 1) max_t |v_t - o| plus the values' own
+    2^-8 max |v|, and the log-sum-exp by delta. Each query is the turned key of one visible
+    token (a dequantized earlier token, a chunk token, a sink or a window slot), so its weight
+    dominates only where that key is turned at its own position: without RoPE, or with the
+    earlier tokens unturned, the outputs leave the bound."""
+    rng = np.random.default_rng(57)
+    G = O.KV4_GROUP
+    Hkv, Gq, d, S, R, theta, amp = 2, 2, 16, 2, 8, 10000.0, 2.0
+    sigma = 1.0 / math.sqrt(d)
+    for bits in (4, 8):
+        start, m = 2 * G + 8, 24
+        k = _bf16_grid(rng, start + m, Hkv, d)
+        v = _bf16_grid(rng, start + m, Hkv, d)
+        ret = [1, 0]
+        # the keys as the decode step reads them, turned
+        kk = np.asarray(k, dtype=np.float64).copy()
+        vv = np.asarray(v, dtype=np.float64).copy()
+        kk[:, 0] = O.kv4_history(k[:, 0], start + m, True, bits)
+        vv[:, 0] = O.kv4_history(v[:, 0], start + m, False, bits)
+        kk = O.rope(kk, np.arange(start + m), theta)
+        q = np.zeros((m, Hkv * Gq, d))
+        for i in range(m):
+            p = start + i
+            for h in range(Hkv * Gq):
+                j = h // Gq
+                if ret[j]:  # an earlier (quantized or residual) token, or one of the chunk
+                    t = int(rng.integers(0, start)) if h % 2 == 0 else int(rng.integers(start, p + 1))
+                else:       # a sink, or a slot of the window
+                    t = int(rng.integers(0, S)) if h % 2 == 0 else int(rng.integers(p - R + 1, p + 1))
+                q[i, h] = O.to_bf16(amp * kk[t, j])
+        c, lc = O.prefill_chunk_kv4(q, k, v, start, ret, S, R, bits=bits, rope_theta=theta)
+        plain, _ = O.prefill_chunk_kv4(q, k, v, start, ret, S, R, bits=bits)
+        outside = 0
+        for i in range(m):
+            p = start + i
+            e, le = O.decode_step_kv4(q[i], k[:p + 1], v[:p + 1], ret, S, R, bits=bits,
+                                      rope_theta=theta)
+            for h in range(Hkv * Gq):
+                j = h // Gq
+                vis = O.visible_mask([p], np.arange(p + 1), bool(ret[j]), S, R)[0]
+                kv, vv_ = kk[:p + 1][vis, j], vv[:p + 1][vis, j]
+                delta = sigma * (2.0 ** -8 + 2.0 ** -22) * (np.abs(kv) @ np.abs(q[i, h])).max()
+                spread = np.abs(vv_ - e[h][None, :]).max(axis=0)
+                bound = (math.expm1(2 * delta) * spread + 2.0 ** -8 * np.abs(vv_).max(axis=0)
+                         + 1e-12)
+                assert np.all(np.abs(c[i, h] - e[h]) <= bound), (bits, i, h)
+                assert abs(lc[i, h] - le[h]) <= delta + 1e-12
+                outside += int(np.any(np.abs(plain[i, h] - e[h]) > bound))
+        assert outside > m  # without RoPE most rows leave the bound
+
+
 def pin_rope_complex_form():
     """RoPE equals multiplying the complex channels z_i = x_i + i x_{i+d/2} by
     exp(i t theta^(-2i/d)), written here with complex arithmetic and the exponent as
@@ -751,7 +810,7 @@ PINS = [pin_cache_policy, pin_streaming_rows, pin_decode_scalar_bruteforce,
         pin_retrieval_count_nearest, pin_binarize_bruteforce, pin_binarize_equation4,
         pin_head_reordering_preserves_layer, pin_gate_mixed_bruteforce, pin_kv4_nearest_level,
         pin_kv4_axes_and_exact_grids, pin_kv4_groups_and_residual, pin_kv4_decode,
-        pin_kv4_prefill,
+        pin_kv4_prefill, pin_kv4_prefill_rope,
         pin_rope_complex_form, pin_rope_relative_positions, pin_kv4_rope_decode]
 
 
@@ -924,7 +983,10 @@ def _kv4_rope_before_quant(q, k_hist, v_hist, retrieval, sink, recent, scale=Non
 
 
 def _kv4_prefill_quantizes_chunk(q, k_hist, v_hist, start, retrieval, sink, recent, scale=None,
-                                 chunk_granular=False, bits=4):
+                                 chunk_granular=False, bits=4, rope_theta=None):
+    if rope_theta:
+        return _ORIG_PF4(q, k_hist, v_hist, start, retrieval, sink, recent, scale,
+                         chunk_granular, bits, rope_theta)
     m = np.asarray(q).shape[0]
     k = np.asarray(k_hist, dtype=np.float64).copy()
     v = np.asarray(v_hist, dtype=np.float64).copy()
@@ -935,7 +997,33 @@ def _kv4_prefill_quantizes_chunk(q, k_hist, v_hist, start, retrieval, sink, rece
     return O.prefill_chunk(q, k, v, start, retrieval, sink, recent, scale, chunk_granular)
 
 
+
+def _kv4_prefill_rope_variant(prefix_unturned=False, chunk_from_zero=False):
+    """prefill_chunk_kv4 with pre-RoPE keys, planted mistakes: the dequantized prefix keys left
+    unturned, or the chunk's own keys turned at their offsets in the chunk."""
+    def f(q, k_hist, v_hist, start, retrieval, sink, recent, scale=None, chunk_granular=False,
+          bits=4, rope_theta=None):
+        if not rope_theta:
+            return _ORIG_PF4(q, k_hist, v_hist, start, retrieval, sink, recent, scale,
+                             chunk_granular, bits)
+        k = np.asarray(k_hist, dtype=np.float64).copy()
+        v = np.asarray(v_hist, dtype=np.float64).copy()
+        pos = np.arange(k.shape[0])
+        if chunk_from_zero:
+            pos = np.where(pos >= start, pos - start, pos)
+        k = O.to_bf16(O.rope(k, pos, rope_theta)).astype(np.float64)
+        for j in range(k.shape[1]):
+            if retrieval[j] and start > 0:
+                kd = O.kv4_history_f32(k_hist[:, j], start, True, bits)
+                k[:start, j] = (O.to_bf16(kd) if prefix_unturned else
+                                O.to_bf16(O.rope(kd, np.arange(start), rope_theta)))
+                v[:start, j] = O.kv4_history_bf16(v_hist[:, j], start, False, bits)
+        return O.prefill_chunk(q, k, v, start, retrieval, sink, recent, scale, chunk_granular)
+    return f
+
+
 _ORIG_KV4 = O.decode_step_kv4
+_ORIG_PF4 = O.prefill_chunk_kv4
 _ORIG_MSA = O.masked_softmax_attention
 _ORIG_BIN = O.binarize_gates
 _ORIG_MIX = O.gate_mixed_attention
@@ -983,6 +1071,10 @@ MUTANTS = {
     "rope_position_plus_one": ("rope", _rope_variant(offset=1)),
     "kv4_rope_before_quantization": ("decode_step_kv4", _kv4_rope_before_quant),
     "kv4_prefill_quantizes_the_chunk": ("prefill_chunk_kv4", _kv4_prefill_quantizes_chunk),
+    "kv4_prefill_rope_prefix_unturned": ("prefill_chunk_kv4",
+                                         _kv4_prefill_rope_variant(prefix_unturned=True)),
+    "kv4_prefill_rope_chunk_from_zero": ("prefill_chunk_kv4",
+                                         _kv4_prefill_rope_variant(chunk_from_zero=True)),
     "query_order_interleaved": ("query_head_order",
                                 lambda o, G: np.array([g * len(o) + j for j in o for g in range(G)])),
 }
