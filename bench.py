@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-attn KV GB/s (% HBM peak) + µs/layer-step at 128K ctx; prefill TFLOP/s"
 ROPE_THETA = 500000.0  # RoPE base of the Llama-3-8B-shaped workload's pre-RoPE 4-bit leg
+PREFILL_ROPE_THETA = 10000.0  # Llama-2's RoPE base (the MHA prefill workload)
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 
@@ -54,10 +55,11 @@ def parse():
     p.add_argument("--workload", default="c3", help="decode workload key (c2, c3, c5, c5q)")
     p.add_argument("--prefill-passes", type=int, default=3)
     p.add_argument("--no-prefill", action="store_true")
-    p.add_argument("--prefill-modes", default="window,chunk,mixed,kv4",
+    p.add_argument("--prefill-modes", default="window,chunk,mixed,kv4,kv4rope",
                    help="prefill legs to time: window (per-query sink + recent mask), chunk "
                         "(chunk-granular streaming heads), mixed (gate-mixed attention), kv4 "
-                        "(window mode over a 4-bit cache, staged)")
+                        "(window mode over a 4-bit cache, staged), kv4rope (the same with "
+                        "pre-RoPE keys, staged turned)")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-kv4", action="store_true", help="skip the 4-bit full-cache decode leg")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -248,10 +250,11 @@ def decode_leg(args, torch, hsk, W, N, kv_bits=0, rope_theta=0.0):
     return result
 
 
-def prefill_leg(args, torch, hsk, W, N, mode="window", kv_bits=0):
+def prefill_leg(args, torch, hsk, W, N, mode="window", kv_bits=0, rope_theta=0.0):
     """The 32K MHA prompt in 4K chunks; with kv_bits 4 over a 4-bit cache
     (duo_attn_prefill_staged: the retrieval prefix read back into bf16 staging, then the
-    prefill kernel; the kernel timers cover the prefill kernel alone)."""
+    prefill kernel; the kernel timers cover the prefill kernel alone); with rope_theta the
+    cache holds pre-RoPE keys, and every key the chunk reads is staged turned."""
     w = W.workload("c2")
     mask = W.retrieval_mask(w)[0]
     dev = torch.device("cuda")
@@ -259,10 +262,16 @@ def prefill_leg(args, torch, hsk, W, N, mode="window", kv_bits=0):
     cache = hsk.DuoCache(num_layers=1, batch=1, num_q_heads=w.hq, num_kv_heads=w.hkv,
                          head_dim=w.d, sink=w.sink, recent=w.recent, capacity=P,
                          retrieval_mask=[mask], dtype=torch.bfloat16, out_dtype=torch.bfloat16,
-                         streaming_prefill=mode, device=dev, kv_bits=kv_bits)
+                         streaming_prefill=mode, device=dev, kv_bits=kv_bits,
+                         rope_theta=rope_theta)
     staged = kv_bits in (4, 8)
-    staging = torch.empty(2 * int(mask.sum()) * P * w.d * 2 if staged else 16,
-                          dtype=torch.uint8, device=dev)
+    # the largest staging of the pass (the last chunk's), as duo_prefill_staging_bytes gives it
+    up = lambda x: (x + 255) // 256 * 256
+    row = w.d * 2
+    need = 2 * int(mask.sum()) * P * row
+    if rope_theta:
+        need = up(need) + up(C * w.hkv * row) + int((mask == 0).sum()) * (w.sink + w.recent) * row
+    staging = torch.empty(need if staged else 16, dtype=torch.uint8, device=dev)
     q = torch.from_numpy(W.tokens(w, "q", 0, 0, 0, P)).to(dev).to(torch.bfloat16)
     k = torch.from_numpy(W.tokens(w, "k", 0, 0, 0, P)).to(dev).to(torch.bfloat16)
     v = torch.from_numpy(W.tokens(w, "v", 0, 0, 0, P)).to(dev).to(torch.bfloat16)
@@ -714,6 +723,12 @@ def main():
         log(f"prefill over a 4-bit cache: {pre_kv4['attn_ms']:.3f} ms attention (read-back "
             f"included) = {pre_kv4['tflops']:.1f} TFLOP/s; attention kernel "
             f"{pre_kv4['kern_ms']:.3f} ms = {pre_kv4['kern_tflops']:.1f} TFLOP/s")
+    pre_kv4r = None
+    if not args.no_prefill and "kv4rope" in modes:
+        pre_kv4r = prefill_leg(args, torch, hsk, W, N, kv_bits=4, rope_theta=PREFILL_ROPE_THETA)
+        log(f"prefill over a 4-bit cache with pre-RoPE keys: {pre_kv4r['attn_ms']:.3f} ms "
+            f"attention (staging included) = {pre_kv4r['tflops']:.1f} TFLOP/s; attention kernel "
+            f"{pre_kv4r['kern_ms']:.3f} ms = {pre_kv4r['kern_tflops']:.1f} TFLOP/s")
     mix = None
     if not args.no_prefill and "mixed" in modes:
         mix = gate_mixed_leg(args, torch, hsk, W, N)
@@ -887,6 +902,17 @@ def main():
             "kernel_ms_per_pass": round(pre_kv4["kern_ms"], 3),
             "kernel_tflops": round(pre_kv4["kern_tflops"], 1),
             "frac": round(pre_kv4["kern_tflops"] / BF16_PEAK_TFLOPS, 4),
+        },
+        "prefill_kv4_rope": None if pre_kv4r is None else {
+            "workload": f"{pre_kv4r['workload'].name}: 32K prompt in 4K chunks over 4-bit full "
+                        f"caches holding pre-RoPE keys (base 10,000): values read back and "
+                        f"every key the chunk reads turned, into bf16 staging per chunk",
+            "attn_ms": round(pre_kv4r["attn_ms"], 3),
+            "ms_incl_append": round(pre_kv4r["pass_ms"], 3),
+            "tflops": round(pre_kv4r["tflops"], 1),
+            "kernel_ms_per_pass": round(pre_kv4r["kern_ms"], 3),
+            "kernel_tflops": round(pre_kv4r["kern_tflops"], 1),
+            "frac": round(pre_kv4r["kern_tflops"] / BF16_PEAK_TFLOPS, 4),
         },
         "prefill_chunk_mode": None if pre_chunk is None else {
             "workload": f"{pre_chunk['workload'].name}: 32K prompt in 4K chunks, streaming heads "

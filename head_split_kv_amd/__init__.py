@@ -279,10 +279,12 @@ def duo_attn_prefill(cache: DuoCache, layer: int, seq: int, q: torch.Tensor, k: 
     return out
 
 
-def duo_prefill_staging_bytes(cache: DuoCache, layer: int, seq: int = -1) -> int:
-    """Bytes of bf16 staging ``duo_attn_prefill_staged`` needs at the current lengths."""
+def duo_prefill_staging_bytes(cache: DuoCache, layer: int, seq: int = -1,
+                              n_chunk: int = 0) -> int:
+    """Bytes of bf16 staging ``duo_attn_prefill_staged`` needs for a chunk of ``n_chunk``
+    tokens at the current lengths."""
     n = ctypes.c_uint64()
-    check(lib().duo_prefill_staging_bytes(cache.handle, layer, seq, ctypes.byref(n)),
+    check(lib().duo_prefill_staging_bytes(cache.handle, layer, seq, n_chunk, ctypes.byref(n)),
           "duo_prefill_staging_bytes")
     return n.value
 
@@ -293,7 +295,8 @@ def duo_attn_prefill_staged(cache: DuoCache, layer: int, seq: int, q: torch.Tens
     """``duo_attn_prefill`` over a 4- or 8-bit cache: the retrieval heads' earlier tokens are
     read back as bf16 rows into ``staging`` (a ``torch.uint8`` device tensor of at least
     ``duo_prefill_staging_bytes`` bytes; allocated here when None), then the chunk attends.
-    Shapes as in ``duo_attn_prefill``."""
+    With pre-RoPE keys (``rope_theta``) ``q`` is after RoPE and ``k`` before it, and the keys
+    are staged turned. Shapes as in ``duo_attn_prefill``."""
     m = q.shape[1] if seq < 0 else q.shape[0]
     lead = (cache.batch, m) if seq < 0 else (m,)
     _check_tensor(q, lead + (cache.hq, cache.d), cache.dtype, cache.device, "q")
@@ -306,7 +309,7 @@ def duo_attn_prefill_staged(cache: DuoCache, layer: int, seq: int, q: torch.Tens
     if lse is not None:
         _check_tensor(lse, lead + (cache.hq,), torch.float32, cache.device, "lse")
         lse_ptr = lse.data_ptr()
-    need = duo_prefill_staging_bytes(cache, layer, seq)
+    need = duo_prefill_staging_bytes(cache, layer, seq, m)
     if staging is None:
         staging = torch.empty(max(need, 16), dtype=torch.uint8, device=cache.device)
     check(lib().duo_attn_prefill_staged(cache.handle, layer, seq, ctypes.c_void_p(q.data_ptr()),

@@ -93,7 +93,7 @@ def lib() -> ctypes.CDLL:
         "duo_decode_step": (st, [vp, i32, vp, vp, vp, vp, vp, vp]),
         "duo_attn_prefill": (st, [vp, i32, i32, vp, vp, vp, i32, vp, vp, vp]),
         "duo_attn_prefill_staged": (st, [vp, i32, i32, vp, vp, vp, i32, vp, vp, vp, u64, vp]),
-        "duo_prefill_staging_bytes": (st, [vp, i32, i32, P(ctypes.c_uint64)]),
+        "duo_prefill_staging_bytes": (st, [vp, i32, i32, i32, P(ctypes.c_uint64)]),
         "duo_attn_gate_mixed": (st, [vp, i32, i32, vp, vp, vp, i32, P(ctypes.c_float), vp, vp]),
         "duo_slot_positions": (st, [vp, i32, P(i32), vp]),
         "duo_cache_lengths": (st, [vp, P(i32)]),

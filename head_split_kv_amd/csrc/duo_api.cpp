@@ -359,6 +359,35 @@ duo_status duo_decode_step(duo_cache* c, int32_t layer, const void* q, const voi
 
 namespace {
 
+// Staging of duo_attn_prefill_staged, byte offsets: the retrieval prefix as bf16 rows, K at 0
+// and V at pv, [nb][Hr][c_max][D] each; with pre-RoPE keys also the chunk's keys turned at
+// `chunk`, [nb][m][Hkv][D], and the layer's streaming keys turned at `str`, [B][Hs][S+R][D]
+// (indexed by sequence like the cache; only the call's sequences are written).
+struct StagingPlan {
+  uint64_t pv = 0, chunk = 0, str = 0, bytes = 0;
+  int32_t c_max = 0;
+};
+StagingPlan staging_plan(const duo_cache* c, int32_t layer, int32_t seq, int32_t n_chunk) {
+  auto up = [](uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; };
+  const int32_t b0 = seq < 0 ? 0 : seq, nb = seq < 0 ? c->cfg.batch : 1;
+  StagingPlan p;
+  for (int32_t b = b0; b < b0 + nb; ++b)
+    p.c_max = std::max(p.c_max, c->lens[(size_t)layer * c->cfg.batch + b]);
+  const uint64_t row = (uint64_t)c->cfg.head_dim * 2;
+  const LayerInfo& li = c->layers[layer];
+  const uint64_t pre = (uint64_t)nb * li.n_ret * (uint64_t)p.c_max * row;
+  p.pv = pre;
+  if (c->cfg.rope_theta > 0.f) {
+    p.chunk = up(2 * pre);
+    p.str = p.chunk + up((uint64_t)nb * n_chunk * c->cfg.num_kv_heads * row);
+    p.bytes = p.str + (uint64_t)c->cfg.batch * li.n_str *
+                          ((uint64_t)c->cfg.sink + c->cfg.recent) * row;
+  } else {
+    p.chunk = p.str = p.bytes = 2 * pre;
+  }
+  return p;
+}
+
 // Checks and launch arguments of one prefill chunk (shared by duo_attn_prefill and
 // duo_attn_gate_mixed). Returns DUO_OK with `a` filled, or the error to report.
 // staged: the caller has a bf16 read-back of a quantized layer's retrieval caches to offer
@@ -366,7 +395,9 @@ namespace {
 duo_status prefill_args(duo_cache* c, int32_t layer, int32_t seq, const void* q, const void* k,
                         const void* v, int32_t n_chunk, void* out, float* lse, PrefillArgs& a,
                         bool staged = false) {
-  if ((c->cfg.kv_bits == 4 || c->cfg.kv_bits == 8) && c->layers[layer].n_ret > 0 && !staged)
+  // quantized retrieval caches, and pre-RoPE keys on any head, are read through staging
+  if ((c->cfg.kv_bits == 4 || c->cfg.kv_bits == 8) &&
+      (c->layers[layer].n_ret > 0 || c->cfg.rope_theta > 0.f) && !staged)
     return DUO_ERR_UNSUPPORTED;
   if (!q || !k || !v || !out || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
       !aligned16(out) || !aligned4(lse))
@@ -447,15 +478,12 @@ duo_status duo_attn_prefill(duo_cache* c, int32_t layer, int32_t seq, const void
 }
 
 duo_status duo_prefill_staging_bytes(const duo_cache* c, int32_t layer, int32_t seq,
-                                     uint64_t* bytes) {
-  if (!layer_ok(c, layer) || seq < -1 || seq >= c->cfg.batch || !bytes) return DUO_ERR_INVALID;
+                                     int32_t n_chunk, uint64_t* bytes) {
+  if (!layer_ok(c, layer) || seq < -1 || seq >= c->cfg.batch || n_chunk < 0 || !bytes)
+    return DUO_ERR_INVALID;
   *bytes = 0;
   if (c->cfg.kv_bits != 4 && c->cfg.kv_bits != 8) return DUO_OK;
-  const int32_t b0 = seq < 0 ? 0 : seq, nb = seq < 0 ? c->cfg.batch : 1;
-  int32_t c_max = 0;
-  for (int32_t b = b0; b < b0 + nb; ++b)
-    c_max = std::max(c_max, c->lens[(size_t)layer * c->cfg.batch + b]);
-  *bytes = 2ull * nb * c->layers[layer].n_ret * (uint64_t)c_max * c->cfg.head_dim * 2;
+  *bytes = staging_plan(c, layer, seq, n_chunk).bytes;
   return DUO_OK;
 }
 
@@ -467,41 +495,57 @@ duo_status duo_attn_prefill_staged(duo_cache* c, int32_t layer, int32_t seq, con
     return DUO_ERR_INVALID;
   const bool quant = c->cfg.kv_bits == 4 || c->cfg.kv_bits == 8;
   if (!quant) return duo_attn_prefill(c, layer, seq, q, k, v, n_chunk, out, lse, stream);
-  if (c->cfg.rope_theta > 0.f) return DUO_ERR_UNSUPPORTED;
-  uint64_t need = 0;
-  if (duo_prefill_staging_bytes(c, layer, seq, &need) != DUO_OK) return DUO_ERR_INVALID;
-  if (need > 0 && (!staging || !aligned16(staging) || staging_bytes < need)) return DUO_ERR_INVALID;
+  const bool rope = c->cfg.rope_theta > 0.f;
+  const StagingPlan sp = staging_plan(c, layer, seq, n_chunk);
+  if (sp.bytes > 0 && (!staging || !aligned16(staging) || staging_bytes < sp.bytes))
+    return DUO_ERR_INVALID;
   if (n_chunk == 0) return DUO_OK;
   PrefillArgs a;
   const duo_status st = prefill_args(c, layer, seq, q, k, v, n_chunk, out, lse, a, true);
   if (st != DUO_OK) return st;
-  // the prefix of every retrieval head, read back as bf16 rows [nb][Hr][c_max][D] (K, then V)
-  int32_t c_max = 0;
-  for (int32_t i = 0; i < a.nb; ++i) c_max = std::max(c_max, a.c0[i]);
-  const uint64_t half = need / 2;
-  if (need > 0) {
-    const Q4Geom g = q4_geom(c->cfg.capacity, c->cfg.head_dim, c->cfg.kv_bits);
-    DequantArgs d;
-    std::memset(&d, 0, sizeof(d));
-    d.full_k = a.full_k;
-    d.full_v = a.full_v;
-    d.out_k = staging;
-    d.out_v = (char*)staging + half;
-    d.q4_stride = (int64_t)g.stride;
-    d.q4_params = (int64_t)g.codes;
-    d.q4_resid = (int64_t)(g.codes + g.params);
-    d.qbits = c->cfg.kv_bits;
-    d.b0 = a.b0;
-    d.nb = a.nb;
-    d.Hr = a.Hr;
-    d.cap_s = c_max;
-    std::memcpy(d.c0, a.c0, sizeof(d.c0));
-    if (launch_dequant_kv4(d, c->cfg.head_dim, stream) != 0) return DUO_ERR_HIP;
+  char* stg = (char*)staging;
+  const Q4Geom g = q4_geom(c->cfg.capacity, c->cfg.head_dim, c->cfg.kv_bits);
+  DequantArgs d;
+  std::memset(&d, 0, sizeof(d));
+  d.full_k = a.full_k;
+  d.full_v = a.full_v;
+  d.out_k = stg;
+  d.out_v = stg + sp.pv;
+  d.q4_stride = (int64_t)g.stride;
+  d.q4_params = (int64_t)g.codes;
+  d.q4_resid = (int64_t)(g.codes + g.params);
+  d.qbits = c->cfg.kv_bits;
+  d.b0 = a.b0;
+  d.nb = a.nb;
+  d.Hr = a.Hr;
+  d.cap_s = sp.c_max;
+  std::memcpy(d.c0, a.c0, sizeof(d.c0));
+  if (rope) {
+    d.rope_base = rope_ptrs(c).base;
+    d.log2_theta = (float)std::log2((double)c->cfg.rope_theta);
+    d.chunk_k = k;
+    d.out_chunk_k = stg + sp.chunk;
+    d.m = n_chunk;
+    d.Hkv = a.Hkv;
+    d.str_k = a.str_k;
+    d.out_str_k = stg + sp.str;
+    d.Hs = a.Hs;
+    d.S = a.S;
+    d.R = a.R;
   }
-  a.full_k = staging;
-  a.full_v = (char*)staging + half;
-  a.cap = c_max;
+  // the prefix of every retrieval head read back as bf16 rows (values only with pre-RoPE
+  // keys), then, with pre-RoPE keys, every key the chunk attends to turned at its position
+  if (a.Hr > 0 && sp.c_max > 0 && launch_dequant_kv4(d, c->cfg.head_dim, stream) != 0)
+    return DUO_ERR_HIP;
+  if (rope && launch_rope_stage(d, c->cfg.head_dim, stream) != 0) return DUO_ERR_HIP;
+  a.full_k = stg;
+  a.full_v = stg + sp.pv;
+  a.cap = sp.c_max;
   a.full_b0 = a.b0;
+  if (rope) {
+    a.k = stg + sp.chunk;
+    a.str_k = stg + sp.str;
+  }
   const int group = c->cfg.num_q_heads / c->cfg.num_kv_heads;
   return launch_status(launch_prefill(a, c->cfg.dtype, c->cfg.head_dim, group, stream,
                                       next_marks(c, DUO_TIMING_PREFILL)));

@@ -196,8 +196,20 @@ struct DequantArgs {
   int64_t q4_stride, q4_params, q4_resid;  // Q4Geom of the regions
   int32_t qbits, b0, nb, Hr, cap_s;
   int32_t c0[kMaxBatch];
+  // Pre-RoPE caches (rope_base set): launch_dequant_kv4 reads back the values only, and
+  // launch_rope_stage writes every key the chunk attends to, turned at its position: the
+  // retrieval prefix into out_k, the chunk's keys into out_chunk_k, the held streaming slots
+  // into out_str_k.
+  const float* rope_base;  // RopeGeom base table: (cos, sin) of 128 g f_i, float32
+  float log2_theta;        // f_i = 2^(-(2 i / D) log2_theta)
+  const void* chunk_k;     // the chunk's keys as given, [nb][m][Hkv][D]
+  void* out_chunk_k;       // [nb][m][Hkv][D]
+  const void* str_k;       // this layer's streaming keys, [B][Hs][S + R][D]
+  void* out_str_k;         // [B][Hs][S + R][D], rows of sequences b0 .. b0 + nb - 1
+  int32_t m, Hkv, Hs, S, R;
 };
 int launch_dequant_kv4(const DequantArgs& a, int head_dim, void* stream);
+int launch_rope_stage(const DequantArgs& a, int head_dim, void* stream);
 int launch_set_lengths(const SetLenArgs& a, void* stream);
 int launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group, void* stream,
                   const KernelMarks& marks);

@@ -226,15 +226,64 @@ __global__ void __launch_bounds__(kThreads) kv4_append_kernel(AppendArgs a) {
   quantize(g);
 }
 
+// 8 channels c0 .. c0 + 7 of key t of a retrieval head whose group is complete, read back
+// through the key layout above: c * scale + zero in float32 (c * scale is exact: at most 8 + 8
+// significant bits; one rounding for the sum).
+template <int D, int BITS>
+__device__ __forceinline__ void key_values8(const char* head, int64_t q4_params, int t, int c0,
+                                            float val[8]) {
+  constexpr int KC = D / 32;
+  const int g = t / kG;
+  const uint16_t* par = (const uint16_t*)(head + q4_params) + (int64_t)g * 2 * D;
+  const uint4 sv = *(const uint4*)(par + c0), zv = *(const uint4*)(par + D + c0);
+  const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w}, zw[4] = {zv.x, zv.y, zv.z, zv.w};
+  const uint32_t* row = (const uint32_t*)(head + (int64_t)t * (D * BITS / 8));
+  const int k = c0 / 32, j = (c0 % 32) / 8;
+  uint32_t code[8];
+  if constexpr (BITS == 4) {
+    const uint32_t cw = row[KC * j + k];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) code[e] = (cw >> (4 * e)) & 15u;
+  } else {
+    const uint2 cw = *(const uint2*)(row + 2 * KC * j + 2 * k);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) code[e] = ((e < 4 ? cw.x : cw.y) >> (8 * (e & 3))) & 255u;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t sb = (e & 1) ? sw[e >> 1] >> 16 : sw[e >> 1] & 0xFFFFu;
+    const uint32_t zb = (e & 1) ? zw[e >> 1] >> 16 : zw[e >> 1] & 0xFFFFu;
+    val[e] = __builtin_fmaf((float)code[e], bf16_to_f32((uint16_t)sb), bf16_to_f32((uint16_t)zb));
+  }
+}
+
+__device__ __forceinline__ void bf16x8_to_f32(uint4 w, float val[8]) {
+  const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    val[2 * i] = __builtin_bit_cast(float, ww[i] << 16);
+    val[2 * i + 1] = __builtin_bit_cast(float, ww[i] & 0xFFFF0000u);
+  }
+}
+
+__device__ __forceinline__ uint4 f32x8_to_bf16(const float val[8]) {
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = (uint32_t)f32_to_bf16_bits(val[2 * i]) | ((uint32_t)f32_to_bf16_bits(val[2 * i + 1]) << 16);
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 // Read-back into bf16 rows (DequantArgs): one thread per (K or V, sequence, head, token, 8
 // channels), reading the codes through the layouts above. A value is c * scale + zero in
-// float32 (c * scale is exact: at most 8 + 8 significant bits; one rounding for the sum),
-// rounded to bf16 to nearest even.
+// float32, rounded to bf16 to nearest even. With a.rope_base set only the values are read
+// back here (launch_rope_stage writes the keys).
 template <int D, int BITS>
 __global__ void __launch_bounds__(kThreads) kv4_dequant_kernel(DequantArgs a) {
-  constexpr int CH = D / 8, KC = D / 32;
+  constexpr int CH = D / 8;
   const int64_t per_tensor = (int64_t)a.nb * a.Hr * a.cap_s * CH;
-  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < 2 * per_tensor;
+  const int64_t u0 = a.rope_base ? per_tensor : 0;
+  for (int64_t u = u0 + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < 2 * per_tensor;
        u += (int64_t)gridDim.x * blockDim.x) {
     const bool is_v = u >= per_tensor;
     int64_t w = is_v ? u - per_tensor : u;
@@ -257,27 +306,7 @@ __global__ void __launch_bounds__(kThreads) kv4_dequant_kernel(DequantArgs a) {
     const int g = t / kG, tt = t % kG, c0 = 8 * x;
     float val[8];
     if (!is_v) {  // per-channel scale and zero of the group
-      const uint16_t* par = (const uint16_t*)(head + a.q4_params) + (int64_t)g * 2 * D;
-      const uint4 sv = *(const uint4*)(par + c0), zv = *(const uint4*)(par + D + c0);
-      const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w}, zw[4] = {zv.x, zv.y, zv.z, zv.w};
-      const uint32_t* row = (const uint32_t*)(head + (int64_t)t * (D * BITS / 8));
-      const int k = c0 / 32, j = (c0 % 32) / 8;
-      uint32_t code[8];
-      if constexpr (BITS == 4) {
-        const uint32_t cw = row[KC * j + k];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) code[e] = (cw >> (4 * e)) & 15u;
-      } else {
-        const uint2 cw = *(const uint2*)(row + 2 * KC * j + 2 * k);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) code[e] = ((e < 4 ? cw.x : cw.y) >> (8 * (e & 3))) & 255u;
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t sb = (e & 1) ? sw[e >> 1] >> 16 : sw[e >> 1] & 0xFFFFu;
-        const uint32_t zb = (e & 1) ? zw[e >> 1] >> 16 : zw[e >> 1] & 0xFFFFu;
-        val[e] = __builtin_fmaf((float)code[e], bf16_to_f32((uint16_t)sb), bf16_to_f32((uint16_t)zb));
-      }
+      key_values8<D, BITS>(head, a.q4_params, t, c0, val);
     } else {  // per-token scale and zero
       const uint32_t pw = ((const uint32_t*)(head + a.q4_params))[t];
       const float sc = bf16_to_f32((uint16_t)(pw & 0xFFFFu)), ze = bf16_to_f32((uint16_t)(pw >> 16));
@@ -299,18 +328,111 @@ __global__ void __launch_bounds__(kThreads) kv4_dequant_kernel(DequantArgs a) {
         val[e] = __builtin_fmaf((float)code, sc, ze);
       }
     }
-    uint32_t o[4];
+    *dst = f32x8_to_bf16(val);
+  }
+}
+
+// Keys of a pre-RoPE cache turned at their positions into bf16 staging (DequantArgs with
+// rope_base set; OpenReview thread, the authors' reply on KV quantization: keys quantized
+// before RoPE). RoPE in its rotate-half form: channels i and i + D/2 turn by t f_i,
+// f_i = theta^(-2 i / D). One thread per (row, 8 pairs): pairs 8 x .. 8 x + 7 of one key row,
+// from three sources in turn: the retrieval heads' earlier tokens (dequantized as in
+// kv4_dequant_kernel, or residual rows), the chunk's keys as given (position c0 + i), and the
+// held streaming slots (slot s < S holds position s, a ring slot the latest t < c0 with
+// t = s (mod R) past the sinks). The angle of position t = 128 g + tau is composed from the
+// base table's (cos, sin) of 128 g f_i (float32 from float64) and sincosf(tau f_i), where
+// tau f_i < 128 keeps the float32 argument accurate; the pair turns in float32 and each result
+// is rounded to bf16 to nearest even.
+template <int D, int BITS>
+__global__ void __launch_bounds__(kThreads) kv4_rope_stage_kernel(DequantArgs a) {
+  constexpr int HX = D / 16;  // pieces of 8 pairs per row
+  constexpr int H = D / 2;
+  const int SR = a.S + a.R;
+  const int64_t n_pre = (int64_t)a.nb * a.Hr * a.cap_s * HX;
+  const int64_t n_chunk = (int64_t)a.nb * a.m * a.Hkv * HX;
+  const int64_t n_str = (int64_t)a.nb * a.Hs * SR * HX;
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < n_pre + n_chunk + n_str;
+       u += (int64_t)gridDim.x * blockDim.x) {
+    float x1[8], x2[8];
+    uint16_t* dst;
+    int pos, x;
+    if (u < n_pre) {
+      int64_t w = u;
+      x = (int)(w % HX);
+      w /= HX;
+      const int t = (int)(w % a.cap_s);
+      w /= a.cap_s;
+      const int r = (int)(w % a.Hr);
+      const int bi = (int)(w / a.Hr);
+      const int n = a.c0[bi];
+      if (t >= n) continue;
+      const char* head = (const char*)a.full_k + ((int64_t)(a.b0 + bi) * a.Hr + r) * a.q4_stride;
+      dst = (uint16_t*)a.out_k + (((int64_t)bi * a.Hr + r) * a.cap_s + t) * D;
+      if (t >= (n / kG) * kG) {  // residual row
+        const uint16_t* row = (const uint16_t*)(head + a.q4_resid) + (int64_t)(t % kG) * D;
+        bf16x8_to_f32(*(const uint4*)(row + 8 * x), x1);
+        bf16x8_to_f32(*(const uint4*)(row + H + 8 * x), x2);
+      } else {
+        key_values8<D, BITS>(head, a.q4_params, t, 8 * x, x1);
+        key_values8<D, BITS>(head, a.q4_params, t, H + 8 * x, x2);
+      }
+      pos = t;
+    } else if (u < n_pre + n_chunk) {
+      int64_t w = u - n_pre;
+      x = (int)(w % HX);
+      w /= HX;
+      const int j = (int)(w % a.Hkv);
+      w /= a.Hkv;
+      const int i = (int)(w % a.m);
+      const int bi = (int)(w / a.m);
+      const int64_t off = (((int64_t)bi * a.m + i) * a.Hkv + j) * D;
+      const uint16_t* row = (const uint16_t*)a.chunk_k + off;
+      bf16x8_to_f32(*(const uint4*)(row + 8 * x), x1);
+      bf16x8_to_f32(*(const uint4*)(row + H + 8 * x), x2);
+      dst = (uint16_t*)a.out_chunk_k + off;
+      pos = a.c0[bi] + i;
+    } else {
+      int64_t w = u - n_pre - n_chunk;
+      x = (int)(w % HX);
+      w /= HX;
+      const int s = (int)(w % SR);
+      w /= SR;
+      const int cls = (int)(w % a.Hs);
+      const int bi = (int)(w / a.Hs);
+      const int n = a.c0[bi];
+      if (s >= n) continue;  // an empty slot: never read
+      const int64_t off = (((int64_t)(a.b0 + bi) * a.Hs + cls) * SR + s) * D;
+      const uint16_t* row = (const uint16_t*)a.str_k + off;
+      bf16x8_to_f32(*(const uint4*)(row + 8 * x), x1);
+      bf16x8_to_f32(*(const uint4*)(row + H + 8 * x), x2);
+      dst = (uint16_t*)a.out_str_k + off;
+      pos = s < a.S ? s : s + a.R * ((n - 1 - s) / a.R);
+    }
+    const int g = pos / kG, tau = pos % kG;
+    const float2* base = (const float2*)a.rope_base + (int64_t)g * H + 8 * x;
+    float y1[8], y2[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      o[i] = (uint32_t)f32_to_bf16_bits(val[2 * i]) | ((uint32_t)f32_to_bf16_bits(val[2 * i + 1]) << 16);
-    *dst = make_uint4(o[0], o[1], o[2], o[3]);
+    for (int e = 0; e < 8; ++e) {
+      const int i = 8 * x + e;
+      const float f = exp2f(-(float)(2 * i) / (float)D * a.log2_theta);
+      float st, ct;
+      sincosf((float)tau * f, &st, &ct);
+      const float2 b = base[e];
+      const float c = b.x * ct - b.y * st;
+      const float sn = b.y * ct + b.x * st;
+      y1[e] = x1[e] * c - x2[e] * sn;
+      y2[e] = x1[e] * sn + x2[e] * c;
+    }
+    *(uint4*)(dst + 8 * x) = f32x8_to_bf16(y1);
+    *(uint4*)(dst + H + 8 * x) = f32x8_to_bf16(y2);
   }
 }
 
 }  // namespace
 
 int launch_dequant_kv4(const DequantArgs& a, int head_dim, void* stream) {
-  const int64_t work = 2 * (int64_t)a.nb * a.Hr * a.cap_s * (head_dim / 8);
+  // K and V, or V alone for a pre-RoPE cache
+  const int64_t work = (a.rope_base ? 1 : 2) * (int64_t)a.nb * a.Hr * a.cap_s * (head_dim / 8);
   if (work == 0) return 0;
   int64_t blocks = (work + kThreads - 1) / kThreads;
   if (blocks > 16384) blocks = 16384;
@@ -324,6 +446,28 @@ int launch_dequant_kv4(const DequantArgs& a, int head_dim, void* stream) {
     hipLaunchKernelGGL((kv4_dequant_kernel<128, 8>), grid, block, 0, st, a);
   else if (head_dim == 64 && a.qbits == 8)
     hipLaunchKernelGGL((kv4_dequant_kernel<64, 8>), grid, block, 0, st, a);
+  else
+    return -1;
+  return (int)hipGetLastError();
+}
+
+int launch_rope_stage(const DequantArgs& a, int head_dim, void* stream) {
+  const int64_t rows = (int64_t)a.nb * a.Hr * a.cap_s + (int64_t)a.nb * a.m * a.Hkv +
+                       (int64_t)a.nb * a.Hs * (a.S + a.R);
+  const int64_t work = rows * (head_dim / 16);
+  if (work == 0) return 0;
+  int64_t blocks = (work + kThreads - 1) / kThreads;
+  if (blocks > 16384) blocks = 16384;
+  const dim3 grid((unsigned)blocks), block(kThreads);
+  hipStream_t st = (hipStream_t)stream;
+  if (head_dim == 128 && a.qbits == 4)
+    hipLaunchKernelGGL((kv4_rope_stage_kernel<128, 4>), grid, block, 0, st, a);
+  else if (head_dim == 64 && a.qbits == 4)
+    hipLaunchKernelGGL((kv4_rope_stage_kernel<64, 4>), grid, block, 0, st, a);
+  else if (head_dim == 128 && a.qbits == 8)
+    hipLaunchKernelGGL((kv4_rope_stage_kernel<128, 8>), grid, block, 0, st, a);
+  else if (head_dim == 64 && a.qbits == 8)
+    hipLaunchKernelGGL((kv4_rope_stage_kernel<64, 8>), grid, block, 0, st, a);
   else
     return -1;
   return (int)hipGetLastError();

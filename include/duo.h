@@ -129,7 +129,8 @@ typedef struct {
  * keeps the keys as given: a retrieval head's codes, scales and zeros are taken of them, and
  * decoding rotates each dequantized key, each residual row and each streaming slot at the
  * position it holds. Values are never rotated. The cos/sin tables live in the arena (layout.rope_off) and are
- * written by duo_cache_reset. */
+ * written by duo_cache_reset. Pre-filling goes through duo_attn_prefill_staged, which stages
+ * every key the chunk reads turned (duo_attn_prefill returns DUO_ERR_UNSUPPORTED). */
 
 /* Byte offsets inside the caller's arena (all 256-byte aligned). Inside each cache region
  * the layers follow one another in order, each starting on a 256-byte boundary. */
@@ -242,20 +243,30 @@ duo_status duo_attn_prefill(duo_cache* cache, int32_t layer, int32_t seq, const 
  * bf16(float32(c * scale + zero)) and residual rows as stored, [nb][Hr][c_max][d] for K then
  * the same for V (nb = 1, or B when seq = -1; Hr the layer's retrieval heads; c_max the
  * longest current length among the sequences); the chunk then attends as in duo_attn_prefill,
- * its own keys and values exact. staging: caller-owned device memory, 16-byte aligned, at
- * least duo_prefill_staging_bytes bytes (else DUO_ERR_INVALID); its contents are scratch.
- * On a dtype cache this is duo_attn_prefill (staging unused). DUO_ERR_UNSUPPORTED with
- * cfg.rope_theta > 0. */
+ * its own keys and values exact.
+ * With cfg.rope_theta > 0 (pre-RoPE keys; OpenReview thread, the authors' reply on KV
+ * quantization) q holds the chunk's queries after RoPE and k its keys before RoPE, as
+ * appended. Every key the chunk attends to is then staged turned at its own position t
+ * (rotate-half pairs (i, i + d/2) by t theta^(-2i/d), in float32) and rounded to bf16: the
+ * retrieval prefix after its read-back, the chunk's keys into [nb][m][Hkv][d], and the held
+ * streaming slots into [B][Hs][S+R][d]. Values are staged as without RoPE.
+ * staging: caller-owned device memory, 16-byte aligned, at least
+ * duo_prefill_staging_bytes(.., n_chunk, ..) bytes (else DUO_ERR_INVALID); its contents are
+ * scratch. On a dtype cache this is duo_attn_prefill (staging unused). On a 4- or 8-bit cache
+ * duo_attn_prefill itself returns DUO_ERR_UNSUPPORTED for layers with retrieval heads, and
+ * for every layer with cfg.rope_theta > 0. */
 duo_status duo_attn_prefill_staged(duo_cache* cache, int32_t layer, int32_t seq, const void* q,
                                    const void* k, const void* v, int32_t n_chunk, void* out,
                                    float* lse, void* staging, uint64_t staging_bytes,
                                    void* stream);
 
-/* Bytes of staging duo_attn_prefill_staged needs for this layer and seq (-1 = all sequences)
- * at the cache's current lengths: 2 * nb * Hr * c_max * d * 2 on a 4- or 8-bit cache, 0
- * otherwise. Host only. */
+/* Bytes of staging duo_attn_prefill_staged needs for this layer, seq (-1 = all sequences) and
+ * a chunk of n_chunk tokens at the cache's current lengths: 2 * nb * Hr * c_max * d * 2 on a
+ * 4- or 8-bit cache (0 on a dtype cache); with cfg.rope_theta > 0 that rounded up to 256 bytes,
+ * plus nb * n_chunk * Hkv * d * 2 rounded up to 256, plus B * Hs * (S + R) * d * 2.
+ * DUO_ERR_INVALID for a bad layer or seq, n_chunk < 0 or a null `bytes`. Host only. */
 duo_status duo_prefill_staging_bytes(const duo_cache* cache, int32_t layer, int32_t seq,
-                                     uint64_t* bytes);
+                                     int32_t n_chunk, uint64_t* bytes);
 
 /* Gate-mixed attention of one chunk, the attention of the retrieval-head identification phase
  * (explainer, "Gate Parameterization"): every query head h of KV head j = h / G returns

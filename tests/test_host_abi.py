@@ -304,28 +304,46 @@ def test_error_paths_leave_state_unchanged():
 
 
 def test_prefill_staged_checks_before_launch():
-    """duo_prefill_staging_bytes: 0 on a dtype cache and on empty caches, argument checks;
-    duo_attn_prefill_staged: rejects bad arguments and pre-RoPE caches before launching."""
+    """duo_prefill_staging_bytes: 0 on a dtype cache and on empty caches without RoPE, the
+    chunk and streaming regions with pre-RoPE keys, argument checks; duo_attn_prefill_staged
+    rejects bad arguments and short staging before launching; duo_attn_prefill refuses every
+    layer of a pre-RoPE cache, streaming-only layers included."""
     L = N.lib()
     n = ctypes.c_uint64(7)
+    p = ctypes.c_void_p(1 << 40)
     for bits in (0, 4, 8):
         fc = FakeCache(kv_bits=bits)
-        assert L.duo_prefill_staging_bytes(fc.h, 0, -1, ctypes.byref(n)) == N.DUO_OK
+        assert L.duo_prefill_staging_bytes(fc.h, 0, -1, 5, ctypes.byref(n)) == N.DUO_OK
         assert n.value == 0
-        assert L.duo_prefill_staging_bytes(fc.h, 2, -1, ctypes.byref(n)) == N.DUO_ERR_INVALID
-        assert L.duo_prefill_staging_bytes(fc.h, 0, 3, ctypes.byref(n)) == N.DUO_ERR_INVALID
-        assert L.duo_prefill_staging_bytes(fc.h, 0, -1, None) == N.DUO_ERR_INVALID
-        p = ctypes.c_void_p(1 << 40)
+        assert L.duo_prefill_staging_bytes(fc.h, 2, -1, 5, ctypes.byref(n)) == N.DUO_ERR_INVALID
+        assert L.duo_prefill_staging_bytes(fc.h, 0, 3, 5, ctypes.byref(n)) == N.DUO_ERR_INVALID
+        assert L.duo_prefill_staging_bytes(fc.h, 0, -1, -1, ctypes.byref(n)) == N.DUO_ERR_INVALID
+        assert L.duo_prefill_staging_bytes(fc.h, 0, -1, 5, None) == N.DUO_ERR_INVALID
         assert L.duo_attn_prefill_staged(fc.h, 0, -2, p, p, p, 4, p, None, p, 0,
                                          None) == N.DUO_ERR_INVALID
         assert L.duo_attn_prefill_staged(fc.h, 0, -1, p, p, p, -1, p, None, p, 0,
                                          None) == N.DUO_ERR_INVALID
         fc.close()
-    fc = FakeCache(kv_bits=4, rope_theta=10000.0)
-    p = ctypes.c_void_p(1 << 40)
-    assert L.duo_attn_prefill_staged(fc.h, 0, -1, p, p, p, 4, p, None, p, 1 << 20,
-                                     None) == N.DUO_ERR_UNSUPPORTED
-    fc.close()
+    # pre-RoPE keys: B 3, Hkv 2 (layer 0: one retrieval, one streaming head; layer 1: two
+    # streaming heads), d 128, S + R = 20, empty caches: the chunk's keys, then the streaming
+    # keys of every sequence
+    row = 128 * 2
+    up = lambda x: (x + 255) // 256 * 256
+    for bits in (4, 8):
+        fc = FakeCache(kv_bits=bits, rope_theta=10000.0, retrieval_mask=[[1, 0], [0, 0]])
+        for layer, hs in ((0, 1), (1, 2)):
+            for seq, nb in ((-1, 3), (1, 1)):
+                assert L.duo_prefill_staging_bytes(fc.h, layer, seq, 5, ctypes.byref(n)) == 0
+                assert n.value == up(nb * 5 * 2 * row) + 3 * hs * 20 * row
+            need = up(3 * 5 * 2 * row) + 3 * hs * 20 * row
+            assert L.duo_attn_prefill_staged(fc.h, layer, -1, p, p, p, 5, p, None, p, need - 16,
+                                             None) == N.DUO_ERR_INVALID
+            assert L.duo_attn_prefill_staged(fc.h, layer, -1, p, p, p, 5, p, None, None, need,
+                                             None) == N.DUO_ERR_INVALID
+            assert L.duo_attn_prefill(fc.h, layer, -1, p, p, p, 5, p, None,
+                                      None) == N.DUO_ERR_UNSUPPORTED
+        fc.close()
+
 
 
 def test_read_probe_rejects_bad_arguments():
