@@ -508,6 +508,12 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // where kCodeHigh is set.
 constexpr int kCodeOrder[8] = {0, 4, 1, 5, 2, 6, 3, 7};
 constexpr bool kCodeHigh[8] = {false, false, true, true, false, false, true, true};
+constexpr bool code_tables_match() {  // the closed forms the query fill uses
+  for (int e = 0; e < 8; ++e)
+    if (kCodeOrder[e] != (e >> 1) + 4 * (e & 1) || kCodeHigh[e] != ((e & 2) != 0)) return false;
+  return true;
+}
+static_assert(code_tables_match(), "slot order: x = e / 2 + 4 (e % 2), high nibble where e & 2");
 // (element x sits in slot 2 (x mod 4) + x / 4, the inverse of kCodeOrder)
 constexpr float kTwo24 = 16777216.f;
 __device__ __forceinline__ half8_t codes_to_f16(uint32_t w) {
@@ -571,7 +577,11 @@ __global__ void __launch_bounds__(kThreads, (kRope || BITS == 8) ? 1 : 2)
   __shared__ float s_o[2 * kWaves][G][D];  // partials: bf16 path per wave, then MFMA path
   __shared__ float s_m[2 * kWaves][G];
   __shared__ float s_l[2 * kWaves][G];
-  __shared__ __attribute__((aligned(16))) uint16_t s_q[G][D];
+  // the G query rows in bf16, then a zero row that the padding columns read
+  __shared__ __attribute__((aligned(16))) uint16_t s_q[G + 1][D];
+  // the query in float32 in operand slot order (slot e of the 8-channel block at 8 b holds
+  // channel 8 b + kCodeOrder[e]), over 16 in the high-nibble slots of 4-bit codes; row G zero
+  __shared__ __attribute__((aligned(16))) float s_qf[kRope ? 1 : G + 1][kRope ? 4 : D];
   __shared__ __attribute__((aligned(16))) uint32_t s_rot[kRope ? kQ4Group * kRotRow : 4];
 
   const int tid = threadIdx.x;
@@ -668,6 +678,10 @@ __global__ void __launch_bounds__(kThreads, (kRope || BITS == 8) ? 1 : 2)
   float mq = live ? kMInit : 1e30f;
   float thq = live ? kMInit : __builtin_inff();
   float lq = 0.f, zq = 0.f;
+  // The logit products accumulate without the group's key-zero term (bias): the threshold is
+  // compared as thb = thq - bias, and the weight of a product x is exp2(x c2s + nb) with
+  // nb = bias c2s - mq (both set by fold() and on a rescale).
+  float thb = thq, nb = -mq;
   // logit (log2 units) per unit of the raw product (codes read as multiples of 2^-24, or the
   // turned keys in real units)
   const float c2s = kRope ? c2 : c2 * kTwo24;
@@ -763,32 +777,40 @@ __global__ void __launch_bounds__(kThreads, (kRope || BITS == 8) ? 1 : 2)
           }
         }
         bias = 0.f;
+        thb = thq;
+        nb = -mq;
         return;
       }
       float bp = 0.f;  // this lane's part of query col's bias
-      const float qlive = live ? 1.f : 0.f;
+      const int qrow = live ? col : G;  // padding columns read the zero row
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        // channels 32 kc + 8 jj + 0..7 of query col, one 16-byte read
-        const uint4 qv = *(const uint4*)&s_q[live ? col : 0][32 * kc + 8 * jj];
+        // channels 32 kc + 8 jj + 0..7 of query col: bf16 in channel order (one 16-byte
+        // read) for the zero term, float32 in slot order (two reads) for the scaled operand
+        const uint4 qv = *(const uint4*)&s_q[qrow][32 * kc + 8 * jj];
+        const float4 f0 = *(const float4*)&s_qf[qrow][32 * kc + 8 * jj];
+        const float4 f1 = *(const float4*)&s_qf[qrow][32 * kc + 8 * jj + 4];
+        const float qs[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
         const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
         const uint32_t sw[4] = {ps[kc].x, ps[kc].y, ps[kc].z, ps[kc].w};
         const uint32_t zw[4] = {pz[kc].x, pz[kc].y, pz[kc].z, pz[kc].w};
+        // zero term: channel pairs (2 i, 2 i + 1) of the query and of the zeros
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          bp = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw[i]),
+                                               __builtin_bit_cast(bf16x2_t, zw[i]), bp, false);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int x = kCodeOrder[e];  // channel 32 kc + 8 jj + x in operand slot e
-          const uint32_t hq = (x & 1) ? qw[x >> 1] & 0xFFFF0000u : qw[x >> 1] << 16;
           const uint32_t hs = (x & 1) ? sw[x >> 1] & 0xFFFF0000u : sw[x >> 1] << 16;
-          const uint32_t hz = (x & 1) ? zw[x >> 1] & 0xFFFF0000u : zw[x >> 1] << 16;
-          const float qf = qlive * __builtin_bit_cast(float, hq);
-          qa[kc][e] = (_Float16)(qf * __builtin_bit_cast(float, hs) *
-                                 ((BITS == 4 && kCodeHigh[e]) ? 0.0625f : 1.f));
-          bp = __builtin_fmaf(qf, __builtin_bit_cast(float, hz), bp);
+          qa[kc][e] = (_Float16)(qs[e] * __builtin_bit_cast(float, hs));
         }
       }
       bp = xor16_sum(bp);
       bp = xor32_sum(bp);
       bias = bp * (1.f / kTwo24);  // the product accumulates in units of 2^-24
+      thb = thq - bias;
+      nb = bias * c2s - mq;
     };
     struct Ld {
       uint32_t k[2][KW];  // key code words of the two 16-token tiles
@@ -845,7 +867,7 @@ __global__ void __launch_bounds__(kThreads, (kRope || BITS == 8) ? 1 : 2)
       f32x4_t sacc[2];
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau) {
-        sacc[tau] = f32x4_t{bias, bias, bias, bias};
+        sacc[tau] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         if constexpr (kRope) {
           // token 32 st + 16 tau + col of the group: dequantize its channels in packed fp16,
           // turn pair (i, i + D/2) by its angle, feed the turned keys
@@ -912,11 +934,11 @@ __global__ void __launch_bounds__(kThreads, (kRope || BITS == 8) ? 1 : 2)
       for (int i = 1; i < 4; ++i) lm = fmaxf(lm, sacc[0][i]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) lm = fmaxf(lm, sacc[1][i]);
-      if (__ballot(lm > thq) != 0) {  // rare
+      if (__ballot(lm > thb) != 0) {  // rare
         float cm = xor16_max(lm);
         cm = xor32_max(cm);
-        if (cm > thq) {
-          const float mn = cm * c2s;
+        if (cm > thb) {
+          const float mn = (cm + bias) * c2s;
           const float al = fexp2(mq - mn);
           lq *= al;
           zq *= al;
@@ -924,6 +946,8 @@ __global__ void __launch_bounds__(kThreads, (kRope || BITS == 8) ? 1 : 2)
           for (int cb = 0; cb < CBK; ++cb) oacc[cb] *= al;
           mq = mn;
           thq = (mn + kTau) * inv_c2s;
+          thb = thq - bias;
+          nb = bias * c2s - mq;
         }
       }
       // element x of a value word is token 16 (x / 4) + 4 jj + x % 4 and sits in operand slot
@@ -933,7 +957,7 @@ __global__ void __launch_bounds__(kThreads, (kRope || BITS == 8) ? 1 : 2)
       for (int x = 0; x < 8; ++x) {
         const int tau = x >> 2, i = x & 3;
         const uint32_t w = f.vp[tau][i];
-        const float p = fexp2(__builtin_fmaf(sacc[tau][i], c2s, -mq));
+        const float p = fexp2(__builtin_fmaf(sacc[tau][i], c2s, nb));
         lq += p;
         zq = __builtin_fmaf(p, __builtin_bit_cast(float, w & 0xFFFF0000u), zq);
         pb[2 * i + tau] = (_Float16)(p * __builtin_bit_cast(float, w << 16) *
@@ -955,8 +979,18 @@ __global__ void __launch_bounds__(kThreads, (kRope || BITS == 8) ? 1 : 2)
     // group's loads.
     {
       const uint32_t* qw = (const uint32_t*)((const char*)a.q + ((int64_t)b * a.Hq + h0) * RB);
-      for (int w = tid; w < G * D / 2; w += kThreads)
-        reinterpret_cast<uint32_t*>(&s_q[0][0])[w] = qw[w];
+      for (int w = tid; w < (G + 1) * D / 2; w += kThreads)
+        reinterpret_cast<uint32_t*>(&s_q[0][0])[w] = w < G * D / 2 ? qw[w] : 0u;
+      if constexpr (!kRope) {
+        const uint16_t* qh = (const uint16_t*)qw;
+        for (int i = tid; i < (G + 1) * D; i += kThreads) {
+          const int row = i / D, e = i % 8;
+          const int ch = (i % D - e) + (e >> 1) + 4 * (e & 1);  // kCodeOrder[e]
+          const float hs = (BITS == 4 && (e & 2)) ? 0.0625f : 1.f;  // kCodeHigh[e]
+          s_qf[row][i % D] =
+              row < G ? __builtin_bit_cast(float, (uint32_t)qh[row * D + ch] << 16) * hs : 0.f;
+        }
+      }
       if constexpr (kRope) {  // the tau16 table, copied whole
         const uint4* src = (const uint4*)a.rope_tau16;
         for (int w = tid; w < kQ4Group * kRotRow / 4; w += kThreads)
