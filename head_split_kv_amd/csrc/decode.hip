@@ -525,7 +525,9 @@ __device__ __forceinline__ half8_t codes_to_f16(uint32_t w) {
 // denormals c 2^-24 (c <= 255, exact), pair j of the operand holding elements j and j + 4: the
 // slot order of codes_to_f16, with no high nibbles.
 __device__ __forceinline__ uint32_t byte_pair(uint32_t w0, uint32_t w1, int j) {
-  return ((w0 >> (8 * j)) & 0xFFu) | (((w1 >> (8 * j)) & 0xFFu) << 16);
+  // one v_perm_b32: result bytes (0, 1, 2, 3) = (w0 byte j, 0, w1 byte j, 0); the selector
+  // indexes the bytes of {w1, w0} (w0 = bytes 0..3), 0x0c gives a zero byte
+  return __builtin_amdgcn_perm(w1, w0, 0x0c000c00u | ((4u + j) << 16) | (uint32_t)j);
 }
 __device__ __forceinline__ half8_t bytes_to_f16(uint32_t w0, uint32_t w1) {
   const u32x4_t r = {byte_pair(w0, w1, 0), byte_pair(w0, w1, 1), byte_pair(w0, w1, 2),
@@ -553,7 +555,7 @@ __device__ __attribute__((aligned(256))) uint32_t g_q4_idle[4096];
 // operand carries the 1/16 of high nibbles.
 // Leading arguments as for decode_kernel.
 template <int D, int G, int LPT, int NS, bool kRope, int BITS>
-__global__ void __launch_bounds__(kThreads, (kRope || BITS == 8) ? 1 : 2)
+__global__ void __launch_bounds__(kThreads, kRope ? 1 : 2)
     decode_q4_kernel(int32_t lead_nsplit, int32_t lead_hr, int32_t lead_hs, int32_t lead_b,
                      int32_t lead_nss, int32_t lead_fused, DecodeArgs a) {
   using T = uint16_t;
@@ -998,36 +1000,78 @@ __global__ void __launch_bounds__(kThreads, (kRope || BITS == 8) ? 1 : 2)
       }
     }
     __syncthreads();
-    Ld f0, f1, f2, f3;
-    if (n_wave > 0) {
-      load_params(0);
-      load_step(f0, 0, 0);
-      load_step(f1, 0, 1);
-      load_step(f2, 0, 2);
-      load_step(f3, 0, 3);
-    }
-    for (int gi = 0; gi < n_full; ++gi) {
-      fold();
-      load_params(gi + 1);  // clamped past the last group
-      // the barriers keep each slot's last use ahead of its reload, so the reload lands in
-      // the same registers (no loop-carried copy, which would wait for the load)
-      step(f0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      load_step(f0, gi + 1, 0);
-      step(f1, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      load_step(f1, gi + 1, 1);
-      step(f2, 2);
-      __builtin_amdgcn_sched_barrier(0);
-      load_step(f2, gi + 1, 2);
-      step(f3, 3);
-      __builtin_amdgcn_sched_barrier(0);
-      load_step(f3, gi + 1, 3);
-    }
-    if (t_step >= 0) {  // the leftover step, already in its slot (the others read the idle buffer)
-      fold();
-      const Ld& ft = t_step == 0 ? f0 : t_step == 1 ? f1 : t_step == 2 ? f2 : f3;
-      step(ft, t_step);
+    if constexpr (BITS == 8) {
+      // 8-bit codes: a step is 8 KB, so two slots (16 KB in flight, as four 4-bit steps):
+      // a slot is refilled two steps ahead, steps 2 and 3 of the same group, then steps 0 and
+      // 1 of the next
+      Ld f0, f1;
+      if (n_wave > 0) {
+        load_params(0);
+        load_step(f0, 0, 0);
+        load_step(f1, 0, 1);
+      }
+      for (int gi = 0; gi < n_full; ++gi) {
+        fold();
+        load_params(gi + 1);  // clamped past the last group
+        step(f0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_step(f0, gi, 2);
+        step(f1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_step(f1, gi, 3);
+        step(f0, 2);
+        __builtin_amdgcn_sched_barrier(0);
+        load_step(f0, gi + 1, 0);
+        step(f1, 3);
+        __builtin_amdgcn_sched_barrier(0);
+        load_step(f1, gi + 1, 1);
+      }
+      if (t_step >= 0) {  // the leftover step: steps 0 and 1 are in their slots, 2 and 3 load here
+        fold();
+        if (t_step == 0) {
+          step(f0, 0);
+        } else if (t_step == 1) {
+          step(f1, 1);
+        } else if (t_step == 2) {
+          load_step(f0, n_full, 2);
+          step(f0, 2);
+        } else {
+          load_step(f1, n_full, 3);
+          step(f1, 3);
+        }
+      }
+    } else {
+      Ld f0, f1, f2, f3;
+      if (n_wave > 0) {
+        load_params(0);
+        load_step(f0, 0, 0);
+        load_step(f1, 0, 1);
+        load_step(f2, 0, 2);
+        load_step(f3, 0, 3);
+      }
+      for (int gi = 0; gi < n_full; ++gi) {
+        fold();
+        load_params(gi + 1);  // clamped past the last group
+        // the barriers keep each slot's last use ahead of its reload, so the reload lands in
+        // the same registers (no loop-carried copy, which would wait for the load)
+        step(f0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_step(f0, gi + 1, 0);
+        step(f1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_step(f1, gi + 1, 1);
+        step(f2, 2);
+        __builtin_amdgcn_sched_barrier(0);
+        load_step(f2, gi + 1, 2);
+        step(f3, 3);
+        __builtin_amdgcn_sched_barrier(0);
+        load_step(f3, gi + 1, 3);
+      }
+      if (t_step >= 0) {  // the leftover step, already in its slot (the others read the idle buffer)
+        fold();
+        const Ld& ft = t_step == 0 ? f0 : t_step == 1 ? f1 : t_step == 2 ? f2 : f3;
+        step(ft, t_step);
+      }
     }
   }
   // MFMA partial of query col: sums over the 4 lanes of the column; every channel of O^T gets
