@@ -335,96 +335,107 @@ __global__ void __launch_bounds__(kThreads) kv4_dequant_kernel(DequantArgs a) {
 // Keys of a pre-RoPE cache turned at their positions into bf16 staging (DequantArgs with
 // rope_base set; OpenReview thread, the authors' reply on KV quantization: keys quantized
 // before RoPE). RoPE in its rotate-half form: channels i and i + D/2 turn by t f_i,
-// f_i = theta^(-2 i / D). One thread per (row, 8 pairs): pairs 8 x .. 8 x + 7 of one key row,
-// from three sources in turn: the retrieval heads' earlier tokens (dequantized as in
-// kv4_dequant_kernel, or residual rows), the chunk's keys as given (position c0 + i), and the
-// held streaming slots (slot s < S holds position s, a ring slot the latest t < c0 with
-// t = s (mod R) past the sinks). The angle of position t = 128 g + tau is composed from the
-// base table's (cos, sin) of 128 g f_i (float32 from float64) and sincosf(tau f_i), where
-// tau f_i < 128 keeps the float32 argument accurate; the pair turns in float32 and each result
-// is rounded to bf16 to nearest even.
+// f_i = theta^(-2 i / D). One thread per (position, 8 pairs, group of kStageHeads heads): the
+// angles of pairs 8 x .. 8 x + 7 at one position, then those pairs of the group's key rows at
+// that position, from three sources in turn: the retrieval heads' earlier tokens (dequantized as in kv4_dequant_kernel,
+// or residual rows), the chunk's keys as given (position c0 + i), and the held streaming slots
+// (slot s < S holds position s, a ring slot the latest t < c0 with t = s (mod R) past the
+// sinks). The angle of position t = 128 g + tau is composed from the base table's (cos, sin)
+// of 128 g f_i (float32 from float64) and sincosf(tau f_i), where tau f_i < 128 keeps the
+// float32 argument accurate; the pair turns in float32 and each result is rounded to bf16 to
+// nearest even.
+constexpr int kStageHeads = 4;
+__host__ __device__ constexpr int stage_groups(int heads) {
+  return (heads + kStageHeads - 1) / kStageHeads;
+}
 template <int D, int BITS>
 __global__ void __launch_bounds__(kThreads) kv4_rope_stage_kernel(DequantArgs a) {
   constexpr int HX = D / 16;  // pieces of 8 pairs per row
   constexpr int H = D / 2;
   const int SR = a.S + a.R;
-  const int64_t n_pre = (int64_t)a.nb * a.Hr * a.cap_s * HX;
-  const int64_t n_chunk = (int64_t)a.nb * a.m * a.Hkv * HX;
-  const int64_t n_str = (int64_t)a.nb * a.Hs * SR * HX;
+  const int gr = stage_groups(a.Hr), gc = stage_groups(a.Hkv), gs = stage_groups(a.Hs);
+  const int64_t n_pre = (int64_t)a.nb * a.cap_s * HX * gr;
+  const int64_t n_chunk = (int64_t)a.nb * a.m * HX * gc;
+  const int64_t n_str = (int64_t)a.nb * SR * HX * gs;
   for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < n_pre + n_chunk + n_str;
        u += (int64_t)gridDim.x * blockDim.x) {
-    float x1[8], x2[8];
-    uint16_t* dst;
-    int pos, x;
-    if (u < n_pre) {
-      int64_t w = u;
-      x = (int)(w % HX);
-      w /= HX;
-      const int t = (int)(w % a.cap_s);
-      w /= a.cap_s;
-      const int r = (int)(w % a.Hr);
-      const int bi = (int)(w / a.Hr);
-      const int n = a.c0[bi];
-      if (t >= n) continue;
-      const char* head = (const char*)a.full_k + ((int64_t)(a.b0 + bi) * a.Hr + r) * a.q4_stride;
-      dst = (uint16_t*)a.out_k + (((int64_t)bi * a.Hr + r) * a.cap_s + t) * D;
-      if (t >= (n / kG) * kG) {  // residual row
-        const uint16_t* row = (const uint16_t*)(head + a.q4_resid) + (int64_t)(t % kG) * D;
-        bf16x8_to_f32(*(const uint4*)(row + 8 * x), x1);
-        bf16x8_to_f32(*(const uint4*)(row + H + 8 * x), x2);
-      } else {
-        key_values8<D, BITS>(head, a.q4_params, t, 8 * x, x1);
-        key_values8<D, BITS>(head, a.q4_params, t, H + 8 * x, x2);
-      }
-      pos = t;
-    } else if (u < n_pre + n_chunk) {
-      int64_t w = u - n_pre;
-      x = (int)(w % HX);
-      w /= HX;
-      const int j = (int)(w % a.Hkv);
-      w /= a.Hkv;
-      const int i = (int)(w % a.m);
-      const int bi = (int)(w / a.m);
-      const int64_t off = (((int64_t)bi * a.m + i) * a.Hkv + j) * D;
-      const uint16_t* row = (const uint16_t*)a.chunk_k + off;
-      bf16x8_to_f32(*(const uint4*)(row + 8 * x), x1);
-      bf16x8_to_f32(*(const uint4*)(row + H + 8 * x), x2);
-      dst = (uint16_t*)a.out_chunk_k + off;
-      pos = a.c0[bi] + i;
-    } else {
-      int64_t w = u - n_pre - n_chunk;
-      x = (int)(w % HX);
-      w /= HX;
-      const int s = (int)(w % SR);
-      w /= SR;
-      const int cls = (int)(w % a.Hs);
-      const int bi = (int)(w / a.Hs);
-      const int n = a.c0[bi];
-      if (s >= n) continue;  // an empty slot: never read
-      const int64_t off = (((int64_t)(a.b0 + bi) * a.Hs + cls) * SR + s) * D;
-      const uint16_t* row = (const uint16_t*)a.str_k + off;
-      bf16x8_to_f32(*(const uint4*)(row + 8 * x), x1);
-      bf16x8_to_f32(*(const uint4*)(row + H + 8 * x), x2);
-      dst = (uint16_t*)a.out_str_k + off;
-      pos = s < a.S ? s : s + a.R * ((n - 1 - s) / a.R);
-    }
+    const int part = u < n_pre ? 0 : u < n_pre + n_chunk ? 1 : 2;
+    int64_t w = part == 0 ? u : part == 1 ? u - n_pre : u - n_pre - n_chunk;
+    const int x = (int)(w % HX);
+    w /= HX;
+    const int ngr = part == 0 ? gr : part == 1 ? gc : gs;
+    const int h0 = (int)(w % ngr) * kStageHeads;  // first head of this item's group
+    w /= ngr;
+    const int rows = part == 0 ? a.cap_s : part == 1 ? a.m : SR;
+    const int row = (int)(w % rows);
+    const int bi = (int)(w / rows);
+    const int n = a.c0[bi];
+    if (part != 1 && row >= n) continue;  // past the prefix, or an empty slot (never read)
+    int pos;
+    if (part == 0) pos = row;
+    else if (part == 1) pos = n + row;
+    else pos = row < a.S ? row : row + a.R * ((n - 1 - row) / a.R);
+    // (cos, sin) of pairs 8 x + e at pos
     const int g = pos / kG, tau = pos % kG;
     const float2* base = (const float2*)a.rope_base + (int64_t)g * H + 8 * x;
-    float y1[8], y2[8];
+    float cs[8], sn[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int i = 8 * x + e;
-      const float f = exp2f(-(float)(2 * i) / (float)D * a.log2_theta);
+      const float f = exp2f(-(float)(2 * (8 * x + e)) / (float)D * a.log2_theta);
       float st, ct;
       sincosf((float)tau * f, &st, &ct);
-      const float2 b = base[e];
-      const float c = b.x * ct - b.y * st;
-      const float sn = b.y * ct + b.x * st;
-      y1[e] = x1[e] * c - x2[e] * sn;
-      y2[e] = x1[e] * sn + x2[e] * c;
+      const float2 bb = base[e];
+      cs[e] = bb.x * ct - bb.y * st;
+      sn[e] = bb.y * ct + bb.x * st;
     }
-    *(uint4*)(dst + 8 * x) = f32x8_to_bf16(y1);
-    *(uint4*)(dst + H + 8 * x) = f32x8_to_bf16(y2);
+    auto turn = [&](const float (&x1)[8], const float (&x2)[8], uint16_t* dst) {
+      float y1[8], y2[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        y1[e] = x1[e] * cs[e] - x2[e] * sn[e];
+        y2[e] = x1[e] * sn[e] + x2[e] * cs[e];
+      }
+      *(uint4*)(dst + 8 * x) = f32x8_to_bf16(y1);
+      *(uint4*)(dst + H + 8 * x) = f32x8_to_bf16(y2);
+    };
+    float x1[8], x2[8];
+    if (part == 0) {
+      const bool resid = row >= (n / kG) * kG;
+#pragma unroll
+      for (int r = h0; r < h0 + kStageHeads; ++r) {
+        if (r >= a.Hr) break;
+        const char* head = (const char*)a.full_k + ((int64_t)(a.b0 + bi) * a.Hr + r) * a.q4_stride;
+        if (resid) {
+          const uint16_t* src = (const uint16_t*)(head + a.q4_resid) + (int64_t)(row % kG) * D;
+          bf16x8_to_f32(*(const uint4*)(src + 8 * x), x1);
+          bf16x8_to_f32(*(const uint4*)(src + H + 8 * x), x2);
+        } else {
+          key_values8<D, BITS>(head, a.q4_params, row, 8 * x, x1);
+          key_values8<D, BITS>(head, a.q4_params, row, H + 8 * x, x2);
+        }
+        turn(x1, x2, (uint16_t*)a.out_k + (((int64_t)bi * a.Hr + r) * a.cap_s + row) * D);
+      }
+    } else if (part == 1) {
+#pragma unroll
+      for (int j = h0; j < h0 + kStageHeads; ++j) {
+        if (j >= a.Hkv) break;
+        const int64_t off = (((int64_t)bi * a.m + row) * a.Hkv + j) * D;
+        const uint16_t* src = (const uint16_t*)a.chunk_k + off;
+        bf16x8_to_f32(*(const uint4*)(src + 8 * x), x1);
+        bf16x8_to_f32(*(const uint4*)(src + H + 8 * x), x2);
+        turn(x1, x2, (uint16_t*)a.out_chunk_k + off);
+      }
+    } else {
+#pragma unroll
+      for (int cls = h0; cls < h0 + kStageHeads; ++cls) {
+        if (cls >= a.Hs) break;
+        const int64_t off = (((int64_t)(a.b0 + bi) * a.Hs + cls) * SR + row) * D;
+        const uint16_t* src = (const uint16_t*)a.str_k + off;
+        bf16x8_to_f32(*(const uint4*)(src + 8 * x), x1);
+        bf16x8_to_f32(*(const uint4*)(src + H + 8 * x), x2);
+        turn(x1, x2, (uint16_t*)a.out_str_k + off);
+      }
+    }
   }
 }
 
@@ -452,8 +463,10 @@ int launch_dequant_kv4(const DequantArgs& a, int head_dim, void* stream) {
 }
 
 int launch_rope_stage(const DequantArgs& a, int head_dim, void* stream) {
-  const int64_t rows = (int64_t)a.nb * a.Hr * a.cap_s + (int64_t)a.nb * a.m * a.Hkv +
-                       (int64_t)a.nb * a.Hs * (a.S + a.R);
+  // one work item per position, 8-pair piece and group of kStageHeads heads
+  const int64_t rows = (int64_t)a.nb * a.cap_s * stage_groups(a.Hr) +
+                       (int64_t)a.nb * a.m * stage_groups(a.Hkv) +
+                       (int64_t)a.nb * (a.S + a.R) * stage_groups(a.Hs);
   const int64_t work = rows * (head_dim / 16);
   if (work == 0) return 0;
   int64_t blocks = (work + kThreads - 1) / kThreads;
