@@ -16,11 +16,13 @@
 // patterns below are free of bank conflicts. Per tile a wave computes S^T = K Q^T with
 // v_mfma_f32_32x32x16_bf16 (keys as MFMA rows, so each lane owns one query and its softmax
 // statistics stay in the lane and its partner lane l ^ 32), takes the online softmax in fp32
-// (log2 domain, lazy rescale above kTau), splits P into two bf16 terms (hi + lo, about 16
-// significant bits) and accumulates O^T += V^T P^T with the same MFMA. The V^T operand comes
-// from ds_read_b64_tr_b16, which transposes 4x16 blocks of the row-major tile on the way out
-// of LDS. The key order inside a 16-key MFMA slab is permuted identically in P and V^T,
-// matching the accumulator layout of the first product.
+// (log2 domain, lazy rescale above kTau), rounds P to fp16 (11 significant bits) and
+// accumulates O^T += V^T P^T with v_mfma_f32_32x32x16_f16. Each V tile is converted to fp16 in
+// LDS once, by the whole block, when it is about to be used (exact for |v| in [2^-14, 65504],
+// since bf16 carries 8 significant bits). The V^T operand comes from ds_read_b64_tr_b16, which
+// transposes 4x16 blocks of the row-major tile on the way out of LDS. The key order inside a
+// 16-key MFMA slab is permuted identically in P and V^T, matching the accumulator layout of
+// the first product.
 //
 // Tiles are classified per block: skipped when no key is visible to any query of the block
 // (causally later, or outside every query's sink + recent window), computed without masks
@@ -47,6 +49,8 @@ constexpr int kNoPos = 0x7FFFFFFF;  // key position of an empty or padding slot
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 half8_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 half2_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
@@ -60,13 +64,15 @@ __device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{x, y}, bf16x2_t));
 }
 
-// P = hi + lo with hi = bf16(P) and lo = bf16(P - hi): the two bf16 products carry about
-// 16 significant bits of each softmax weight into the fp32 accumulation of O.
-__device__ __forceinline__ void split_bf16(float x, float y, uint32_t& hi, uint32_t& lo) {
-  hi = pack_bf16(x, y);
-  const float hx = __builtin_bit_cast(float, hi << 16);
-  const float hy = __builtin_bit_cast(float, hi & 0xFFFF0000u);
-  lo = pack_bf16(x - hx, y - hy);
+// Two floats to an fp16 pair, round to nearest even; x in the low half.
+__device__ __forceinline__ uint32_t pack_f16(float x, float y) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{x, y}, half2_t));
+}
+
+// A bf16 pair to an fp16 pair (exact for magnitudes in [2^-14, 65504]: bf16 carries 8
+// significant bits, fp16 11; smaller values round to fp16 subnormals, within 2^-25).
+__device__ __forceinline__ uint32_t bf16w_to_f16w(uint32_t w) {
+  return pack_f16(__builtin_bit_cast(float, w << 16), __builtin_bit_cast(float, w & 0xFFFF0000u));
 }
 
 template <int D>
@@ -350,6 +356,16 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
   // without spills.
   auto iterate = [&](f32x16_t (&sc)[2], f32x16_t (&sn)[2], int kind, const char* skn,
                      const char* sv, const int* sp) {
+    // V(cur) to fp16 in place (each 16-byte chunk keeps its swizzled place), shared by the
+    // block's waves; the barrier waits for these LDS writes only: the DMAs in flight (at most
+    // three batches) stay in flight
+    for (int c = tid; c < Gm::kTileBytes / 16; c += kThreads) {
+      uint4* chunk = (uint4*)(const_cast<char*>(sv) + c * 16);
+      const uint4 w = *chunk;
+      *chunk = uint4{bf16w_to_f16w(w.x), bf16w_to_f16w(w.y), bf16w_to_f16w(w.z),
+                     bf16w_to_f16w(w.w)};
+    }
+    wait_vm_barrier<3 * kDma>();
     if (kind != 0) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
@@ -424,16 +440,15 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int blk = k >> 1, e0 = (k & 1) * 8;
-      uint32_t hw[4], lw[4];
+      uint32_t pw[4];
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         const float p0 = fexp2(__builtin_fmaf(sc[blk][e0 + e], c2, -m));
         const float p1 = fexp2(__builtin_fmaf(sc[blk][e0 + e + 1], c2, -m));
         l += p0 + p1;
-        split_bf16(p0, p1, hw[e / 2], lw[e / 2]);
+        pw[e / 2] = pack_f16(p0, p1);
       }
-      const bf16x8_t pfh = __builtin_bit_cast(bf16x8_t, uint4{hw[0], hw[1], hw[2], hw[3]});
-      const bf16x8_t pfl = __builtin_bit_cast(bf16x8_t, uint4{lw[0], lw[1], lw[2], lw[3]});
+      const half8_t pf = __builtin_bit_cast(half8_t, uint4{pw[0], pw[1], pw[2], pw[3]});
       bf16x8_t (&vf)[Gm::kDBlocks] = (k & 1) ? vB : vA;
       bf16x8_t (&vn)[Gm::kDBlocks] = (k & 1) ? vA : vB;
       // the next slab's operands (after the last slab, the first K operands of the next
@@ -442,10 +457,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int db = 0; db < Gm::kDBlocks; ++db)
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pfh, o[db], 0, 0, 0);
-#pragma unroll
-      for (int db = 0; db < Gm::kDBlocks; ++db)
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pfl, o[db], 0, 0, 0);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, vf[db]), pf,
+                                                       o[db], 0, 0, 0);
     }
     // K(next) came by DMA in the previous iteration: wait for it (this iteration's two
     // batches stay in flight), then the scores of the next tile, the K operands of each

@@ -232,7 +232,9 @@ duo_status duo_decode_step(duo_cache* cache, int32_t layer, const void* q, const
  * chunk, plus the chunk) under DUO_PREFILL_WINDOW, or to every token the streaming cache
  * holds plus the chunk's t <= p under DUO_PREFILL_CHUNK (cfg.streaming_prefill). The cache is
  * not modified: the caller then appends the same k, v with duo_kv_append. Layouts as in the
- * header comment; n_chunk = 0 is a no-op. */
+ * header comment; n_chunk = 0 is a no-op. Precision (bf16 caches): the PV product takes the
+ * softmax weights and the values in fp16, so value magnitudes must stay below 65504 (the
+ * values read, cache rows and chunk alike); the fp32 dtype has no such limit. */
 duo_status duo_attn_prefill(duo_cache* cache, int32_t layer, int32_t seq, const void* q,
                             const void* k, const void* v, int32_t n_chunk, void* out,
                             float* lse, void* stream);
