@@ -200,3 +200,36 @@ def test_prefill_f32_chunk_mode():
     w = W.Workload("prefill-f32-chunk", 1, 2, 8, 2, 64, "f32", 4, 28, 0, 0, 1,
                    fixed_mask=((0,),), seed=65)
     run_prefill(w, [300, 300], 70, mode="chunk", max_abs=1e-4)
+
+
+def test_prefill_large_values_within_fp16_bound():
+    """Values up to about 45,000 in magnitude (bf16, inside the fp16 range the PV product takes
+    them in): every output stays within 2^-10 max |v| of the oracle (twice the bound that fp16
+    weights allow, 2^-11 sum_t w_t |v_t|), and the log-sum-exp, which the values do not enter,
+    within the ordinary tolerance. Both head classes; chunks that start the sequence (few
+    visible keys) and later ones."""
+    w = W.Workload("large-v", 1, 1, 4, 4, 128, "bf16", 4, 32, 0, 0, 2, fixed_mask=((0, 2),),
+                   seed=601)
+    mask = W.retrieval_mask(w)[0]
+    cache = make_cache(w, capacity=401)
+    n, chunk = 400, 200
+    q = W.tokens(w, "q", 0, 0, 0, n)
+    k = W.tokens(w, "k", 0, 0, 0, n)
+    v = torch.from_numpy(W.tokens(w, "v", 0, 0, 0, n) * 10000.0).to(torch.bfloat16)
+    vmax = float(v.float().abs().max())
+    assert 20000.0 < vmax < 65504.0, vmax
+    v = v.double().numpy()
+    for c0 in range(0, n, chunk):
+        c1 = c0 + chunk
+        dq, dk = to_dev(q[c0:c1], torch.bfloat16), to_dev(k[c0:c1], torch.bfloat16)
+        dv = to_dev(v[c0:c1], torch.bfloat16)
+        lse = torch.empty((c1 - c0, w.hq), dtype=torch.float32, device="cuda")
+        out = cache.attn_prefill(0, dq, dk, dv, seq=0, lse=lse)
+        cache.kv_append(0, dk, dv, seq=0)
+        torch.cuda.synchronize()
+        ref, ref_lse = O.prefill_chunk(q[c0:c1], k[:c1], v[:c1], c0, mask, w.sink, w.recent)
+        got = out.float().cpu().numpy()
+        assert np.all(np.isfinite(got))
+        err = np.abs(got - ref).max()
+        assert err <= 2.0 ** -10 * vmax, (c0, err, 2.0 ** -10 * vmax)
+        assert_close(lse.cpu().numpy(), ref_lse, f"chunk [{c0},{c1}) lse")
