@@ -92,9 +92,9 @@ def source_sha(name: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def committed_traffic(kernel_file: str, key: str):
-    """HBM bytes per launch measured with rocprofv3 counters for the current kernel source,
-    or None when the counters were taken on another version of the kernel."""
+def committed_record(kernel_file: str, key: str):
+    """The rocprofv3 counter record ``key`` of profiles/traffic.json when it was taken on the
+    current kernel source, else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -103,7 +103,24 @@ def committed_traffic(kernel_file: str, key: str):
     rec = data.get(key)
     if not rec or rec.get("source_sha") != source_sha(kernel_file):
         return None
-    return rec.get("bytes_per_launch")
+    return rec
+
+
+def committed_traffic(kernel_file: str, key: str):
+    """HBM bytes per launch measured with rocprofv3 counters for the current kernel source,
+    or None when the counters were taken on another version of the kernel."""
+    rec = committed_record(kernel_file, key)
+    return None if rec is None else rec.get("bytes_per_launch")
+
+
+def committed_mfma(kernel_file: str, key: str):
+    """Matrix-core counters of the current kernel source (SQ_VALU_MFMA_BUSY_CYCLES against
+    GRBM_GUI_ACTIVE, executed MFMA work against the algorithmic work), or None."""
+    rec = committed_record(kernel_file, key)
+    if rec is None or "mfma_busy_frac_active" not in rec:
+        return None
+    return {k: rec[k] for k in ("mfma_busy_frac_active", "mfma_busy_frac_at_peak_clock",
+                                "executed_over_algorithmic", "clock_ghz")}
 
 
 class Timer:
@@ -889,6 +906,7 @@ def main():
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(pre["kern_tflops"] / BF16_PEAK_TFLOPS, 4),
                          "traffic": committed_traffic("prefill.hip", "prefill_c2"),
+                         "mfma_counters": committed_mfma("prefill.hip", "prefill_c2_mfma"),
                          "kernel": "prefill_kernel<d128, G1> (8 launches per pass)",
                          "kernel_ms_per_pass": round(pre["kern_ms"], 3),
                          "algorithmic_flops": int(pre["flops"])},
