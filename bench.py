@@ -55,11 +55,11 @@ def parse():
     p.add_argument("--workload", default="c3", help="decode workload key (c2, c3, c5, c5q)")
     p.add_argument("--prefill-passes", type=int, default=3)
     p.add_argument("--no-prefill", action="store_true")
-    p.add_argument("--prefill-modes", default="window,chunk,mixed,kv4,kv4rope",
+    p.add_argument("--prefill-modes", default="window,chunk,mixed,kv4,kv4rope,gqa",
                    help="prefill legs to time: window (per-query sink + recent mask), chunk "
                         "(chunk-granular streaming heads), mixed (gate-mixed attention), kv4 "
                         "(window mode over a 4-bit cache, staged), kv4rope (the same with "
-                        "pre-RoPE keys, staged turned)")
+                        "pre-RoPE keys, staged turned), gqa (the prompt on the GQA layer)")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-kv4", action="store_true", help="skip the 4-bit full-cache decode leg")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -267,12 +267,16 @@ def decode_leg(args, torch, hsk, W, N, kv_bits=0, rope_theta=0.0):
     return result
 
 
-def prefill_leg(args, torch, hsk, W, N, mode="window", kv_bits=0, rope_theta=0.0):
+def prefill_leg(args, torch, hsk, W, N, mode="window", kv_bits=0, rope_theta=0.0, gqa=False):
     """The 32K MHA prompt in 4K chunks; with kv_bits 4 over a 4-bit cache
     (duo_attn_prefill_staged: the retrieval prefix read back into bf16 staging, then the
     prefill kernel; the kernel timers cover the prefill kernel alone); with rope_theta the
-    cache holds pre-RoPE keys, and every key the chunk reads is staged turned."""
+    cache holds pre-RoPE keys, and every key the chunk reads is staged turned. With gqa the
+    same 32K prompt in 4K chunks on the Llama-3-8B-shaped GQA layer (32 q / 8 KV heads, 4
+    retrieval)."""
     w = W.workload("c2")
+    if gqa:
+        w = W.workload("c3").with_(prefill_len=w.prefill_len, prefill_chunk=w.prefill_chunk)
     mask = W.retrieval_mask(w)[0]
     dev = torch.device("cuda")
     P, C = w.prefill_len, w.prefill_chunk
@@ -734,6 +738,12 @@ def main():
             f"for {pre_chunk['flops'] / 1e12:.3f} TFLOP = {pre_chunk['tflops']:.1f} TFLOP/s; "
             f"attention kernel {pre_chunk['kern_ms']:.3f} ms = "
             f"{pre_chunk['kern_tflops']:.1f} TFLOP/s")
+    pre_gqa = None
+    if not args.no_prefill and "gqa" in modes:
+        pre_gqa = prefill_leg(args, torch, hsk, W, N, gqa=True)
+        log(f"prefill, GQA layer: {pre_gqa['attn_ms']:.3f} ms attention for "
+            f"{pre_gqa['flops'] / 1e12:.3f} TFLOP = {pre_gqa['tflops']:.1f} TFLOP/s; attention "
+            f"kernel {pre_gqa['kern_ms']:.3f} ms = {pre_gqa['kern_tflops']:.1f} TFLOP/s")
     pre_kv4 = None
     if not args.no_prefill and "kv4" in modes:
         pre_kv4 = prefill_leg(args, torch, hsk, W, N, kv_bits=4)
@@ -942,6 +952,17 @@ def main():
             "kernel_tflops": round(pre_chunk["kern_tflops"], 1),
             "frac": round(pre_chunk["kern_tflops"] / BF16_PEAK_TFLOPS, 4),
             "algorithmic_flops": int(pre_chunk["flops"]),
+        },
+        "prefill_gqa": None if pre_gqa is None else {
+            "workload": f"{pre_gqa['workload'].name}: the 32K prompt in 4K chunks on the GQA layer "
+                        f"(32 q / 8 KV heads, 4 retrieval, sink 16 + recent 512)",
+            "attn_ms": round(pre_gqa["attn_ms"], 3),
+            "ms_incl_append": round(pre_gqa["pass_ms"], 3),
+            "tflops": round(pre_gqa["tflops"], 1),
+            "kernel_ms_per_pass": round(pre_gqa["kern_ms"], 3),
+            "kernel_tflops": round(pre_gqa["kern_tflops"], 1),
+            "frac": round(pre_gqa["kern_tflops"] / BF16_PEAK_TFLOPS, 4),
+            "algorithmic_flops": int(pre_gqa["flops"]),
         },
         "cpu_prefill_baseline": None if cpu is None else {
             "value": round(cpu_pre["tflops"], 6), "unit": "TFLOP/s", "cores": cpu["threads"],
