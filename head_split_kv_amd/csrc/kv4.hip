@@ -337,10 +337,10 @@ __global__ void __launch_bounds__(kThreads) kv4_dequant_kernel(DequantArgs a) {
 // before RoPE). RoPE in its rotate-half form: channels i and i + D/2 turn by t f_i,
 // f_i = theta^(-2 i / D). One thread per (position, 8 pairs, group of kStageHeads heads): the
 // angles of pairs 8 x .. 8 x + 7 at one position, then those pairs of the group's key rows at
-// that position, from three sources in turn: the retrieval heads' earlier tokens (dequantized as in kv4_dequant_kernel,
-// or residual rows), the chunk's keys as given (position c0 + i), and the held streaming slots
-// (slot s < S holds position s, a ring slot the latest t < c0 with t = s (mod R) past the
-// sinks). The angle of position t = 128 g + tau is composed from the base table's (cos, sin)
+// that position, from three sources in turn: the retrieval heads' earlier tokens (dequantized
+// as in kv4_dequant_kernel, or residual rows), the chunk's keys as given (position c0 + i),
+// and the held streaming slots (slot s < S holds position s, a ring slot the latest t < c0
+// with t = s (mod R) past the sinks). The angle of position t = 128 g + tau is composed from the base table's (cos, sin)
 // of 128 g f_i (float32 from float64) and sincosf(tau f_i), where tau f_i < 128 keeps the
 // float32 argument accurate; the pair turns in float32 and each result is rounded to bf16 to
 // nearest even.
