@@ -157,18 +157,16 @@ def test_prefill_equals_decode_sequence():
     assert np.max(np.abs(outs[0] - dec)) < 4e-3
 
 
-@pytest.mark.timeout(900)
-def test_prefill_c2_mha_32k_in_4k_chunks():
-    """Llama-2-7B-shaped MHA layer: 32,768-token prompt in 8 chunks of 4,096 (the launch
-    configuration of the benchmark). Every output row and log-sum-exp of all 32 heads is
-    checked (32,768 x 32 rows). The oracle runs per chunk and KV head in a thread pool (its
-    large-array numpy work releases the GIL); a streaming head is given only the keys its
-    chunk can see (the sink, the window before the chunk, the chunk) at their true positions,
-    which leaves its explicit mask, and so its result, unchanged."""
-    w = W.workload("c2")
+def prefill_every_row(w, mode="window"):
+    """The prompt of ``w`` (one sequence) in chunks of ``w.prefill_chunk`` through the GPU,
+    then every output row and log-sum-exp of every head against the oracle. The oracle runs
+    per chunk and KV head in a thread pool (its large-array numpy work releases the GIL); a
+    streaming head is given only the keys its chunk can see in either mode (the sink, the R
+    tokens before the chunk, the chunk) at their true positions, which leaves its explicit
+    mask, and so its result, unchanged."""
     mask = W.retrieval_mask(w)[0]
     P, C, S, R, G = w.prefill_len, w.prefill_chunk, w.sink, w.recent, w.group
-    cache = make_cache(w, out_dtype=torch.float32, capacity=P + 1)
+    cache = make_cache(w, out_dtype=torch.float32, capacity=P + 1, streaming_prefill=mode)
     dt = torch_dtype(w.dtype)
     q = W.tokens(w, "q", 0, 0, 0, P)
     k = W.tokens(w, "k", 0, 0, 0, P)
@@ -184,7 +182,7 @@ def test_prefill_c2_mha_32k_in_4k_chunks():
         torch.cuda.synchronize()
         got[c0:c1] = out.float().cpu().numpy()[0]
         got_lse[c0:c1] = lse.cpu().numpy()[0]
-    _progress("c2 prefill: 8 chunks on the GPU")
+    _progress(f"{w.name} prefill ({mode}): every chunk on the GPU")
 
     def check(c0, j):
         c1 = min(P, c0 + C)
@@ -192,10 +190,11 @@ def test_prefill_c2_mha_32k_in_4k_chunks():
             keys = np.arange(c1)
         else:
             keys = np.unique(np.concatenate([np.arange(min(S, c1)),
-                                             np.arange(max(S, c0 - R + 1), c1)]))
+                                             np.arange(max(S, c0 - R), c1)]))
         hq = slice(j * G, (j + 1) * G)
         ref, ref_lse = O.attention(q[c0:c1, hq], k[keys, j:j + 1], v[keys, j:j + 1],
-                                   np.arange(c0, c1), keys, mask[j:j + 1], S, R)
+                                   np.arange(c0, c1), keys, mask[j:j + 1], S, R,
+                                   chunk_start=c0 if mode == "chunk" else None)
         assert_close(got[c0:c1, hq], ref, f"chunk [{c0},{c1}) kv {j} out")
         assert_close(got_lse[c0:c1, hq], ref_lse, f"chunk [{c0},{c1}) kv {j} lse")
 
@@ -203,8 +202,16 @@ def test_prefill_c2_mha_32k_in_4k_chunks():
         for c0 in range(0, P, C):
             for f in [ex.submit(check, c0, j) for j in range(w.hkv)]:
                 f.result()
-            _progress(f"c2 prefill: chunk at {c0} checked, every row")
+            _progress(f"{w.name} prefill ({mode}): chunk at {c0} checked, every row")
     cache.close()
+
+
+@pytest.mark.timeout(900)
+def test_prefill_c2_mha_32k_in_4k_chunks():
+    """Llama-2-7B-shaped MHA layer: 32,768-token prompt in 8 chunks of 4,096 (the launch
+    configuration of the benchmark): every output row and log-sum-exp of all 32 heads
+    (32,768 x 32 rows)."""
+    prefill_every_row(W.workload("c2"))
 
 
 def test_prefill_gqa_8k_in_2k_chunks():
