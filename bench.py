@@ -963,6 +963,7 @@ def main():
             "kernel_tflops": round(pre_gqa["kern_tflops"], 1),
             "frac": round(pre_gqa["kern_tflops"] / BF16_PEAK_TFLOPS, 4),
             "algorithmic_flops": int(pre_gqa["flops"]),
+            "mfma_counters": committed_mfma("prefill.hip", "prefill_gqa_mfma"),
         },
         "cpu_prefill_baseline": None if cpu is None else {
             "value": round(cpu_pre["tflops"], 6), "unit": "TFLOP/s", "cores": cpu["threads"],
