@@ -267,8 +267,11 @@ def decode_leg(args, torch, hsk, W, N, kv_bits=0, rope_theta=0.0):
     return result
 
 
-def prefill_leg(args, torch, hsk, W, N, mode="window", kv_bits=0, rope_theta=0.0, gqa=False):
-    """The 32K MHA prompt in 4K chunks; with kv_bits 4 over a 4-bit cache
+def prefill_leg(args, torch, hsk, W, N, mode="window", kv_bits=0, rope_theta=0.0, gqa=False,
+                v16=False):
+    """The 32K MHA prompt in 4K chunks; with v16 through duo_attn_prefill_staged on the bf16
+    cache (the values the chunk reads converted to fp16 copies in staging first, which the
+    calls' time includes; the kernel timers cover the prefill kernel alone); with kv_bits 4 over a 4-bit cache
     (duo_attn_prefill_staged: the retrieval prefix read back into bf16 staging, then the
     prefill kernel; the kernel timers cover the prefill kernel alone); with rope_theta the
     cache holds pre-RoPE keys, and every key the chunk reads is staged turned. With gqa the
@@ -285,13 +288,16 @@ def prefill_leg(args, torch, hsk, W, N, mode="window", kv_bits=0, rope_theta=0.0
                          retrieval_mask=[mask], dtype=torch.bfloat16, out_dtype=torch.bfloat16,
                          streaming_prefill=mode, device=dev, kv_bits=kv_bits,
                          rope_theta=rope_theta)
-    staged = kv_bits in (4, 8)
+    staged = kv_bits in (4, 8) or v16
     # the largest staging of the pass (the last chunk's), as duo_prefill_staging_bytes gives it
     up = lambda x: (x + 255) // 256 * 256
     row = w.d * 2
     need = 2 * int(mask.sum()) * P * row
     if rope_theta:
         need = up(need) + up(C * w.hkv * row) + int((mask == 0).sum()) * (w.sink + w.recent) * row
+    if v16:
+        need = (up(int(mask.sum()) * P * row) + up(C * w.hkv * row)
+                + int((mask == 0).sum()) * (w.sink + w.recent) * row)
     staging = torch.empty(need if staged else 16, dtype=torch.uint8, device=dev)
     q = torch.from_numpy(W.tokens(w, "q", 0, 0, 0, P)).to(dev).to(torch.bfloat16)
     k = torch.from_numpy(W.tokens(w, "k", 0, 0, 0, P)).to(dev).to(torch.bfloat16)
@@ -744,6 +750,18 @@ def main():
         log(f"prefill, GQA layer: {pre_gqa['attn_ms']:.3f} ms attention for "
             f"{pre_gqa['flops'] / 1e12:.3f} TFLOP = {pre_gqa['tflops']:.1f} TFLOP/s; attention "
             f"kernel {pre_gqa['kern_ms']:.3f} ms = {pre_gqa['kern_tflops']:.1f} TFLOP/s")
+    pre_v16 = None
+    if not args.no_prefill and "v16" in modes:
+        pre_v16 = prefill_leg(args, torch, hsk, W, N, v16=True)
+        log(f"prefill, values staged as fp16: {pre_v16['attn_ms']:.3f} ms attention (staging "
+            f"included) = {pre_v16['tflops']:.1f} TFLOP/s; attention kernel "
+            f"{pre_v16['kern_ms']:.3f} ms = {pre_v16['kern_tflops']:.1f} TFLOP/s")
+    pre_gqa16 = None
+    if not args.no_prefill and "gqa16" in modes:
+        pre_gqa16 = prefill_leg(args, torch, hsk, W, N, gqa=True, v16=True)
+        log(f"prefill, GQA layer, values staged as fp16: {pre_gqa16['attn_ms']:.3f} ms attention "
+            f"(staging included) = {pre_gqa16['tflops']:.1f} TFLOP/s; attention kernel "
+            f"{pre_gqa16['kern_ms']:.3f} ms = {pre_gqa16['kern_tflops']:.1f} TFLOP/s")
     pre_kv4 = None
     if not args.no_prefill and "kv4" in modes:
         pre_kv4 = prefill_leg(args, torch, hsk, W, N, kv_bits=4)

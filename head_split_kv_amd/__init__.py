@@ -281,8 +281,9 @@ def duo_attn_prefill(cache: DuoCache, layer: int, seq: int, q: torch.Tensor, k: 
 
 def duo_prefill_staging_bytes(cache: DuoCache, layer: int, seq: int = -1,
                               n_chunk: int = 0) -> int:
-    """Bytes of bf16 staging ``duo_attn_prefill_staged`` needs for a chunk of ``n_chunk``
-    tokens at the current lengths."""
+    """Bytes of staging ``duo_attn_prefill_staged`` needs for a chunk of ``n_chunk`` tokens at
+    the current lengths (bf16 read-backs on a 4- or 8-bit cache, fp16 values on a bf16
+    cache, 0 on an fp32 cache)."""
     n = ctypes.c_uint64()
     check(lib().duo_prefill_staging_bytes(cache.handle, layer, seq, n_chunk, ctypes.byref(n)),
           "duo_prefill_staging_bytes")
@@ -292,11 +293,13 @@ def duo_prefill_staging_bytes(cache: DuoCache, layer: int, seq: int = -1,
 def duo_attn_prefill_staged(cache: DuoCache, layer: int, seq: int, q: torch.Tensor,
                             k: torch.Tensor, v: torch.Tensor, out=None, lse=None, staging=None,
                             stream=None):
-    """``duo_attn_prefill`` over a 4- or 8-bit cache: the retrieval heads' earlier tokens are
-    read back as bf16 rows into ``staging`` (a ``torch.uint8`` device tensor of at least
-    ``duo_prefill_staging_bytes`` bytes; allocated here when None), then the chunk attends.
-    With pre-RoPE keys (``rope_theta``) ``q`` is after RoPE and ``k`` before it, and the keys
-    are staged turned. Shapes as in ``duo_attn_prefill``."""
+    """``duo_attn_prefill`` through caller staging (a ``torch.uint8`` device tensor of at
+    least ``duo_prefill_staging_bytes`` bytes; allocated here when None). Over a 4- or 8-bit
+    cache the retrieval heads' earlier tokens are read back as bf16 rows into it, then the
+    chunk attends; with pre-RoPE keys (``rope_theta``) ``q`` is after RoPE and ``k`` before
+    it, and the keys are staged turned. On a bf16 cache the values the chunk reads are staged
+    as fp16 copies, and the result is bit-identical to ``duo_attn_prefill``. Shapes as in
+    ``duo_attn_prefill``."""
     m = q.shape[1] if seq < 0 else q.shape[0]
     lead = (cache.batch, m) if seq < 0 else (m,)
     _check_tensor(q, lead + (cache.hq, cache.d), cache.dtype, cache.device, "q")

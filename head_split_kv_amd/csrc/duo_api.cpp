@@ -376,12 +376,21 @@ StagingPlan staging_plan(const duo_cache* c, int32_t layer, int32_t seq, int32_t
   const uint64_t row = (uint64_t)c->cfg.head_dim * 2;
   const LayerInfo& li = c->layers[layer];
   const uint64_t pre = (uint64_t)nb * li.n_ret * (uint64_t)p.c_max * row;
+  const uint64_t str_bytes =
+      (uint64_t)c->cfg.batch * li.n_str * ((uint64_t)c->cfg.sink + c->cfg.recent) * row;
+  if (c->cfg.dtype == DUO_BF16 && c->cfg.kv_bits != 4 && c->cfg.kv_bits != 8) {
+    // fp16 copies of the values: the retrieval prefix, the chunk's, the streaming caches'
+    p.pv = 0;
+    p.chunk = up(pre);
+    p.str = p.chunk + up((uint64_t)nb * n_chunk * c->cfg.num_kv_heads * row);
+    p.bytes = p.str + str_bytes;
+    return p;
+  }
   p.pv = pre;
   if (c->cfg.rope_theta > 0.f) {
     p.chunk = up(2 * pre);
     p.str = p.chunk + up((uint64_t)nb * n_chunk * c->cfg.num_kv_heads * row);
-    p.bytes = p.str + (uint64_t)c->cfg.batch * li.n_str *
-                          ((uint64_t)c->cfg.sink + c->cfg.recent) * row;
+    p.bytes = p.str + str_bytes;
   } else {
     p.chunk = p.str = p.bytes = 2 * pre;
   }
@@ -463,6 +472,56 @@ duo_status launch_status(int rc) {
 
 }  // namespace
 
+namespace {
+
+// duo_attn_prefill_staged on a bf16 cache: the values the chunk reads are converted to fp16
+// once into the staging (the prefix of every retrieval head [nb][Hr][c_max][d], the chunk's
+// [nb][m][Hkv][d], the streaming caches [B][Hs][S+R][d]), and the prefill kernel reads them
+// without converting each V tile in LDS. The products are the same: the kernel's conversion
+// and the staging's are one function of each element.
+duo_status prefill_v16(duo_cache* c, int32_t layer, int32_t seq, const void* q, const void* k,
+                       const void* v, int32_t n_chunk, void* out, float* lse, void* staging,
+                       uint64_t staging_bytes, void* stream) {
+  const StagingPlan sp = staging_plan(c, layer, seq, n_chunk);
+  if (!aligned16(staging) || staging_bytes < sp.bytes) return DUO_ERR_INVALID;
+  if (n_chunk == 0) return DUO_OK;
+  PrefillArgs a;
+  const duo_status st = prefill_args(c, layer, seq, q, k, v, n_chunk, out, lse, a);
+  if (st != DUO_OK) return st;
+  char* stg = (char*)staging;
+  V16StageArgs d;
+  std::memset(&d, 0, sizeof(d));
+  d.full_v = a.full_v;
+  d.v = a.v;
+  d.str_v = a.str_v;
+  d.out_pv = stg;
+  d.out_chunk = stg + sp.chunk;
+  d.out_str = stg + sp.str;
+  d.cap = a.cap;
+  d.c_max = sp.c_max;
+  d.b0 = a.b0;
+  d.nb = a.nb;
+  d.Hr = a.Hr;
+  d.Hs = a.Hs;
+  d.SR = a.S + a.R;
+  d.m = n_chunk;
+  d.Hkv = a.Hkv;
+  d.D = c->cfg.head_dim;
+  std::memcpy(d.c0, a.c0, sizeof(d.c0));
+  if (launch_v16_stage(d, stream) != 0) return DUO_ERR_HIP;
+  a.v16 = 1;
+  a.full_v = stg;
+  a.vcap = sp.c_max;
+  a.v_b0 = a.b0;
+  a.v = stg + sp.chunk;
+  a.str_v = stg + sp.str;
+  const int group = c->cfg.num_q_heads / c->cfg.num_kv_heads;
+  return launch_status(launch_prefill(a, c->cfg.dtype, c->cfg.head_dim, group, stream,
+                                      next_marks(c, DUO_TIMING_PREFILL)));
+}
+
+}  // namespace
+
 duo_status duo_attn_prefill(duo_cache* c, int32_t layer, int32_t seq, const void* q,
                             const void* k, const void* v, int32_t n_chunk, void* out,
                             float* lse, void* stream) {
@@ -482,7 +541,8 @@ duo_status duo_prefill_staging_bytes(const duo_cache* c, int32_t layer, int32_t 
   if (!layer_ok(c, layer) || seq < -1 || seq >= c->cfg.batch || n_chunk < 0 || !bytes)
     return DUO_ERR_INVALID;
   *bytes = 0;
-  if (c->cfg.kv_bits != 4 && c->cfg.kv_bits != 8) return DUO_OK;
+  const bool quant = c->cfg.kv_bits == 4 || c->cfg.kv_bits == 8;
+  if (!quant && c->cfg.dtype != DUO_BF16) return DUO_OK;
   *bytes = staging_plan(c, layer, seq, n_chunk).bytes;
   return DUO_OK;
 }
@@ -494,7 +554,10 @@ duo_status duo_attn_prefill_staged(duo_cache* c, int32_t layer, int32_t seq, con
   if (!layer_ok(c, layer) || seq < -1 || seq >= c->cfg.batch || n_chunk < 0)
     return DUO_ERR_INVALID;
   const bool quant = c->cfg.kv_bits == 4 || c->cfg.kv_bits == 8;
-  if (!quant) return duo_attn_prefill(c, layer, seq, q, k, v, n_chunk, out, lse, stream);
+  if (!quant && (c->cfg.dtype != DUO_BF16 || !staging))
+    return duo_attn_prefill(c, layer, seq, q, k, v, n_chunk, out, lse, stream);
+  if (!quant) return prefill_v16(c, layer, seq, q, k, v, n_chunk, out, lse, staging,
+                                 staging_bytes, stream);
   const bool rope = c->cfg.rope_theta > 0.f;
   const StagingPlan sp = staging_plan(c, layer, seq, n_chunk);
   if (sp.bytes > 0 && (!staging || !aligned16(staging) || staging_bytes < sp.bytes))

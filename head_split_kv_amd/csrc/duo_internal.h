@@ -165,6 +165,10 @@ struct PrefillArgs {
   int32_t full_heads;       // full caches per sequence of this layer
   int32_t full_b0;          // sequence whose full caches start at full_k / full_v (0, or b0
                             // when they are a staging copy of sequences b0 .. b0 + nb - 1)
+  // fp16 values (duo_attn_prefill_staged on a bf16 cache): v, str_v and the retrieval
+  // prefix in full_v are fp16 copies, the prefix laid out [nb][Hr][vcap][D] from sequence
+  // v_b0; the kernel then reads V tiles as they are instead of converting them in LDS
+  int32_t v16, vcap, v_b0;
   float alpha[kMaxKvHeads];
   int16_t cls_idx[kMaxKvHeads];
   uint8_t ret_kv[kMaxKvHeads];
@@ -209,6 +213,24 @@ struct DequantArgs {
   int32_t m, Hkv, Hs, S, R;
 };
 int launch_dequant_kv4(const DequantArgs& a, int head_dim, void* stream);
+
+// fp16 copies of the values a bf16 prefill chunk reads (prefill.hip): the retrieval prefix
+// rows [0, c0) of sequences b0 .. b0 + nb - 1 into out_pv ([nb][Hr][c_max][D]), the chunk's
+// values v ([nb][m][Hkv][D]) into out_chunk, and the streaming values of those sequences into
+// out_str at their places in [B][Hs][S + R][D]. Every element is converted exactly as the
+// prefill kernel converts a V tile in LDS.
+struct V16StageArgs {
+  const void* full_v;  // this layer's retrieval values, [B][Hr][cap][D]
+  const void* v;
+  const void* str_v;   // this layer's streaming values, [B][Hs][S + R][D]
+  void* out_pv;
+  void* out_chunk;
+  void* out_str;
+  int64_t cap;
+  int32_t c_max, b0, nb, Hr, Hs, SR, m, Hkv, D;
+  int32_t c0[kMaxBatch];
+};
+int launch_v16_stage(const V16StageArgs& a, void* stream);
 int launch_rope_stage(const DequantArgs& a, int head_dim, void* stream);
 int launch_set_lengths(const SetLenArgs& a, void* stream);
 int launch_decode(const DecodeArgs& a, int dtype, int head_dim, int group, void* stream,

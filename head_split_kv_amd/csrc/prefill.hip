@@ -118,9 +118,11 @@ __device__ __forceinline__ void wait_vm_barrier() {
 }
 
 // kMix: the streaming pass of gate-mixed attention (full-cache source, blended output); a
-// separate instantiation so that the ordinary kernel carries none of it.
-template <int D, int G, bool kMix>
+// separate instantiation so that the ordinary kernel carries none of it. kV16: the values
+// arrive as fp16 copies (a.v16), so the V tiles need no conversion in LDS.
+template <int D, int G, bool kMix, bool kV16 = false>
 __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
+  static_assert(!(kMix && kV16), "the gate-mixed pass reads bf16 values");
   using Gm = Geo<D>;
   constexpr int NCH = Gm::kChunks;
   constexpr int RB = Gm::kRowBytes;
@@ -202,7 +204,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
                              ? ((int64_t)(b - a.full_b0) * a.full_heads + a.cls_idx[j]) * a.cap * RB
                              : ((int64_t)(b - a.full_b0) * a.Hr + cls) * a.cap * RB;
     cache_k = (const char*)a.full_k + base;
-    cache_v = (const char*)a.full_v + base;
+    cache_v = (const char*)a.full_v +
+              (kV16 ? ((int64_t)(b - a.v_b0) * a.Hr + cls) * a.vcap * RB : base);
   } else {
     n_cache_tiles = c0 > 0 ? (SR + kBN - 1) / kBN : 0;
     const int64_t base = ((int64_t)b * a.Hs + cls) * SR * RB;
@@ -358,14 +361,18 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PrefillArgs a) {
                      const char* sv, const int* sp) {
     // V(cur) to fp16 in place (each 16-byte chunk keeps its swizzled place), shared by the
     // block's waves; the barrier waits for these LDS writes only: the DMAs in flight (at most
-    // three batches) stay in flight
-    for (int c = tid; c < Gm::kTileBytes / 16; c += kThreads) {
-      uint4* chunk = (uint4*)(const_cast<char*>(sv) + c * 16);
-      const uint4 w = *chunk;
-      *chunk = uint4{bf16w_to_f16w(w.x), bf16w_to_f16w(w.y), bf16w_to_f16w(w.z),
-                     bf16w_to_f16w(w.w)};
+    // three batches) stay in flight. With fp16 copies of the values there is nothing to
+    // convert, and V(cur) is already complete in LDS: the barrier at the end of the previous
+    // iteration (or the prologue's) waited for its DMA.
+    if constexpr (!kV16) {
+      for (int c = tid; c < Gm::kTileBytes / 16; c += kThreads) {
+        uint4* chunk = (uint4*)(const_cast<char*>(sv) + c * 16);
+        const uint4 w = *chunk;
+        *chunk = uint4{bf16w_to_f16w(w.x), bf16w_to_f16w(w.y), bf16w_to_f16w(w.z),
+                       bf16w_to_f16w(w.w)};
+      }
+      wait_vm_barrier<3 * kDma>();
     }
-    wait_vm_barrier<3 * kDma>();
     if (kind != 0) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
@@ -639,6 +646,51 @@ __global__ void __launch_bounds__(kMergeThreads) prefill_merge_kernel(PrefillArg
     }
   }
   if (tid % 16 == 0 && a.lse) a.lse[orow] = (M + __builtin_log2f(L)) * kLn2;
+}
+
+// fp16 copies of the values of one prefill chunk. Grid: (x, group), groups being the
+// retrieval prefixes (nb * Hr), then the chunk's values, then the streaming values; every
+// thread converts up to kV16PerThread 16-byte chunks of its group, 256 threads apart, all
+// loads issued before the first store.
+constexpr int kV16PerThread = 8;
+
+__global__ void __launch_bounds__(256) v16_stage_kernel(V16StageArgs a) {
+  const int g = blockIdx.y;
+  const int64_t row16 = a.D / 8;  // 16-byte chunks per row
+  const int npre = a.nb * a.Hr;
+  const uint4* src;
+  uint4* dst;
+  int64_t n;  // chunks of this group
+  if (g < npre) {
+    const int i = g / a.Hr, r = g % a.Hr;
+    src = (const uint4*)a.full_v + ((int64_t)(a.b0 + i) * a.Hr + r) * a.cap * row16;
+    dst = (uint4*)a.out_pv + (int64_t)g * a.c_max * row16;
+    n = (int64_t)a.c0[i] * row16;
+  } else if (g == npre) {
+    src = (const uint4*)a.v;
+    dst = (uint4*)a.out_chunk;
+    n = (int64_t)a.nb * a.m * a.Hkv * row16;
+  } else {
+    const int64_t off = (int64_t)a.b0 * a.Hs * a.SR * row16;
+    src = (const uint4*)a.str_v + off;
+    dst = (uint4*)a.out_str + off;
+    n = (int64_t)a.nb * a.Hs * a.SR * row16;
+  }
+  const int64_t c0 = (int64_t)blockIdx.x * 256 * kV16PerThread + threadIdx.x;
+  if (c0 >= n) return;
+  uint4 w[kV16PerThread];
+#pragma unroll
+  for (int k = 0; k < kV16PerThread; ++k) {
+    const int64_t c = c0 + 256 * k;
+    if (c < n) w[k] = src[c];
+  }
+#pragma unroll
+  for (int k = 0; k < kV16PerThread; ++k) {
+    const int64_t c = c0 + 256 * k;
+    if (c < n)
+      dst[c] = uint4{bf16w_to_f16w(w[k].x), bf16w_to_f16w(w[k].y), bf16w_to_f16w(w[k].z),
+                     bf16w_to_f16w(w[k].w)};
+  }
 }
 
 // ---- fp32 inputs ------------------------------------------------------------------------
@@ -921,6 +973,9 @@ struct Variant {
     if (a.mixed)
       hipLaunchKernelGGL((prefill_kernel<D, G, true>), dim3((unsigned)blocks), dim3(kThreads), 0,
                          (hipStream_t)stream, a);
+    else if (a.v16)
+      hipLaunchKernelGGL((prefill_kernel<D, G, false, true>), dim3((unsigned)blocks),
+                         dim3(kThreads), 0, (hipStream_t)stream, a);
     else
       hipLaunchKernelGGL((prefill_kernel<D, G, false>), dim3((unsigned)blocks), dim3(kThreads), 0,
                          (hipStream_t)stream, a);
@@ -968,6 +1023,20 @@ int launch_prefill(const PrefillArgs& a, int dtype, int head_dim, int group, voi
     return -1;
   }
   return dispatch(head_dim, group, false, &a, stream, &marks);
+}
+
+int launch_v16_stage(const V16StageArgs& a, void* stream) {
+  const int64_t row16 = a.D / 8;
+  int64_t n_max = (int64_t)a.c_max * row16;
+  n_max = n_max > (int64_t)a.nb * a.m * a.Hkv * row16 ? n_max : (int64_t)a.nb * a.m * a.Hkv * row16;
+  n_max = n_max > (int64_t)a.nb * a.Hs * a.SR * row16 ? n_max : (int64_t)a.nb * a.Hs * a.SR * row16;
+  const int64_t per_block = 256 * kV16PerThread;
+  const int64_t gx = (n_max + per_block - 1) / per_block;
+  if (gx == 0) return 0;
+  if (gx > 0x7FFFFFFF) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(v16_stage_kernel, dim3((unsigned)gx, (unsigned)(a.nb * a.Hr + 2)), dim3(256),
+                     0, (hipStream_t)stream, a);
+  return (int)hipGetLastError();
 }
 
 int prefill_resident_blocks(int head_dim, int group) {

@@ -252,11 +252,17 @@ duo_status duo_attn_prefill(duo_cache* cache, int32_t layer, int32_t seq, const 
  * (rotate-half pairs (i, i + d/2) by t theta^(-2i/d), in float32) and rounded to bf16: the
  * retrieval prefix after its read-back, the chunk's keys into [nb][m][Hkv][d], and the held
  * streaming slots into [B][Hs][S+R][d]. Values are staged as without RoPE.
+ * On a bf16 cache (kv_bits 0) with non-null staging, the values the chunk attends to are
+ * first converted to fp16 copies in staging, each element as duo_attn_prefill converts it on
+ * the way into its PV product: the retrieval prefix [nb][Hr][c_max][d], the chunk's values
+ * [nb][m][Hkv][d] and the streaming caches [B][Hs][S+R][d] (the rows of the call's sequences).
+ * The prefill kernel then reads V tiles without converting them, and the outputs and
+ * log-sum-exps are bit-identical to duo_attn_prefill's. With null staging, and on an fp32
+ * cache, this is duo_attn_prefill.
  * staging: caller-owned device memory, 16-byte aligned, at least
  * duo_prefill_staging_bytes(.., n_chunk, ..) bytes (else DUO_ERR_INVALID); its contents are
- * scratch. On a dtype cache this is duo_attn_prefill (staging unused). On a 4- or 8-bit cache
- * duo_attn_prefill itself returns DUO_ERR_UNSUPPORTED for layers with retrieval heads, and
- * for every layer with cfg.rope_theta > 0. */
+ * scratch. On a 4- or 8-bit cache duo_attn_prefill itself returns DUO_ERR_UNSUPPORTED for
+ * layers with retrieval heads, and for every layer with cfg.rope_theta > 0. */
 duo_status duo_attn_prefill_staged(duo_cache* cache, int32_t layer, int32_t seq, const void* q,
                                    const void* k, const void* v, int32_t n_chunk, void* out,
                                    float* lse, void* staging, uint64_t staging_bytes,
@@ -264,8 +270,10 @@ duo_status duo_attn_prefill_staged(duo_cache* cache, int32_t layer, int32_t seq,
 
 /* Bytes of staging duo_attn_prefill_staged needs for this layer, seq (-1 = all sequences) and
  * a chunk of n_chunk tokens at the cache's current lengths: 2 * nb * Hr * c_max * d * 2 on a
- * 4- or 8-bit cache (0 on a dtype cache); with cfg.rope_theta > 0 that rounded up to 256 bytes,
- * plus nb * n_chunk * Hkv * d * 2 rounded up to 256, plus B * Hs * (S + R) * d * 2.
+ * 4- or 8-bit cache; with cfg.rope_theta > 0 that rounded up to 256 bytes, plus
+ * nb * n_chunk * Hkv * d * 2 rounded up to 256, plus B * Hs * (S + R) * d * 2. On a bf16 cache
+ * nb * Hr * c_max * d * 2 rounded up to 256, plus nb * n_chunk * Hkv * d * 2 rounded up to 256,
+ * plus B * Hs * (S + R) * d * 2 (the fp16 values); 0 on an fp32 cache.
  * DUO_ERR_INVALID for a bad layer or seq, n_chunk < 0 or a null `bytes`. Host only. */
 duo_status duo_prefill_staging_bytes(const duo_cache* cache, int32_t layer, int32_t seq,
                                      int32_t n_chunk, uint64_t* bytes);

@@ -39,7 +39,7 @@ def edge_rows(c0, c1, group, n_random, rng):
 
 def run_prefill(w, lens, chunk, layer=0, check_rows=None, cache=None, seqwise=False,
                 out_dtype=torch.float32, rng_seed=0, mode="window", edges=False,
-                max_abs=None):
+                max_abs=None, staged=False):
     """Prefill prompts of lengths ``lens`` in chunks of ``chunk``; returns the outputs.
 
     ``mode`` is the streaming-head prefill mode: "window" (per-query sink + recent mask) or
@@ -50,7 +50,8 @@ def run_prefill(w, lens, chunk, layer=0, check_rows=None, cache=None, seqwise=Fa
     tile of the others, plus that many random rows; see ``edge_rows``).
     With ``seqwise`` every sequence is prefilled by its own calls (ragged prompts);
     otherwise all sequences share the chunk calls (equal lengths). ``max_abs``: a tighter
-    bound on the largest absolute error of every chunk (fp32 inputs).
+    bound on the largest absolute error of every chunk (fp32 inputs). ``staged``: the chunks
+    go through duo_attn_prefill_staged (on a bf16 cache: values staged as fp16 copies).
     """
     if cache is None:
         cache = make_cache(w, out_dtype=out_dtype, capacity=max(lens) + 1, streaming_prefill=mode)
@@ -74,7 +75,8 @@ def run_prefill(w, lens, chunk, layer=0, check_rows=None, cache=None, seqwise=Fa
             dq, dk, dv = dq[0], dk[0], dv[0]
         shape = (dq.shape[0], c1 - c0, w.hq) if b < 0 else (c1 - c0, w.hq)
         lse = torch.empty(shape, dtype=torch.float32, device="cuda")
-        out = cache.attn_prefill(layer, dq, dk, dv, seq=b, lse=lse)
+        call = cache.attn_prefill_staged if staged else cache.attn_prefill
+        out = call(layer, dq, dk, dv, seq=b, lse=lse)
         cache.kv_append(layer, dk, dv, seq=b)
         torch.cuda.synchronize()
         got = out.float().cpu().numpy()

@@ -10,6 +10,7 @@ import os
 import re
 
 import numpy as np
+import torch
 import pytest
 
 from oracle import duo_oracle as O
@@ -304,17 +305,32 @@ def test_error_paths_leave_state_unchanged():
 
 
 def test_prefill_staged_checks_before_launch():
-    """duo_prefill_staging_bytes: 0 on a dtype cache and on empty caches without RoPE, the
-    chunk and streaming regions with pre-RoPE keys, argument checks; duo_attn_prefill_staged
-    rejects bad arguments and short staging before launching; duo_attn_prefill refuses every
-    layer of a pre-RoPE cache, streaming-only layers included."""
+    """duo_prefill_staging_bytes: 0 on an fp32 cache and on empty 4- and 8-bit caches without
+    RoPE; on a bf16 cache the fp16 copies of the chunk's and the streaming caches' values
+    (empty caches here); the chunk and streaming regions with pre-RoPE keys; argument checks.
+    duo_attn_prefill_staged rejects bad arguments and short staging before launching;
+    duo_attn_prefill refuses every layer of a pre-RoPE cache, streaming-only layers
+    included."""
     L = N.lib()
     n = ctypes.c_uint64(7)
     p = ctypes.c_void_p(1 << 40)
+    row = 128 * 2
+    up = lambda x: (x + 255) // 256 * 256
+    fc = FakeCache(dtype=torch.float32)
+    assert L.duo_prefill_staging_bytes(fc.h, 0, -1, 5, ctypes.byref(n)) == N.DUO_OK
+    assert n.value == 0
+    fc.close()
     for bits in (0, 4, 8):
         fc = FakeCache(kv_bits=bits)
         assert L.duo_prefill_staging_bytes(fc.h, 0, -1, 5, ctypes.byref(n)) == N.DUO_OK
-        assert n.value == 0
+        # B 3, Hkv 2 (layer 0: one streaming head), d 128, S + R = 20
+        assert n.value == (up(3 * 5 * 2 * row) + 3 * 1 * 20 * row if bits == 0 else 0)
+        if bits == 0:
+            assert L.duo_attn_prefill_staged(fc.h, 0, -1, p, p, p, 5, p, None, p,
+                                             n.value - 16, None) == N.DUO_ERR_INVALID
+            assert L.duo_attn_prefill_staged(fc.h, 0, -1, p, p, p, 5, p, None,
+                                             ctypes.c_void_p((1 << 40) + 8), n.value,
+                                             None) == N.DUO_ERR_INVALID
         assert L.duo_prefill_staging_bytes(fc.h, 2, -1, 5, ctypes.byref(n)) == N.DUO_ERR_INVALID
         assert L.duo_prefill_staging_bytes(fc.h, 0, 3, 5, ctypes.byref(n)) == N.DUO_ERR_INVALID
         assert L.duo_prefill_staging_bytes(fc.h, 0, -1, -1, ctypes.byref(n)) == N.DUO_ERR_INVALID
@@ -327,8 +343,6 @@ def test_prefill_staged_checks_before_launch():
     # pre-RoPE keys: B 3, Hkv 2 (layer 0: one retrieval, one streaming head; layer 1: two
     # streaming heads), d 128, S + R = 20, empty caches: the chunk's keys, then the streaming
     # keys of every sequence
-    row = 128 * 2
-    up = lambda x: (x + 255) // 256 * 256
     for bits in (4, 8):
         fc = FakeCache(kv_bits=bits, rope_theta=10000.0, retrieval_mask=[[1, 0], [0, 0]])
         for layer, hs in ((0, 1), (1, 2)):
