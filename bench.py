@@ -267,6 +267,12 @@ def decode_leg(args, torch, hsk, W, N, kv_bits=0, rope_theta=0.0):
     return result
 
 
+STAGED_PATH = ("duo_attn_prefill_staged on the bf16 cache: the values each chunk reads (retrieval "
+               "prefix, chunk, streaming caches) converted to fp16 copies in caller staging by a "
+               "separate kernel, whose time attn_ms includes; the kernel figures cover "
+               "prefill_kernel alone. Outputs bit-identical to duo_attn_prefill (below).")
+
+
 def prefill_leg(args, torch, hsk, W, N, mode="window", kv_bits=0, rope_theta=0.0, gqa=False,
                 v16=False):
     """The 32K MHA prompt in 4K chunks; with v16 through duo_attn_prefill_staged on the bf16
@@ -731,37 +737,27 @@ def main():
             f"call {dec4r['dec_us']:.2f} us")
     modes = set(args.prefill_modes.split(","))
     # a failing leg ends the run with an error (no leg is dropped from the line silently)
-    pre = None
+    # the window, chunk and GQA legs time both paths of a bf16 cache: duo_attn_prefill_staged
+    # with the values staged as fp16 copies (the line's figures, staging included) and
+    # duo_attn_prefill (the V tiles converted in LDS)
+    def both(label, **kw):
+        r16 = prefill_leg(args, torch, hsk, W, N, v16=True, **kw)
+        r = prefill_leg(args, torch, hsk, W, N, **kw)
+        for tag, x in (("values staged as fp16", r16), ("duo_attn_prefill", r)):
+            log(f"{label} ({tag}): {x['attn_ms']:.3f} ms attention for {x['flops'] / 1e12:.3f} "
+                f"TFLOP = {x['tflops']:.1f} TFLOP/s; attention kernel {x['kern_ms']:.3f} ms = "
+                f"{x['kern_tflops']:.1f} TFLOP/s")
+        return r16, r
+
+    pre = pre_plain = None
     if not args.no_prefill and "window" in modes:
-        pre = prefill_leg(args, torch, hsk, W, N)
-        log(f"prefill: {pre['attn_ms']:.3f} ms attention for {pre['flops'] / 1e12:.3f} TFLOP "
-            f"= {pre['tflops']:.1f} TFLOP/s; attention kernel {pre['kern_ms']:.3f} ms = "
-            f"{pre['kern_tflops']:.1f} TFLOP/s")
-    pre_chunk = None
+        pre, pre_plain = both("prefill")
+    pre_chunk = pre_chunk_plain = None
     if not args.no_prefill and "chunk" in modes:
-        pre_chunk = prefill_leg(args, torch, hsk, W, N, mode="chunk")
-        log(f"prefill, chunk-granular streaming heads: {pre_chunk['attn_ms']:.3f} ms attention "
-            f"for {pre_chunk['flops'] / 1e12:.3f} TFLOP = {pre_chunk['tflops']:.1f} TFLOP/s; "
-            f"attention kernel {pre_chunk['kern_ms']:.3f} ms = "
-            f"{pre_chunk['kern_tflops']:.1f} TFLOP/s")
-    pre_gqa = None
+        pre_chunk, pre_chunk_plain = both("prefill, chunk-granular streaming heads", mode="chunk")
+    pre_gqa = pre_gqa_plain = None
     if not args.no_prefill and "gqa" in modes:
-        pre_gqa = prefill_leg(args, torch, hsk, W, N, gqa=True)
-        log(f"prefill, GQA layer: {pre_gqa['attn_ms']:.3f} ms attention for "
-            f"{pre_gqa['flops'] / 1e12:.3f} TFLOP = {pre_gqa['tflops']:.1f} TFLOP/s; attention "
-            f"kernel {pre_gqa['kern_ms']:.3f} ms = {pre_gqa['kern_tflops']:.1f} TFLOP/s")
-    pre_v16 = None
-    if not args.no_prefill and "v16" in modes:
-        pre_v16 = prefill_leg(args, torch, hsk, W, N, v16=True)
-        log(f"prefill, values staged as fp16: {pre_v16['attn_ms']:.3f} ms attention (staging "
-            f"included) = {pre_v16['tflops']:.1f} TFLOP/s; attention kernel "
-            f"{pre_v16['kern_ms']:.3f} ms = {pre_v16['kern_tflops']:.1f} TFLOP/s")
-    pre_gqa16 = None
-    if not args.no_prefill and "gqa16" in modes:
-        pre_gqa16 = prefill_leg(args, torch, hsk, W, N, gqa=True, v16=True)
-        log(f"prefill, GQA layer, values staged as fp16: {pre_gqa16['attn_ms']:.3f} ms attention "
-            f"(staging included) = {pre_gqa16['tflops']:.1f} TFLOP/s; attention kernel "
-            f"{pre_gqa16['kern_ms']:.3f} ms = {pre_gqa16['kern_tflops']:.1f} TFLOP/s")
+        pre_gqa, pre_gqa_plain = both("prefill, GQA layer", gqa=True)
     pre_kv4 = None
     if not args.no_prefill and "kv4" in modes:
         pre_kv4 = prefill_leg(args, torch, hsk, W, N, kv_bits=4)
@@ -804,6 +800,18 @@ def main():
         log(f"oracle prefill sample: {cpu_pre['sec']:.2f} s, {cpu_pre['tflops'] * 1e3:.3f} GFLOP/s")
     cores = host_cores()
     traffic = committed_traffic("decode.hip", f"decode_{args.workload}")
+
+    def plain_obj(x, traffic_key):
+        """The same prompt through duo_attn_prefill (each V tile converted in LDS)."""
+        o = {"attn_ms": round(x["attn_ms"], 3), "tflops": round(x["tflops"], 1),
+             "kernel_ms_per_pass": round(x["kern_ms"], 3),
+             "kernel_tflops": round(x["kern_tflops"], 1),
+             "frac": round(x["kern_tflops"] / BF16_PEAK_TFLOPS, 4)}
+        if traffic_key:
+            o["traffic"] = committed_traffic("prefill.hip", traffic_key)
+            o["mfma_counters"] = committed_mfma("prefill.hip", traffic_key + "_mfma")
+        return o
+
     out = {
         "metric": METRIC,
         "value": round(dec["gbs"], 1),
@@ -927,17 +935,19 @@ def main():
         },
         "prefill": None if pre is None else {
             "workload": f"{pre['workload'].name}: 32K prompt in 4K chunks",
+            "path": STAGED_PATH,
             "attn_ms": round(pre["attn_ms"], 3),
             "ms_incl_append": round(pre["pass_ms"], 3),
             "tflops": round(pre["tflops"], 1),
             "roofline": {"bound": "mfma", "achieved": round(pre["kern_tflops"], 1),
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(pre["kern_tflops"] / BF16_PEAK_TFLOPS, 4),
-                         "traffic": committed_traffic("prefill.hip", "prefill_c2"),
-                         "mfma_counters": committed_mfma("prefill.hip", "prefill_c2_mfma"),
-                         "kernel": "prefill_kernel<d128, G1> (8 launches per pass)",
+                         "traffic": committed_traffic("prefill.hip", "prefill_c2_v16"),
+                         "mfma_counters": committed_mfma("prefill.hip", "prefill_c2_v16_mfma"),
+                         "kernel": "prefill_kernel<d128, G1, fp16 values> (8 launches per pass)",
                          "kernel_ms_per_pass": round(pre["kern_ms"], 3),
                          "algorithmic_flops": int(pre["flops"])},
+            "duo_attn_prefill": plain_obj(pre_plain, "prefill_c2"),
         },
         "prefill_kv4": None if pre_kv4 is None else {
             "workload": f"{pre_kv4['workload'].name}: 32K prompt in 4K chunks over 4-bit full "
@@ -963,6 +973,7 @@ def main():
         "prefill_chunk_mode": None if pre_chunk is None else {
             "workload": f"{pre_chunk['workload'].name}: 32K prompt in 4K chunks, streaming heads "
                         f"over the pruned cache plus the chunk",
+            "path": STAGED_PATH,
             "attn_ms": round(pre_chunk["attn_ms"], 3),
             "ms_incl_append": round(pre_chunk["pass_ms"], 3),
             "tflops": round(pre_chunk["tflops"], 1),
@@ -970,10 +981,12 @@ def main():
             "kernel_tflops": round(pre_chunk["kern_tflops"], 1),
             "frac": round(pre_chunk["kern_tflops"] / BF16_PEAK_TFLOPS, 4),
             "algorithmic_flops": int(pre_chunk["flops"]),
+            "duo_attn_prefill": plain_obj(pre_chunk_plain, None),
         },
         "prefill_gqa": None if pre_gqa is None else {
             "workload": f"{pre_gqa['workload'].name}: the 32K prompt in 4K chunks on the GQA layer "
                         f"(32 q / 8 KV heads, 4 retrieval, sink 16 + recent 512)",
+            "path": STAGED_PATH,
             "attn_ms": round(pre_gqa["attn_ms"], 3),
             "ms_incl_append": round(pre_gqa["pass_ms"], 3),
             "tflops": round(pre_gqa["tflops"], 1),
@@ -981,7 +994,8 @@ def main():
             "kernel_tflops": round(pre_gqa["kern_tflops"], 1),
             "frac": round(pre_gqa["kern_tflops"] / BF16_PEAK_TFLOPS, 4),
             "algorithmic_flops": int(pre_gqa["flops"]),
-            "mfma_counters": committed_mfma("prefill.hip", "prefill_gqa_mfma"),
+            "mfma_counters": committed_mfma("prefill.hip", "prefill_gqa_v16_mfma"),
+            "duo_attn_prefill": plain_obj(pre_gqa_plain, None),
         },
         "cpu_prefill_baseline": None if cpu is None else {
             "value": round(cpu_pre["tflops"], 6), "unit": "TFLOP/s", "cores": cpu["threads"],
