@@ -298,12 +298,12 @@ def prefill_leg(args, torch, hsk, W, N, mode="window", kv_bits=0, rope_theta=0.0
     # the largest staging of the pass (the last chunk's), as duo_prefill_staging_bytes gives it
     up = lambda x: (x + 255) // 256 * 256
     row = w.d * 2
-    need = 2 * int(mask.sum()) * P * row
+    chunk_b = C * w.hkv * row
+    str_b = int((mask == 0).sum()) * (w.sink + w.recent) * row
+    end = (1 if v16 else 2) * int(mask.sum()) * P * row  # read-backs (bf16 cache: fp16 values)
     if rope_theta:
-        need = up(need) + up(C * w.hkv * row) + int((mask == 0).sum()) * (w.sink + w.recent) * row
-    if v16:
-        need = (up(int(mask.sum()) * P * row) + up(C * w.hkv * row)
-                + int((mask == 0).sum()) * (w.sink + w.recent) * row)
+        end = up(end) + up(chunk_b) + str_b
+    need = up(end) + up(chunk_b) + str_b  # the chunk's and the streaming values in fp16
     staging = torch.empty(need if staged else 16, dtype=torch.uint8, device=dev)
     q = torch.from_numpy(W.tokens(w, "q", 0, 0, 0, P)).to(dev).to(torch.bfloat16)
     k = torch.from_numpy(W.tokens(w, "k", 0, 0, 0, P)).to(dev).to(torch.bfloat16)

@@ -363,8 +363,14 @@ namespace {
 // and V at pv, [nb][Hr][c_max][D] each; with pre-RoPE keys also the chunk's keys turned at
 // `chunk`, [nb][m][Hkv][D], and the layer's streaming keys turned at `str`, [B][Hs][S+R][D]
 // (indexed by sequence like the cache; only the call's sequences are written).
+// Staging of duo_attn_prefill_staged (byte offsets). On a 4- or 8-bit cache: the retrieval
+// prefix read back, keys (bf16) at 0 and values (fp16) at pv, both [nb][Hr][c_max][d]; with
+// pre-RoPE keys the chunk's keys turned at `chunk` and the streaming keys turned at `str`.
+// On every staged bf16 path: the chunk's values in fp16 at cv ([nb][m][Hkv][d]) and the
+// streaming values in fp16 at sv ([B][Hs][S+R][d]); on a bf16 cache the prefix values in fp16
+// at pv = 0 ([nb][Hr][c_max][d]). Regions start on 256-byte boundaries.
 struct StagingPlan {
-  uint64_t pv = 0, chunk = 0, str = 0, bytes = 0;
+  uint64_t pv = 0, chunk = 0, str = 0, cv = 0, sv = 0, bytes = 0;
   int32_t c_max = 0;
 };
 StagingPlan staging_plan(const duo_cache* c, int32_t layer, int32_t seq, int32_t n_chunk) {
@@ -376,24 +382,25 @@ StagingPlan staging_plan(const duo_cache* c, int32_t layer, int32_t seq, int32_t
   const uint64_t row = (uint64_t)c->cfg.head_dim * 2;
   const LayerInfo& li = c->layers[layer];
   const uint64_t pre = (uint64_t)nb * li.n_ret * (uint64_t)p.c_max * row;
+  const uint64_t chunk_bytes = (uint64_t)nb * n_chunk * c->cfg.num_kv_heads * row;
   const uint64_t str_bytes =
       (uint64_t)c->cfg.batch * li.n_str * ((uint64_t)c->cfg.sink + c->cfg.recent) * row;
-  if (c->cfg.dtype == DUO_BF16 && c->cfg.kv_bits != 4 && c->cfg.kv_bits != 8) {
-    // fp16 copies of the values: the retrieval prefix, the chunk's, the streaming caches'
+  uint64_t end;
+  if (c->cfg.kv_bits != 4 && c->cfg.kv_bits != 8) {
     p.pv = 0;
-    p.chunk = up(pre);
-    p.str = p.chunk + up((uint64_t)nb * n_chunk * c->cfg.num_kv_heads * row);
-    p.bytes = p.str + str_bytes;
-    return p;
-  }
-  p.pv = pre;
-  if (c->cfg.rope_theta > 0.f) {
-    p.chunk = up(2 * pre);
-    p.str = p.chunk + up((uint64_t)nb * n_chunk * c->cfg.num_kv_heads * row);
-    p.bytes = p.str + str_bytes;
+    end = pre;
   } else {
-    p.chunk = p.str = p.bytes = 2 * pre;
+    p.pv = pre;
+    end = 2 * pre;
+    if (c->cfg.rope_theta > 0.f) {
+      p.chunk = up(end);
+      p.str = p.chunk + up(chunk_bytes);
+      end = p.str + str_bytes;
+    }
   }
+  p.cv = up(end);
+  p.sv = p.cv + up(chunk_bytes);
+  p.bytes = p.sv + str_bytes;
   return p;
 }
 
@@ -494,9 +501,9 @@ duo_status prefill_v16(duo_cache* c, int32_t layer, int32_t seq, const void* q, 
   d.full_v = a.full_v;
   d.v = a.v;
   d.str_v = a.str_v;
-  d.out_pv = stg;
-  d.out_chunk = stg + sp.chunk;
-  d.out_str = stg + sp.str;
+  d.out_pv = stg + sp.pv;
+  d.out_chunk = stg + sp.cv;
+  d.out_str = stg + sp.sv;
   d.cap = a.cap;
   d.c_max = sp.c_max;
   d.b0 = a.b0;
@@ -510,11 +517,11 @@ duo_status prefill_v16(duo_cache* c, int32_t layer, int32_t seq, const void* q, 
   std::memcpy(d.c0, a.c0, sizeof(d.c0));
   if (launch_v16_stage(d, stream) != 0) return DUO_ERR_HIP;
   a.v16 = 1;
-  a.full_v = stg;
+  a.full_v = stg + sp.pv;
   a.vcap = sp.c_max;
   a.v_b0 = a.b0;
-  a.v = stg + sp.chunk;
-  a.str_v = stg + sp.str;
+  a.v = stg + sp.cv;
+  a.str_v = stg + sp.sv;
   const int group = c->cfg.num_q_heads / c->cfg.num_kv_heads;
   return launch_status(launch_prefill(a, c->cfg.dtype, c->cfg.head_dim, group, stream,
                                       next_marks(c, DUO_TIMING_PREFILL)));
@@ -582,6 +589,7 @@ duo_status duo_attn_prefill_staged(duo_cache* c, int32_t layer, int32_t seq, con
   d.nb = a.nb;
   d.Hr = a.Hr;
   d.cap_s = sp.c_max;
+  d.v_f16 = 1;
   std::memcpy(d.c0, a.c0, sizeof(d.c0));
   if (rope) {
     d.rope_base = rope_ptrs(c).base;
@@ -601,10 +609,32 @@ duo_status duo_attn_prefill_staged(duo_cache* c, int32_t layer, int32_t seq, con
   if (a.Hr > 0 && sp.c_max > 0 && launch_dequant_kv4(d, c->cfg.head_dim, stream) != 0)
     return DUO_ERR_HIP;
   if (rope && launch_rope_stage(d, c->cfg.head_dim, stream) != 0) return DUO_ERR_HIP;
+  // the chunk's and the streaming caches' values as fp16 copies too (the prefix values were
+  // read back in fp16), so the prefill kernel reads every V tile as it is
+  V16StageArgs v16;
+  std::memset(&v16, 0, sizeof(v16));
+  v16.v = a.v;
+  v16.str_v = a.str_v;
+  v16.out_chunk = stg + sp.cv;
+  v16.out_str = stg + sp.sv;
+  v16.b0 = a.b0;
+  v16.nb = a.nb;
+  v16.Hr = 0;  // no prefix groups
+  v16.Hs = a.Hs;
+  v16.SR = a.S + a.R;
+  v16.m = n_chunk;
+  v16.Hkv = a.Hkv;
+  v16.D = c->cfg.head_dim;
+  if (launch_v16_stage(v16, stream) != 0) return DUO_ERR_HIP;
   a.full_k = stg;
   a.full_v = stg + sp.pv;
   a.cap = sp.c_max;
   a.full_b0 = a.b0;
+  a.v16 = 1;
+  a.vcap = sp.c_max;
+  a.v_b0 = a.b0;
+  a.v = stg + sp.cv;
+  a.str_v = stg + sp.sv;
   if (rope) {
     a.k = stg + sp.chunk;
     a.str_k = stg + sp.str;

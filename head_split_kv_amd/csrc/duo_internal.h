@@ -199,6 +199,7 @@ struct DequantArgs {
   void* out_v;
   int64_t q4_stride, q4_params, q4_resid;  // Q4Geom of the regions
   int32_t qbits, b0, nb, Hr, cap_s;
+  int32_t v_f16;       // value rows in fp16 (each the bf16 read-back, converted exactly)
   int32_t c0[kMaxBatch];
   // Pre-RoPE caches (rope_base set): launch_dequant_kv4 reads back the values only, and
   // launch_rope_stage writes every key the chunk attends to, turned at its position: the

@@ -274,10 +274,24 @@ __device__ __forceinline__ uint4 f32x8_to_bf16(const float val[8]) {
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
+// A bf16 pair to an fp16 pair through float32, rounding to nearest even: exact for magnitudes
+// in [2^-14, 65504] (bf16 carries 8 significant bits, fp16 11), which is how the prefill kernel
+// takes bf16 values into its fp16 PV product.
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 half2_t;
+__device__ __forceinline__ uint32_t bf16w_to_f16w(uint32_t w) {
+  const f32x2_t x = {__builtin_bit_cast(float, w << 16), __builtin_bit_cast(float, w & 0xFFFF0000u)};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, half2_t));
+}
+__device__ __forceinline__ uint4 bf16x8_to_f16(uint4 w) {
+  return make_uint4(bf16w_to_f16w(w.x), bf16w_to_f16w(w.y), bf16w_to_f16w(w.z), bf16w_to_f16w(w.w));
+}
+
 // Read-back into bf16 rows (DequantArgs): one thread per (K or V, sequence, head, token, 8
 // channels), reading the codes through the layouts above. A value is c * scale + zero in
 // float32, rounded to bf16 to nearest even. With a.rope_base set only the values are read
-// back here (launch_rope_stage writes the keys).
+// back here (launch_rope_stage writes the keys). With a.v_f16 the value rows are written as
+// fp16 (the bf16 value, converted exactly) for the prefill kernel's fp16-value form.
 template <int D, int BITS>
 __global__ void __launch_bounds__(kThreads) kv4_dequant_kernel(DequantArgs a) {
   constexpr int CH = D / 8;
@@ -300,7 +314,8 @@ __global__ void __launch_bounds__(kThreads) kv4_dequant_kernel(DequantArgs a) {
     uint4* dst = (uint4*)((uint16_t*)(is_v ? a.out_v : a.out_k) +
                           (((int64_t)bi * a.Hr + r) * a.cap_s + t) * D + 8 * x);
     if (t >= (n / kG) * kG) {  // residual row
-      *dst = *(const uint4*)(head + a.q4_resid + (int64_t)(t % kG) * D * 2 + 16 * x);
+      const uint4 bw = *(const uint4*)(head + a.q4_resid + (int64_t)(t % kG) * D * 2 + 16 * x);
+      *dst = (is_v && a.v_f16) ? bf16x8_to_f16(bw) : bw;
       continue;
     }
     const int g = t / kG, tt = t % kG, c0 = 8 * x;
@@ -328,7 +343,8 @@ __global__ void __launch_bounds__(kThreads) kv4_dequant_kernel(DequantArgs a) {
         val[e] = __builtin_fmaf((float)code, sc, ze);
       }
     }
-    *dst = f32x8_to_bf16(val);
+    const uint4 bw = f32x8_to_bf16(val);
+    *dst = (is_v && a.v_f16) ? bf16x8_to_f16(bw) : bw;
   }
 }
 

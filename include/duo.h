@@ -241,11 +241,13 @@ duo_status duo_attn_prefill(duo_cache* cache, int32_t layer, int32_t seq, const 
 
 /* duo_attn_prefill over a layer whose retrieval caches are in 4 or 8 bits (explainer,
  * "Combination with Quantization": quantized caches serve the whole context). The retrieval
- * heads' earlier tokens are first read back into `staging` as bf16 rows, complete groups as
+ * heads' earlier tokens are first read back into `staging` as bf16 values, complete groups as
  * bf16(float32(c * scale + zero)) and residual rows as stored, [nb][Hr][c_max][d] for K then
  * the same for V (nb = 1, or B when seq = -1; Hr the layer's retrieval heads; c_max the
  * longest current length among the sequences); the chunk then attends as in duo_attn_prefill,
- * its own keys and values exact.
+ * its own keys and values exact. The values (the read-back, the chunk's and the streaming
+ * caches') enter staging as fp16 copies of those bf16 values, as the kernel's PV product takes
+ * them (below).
  * With cfg.rope_theta > 0 (pre-RoPE keys; OpenReview thread, the authors' reply on KV
  * quantization) q holds the chunk's queries after RoPE and k its keys before RoPE, as
  * appended. Every key the chunk attends to is then staged turned at its own position t
@@ -269,11 +271,12 @@ duo_status duo_attn_prefill_staged(duo_cache* cache, int32_t layer, int32_t seq,
                                    void* stream);
 
 /* Bytes of staging duo_attn_prefill_staged needs for this layer, seq (-1 = all sequences) and
- * a chunk of n_chunk tokens at the cache's current lengths: 2 * nb * Hr * c_max * d * 2 on a
- * 4- or 8-bit cache; with cfg.rope_theta > 0 that rounded up to 256 bytes, plus
- * nb * n_chunk * Hkv * d * 2 rounded up to 256, plus B * Hs * (S + R) * d * 2. On a bf16 cache
- * nb * Hr * c_max * d * 2 rounded up to 256, plus nb * n_chunk * Hkv * d * 2 rounded up to 256,
- * plus B * Hs * (S + R) * d * 2 (the fp16 values); 0 on an fp32 cache.
+ * a chunk of n_chunk tokens at the cache's current lengths, with P = nb * Hr * c_max * d * 2,
+ * C = nb * n_chunk * Hkv * d * 2, T = B * Hs * (S + R) * d * 2 and up() rounding up to 256
+ * bytes: up(E) + up(C) + T, the chunk's and the streaming values in fp16 after E bytes of
+ * read-backs, where E = 2 P on a 4- or 8-bit cache (E = up(2 P) + up(C) + T with
+ * cfg.rope_theta > 0: the turned chunk and streaming keys) and E = P on a bf16 cache (the
+ * prefix values in fp16); 0 on an fp32 cache.
  * DUO_ERR_INVALID for a bad layer or seq, n_chunk < 0 or a null `bytes`. Host only. */
 duo_status duo_prefill_staging_bytes(const duo_cache* cache, int32_t layer, int32_t seq,
                                      int32_t n_chunk, uint64_t* bytes);

@@ -29,14 +29,17 @@ def kvq_cache(w, capacity, bits, mode="window", out_dtype=torch.float32, rope_th
 
 
 def staging_need(w, mask, nb, c_max, m, rope):
-    """duo_prefill_staging_bytes as the header states it."""
+    """duo_prefill_staging_bytes as the header states it: the prefix keys and values, with
+    pre-RoPE keys the chunk's and the streaming keys, then the chunk's and the streaming
+    values (fp16), each region but the last rounded up to 256 bytes."""
     row = w.d * 2
-    pre = 2 * nb * int(mask.sum()) * c_max * row
-    if not rope:
-        return pre
     up = lambda x: (x + 255) // 256 * 256
-    return up(pre) + up(nb * m * w.hkv * row) + w.batch * int((mask == 0).sum()) * (
-        w.sink + w.recent) * row
+    chunk = nb * m * w.hkv * row
+    streaming = w.batch * int((mask == 0).sum()) * (w.sink + w.recent) * row
+    end = 2 * nb * int(mask.sum()) * c_max * row
+    if rope:
+        end = up(end) + up(chunk) + streaming
+    return up(end) + up(chunk) + streaming
 
 
 def run_prefill_kvq(w, lens, chunks, bits, mode="window", seqwise=False, heads=None,

@@ -305,9 +305,9 @@ def test_error_paths_leave_state_unchanged():
 
 
 def test_prefill_staged_checks_before_launch():
-    """duo_prefill_staging_bytes: 0 on an fp32 cache and on empty 4- and 8-bit caches without
-    RoPE; on a bf16 cache the fp16 copies of the chunk's and the streaming caches' values
-    (empty caches here); the chunk and streaming regions with pre-RoPE keys; argument checks.
+    """duo_prefill_staging_bytes: 0 on an fp32 cache; on bf16, 4- and 8-bit caches the fp16
+    copies of the chunk's and the streaming caches' values (empty caches here, so no prefix),
+    after the chunk and streaming keys with pre-RoPE keys; argument checks.
     duo_attn_prefill_staged rejects bad arguments and short staging before launching;
     duo_attn_prefill refuses every layer of a pre-RoPE cache, streaming-only layers
     included."""
@@ -323,8 +323,9 @@ def test_prefill_staged_checks_before_launch():
     for bits in (0, 4, 8):
         fc = FakeCache(kv_bits=bits)
         assert L.duo_prefill_staging_bytes(fc.h, 0, -1, 5, ctypes.byref(n)) == N.DUO_OK
-        # B 3, Hkv 2 (layer 0: one streaming head), d 128, S + R = 20
-        assert n.value == (up(3 * 5 * 2 * row) + 3 * 1 * 20 * row if bits == 0 else 0)
+        # B 3, Hkv 2 (layer 0: one streaming head), d 128, S + R = 20, empty caches: the fp16
+        # values of the chunk and of the streaming caches
+        assert n.value == up(3 * 5 * 2 * row) + 3 * 1 * 20 * row
         if bits == 0:
             assert L.duo_attn_prefill_staged(fc.h, 0, -1, p, p, p, 5, p, None, p,
                                              n.value - 16, None) == N.DUO_ERR_INVALID
@@ -348,8 +349,10 @@ def test_prefill_staged_checks_before_launch():
         for layer, hs in ((0, 1), (1, 2)):
             for seq, nb in ((-1, 3), (1, 1)):
                 assert L.duo_prefill_staging_bytes(fc.h, layer, seq, 5, ctypes.byref(n)) == 0
-                assert n.value == up(nb * 5 * 2 * row) + 3 * hs * 20 * row
-            need = up(3 * 5 * 2 * row) + 3 * hs * 20 * row
+                keys = up(nb * 5 * 2 * row) + 3 * hs * 20 * row  # chunk, streaming keys
+                assert n.value == up(keys) + up(nb * 5 * 2 * row) + 3 * hs * 20 * row
+            keys = up(3 * 5 * 2 * row) + 3 * hs * 20 * row
+            need = up(keys) + up(3 * 5 * 2 * row) + 3 * hs * 20 * row
             assert L.duo_attn_prefill_staged(fc.h, layer, -1, p, p, p, 5, p, None, p, need - 16,
                                              None) == N.DUO_ERR_INVALID
             assert L.duo_attn_prefill_staged(fc.h, layer, -1, p, p, p, 5, p, None, None, need,
