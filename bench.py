@@ -277,9 +277,10 @@ def prefill_leg(args, torch, hsk, W, N, mode="window", kv_bits=0, rope_theta=0.0
                 v16=False):
     """The 32K MHA prompt in 4K chunks; with v16 through duo_attn_prefill_staged on the bf16
     cache (the values the chunk reads converted to fp16 copies in staging first, which the
-    calls' time includes; the kernel timers cover the prefill kernel alone); with kv_bits 4 over a 4-bit cache
-    (duo_attn_prefill_staged: the retrieval prefix read back into bf16 staging, then the
-    prefill kernel; the kernel timers cover the prefill kernel alone); with rope_theta the
+    calls' time includes; the kernel timers cover the prefill kernel alone); with kv_bits 4
+    over a 4-bit cache (duo_attn_prefill_staged: the retrieval prefix read back into staging,
+    keys in bf16 and values in fp16, the chunk's and streaming values in fp16 beside them,
+    then the prefill kernel; the kernel timers cover it alone); with rope_theta the
     cache holds pre-RoPE keys, and every key the chunk reads is staged turned. With gqa the
     same 32K prompt in 4K chunks on the Llama-3-8B-shaped GQA layer (32 q / 8 KV heads, 4
     retrieval)."""
@@ -951,7 +952,8 @@ def main():
         },
         "prefill_kv4": None if pre_kv4 is None else {
             "workload": f"{pre_kv4['workload'].name}: 32K prompt in 4K chunks over 4-bit full "
-                        f"caches (retrieval prefix read back into bf16 staging per chunk)",
+                        f"caches (retrieval prefix read back into staging per chunk, keys in "
+                        f"bf16, values and the chunk's and streaming values in fp16)",
             "attn_ms": round(pre_kv4["attn_ms"], 3),
             "ms_incl_append": round(pre_kv4["pass_ms"], 3),
             "tflops": round(pre_kv4["tflops"], 1),
@@ -962,7 +964,8 @@ def main():
         "prefill_kv4_rope": None if pre_kv4r is None else {
             "workload": f"{pre_kv4r['workload'].name}: 32K prompt in 4K chunks over 4-bit full "
                         f"caches holding pre-RoPE keys (base 10,000): values read back and "
-                        f"every key the chunk reads turned, into bf16 staging per chunk",
+                        f"every key the chunk reads turned, into staging per chunk (keys "
+                        f"bf16, values fp16)",
             "attn_ms": round(pre_kv4r["attn_ms"], 3),
             "ms_incl_append": round(pre_kv4r["pass_ms"], 3),
             "tflops": round(pre_kv4r["tflops"], 1),
