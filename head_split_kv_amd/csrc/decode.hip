@@ -491,9 +491,8 @@ __global__ void __launch_bounds__(kThreads, 2)
 // unit; the partner operand carries 1/16 where the nibble was high and the products are
 // scaled back by 2^24 (also exact). Masking takes the elements of a word in the order
 // 0, 4, 1, 5, 2, 6, 3, 7, which the partner operand follows. A wave streams whole groups in
-// steps of 32 tokens, one register slot per step, each refilled with the same step of the next
-// group as soon as it is used: three steps of codes and the next group's (bf16) key parameters
-// are in flight (a wave moves the bytes it has in flight per memory latency). Codes are stored
+// steps of 32 tokens through two register slots, each refilled two steps ahead as soon as it
+// is used, with the next group's (bf16) key parameters also in flight. Codes are stored
 // in operand order (layout in duo.h): the KC key words of one token that a lane needs are
 // contiguous, and a wave's value words of a step are D / 64 contiguous KB, so every load
 // instruction reads one contiguous KB. The incomplete last group (bf16 residual rows) and the
@@ -973,9 +972,7 @@ __global__ void __launch_bounds__(kThreads, kRope ? 1 : 2)
       }
     };
 
-    // one register slot per step of a group: slot s is refilled with step s of the next
-    // group right after use, so three steps of loads stay in flight
-    static_assert(kSteps == 4, "one register slot per step of a group");
+    static_assert(kSteps == 4, "a group is four steps, walked by two register slots");
     // The query first, on a quiet memory system (fetched together with every wave's first
     // group, it waited behind that burst and the compute started later), then the first
     // group's loads.
@@ -1000,10 +997,11 @@ __global__ void __launch_bounds__(kThreads, kRope ? 1 : 2)
       }
     }
     __syncthreads();
-    if constexpr (BITS == 8) {
-      // 8-bit codes: a step is 8 KB, so two slots (16 KB in flight, as four 4-bit steps):
-      // a slot is refilled two steps ahead, steps 2 and 3 of the same group, then steps 0 and
-      // 1 of the next
+    {
+      // Two register slots of one step each, a slot refilled two steps ahead (steps 2 and 3
+      // of the same group, then steps 0 and 1 of the next): 8 KB in flight per wave with 4-bit
+      // codes, 16 KB with 8-bit ones. Four slots (a whole group ahead) put 35 MB of 4-bit
+      // loads in flight at the start and measured 3 % slower (6 % with pre-RoPE keys).
       Ld f0, f1;
       if (n_wave > 0) {
         load_params(0);
@@ -1013,6 +1011,8 @@ __global__ void __launch_bounds__(kThreads, kRope ? 1 : 2)
       for (int gi = 0; gi < n_full; ++gi) {
         fold();
         load_params(gi + 1);  // clamped past the last group
+        // the barriers keep each slot's last use ahead of its reload, so the reload lands in
+        // the same registers (no loop-carried copy, which would wait for the load)
         step(f0, 0);
         __builtin_amdgcn_sched_barrier(0);
         load_step(f0, gi, 2);
@@ -1039,38 +1039,6 @@ __global__ void __launch_bounds__(kThreads, kRope ? 1 : 2)
           load_step(f1, n_full, 3);
           step(f1, 3);
         }
-      }
-    } else {
-      Ld f0, f1, f2, f3;
-      if (n_wave > 0) {
-        load_params(0);
-        load_step(f0, 0, 0);
-        load_step(f1, 0, 1);
-        load_step(f2, 0, 2);
-        load_step(f3, 0, 3);
-      }
-      for (int gi = 0; gi < n_full; ++gi) {
-        fold();
-        load_params(gi + 1);  // clamped past the last group
-        // the barriers keep each slot's last use ahead of its reload, so the reload lands in
-        // the same registers (no loop-carried copy, which would wait for the load)
-        step(f0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        load_step(f0, gi + 1, 0);
-        step(f1, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        load_step(f1, gi + 1, 1);
-        step(f2, 2);
-        __builtin_amdgcn_sched_barrier(0);
-        load_step(f2, gi + 1, 2);
-        step(f3, 3);
-        __builtin_amdgcn_sched_barrier(0);
-        load_step(f3, gi + 1, 3);
-      }
-      if (t_step >= 0) {  // the leftover step, already in its slot (the others read the idle buffer)
-        fold();
-        const Ld& ft = t_step == 0 ? f0 : t_step == 1 ? f1 : t_step == 2 ? f2 : f3;
-        step(ft, t_step);
       }
     }
   }
